@@ -1,0 +1,150 @@
+"""CPU oracle for DSpark's serial Markov draft walk -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path
+(``serial_draft_head_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``walk_oracle.c`` (plain C, binary64, OpenMP over
+vocabulary rows).  This module only compiles it with gcc, loads it with
+ctypes and converts numpy arrays.  bf16 tensors are passed as ``uint16`` bit
+patterns.
+
+What it computes (see the header of walk_oracle.c for the passages followed):
+"Keeping the Draft Walk on Chip" (tie-pilot-qxw.github.io), section
+"The serial part of a parallel drafter": ``u = W1[prev]``,
+``logit = bf16(base + bf16(W2 @ u))``, argmax or a sample of
+``softmax(logit / T)``, ``prev = tok``; the sampler is the inverse CDF of
+vLLM PR #64442, section "Details".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "walk_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile walk_oracle.c into liboracle.so with gcc (IEEE binary64, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i, f = ctypes.c_int, ctypes.c_float
+    lib.oracle_rne_bf16.restype = ctypes.c_double
+    lib.oracle_rne_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_rne_bf16_array.restype = None
+    lib.oracle_rne_bf16_array.argtypes = [P, P, P, ctypes.c_long]
+    lib.oracle_step.restype = i
+    lib.oracle_step.argtypes = [i, i, P, P, P, P, P, f, f, P]
+    lib.oracle_sample.restype = i
+    lib.oracle_sample.argtypes = [i, P, f, f]
+    lib.oracle_walk.restype = i
+    lib.oracle_walk.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_threads.restype = i
+    lib.oracle_threads.argtypes = []
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [i]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def rne_bf16(x):
+    """Round float64 values to bf16, ties to even.  Returns (values f64, bits u16)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    bits = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_rne_bf16_array(_ptr(x), _ptr(y), _ptr(bits), x.size)
+    return y, bits
+
+
+def bf16_bits_to_f64(bits):
+    """Exact value of bf16 bit patterns (a plain reinterpretation)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def step(u_bits, base_bits, T, uniform, W2_bits=None, Q=None, scale=None):
+    """One step for one request.  Returns (token, logits_bits[V])."""
+    u_bits = _c(u_bits, np.uint16)
+    base_bits = _c(base_bits, np.uint16)
+    W2_bits, Q, scale = _c(W2_bits, np.uint16), _c(Q, np.int8), _c(scale, np.float32)
+    V = base_bits.shape[0]
+    r = u_bits.shape[0]
+    out = np.empty(V, dtype=np.uint16)
+    tok = _load().oracle_step(V, r, _ptr(u_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+                              _ptr(base_bits), float(T), float(uniform), _ptr(out))
+    if tok < 0:
+        raise RuntimeError(f"oracle_step failed with {tok}")
+    return tok, out
+
+
+def sample(logits_bits, T, uniform) -> int:
+    """Inverse-CDF draw over softmax(logits / T) for given bf16 logits."""
+    lb = _c(logits_bits, np.uint16)
+    tok = _load().oracle_sample(lb.shape[0], _ptr(lb), float(T), float(uniform))
+    if tok < 0:
+        raise RuntimeError(f"oracle_sample failed with {tok}")
+    return tok
+
+
+def walk(W1_bits, base_bits, anchor, T, uniforms=None, W2_bits=None, Q=None, scale=None,
+         forced=None, want_logits=True):
+    """The whole walk.  Shapes: W1 [V,r] u16, W2 [V,r] u16 (or Q [V,r] i8 + scale [V] f32),
+    base [B,gamma,V] u16, anchor [B] i32, T [B] f32, uniforms [B,gamma] f32 or None,
+    forced [B,gamma] i32 or None (teacher forcing: step k>0 uses forced[:,k-1] as prev).
+
+    Returns (tokens [B,gamma] i32, logits [B,gamma,V] u16 or None)."""
+    W1_bits = _c(W1_bits, np.uint16)
+    W2_bits, Q, scale = _c(W2_bits, np.uint16), _c(Q, np.int8), _c(scale, np.float32)
+    base_bits = _c(base_bits, np.uint16)
+    anchor = _c(anchor, np.int32)
+    T = _c(T, np.float32)
+    uniforms = _c(uniforms, np.float32)
+    forced = _c(forced, np.int32)
+    V, r = W1_bits.shape
+    B, gamma = base_bits.shape[0], base_bits.shape[1]
+    assert base_bits.shape[2] == V
+    tokens = np.empty((B, gamma), dtype=np.int32)
+    logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
+    rc = _load().oracle_walk(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+                             _ptr(base_bits), _ptr(anchor), _ptr(T), _ptr(uniforms),
+                             _ptr(forced), _ptr(tokens), _ptr(logits))
+    if rc != 0:
+        raise RuntimeError(f"oracle_walk failed with {rc}")
+    return tokens, logits

@@ -1,0 +1,248 @@
+/*
+ * walk_oracle.c -- plain CPU oracle for the serial Markov draft walk of
+ * DSpark's head.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The GPU product path
+ * never calls it, shares no code with it and must fail loudly without its own
+ * HIP library.
+ *
+ * Source: "Keeping the Draft Walk on Chip: One Launch for DSpark's Markov
+ * Head" (tie-pilot-qxw.github.io), sections "The serial part of a parallel
+ * drafter" (the walk and its rounding points), "The idea: make the walk
+ * resident" (ties go to the smallest token id; the token is chosen from the
+ * very bf16 logits that are emitted) and "B200: the bf16 table fits on chip"
+ * (fp32 accumulation, bias rounded to bf16, then the sum rounded to bf16).
+ * Sampling follows vLLM PR #64442 "fused Markov sampling", section "Details"
+ * (inverse CDF over softmax(cached logits / T) driven by one uniform per
+ * request and step).
+ *
+ * Everything is computed in IEEE binary64 with plain loops:
+ *   u_j      = W1[prev, j]                               (bf16 -> f64, exact)
+ *   acc_v    = sum_j W2[v, j] * u_j   in ascending j     (products exact in f64)
+ *   int8:      acc_v = scale_v * sum_j q[v, j] * u_j
+ *   bias_v   = RNE_bf16(acc_v)        rounded straight from f64
+ *   logit_v  = RNE_bf16(base_v + bias_v)  (the f64 sum of two bf16 is exact)
+ *   T == 0 : tok = smallest v with logit_v == max_w logit_w
+ *   T  > 0 : M = max logit, w_v = exp((logit_v - M) / T), C_v = sum_{j<=v} w_j,
+ *            Z = C_{V-1}, t = uniform * Z, tok = smallest v with C_v > t
+ *            (if rounding leaves none, the largest v with w_v > 0).
+ *   prev     = tok for the next step.
+ *
+ * Parallelism: OpenMP over vocabulary rows inside one GEMV.  Each row's sum
+ * is formed by one thread in a fixed order, so results do not depend on the
+ * thread count.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 bit pattern -> its exact value as a double. */
+static double bf16_value(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Round x to the nearest bf16 value (8 significant bits, exponent range of
+ * binary32), ties to even, directly from binary64.  The result is returned as
+ * a double that is exactly representable in bf16.  Overflow goes to +-inf. */
+double oracle_rne_bf16(double x) {
+    if (isnan(x) || isinf(x) || x == 0.0) return x;
+    int e = ilogb(x);           /* x = m * 2^e with 1 <= |m| < 2 */
+    if (e < -126) e = -126;     /* below the normal range the spacing is 2^-133 */
+    /* scale so that one bf16 unit in the last place becomes 1.0, round to an
+     * integer in the current (to-nearest-even) mode, scale back */
+    double y = ldexp(nearbyint(ldexp(x, 7 - e)), e - 7);
+    if (fabs(y) >= ldexp(1.0, 128)) y = copysign(INFINITY, x);
+    return y;
+}
+
+/* bf16 bit pattern of a double that is exactly representable in bf16. */
+uint16_t oracle_bf16_bits(double y) {
+    float f = (float)y;         /* exact for bf16-representable values */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(bits >> 16);
+}
+
+/* Vectorised helpers for the Python side: RNE of n doubles (values and bits). */
+void oracle_rne_bf16_array(const double* x, double* y, uint16_t* bits, long n) {
+    for (long i = 0; i < n; ++i) {
+        double v = oracle_rne_bf16(x[i]);
+        if (y) y[i] = v;
+        if (bits) bits[i] = oracle_bf16_bits(v);
+    }
+}
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Inverse-CDF draw over softmax(logit / T) from one uniform in [0, 1).
+ * logit holds V finite values.  Returns the chosen token id. */
+static int sample_inverse_cdf(const double* logit, int V, double T, double uniform) {
+    double M = logit[0];
+    for (int v = 1; v < V; ++v)
+        if (logit[v] > M) M = logit[v];
+    double* C = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!C) return -3;
+    double run = 0.0;
+    int last_positive = -1;
+    for (int v = 0; v < V; ++v) {
+        double w = exp((logit[v] - M) / T);
+        if (w > 0.0) last_positive = v;
+        run += w;
+        C[v] = run;
+    }
+    double t = uniform * C[V - 1];
+    int tok = -1;
+    for (int v = 0; v < V; ++v) {
+        if (C[v] > t) { tok = v; break; }
+    }
+    if (tok < 0) tok = last_positive;
+    free(C);
+    return tok;
+}
+
+/*
+ * One step for one request.
+ *   u        : W1 row of the previous token, r bf16 values (bits)
+ *   W2       : [V][r] bf16 bits, or NULL when Q/scale are given
+ *   Q, scale : [V][r] int8 and [V] f32 (int8 variant), else NULL
+ *   base     : [V] bf16 bits of this step's base logits
+ *   T        : temperature; exactly 0 selects greedy argmax
+ *   uniform  : the step's uniform in [0,1) (ignored when T == 0)
+ *   logits   : [V] bf16 bits out (may be NULL)
+ *   scratch  : [V] doubles of caller-provided work space
+ * Returns the token (>= 0) or a negative error (-2: a logit is not finite).
+ */
+static int oracle_step_impl(int V, int r, const uint16_t* u_bits,
+                            const uint16_t* W2, const int8_t* Q, const float* scale,
+                            const uint16_t* base, float T, float uniform,
+                            uint16_t* logits, double* lg) {
+    double* u = (double*)malloc(sizeof(double) * (size_t)r);
+    if (!u) return -3;
+    for (int j = 0; j < r; ++j) u[j] = bf16_value(u_bits[j]);
+
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int v = 0; v < V; ++v) {
+        double acc = 0.0;
+        if (W2) {
+            const uint16_t* row = W2 + (size_t)v * (size_t)r;
+            for (int j = 0; j < r; ++j) acc += bf16_value(row[j]) * u[j];
+        } else {
+            const int8_t* row = Q + (size_t)v * (size_t)r;
+            double dot = 0.0;
+            for (int j = 0; j < r; ++j) dot += (double)row[j] * u[j];
+            acc = (double)scale[v] * dot;
+        }
+        double bias = oracle_rne_bf16(acc);
+        double logit = oracle_rne_bf16(bf16_value(base[v]) + bias);
+        if (!isfinite(logit)) bad = 1;
+        lg[v] = logit;
+        if (logits) logits[v] = oracle_bf16_bits(logit);
+    }
+    free(u);
+    if (bad) return -2;
+
+    if (T == 0.0f) {
+        int best = 0;
+        for (int v = 1; v < V; ++v)
+            if (lg[v] > lg[best]) best = v;   /* strict: the first maximum wins */
+        return best;
+    }
+    return sample_inverse_cdf(lg, V, (double)T, (double)uniform);
+}
+
+/* Public single step (see oracle_step_impl). */
+int oracle_step(int V, int r, const uint16_t* u_bits, const uint16_t* W2,
+                const int8_t* Q, const float* scale, const uint16_t* base,
+                float T, float uniform, uint16_t* logits) {
+    if (V <= 0 || r <= 0 || !u_bits || !base || (!W2 && (!Q || !scale))) return -1;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!lg) return -3;
+    int tok = oracle_step_impl(V, r, u_bits, W2, Q, scale, base, T, uniform, logits, lg);
+    free(lg);
+    return tok;
+}
+
+/* Inverse-CDF draw on given bf16 logits (used to judge sampled GPU tokens
+ * against the GPU's own emitted logits). */
+int oracle_sample(int V, const uint16_t* logits, float T, float uniform) {
+    if (V <= 0 || !logits || !(T > 0.0f)) return -1;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!lg) return -3;
+    for (int v = 0; v < V; ++v) lg[v] = bf16_value(logits[v]);
+    int tok = sample_inverse_cdf(lg, V, (double)T, (double)uniform);
+    free(lg);
+    return tok;
+}
+
+/*
+ * The whole walk for B independent requests.
+ *   W1       : [V][r] bf16 bits
+ *   W2       : [V][r] bf16 bits, or NULL with Q [V][r] int8 + scale [V] f32
+ *   base     : [B][gamma][V] bf16 bits
+ *   anchor   : [B] token ids in [0, V)
+ *   T        : [B] temperatures (0 = greedy)
+ *   uniforms : [B][gamma] in [0, 1), or NULL when every T is 0
+ *   forced   : [B][gamma] or NULL.  When given, step k > 0 of request b uses
+ *              prev = forced[b][k-1] instead of the oracle's own token
+ *              (teacher forcing, so each step can be judged on its own).
+ *   tokens   : [B][gamma] out
+ *   logits   : [B][gamma][V] bf16 bits out, or NULL
+ * Returns 0, or a negative error (-1 bad argument, -2 non-finite logit,
+ * -3 out of memory).
+ */
+int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
+                const uint16_t* W2, const int8_t* Q, const float* scale,
+                const uint16_t* base, const int32_t* anchor, const float* T,
+                const float* uniforms, const int32_t* forced, int32_t* tokens,
+                uint16_t* logits) {
+    if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !base || !anchor || !T ||
+        !tokens || (!W2 && (!Q || !scale)))
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        if (T[b] != 0.0f && !uniforms) return -1;
+        if (anchor[b] < 0 || anchor[b] >= V) return -1;
+    }
+    double* lg = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!lg) return -3;
+    for (int b = 0; b < B; ++b) {
+        int prev = anchor[b];
+        for (int k = 0; k < gamma; ++k) {
+            if (forced && k > 0) prev = forced[(size_t)b * gamma + (k - 1)];
+            if (prev < 0 || prev >= V) { free(lg); return -1; }
+            const uint16_t* base_k = base + ((size_t)b * gamma + k) * (size_t)V;
+            uint16_t* out = logits ? logits + ((size_t)b * gamma + k) * (size_t)V : NULL;
+            float uni = uniforms ? uniforms[(size_t)b * gamma + k] : 0.0f;
+            int tok = oracle_step_impl(V, r, W1 + (size_t)prev * (size_t)r, W2, Q, scale,
+                                       base_k, T[b], uni, out, lg);
+            if (tok < 0) { free(lg); return tok; }
+            tokens[(size_t)b * gamma + k] = tok;
+            prev = tok;
+        }
+    }
+    free(lg);
+    return 0;
+}

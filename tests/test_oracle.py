@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: hand-worked
+fixtures, exact rational brute force, a bit-pattern search for rounding,
+library routines (numpy argmax, torch's float32->bf16 cast, numpy matmul) on
+special cases, and closed-form sampler probabilities.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import brute_force as bf
+import workloads
+from exact_bf16 import rne_bits, value
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def f32_to_bf16_bits_torch(x):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_of(values):
+    """Exact bf16 values (python floats) -> bit patterns, via the exact search."""
+    return np.array([rne_bits(Fraction(v)) for v in values], dtype=np.uint16)
+
+
+# --------------------------------------------------------------------------- RNE
+class TestRounding:
+    def test_random_against_exact_search(self, oracle_mod):
+        rng = np.random.default_rng(1)
+        x = np.concatenate([
+            rng.standard_normal(3000) * 10.0 ** rng.integers(-40, 38, 3000),
+            rng.standard_normal(1000),
+        ])
+        _, bits = oracle_mod.rne_bf16(x)
+        for xi, bi in zip(x, bits):
+            assert int(bi) == rne_bits(Fraction(float(xi))), xi
+
+    def test_every_halfway_point_in_several_binades(self, oracle_mod):
+        mids, want = [], []
+        for hi in (0x3F, 0x40, 0x41, 0x00, 0x80 | 0x3F, 0x7F):
+            for lo in range(0, 0x100):
+                p = (hi << 8) | lo
+                if (p & 0x7F80) == 0x7F80:
+                    continue
+                q = p + 1
+                if (q & 0x7F80) == 0x7F80:
+                    continue
+                m = (value(p) + value(q)) / 2
+                mids.append(float(m))          # exact in binary64
+                want.append(rne_bits(m))
+        _, bits = oracle_mod.rne_bf16(np.array(mids))
+        assert [int(b) for b in bits] == want
+        # the tie goes to the even pattern in every case
+        assert all(w % 2 == 0 for w in want)
+
+    def test_matches_torch_cast_where_f64_equals_f32(self, oracle_mod):
+        rng = np.random.default_rng(2)
+        x32 = (rng.standard_normal(200_000) * 3).astype(np.float32)
+        x32 = np.concatenate([x32, x32 * np.float32(1e-30), x32 * np.float32(1e30)])
+        _, bits = oracle_mod.rne_bf16(x32.astype(np.float64))
+        assert np.array_equal(bits, f32_to_bf16_bits_torch(x32))
+
+    def test_edges(self, oracle_mod):
+        cases = [
+            (0.0, 0x0000), (-0.0, 0x8000),
+            (2.0 ** -133, 0x0001),                    # smallest subnormal
+            (3 * 2.0 ** -134, 0x0002),                # tie between 1 and 2 ulps -> even (2)
+            (2.0 ** -134, 0x0000),                    # tie between 0 and 1 ulp -> even (0)
+            (-(2.0 ** -135), 0x8000),                 # tiny negative rounds to -0
+            (float(value(0x7F7F)), 0x7F7F),           # largest finite
+            (2.0 ** 128 - 2.0 ** 119, 0x7F80),        # tie between max (2^128 - 2^120) and 2^128 -> inf
+            (2.0 ** 128 - 2.0 ** 119 - 2.0 ** 100, 0x7F7F),
+            (-(2.0 ** 129), 0xFF80),
+        ]
+        xs = np.array([c[0] for c in cases])
+        _, bits = oracle_mod.rne_bf16(xs)
+        for (x, want), b in zip(cases, bits):
+            assert int(b) == want, (x, hex(int(b)))
+
+
+# ------------------------------------------------------------------ hand fixtures
+def test_hand_worked_walk(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_walk_v4_r2.json")) as f:
+        g = json.load(f)
+    W1 = bits_of(np.ravel(g["W1"])).reshape(g["V"], g["r"])
+    W2 = bits_of(np.ravel(g["W2"])).reshape(g["V"], g["r"])
+    base = bits_of(np.ravel(g["base"])).reshape(1, g["gamma"], g["V"])
+    toks, logits = oracle_mod.walk(W1, base, [g["anchor"]], [g["T"]], W2_bits=W2)
+    assert toks[0].tolist() == g["expected_tokens"]
+    want = [[int(x, 16) for x in row] for row in g["expected_logits_bits"]]
+    assert logits[0].tolist() == want
+
+
+def test_hand_worked_sampler(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_sampler.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        lb = bits_of(c["logits"])
+        assert oracle_mod.sample(lb, c["T"], c["u"]) == c["token"], c
+    # the closed-form boundary e/(e+1)
+    p0 = math.e / (math.e + 1.0)
+    lb = bits_of([1.0, 0.0])
+    assert oracle_mod.sample(lb, 1.0, np.nextafter(np.float32(p0), np.float32(0))) == 0
+    assert oracle_mod.sample(lb, 1.0, np.nextafter(np.float32(p0), np.float32(1))) == 1
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("seed", range(50))
+def test_brute_force_v12_r4_all_anchors(oracle_mod, seed):
+    d = workloads.toy(seed, V=12, r=4, B=12, gamma=3, w2_std=0.5, base_std=1.0)
+    anchors = np.arange(12, dtype=np.int32)
+    base = d["base"]
+    T = np.zeros(12, dtype=np.float32)
+    toks, logits = oracle_mod.walk(d["W1"], base, anchors, T, W2_bits=d["W2"])
+    for b in range(12):
+        bt, bl, _ = bf.walk(d["W1"], d["W2"], base[b], anchors[b])
+        assert toks[b].tolist() == bt
+        assert logits[b].tolist() == bl
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_brute_force_int8_variant(oracle_mod, seed):
+    d = workloads.toy(seed + 100, V=12, r=4, B=12, gamma=3, w2_std=0.5, base_std=0.2)
+    Q, scale = workloads.quantize_int8(d["W2"])
+    anchors = np.arange(12, dtype=np.int32)
+    T = np.zeros(12, dtype=np.float32)
+    toks, logits = oracle_mod.walk(d["W1"], d["base"], anchors, T, Q=Q, scale=scale)
+    for b in range(12):
+        bt, bl, _ = bf.walk(d["W1"], None, d["base"][b], anchors[b], Q=Q, scale=scale)
+        assert toks[b].tolist() == bt
+        assert logits[b].tolist() == bl
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_bigram_route(oracle_mod, seed):
+    """logit_k = bf16(base_k + bf16((W2 W1^T)[:, prev])), through the exact V x V bigram matrix."""
+    V, r = 12, 4
+    d = workloads.toy(seed + 200, V=V, r=r, B=1, gamma=3)
+    W1 = [[value(x) for x in row] for row in d["W1"]]
+    W2 = [[value(x) for x in row] for row in d["W2"]]
+    bigram = [[sum(W2[v][j] * W1[p][j] for j in range(r)) for p in range(V)] for v in range(V)]
+    toks, logits = oracle_mod.walk(d["W1"], d["base"], d["anchor"], [0.0], W2_bits=d["W2"])
+    prev = int(d["anchor"][0])
+    for k in range(3):
+        want = [rne_bits(value(d["base"][0, k, v]) + value(rne_bits(bigram[v][prev]))) for v in range(V)]
+        assert logits[0, k].tolist() == want
+        prev = int(toks[0, k])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_sampled(oracle_mod, seed):
+    V = 12
+    d = workloads.toy(seed + 300, V=V, r=4, B=1, gamma=3, base_std=1.5)
+    for T in (0.6, 1.0, 2.5):
+        toks, logits = oracle_mod.walk(d["W1"], d["base"], d["anchor"], [T],
+                                       uniforms=d["uniforms"], W2_bits=d["W2"])
+        bt, bl, margin = bf.walk(d["W1"], d["W2"], d["base"][0], d["anchor"][0], T=T,
+                                 uniforms=d["uniforms"][0])
+        assert logits[0].tolist() == bl
+        if margin > 1e-12:
+            assert toks[0].tolist() == bt
+
+
+# ------------------------------------------------------------- special cases
+def test_zero_w2_gives_argmax_of_base(oracle_mod):
+    V, r, gamma = 300, 256, 4
+    d = workloads.toy(7, V=V, r=r, B=V, gamma=gamma)
+    W2 = np.zeros((V, r), dtype=np.uint16)
+    anchors = np.arange(V, dtype=np.int32)
+    toks, logits = oracle_mod.walk(d["W1"], d["base"], anchors, np.zeros(V, np.float32), W2_bits=W2)
+    assert np.array_equal(logits, d["base"])
+    basef = oracle_mod.bf16_bits_to_f64(d["base"])
+    assert np.array_equal(toks, np.argmax(basef, axis=2))
+
+
+def test_zero_base_is_single_rounding_of_numpy_matmul(oracle_mod):
+    V, r = 1000, 256
+    W1, W2 = workloads.weights(0, V=V, r=r)
+    base = np.zeros((1, 7, V), dtype=np.uint16)
+    toks, logits = oracle_mod.walk(W1, base, [5], [0.0], W2_bits=W2)
+    W1f, W2f = oracle_mod.bf16_bits_to_f64(W1), oracle_mod.bf16_bits_to_f64(W2)
+    prev = 5
+    for k in range(7):
+        acc = W2f @ W1f[prev]                          # numpy / BLAS route
+        want = [rne_bits(Fraction(float(a))) for a in acc]
+        assert logits[0, k].tolist() == want
+        wv = [value(w) for w in want]
+        assert int(toks[0, k]) == wv.index(max(wv))    # first maximum of the emitted logits
+        prev = int(toks[0, k])
+
+
+def test_medium_vocab_against_numpy_and_exact_rounding(oracle_mod):
+    V, r, gamma = 1000, 256, 7
+    W1, W2 = workloads.weights(0, V=V, r=r)
+    inp = workloads.round_inputs(0, 0, B=1, gamma=gamma, V=V)
+    toks, logits = oracle_mod.walk(W1, inp["base"], inp["anchor"], inp["T"], W2_bits=W2)
+    W1f, W2f = oracle_mod.bf16_bits_to_f64(W1), oracle_mod.bf16_bits_to_f64(W2)
+    prev = int(inp["anchor"][0])
+    for k in range(gamma):
+        acc = W2f @ W1f[prev]
+        bias = [rne_bits(Fraction(float(a))) for a in acc]
+        want = [rne_bits(value(inp["base"][0, k, v]) + value(bias[v])) for v in range(V)]
+        assert logits[0, k].tolist() == want
+        lv = oracle_mod.bf16_bits_to_f64(logits[0, k])
+        assert toks[0, k] == int(np.argmax(lv))        # numpy: first occurrence
+        prev = int(toks[0, k])
+
+
+def test_vocab_of_one():
+    import oracle
+    W1 = workloads.to_bf16_bits(np.ones((1, 8)))
+    W2 = workloads.to_bf16_bits(np.full((1, 8), 0.5))
+    base = workloads.to_bf16_bits(np.zeros((2, 5, 1)))
+    toks, _ = oracle.walk(W1, base, [0, 0], [0.0, 1.0], uniforms=np.full((2, 5), 0.99, np.float32),
+                          W2_bits=W2)
+    assert toks.tolist() == [[0] * 5, [0] * 5]
+
+
+def test_constructed_exact_ties_pick_lowest_index(oracle_mod):
+    V, r = 64, 256
+    W1 = workloads.to_bf16_bits(np.ones((V, r)))
+    W2 = np.zeros((V, r), dtype=np.uint16)
+    base = np.zeros((1, 3, V), dtype=np.float32)
+    base[0, 0, [17, 40, 63]] = 2.5                   # three-way tie at the top
+    base[0, 1, :] = 1.0                              # all equal
+    base[0, 2, [63, 5]] = -0.0                       # -0 and +0 compare equal
+    base[0, 2, :5] = -1.0
+    toks, _ = oracle_mod.walk(W1, workloads.to_bf16_bits(base), [0], [0.0], W2_bits=W2)
+    assert toks[0].tolist() == [17, 0, 5]
+
+
+# ------------------------------------------------------------------- sampler
+def test_sampler_grid_matches_closed_form(oracle_mod):
+    rng = np.random.default_rng(5)
+    logits_bits = workloads.to_bf16_bits(rng.standard_normal(40) * 2)
+    vals = list(oracle_mod.bf16_bits_to_f64(logits_bits))
+    for T in (0.6, 1.0):
+        import mpmath
+        M = max(vals)
+        w = [mpmath.e ** ((mpmath.mpf(l) - M) / mpmath.mpf(float(np.float32(T)))) for l in vals]
+        Z = sum(w)
+        p = [float(x / Z) for x in w]
+        N = 20000
+        counts = np.zeros(len(vals), dtype=int)
+        for i in range(N):
+            u = np.float32((i + 0.5) / N)
+            counts[oracle_mod.sample(logits_bits, T, u)] += 1
+        assert np.all(np.abs(counts - N * np.asarray(p)) <= 1.0 + 1e-9), (counts, N * np.asarray(p))
+
+
+def test_sampler_monotone_and_endpoints(oracle_mod):
+    rng = np.random.default_rng(6)
+    logits_bits = workloads.to_bf16_bits(rng.standard_normal(500) * 3)
+    us = np.sort(rng.random(400).astype(np.float32))
+    toks = [oracle_mod.sample(logits_bits, 1.0, u) for u in us]
+    assert all(a <= b for a, b in zip(toks, toks[1:]))
+    assert oracle_mod.sample(logits_bits, 1.0, 0.0) == 0
+    # weights that underflow to zero are never drawn; u = 0 takes the first positive weight
+    lb = bits_of([-3.0e38, -3.0e38, 5.0, 1.0, -3.0e38])
+    assert oracle_mod.sample(lb, 0.6, 0.0) == 2
+    assert oracle_mod.sample(lb, 0.6, np.float32(0.9999999)) == 3
+
+
+def test_small_temperature_is_argmax_and_zero_temperature_is_argmax(oracle_mod):
+    V = 2000
+    W1, W2 = workloads.weights(0, V=V)
+    inp = workloads.round_inputs(0, 3, B=1, gamma=7, V=V)
+    t0, lg0 = oracle_mod.walk(W1, inp["base"], inp["anchor"], [0.0], W2_bits=W2)
+    # T = 0 is the lowest-index argmax of the emitted logits
+    for k in range(7):
+        assert t0[0, k] == int(np.argmax(oracle_mod.bf16_bits_to_f64(lg0[0, k])))
+    # T -> 0+ with a clear gap reduces to the argmax
+    t1, lg1 = oracle_mod.walk(W1, inp["base"], inp["anchor"], [1e-4],
+                              uniforms=np.full((1, 7), 0.5, np.float32), forced=t0, W2_bits=W2)
+    for k in range(7):
+        lv = np.sort(oracle_mod.bf16_bits_to_f64(lg1[0, k]))
+        if lv[-1] - lv[-2] > 0.01:
+            assert t1[0, k] == t0[0, k]
+
+
+def test_teacher_forcing_with_own_tokens_is_free_running(oracle_mod):
+    V = 3000
+    W1, W2 = workloads.weights(1, V=V)
+    inp = workloads.round_inputs(2, 1, B=3, gamma=6, V=V, temps="mixed")
+    t0, l0 = oracle_mod.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2)
+    t1, l1 = oracle_mod.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2,
+                             forced=t0)
+    assert np.array_equal(t0, t1) and np.array_equal(l0, l1)
+    # forcing a different history changes later steps only
+    f = t0.copy()
+    f[:, 2] = (f[:, 2] + 1) % V
+    t2, l2 = oracle_mod.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2,
+                             forced=f)
+    assert np.array_equal(l2[:, :3], l0[:, :3])
+    assert not np.array_equal(l2[:, 3], l0[:, 3])
+
+
+def test_thread_count_does_not_change_results(oracle_mod):
+    V = 5000
+    W1, W2 = workloads.weights(0, V=V)
+    inp = workloads.round_inputs(2, 4, B=2, gamma=5, V=V, temps="mixed")
+    oracle_mod.set_threads(1)
+    a = oracle_mod.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2)
+    oracle_mod.set_threads(8)
+    b = oracle_mod.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_int8_quantizer_recipe():
+    # row max 127 * 2^-7 gives the exact scale 2^-7; -63.5 * 2^-7 / 2^-7 is a tie -> even -64
+    W2 = workloads.to_bf16_bits(np.array([[0.0, 0.0], [127 / 128, -63.5 / 128], [0.02, -0.0201]]))
+    Q, s = workloads.quantize_int8(W2)
+    assert s[0] == 0 and Q[0].tolist() == [0, 0]
+    assert s[1] == np.float32(2.0 ** -7) and Q[1].tolist() == [127, -64]
+    assert int(Q[2, 1]) == -127 and s[2] == np.float32(abs(float(value(int(W2[2, 1])))) / 127)
