@@ -1,0 +1,255 @@
+"""Benchmark of the serial Markov draft walk on one MI355X.
+
+One "step" of this benchmark is one round of the walk: one dsw_walk call over
+one seeded synthetic round (base logits, anchor, temperatures, uniforms) of
+the chosen workload.  Default: vocabulary 151,936, r = 256, gamma = 7, one
+greedy request (the Qwen3-size configuration), 1000 distinct seeded rounds
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is microseconds per round over K back-to-back
+rounds, bracketed by device synchronisation (lower is better).  Extra fields:
+per-launch kernel time from HIP events (the roofline's denominator), a
+cold-cache leg (L2 and the 256 MB Infinity Cache flushed before each round),
+gamma = 16 at the same vocabulary, the step-wise torch loop (the pages'
+default walk: gamma x {GEMV, add, argmax}) and the CPU oracle on a bounded
+sample of the same rounds.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(V, B, gamma, want_logits=False, r=256):
+    """Bytes one round must move at minimum: W2 once, base, the gathered W1
+    rows, tokens, anchors, temperatures and uniforms (+ logits if written)."""
+    n = V * r * 2 + B * gamma * V * 2 + B * gamma * r * 2 + B * gamma * 4 + B * 8 + B * gamma * 4
+    if want_logits:
+        n += B * gamma * V * 2
+    return n
+
+
+def make_rounds(index, n, B, gamma, V, temps):
+    import workloads
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        return list(ex.map(lambda r: workloads.round_inputs(index, r, B=B, gamma=gamma, V=V,
+                                                            temps=temps), range(n)))
+
+
+def to_device(rounds, torch, dev):
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+    base = torch.stack([bf(r["base"]) for r in rounds]).to(dev)
+    anchor = torch.stack([torch.from_numpy(r["anchor"]) for r in rounds]).to(dev)
+    T = torch.stack([torch.from_numpy(r["T"]) for r in rounds]).to(dev)
+    uni = torch.stack([torch.from_numpy(r["uniforms"]) for r in rounds]).to(dev)
+    return base, anchor, T, uni
+
+
+def time_walk(torch, walker, W1d, W2d, dev_rounds, K, W, per_launch=False, flush=None):
+    base, anchor, T, uni = dev_rounds
+    n = base.shape[0]
+    B, gamma = base.shape[1], base.shape[2]
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=W1d.device)
+    for i in range(W):
+        j = i % n
+        walker.walk(W1d, W2d, base[j], anchor[j], T[j], uni[j], tokens=tokens)
+    torch.cuda.synchronize()
+    if not per_launch and flush is None:
+        t0 = time.perf_counter()
+        for i in range(K):
+            j = (W + i) % n
+            walker.walk(W1d, W2d, base[j], anchor[j], T[j], uni[j], tokens=tokens)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K * 1e6, None
+    durs = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        j = (W + i) % n
+        if flush is not None:
+            flush()
+        ev[i][0].record()
+        walker.walk(W1d, W2d, base[j], anchor[j], T[j], uni[j], tokens=tokens)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return statistics.fmean(durs), durs
+
+
+def stepwise_torch(torch, W1d, W2d, dev_rounds, K):
+    """The pages' default walk as separate library ops per step (re-reads W2 every step)."""
+    base, anchor, T, uni = dev_rounds
+    n, B, gamma, V = base.shape
+
+    def one(j):
+        prev = anchor[j].long()
+        out = []
+        for k in range(gamma):
+            u = W1d[prev]                                  # [B, 256]
+            bias = torch.matmul(u, W2d.t())                # bf16 out: rounded once
+            logit = base[j][:, k] + bias                   # bf16 add: rounded again
+            prev = torch.argmax(logit, dim=-1)
+            out.append(prev)
+        return out
+
+    for j in range(3):
+        one(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        one(i % n)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / K * 1e6
+
+
+def cpu_baseline(index, B, gamma, V, W1, W2, budget_s=15.0):
+    import oracle
+    import workloads
+    times = []
+    t_start = time.perf_counter()
+    r = 0
+    while True:
+        inp = workloads.round_inputs(index, r, B=B, gamma=gamma, V=V)
+        t0 = time.perf_counter()
+        oracle.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2,
+                    want_logits=False)
+        times.append(time.perf_counter() - t0)
+        r += 1
+        if time.perf_counter() - t_start > budget_s or r >= 1000:
+            break
+    return {"value": statistics.median(times) * 1e6, "unit": "us/round", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{r} rounds of the same workload (seeded rounds 0..{r - 1}), "
+                      f"median wall time per round, binary64 C oracle with OpenMP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--B", type=int, default=None)
+    ap.add_argument("--gamma", type=int, default=None)
+    ap.add_argument("--rounds", type=int, default=1000, help="distinct seeded rounds resident in HBM")
+    ap.add_argument("--cold-rounds", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the timed walk (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import serial_draft_head_amd as dsw
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    B = args.B if args.B is not None else wl.batches[0]
+    gamma = args.gamma if args.gamma is not None else wl.gamma
+    V = wl.V
+    dev = torch.device("cuda", 0)
+    log(f"workload {wl.name} V={V} B={B} gamma={gamma}: generating inputs")
+    W1, W2 = workloads.weights(args.workload)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W1d, W2d = bf(W1), bf(W2)
+    n_rounds = min(args.rounds, args.steps + args.warmup)
+    rounds = make_rounds(args.workload, n_rounds, B, gamma, V, wl.temps)
+    dev_rounds = to_device(rounds, torch, dev)
+    del rounds
+    walker = dsw.Walker(V, gamma_max=max(gamma, 16), B_max=B)
+    plan = walker.query_plan(B).as_dict()
+    log("plan", plan)
+
+    us_round, _ = time_walk(torch, walker, W1d, W2d, dev_rounds, args.steps, args.warmup)
+    st = walker.status()
+    if st != 0:
+        raise SystemExit(f"device status {st} during the timed walk")
+    log(f"warm: {us_round:.2f} us/round")
+    result = {
+        "metric": "Markov-walk µs/round (γ=7,16; bs=1) and HBM bytes/round vs streaming roofline",
+        "value": round(us_round, 3), "unit": "us/round", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us_round / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "V": V, "r": 256, "gamma": gamma, "B": B,
+                   "temps": wl.temps, "rounds_resident": n_rounds, "w2": "bf16"},
+    }
+    if args.no_extras:
+        print(json.dumps(result), flush=True)
+        return
+
+    # per-launch kernel time (HIP events on the launch stream)
+    k_launch = min(args.steps, 300)
+    mean_launch, durs = time_walk(torch, walker, W1d, W2d, dev_rounds, k_launch, 10, per_launch=True)
+    abytes = algorithmic_bytes(V, B, gamma)
+    achieved = abytes / (mean_launch * 1e-6) / 1e9
+    w2_bytes = V * 256 * 2
+    stepwise_bound = gamma * w2_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                          "traffic": None,
+                          "kernel": "walk_persistent", "algorithmic_bytes_per_launch": abytes,
+                          "launch_us_mean": round(mean_launch, 3),
+                          "launch_us_median": round(statistics.median(durs), 3)}
+    result["stepwise_hbm_bound_us"] = round(stepwise_bound, 3)
+    result["frac_of_stepwise_bound"] = round(us_round / stepwise_bound, 4)
+    result["one_w2_read_floor_us"] = round(w2_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3)
+    log(f"per launch {mean_launch:.2f} us, {achieved:.0f} GB/s algorithmic")
+
+    # cold: flush L2 + Infinity Cache before each round (outside the events)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        scratch.zero_()
+    kc = min(args.cold_rounds, n_rounds)
+    cold_mean, cold = time_walk(torch, walker, W1d, W2d, dev_rounds, kc, 2, flush=flush)
+    cold.sort()
+    result["cold_us_per_round"] = {"median": round(statistics.median(cold), 3),
+                                   "p10": round(cold[len(cold) // 10], 3),
+                                   "p90": round(cold[(9 * len(cold)) // 10], 3), "rounds": kc}
+    del scratch
+    log("cold", result["cold_us_per_round"])
+
+    # gamma = 16 at the same vocabulary (the metric's second walk length)
+    if gamma != 16 and V == 151_936:
+        r16 = make_rounds(2, 100, 1, 16, V, "greedy")
+        d16 = to_device(r16, torch, dev)
+        us16, _ = time_walk(torch, walker, W1d, W2d, d16, 300, 20)
+        result["gamma16_us_per_round"] = round(us16, 3)
+        result["gamma16_stepwise_hbm_bound_us"] = round(16 * w2_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 3)
+        log(f"gamma16: {us16:.2f} us/round")
+        del d16
+
+    # the step-wise loop of library ops (re-reads W2 every step)
+    if B <= 16:
+        sw = stepwise_torch(torch, W1d, W2d, dev_rounds, 100)
+        result["stepwise_torch_us_per_round"] = round(sw, 3)
+        result["stepwise_torch_w2_gbs"] = round(gamma * w2_bytes / (sw * 1e-6) / 1e9, 1)
+        log(f"step-wise torch: {sw:.2f} us/round")
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(args.workload, B, gamma, V, W1, W2)
+    walker.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * dsw.h -- C ABI of the MI355X (gfx950) serial Markov draft walk library.
+ *
+ * The operation (from "Keeping the Draft Walk on Chip: One Launch for DSpark's
+ * Markov Head", tie-pilot-qxw.github.io, section "The serial part of a
+ * parallel drafter"): for each request b and k = 0 .. gamma-1
+ *
+ *     u        = W1[prev]                                  (r = 256)
+ *     logit_k  = bf16( base[b,k,:] + bf16( W2 . u ) )       over the vocabulary V
+ *     tok_k    = argmax(logit_k)              if T[b] == 0 (lowest id on ties)
+ *              = inverse-CDF sample of softmax(logit_k / T[b]) with uniforms[b,k]
+ *     prev     = tok_k                        (prev starts at anchor[b])
+ *
+ * The double rounding (the GEMV result rounded to bf16 before the add, then
+ * the sum rounded again) is the one of SGLang's default walk described in the
+ * same section and in section "B200: the bf16 table fits on chip".  Ties go to
+ * the smallest token id (section "The idea: make the walk resident").  The
+ * sampler is the inverse CDF of vLLM PR #64442 ("fused Markov sampling",
+ * section "Details"), driven by caller-supplied uniforms.  Temperatures are
+ * read per request on the device, so greedy, sampled and mixed batches share
+ * one launch (section "The idea: make the walk resident").
+ *
+ * All tensors are row-major and contiguous.  bf16 values are IEEE bfloat16
+ * bit patterns (uint16_t).  Unless stated otherwise, pointers passed to
+ * dsw_walk are DEVICE pointers on the handle's device, owned by the caller;
+ * the library never frees or retains them past the call.
+ *
+ * Errors: every function returns 0 on success or a negative DSW_ERR_* code.
+ * Device-side faults (a cross-workgroup wait that exceeded its bound, a token
+ * id out of range) cannot be returned by the asynchronous dsw_walk; they latch
+ * into a status word that dsw_status() reads.  After any error the contents of
+ * tokens and logits are unspecified.
+ */
+#ifndef DSW_H
+#define DSW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- codes ------------------------------------------------------------- */
+#define DSW_OK 0
+#define DSW_ERR_NULL -1          /* a required pointer is NULL                       */
+#define DSW_ERR_BATCH -2         /* B < 0 or B > B_max                               */
+#define DSW_ERR_GAMMA -3         /* gamma < 0 or gamma > gamma_max                   */
+#define DSW_ERR_RANK -4          /* r != 256 (the only rank the kernels support)     */
+#define DSW_ERR_DTYPE -5         /* unknown W2 dtype, or scale given/missing wrongly */
+#define DSW_ERR_VOCAB -6         /* V < 1 or too large for the device               */
+#define DSW_ERR_LAUNCH -7        /* the persistent grid cannot be co-resident       */
+#define DSW_ERR_HIP -8           /* a HIP runtime call failed                        */
+#define DSW_ERR_DEVICE -9        /* no such device                                   */
+#define DSW_ERR_PLAN -10         /* no execution plan fits the request              */
+#define DSW_ERR_ARG -11          /* another invalid argument                         */
+/* latched by the device, reported by dsw_status() */
+#define DSW_ERR_DEV_TIMEOUT -20  /* a cross-workgroup wait exceeded its bound        */
+#define DSW_ERR_DEV_TOKEN -21    /* an anchor or token id was outside [0, V)        */
+#define DSW_ERR_DEV_UNIFORMS -22 /* T > 0 for a request but uniforms was NULL       */
+
+/* W2 storage */
+#define DSW_BF16 0               /* W2 bf16 [V][r]                                   */
+#define DSW_INT8 1               /* W2 int8 [V][r] + one fp32 scale per row [V]      */
+
+/* execution paths chosen by the planner */
+#define DSW_PATH_RESIDENT 0      /* every row on chip (VGPR + LDS), one launch       */
+#define DSW_PATH_PARTIAL 1       /* rows on chip + rows streamed every step          */
+
+/* dsw_create flags */
+#define DSW_FLAG_FORCE_STREAM 1u /* keep nothing on chip: stream W2 every step      */
+
+/* Device description the planner works from.  dsw_device_info() fills it
+ * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
+typedef struct dsw_devinfo {
+    int cu_count;            /* compute units                                   */
+    int simds_per_cu;        /* 4 on CDNA                                       */
+    int wave_size;           /* 64                                              */
+    int vgprs_per_simd_lane; /* unified VGPR+AGPR file per SIMD lane (512)     */
+    int lds_bytes_per_cu;    /* local data share per CU                         */
+    int max_lds_per_block;   /* largest LDS allocation for one workgroup        */
+    int xcd_count;           /* accelerator complex dies                        */
+    int clock_khz;           /* peak engine clock                               */
+    long long l2_bytes;      /* L2 per XCD                                      */
+    long long hbm_bytes;     /* device memory                                   */
+    int cooperative;         /* cooperative launch supported                    */
+} dsw_devinfo;
+
+/* What the planner decided for one (V, r, gamma, B, dtype). */
+typedef struct dsw_plan_info {
+    int path;                /* DSW_PATH_*                                      */
+    int grid;                /* workgroups: one per CU                          */
+    int block;               /* threads per workgroup                           */
+    int rows_per_wg;         /* vocabulary rows owned by each workgroup         */
+    int reg_slots;           /* 256-row groups per workgroup held in VGPRs      */
+    int reg_rows;            /* rows per workgroup held in VGPRs                */
+    int lds_rows;            /* rows per workgroup held in LDS                  */
+    int stream_rows;         /* rows per workgroup re-read every step           */
+    int batch_tile;          /* compiled request capacity of the chosen kernel  */
+    int lds_bytes;           /* dynamic LDS per workgroup                       */
+    long long onchip_bytes;  /* W2 bytes held on chip over the whole grid      */
+    long long stream_bytes;  /* W2 bytes re-read per step over the whole grid  */
+    long long workspace_bytes; /* device workspace owned by the handle         */
+} dsw_plan_info;
+
+typedef struct dsw_handle* dsw_handle_t;
+
+/* Fill *out from the HIP runtime for `device`.  Host only; no kernel runs. */
+int dsw_device_info(int device, dsw_devinfo* out);
+
+/* Pure host function: the plan for a walk of (V, r, gamma, B, w2_dtype) on
+ * the described device.  Rows are split in contiguous shards of
+ * ceil(V / grid) rows, one per workgroup, as the pages' resident kernel gives
+ * each CTA one slice of vocabulary rows (section "The idea: make the walk
+ * resident"); each shard is placed in VGPRs first, then LDS, and whatever is
+ * left is streamed every step (section "V = 248,320: 62% on chip, the rest
+ * streamed").  flags: DSW_FLAG_FORCE_STREAM.  Returns DSW_ERR_* on invalid
+ * sizes or when no plan fits. */
+int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int w2_dtype,
+                     unsigned flags, dsw_plan_info* out);
+
+/* Create a handle for walks on `device` with vocabulary V, rank r (must be
+ * 256), at most gamma_max steps and B_max requests per call, and W2 stored
+ * as w2_dtype.  Allocates and zeroes the device workspace (cross-workgroup
+ * mailboxes, arrival counters, a round counter and a status word); the handle
+ * owns it.  The calling thread's current device is left unchanged. */
+int dsw_create(dsw_handle_t* h, int device, int V, int r, int gamma_max, int B_max,
+               int w2_dtype, unsigned flags);
+
+/* One round of the walk: one persistent launch on `stream` (a hipStream_t;
+ * NULL = the null stream).  Asynchronous: it never waits for the device and
+ * allocates nothing.  Argument layout (all device pointers):
+ *   W1        bf16 [V][r]
+ *   W2        bf16 [V][r] (DSW_BF16) or int8 [V][r] (DSW_INT8)
+ *   w2_scale  f32 [V] for DSW_INT8, must be NULL for DSW_BF16
+ *   base      bf16 [B][gamma][V]   base logits of the drafter's parallel pass
+ *   anchor    int32 [B]            last accepted token of each request
+ *   T         f32 [B]              temperature; exactly 0 = greedy
+ *   uniforms  f32 [B][gamma] in [0,1), one per request and step; may be NULL
+ *             when every T is 0
+ *   tokens    int32 [B][gamma] out: tokens[b][0] follows the anchor
+ *   logits    bf16 [B][gamma][V] out, or NULL: the exact values the tokens
+ *             were selected from (section "The idea: make the walk resident":
+ *             the same bits are handed to the verifier)
+ * Rows of base/logits beyond V and entries beyond [B][gamma] are never
+ * touched.  One handle serves one stream at a time: calls on one handle must
+ * not overlap on the device.  B == 0 or gamma == 0 returns 0 and launches
+ * nothing. */
+int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale,
+             const void* base, const int32_t* anchor, const float* T, const float* uniforms,
+             int32_t* tokens, void* logits, int B, int gamma, void* stream);
+
+/* Wait for the handle's device, then return and clear the status word that
+ * the device latches (0 or a DSW_ERR_DEV_* code).  After a device error the
+ * workspace is re-zeroed so that the next call starts clean. */
+int dsw_status(dsw_handle_t h);
+
+/* The plan dsw_walk uses for batch size B on this handle. */
+int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out);
+
+/* Free the workspace and the handle.  NULL is accepted. */
+int dsw_destroy(dsw_handle_t h);
+
+/* Static description of a DSW_* code. */
+const char* dsw_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSW_H */

@@ -1,0 +1,222 @@
+"""MI355X-native serial Markov draft walk (DSpark's head): Python binding.
+
+This module only marshals arguments into the C ABI of ``include/dsw.h``
+(``libdsw.so``, built in-tree by ``serial_draft_head_amd.build``).  Every step
+of the walk runs in the library's HIP kernels; PyTorch supplies device memory
+and the stream.  Importing works without a GPU (the planner and the error
+strings are host code); calling ``walk`` needs the built library and a GPU,
+and raises if either is missing -- there is no fallback.
+
+The walk (from "Keeping the Draft Walk on Chip", tie-pilot-qxw.github.io,
+section "The serial part of a parallel drafter"): for k < gamma,
+``u = W1[prev]``, ``logit = bf16(base[:, k] + bf16(W2 @ u))``, then the
+lowest-index argmax (T == 0) or an inverse-CDF sample of ``softmax(logit / T)``
+driven by ``uniforms[:, k]``, and ``prev = tok``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsw.so")
+
+OK = 0
+ERR = {
+    -1: "DSW_ERR_NULL", -2: "DSW_ERR_BATCH", -3: "DSW_ERR_GAMMA", -4: "DSW_ERR_RANK",
+    -5: "DSW_ERR_DTYPE", -6: "DSW_ERR_VOCAB", -7: "DSW_ERR_LAUNCH", -8: "DSW_ERR_HIP",
+    -9: "DSW_ERR_DEVICE", -10: "DSW_ERR_PLAN", -11: "DSW_ERR_ARG",
+    -20: "DSW_ERR_DEV_TIMEOUT", -21: "DSW_ERR_DEV_TOKEN", -22: "DSW_ERR_DEV_UNIFORMS",
+}
+BF16, INT8 = 0, 1
+PATH_RESIDENT, PATH_PARTIAL = 0, 1
+FLAG_FORCE_STREAM = 1
+RANK = 256
+
+
+class DswError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERR.get(code, code)} ({strerror(code)})")
+
+
+class DevInfo(ctypes.Structure):
+    _fields_ = [("cu_count", ctypes.c_int), ("simds_per_cu", ctypes.c_int),
+                ("wave_size", ctypes.c_int), ("vgprs_per_simd_lane", ctypes.c_int),
+                ("lds_bytes_per_cu", ctypes.c_int), ("max_lds_per_block", ctypes.c_int),
+                ("xcd_count", ctypes.c_int), ("clock_khz", ctypes.c_int),
+                ("l2_bytes", ctypes.c_longlong), ("hbm_bytes", ctypes.c_longlong),
+                ("cooperative", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("grid", ctypes.c_int), ("block", ctypes.c_int),
+                ("rows_per_wg", ctypes.c_int), ("reg_slots", ctypes.c_int),
+                ("reg_rows", ctypes.c_int), ("lds_rows", ctypes.c_int),
+                ("stream_rows", ctypes.c_int), ("batch_tile", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int), ("onchip_bytes", ctypes.c_longlong),
+                ("stream_bytes", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """The loaded libdsw.so.  Raises if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
+        L.dsw_device_info.argtypes = [I, ctypes.POINTER(DevInfo)]
+        L.dsw_plan_compute.argtypes = [ctypes.POINTER(DevInfo), I, I, I, I, I, U,
+                                       ctypes.POINTER(PlanInfo)]
+        L.dsw_create.argtypes = [ctypes.POINTER(P), I, I, I, I, I, I, U]
+        L.dsw_walk.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, P]
+        L.dsw_status.argtypes = [P]
+        L.dsw_query_plan.argtypes = [P, I, ctypes.POINTER(PlanInfo)]
+        L.dsw_destroy.argtypes = [P]
+        L.dsw_strerror.argtypes = [I]
+        L.dsw_strerror.restype = ctypes.c_char_p
+        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_status",
+                  "dsw_query_plan", "dsw_destroy"):
+            getattr(L, f).restype = I
+        _lib = L
+        return L
+
+
+def strerror(code: int) -> str:
+    return lib().dsw_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != OK:
+        raise DswError(code, where)
+
+
+def device_info(device: int = 0) -> DevInfo:
+    d = DevInfo()
+    _check(lib().dsw_device_info(int(device), ctypes.byref(d)), "dsw_device_info")
+    return d
+
+
+def plan(dev: DevInfo, V: int, gamma: int, B: int, w2_dtype: int = BF16, flags: int = 0,
+         r: int = RANK) -> PlanInfo:
+    """The planner's decision for an (invented or real) device.  Host only."""
+    out = PlanInfo()
+    _check(lib().dsw_plan_compute(ctypes.byref(dev), int(V), int(r), int(gamma), int(B),
+                                  int(w2_dtype), int(flags), ctypes.byref(out)),
+           "dsw_plan_compute")
+    return out
+
+
+def _stream_handle(torch, device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+class Walker:
+    """A handle of the library: workspace for walks of vocabulary V with at
+    most gamma_max steps and B_max requests on one device."""
+
+    def __init__(self, V: int, gamma_max: int, B_max: int, w2_dtype: int = BF16,
+                 device: int = 0, flags: int = 0, r: int = RANK):
+        self.V, self.gamma_max, self.B_max = int(V), int(gamma_max), int(B_max)
+        self.w2_dtype, self.device, self.flags, self.r = int(w2_dtype), int(device), int(flags), r
+        h = ctypes.c_void_p()
+        _check(lib().dsw_create(ctypes.byref(h), self.device, self.V, int(r), self.gamma_max,
+                                self.B_max, self.w2_dtype, int(flags)), "dsw_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().dsw_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def query_plan(self, B: int) -> PlanInfo:
+        out = PlanInfo()
+        _check(lib().dsw_query_plan(self._h, int(B), ctypes.byref(out)), "dsw_query_plan")
+        return out
+
+    def status(self) -> int:
+        """Wait for the device; return (and clear) the latched device status code."""
+        return lib().dsw_status(self._h)
+
+    def walk(self, W1, W2, base, anchor, T, uniforms=None, w2_scale=None, tokens=None,
+             logits=None, want_logits=False, stream=None):
+        """One round.  Tensors live on this handle's device:
+        W1 bf16 [V,256]; W2 bf16 [V,256] (or int8 + w2_scale f32 [V]);
+        base bf16 [B,gamma,V]; anchor int32 [B]; T float32 [B] (0 = greedy);
+        uniforms float32 [B,gamma] or None when every T is 0.
+        Returns (tokens int32 [B,gamma], logits bf16 [B,gamma,V] or None)."""
+        import torch
+        dev = torch.device("cuda", self.device)
+        B, gamma, V = (int(x) for x in base.shape)
+        need = [(W1, torch.bfloat16, (self.V, self.r), "W1"),
+                (base, torch.bfloat16, (B, gamma, self.V), "base"),
+                (anchor, torch.int32, (B,), "anchor"), (T, torch.float32, (B,), "T")]
+        if self.w2_dtype == BF16:
+            need.append((W2, torch.bfloat16, (self.V, self.r), "W2"))
+        else:
+            need.append((W2, torch.int8, (self.V, self.r), "W2"))
+            need.append((w2_scale, torch.float32, (self.V,), "w2_scale"))
+        if uniforms is not None:
+            need.append((uniforms, torch.float32, (B, gamma), "uniforms"))
+        if tokens is None:
+            tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        need.append((tokens, torch.int32, (B, gamma), "tokens"))
+        if logits is None and want_logits:
+            logits = torch.empty((B, gamma, self.V), dtype=torch.bfloat16, device=dev)
+        if logits is not None:
+            need.append((logits, torch.bfloat16, (B, gamma, self.V), "logits"))
+        for t, dt, shape, name in need:
+            if t is None:
+                raise ValueError(f"{name} is required")
+            if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"{name}: want {dt} {shape} contiguous on {dev}, got "
+                                 f"{t.dtype} {tuple(t.shape)} on {t.device}")
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        rc = lib().dsw_walk(self._h, ptr(W1), ptr(W2), ptr(w2_scale), ptr(base), ptr(anchor),
+                            ptr(T), ptr(uniforms), ptr(tokens), ptr(logits), B, gamma,
+                            _stream_handle(torch, dev, stream))
+        _check(rc, "dsw_walk")
+        return tokens, logits
+
+
+_walkers = {}
+
+
+def walk(W1, W2, base, anchor, T, uniforms=None, w2_scale=None, want_logits=False, stream=None):
+    """Functional form: one round with a cached handle per (device, V, dtype)."""
+    import torch
+    B, gamma, V = (int(x) for x in base.shape)
+    device = W1.device.index if W1.device.index is not None else torch.cuda.current_device()
+    dtype = INT8 if W2.dtype == torch.int8 else BF16
+    key = (device, V, dtype)
+    w = _walkers.get(key)
+    if w is None or w.gamma_max < gamma or w.B_max < B:
+        if w is not None:
+            w.close()
+        w = Walker(V, max(gamma, 16), max(B, 16), dtype, device)
+        _walkers[key] = w
+    return w.walk(W1, W2, base, anchor, T, uniforms, w2_scale, want_logits=want_logits,
+                  stream=stream)

@@ -1,0 +1,242 @@
+// api.cpp -- the C ABI of include/dsw.h: device probing, handle and workspace
+// management, argument checks and the one persistent launch per round.
+#include <hip/hip_runtime_api.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+
+#include "../../include/dsw.h"
+#include "walk_params.h"
+
+extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile);
+
+struct dsw_handle {
+    int device;
+    int V, r, gamma_max, B_max, dtype;
+    unsigned flags;
+    dsw_devinfo dev;
+    char* ws_mem;
+    size_t ws_bytes;
+    dsw::Workspace ws;
+    std::mutex mu;  // guards the per-kernel attribute cache below
+    const void* lds_configured[4][17];
+    int lds_configured_bytes[4][17];
+};
+
+namespace {
+
+// Makes `device` current for the lifetime of the guard and restores the
+// caller's device afterwards.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int device) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        ok = hipSetDevice(device) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+int clear_workspace(dsw_handle* h) {
+    if (hipMemset(h->ws_mem, 0, h->ws_bytes) != hipSuccess) return DSW_ERR_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return DSW_ERR_HIP;
+    return DSW_OK;
+}
+
+constexpr unsigned kSpinLimit = 1u << 20;  // polls; each costs well over 100 ns
+
+}  // namespace
+
+extern "C" int dsw_device_info(int device, dsw_devinfo* out) {
+    if (!out) return DSW_ERR_NULL;
+    memset(out, 0, sizeof(*out));
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return DSW_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return DSW_ERR_HIP;
+    out->cu_count = prop.multiProcessorCount;
+    out->simds_per_cu = 4;
+    out->wave_size = prop.warpSize;
+    out->vgprs_per_simd_lane = 512;
+    int lds_cu = 0, lds_blk = 0, coop = 0, clock = 0;
+    (void)hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device);
+    (void)hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
+    (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device);
+    (void)hipDeviceGetAttribute(&clock, hipDeviceAttributeClockRate, device);
+    out->lds_bytes_per_cu = lds_cu > 0 ? lds_cu : (int)prop.sharedMemPerBlock;
+    out->max_lds_per_block = lds_blk > 0 ? lds_blk : (int)prop.sharedMemPerBlock;
+    out->xcd_count = 8;
+    out->clock_khz = clock;
+    out->l2_bytes = prop.l2CacheSize;
+    out->hbm_bytes = (long long)prop.totalGlobalMem;
+    out->cooperative = coop;
+    return DSW_OK;
+}
+
+extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma_max, int B_max,
+                          int w2_dtype, unsigned flags) {
+    if (!out) return DSW_ERR_NULL;
+    *out = nullptr;
+    if (r != dsw::kRank) return DSW_ERR_RANK;
+    if (w2_dtype != DSW_BF16) return DSW_ERR_DTYPE;
+    if (V < 1) return DSW_ERR_VOCAB;
+    if (gamma_max < 1) return DSW_ERR_GAMMA;
+    if (B_max < 1 || B_max > 16) return DSW_ERR_BATCH;
+    dsw_devinfo dev;
+    int rc = dsw_device_info(device, &dev);
+    if (rc) return rc;
+    dsw_plan_info plan;
+    rc = dsw_plan_compute(&dev, V, r, gamma_max, B_max, w2_dtype, flags, &plan);
+    if (rc) return rc;
+    if (!dev.cooperative) return DSW_ERR_LAUNCH;
+
+    dsw_handle* h = new (std::nothrow) dsw_handle();
+    if (!h) return DSW_ERR_ARG;
+    h->device = device;
+    h->V = V;
+    h->r = r;
+    h->gamma_max = gamma_max;
+    h->B_max = B_max;
+    h->dtype = w2_dtype;
+    h->flags = flags;
+    h->dev = dev;
+    memset(h->lds_configured, 0, sizeof(h->lds_configured));
+    memset(h->lds_configured_bytes, 0, sizeof(h->lds_configured_bytes));
+
+    DeviceGuard g(device);
+    if (!g.ok) { delete h; return DSW_ERR_DEVICE; }
+    const dsw::WorkspaceLayout L = dsw::workspace_layout(gamma_max, B_max);
+    h->ws_bytes = L.total;
+    if (hipMalloc(&h->ws_mem, L.total) != hipSuccess) { delete h; return DSW_ERR_HIP; }
+    h->ws.keys = reinterpret_cast<unsigned long long*>(h->ws_mem + L.keys);
+    h->ws.counts = reinterpret_cast<unsigned*>(h->ws_mem + L.counts);
+    h->ws.partials = reinterpret_cast<unsigned long long*>(h->ws_mem + L.partials);
+    h->ws.tok_slots = reinterpret_cast<unsigned*>(h->ws_mem + L.tok_slots);
+    h->ws.round_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.round_ctr);
+    h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.status);
+    if (clear_workspace(h) != DSW_OK) {
+        (void)hipFree(h->ws_mem);
+        delete h;
+        return DSW_ERR_HIP;
+    }
+    *out = h;
+    return DSW_OK;
+}
+
+extern "C" int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out) {
+    if (!h || !out) return DSW_ERR_NULL;
+    if (B < 0 || B > h->B_max) return DSW_ERR_BATCH;
+    return dsw_plan_compute(&h->dev, h->V, h->r, h->gamma_max, B, h->dtype, h->flags, out);
+}
+
+extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale,
+                        const void* base, const int32_t* anchor, const float* T,
+                        const float* uniforms, int32_t* tokens, void* logits, int B, int gamma,
+                        void* stream) {
+    if (!h) return DSW_ERR_NULL;
+    if (B < 0 || B > h->B_max) return DSW_ERR_BATCH;
+    if (gamma < 0 || gamma > h->gamma_max) return DSW_ERR_GAMMA;
+    if (h->dtype == DSW_BF16 && w2_scale != nullptr) return DSW_ERR_DTYPE;
+    if (h->dtype == DSW_INT8 && w2_scale == nullptr) return DSW_ERR_DTYPE;
+    if (B == 0 || gamma == 0) return DSW_OK;
+    if (!W1 || !W2 || !base || !anchor || !T || !tokens) return DSW_ERR_NULL;
+
+    dsw_plan_info plan;
+    int rc = dsw_plan_compute(&h->dev, h->V, h->r, gamma, B, h->dtype, h->flags, &plan);
+    if (rc) return rc;
+    const void* fn = dsw_internal_walk_kernel(plan.reg_slots, plan.batch_tile);
+    if (!fn) return DSW_ERR_PLAN;
+
+    DeviceGuard g(h->device);
+    if (!g.ok) return DSW_ERR_DEVICE;
+    {
+        std::lock_guard<std::mutex> lock(h->mu);
+        int& done = h->lds_configured_bytes[plan.reg_slots][plan.batch_tile];
+        if (h->lds_configured[plan.reg_slots][plan.batch_tile] != fn || done < plan.lds_bytes) {
+            // Raises the dynamic-LDS ceiling where the runtime enforces one;
+            // a failure here surfaces as a launch error below.
+            (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
+            (void)hipGetLastError();
+            h->lds_configured[plan.reg_slots][plan.batch_tile] = fn;
+            done = plan.lds_bytes;
+        }
+    }
+
+    dsw::WalkParams p;
+    p.W1 = static_cast<const uint16_t*>(W1);
+    p.W2 = W2;
+    p.w2_scale = w2_scale;
+    p.base = static_cast<const uint16_t*>(base);
+    p.anchor = anchor;
+    p.T = T;
+    p.uniforms = uniforms;
+    p.tokens = tokens;
+    p.logits = static_cast<uint16_t*>(logits);
+    p.ws = h->ws;
+    p.V = h->V;
+    p.B = B;
+    p.gamma = gamma;
+    p.gamma_max = h->gamma_max;
+    p.B_max = h->B_max;
+    p.rows_per_wg = plan.rows_per_wg;
+    p.lds_rows = plan.lds_rows;
+    p.spin_limit = kSpinLimit;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(plan.grid), dim3(plan.block), args,
+                                              (unsigned)plan.lds_bytes,
+                                              static_cast<hipStream_t>(stream));
+    if (e == hipErrorCooperativeLaunchTooLarge) return DSW_ERR_LAUNCH;
+    return e == hipSuccess ? DSW_OK : DSW_ERR_HIP;
+}
+
+extern "C" int dsw_status(dsw_handle_t h) {
+    if (!h) return DSW_ERR_NULL;
+    DeviceGuard g(h->device);
+    if (!g.ok) return DSW_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return DSW_ERR_HIP;
+    unsigned st = 0;
+    if (hipMemcpy(&st, h->ws.status, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) return DSW_ERR_HIP;
+    if (st == 0) return DSW_OK;
+    // the parity state may be half-written after a failed round: start clean
+    if (clear_workspace(h) != DSW_OK) return DSW_ERR_HIP;
+    if (st & dsw::kStatusTimeout) return DSW_ERR_DEV_TIMEOUT;
+    if (st & dsw::kStatusToken) return DSW_ERR_DEV_TOKEN;
+    return DSW_ERR_DEV_UNIFORMS;
+}
+
+extern "C" int dsw_destroy(dsw_handle_t h) {
+    if (!h) return DSW_OK;
+    {
+        DeviceGuard g(h->device);
+        if (h->ws_mem) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(h->ws_mem);
+        }
+    }
+    delete h;
+    return DSW_OK;
+}
+
+extern "C" const char* dsw_strerror(int code) {
+    switch (code) {
+        case DSW_OK: return "ok";
+        case DSW_ERR_NULL: return "a required pointer is NULL";
+        case DSW_ERR_BATCH: return "batch size out of range";
+        case DSW_ERR_GAMMA: return "walk length out of range";
+        case DSW_ERR_RANK: return "rank must be 256";
+        case DSW_ERR_DTYPE: return "unsupported W2 dtype or scale mismatch";
+        case DSW_ERR_VOCAB: return "vocabulary size out of range for this device";
+        case DSW_ERR_LAUNCH: return "the persistent grid cannot be co-resident";
+        case DSW_ERR_HIP: return "HIP runtime error";
+        case DSW_ERR_DEVICE: return "no such device";
+        case DSW_ERR_PLAN: return "no execution plan fits";
+        case DSW_ERR_ARG: return "invalid argument";
+        case DSW_ERR_DEV_TIMEOUT: return "device: a cross-workgroup wait exceeded its bound";
+        case DSW_ERR_DEV_TOKEN: return "device: token id outside [0, V)";
+        case DSW_ERR_DEV_UNIFORMS: return "device: T > 0 but uniforms is NULL";
+        default: return "unknown error";
+    }
+}

@@ -1,0 +1,119 @@
+"""Teacher-forced parity of a GPU round against the CPU oracle.
+
+Rules (the walk is exact by definition; the GPU only sums in fp32 in another
+order):
+  * logits: each GPU logit lies in [bf16(base + bf16(acc - E)), bf16(base + bf16(acc + E))]
+    where acc is the exact dot product and E = g_r * sum_j |w_j u_j| bounds
+    any fp32 summation of r = 256 terms (g_r = r 2^-24 / (1 - r 2^-24)); and it
+    is within one bf16 ulp of the oracle's logit (the ulp taken at the largest
+    of |oracle logit|, |GPU logit| and |bias|, so that cancellation in
+    base + bias cannot fake a miss), except where that fp32 interval itself
+    reaches two ulps: when the fp32 sum straddles a midpoint of the first
+    rounding and the second rounding then meets a tie, double rounding turns
+    one bias ulp into two logit ulps.  There 2 ulps are allowed and counted;
+  * greedy tokens: the GPU token is always the lowest-index argmax of the
+    GPU's own logits; it equals the oracle's token wherever the oracle's
+    top-two gap exceeds 2 ulps, and elsewhere its oracle logit is within
+    2 ulps of the oracle's maximum;
+  * sampled tokens: from the GPU's own logits in binary64, C_{t-1} - d <= u Z < C_t + d
+    with d = 1e-5 Z, and the token equals the oracle's draw on those logits
+    wherever u Z is farther than d from every boundary.
+Step k uses prev = the GPU's token k-1 (teacher forcing), so every step is
+judged on its own.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+R = 256
+GAMMA_R = R * 2.0 ** -24 / (1 - R * 2.0 ** -24)
+SAMPLE_TOL = 1e-5
+
+
+def bf16_ulp(x):
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+class Weights:
+    """f64 views of the bf16 (or int8) tables, computed once per test."""
+
+    def __init__(self, W1_bits, W2_bits=None, Q=None, scale=None):
+        self.W1_bits, self.W2_bits, self.Q, self.scale = W1_bits, W2_bits, Q, scale
+        self.W1 = oracle.bf16_bits_to_f64(W1_bits)
+        if W2_bits is not None:
+            self.W2 = oracle.bf16_bits_to_f64(W2_bits)
+        else:
+            self.W2 = Q.astype(np.float64) * scale.astype(np.float64)[:, None]
+        self.W2abs = np.abs(self.W2)
+
+
+def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, steps=None):
+    """Assert the parity rules for one round; return a small report dict."""
+    B, gamma, V = base.shape
+    or_tok, or_lg = oracle.walk(w.W1_bits, base, anchor, T, uniforms, W2_bits=w.W2_bits, Q=w.Q,
+                                scale=w.scale, forced=gpu_tokens)
+    rep = {"steps": 0, "exact_logits": 0, "logits": 0, "near_ties": 0, "token_match": 0,
+           "sampled": 0, "sampled_exact_checked": 0}
+    for b in range(B):
+        for k in range(gamma) if steps is None else steps:
+            prev = int(anchor[b]) if k == 0 else int(gpu_tokens[b, k - 1])
+            u = w.W1[prev]
+            acc = w.W2 @ u
+            E = GAMMA_R * (w.W2abs @ np.abs(u))
+            bias = oracle.rne_bf16(acc)[0]
+            lo = oracle.rne_bf16(acc - E)[0]
+            hi = oracle.rne_bf16(acc + E)[0]
+            bse = oracle.bf16_bits_to_f64(base[b, k])
+            Llo = oracle.rne_bf16(bse + lo)[0]
+            Lhi = oracle.rne_bf16(bse + hi)[0]
+            g = oracle.bf16_bits_to_f64(gpu_logits[b, k])
+            o = oracle.bf16_bits_to_f64(or_lg[b, k])
+            bad = np.nonzero((g < Llo) | (g > Lhi))[0]
+            assert bad.size == 0, f"b={b} k={k}: logits outside the fp32 bound at {bad[:5]} " \
+                                  f"gpu={g[bad[:5]]} oracle={o[bad[:5]]}"
+            ulp = bf16_ulp(np.maximum.reduce([np.abs(o), np.abs(g), np.abs(bias)]))
+            diff = np.abs(g - o)
+            reach = np.maximum(Lhi - o, o - Llo)          # what fp32 accumulation can reach
+            far = np.nonzero((diff > ulp) & ~((reach > ulp) & (diff <= 2 * ulp)))[0]
+            assert far.size == 0, f"b={b} k={k}: logits beyond 1 ulp at {far[:5]} " \
+                                  f"gpu={g[far[:5]]} oracle={o[far[:5]]}"
+            rep["two_ulp_double_rounding"] = rep.get("two_ulp_double_rounding", 0) + \
+                int(np.count_nonzero(diff > ulp))
+            rep["steps"] += 1
+            rep["logits"] += V
+            rep["exact_logits"] += int(np.count_nonzero(g == o))
+            tok = int(gpu_tokens[b, k])
+            assert 0 <= tok < V
+            if T[b] == 0:
+                assert tok == int(np.argmax(g)), f"b={b} k={k}: token {tok} is not the first argmax of the GPU's own logits"
+                top = int(np.argmax(o))
+                omax = o[top]
+                rest = np.delete(o, top)
+                gap = omax - (rest.max() if rest.size else -np.inf)
+                if gap > 2 * bf16_ulp(omax):
+                    assert tok == int(or_tok[b, k]), f"b={b} k={k}: token {tok} vs oracle {or_tok[b, k]}"
+                    rep["token_match"] += 1
+                else:
+                    rep["near_ties"] += 1
+                    assert o[tok] >= omax - 2 * bf16_ulp(omax)
+                    rep["token_match"] += int(tok == int(or_tok[b, k]))
+            else:
+                rep["sampled"] += 1
+                Tb = float(np.float32(T[b]))
+                M = g.max()
+                wts = np.exp((g - M) / Tb)
+                C = np.cumsum(wts)
+                Z = C[-1]
+                t = float(np.float32(uniforms[b, k])) * Z
+                d = SAMPLE_TOL * Z
+                cprev = C[tok - 1] if tok > 0 else 0.0
+                assert cprev - d <= t < C[tok] + d, f"b={b} k={k}: sampled token {tok} does not hold u*Z"
+                margin = np.min(np.abs(C - t))
+                if margin > d:
+                    want = oracle.sample(gpu_logits[b, k], T[b], uniforms[b, k])
+                    assert tok == want, f"b={b} k={k}: sampled {tok} vs oracle {want}"
+                    rep["sampled_exact_checked"] += 1
+    return rep

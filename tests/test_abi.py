@@ -1,0 +1,149 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every function include/dsw.h declares, and the planner behaves on invented
+devices.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsw.h")
+
+
+@pytest.fixture(scope="module")
+def dsw():
+    import serial_draft_head_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libdsw.so is not built (run __graft_entry__.build())")
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsw_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("dsw_create", "dsw_walk", "dsw_status", "dsw_query_plan", "dsw_destroy",
+                 "dsw_strerror", "dsw_plan_compute", "dsw_device_info"):
+        assert want in names
+
+
+def test_library_exports_every_declared_function(dsw):
+    lib = ctypes.CDLL(dsw.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_error_strings(dsw):
+    for code in list(dsw.ERR) + [0]:
+        s = dsw.strerror(code)
+        assert s and s != "unknown error", code
+    assert dsw.strerror(12345) == "unknown error"
+
+
+def test_null_and_argument_errors_without_a_device(dsw):
+    L = dsw.lib()
+    assert L.dsw_walk(None, None, None, None, None, None, None, None, None, None, 1, 1, None) == -1
+    assert L.dsw_status(None) == -1
+    assert L.dsw_query_plan(None, 1, None) == -1
+    assert L.dsw_destroy(None) == 0
+    h = ctypes.c_void_p()
+    assert L.dsw_create(None, 0, 100, 256, 7, 1, 0, 0) == -1
+    assert L.dsw_create(ctypes.byref(h), 0, 100, 128, 7, 1, 0, 0) == -4      # rank
+    assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 7, 1, 7, 0) == -5      # dtype
+    assert L.dsw_create(ctypes.byref(h), 0, 0, 256, 7, 1, 0, 0) == -6        # vocab
+    assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 0, 1, 0, 0) == -3      # gamma
+    assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 7, 0, 0, 0) == -2      # batch
+
+
+def fake_device(dsw, cus=256, lds_cu=160 * 1024, lds_blk=160 * 1024):
+    d = dsw.DevInfo()
+    d.cu_count, d.simds_per_cu, d.wave_size, d.vgprs_per_simd_lane = cus, 4, 64, 512
+    d.lds_bytes_per_cu, d.max_lds_per_block, d.xcd_count = lds_cu, lds_blk, 8
+    d.clock_khz, d.l2_bytes, d.hbm_bytes, d.cooperative = 2_400_000, 4 << 20, 288 << 30, 1
+    return d
+
+
+def shards_cover(V, grid, R):
+    covered = 0
+    for c in range(grid):
+        lo, hi = c * R, min(V, c * R + R)
+        if hi > lo:
+            assert lo == covered
+            covered = hi
+    return covered == V
+
+
+@pytest.mark.parametrize("cus", [8, 80, 256])
+@pytest.mark.parametrize("V", [1, 12, 1000, 32_000, 65_537, 151_936, 248_320])
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_planner_partitions_rows_and_respects_capacity(dsw, cus, V, B):
+    d = fake_device(dsw, cus=cus)
+    rows = -(-V // min(cus, 256))
+    if rows > 4 * 256:
+        with pytest.raises(dsw.DswError) as e:
+            dsw.plan(d, V, 7, B)
+        assert e.value.code == -6
+        return
+    p = dsw.plan(d, V, 7, B)
+    assert p.grid == min(cus, 256) and p.block == 256
+    assert p.rows_per_wg == rows
+    assert shards_cover(V, p.grid, p.rows_per_wg)
+    assert p.reg_rows + p.lds_rows + p.stream_rows == p.rows_per_wg
+    assert p.reg_rows <= p.reg_slots * 256
+    cap = {1: 3, 4: 2, 16: 1}[p.batch_tile]
+    assert p.reg_slots <= cap
+    assert p.batch_tile >= B
+    assert p.lds_bytes >= p.lds_rows * 512
+    assert p.lds_bytes + 1024 + 672 * p.batch_tile <= d.max_lds_per_block
+    assert p.lds_bytes + 1024 + 672 * p.batch_tile > d.lds_bytes_per_cu // 2   # one WG per CU
+    assert p.onchip_bytes + p.stream_bytes == V * 512
+    assert p.path == (1 if p.stream_rows > 0 else 0)
+
+
+def test_planner_choices_on_mi355x_shapes(dsw):
+    d = fake_device(dsw)
+    c0 = dsw.plan(d, 32_000, 7, 1)
+    assert (c0.rows_per_wg, c0.reg_slots, c0.lds_rows, c0.stream_rows) == (125, 1, 0, 0)
+    c1 = dsw.plan(d, 151_936, 7, 1)
+    assert (c1.rows_per_wg, c1.reg_slots, c1.reg_rows, c1.lds_rows, c1.stream_rows) == (594, 3, 594, 0, 0)
+    assert c1.path == 0 and c1.onchip_bytes == 151_936 * 512
+    c3 = dsw.plan(d, 248_320, 16, 1)
+    assert (c3.rows_per_wg, c3.reg_slots, c3.lds_rows, c3.stream_rows) == (970, 3, 202, 0)
+    c2 = dsw.plan(d, 151_936, 16, 16)
+    assert c2.reg_slots == 1 and c2.stream_rows > 0 and c2.path == 1
+
+
+def test_planner_stream_fallback_on_small_devices(dsw):
+    # 64 KiB of LDS next to one VGPR row group (16-request tile) cannot hold
+    # 594 rows per CU: the rest streams every step
+    d = fake_device(dsw, cus=256, lds_cu=64 * 1024, lds_blk=64 * 1024)
+    p = dsw.plan(d, 151_936, 7, 16)
+    assert p.rows_per_wg == 594 and p.reg_rows == 256
+    assert p.lds_rows == (64 * 1024 - (1024 + 672 * 16)) // 512
+    assert p.stream_rows == 594 - 256 - p.lds_rows > 0 and p.path == 1
+    # a bigger device holds the same walk fully on chip
+    assert dsw.plan(fake_device(dsw), 151_936, 7, 1).stream_rows == 0
+
+
+def test_planner_force_stream_keeps_nothing_on_chip(dsw):
+    d = fake_device(dsw)
+    p = dsw.plan(d, 151_936, 7, 1, flags=dsw.FLAG_FORCE_STREAM)
+    assert p.reg_rows == 0 and p.lds_rows == 0 and p.stream_rows == 594 and p.onchip_bytes == 0
+
+
+def test_planner_rejects_bad_arguments(dsw):
+    d = fake_device(dsw)
+    for kw, code in [(dict(r=128), -4), (dict(w2_dtype=9), -5), (dict(V=0), -6),
+                     (dict(B=17), -2), (dict(gamma=-1), -3)]:
+        args = dict(V=1000, gamma=7, B=1)
+        args.update(kw)
+        r = args.pop("r", 256)
+        with pytest.raises(dsw.DswError) as e:
+            dsw.plan(d, r=r, **args)
+        assert e.value.code == code

@@ -1,0 +1,213 @@
+"""GPU parity of the persistent walk against the CPU oracle, through the C ABI.
+
+Every case prints what it runs before it runs it, so a failure names itself.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import parity
+import workloads
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dsw():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import serial_draft_head_amd as m
+    m.lib()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def bf16_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def round_dev(inp):
+    return (bf16_dev(inp["base"]), torch.from_numpy(inp["anchor"]).to(DEV),
+            torch.from_numpy(inp["T"]).to(DEV), torch.from_numpy(inp["uniforms"]).to(DEV))
+
+
+def run(walker, W1d, W2d, inp, want_logits=True):
+    base, anchor, T, uni = round_dev(inp)
+    tokens, logits = walker.walk(W1d, W2d, base, anchor, T, uni, want_logits=want_logits)
+    torch.cuda.synchronize()
+    st = walker.status()
+    assert st == 0, f"device status {st}"
+    lg = None if logits is None else logits.view(torch.int16).cpu().numpy().view(np.uint16)
+    return tokens.cpu().numpy(), lg
+
+
+SHAPES = [  # (V, B, gamma, temps)
+    (1, 2, 2, "greedy"),
+    (12, 1, 3, "greedy"),
+    (257, 3, 4, "mixed"),
+    (1000, 1, 7, "greedy"),
+    (4097, 4, 5, "mixed"),
+    (32_000, 1, 7, "greedy"),
+    (65_537, 16, 3, "mixed"),
+    (100_003, 5, 16, "mixed"),
+]
+
+
+@pytest.mark.parametrize("V,B,gamma,temps", SHAPES)
+def test_parity_small_and_ragged(dsw, V, B, gamma, temps):
+    say(f"parity V={V} B={B} gamma={gamma} temps={temps}")
+    W1, W2 = workloads.weights(0, V=V)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(V, gamma_max=16, B_max=16)
+    say("plan", walker.query_plan(B).as_dict())
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, rnd, B=B, gamma=gamma, V=V, temps=temps)
+        toks, lg = run(walker, W1d, W2d, inp)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg)
+        say("round", rnd, rep)
+    walker.close()
+
+
+def test_toy_workload_many_rounds(dsw):
+    """Back-to-back rounds on one handle: the parity state alternates, no memset."""
+    wl = workloads.WORKLOADS[0]
+    say("toy workload, 40 rounds back to back")
+    W1, W2 = workloads.weights(0)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=1)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    rounds = [workloads.round_inputs(0, r, B=1) for r in range(40)]
+    outs = []
+    for inp in rounds:
+        base, anchor, T, uni = round_dev(inp)
+        outs.append(walker.walk(W1d, W2d, base, anchor, T, uni, want_logits=True))
+    torch.cuda.synchronize()
+    assert walker.status() == 0
+    for r, (inp, (t, l)) in enumerate(zip(rounds, outs)):
+        lg = l.view(torch.int16).cpu().numpy().view(np.uint16)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"],
+                                 t.cpu().numpy(), lg)
+        if r % 10 == 0:
+            say("round", r, rep)
+
+
+def test_no_state_pollution_between_greedy_and_sampled(dsw):
+    V = 32_000
+    say("greedy -> sampled -> greedy on one handle")
+    W1, W2 = workloads.weights(0, V=V)
+    walker = dsw.Walker(V, gamma_max=7, B_max=4)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    g = workloads.round_inputs(0, 5, B=4, gamma=7, V=V, temps="greedy")
+    s = workloads.round_inputs(2, 6, B=4, gamma=7, V=V, temps="mixed")
+    s["T"][:] = 1.0
+    t1, l1 = run(walker, W1d, W2d, g)
+    run(walker, W1d, W2d, s)
+    t2, l2 = run(walker, W1d, W2d, g)
+    assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+
+
+def test_logits_optional_and_tokens_identical(dsw):
+    V = 40_000
+    say("tokens without the logits output")
+    W1, W2 = workloads.weights(0, V=V)
+    walker = dsw.Walker(V, gamma_max=7, B_max=4)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(2, 9, B=4, gamma=7, V=V, temps="mixed")
+    t1, _ = run(walker, W1d, W2d, inp, want_logits=True)
+    t2, l2 = run(walker, W1d, W2d, inp, want_logits=False)
+    assert l2 is None and np.array_equal(t1, t2)
+
+
+def test_force_stream_is_bit_identical_to_resident(dsw):
+    V = 60_000
+    say("streamed plan vs resident plan")
+    W1, W2 = workloads.weights(0, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    res = dsw.Walker(V, gamma_max=7, B_max=4)
+    st = dsw.Walker(V, gamma_max=7, B_max=4, flags=dsw.FLAG_FORCE_STREAM)
+    assert st.query_plan(4).stream_rows == st.query_plan(4).rows_per_wg
+    inp = workloads.round_inputs(2, 11, B=4, gamma=7, V=V, temps="mixed")
+    a = run(res, W1d, W2d, inp)
+    b = run(st, W1d, W2d, inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_outputs_outside_the_request_untouched(dsw):
+    V, B, gamma = 9_999, 3, 5
+    say("sentinels around tokens and logits")
+    W1, W2 = workloads.weights(0, V=V)
+    walker = dsw.Walker(V, gamma_max=8, B_max=8)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(2, 2, B=B, gamma=gamma, V=V, temps="mixed")
+    base, anchor, T, uni = round_dev(inp)
+    n = B * gamma * V
+    big_l = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    big_t = torch.full((B * gamma + 64,), -5, dtype=torch.int32, device=DEV)
+    lg = big_l[:n].view(B, gamma, V)
+    tk = big_t[:B * gamma].view(B, gamma)
+    walker.walk(W1d, W2d, base, anchor, T, uni, tokens=tk, logits=lg)
+    torch.cuda.synchronize()
+    assert walker.status() == 0
+    assert torch.all(big_l[n:] == 7.0).item() and torch.all(big_t[B * gamma:] == -5).item()
+
+
+def test_device_checks_latch_status_and_recover(dsw):
+    V = 5_000
+    say("anchor out of range and missing uniforms latch a status; the next call is clean")
+    W1, W2 = workloads.weights(0, V=V)
+    walker = dsw.Walker(V, gamma_max=4, B_max=2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(0, 1, B=2, gamma=4, V=V)
+    base, anchor, T, uni = round_dev(inp)
+    bad = torch.tensor([3, V + 7], dtype=torch.int32, device=DEV)
+    walker.walk(W1d, W2d, base, bad, T, uni)
+    assert walker.status() == -21
+    Ts = torch.tensor([0.0, 1.0], dtype=torch.float32, device=DEV)
+    walker.walk(W1d, W2d, base, anchor, Ts, None)
+    assert walker.status() == -22
+    toks, lg = run(walker, W1d, W2d, inp)
+    parity.check_round(parity.Weights(W1, W2), inp["base"], inp["anchor"], inp["T"],
+                       inp["uniforms"], toks, lg)
+
+
+def test_host_argument_errors(dsw):
+    V = 1_000
+    walker = dsw.Walker(V, gamma_max=4, B_max=2)
+    W1, W2 = workloads.weights(0, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(0, 1, B=3, gamma=4, V=V)
+    base, anchor, T, uni = round_dev(inp)
+    with pytest.raises(dsw.DswError) as e:
+        walker.walk(W1d, W2d, base, anchor, T, uni)
+    assert e.value.code == -2
+    with pytest.raises(ValueError):
+        walker.walk(W1d, W2d.float(), base, anchor, T, uni)
+
+
+@pytest.mark.parametrize("index,B", [(1, 1), (2, 1), (2, 4), (2, 16), (3, 1)])
+def test_full_size_workloads(dsw, index, B):
+    wl = workloads.WORKLOADS[index]
+    say(f"full size {wl.name} B={B}")
+    W1, W2 = workloads.weights(index)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=B)
+    say("plan", walker.query_plan(B).as_dict())
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    for rnd in range(2 if B <= 4 else 1):
+        inp = workloads.round_inputs(index, rnd, B=B)
+        toks, lg = run(walker, W1d, W2d, inp)
+        steps = None if B * wl.gamma <= 32 else [0, wl.gamma - 1]
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 steps=steps)
+        say("round", rnd, rep)
