@@ -68,6 +68,17 @@ extern "C" {
 
 /* dsw_create flags */
 #define DSW_FLAG_FORCE_STREAM 1u /* keep nothing on chip: stream W2 every step      */
+#define DSW_FLAG_COOPERATIVE 2u  /* launch cooperatively.  By default the walk is an
+                                    ordinary launch of one workgroup per CU whose
+                                    size (LDS above half a CU) admits exactly one
+                                    workgroup per CU, so on a device not shared
+                                    with other kernels the whole grid is resident
+                                    (checked with the occupancy API at create).
+                                    A cooperative launch guarantees residency on a
+                                    shared device but costs ~20 us per launch on
+                                    MI355X.  If the grid is ever not resident, the
+                                    bounded waits give up and dsw_status() returns
+                                    DSW_ERR_DEV_TIMEOUT; the kernel never hangs.    */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -156,6 +167,15 @@ int dsw_status(dsw_handle_t h);
 
 /* The plan dsw_walk uses for batch size B on this handle. */
 int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out);
+
+/* Diagnostics: record per-workgroup, per-step phase timestamps of later
+ * dsw_walk calls into `trace`, a device buffer of `bytes` bytes owned by the
+ * caller (NULL disables).  Layout: uint64 [grid][gamma+1][8]; row k < gamma
+ * holds s_memtime counts at: step start, inputs staged, GEMV done, workgroup
+ * argmax known, key posted, all workgroups arrived, tokens known, and (slot 7)
+ * s_memrealtime (100 MHz) at the end of the step; row gamma slot 0 is the
+ * kernel's start.  Calls whose trace would not fit in `bytes` record nothing. */
+int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes);
 
 /* Free the workspace and the handle.  NULL is accepted. */
 int dsw_destroy(dsw_handle_t h);

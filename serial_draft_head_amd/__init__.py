@@ -32,6 +32,7 @@ ERR = {
 BF16, INT8 = 0, 1
 PATH_RESIDENT, PATH_PARTIAL = 0, 1
 FLAG_FORCE_STREAM = 1
+FLAG_COOPERATIVE = 2
 RANK = 256
 
 

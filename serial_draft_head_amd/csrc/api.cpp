@@ -19,6 +19,8 @@ struct dsw_handle {
     char* ws_mem;
     size_t ws_bytes;
     dsw::Workspace ws;
+    unsigned long long* trace;  // optional device trace buffer (caller-owned)
+    long long trace_bytes;
     std::mutex mu;  // guards the per-kernel attribute cache below
     const void* lds_configured[4][17];
     int lds_configured_bytes[4][17];
@@ -91,7 +93,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     dsw_plan_info plan;
     rc = dsw_plan_compute(&dev, V, r, gamma_max, B_max, w2_dtype, flags, &plan);
     if (rc) return rc;
-    if (!dev.cooperative) return DSW_ERR_LAUNCH;
+    if ((flags & DSW_FLAG_COOPERATIVE) && !dev.cooperative) return DSW_ERR_LAUNCH;
 
     dsw_handle* h = new (std::nothrow) dsw_handle();
     if (!h) return DSW_ERR_ARG;
@@ -103,24 +105,42 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->dtype = w2_dtype;
     h->flags = flags;
     h->dev = dev;
+    h->trace = nullptr;
+    h->trace_bytes = 0;
     memset(h->lds_configured, 0, sizeof(h->lds_configured));
     memset(h->lds_configured_bytes, 0, sizeof(h->lds_configured_bytes));
 
     DeviceGuard g(device);
     if (!g.ok) { delete h; return DSW_ERR_DEVICE; }
-    const dsw::WorkspaceLayout L = dsw::workspace_layout(gamma_max, B_max);
+    const dsw::WorkspaceLayout L = dsw::workspace_layout();
     h->ws_bytes = L.total;
     if (hipMalloc(&h->ws_mem, L.total) != hipSuccess) { delete h; return DSW_ERR_HIP; }
-    h->ws.keys = reinterpret_cast<unsigned long long*>(h->ws_mem + L.keys);
-    h->ws.counts = reinterpret_cast<unsigned*>(h->ws_mem + L.counts);
-    h->ws.partials = reinterpret_cast<unsigned long long*>(h->ws_mem + L.partials);
-    h->ws.tok_slots = reinterpret_cast<unsigned*>(h->ws_mem + L.tok_slots);
+    h->ws.mail = reinterpret_cast<unsigned long long*>(h->ws_mem + L.mail);
+    h->ws.tok_mail = reinterpret_cast<unsigned long long*>(h->ws_mem + L.tok_mail);
     h->ws.round_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.round_ctr);
     h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.status);
     if (clear_workspace(h) != DSW_OK) {
         (void)hipFree(h->ws_mem);
         delete h;
         return DSW_ERR_HIP;
+    }
+    // Residency: every batch size this handle serves must fit one workgroup
+    // on each CU, and the grid must not exceed the CU count.
+    for (int B = 1; B <= B_max; ++B) {
+        dsw_plan_info pl;
+        if (dsw_plan_compute(&dev, V, r, gamma_max, B, w2_dtype, flags, &pl) != DSW_OK) continue;
+        const void* fn = dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile);
+        int per_cu = 0;
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pl.lds_bytes);
+        if (!fn ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, pl.block, (size_t)pl.lds_bytes) !=
+                hipSuccess ||
+            per_cu < 1 || pl.grid > dev.cu_count) {
+            (void)hipGetLastError();
+            (void)hipFree(h->ws_mem);
+            delete h;
+            return DSW_ERR_LAUNCH;
+        }
     }
     *out = h;
     return DSW_OK;
@@ -184,12 +204,28 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     p.rows_per_wg = plan.rows_per_wg;
     p.lds_rows = plan.lds_rows;
     p.spin_limit = kSpinLimit;
+    p.trace = nullptr;
+    if (h->trace != nullptr &&
+        (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)
+        p.trace = h->trace;
     void* args[] = {&p};
-    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(plan.grid), dim3(plan.block), args,
-                                              (unsigned)plan.lds_bytes,
-                                              static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (h->flags & DSW_FLAG_COOPERATIVE)
+        e = hipLaunchCooperativeKernel(fn, dim3(plan.grid), dim3(plan.block), args,
+                                       (unsigned)plan.lds_bytes, static_cast<hipStream_t>(stream));
+    else
+        e = hipLaunchKernel(fn, dim3(plan.grid), dim3(plan.block), args, (size_t)plan.lds_bytes,
+                            static_cast<hipStream_t>(stream));
     if (e == hipErrorCooperativeLaunchTooLarge) return DSW_ERR_LAUNCH;
     return e == hipSuccess ? DSW_OK : DSW_ERR_HIP;
+}
+
+extern "C" int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes) {
+    if (!h) return DSW_ERR_NULL;
+    if (trace != nullptr && bytes < 0) return DSW_ERR_ARG;
+    h->trace = static_cast<unsigned long long*>(trace);
+    h->trace_bytes = trace ? bytes : 0;
+    return DSW_OK;
 }
 
 extern "C" int dsw_status(dsw_handle_t h) {

@@ -46,7 +46,7 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     memset(out, 0, sizeof(*out));
     if (r != kRank) return DSW_ERR_RANK;
     if (w2_dtype != DSW_BF16) return DSW_ERR_DTYPE;
-    if (V < 1) return DSW_ERR_VOCAB;
+    if (V < 1 || V > (1 << 20)) return DSW_ERR_VOCAB;  // row ids live in 20 key bits
     if (gamma < 0) return DSW_ERR_GAMMA;
     if (B < 0 || B > 16) return DSW_ERR_BATCH;
     if (dev->cu_count < 1 || dev->max_lds_per_block < 1) return DSW_ERR_DEVICE;
@@ -103,6 +103,6 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     }
     out->onchip_bytes = onchip;
     out->stream_bytes = streamed;
-    out->workspace_bytes = (long long)workspace_layout(gamma > 0 ? gamma : 1, B > 0 ? B : 1).total;
+    out->workspace_bytes = (long long)workspace_layout().total;
     return DSW_OK;
 }

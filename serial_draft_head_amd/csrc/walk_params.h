@@ -13,17 +13,18 @@ constexpr int kMaxSlots = 4;        // 256-row groups per workgroup (rows <= 102
 constexpr int kMaxGrid = 256;       // one workgroup per CU; partial scans assume <= 256
 constexpr int kLdsWork = 16384;     // LDS bytes reserved for u vectors and reductions
 
-// Device workspace.  Every cross-workgroup slot exists twice, indexed by the
-// parity of a device-side round counter: a launch uses parity p and clears
-// parity 1-p for the next launch, so repeated launches (and graph replays)
-// need no memset.
+// Device workspace.  Cross-workgroup traffic goes through per-workgroup
+// mailboxes tagged with a step epoch: workgroup c writes its words for step
+// s into mail[s & 1][c], and readers wait until a word carries the epoch of
+// s.  Nothing needs clearing between steps, launches or graph replays.
+constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 16 exp-sum words
+constexpr int kMaxBatchPersistent = 16;
+constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // epochs live in the low 28 bits, never 0
 struct Workspace {
-    unsigned long long* keys;      // [2][gamma_max][B_max]  packed {ordered logit, ~index}
-    unsigned* counts;              // [2][gamma_max]         arrivals per step
-    unsigned long long* partials;  // [2][gamma_max][B_max][kMaxGrid] {m_c, s_c} per shard
-    unsigned* tok_slots;           // [2][gamma_max][B_max]  sampled token + 1
-    unsigned* round_ctr;           // [1]
-    unsigned* status;              // [1]  latched DSW_DEV_* bits
+    unsigned long long* mail;      // [2][kMaxGrid][kMailWords]
+    unsigned long long* tok_mail;  // [2][kMaxBatchPersistent] sampled token << 32 | epoch
+    unsigned* round_ctr;           // [1]  launches so far (selects the step epochs)
+    unsigned* status;              // [1]  latched kStatus* bits
 };
 
 // Status bits latched by the device (translated to DSW_ERR_DEV_* on the host).
@@ -31,20 +32,16 @@ constexpr unsigned kStatusTimeout = 1u;
 constexpr unsigned kStatusToken = 2u;
 constexpr unsigned kStatusUniforms = 4u;
 
-// Byte offsets of the workspace regions (each 256-byte aligned) for a handle
-// serving at most gamma_max steps and B_max requests.
+// Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t keys, counts, partials, tok_slots, round_ctr, status, total;
+    size_t mail, tok_mail, round_ctr, status, total;
 };
-inline WorkspaceLayout workspace_layout(int gamma_max, int B_max) {
+inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t gb = (size_t)gamma_max * (size_t)B_max;
     WorkspaceLayout L;
     size_t o = 0;
-    L.keys = o;      o = up(o + 2 * gb * 8);
-    L.counts = o;    o = up(o + 2 * (size_t)gamma_max * 4);
-    L.partials = o;  o = up(o + 2 * gb * kMaxGrid * 8);
-    L.tok_slots = o; o = up(o + 2 * gb * 4);
+    L.mail = o;      o = up(o + 2 * (size_t)kMaxGrid * kMailWords * 8);
+    L.tok_mail = o;  o = up(o + 2 * (size_t)kMaxBatchPersistent * 8);
     L.round_ctr = o; o = up(o + 4);
     L.status = o;    o = up(o + 4);
     L.total = o;
@@ -70,6 +67,20 @@ struct WalkParams {
     int rows_per_wg;
     int lds_rows;            // rows per workgroup resident in LDS (after the register slots)
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
+    unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
+};
+
+// Phase timestamps recorded per workgroup and step when a trace buffer is set
+// (s_memtime core-clock counts; slot 7 holds s_memrealtime at 100 MHz).
+enum TracePhase {
+    kTrStepStart = 0,   // top of the step
+    kTrGathered = 1,    // u and the base logits staged (after the barrier)
+    kTrGemvDone = 2,    // GEMV and epilogue done (wave 0)
+    kTrReduced = 3,     // workgroup argmax known
+    kTrPosted = 4,      // key posted and arrival counted
+    kTrArrived = 5,     // every workgroup has arrived
+    kTrSelected = 6,    // tokens known (end of step)
+    kTrReal = 7,        // s_memrealtime at the end of the step
 };
 
 }  // namespace dsw

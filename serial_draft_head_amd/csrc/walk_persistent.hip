@@ -17,18 +17,20 @@
 //   * per step every lane computes whole dot products for its rows with
 //     v_dot2_f32_bf16 against u broadcast from LDS (fp32 accumulation), then
 //     rounds twice to bf16 as the pages' default walk does;
-//   * the workgroup reduces its rows to one 64-bit key per request
-//     (order-preserving bits of the fp32 logit, then the inverted row index,
-//     so equal logits resolve to the smallest id: section "The idea"), posts
-//     it with a device-scope atomic max, counts its arrival with an atomic
-//     add and waits until every workgroup has arrived;
-//   * sampled requests also post each shard's {local max, local exp-sum}
-//     (the per-block max and exp-sum of vLLM's sample kernel); after the
-//     rendezvous every workgroup scans the shard masses in vocabulary order,
-//     the shard that holds u*Z finds the token inside its rows and publishes
-//     it through a mailbox;
-//   * the cross-workgroup slots alternate with the parity of a device round
-//     counter, so repeated launches need no memset (section "The idea").
+//   * the workgroup reduces its rows to one key per request: the
+//     order-preserving bits of the bf16 logit, then the inverted row index, so
+//     equal logits resolve to the smallest id (section "The idea");
+//   * rendezvous: instead of the pages' atomic {key, count} pair, every
+//     workgroup stores its keys into its own mailbox line, tagged with the
+//     step's epoch, and every workgroup reads all mailboxes until each carries
+//     the epoch.  On MI355X device-scope atomics on one line serialise across
+//     the 8 XCDs, so 256 posters cost far more than 256 independent stores;
+//   * sampled requests also post each shard's exp-sum (the per-block max and
+//     exp-sum of vLLM's sample kernel); every workgroup scans the shard masses
+//     in vocabulary order, the shard that holds u*Z finds the token inside its
+//     rows and publishes it through a token mailbox;
+//   * mailboxes alternate between two buffers by step parity and carry the
+//     epoch, so launches and graph replays need no memset (section "The idea").
 #include <hip/hip_runtime.h>
 
 #include "walk_params.h"
@@ -59,20 +61,22 @@ __device__ __forceinline__ float dot8(const uint4 w, const uint4 u, float acc) {
     return acc;
 }
 
-// 64-bit selection key: order-preserving bits of the logit, then ~index.
-__device__ __forceinline__ unsigned long long make_key(float logit, uint32_t v) {
-    uint32_t b = __float_as_uint(logit);
-    if (b == 0x80000000u) b = 0u;  // -0 and +0 compare equal
-    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - v);
+// Selection key (36 bits): order-preserving bits of the bf16 logit, then the
+// inverted row index (rows < 2^20).  Larger key = larger logit, then smaller id.
+constexpr int kIdxBits = 20;
+constexpr unsigned kIdxMask = (1u << kIdxBits) - 1u;
+__device__ __forceinline__ unsigned long long make_key(uint32_t lbits, uint32_t v) {
+    if (lbits == 0x8000u) lbits = 0u;  // -0 and +0 compare equal
+    const uint32_t ord = (lbits & 0x8000u) ? (~lbits & 0xFFFFu) : (lbits | 0x8000u);
+    return ((unsigned long long)ord << kIdxBits) | (unsigned long long)(kIdxMask - v);
 }
 __device__ __forceinline__ float key_logit(unsigned long long key) {
-    const uint32_t ord = (uint32_t)(key >> 32);
-    const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-    return __uint_as_float(b);
+    const uint32_t ord = (uint32_t)(key >> kIdxBits) & 0xFFFFu;
+    const uint32_t b = (ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu);
+    return bf16_to_f32(b);
 }
 __device__ __forceinline__ int key_index(unsigned long long key) {
-    return (int)(0xFFFFFFFFu - (uint32_t)key);
+    return (int)(kIdxMask - ((uint32_t)key & kIdxMask));
 }
 
 // ------------------------------------------------------- wave reductions
@@ -82,11 +86,6 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
         const unsigned long long y = __shfl_xor(x, off, 64);
         x = x > y ? x : y;
     }
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
 __device__ __forceinline__ int wave_min_i(int x) {
@@ -119,58 +118,39 @@ __device__ __forceinline__ int checked_token(int tok, int V, unsigned* status) {
     return tok;
 }
 
-// ------------------------------------------------------ device atomics
+// --------------------------------------------------- device-coherent I/O
 __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ unsigned long long ld_agent64(const unsigned long long* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Poll *p until it reaches `target`; gives up after `limit` polls (or when
-// another workgroup has already latched a status) and returns false.
-__device__ __noinline__ bool wait_at_least(const unsigned* p, unsigned target, unsigned limit,
-                                           unsigned* status) {
-    unsigned it = 0;
-    while (ld_agent(p) < target) {
-        if (++it >= limit) {
-            __hip_atomic_fetch_or(status, kStatusTimeout, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-            return false;
-        }
-        if ((it & 255u) == 0u && ld_agent(status) != 0u) return false;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return true;
+__device__ __forceinline__ void st_agent64(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __noinline__ unsigned wait_nonzero(const unsigned* p, unsigned limit, unsigned* status) {
-    unsigned it = 0, v;
-    while ((v = ld_agent(p)) == 0u) {
-        if (++it >= limit) {
-            __hip_atomic_fetch_or(status, kStatusTimeout, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-            return 0u;
-        }
-        if ((it & 255u) == 0u && ld_agent(status) != 0u) return 0u;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return v;
+__device__ __forceinline__ void latch(unsigned* status, unsigned bits) {
+    __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ the kernel
+#define DSW_TRACE(k, ph)                                                                    \
+    do {                                                                                    \
+        if (p.trace != nullptr && t == 0)                                                   \
+            p.trace[((size_t)c * (gamma + 1) + (k)) * 8 + (ph)] = __builtin_amdgcn_s_memtime(); \
+    } while (0)
+
 template <int REG_SLOTS, int NB>
 __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
     static_assert(REG_SLOTS >= 0 && REG_SLOTS <= kMaxSlots, "register slots");
+    static_assert(NB <= kMaxBatchPersistent, "batch tile");
     extern __shared__ uint4 s_w[];  // LDS-resident rows: [lds_rows][32] swizzled chunks
 
-    __shared__ uint4 s_u[NB * kRowChunks];            // u = W1[prev] per request
+    __shared__ uint4 s_u[NB * kRowChunks];  // u = W1[prev] per request
     __shared__ unsigned long long s_red64[4][NB];
     __shared__ float s_redf[4][NB * kMaxSlots];
     __shared__ float s_scan[kMaxGrid];
     __shared__ int s_redi[4];
-    __shared__ unsigned long long s_key[NB];
     __shared__ float s_T[NB];
-    __shared__ float s_mloc[NB];
     __shared__ float s_sloc[NB];
     __shared__ int s_prev[NB];
     __shared__ unsigned s_round;
@@ -197,6 +177,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
         s_round = ld_agent(p.ws.round_ctr);
         s_abort = 0;
     }
+    DSW_TRACE(gamma, 0);
     if (t < NB) {
         int a = 0;
         float temp = 0.0f;
@@ -204,15 +185,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
             a = p.anchor[t];
             temp = p.T[t];
             if (a < 0 || a >= V) {
-                if (c == 0)
-                    __hip_atomic_fetch_or(status, kStatusToken, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (c == 0) latch(status, kStatusToken);
                 a = 0;
             }
             if (temp > 0.0f && p.uniforms == nullptr) {
-                if (c == 0)
-                    __hip_atomic_fetch_or(status, kStatusUniforms, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (c == 0) latch(status, kStatusUniforms);
                 temp = 0.0f;
             }
             if (!(temp > 0.0f)) temp = 0.0f;
@@ -221,21 +198,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
         s_T[t] = temp;
     }
     for (int j = t; j < NB * kRowChunks; j += kBlock) s_u[j] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    const unsigned par = s_round & 1u;
-    const size_t slot_base = (size_t)par * p.gamma_max * p.B_max;
-
-    // Clear the other parity's slots for the next launch (the previous
-    // launch, which used them, has finished).
-    if (c == 0) {
-        const size_t other = (size_t)(1u - par) * p.gamma_max * p.B_max;
-        for (int j = t; j < p.gamma_max * p.B_max; j += kBlock) {
-            p.ws.keys[other + j] = 0ull;
-            p.ws.tok_slots[other + j] = 0u;
-        }
-        for (int j = t; j < p.gamma_max; j += kBlock)
-            p.ws.counts[(size_t)(1u - par) * p.gamma_max + j] = 0u;
-    }
 
     // ---- entry: load this workgroup's shard on chip ----------------------
     uint4 wr[REG_SLOTS > 0 ? REG_SLOTS : 1][kRowChunks];
@@ -255,26 +217,34 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
         const int il = j >> 5, ch = j & 31;
         s_w[il * kRowChunks + (ch ^ (il & 31))] = W2[(size_t)(v0 + reg_cap + il) * kRowChunks + ch];
     }
+    // base logits of step 0 for the lane's rows (later steps are prefetched
+    // one step ahead, while the rendezvous is in flight)
+    uint32_t bs[NB][kMaxSlots];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int s = 0; s < kMaxSlots; ++s) {
+            const int i = s * kBlock + t;
+            bs[b][s] = (b < B && i < nrows) ? (uint32_t)p.base[((size_t)b * gamma) * V + v0 + i] : 0u;
+        }
+    __syncthreads();
+    const unsigned round = s_round;
 
     // ---- the walk --------------------------------------------------------
     for (int k = 0; k < gamma; ++k) {
+        DSW_TRACE(k, kTrStepStart);
+        const unsigned seq = round * (unsigned)p.gamma_max + (unsigned)k;
+        const unsigned long long epoch = (unsigned long long)(seq % kEpochMod + 1u);
+        const int q = (int)(seq & 1u);
+        unsigned long long* mail_q = p.ws.mail + (size_t)q * kMaxGrid * kMailWords;
+
         // gather u = W1[prev] for every request into LDS
         for (int j = t; j < B * kRowChunks; j += kBlock) {
             const int b = j >> 5, ch = j & 31;
             s_u[j] = W1[(size_t)s_prev[b] * kRowChunks + ch];
         }
-        // this step's base logits for the lane's rows
-        uint32_t bs[NB][kMaxSlots];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int s = 0; s < kMaxSlots; ++s) {
-                const int i = s * kBlock + t;
-                bs[b][s] = (b < B && i < nrows)
-                               ? (uint32_t)p.base[((size_t)b * gamma + k) * V + v0 + i]
-                               : 0u;
-            }
         __syncthreads();
+        DSW_TRACE(k, kTrGathered);
 
         // shard GEMV, fp32 accumulation
         float acc[NB][kMaxSlots];
@@ -331,16 +301,28 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
                 const int i = s * kBlock + t;
                 const uint32_t bias = f32_to_bf16(acc[b][s]);
                 const uint32_t lbits = f32_to_bf16(bf16_to_f32(bs[b][s]) + bf16_to_f32(bias));
-                const float l = bf16_to_f32(lbits);
                 const bool valid = (b < B) && (i < nrows);
-                lg[b][s] = valid ? l : -INFINITY;
+                lg[b][s] = valid ? bf16_to_f32(lbits) : -INFINITY;
                 if (valid) {
-                    const unsigned long long key = make_key(l, (uint32_t)(v0 + i));
+                    const unsigned long long key = make_key(lbits, (uint32_t)(v0 + i));
                     best[b] = key > best[b] ? key : best[b];
                     if (p.logits != nullptr)
                         p.logits[((size_t)b * gamma + k) * V + v0 + i] = (uint16_t)lbits;
                 }
             }
+        }
+        DSW_TRACE(k, kTrGemvDone);
+        // prefetch the next step's base logits; they land during the rendezvous
+        if (k + 1 < gamma) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int s = 0; s < kMaxSlots; ++s) {
+                    const int i = s * kBlock + t;
+                    bs[b][s] = (b < B && i < nrows)
+                                   ? (uint32_t)p.base[((size_t)b * gamma + k + 1) * V + v0 + i]
+                                   : 0u;
+                }
         }
         // workgroup max of the keys
 #pragma unroll
@@ -356,11 +338,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
             for (int w = 1; w < 4; ++w) m = s_red64[w][b] > m ? s_red64[w][b] : m;
             best[b] = m;
         }
+        DSW_TRACE(k, kTrReduced);
 
         // sampled requests: local weights w = exp((l - m_c) / T), their
         // inclusive prefix in vocabulary order (slot-major, then lane), and
         // the shard total s_c
-        float cw[NB][kMaxSlots];   // inclusive prefix of w within the shard (rows of this lane)
+        float cw[NB][kMaxSlots];
         bool any_sampled = false;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -393,61 +376,100 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
                         }
                         cw[b][s] += before;
                     }
-                    if (t == 0) {
-                        s_mloc[b] = (best[b] != 0ull) ? key_logit(best[b]) : -INFINITY;
-                        s_sloc[b] = carry;
-                    }
+                    if (t == 0) s_sloc[b] = carry;
                 }
             }
+            __syncthreads();
         }
 
-        // ---- rendezvous: post keys (and shard masses), count, wait -------
-        if (wave == 0) {
-            if (lane < B) {
-                unsigned long long mine = 0ull;
+        // ---- rendezvous: post this workgroup's mailbox words ---------------
+        if (wave == 0 && lane < B) {
+            unsigned long long mine = 0ull;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    if (b == lane) mine = best[b];
-                const size_t slot = slot_base + (size_t)k * p.B_max + lane;
-                __hip_atomic_fetch_max(&p.ws.keys[slot], mine, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                if (s_T[lane] > 0.0f) {
-                    const unsigned long long pk =
-                        ((unsigned long long)__float_as_uint(s_sloc[lane]) << 32) |
-                        (unsigned long long)__float_as_uint(s_mloc[lane]);
-                    __hip_atomic_store(&p.ws.partials[slot * kMaxGrid + c], pk, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+            for (int b = 0; b < NB; ++b)
+                if (b == lane) mine = best[b];
+            unsigned long long* box = mail_q + (size_t)c * kMailWords;
+            st_agent64(&box[lane], (mine << 28) | epoch);
+            if (s_T[lane] > 0.0f)
+                st_agent64(&box[kMaxBatchPersistent + lane],
+                           ((unsigned long long)__float_as_uint(s_sloc[lane]) << 32) | epoch);
+        }
+        DSW_TRACE(k, kTrPosted);
+        // ... and read every workgroup's words: thread t reads workgroup t
+        unsigned long long kw[NB];
+        float sw[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            kw[b] = 0ull;
+            sw[b] = 0.0f;
+        }
+        if (t < G) {
+            const unsigned long long* box = mail_q + (size_t)t * kMailWords;
+            unsigned it = 0;
+            bool ready = false;
+            while (!ready) {
+                ready = true;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < B) {
+                        const unsigned long long wk = ld_agent64(&box[b]);
+                        if ((wk & kEpochMod) == epoch) kw[b] = wk >> 28;
+                        else ready = false;
+                        if (s_T[b] > 0.0f) {
+                            const unsigned long long ws = ld_agent64(&box[kMaxBatchPersistent + b]);
+                            if ((ws & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(ws >> 32));
+                            else ready = false;
+                        }
+                    }
                 }
+                if (ready) break;
+                if (++it >= p.spin_limit) {
+                    latch(status, kStatusTimeout);
+                    s_abort = 1;
+                    break;
+                }
+                if ((it & 255u) == 0u && ld_agent(status) != 0u) {
+                    s_abort = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            if (lane == 0) {
-                unsigned* cnt = &p.ws.counts[(size_t)par * p.gamma_max + k];
-                __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                if (!wait_at_least(cnt, (unsigned)G, p.spin_limit, status)) s_abort = 1;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (lane < B) s_key[lane] = ld_agent64(&p.ws.keys[slot_base + (size_t)k * p.B_max + lane]);
+        }
+        DSW_TRACE(k, kTrArrived);
+        // global argmax per request
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const unsigned long long m = wave_max_u64(kw[b]);
+            if (lane == 0) s_red64[wave][b] = m;
         }
         __syncthreads();
         if (s_abort) break;
+        unsigned long long win[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            unsigned long long m = s_red64[0][b];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) m = s_red64[w][b] > m ? s_red64[w][b] : m;
+            win[b] = m;
+        }
 
         // ---- selection ----------------------------------------------------
-        for (int b = t; b < B; b += kBlock)
-            if (!(s_T[b] > 0.0f)) s_prev[b] = checked_token(key_index(s_key[b]), V, status);
+        if (t < B) {
+            unsigned long long mine = 0ull;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (b == t) mine = win[b];
+            if (!(s_T[t] > 0.0f)) s_prev[t] = checked_token(key_index(mine), V, status);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (!((b < B) && (s_T[b] > 0.0f))) continue;
             const float Tb = s_T[b];
-            const float M = key_logit(s_key[b]);
-            const size_t slot = slot_base + (size_t)k * p.B_max + b;
+            const float M = key_logit(win[b]);
+            unsigned long long* tbox = p.ws.tok_mail + (size_t)q * kMaxBatchPersistent + b;
             // shard masses S_c = s_c * exp((m_c - M) / T), scanned in shard order
             float S = 0.0f;
-            if (t < G) {
-                const unsigned long long pk = ld_agent64(&p.ws.partials[slot * kMaxGrid + t]);
-                const float mc = __uint_as_float((uint32_t)pk);
-                const float sc = __uint_as_float((uint32_t)(pk >> 32));
-                S = (mc == -INFINITY) ? 0.0f : sc * __expf((mc - M) / Tb);
-            }
+            if (t < G && kw[b] != 0ull) S = sw[b] * __expf((key_logit(kw[b]) - M) / Tb);
             float P = wave_incl_scan(S, lane);
             if (lane == 63) s_redf[wave][0] = P;
             __syncthreads();
@@ -462,11 +484,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
             // owner shard: the first c whose inclusive prefix exceeds target
             const int below = (t < G && P <= target) ? 1 : 0;
             const int last_pos = (t < G && S > 0.0f) ? t : -1;
-            int nb = __popcll(__ballot(below));
-            int lp = wave_max_i(last_pos);
-            if (lane == 0) {
-                s_redi[wave] = nb;
-            }
+            const int nb = __popcll(__ballot(below));
+            const int lp = wave_max_i(last_pos);
+            if (lane == 0) s_redi[wave] = nb;
             __syncthreads();
             int owner = s_redi[0] + s_redi[1] + s_redi[2] + s_redi[3];
             __syncthreads();
@@ -476,16 +496,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
             if (owner >= G) owner = last_c;
             __syncthreads();
             if (c == owner) {
-                // find the first row of this shard whose cumulative mass exceeds target
+                // the first row of this shard whose cumulative mass exceeds target
                 const float pexcl = (owner == 0) ? 0.0f : s_scan[owner - 1];
-                const float scale = __expf((s_mloc[b] - M) / Tb);
+                const float mloc = key_logit(best[b]);
+                const float scale = __expf((mloc - M) / Tb);
                 int first = 0x7FFFFFFF, lastw = -1;
 #pragma unroll
                 for (int s = 0; s < kMaxSlots; ++s) {
                     const int i = s * kBlock + t;
                     if (i < nrows && lg[b][s] != -INFINITY) {
                         if (pexcl + scale * cw[b][s] > target) first = min(first, i);
-                        if (__expf((lg[b][s] - s_mloc[b]) / Tb) > 0.0f) lastw = max(lastw, i);
+                        if (__expf((lg[b][s] - mloc) / Tb) > 0.0f) lastw = max(lastw, i);
                     }
                 }
                 first = wave_min_i(first);
@@ -500,13 +521,24 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
                 const int tok = checked_token(v0 + (first != 0x7FFFFFFF ? first : lastw), V, status);
                 if (t == 0) {
                     s_prev[b] = tok;
-                    __hip_atomic_store(&p.ws.tok_slots[slot], (unsigned)(tok + 1), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    st_agent64(tbox, ((unsigned long long)(unsigned)tok << 32) | epoch);
                 }
             } else if (t == 0) {
-                const unsigned v = wait_nonzero(&p.ws.tok_slots[slot], p.spin_limit, status);
-                if (v == 0u) s_abort = 1;
-                s_prev[b] = (v == 0u) ? 0 : checked_token((int)(v - 1u), V, status);
+                unsigned it = 0;
+                unsigned long long v = 0ull;
+                while (((v = ld_agent64(tbox)) & kEpochMod) != epoch) {
+                    if (++it >= p.spin_limit) {
+                        latch(status, kStatusTimeout);
+                        s_abort = 1;
+                        break;
+                    }
+                    if ((it & 255u) == 0u && ld_agent(status) != 0u) {
+                        s_abort = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                s_prev[b] = s_abort ? 0 : checked_token((int)(v >> 32), V, status);
             }
             __syncthreads();
         }
@@ -514,6 +546,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_persistent(WalkParams p) {
         if (c == 0)
             for (int b = t; b < B; b += kBlock) p.tokens[(size_t)b * gamma + k] = s_prev[b];
         __syncthreads();
+        DSW_TRACE(k, kTrSelected);
+        if (p.trace != nullptr && t == 0)
+            p.trace[((size_t)c * (gamma + 1) + k) * 8 + kTrReal] = __builtin_amdgcn_s_memrealtime();
     }
 
     if (c == 0 && t == 0 && !s_abort)

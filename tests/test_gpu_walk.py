@@ -211,3 +211,17 @@ def test_full_size_workloads(dsw, index, B):
         rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
                                  steps=steps)
         say("round", rnd, rep)
+
+
+def test_cooperative_launch_is_bit_identical(dsw):
+    V = 50_000
+    say("cooperative launch vs the default launch")
+    W1, W2 = workloads.weights(0, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    plain = dsw.Walker(V, gamma_max=7, B_max=4)
+    coop = dsw.Walker(V, gamma_max=7, B_max=4, flags=dsw.FLAG_COOPERATIVE)
+    for rnd in range(3):
+        inp = workloads.round_inputs(2, 20 + rnd, B=4, gamma=7, V=V, temps="mixed")
+        a = run(plain, W1d, W2d, inp)
+        b = run(coop, W1d, W2d, inp)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
