@@ -62,6 +62,10 @@ extern "C" {
 #define DSW_BF16 0               /* W2 bf16 [V][r]                                   */
 #define DSW_INT8 1               /* W2 int8 [V][r] + one fp32 scale per row [V]      */
 
+/* shard GEMV engines */
+#define DSW_ENGINE_VALU 0        /* v_dot2 per lane, one row per lane                */
+#define DSW_ENGINE_MFMA 1        /* 16x16x32 bf16 MFMA tiles, up to 16 requests free */
+
 /* execution paths chosen by the planner */
 #define DSW_PATH_RESIDENT 0      /* every row on chip (VGPR + LDS), one launch       */
 #define DSW_PATH_PARTIAL 1       /* rows on chip + rows streamed every step          */
@@ -79,6 +83,10 @@ extern "C" {
                                     MI355X.  If the grid is ever not resident, the
                                     bounded waits give up and dsw_status() returns
                                     DSW_ERR_DEV_TIMEOUT; the kernel never hangs.    */
+#define DSW_FLAG_VALU_GEMV 4u    /* force the VALU shard GEMV                        */
+#define DSW_FLAG_MFMA_GEMV 8u    /* force the MFMA shard GEMV.  Without either flag
+                                    one request per call takes the VALU engine and
+                                    more take the MFMA engine (measured faster).     */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -111,6 +119,12 @@ typedef struct dsw_plan_info {
     long long onchip_bytes;  /* W2 bytes held on chip over the whole grid      */
     long long stream_bytes;  /* W2 bytes re-read per step over the whole grid  */
     long long workspace_bytes; /* device workspace owned by the handle         */
+    int engine;              /* DSW_ENGINE_*                                    */
+    int tiles_per_wave;      /* MFMA: 16-row tiles per wave                     */
+    int reg_tiles;           /* MFMA: tiles per wave held in VGPR/AGPRs         */
+    int lds_tiles;           /* MFMA: tiles per wave held in LDS                */
+    int max_tiles;           /* MFMA: compiled tiles-per-wave capacity          */
+    int static_lds_bytes;    /* the kernel's static LDS (an upper bound)        */
 } dsw_plan_info;
 
 typedef struct dsw_handle* dsw_handle_t;

@@ -33,6 +33,9 @@ BF16, INT8 = 0, 1
 PATH_RESIDENT, PATH_PARTIAL = 0, 1
 FLAG_FORCE_STREAM = 1
 FLAG_COOPERATIVE = 2
+FLAG_VALU_GEMV = 4
+FLAG_MFMA_GEMV = 8
+ENGINE_VALU, ENGINE_MFMA = 0, 1
 RANK = 256
 
 
@@ -60,7 +63,10 @@ class PlanInfo(ctypes.Structure):
                 ("reg_rows", ctypes.c_int), ("lds_rows", ctypes.c_int),
                 ("stream_rows", ctypes.c_int), ("batch_tile", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int), ("onchip_bytes", ctypes.c_longlong),
-                ("stream_bytes", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong)]
+                ("stream_bytes", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong),
+                ("engine", ctypes.c_int), ("tiles_per_wave", ctypes.c_int),
+                ("reg_tiles", ctypes.c_int), ("lds_tiles", ctypes.c_int),
+                ("max_tiles", ctypes.c_int), ("static_lds_bytes", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -10,6 +10,18 @@
 #include "walk_params.h"
 
 extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile);
+extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
+
+namespace {
+// The compiled kernel a plan runs, or nullptr.
+const void* kernel_for(const dsw_plan_info& pl) {
+    if (pl.engine == DSW_ENGINE_VALU) return dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile);
+    if (pl.batch_tile == 4) return dsw_internal_mfma_kernel_b4(pl.reg_tiles, pl.max_tiles);
+    if (pl.batch_tile == 16) return dsw_internal_mfma_kernel_b16(pl.reg_tiles, pl.max_tiles);
+    return nullptr;
+}
+}  // namespace
 
 struct dsw_handle {
     int device;
@@ -22,8 +34,9 @@ struct dsw_handle {
     unsigned long long* trace;  // optional device trace buffer (caller-owned)
     long long trace_bytes;
     std::mutex mu;  // guards the per-kernel attribute cache below
-    const void* lds_configured[4][17];
-    int lds_configured_bytes[4][17];
+    const void* lds_configured[64];  // kernels whose dynamic-LDS ceiling was raised
+    int lds_configured_bytes[64];
+    int n_configured;
 };
 
 namespace {
@@ -109,6 +122,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->trace_bytes = 0;
     memset(h->lds_configured, 0, sizeof(h->lds_configured));
     memset(h->lds_configured_bytes, 0, sizeof(h->lds_configured_bytes));
+    h->n_configured = 0;
 
     DeviceGuard g(device);
     if (!g.ok) { delete h; return DSW_ERR_DEVICE; }
@@ -125,21 +139,26 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         return DSW_ERR_HIP;
     }
     // Residency: every batch size this handle serves must fit one workgroup
-    // on each CU, and the grid must not exceed the CU count.
+    // on each CU within the LDS limit, and the grid must not exceed the CUs.
     for (int B = 1; B <= B_max; ++B) {
         dsw_plan_info pl;
-        if (dsw_plan_compute(&dev, V, r, gamma_max, B, w2_dtype, flags, &pl) != DSW_OK) continue;
-        const void* fn = dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile);
+        int prc = dsw_plan_compute(&dev, V, r, gamma_max, B, w2_dtype, flags, &pl);
+        const void* fn = prc == DSW_OK ? kernel_for(pl) : nullptr;
+        hipFuncAttributes attr;
         int per_cu = 0;
-        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pl.lds_bytes);
-        if (!fn ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, pl.block, (size_t)pl.lds_bytes) !=
-                hipSuccess ||
-            per_cu < 1 || pl.grid > dev.cu_count) {
+        bool ok = fn != nullptr && hipFuncGetAttributes(&attr, fn) == hipSuccess &&
+                  (int)attr.sharedSizeBytes <= pl.static_lds_bytes &&
+                  (int)attr.sharedSizeBytes + pl.lds_bytes <= dev.max_lds_per_block && pl.grid <= dev.cu_count;
+        if (ok) {
+            (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pl.lds_bytes);
+            ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, pl.block, (size_t)pl.lds_bytes) ==
+                     hipSuccess && per_cu >= 1;
+        }
+        if (!ok) {
             (void)hipGetLastError();
             (void)hipFree(h->ws_mem);
             delete h;
-            return DSW_ERR_LAUNCH;
+            return prc != DSW_OK ? prc : DSW_ERR_LAUNCH;
         }
     }
     *out = h;
@@ -167,21 +186,26 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     dsw_plan_info plan;
     int rc = dsw_plan_compute(&h->dev, h->V, h->r, gamma, B, h->dtype, h->flags, &plan);
     if (rc) return rc;
-    const void* fn = dsw_internal_walk_kernel(plan.reg_slots, plan.batch_tile);
+    const void* fn = kernel_for(plan);
     if (!fn) return DSW_ERR_PLAN;
 
     DeviceGuard g(h->device);
     if (!g.ok) return DSW_ERR_DEVICE;
     {
         std::lock_guard<std::mutex> lock(h->mu);
-        int& done = h->lds_configured_bytes[plan.reg_slots][plan.batch_tile];
-        if (h->lds_configured[plan.reg_slots][plan.batch_tile] != fn || done < plan.lds_bytes) {
+        int slot = -1;
+        for (int i = 0; i < h->n_configured; ++i)
+            if (h->lds_configured[i] == fn) slot = i;
+        if (slot < 0 || h->lds_configured_bytes[slot] < plan.lds_bytes) {
             // Raises the dynamic-LDS ceiling where the runtime enforces one;
             // a failure here surfaces as a launch error below.
             (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
             (void)hipGetLastError();
-            h->lds_configured[plan.reg_slots][plan.batch_tile] = fn;
-            done = plan.lds_bytes;
+            if (slot < 0 && h->n_configured < 64) slot = h->n_configured++;
+            if (slot >= 0) {
+                h->lds_configured[slot] = fn;
+                h->lds_configured_bytes[slot] = plan.lds_bytes;
+            }
         }
     }
 
@@ -203,6 +227,8 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     p.B_max = h->B_max;
     p.rows_per_wg = plan.rows_per_wg;
     p.lds_rows = plan.lds_rows;
+    p.tiles_per_wave = plan.tiles_per_wave;
+    p.lds_tiles = plan.lds_tiles;
     p.spin_limit = kSpinLimit;
     p.trace = nullptr;
     if (h->trace != nullptr &&

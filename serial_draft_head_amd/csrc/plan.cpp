@@ -4,11 +4,16 @@
 //
 // Each workgroup (one per CU) owns ceil(V / grid) contiguous vocabulary rows,
 // the slice-per-CTA split of "Keeping the Draft Walk on Chip", section "The
-// idea: make the walk resident".  The slice is placed in VGPRs first (whole
-// 256-row groups, one row per lane), then in LDS, and whatever is left is
-// streamed from memory every step, as the pages' partially resident kernel
-// does when the table does not fit (section "V = 248,320: 62% on chip, the
-// rest streamed").
+// idea: make the walk resident".  The slice goes to registers first, then to
+// LDS, and whatever is left is streamed from memory every step, as the pages'
+// partially resident kernel does when the table does not fit (section
+// "V = 248,320: 62% on chip, the rest streamed").
+//
+// Two shard-GEMV engines share that plan:
+//   MFMA (default): rows in 16-row tiles, a contiguous run of tiles per wave;
+//     up to kMaxRegTiles tiles per wave in AGPRs, then LDS tiles, then streamed.
+//   VALU: one row per lane in 256-row groups ("slots") in VGPR/AGPRs, then LDS
+//     rows, then streamed rows.
 #include <string.h>
 
 #include "../../include/dsw.h"
@@ -16,26 +21,153 @@
 
 namespace dsw {
 
-// Largest number of VGPR row groups a compiled kernel holds without spilling
-// to scratch, by batch tile (the GEMV keeps batch_tile x 4 accumulators, the
-// weights take 128 registers per group).
-static int reg_slot_cap(int batch_tile) {
+// ---- VALU engine ----------------------------------------------------------
+static int valu_reg_slot_cap(int batch_tile) {
     switch (batch_tile) {
         case 1: return 3;
         case 4: return 2;
         default: return 1;
     }
 }
+static int valu_static_lds(int batch_tile) { return 1024 + 672 * batch_tile; }
+static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 
-// Upper bound of the kernel's static LDS (u vectors, reduction scratch).
-static int static_lds_bytes(int batch_tile) { return 1024 + 672 * batch_tile; }
-
-static int batch_tile_for(int B) {
-    if (B <= 1) return 1;
-    if (B <= 4) return 4;
-    return 16;
+// ---- MFMA engine ----------------------------------------------------------
+// (register tiles, tiles per wave) shapes compiled for each batch tile; must
+// match DSW_MFMA_SHAPES in walk_mfma.h.
+static const int kShapes[][2] = {{2, 2}, {4, 4}, {8, 8}, {8, 10}, {8, 16}};
+static const int kStreamShape[2] = {0, 16};
+static int mfma_tile_for(int B) { return B <= 4 ? 4 : 16; }
+// Upper bound of walk_mfma's static LDS for (batch tile, tiles per wave).
+static int mfma_static_lds(int nb, int max_tiles) {
+    const int rpad = max_tiles * 4 * kTileRows;
+    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 76 + 4 * kBlock) + 1048 + 64;
 }
 
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Rows of tile j of wave w in the first (largest) shard.
+static int tile_rows(int R, int TW, int w, int j) {
+    const int r0 = (w * TW + j) * kTileRows;
+    const int n = R - r0;
+    return n <= 0 ? 0 : (n < kTileRows ? n : kTileRows);
+}
+
+static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int grid, int R,
+                     dsw_plan_info* out) {
+    const int tiles = ceil_div(R, kTileRows);
+    const int TW = ceil_div(tiles, 4);
+    int reg_t = -1, max_t = -1;
+    if (flags & DSW_FLAG_FORCE_STREAM) {
+        reg_t = kStreamShape[0];
+        max_t = kStreamShape[1];
+    } else {
+        for (const auto& sh : kShapes)
+            if (sh[1] >= TW) {
+                reg_t = sh[0];
+                max_t = sh[1];
+                break;
+            }
+    }
+    if (max_t < TW) return DSW_ERR_VOCAB;
+    const int nb = mfma_tile_for(B);
+    const int lds_static = mfma_static_lds(nb, max_t);
+    int avail = dev->max_lds_per_block - lds_static;
+    if (avail < 0) return DSW_ERR_PLAN;
+
+    int n_w[4];
+    for (int w = 0; w < 4; ++w) {
+        int n = tiles - w * TW;
+        n_w[w] = n < 0 ? 0 : (n > TW ? TW : n);
+    }
+    auto slots = [&](int L) {
+        int s = 0;
+        for (int w = 0; w < 4; ++w) {
+            int extra = n_w[w] - reg_t;
+            if (extra < 0) extra = 0;
+            s += extra < L ? extra : L;
+        }
+        return s;
+    };
+    int LT = TW - reg_t;
+    if (LT < 0) LT = 0;
+    if (flags & DSW_FLAG_FORCE_STREAM) LT = 0;
+    while (LT > 0 && slots(LT) * kTileBytes > avail) --LT;
+
+    int reg_rows = 0, lds_rows = 0, stream_rows = 0;
+    for (int w = 0; w < 4; ++w)
+        for (int j = 0; j < TW; ++j) {
+            const int n = tile_rows(R, TW, w, j);
+            if (j < reg_t) reg_rows += n;
+            else if (j < reg_t + LT) lds_rows += n;
+            else stream_rows += n;
+        }
+
+    int lds_bytes = slots(LT) * kTileBytes;
+    const int half = dev->lds_bytes_per_cu / 2 + 1024 - lds_static;  // one workgroup per CU
+    if (lds_bytes < half) lds_bytes = half;
+    if (lds_bytes > avail) lds_bytes = avail;
+    if (lds_bytes < slots(LT) * kTileBytes) return DSW_ERR_PLAN;
+
+    out->engine = DSW_ENGINE_MFMA;
+    out->path = stream_rows > 0 ? DSW_PATH_PARTIAL : DSW_PATH_RESIDENT;
+    out->grid = grid;
+    out->block = kBlock;
+    out->rows_per_wg = R;
+    out->reg_slots = 0;
+    out->reg_rows = reg_rows;
+    out->lds_rows = lds_rows;
+    out->stream_rows = stream_rows;
+    out->batch_tile = nb;
+    out->lds_bytes = lds_bytes;
+    out->tiles_per_wave = TW;
+    out->reg_tiles = reg_t;
+    out->lds_tiles = LT;
+    out->max_tiles = max_t;
+    out->static_lds_bytes = lds_static;
+    return DSW_OK;
+}
+
+static int plan_valu(const dsw_devinfo* dev, int B, unsigned flags, int grid, int R,
+                     dsw_plan_info* out) {
+    if (R > kMaxSlots * kBlock) return DSW_ERR_VOCAB;
+    const int row_bytes = kRank * 2;
+    const int tile = valu_tile_for(B);
+    const int slots = ceil_div(R, kBlock);
+    int reg_slots = slots < valu_reg_slot_cap(tile) ? slots : valu_reg_slot_cap(tile);
+    if (flags & DSW_FLAG_FORCE_STREAM) reg_slots = 0;
+    const int reg_rows = R < reg_slots * kBlock ? R : reg_slots * kBlock;
+
+    const int lds_static = valu_static_lds(tile);
+    int lds_avail = dev->max_lds_per_block - lds_static;
+    if (lds_avail < 0) lds_avail = 0;
+    int lds_rows = R - reg_rows;
+    if (lds_rows > lds_avail / row_bytes) lds_rows = lds_avail / row_bytes;
+    if (lds_rows > (kMaxSlots - reg_slots) * kBlock) lds_rows = (kMaxSlots - reg_slots) * kBlock;
+    if (flags & DSW_FLAG_FORCE_STREAM) lds_rows = 0;
+    if (lds_rows < 0) lds_rows = 0;
+    const int stream_rows = R - reg_rows - lds_rows;
+
+    int lds_bytes = lds_rows * row_bytes;
+    const int half = dev->lds_bytes_per_cu / 2 + 1024 - lds_static;
+    if (lds_bytes < half) lds_bytes = half;
+    if (lds_bytes + lds_static > dev->max_lds_per_block) lds_bytes = dev->max_lds_per_block - lds_static;
+    if (lds_bytes < lds_rows * row_bytes) return DSW_ERR_PLAN;
+
+    out->engine = DSW_ENGINE_VALU;
+    out->path = stream_rows > 0 ? DSW_PATH_PARTIAL : DSW_PATH_RESIDENT;
+    out->grid = grid;
+    out->block = kBlock;
+    out->rows_per_wg = R;
+    out->reg_slots = reg_slots;
+    out->reg_rows = reg_rows;
+    out->lds_rows = lds_rows;
+    out->stream_rows = stream_rows;
+    out->batch_tile = tile;
+    out->lds_bytes = lds_bytes;
+    out->static_lds_bytes = lds_static;
+    return DSW_OK;
+}
 
 }  // namespace dsw
 
@@ -48,56 +180,41 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (w2_dtype != DSW_BF16) return DSW_ERR_DTYPE;
     if (V < 1 || V > (1 << 20)) return DSW_ERR_VOCAB;  // row ids live in 20 key bits
     if (gamma < 0) return DSW_ERR_GAMMA;
-    if (B < 0 || B > 16) return DSW_ERR_BATCH;
+    if (B < 0 || B > kMaxBatchPersistent) return DSW_ERR_BATCH;
     if (dev->cu_count < 1 || dev->max_lds_per_block < 1) return DSW_ERR_DEVICE;
 
     const int grid = dev->cu_count < kMaxGrid ? dev->cu_count : kMaxGrid;
     const long long rows = ((long long)V + grid - 1) / grid;
-    if (rows > (long long)kMaxSlots * kBlock) return DSW_ERR_VOCAB;
+    if (rows > 4 * 16 * kTileRows) return DSW_ERR_VOCAB;  // 4 waves x 16 tiles x 16 rows
+    if ((flags & DSW_FLAG_VALU_GEMV) && (flags & DSW_FLAG_MFMA_GEMV)) return DSW_ERR_ARG;
     const int R = (int)rows;
+    // engine: forced by a flag, else VALU for a single request, MFMA for more
+    bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
+    if (!(flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV))) valu = B <= 1;
+    const int rc = valu ? plan_valu(dev, B, flags, grid, R, out)
+                        : plan_mfma(dev, V, B, flags, grid, R, out);
+    if (rc != DSW_OK) {
+        memset(out, 0, sizeof(*out));
+        return rc;
+    }
     const int row_bytes = kRank * 2;
-    const int tile = batch_tile_for(B);
-    const int slots = (R + kBlock - 1) / kBlock;
-
-    int reg_slots = slots < reg_slot_cap(tile) ? slots : reg_slot_cap(tile);
-    if (flags & DSW_FLAG_FORCE_STREAM) reg_slots = 0;
-    const int reg_rows = R < reg_slots * kBlock ? R : reg_slots * kBlock;
-
-    const int lds_static = static_lds_bytes(tile);
-    int lds_avail = dev->max_lds_per_block - lds_static;
-    if (lds_avail < 0) lds_avail = 0;
-    int lds_rows = R - reg_rows;
-    if (lds_rows > lds_avail / row_bytes) lds_rows = lds_avail / row_bytes;
-    if (lds_rows > (kMaxSlots - reg_slots) * kBlock) lds_rows = (kMaxSlots - reg_slots) * kBlock;
-    if (flags & DSW_FLAG_FORCE_STREAM) lds_rows = 0;
-    if (lds_rows < 0) lds_rows = 0;
-    const int stream_rows = R - reg_rows - lds_rows;
-
-    // Dynamic LDS: the resident rows, but at least half of the CU's LDS so
-    // that two workgroups can never share a CU.
-    int lds_bytes = lds_rows * row_bytes;
-    const int half = dev->lds_bytes_per_cu / 2 + 1024 - lds_static;
-    if (lds_bytes < half) lds_bytes = half;
-    if (lds_bytes + lds_static > dev->max_lds_per_block) lds_bytes = dev->max_lds_per_block - lds_static;
-    if (lds_bytes < lds_rows * row_bytes) return DSW_ERR_PLAN;
-
-    out->path = stream_rows > 0 ? DSW_PATH_PARTIAL : DSW_PATH_RESIDENT;
-    out->grid = grid;
-    out->block = kBlock;
-    out->rows_per_wg = R;
-    out->reg_slots = reg_slots;
-    out->reg_rows = reg_rows;
-    out->lds_rows = lds_rows;
-    out->stream_rows = stream_rows;
-    out->batch_tile = tile;
-    out->lds_bytes = lds_bytes;
-    // bytes over the grid, counting only rows that exist (the last shards may be short)
     long long onchip = 0, streamed = 0;
+    // every shard but the last is full; shards beyond V are empty
     for (int c = 0; c < grid; ++c) {
         long long n = (long long)V - (long long)c * R;
         if (n <= 0) break;
         if (n > R) n = R;
-        long long on = n < reg_rows + lds_rows ? n : reg_rows + lds_rows;
+        // a short shard keeps its first rows in the same classes as the first shard
+        long long on = out->reg_rows + out->lds_rows;
+        if (out->engine == DSW_ENGINE_MFMA) {
+            on = 0;
+            const int TW = out->tiles_per_wave;
+            for (int w = 0; w < 4; ++w)
+                for (int j = 0; j < TW && j < out->reg_tiles + out->lds_tiles; ++j)
+                    on += tile_rows((int)n, TW, w, j);
+        } else if (on > n) {
+            on = n;
+        }
         onchip += on * row_bytes;
         streamed += (n - on) * row_bytes;
     }

@@ -1,0 +1,131 @@
+// walk_device.h -- device helpers shared by the walk kernels: bf16 rounding,
+// the selection key, device-coherent mailbox I/O and wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "walk_params.h"
+
+namespace dsw {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; inf stays inf).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float dot8(const uint4 w, const uint4 u, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x),
+                                          __builtin_bit_cast(bf16x2_t, u.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y),
+                                          __builtin_bit_cast(bf16x2_t, u.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z),
+                                          __builtin_bit_cast(bf16x2_t, u.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w),
+                                          __builtin_bit_cast(bf16x2_t, u.w), acc, false);
+    return acc;
+}
+
+// Selection key (36 bits): order-preserving bits of the bf16 logit, then the
+// inverted row index (rows < 2^20).  Larger key = larger logit, then smaller id.
+constexpr int kIdxBits = 20;
+constexpr unsigned kIdxMask = (1u << kIdxBits) - 1u;
+__device__ __forceinline__ unsigned long long make_key(uint32_t lbits, uint32_t v) {
+    if (lbits == 0x8000u) lbits = 0u;  // -0 and +0 compare equal
+    const uint32_t ord = (lbits & 0x8000u) ? (~lbits & 0xFFFFu) : (lbits | 0x8000u);
+    return ((unsigned long long)ord << kIdxBits) | (unsigned long long)(kIdxMask - v);
+}
+__device__ __forceinline__ float key_logit(unsigned long long key) {
+    const uint32_t ord = (uint32_t)(key >> kIdxBits) & 0xFFFFu;
+    const uint32_t b = (ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu);
+    return bf16_to_f32(b);
+}
+__device__ __forceinline__ int key_index(unsigned long long key) {
+    return (int)(kIdxMask - ((uint32_t)key & kIdxMask));
+}
+
+// ------------------------------------------------------- wave reductions
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long y = __shfl_xor(x, off, 64);
+        x = x > y ? x : y;
+    }
+    return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+    return x;
+}
+// inclusive prefix sum across the 64 lanes of a wave
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// A token id that will index W1: out-of-range ids latch kStatusToken and
+// are replaced by 0 so that no access leaves the table.
+__device__ __forceinline__ int checked_token(int tok, int V, unsigned* status) {
+    if (tok < 0 || tok >= V) {
+        __hip_atomic_fetch_or(status, kStatusToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return 0;
+    }
+    return tok;
+}
+
+// --------------------------------------------------- device-coherent I/O
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_agent64(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent64(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void latch(unsigned* status, unsigned bits) {
+    __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Max of a 32-bit value over the 16 lanes of a DPP row; every lane of the
+// row receives it (quad swaps, then half-row and row mirrors).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));
+    return x;
+}
+
+// Order-preserving 16-bit image of a bf16 pattern (-0 maps like +0).
+__device__ __forceinline__ uint32_t ord16(uint32_t lbits) {
+    if (lbits == 0x8000u) lbits = 0u;
+    return (lbits & 0x8000u) ? (~lbits & 0xFFFFu) : (lbits | 0x8000u);
+}
+__device__ __forceinline__ uint32_t unord16(uint32_t ord) {
+    return (ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu);
+}
+
+// Phase timestamp into the optional trace buffer (thread 0 of each workgroup).
+#define DSW_TRACE(k, ph)                                                                    \
+    do {                                                                                    \
+        if (p.trace != nullptr && t == 0)                                                   \
+            p.trace[((size_t)c * (gamma + 1) + (k)) * 8 + (ph)] = __builtin_amdgcn_s_memtime(); \
+    } while (0)
+
+}  // namespace dsw

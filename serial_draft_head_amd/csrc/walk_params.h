@@ -12,6 +12,9 @@ constexpr int kRowChunks = 32;      // 16-byte chunks in one bf16 row of 256
 constexpr int kMaxSlots = 4;        // 256-row groups per workgroup (rows <= 1024)
 constexpr int kMaxGrid = 256;       // one workgroup per CU; partial scans assume <= 256
 constexpr int kLdsWork = 16384;     // LDS bytes reserved for u vectors and reductions
+constexpr int kTileRows = 16;       // MFMA engine: vocabulary rows per 16x16x32 tile
+constexpr int kTileBytes = kTileRows * kRank * 2;   // 8 KiB of bf16 weights per tile
+constexpr int kMaxRegTiles = 8;     // weight tiles per wave in the 256 AGPRs
 
 // Device workspace.  Cross-workgroup traffic goes through per-workgroup
 // mailboxes tagged with a step epoch: workgroup c writes its words for step
@@ -66,6 +69,8 @@ struct WalkParams {
     int B_max;
     int rows_per_wg;
     int lds_rows;            // rows per workgroup resident in LDS (after the register slots)
+    int tiles_per_wave;      // MFMA engine: 16-row tiles per wave (contiguous rows)
+    int lds_tiles;           // MFMA engine: tiles per wave held in LDS after the VGPR tiles
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };

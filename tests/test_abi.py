@@ -79,62 +79,86 @@ def shards_cover(V, grid, R):
     return covered == V
 
 
+ENGINES = {"mfma": 8, "valu": 4}   # flags forcing each shard-GEMV engine
+
+
+@pytest.mark.parametrize("engine", list(ENGINES))
 @pytest.mark.parametrize("cus", [8, 80, 256])
 @pytest.mark.parametrize("V", [1, 12, 1000, 32_000, 65_537, 151_936, 248_320])
 @pytest.mark.parametrize("B", [1, 4, 16])
-def test_planner_partitions_rows_and_respects_capacity(dsw, cus, V, B):
+def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
     d = fake_device(dsw, cus=cus)
+    flags = ENGINES[engine]
     rows = -(-V // min(cus, 256))
-    if rows > 4 * 256:
+    cap = 4 * 256 if engine == "valu" else 4 * 16 * 16
+    if rows > cap:
         with pytest.raises(dsw.DswError) as e:
-            dsw.plan(d, V, 7, B)
+            dsw.plan(d, V, 7, B, flags=flags)
         assert e.value.code == -6
         return
-    p = dsw.plan(d, V, 7, B)
+    p = dsw.plan(d, V, 7, B, flags=flags)
+    assert p.engine == (1 if engine == "mfma" else 0)
     assert p.grid == min(cus, 256) and p.block == 256
     assert p.rows_per_wg == rows
     assert shards_cover(V, p.grid, p.rows_per_wg)
     assert p.reg_rows + p.lds_rows + p.stream_rows == p.rows_per_wg
-    assert p.reg_rows <= p.reg_slots * 256
-    cap = {1: 3, 4: 2, 16: 1}[p.batch_tile]
-    assert p.reg_slots <= cap
     assert p.batch_tile >= B
     assert p.lds_bytes >= p.lds_rows * 512
-    assert p.lds_bytes + 1024 + 672 * p.batch_tile <= d.max_lds_per_block
-    assert p.lds_bytes + 1024 + 672 * p.batch_tile > d.lds_bytes_per_cu // 2   # one WG per CU
+    assert p.lds_bytes + p.static_lds_bytes <= d.max_lds_per_block
+    assert p.lds_bytes + p.static_lds_bytes > d.lds_bytes_per_cu // 2   # one workgroup per CU
     assert p.onchip_bytes + p.stream_bytes == V * 512
     assert p.path == (1 if p.stream_rows > 0 else 0)
+    if engine == "mfma":
+        assert p.tiles_per_wave * 4 * 16 >= rows
+        assert p.reg_tiles <= 8 and p.tiles_per_wave <= p.max_tiles
+        assert p.reg_tiles + p.lds_tiles <= max(p.tiles_per_wave, p.reg_tiles)
+        assert p.lds_bytes >= p.lds_rows * 512
+    else:
+        assert p.reg_rows <= p.reg_slots * 256
+        assert p.reg_slots <= {1: 3, 4: 2, 16: 1}[p.batch_tile]
 
 
 def test_planner_choices_on_mi355x_shapes(dsw):
     d = fake_device(dsw)
-    c0 = dsw.plan(d, 32_000, 7, 1)
-    assert (c0.rows_per_wg, c0.reg_slots, c0.lds_rows, c0.stream_rows) == (125, 1, 0, 0)
-    c1 = dsw.plan(d, 151_936, 7, 1)
-    assert (c1.rows_per_wg, c1.reg_slots, c1.reg_rows, c1.lds_rows, c1.stream_rows) == (594, 3, 594, 0, 0)
-    assert c1.path == 0 and c1.onchip_bytes == 151_936 * 512
-    c3 = dsw.plan(d, 248_320, 16, 1)
-    assert (c3.rows_per_wg, c3.reg_slots, c3.lds_rows, c3.stream_rows) == (970, 3, 202, 0)
+    pick = lambda p: (p.rows_per_wg, p.tiles_per_wave, p.reg_tiles, p.lds_tiles, p.stream_rows)
+    # by default one request takes the VALU engine, more take the MFMA engine
+    assert dsw.plan(d, 151_936, 7, 1).engine == 0 and dsw.plan(d, 151_936, 7, 2).engine == 1
+    assert pick(dsw.plan(d, 32_000, 7, 1, flags=8)) == (125, 2, 2, 0, 0)
+    c1 = dsw.plan(d, 151_936, 7, 1, flags=8)
+    assert pick(c1) == (594, 10, 8, 2, 0) and c1.path == 0 and c1.onchip_bytes == 151_936 * 512
     c2 = dsw.plan(d, 151_936, 16, 16)
-    assert c2.reg_slots == 1 and c2.stream_rows > 0 and c2.path == 1
+    assert pick(c2) == (594, 10, 8, 2, 0) and c2.batch_tile == 16
+    c3 = dsw.plan(d, 248_320, 16, 1, flags=8)
+    assert c3.rows_per_wg == 970 and c3.tiles_per_wave == 16 and c3.path == 1 and c3.stream_rows > 0
+    c4 = dsw.plan(d, 129_280, 5, 16)
+    assert pick(c4) == (505, 8, 8, 0, 0)
+    # the VALU engine keeps whole 256-row groups per lane
+    v1 = dsw.plan(d, 151_936, 7, 1, flags=4)
+    assert (v1.engine, v1.reg_slots, v1.reg_rows, v1.lds_rows, v1.stream_rows) == (0, 3, 594, 0, 0)
+    v3 = dsw.plan(d, 248_320, 16, 1, flags=4)
+    assert (v3.reg_slots, v3.lds_rows, v3.stream_rows) == (3, 202, 0)
 
 
 def test_planner_stream_fallback_on_small_devices(dsw):
-    # 64 KiB of LDS next to one VGPR row group (16-request tile) cannot hold
-    # 594 rows per CU: the rest streams every step
-    d = fake_device(dsw, cus=256, lds_cu=64 * 1024, lds_blk=64 * 1024)
-    p = dsw.plan(d, 151_936, 7, 16)
-    assert p.rows_per_wg == 594 and p.reg_rows == 256
-    assert p.lds_rows == (64 * 1024 - (1024 + 672 * 16)) // 512
-    assert p.stream_rows == 594 - 256 - p.lds_rows > 0 and p.path == 1
-    # a bigger device holds the same walk fully on chip
-    assert dsw.plan(fake_device(dsw), 151_936, 7, 1).stream_rows == 0
+    # 32 KiB of LDS beside the 4-request kernel's staging leaves no room for
+    # the two LDS tiles per wave that V = 151,936 needs: those rows stream
+    d = fake_device(dsw, cus=256, lds_cu=32 * 1024, lds_blk=32 * 1024)
+    p = dsw.plan(d, 151_936, 7, 4)
+    assert (p.engine, p.reg_tiles, p.lds_tiles) == (1, 8, 0)
+    assert p.stream_rows == 96 and p.path == 1
+    # the same walk on the full device stays on chip
+    assert dsw.plan(fake_device(dsw), 151_936, 7, 4).stream_rows == 0
+    # and the 16-request kernel does not fit 64 KiB at all
+    with pytest.raises(dsw.DswError) as e:
+        dsw.plan(fake_device(dsw, lds_cu=64 * 1024, lds_blk=64 * 1024), 151_936, 7, 16)
+    assert e.value.code == -10
 
 
 def test_planner_force_stream_keeps_nothing_on_chip(dsw):
     d = fake_device(dsw)
-    p = dsw.plan(d, 151_936, 7, 1, flags=dsw.FLAG_FORCE_STREAM)
-    assert p.reg_rows == 0 and p.lds_rows == 0 and p.stream_rows == 594 and p.onchip_bytes == 0
+    for flags in (1, 1 | 4):
+        p = dsw.plan(d, 151_936, 7, 1, flags=flags)
+        assert p.reg_rows == 0 and p.lds_rows == 0 and p.stream_rows == 594 and p.onchip_bytes == 0
 
 
 def test_planner_rejects_bad_arguments(dsw):

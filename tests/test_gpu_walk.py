@@ -63,12 +63,16 @@ SHAPES = [  # (V, B, gamma, temps)
 ]
 
 
+ENGINES = {"mfma": 8, "valu": 4}
+
+
+@pytest.mark.parametrize("engine", list(ENGINES))
 @pytest.mark.parametrize("V,B,gamma,temps", SHAPES)
-def test_parity_small_and_ragged(dsw, V, B, gamma, temps):
-    say(f"parity V={V} B={B} gamma={gamma} temps={temps}")
+def test_parity_small_and_ragged(dsw, V, B, gamma, temps, engine):
+    say(f"parity V={V} B={B} gamma={gamma} temps={temps} engine={engine}")
     W1, W2 = workloads.weights(0, V=V)
     w = parity.Weights(W1, W2)
-    walker = dsw.Walker(V, gamma_max=16, B_max=16)
+    walker = dsw.Walker(V, gamma_max=16, B_max=16, flags=ENGINES[engine])
     say("plan", walker.query_plan(B).as_dict())
     W1d, W2d = bf16_dev(W1), bf16_dev(W2)
     for rnd in range(2):
@@ -129,13 +133,14 @@ def test_logits_optional_and_tokens_identical(dsw):
     assert l2 is None and np.array_equal(t1, t2)
 
 
-def test_force_stream_is_bit_identical_to_resident(dsw):
+@pytest.mark.parametrize("engine", list(ENGINES))
+def test_force_stream_is_bit_identical_to_resident(dsw, engine):
     V = 60_000
-    say("streamed plan vs resident plan")
+    say(f"streamed plan vs resident plan, engine={engine}")
     W1, W2 = workloads.weights(0, V=V)
     W1d, W2d = bf16_dev(W1), bf16_dev(W2)
-    res = dsw.Walker(V, gamma_max=7, B_max=4)
-    st = dsw.Walker(V, gamma_max=7, B_max=4, flags=dsw.FLAG_FORCE_STREAM)
+    res = dsw.Walker(V, gamma_max=7, B_max=4, flags=ENGINES[engine])
+    st = dsw.Walker(V, gamma_max=7, B_max=4, flags=dsw.FLAG_FORCE_STREAM | ENGINES[engine])
     assert st.query_plan(4).stream_rows == st.query_plan(4).rows_per_wg
     inp = workloads.round_inputs(2, 11, B=4, gamma=7, V=V, temps="mixed")
     a = run(res, W1d, W2d, inp)
@@ -195,13 +200,14 @@ def test_host_argument_errors(dsw):
         walker.walk(W1d, W2d.float(), base, anchor, T, uni)
 
 
+@pytest.mark.parametrize("engine", list(ENGINES))
 @pytest.mark.parametrize("index,B", [(1, 1), (2, 1), (2, 4), (2, 16), (3, 1)])
-def test_full_size_workloads(dsw, index, B):
+def test_full_size_workloads(dsw, index, B, engine):
     wl = workloads.WORKLOADS[index]
-    say(f"full size {wl.name} B={B}")
+    say(f"full size {wl.name} B={B} engine={engine}")
     W1, W2 = workloads.weights(index)
     w = parity.Weights(W1, W2)
-    walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=B)
+    walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=B, flags=ENGINES[engine])
     say("plan", walker.query_plan(B).as_dict())
     W1d, W2d = bf16_dev(W1), bf16_dev(W2)
     for rnd in range(2 if B <= 4 else 1):
@@ -225,3 +231,26 @@ def test_cooperative_launch_is_bit_identical(dsw):
         a = run(plain, W1d, W2d, inp)
         b = run(coop, W1d, W2d, inp)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# One vocabulary size per compiled MFMA shape (register tiles, tiles per wave):
+# the planner picks the shape from ceil(ceil(V / 256) / 16 / 4) tiles per wave.
+SHAPE_VOCABS = [(32_000, (2, 2)), (60_000, (4, 4)), (129_280, (8, 8)), (151_936, (8, 10)),
+                (200_000, (8, 16))]
+
+
+@pytest.mark.parametrize("B", [3, 13])
+@pytest.mark.parametrize("V,shape", SHAPE_VOCABS)
+def test_every_mfma_shape(dsw, V, shape, B):
+    say(f"mfma shape {shape} V={V} B={B}")
+    W1, W2 = workloads.weights(0, V=V)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(V, gamma_max=4, B_max=16, flags=dsw.FLAG_MFMA_GEMV)
+    pl = walker.query_plan(B)
+    assert (pl.reg_tiles, pl.max_tiles) == shape and pl.batch_tile == (4 if B <= 4 else 16)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    for temps in ("greedy", "mixed"):
+        inp = workloads.round_inputs(2, 7, B=B, gamma=3, V=V, temps=temps)
+        toks, lg = run(walker, W1d, W2d, inp)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg)
+        say(temps, rep)
