@@ -22,6 +22,8 @@
 namespace dsw {
 
 // ---- VALU engine ----------------------------------------------------------
+// Largest number of VGPR row groups per lane a compiled kernel holds without
+// spilling to scratch (checked in the compiled code objects).
 static int valu_reg_slot_cap(int batch_tile) {
     switch (batch_tile) {
         case 1: return 3;
@@ -29,7 +31,10 @@ static int valu_reg_slot_cap(int batch_tile) {
         default: return 1;
     }
 }
-static int valu_static_lds(int batch_tile) { return 1024 + 672 * batch_tile; }
+// Upper bound of the VALU kernel's static LDS for a batch tile.
+static int valu_static_lds(int nb) {
+    return nb * ((kRowChunks + 1) * 16 + kMaxSlots * kBlock * 2 + 2 * 4 * kBlock + 144) + 1104;
+}
 static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 
 // ---- MFMA engine ----------------------------------------------------------
@@ -41,7 +46,7 @@ static int mfma_tile_for(int B) { return B <= 4 ? 4 : 16; }
 // Upper bound of walk_mfma's static LDS for (batch tile, tiles per wave).
 static int mfma_static_lds(int nb, int max_tiles) {
     const int rpad = max_tiles * 4 * kTileRows;
-    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 76 + 4 * kBlock) + 1048 + 64;
+    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96;
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }

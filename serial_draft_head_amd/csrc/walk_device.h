@@ -112,6 +112,66 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
     return x;
 }
 
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+
+// Max of a 32-bit value over the whole wave, returned to every lane: a DPP
+// row max, then the four row results read out as scalars.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = row16_max_u32(x);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane(x, 0), b = (uint32_t)__builtin_amdgcn_readlane(x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(x, 32), d = (uint32_t)__builtin_amdgcn_readlane(x, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// 64-bit max over the whole wave, returned to every lane.
+__device__ __forceinline__ unsigned long long wave_max_u64_dpp(unsigned long long x) {
+    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+#define DSW_STEP64(ctrl)                                                                      \
+    do {                                                                                      \
+        const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, ctrl, 0xF, 0xF, false); \
+        const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, ctrl, 0xF, 0xF, false); \
+        const bool gt = (ohi > hi) || (ohi == hi && olo > lo);                                \
+        lo = gt ? olo : lo;                                                                   \
+        hi = gt ? ohi : hi;                                                                   \
+    } while (0)
+    DSW_STEP64(kDppQuadSwap1);
+    DSW_STEP64(kDppQuadSwap2);
+    DSW_STEP64(kDppRowHalfMirror);
+    DSW_STEP64(kDppRowMirror);
+#undef DSW_STEP64
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t rh = (uint32_t)__builtin_amdgcn_readlane(hi, 16 * r);
+        const uint32_t rl = (uint32_t)__builtin_amdgcn_readlane(lo, 16 * r);
+        const unsigned long long v = ((unsigned long long)rh << 32) | (unsigned long long)rl;
+        best = v > best ? v : best;
+    }
+    return best;
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: DPP row shifts, then
+// the row broadcasts carry row totals forward.
+__device__ __forceinline__ float wave_incl_scan_dpp(float x) {
+#define DSW_ADD(ctrl, rmask)                                                                   \
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xF, false))
+    DSW_ADD(kDppRowShr1, 0xF);
+    DSW_ADD(kDppRowShr2, 0xF);
+    DSW_ADD(kDppRowShr4, 0xF);
+    DSW_ADD(kDppRowShr8, 0xF);
+    DSW_ADD(kDppRowBcast15, 0xA);
+    DSW_ADD(kDppRowBcast31, 0xC);
+#undef DSW_ADD
+    return x;
+}
+
 // Order-preserving 16-bit image of a bf16 pattern (-0 maps like +0).
 __device__ __forceinline__ uint32_t ord16(uint32_t lbits) {
     if (lbits == 0x8000u) lbits = 0u;

@@ -1,0 +1,683 @@
+// walk_kernel.h -- one persistent launch per round of DSpark's serial Markov
+// draft walk on gfx950 (MI355X), with two shard-GEMV engines.
+//
+// What is computed ("Keeping the Draft Walk on Chip", tie-pilot-qxw.github.io,
+// section "The serial part of a parallel drafter"): for k < gamma,
+// u = W1[prev], logit = bf16(base_k + bf16(W2 . u)), tok = argmax (T = 0) or an
+// inverse-CDF sample of softmax(logit / T) (vLLM PR #64442, "Details"),
+// prev = tok.
+//
+// Residency (section "The idea: make the walk resident"): workgroup c owns the
+// contiguous rows [c*R, c*R + R) of W2 and keeps them on chip for the whole
+// walk, so W2 crosses HBM once per round.
+//
+// GEMV engines:
+//   VALU (A = VGPR row groups per lane): lane t owns rows s*256 + t; the
+//     first A groups live in VGPR/AGPRs (128 dwords per row), then rows in LDS
+//     (16-byte chunks XOR-swizzled), then rows re-read every step.  Each lane
+//     forms whole dot products with v_dot2_f32_bf16 against u broadcast from
+//     LDS, so the GEMV needs no cross-lane reduction.
+//   MFMA (A = VGPR tiles per wave, M = tiles per wave): rows in 16-row tiles,
+//     each the B operand of v_mfma_f32_16x16x32_bf16 (N = rows, K = 32 latent
+//     values); u of up to 16 requests is the A operand, so extra requests cost
+//     no extra matrix work (section "B200: the bf16 table fits on chip":
+//     batching is almost free on the tensor cores).  Each request's results
+//     land in one 16-lane DPP row.
+// Both engines round twice to bf16 (bias, then base + bias) and reduce their
+// rows to workgroup-local keys {order-preserving bf16 logit, ~row}, so equal
+// logits resolve to the smallest id (section "The idea").
+//
+// Rendezvous: each workgroup stores one word per request {logit, ~id, epoch}
+// (and the shard's exp-sum for sampled requests) into its own mailbox region;
+// every workgroup reads all regions until each carries the step's epoch.
+// Regions alternate by step parity and epochs come from a device round
+// counter, so nothing is cleared between steps, launches or graph replays.
+// Sampling scans shard masses in vocabulary order; the owner shard of u*Z finds
+// the token and publishes it through a token mailbox (vLLM PR #64442,
+// "Details": block masses, then a token inside the block).
+#pragma once
+#include "walk_device.h"
+
+namespace dsw {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kEngineValu = 0;
+constexpr int kEngineMfma = 1;
+
+__device__ __forceinline__ f32x4_t mfma_tile(const uint4 a, const uint4 b, f32x4_t acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
+// Workgroup-local 32-bit key: {order-preserving bf16 logit, ~row in shard}.
+__device__ __forceinline__ uint32_t local_key(uint32_t lbits, int r) {
+    return (ord16(lbits) << 16) | (0xFFFFu - (uint32_t)r);
+}
+__device__ __forceinline__ float local_key_logit(uint32_t lk) { return bf16_to_f32(unord16(lk >> 16)); }
+
+// Global 36-bit key {ordered bf16 logit, ~vocabulary id} from a local key; 0 stays 0.
+__device__ __forceinline__ unsigned long long global_key(uint32_t lk, int v0) {
+    if (lk == 0u) return 0ull;
+    const uint32_t v = (uint32_t)v0 + (0xFFFFu - (lk & 0xFFFFu));
+    return ((unsigned long long)(lk >> 16) << kIdxBits) | (unsigned long long)(kIdxMask - v);
+}
+
+// Pin a value in registers: the compiler may not re-load it from memory later.
+#define DSW_PIN4(v_) asm volatile("" : "+a"((v_).x), "+a"((v_).y), "+a"((v_).z), "+a"((v_).w))
+
+template <int ENGINE, int A, int M, int NB>
+__global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
+    constexpr bool kMfma = ENGINE == kEngineMfma;
+    static_assert(NB == 1 || NB == 4 || NB == 16, "batch tile");
+    static_assert(!kMfma || (NB >= 4 && A <= M && A <= kMaxRegTiles), "MFMA shape");
+    static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
+    constexpr int RPAD = kMfma ? M * 4 * kTileRows : kMaxSlots * kBlock;  // rows per shard, bound
+    constexpr int CHMAX = (RPAD + kBlock - 1) / kBlock;                    // scan rows per thread
+    constexpr int US = kRowChunks + 1;                                     // padded u row (uint4)
+    constexpr int KPL = kMfma ? 4 : NB;                                    // request keys per lane
+    extern __shared__ uint4 s_w[];  // LDS-resident weights (engine-specific layout)
+
+    __shared__ uint4 s_u[NB * US];
+    __shared__ uint16_t s_base[kMfma ? NB * RPAD : 1];
+    __shared__ uint16_t s_logit[NB * RPAD];
+    __shared__ uint32_t s_wbest[4][NB];
+    __shared__ unsigned long long s_red64[4][NB];
+    __shared__ float s_redf[4][NB];
+    __shared__ float s_S[NB * kBlock];
+    __shared__ int s_own[NB];
+    __shared__ float s_pex[NB];
+    __shared__ float s_tgt[NB];
+    __shared__ float s_Mg[NB];
+    __shared__ float s_excl[NB * kBlock];
+    __shared__ int s_redi[4];
+    __shared__ int s_redj[4];
+    __shared__ float s_T[NB];
+    __shared__ float s_tot[NB];
+    __shared__ int s_anchor[NB];
+    __shared__ int s_prev[NB];
+    __shared__ unsigned s_round;
+    __shared__ int s_abort;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int g = lane >> 4;  // MFMA: DPP row holding requests 4g .. 4g+3
+    const int n = lane & 15;  // MFMA: row within a tile
+    const int c = blockIdx.x;
+    const int G = gridDim.x;
+    const int V = p.V;
+    const int B = p.B;
+    const int gamma = p.gamma;
+    const int v0 = c * p.rows_per_wg;
+    const int nrows = max(0, min(V, v0 + p.rows_per_wg) - v0);
+    const uint4* __restrict__ W2 = reinterpret_cast<const uint4*>(p.W2);
+    const uint4* __restrict__ W1 = reinterpret_cast<const uint4*>(p.W1);
+    const uint16_t* __restrict__ base = p.base;
+    unsigned* status = p.ws.status;
+    // VALU layout
+    const int reg_cap = kMfma ? 0 : A * kBlock;
+    const int reg_rows = kMfma ? 0 : min(nrows, reg_cap);
+    const int lds_rows = kMfma ? 0 : min(nrows - reg_rows, p.lds_rows);
+    // MFMA layout
+    const int TW = kMfma ? p.tiles_per_wave : 0;
+    const int LT = kMfma ? p.lds_tiles : 0;
+    const int wrow0 = wave * TW * kTileRows;
+    const int nt_w = kMfma ? max(0, min(TW, (nrows - wrow0 + kTileRows - 1) / kTileRows)) : 0;
+
+    if (t == 0) {
+        s_round = ld_agent(p.ws.round_ctr);
+        s_abort = 0;
+    }
+    DSW_TRACE(gamma, 0);
+    if (t < NB) {
+        int a = 0;
+        float temp = 0.0f;
+        if (t < B) {
+            a = p.anchor[t];
+            temp = p.T[t];
+            if (a < 0 || a >= V) {
+                if (c == 0) latch(status, kStatusToken);
+                a = 0;
+            }
+            if (temp > 0.0f && p.uniforms == nullptr) {
+                if (c == 0) latch(status, kStatusUniforms);
+                temp = 0.0f;
+            }
+            if (!(temp > 0.0f)) temp = 0.0f;
+        }
+        s_anchor[t] = a;
+        s_prev[t] = a;
+        s_T[t] = temp;
+    }
+    for (int j = t; j < NB * US; j += kBlock) s_u[j] = make_uint4(0u, 0u, 0u, 0u);
+
+    // ---- entry: this workgroup's shard on chip -------------------------
+    uint4 wr[A > 0 ? A : 1][kMfma ? 8 : kRowChunks];
+    uint32_t bs[kMfma ? 1 : NB][kMfma ? 1 : kMaxSlots];  // VALU: base logits of the lane's rows
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int j = 0; j < A; ++j) {
+            const int r = wrow0 + j * kTileRows + n;
+            if (j < nt_w && r < nrows) {
+                const uint4* src = W2 + (size_t)(v0 + r) * kRowChunks + g;
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) wr[j][kb] = make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) DSW_PIN4(wr[j][kb]);
+        }
+        // LDS tiles: 8 loads per thread in flight before their stores; only
+        // tiles that exist in this shard have an LDS slot
+        for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
+            uint4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = i0 + q * kBlock + t;
+                const int s = idx >> 9, kb = (idx >> 6) & 7, ln = idx & 63;
+                const int ws = s / max(LT, 1);
+                const int j = A + (s - ws * LT);
+                const int r = ws * TW * kTileRows + j * kTileRows + (ln & 15);
+                v[q] = make_uint4(0u, 0u, 0u, 0u);
+                if (idx < 4 * LT * 512 && j < TW && r < nrows)
+                    v[q] = W2[(size_t)(v0 + r) * kRowChunks + kb * 4 + (ln >> 4)];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = i0 + q * kBlock + t;
+                if (idx < 4 * LT * 512) s_w[idx] = v[q];
+            }
+        }
+        for (int i0 = 0; i0 < NB * RPAD; i0 += 8 * kBlock) {
+            uint16_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = i0 + q * kBlock + t;
+                const int b = idx / RPAD, r = idx - b * RPAD;
+                v[q] = (idx < NB * RPAD && b < B && r < nrows) ? base[((size_t)b * gamma) * V + v0 + r] : (uint16_t)0;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int idx = i0 + q * kBlock + t;
+                if (idx < NB * RPAD) s_base[idx] = v[q];
+            }
+        }
+    } else {
+        // no pin here: A = 3 needs 384 registers, more than the 256 VGPRs a "v"
+        // constraint would force them through; the loads land in AGPRs directly
+#pragma unroll
+        for (int s = 0; s < A; ++s) {
+            const int i = s * kBlock + t;
+            if (i < reg_rows) {
+                const uint4* src = W2 + (size_t)(v0 + i) * kRowChunks;
+#pragma unroll
+                for (int ch = 0; ch < kRowChunks; ++ch) wr[s][ch] = src[ch];
+            } else {
+#pragma unroll
+                for (int ch = 0; ch < kRowChunks; ++ch) wr[s][ch] = make_uint4(0u, 0u, 0u, 0u);
+            }
+
+        }
+        for (int j = t; j < lds_rows * kRowChunks; j += kBlock) {
+            const int il = j >> 5, ch = j & 31;
+            s_w[il * kRowChunks + (ch ^ (il & 31))] = W2[(size_t)(v0 + reg_cap + il) * kRowChunks + ch];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int s = 0; s < kMaxSlots; ++s) {
+                const int i = s * kBlock + t;
+                bs[b][s] = (b < B && i < nrows) ? (uint32_t)base[((size_t)b * gamma) * V + v0 + i] : 0u;
+            }
+    }
+    __syncthreads();
+    const unsigned round = s_round;
+    bool any_samp = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) any_samp |= (b < B) && (s_T[b] > 0.0f);
+    const int CH = (nrows + kBlock - 1) / kBlock;  // rows per thread in vocabulary-order scans
+
+    // token of request b at the end of the current step (after the winner
+    // reduction and, for sampled requests, the owner's publication)
+#define DSW_TOKEN(b)                                                                             \
+    ((s_T[b] > 0.0f)                                                                             \
+         ? s_prev[b]                                                                             \
+         : checked_token(key_index(max(max(s_red64[0][b], s_red64[1][b]),                        \
+                                       max(s_red64[2][b], s_red64[3][b]))),                      \
+                         V, status))
+
+    // ---- the walk --------------------------------------------------------
+    for (int k = 0; k < gamma; ++k) {
+        DSW_TRACE(k, kTrStepStart);
+        const unsigned seq = round * (unsigned)p.gamma_max + (unsigned)k;
+        const unsigned long long epoch = (unsigned long long)(seq % kEpochMod + 1u);
+        const int q = (int)(seq & 1u);
+        unsigned long long* mail_q = p.ws.mail + (size_t)q * kMaxGrid * kMailWords;
+
+        if constexpr (kMfma) {
+            if (k > 0) {  // this step's base logits for the shard, loads batched
+                for (int b = 0; b < B; ++b) {
+                    const uint16_t* src = base + ((size_t)b * gamma + k) * V + v0;
+                    uint16_t v[CHMAX];
+#pragma unroll
+                    for (int q = 0; q < CHMAX; ++q) {
+                        const int r = q * kBlock + t;
+                        if (r < nrows) v[q] = src[r];
+                    }
+#pragma unroll
+                    for (int q = 0; q < CHMAX; ++q) {
+                        const int r = q * kBlock + t;
+                        if (r < nrows) s_base[b * RPAD + r] = v[q];
+                    }
+                }
+            }
+        }
+        // gather u = W1[prev] for every request
+        for (int j = t; j < B * kRowChunks; j += kBlock) {
+            const int b = j >> 5, ch = j & 31;
+            const int prev = (k == 0) ? s_anchor[b] : DSW_TOKEN(b);
+            s_u[b * US + ch] = W1[(size_t)prev * kRowChunks + ch];
+        }
+        __syncthreads();
+        DSW_TRACE(k, kTrGathered);
+
+        uint32_t best[KPL];
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) best[i] = 0u;
+
+        if constexpr (kMfma) {
+            // A operand: lane l carries u of request l%16, latent 8*(l/16).. of each K block
+            uint4 a[8];
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) a[kb] = (n < B) ? s_u[n * US + kb * 4 + g] : make_uint4(0u, 0u, 0u, 0u);
+            const int lofs = 4 * g * RPAD + wrow0 + n;
+#define DSW_EPI_MFMA(dv, j)                                                                      \
+    do {                                                                                         \
+        const int r_ = wrow0 + (j) * kTileRows + n;                                              \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
+            if (4 * g + i < B && r_ < nrows) {                                                   \
+                const int e_ = lofs + i * RPAD + (j) * kTileRows;                                \
+                const uint32_t bias_ = f32_to_bf16((dv)[i]);                                     \
+                const uint32_t lb_ = f32_to_bf16(bf16_to_f32(s_base[e_]) + bf16_to_f32(bias_));  \
+                best[i] = max(best[i], local_key(lb_, r_));                                      \
+                s_logit[e_] = (uint16_t)lb_;                                                     \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
+            f32x4_t d[A > 0 ? A : 1];
+#pragma unroll
+            for (int j = 0; j < (A > 0 ? A : 1); ++j) d[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int j = 0; j < A; ++j)
+                    if (j < nt_w) d[j] = mfma_tile(a[kb], wr[j][kb], d[j]);
+#pragma unroll
+            for (int j = 0; j < A; ++j)
+                if (j < nt_w) DSW_EPI_MFMA(d[j], j);
+#pragma unroll 1
+            for (int j = A; j < M; ++j) {
+                if (j < nt_w) {
+                    f32x4_t dd = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (j - A < LT) {
+                        const int sb = (wave * LT + (j - A)) * 512 + lane;
+#pragma unroll
+                        for (int kb = 0; kb < 8; ++kb) dd = mfma_tile(a[kb], s_w[sb + kb * 64], dd);
+                    } else {
+                        const int r = wrow0 + j * kTileRows + n;
+                        const bool ok = r < nrows;
+                        const uint4* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks + g;
+#pragma unroll
+                        for (int kb = 0; kb < 8; ++kb)
+                            dd = mfma_tile(a[kb], ok ? src[kb * 4] : make_uint4(0u, 0u, 0u, 0u), dd);
+                    }
+                    DSW_EPI_MFMA(dd, j);
+                }
+            }
+#undef DSW_EPI_MFMA
+        } else {
+            float acc[NB][kMaxSlots];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int s = 0; s < kMaxSlots; ++s) acc[b][s] = 0.0f;
+            if (A > 0) {
+#pragma unroll
+                for (int ch = 0; ch < kRowChunks; ++ch) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        if (NB == 1 || b < B) {
+                            const uint4 u4 = s_u[b * US + ch];
+#pragma unroll
+                            for (int s = 0; s < A; ++s) acc[b][s] = dot8(wr[s][ch], u4, acc[b][s]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = A; s < kMaxSlots; ++s) {
+                const int i = s * kBlock + t;
+                if (i < nrows) {
+                    const int il = i - reg_cap;
+                    // weights in groups of kGrp chunks: every load of a group is
+                    // issued before the first dot product waits on it
+                    constexpr int kGrp = NB == 16 ? 4 : 8;
+                    if (il < lds_rows) {
+#pragma unroll 1
+                        for (int c0 = 0; c0 < kRowChunks; c0 += kGrp) {
+                            uint4 w4[kGrp];
+#pragma unroll
+                            for (int q = 0; q < kGrp; ++q) w4[q] = s_w[il * kRowChunks + ((c0 + q) ^ (il & 31))];
+#pragma unroll
+                            for (int q = 0; q < kGrp; ++q)
+#pragma unroll
+                                for (int b = 0; b < NB; ++b)
+                                    if (NB == 1 || b < B) acc[b][s] = dot8(w4[q], s_u[b * US + c0 + q], acc[b][s]);
+                        }
+                    } else {
+                        const uint4* src = W2 + (size_t)(v0 + i) * kRowChunks;
+#pragma unroll 1
+                        for (int c0 = 0; c0 < kRowChunks; c0 += kGrp) {
+                            uint4 w4[kGrp];
+#pragma unroll
+                            for (int q = 0; q < kGrp; ++q) w4[q] = src[c0 + q];
+#pragma unroll
+                            for (int q = 0; q < kGrp; ++q)
+#pragma unroll
+                                for (int b = 0; b < NB; ++b)
+                                    if (NB == 1 || b < B) acc[b][s] = dot8(w4[q], s_u[b * US + c0 + q], acc[b][s]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int s = 0; s < kMaxSlots; ++s) {
+                    const int i = s * kBlock + t;
+                    if ((NB == 1 || b < B) && i < nrows) {
+                        const uint32_t bias = f32_to_bf16(acc[b][s]);
+                        const uint32_t lbits = f32_to_bf16(bf16_to_f32(bs[b][s]) + bf16_to_f32(bias));
+                        best[b] = max(best[b], local_key(lbits, i));
+                        s_logit[b * RPAD + i] = (uint16_t)lbits;
+                    }
+                }
+            }
+            // the next step's base logits land while the rendezvous is in flight
+            if (k + 1 < gamma) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int s = 0; s < kMaxSlots; ++s) {
+                        const int i = s * kBlock + t;
+                        bs[b][s] = (b < B && i < nrows)
+                                       ? (uint32_t)base[((size_t)b * gamma + k + 1) * V + v0 + i]
+                                       : 0u;
+                    }
+            }
+        }
+        DSW_TRACE(k, kTrGemvDone);
+
+        // workgroup argmax per request: DPP within the wave, then 4 waves via LDS
+        if constexpr (kMfma) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) best[i] = row16_max_u32(best[i]);
+            if (n == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i < NB) s_wbest[wave][4 * g + i] = best[i];
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint32_t m = wave_max_u32(best[b]);
+                if (lane == 0) s_wbest[wave][b] = m;
+            }
+        }
+        __syncthreads();
+        DSW_TRACE(k, kTrReduced);
+
+        // sampled requests: masses w = exp((l - m_c) / T) of the shard's rows in
+        // vocabulary order, CH consecutive rows per thread
+        if (any_samp) {
+            float part[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                part[b] = 0.0f;
+                if (b < B && s_T[b] > 0.0f) {
+                    const uint32_t lk = max(max(s_wbest[0][b], s_wbest[1][b]), max(s_wbest[2][b], s_wbest[3][b]));
+                    const float ml = local_key_logit(lk);
+                    const float Tb = s_T[b];
+#pragma unroll
+                    for (int rr = 0; rr < CHMAX; ++rr) {
+                        const int r = t * CH + rr;
+                        if (rr < CH && r < nrows)
+                            part[b] += __expf((bf16_to_f32(s_logit[b * RPAD + r]) - ml) / Tb);
+                    }
+                }
+            }
+            float incl[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                incl[b] = 0.0f;
+                if (b < B && s_T[b] > 0.0f) {
+                    incl[b] = wave_incl_scan_dpp(part[b]);
+                    if (lane == 63) s_redf[wave][b] = incl[b];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b < B && s_T[b] > 0.0f) {
+                    float off = 0.0f, tot = 0.0f;
+                    for (int w = 0; w < 4; ++w) {
+                        if (w < wave) off += s_redf[w][b];
+                        tot += s_redf[w][b];
+                    }
+                    s_excl[b * kBlock + t] = off + (incl[b] - part[b]);
+                    if (t == 0) s_tot[b] = tot;
+                }
+            }
+        }
+
+        // ---- rendezvous: post, write the logits out, read every mailbox ------
+        if (wave == 0 && lane < B) {
+            const uint32_t lk = max(max(s_wbest[0][lane], s_wbest[1][lane]), max(s_wbest[2][lane], s_wbest[3][lane]));
+            unsigned long long* box = mail_q + (size_t)c * kMailWords;
+            st_agent64(&box[lane], (global_key(lk, v0) << 28) | epoch);
+            if (s_T[lane] > 0.0f)
+                st_agent64(&box[kMaxBatchPersistent + lane],
+                           ((unsigned long long)__float_as_uint(s_tot[lane]) << 32) | epoch);
+        }
+        DSW_TRACE(k, kTrPosted);
+        if (p.logits != nullptr) {  // the exact values the tokens are selected from
+            for (int b = 0; b < B; ++b) {
+                uint16_t* dst = p.logits + ((size_t)b * gamma + k) * V + v0;
+                for (int r = t; r < nrows; r += kBlock) dst[r] = s_logit[b * RPAD + r];
+            }
+        }
+        unsigned long long kw[NB];
+        float sw[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            kw[b] = 0ull;
+            sw[b] = 0.0f;
+        }
+        if (t < G) {
+            const unsigned long long* box = mail_q + (size_t)t * kMailWords;
+            unsigned it = 0;
+            for (;;) {
+                bool ready = true;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (NB == 1 || b < B) {
+                        const unsigned long long wk = ld_agent64(&box[b]);
+                        if ((wk & kEpochMod) == epoch) kw[b] = wk >> 28;
+                        else ready = false;
+                        if (s_T[b] > 0.0f) {
+                            const unsigned long long ws = ld_agent64(&box[kMaxBatchPersistent + b]);
+                            if ((ws & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(ws >> 32));
+                            else ready = false;
+                        }
+                    }
+                }
+                if (ready) break;
+                if (++it >= p.spin_limit) {
+                    latch(status, kStatusTimeout);
+                    s_abort = 1;
+                    break;
+                }
+                if ((it & 255u) == 0u && ld_agent(status) != 0u) {
+                    s_abort = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        DSW_TRACE(k, kTrArrived);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const unsigned long long m = wave_max_u64_dpp(kw[b]);
+            if (lane == 0) s_red64[wave][b] = m;
+        }
+        __syncthreads();
+        if (s_abort) break;
+
+        // ---- sampled requests: owner shard of u*Z ------------------------
+        // Every workgroup derives the same owner from the same mailbox words
+        // with the same code, so they agree without another exchange.
+        if (any_samp) {
+            // shard masses S_c = s_c * exp((m_c - M) / T), one request per row of s_S
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if ((b < B) && (s_T[b] > 0.0f)) {
+                    const unsigned long long win =
+                        max(max(s_red64[0][b], s_red64[1][b]), max(s_red64[2][b], s_red64[3][b]));
+                    float S = 0.0f;
+                    if (t < G && kw[b] != 0ull) S = sw[b] * __expf((key_logit(kw[b]) - key_logit(win)) / s_T[b]);
+                    s_S[b * kBlock + t] = S;
+                }
+            }
+            __syncthreads();
+            // wave w scans the shard masses of requests w, w + 4, ...; lane l holds
+            // shards 4l .. 4l+3.  The owner is the first shard with positive mass
+            // whose inclusive prefix exceeds u*Z, else the last one with positive mass.
+            for (int b = wave; b < B; b += 4) {
+                if (!(s_T[b] > 0.0f)) continue;
+                const float4 m4 = reinterpret_cast<const float4*>(s_S + b * kBlock)[lane];
+                const float q0 = m4.x, q1 = q0 + m4.y, q2 = q1 + m4.z, q3 = q2 + m4.w;
+                const float incl = wave_incl_scan_dpp(q3);
+                const float ex = incl - q3;
+                const float Z = __shfl(incl, 63);
+                const float target = p.uniforms[(size_t)b * gamma + k] * Z;
+                const float c4[4] = {ex + q0, ex + q1, ex + q2, ex + q3};
+                const float w4[4] = {m4.x, m4.y, m4.z, m4.w};
+                uint32_t first = 0u, lastp = 0u;  // shard + 1, 0 = none
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    if (w4[i] > 0.0f && c4[i] > target) first = (uint32_t)(4 * lane + i) + 1u;
+                    if (lastp == 0u && w4[i] > 0.0f) lastp = (uint32_t)(4 * lane + i) + 1u;
+                }
+                const uint32_t fmin = wave_max_u32(first ? 0xFFFFFFFFu - first : 0u);
+                const uint32_t lmax = wave_max_u32(lastp);
+                const int owner = fmin ? (int)(0xFFFFFFFFu - fmin) - 1 : (int)lmax - 1;
+                // exclusive prefix of the owner: c4 of shard owner - 1
+                const int pj = max(owner - 1, 0);
+                const float cj = (pj & 3) == 0 ? c4[0] : ((pj & 3) == 1 ? c4[1] : ((pj & 3) == 2 ? c4[2] : c4[3]));
+                const float pexcl = __shfl(cj, pj >> 2);
+                if (lane == 0) {
+                    s_own[b] = owner;
+                    s_pex[b] = owner > 0 ? pexcl : 0.0f;
+                    s_tgt[b] = target;
+                    s_Mg[b] = key_logit(max(max(s_red64[0][b], s_red64[1][b]), max(s_red64[2][b], s_red64[3][b])));
+                }
+            }
+            __syncthreads();
+            // the owner finds the token inside its rows and publishes it
+            for (int b = 0; b < B; ++b) {
+                if (!(s_T[b] > 0.0f) || s_own[b] != c) continue;
+                const float Tb = s_T[b];
+                const float target = s_tgt[b];
+                const float pexcl = s_pex[b];
+                const uint32_t lk = max(max(s_wbest[0][b], s_wbest[1][b]), max(s_wbest[2][b], s_wbest[3][b]));
+                const float ml = local_key_logit(lk);
+                const float scale = __expf((ml - s_Mg[b]) / Tb);
+                float run = s_excl[b * kBlock + t];
+                uint32_t first = 0u, lastw = 0u;  // row + 1, 0 = none
+#pragma unroll
+                for (int rr = 0; rr < CHMAX; ++rr) {
+                    const int r = t * CH + rr;
+                    if (rr < CH && r < nrows) {
+                        const float w = __expf((bf16_to_f32(s_logit[b * RPAD + r]) - ml) / Tb);
+                        run += w;
+                        if (first == 0u && pexcl + scale * run > target) first = (uint32_t)r + 1u;
+                        if (w > 0.0f) lastw = (uint32_t)r + 1u;
+                    }
+                }
+                // smallest crossing row: max over the complement
+                const uint32_t fmin = wave_max_u32(first ? 0xFFFFFFFFu - first : 0u);
+                const uint32_t lmax = wave_max_u32(lastw);
+                if (lane == 0) {
+                    s_redi[wave] = (int)fmin;
+                    s_redj[wave] = (int)lmax;
+                }
+                __syncthreads();
+                uint32_t fm = 0u, lm = 0u;
+                for (int w = 0; w < 4; ++w) {
+                    fm = max(fm, (uint32_t)s_redi[w]);
+                    lm = max(lm, (uint32_t)s_redj[w]);
+                }
+                // no crossing row (rounding): the last row with positive mass;
+                // none at all cannot happen for the owner, flag it if it does
+                const int row = fm ? (int)(0xFFFFFFFFu - fm) - 1 : (lm ? (int)lm - 1 : -1);
+                const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
+                __syncthreads();
+                if (t == 0) {
+                    s_prev[b] = tok;
+                    st_agent64(p.ws.tok_mail + (size_t)q * kMaxBatchPersistent + b,
+                               ((unsigned long long)(unsigned)tok << 32) | epoch);
+                }
+            }
+            // every other sampled request: thread b reads its token mailbox
+            if (t < B && s_T[t] > 0.0f && s_own[t] != c) {
+                const unsigned long long* tbox = p.ws.tok_mail + (size_t)q * kMaxBatchPersistent + t;
+                unsigned it = 0;
+                unsigned long long v = 0ull;
+                bool ok = true;
+                while (((v = ld_agent64(tbox)) & kEpochMod) != epoch) {
+                    if (++it >= p.spin_limit) {
+                        latch(status, kStatusTimeout);
+                        ok = false;
+                        break;
+                    }
+                    if ((it & 255u) == 0u && ld_agent(status) != 0u) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (!ok) s_abort = 1;
+                s_prev[t] = ok ? checked_token((int)(v >> 32), V, status) : 0;
+            }
+            __syncthreads();
+            if (s_abort) break;
+        }
+        if (c == 0 && t < B) p.tokens[(size_t)t * gamma + k] = DSW_TOKEN(t);
+        DSW_TRACE(k, kTrSelected);
+        if (p.trace != nullptr && t == 0)
+            p.trace[((size_t)c * (gamma + 1) + k) * 8 + kTrReal] = __builtin_amdgcn_s_memrealtime();
+    }
+#undef DSW_TOKEN
+
+    if (c == 0 && t == 0 && !s_abort)
+        __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// (register tiles, tiles per wave) shapes of the MFMA engine, per batch tile
+#define DSW_MFMA_SHAPES(X) X(2, 2) X(4, 4) X(8, 8) X(8, 10) X(8, 16) X(0, 16)
+
+}  // namespace dsw

@@ -1,12 +1,12 @@
-// walk_mfma_b16.hip -- MFMA-engine walk kernels for batch tile 16 (up to 16
-// requests per launch); the kernel itself is in walk_mfma.h.
-#include "walk_mfma.h"
+// walk_mfma_b16.hip -- MFMA-engine walk kernels (walk_kernel.h) for batch
+// tile 16 (up to 16 requests per launch).
+#include "walk_kernel.h"
 
 // Host-side lookup used by the launcher: the kernel for (register tiles,
 // tiles per wave) at batch tile 16, or nullptr when that shape is not compiled.
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles) {
 #define DSW_PICK(R, M) \
-    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_mfma<(R), (M), 16>;
+    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_kernel<dsw::kEngineMfma, (R), (M), 16>;
     DSW_MFMA_SHAPES(DSW_PICK)
 #undef DSW_PICK
     return nullptr;

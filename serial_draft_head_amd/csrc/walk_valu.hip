@@ -1,0 +1,16 @@
+// walk_valu.hip -- VALU-engine walk kernels (walk_kernel.h) for every
+// (VGPR row groups per lane, batch tile) the planner may pick.
+#include "walk_kernel.h"
+
+// Host-side lookup used by the launcher: the kernel for (register row groups,
+// batch tile), or nullptr when it is not compiled.
+extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile) {
+#define DSW_PICK(R, NB)                                  \
+    if (reg_slots == (R) && batch_tile == (NB))          \
+        return (const void*)dsw::walk_kernel<dsw::kEngineValu, (R), 0, (NB)>;
+    DSW_PICK(0, 1) DSW_PICK(1, 1) DSW_PICK(2, 1) DSW_PICK(3, 1)
+    DSW_PICK(0, 4) DSW_PICK(1, 4) DSW_PICK(2, 4)
+    DSW_PICK(0, 16) DSW_PICK(1, 16)
+#undef DSW_PICK
+    return nullptr;
+}
