@@ -245,7 +245,9 @@ def main():
     achieved = abytes / (mean_launch * 1e-6) / 1e9
     w2_bytes = V * 256 * 2
     stepwise_bound = gamma * w2_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
-    kernel = "walk_mfma" if plan["engine"] == dsw.ENGINE_MFMA else "walk_persistent"
+    kernel = (f"walk_kernel<{plan['engine']}, "
+              f"{plan['reg_tiles'] if plan['engine'] == dsw.ENGINE_MFMA else plan['reg_slots']}, "
+              f"{plan['max_tiles'] if plan['engine'] == dsw.ENGINE_MFMA else 0}, {plan['batch_tile']}>")
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                           "traffic": recorded_traffic(wl.name, B, gamma),

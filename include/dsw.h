@@ -60,7 +60,11 @@ extern "C" {
 
 /* W2 storage */
 #define DSW_BF16 0               /* W2 bf16 [V][r]                                   */
-#define DSW_INT8 1               /* W2 int8 [V][r] + one fp32 scale per row [V]      */
+#define DSW_INT8 1               /* W2 int8 [V][r] + one fp32 scale per row [V]:
+                                    bias = bf16(scale[v] * fp32 sum_j q[v][j] u[j])
+                                    (the int8 table with one fp32 scale per row of
+                                    section "V = 248,320: 62% on chip, the rest
+                                    streamed"); always on the MFMA engine      */
 
 /* shard GEMV engines */
 #define DSW_ENGINE_VALU 0        /* v_dot2 per lane, one row per lane                */
@@ -125,6 +129,7 @@ typedef struct dsw_plan_info {
     int lds_tiles;           /* MFMA: tiles per wave held in LDS                */
     int max_tiles;           /* MFMA: compiled tiles-per-wave capacity          */
     int static_lds_bytes;    /* the kernel's static LDS (an upper bound)        */
+    int w2_dtype;            /* DSW_BF16 or DSW_INT8 (int8: MFMA engine only)    */
 } dsw_plan_info;
 
 typedef struct dsw_handle* dsw_handle_t;
@@ -138,8 +143,9 @@ int dsw_device_info(int device, dsw_devinfo* out);
  * each CTA one slice of vocabulary rows (section "The idea: make the walk
  * resident"); each shard is placed in VGPRs first, then LDS, and whatever is
  * left is streamed every step (section "V = 248,320: 62% on chip, the rest
- * streamed").  flags: DSW_FLAG_FORCE_STREAM.  Returns DSW_ERR_* on invalid
- * sizes or when no plan fits. */
+ * streamed").  flags: DSW_FLAG_FORCE_STREAM and the engine flags.  int8 W2
+ * always plans the MFMA engine (DSW_ERR_DTYPE with DSW_FLAG_VALU_GEMV).
+ * Returns DSW_ERR_* on invalid sizes or when no plan fits. */
 int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int w2_dtype,
                      unsigned flags, dsw_plan_info* out);
 

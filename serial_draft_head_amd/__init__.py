@@ -66,7 +66,8 @@ class PlanInfo(ctypes.Structure):
                 ("stream_bytes", ctypes.c_longlong), ("workspace_bytes", ctypes.c_longlong),
                 ("engine", ctypes.c_int), ("tiles_per_wave", ctypes.c_int),
                 ("reg_tiles", ctypes.c_int), ("lds_tiles", ctypes.c_int),
-                ("max_tiles", ctypes.c_int), ("static_lds_bytes", ctypes.c_int)]
+                ("max_tiles", ctypes.c_int), ("static_lds_bytes", ctypes.c_int),
+                ("w2_dtype", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

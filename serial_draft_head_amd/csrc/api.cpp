@@ -12,11 +12,13 @@
 extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile);
 extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs, or nullptr.
 const void* kernel_for(const dsw_plan_info& pl) {
     if (pl.engine == DSW_ENGINE_VALU) return dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile);
+    if (pl.w2_dtype == DSW_INT8) return dsw_internal_mfma_i8_kernel(pl.batch_tile, pl.reg_tiles, pl.max_tiles);
     if (pl.batch_tile == 4) return dsw_internal_mfma_kernel_b4(pl.reg_tiles, pl.max_tiles);
     if (pl.batch_tile == 16) return dsw_internal_mfma_kernel_b16(pl.reg_tiles, pl.max_tiles);
     return nullptr;
@@ -96,7 +98,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     if (!out) return DSW_ERR_NULL;
     *out = nullptr;
     if (r != dsw::kRank) return DSW_ERR_RANK;
-    if (w2_dtype != DSW_BF16) return DSW_ERR_DTYPE;
+    if (w2_dtype != DSW_BF16 && w2_dtype != DSW_INT8) return DSW_ERR_DTYPE;
     if (V < 1) return DSW_ERR_VOCAB;
     if (gamma_max < 1) return DSW_ERR_GAMMA;
     if (B_max < 1 || B_max > 16) return DSW_ERR_BATCH;

@@ -39,14 +39,17 @@ static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 
 // ---- MFMA engine ----------------------------------------------------------
 // (register tiles, tiles per wave) shapes compiled for each batch tile; must
-// match DSW_MFMA_SHAPES in walk_mfma.h.
+// match DSW_MFMA_SHAPES in walk_kernel.h.
 static const int kShapes[][2] = {{2, 2}, {4, 4}, {8, 8}, {8, 10}, {8, 16}};
+// int8 rows (DSW_MFMA_I8_SHAPES): a tile row takes half the registers
+static const int kShapesI8[][2] = {{4, 4}, {8, 8}, {16, 16}};
 static const int kStreamShape[2] = {0, 16};
 static int mfma_tile_for(int B) { return B <= 4 ? 4 : 16; }
-// Upper bound of walk_mfma's static LDS for (batch tile, tiles per wave).
-static int mfma_static_lds(int nb, int max_tiles) {
+// Upper bound of the MFMA kernel's static LDS for (batch tile, tiles per
+// wave, int8 rows with their fp32 scales).
+static int mfma_static_lds(int nb, int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
-    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96;
+    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0);
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -58,14 +61,22 @@ static int tile_rows(int R, int TW, int w, int j) {
     return n <= 0 ? 0 : (n < kTileRows ? n : kTileRows);
 }
 
-static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int grid, int R,
+static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int grid, int R, bool i8,
                      dsw_plan_info* out) {
     const int tiles = ceil_div(R, kTileRows);
     const int TW = ceil_div(tiles, 4);
+    const int tile_bytes = i8 ? kTileBytes / 2 : kTileBytes;
     int reg_t = -1, max_t = -1;
     if (flags & DSW_FLAG_FORCE_STREAM) {
         reg_t = kStreamShape[0];
         max_t = kStreamShape[1];
+    } else if (i8) {
+        for (const auto& sh : kShapesI8)
+            if (sh[1] >= TW) {
+                reg_t = sh[0];
+                max_t = sh[1];
+                break;
+            }
     } else {
         for (const auto& sh : kShapes)
             if (sh[1] >= TW) {
@@ -76,7 +87,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
     const int nb = mfma_tile_for(B);
-    const int lds_static = mfma_static_lds(nb, max_t);
+    const int lds_static = mfma_static_lds(nb, max_t, i8);
     int avail = dev->max_lds_per_block - lds_static;
     if (avail < 0) return DSW_ERR_PLAN;
 
@@ -97,7 +108,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     int LT = TW - reg_t;
     if (LT < 0) LT = 0;
     if (flags & DSW_FLAG_FORCE_STREAM) LT = 0;
-    while (LT > 0 && slots(LT) * kTileBytes > avail) --LT;
+    while (LT > 0 && slots(LT) * tile_bytes > avail) --LT;
 
     int reg_rows = 0, lds_rows = 0, stream_rows = 0;
     for (int w = 0; w < 4; ++w)
@@ -108,11 +119,11 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
             else stream_rows += n;
         }
 
-    int lds_bytes = slots(LT) * kTileBytes;
+    int lds_bytes = slots(LT) * tile_bytes;
     const int half = dev->lds_bytes_per_cu / 2 + 1024 - lds_static;  // one workgroup per CU
     if (lds_bytes < half) lds_bytes = half;
     if (lds_bytes > avail) lds_bytes = avail;
-    if (lds_bytes < slots(LT) * kTileBytes) return DSW_ERR_PLAN;
+    if (lds_bytes < slots(LT) * tile_bytes) return DSW_ERR_PLAN;
 
     out->engine = DSW_ENGINE_MFMA;
     out->path = stream_rows > 0 ? DSW_PATH_PARTIAL : DSW_PATH_RESIDENT;
@@ -182,7 +193,9 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (!dev || !out) return DSW_ERR_NULL;
     memset(out, 0, sizeof(*out));
     if (r != kRank) return DSW_ERR_RANK;
-    if (w2_dtype != DSW_BF16) return DSW_ERR_DTYPE;
+    if (w2_dtype != DSW_BF16 && w2_dtype != DSW_INT8) return DSW_ERR_DTYPE;
+    const bool i8 = w2_dtype == DSW_INT8;
+    if (i8 && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_DTYPE;  // int8 runs on the MFMA engine
     if (V < 1 || V > (1 << 20)) return DSW_ERR_VOCAB;  // row ids live in 20 key bits
     if (gamma < 0) return DSW_ERR_GAMMA;
     if (B < 0 || B > kMaxBatchPersistent) return DSW_ERR_BATCH;
@@ -193,16 +206,17 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (rows > 4 * 16 * kTileRows) return DSW_ERR_VOCAB;  // 4 waves x 16 tiles x 16 rows
     if ((flags & DSW_FLAG_VALU_GEMV) && (flags & DSW_FLAG_MFMA_GEMV)) return DSW_ERR_ARG;
     const int R = (int)rows;
-    // engine: forced by a flag, else VALU for a single request, MFMA for more
+    // engine: forced by a flag, else VALU for a single bf16 request, MFMA otherwise
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
-    if (!(flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV))) valu = B <= 1;
+    if (!(flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV))) valu = B <= 1 && !i8;
     const int rc = valu ? plan_valu(dev, B, flags, grid, R, out)
-                        : plan_mfma(dev, V, B, flags, grid, R, out);
+                        : plan_mfma(dev, V, B, flags, grid, R, i8, out);
     if (rc != DSW_OK) {
         memset(out, 0, sizeof(*out));
         return rc;
     }
-    const int row_bytes = kRank * 2;
+    out->w2_dtype = w2_dtype;
+    const int row_bytes = i8 ? kRank : kRank * 2;
     long long onchip = 0, streamed = 0;
     // every shard but the last is full; shards beyond V are empty
     for (int c = 0; c < grid; ++c) {

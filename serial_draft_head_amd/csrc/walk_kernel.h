@@ -23,6 +23,10 @@
 //     no extra matrix work (section "B200: the bf16 table fits on chip":
 //     batching is almost free on the tensor cores).  Each request's results
 //     land in one 16-lane DPP row.
+// int8 weights (MFMA engine): one fp32 scale per row; each lane widens its
+//   int8 codes to bf16 (exact: |q| <= 127 needs 7 significant bits) before the
+//   MFMA, and the shard bias is bf16(scale * fp32 dot) (the int8-plus-row-scale
+//   table of section "V = 248,320: 62% on chip, the rest streamed").
 // Both engines round twice to bf16 (bias, then base + bias) and reduce their
 // rows to workgroup-local keys {order-preserving bf16 logit, ~row}, so equal
 // logits resolve to the smallest id (section "The idea").
@@ -36,6 +40,8 @@
 // the token and publishes it through a token mailbox (vLLM PR #64442,
 // "Details": block masses, then a token inside the block).
 #pragma once
+#include <type_traits>
+
 #include "walk_device.h"
 
 namespace dsw {
@@ -64,14 +70,34 @@ __device__ __forceinline__ unsigned long long global_key(uint32_t lk, int v0) {
     return ((unsigned long long)(lk >> 16) << kIdxBits) | (unsigned long long)(kIdxMask - v);
 }
 
-// Pin a value in registers: the compiler may not re-load it from memory later.
-#define DSW_PIN4(v_) asm volatile("" : "+a"((v_).x), "+a"((v_).y), "+a"((v_).z), "+a"((v_).w))
+// Pin a weight in AGPRs: the compiler may not re-load it from memory later.
+__device__ __forceinline__ void pin_agpr(uint4& v) {
+    asm volatile("" : "+a"(v.x), "+a"(v.y), "+a"(v.z), "+a"(v.w));
+}
+__device__ __forceinline__ void pin_agpr(uint2& v) { asm volatile("" : "+a"(v.x), "+a"(v.y)); }
 
-template <int ENGINE, int A, int M, int NB>
+// One K block of a lane's tile row as the MFMA's 8 bf16 values.
+__device__ __forceinline__ uint4 as_bf16x8(const uint4& w) { return w; }
+// Signed byte `i` of w as an exact fp32 value.
+__device__ __forceinline__ float i8_at(uint32_t w, int i) { return (float)(int)(int8_t)(w >> (8 * i)); }
+// Two fp32 values with zero low halves as a bf16 pair (lo in the low half).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ uint4 as_bf16x8(const uint2& q) {
+    return make_uint4(bf16_pair(i8_at(q.x, 0), i8_at(q.x, 1)), bf16_pair(i8_at(q.x, 2), i8_at(q.x, 3)),
+                      bf16_pair(i8_at(q.y, 0), i8_at(q.y, 1)), bf16_pair(i8_at(q.y, 2), i8_at(q.y, 3)));
+}
+
+template <int ENGINE, int A, int M, int NB, int DT = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
+    constexpr bool kI8 = DT == 1;  // int8 rows + fp32 row scales
+    static_assert(!kI8 || kMfma, "int8 weights run on the MFMA engine");
+    // one K block of 8 weights of a lane's tile row (MFMA), or 16 bytes of a row (VALU)
+    using WT = typename std::conditional<kI8, uint2, uint4>::type;
     static_assert(NB == 1 || NB == 4 || NB == 16, "batch tile");
-    static_assert(!kMfma || (NB >= 4 && A <= M && A <= kMaxRegTiles), "MFMA shape");
+    static_assert(!kMfma || (NB >= 4 && A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles), "MFMA shape");
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
     constexpr int RPAD = kMfma ? M * 4 * kTileRows : kMaxSlots * kBlock;  // rows per shard, bound
     constexpr int CHMAX = (RPAD + kBlock - 1) / kBlock;                    // scan rows per thread
@@ -81,6 +107,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 
     __shared__ uint4 s_u[NB * US];
     __shared__ uint16_t s_base[kMfma ? NB * RPAD : 1];
+    __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ uint16_t s_logit[NB * RPAD];
     __shared__ uint32_t s_wbest[4][NB];
     __shared__ unsigned long long s_red64[4][NB];
@@ -102,7 +129,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = t >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // provably wave-uniform
     const int g = lane >> 4;  // MFMA: DPP row holding requests 4g .. 4g+3
     const int n = lane & 15;  // MFMA: row within a tile
     const int c = blockIdx.x;
@@ -112,7 +139,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     const int gamma = p.gamma;
     const int v0 = c * p.rows_per_wg;
     const int nrows = max(0, min(V, v0 + p.rows_per_wg) - v0);
-    const uint4* __restrict__ W2 = reinterpret_cast<const uint4*>(p.W2);
+    const WT* __restrict__ W2 = reinterpret_cast<const WT*>(p.W2);
+    WT* s_wt = reinterpret_cast<WT*>(s_w);
     const uint4* __restrict__ W1 = reinterpret_cast<const uint4*>(p.W1);
     const uint16_t* __restrict__ base = p.base;
     unsigned* status = p.ws.status;
@@ -154,27 +182,24 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     for (int j = t; j < NB * US; j += kBlock) s_u[j] = make_uint4(0u, 0u, 0u, 0u);
 
     // ---- entry: this workgroup's shard on chip -------------------------
-    uint4 wr[A > 0 ? A : 1][kMfma ? 8 : kRowChunks];
+    WT wr[A > 0 ? A : 1][kMfma ? 8 : kRowChunks];
     uint32_t bs[kMfma ? 1 : NB][kMfma ? 1 : kMaxSlots];  // VALU: base logits of the lane's rows
     if constexpr (kMfma) {
 #pragma unroll
         for (int j = 0; j < A; ++j) {
-            const int r = wrow0 + j * kTileRows + n;
-            if (j < nt_w && r < nrows) {
-                const uint4* src = W2 + (size_t)(v0 + r) * kRowChunks + g;
+            // rows outside the shard load some valid row instead (no second,
+            // zeroed copy of the registers); their results are never used
+            const int row = min(v0 + wrow0 + j * kTileRows + n, V - 1);
+            const WT* src = W2 + (size_t)row * kRowChunks + g;
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
-            } else {
+            for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) wr[j][kb] = make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb) DSW_PIN4(wr[j][kb]);
+            for (int kb = 0; kb < 8; ++kb) pin_agpr(wr[j][kb]);
         }
         // LDS tiles: 8 loads per thread in flight before their stores; only
         // tiles that exist in this shard have an LDS slot
         for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
-            uint4 v[8];
+            WT v[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int idx = i0 + q * kBlock + t;
@@ -182,16 +207,18 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int ws = s / max(LT, 1);
                 const int j = A + (s - ws * LT);
                 const int r = ws * TW * kTileRows + j * kTileRows + (ln & 15);
-                v[q] = make_uint4(0u, 0u, 0u, 0u);
+                v[q] = WT{};
                 if (idx < 4 * LT * 512 && j < TW && r < nrows)
                     v[q] = W2[(size_t)(v0 + r) * kRowChunks + kb * 4 + (ln >> 4)];
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int idx = i0 + q * kBlock + t;
-                if (idx < 4 * LT * 512) s_w[idx] = v[q];
+                if (idx < 4 * LT * 512) s_wt[idx] = v[q];
             }
         }
+        if constexpr (kI8)
+            for (int r = t; r < RPAD; r += kBlock) s_scale[r] = r < nrows ? p.w2_scale[v0 + r] : 0.0f;
         for (int i0 = 0; i0 < NB * RPAD; i0 += 8 * kBlock) {
             uint16_t v[8];
 #pragma unroll
@@ -213,7 +240,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         for (int s = 0; s < A; ++s) {
             const int i = s * kBlock + t;
             if (i < reg_rows) {
-                const uint4* src = W2 + (size_t)(v0 + i) * kRowChunks;
+                const WT* src = W2 + (size_t)(v0 + i) * kRowChunks;
 #pragma unroll
                 for (int ch = 0; ch < kRowChunks; ++ch) wr[s][ch] = src[ch];
             } else {
@@ -301,24 +328,37 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
             if (4 * g + i < B && r_ < nrows) {                                                   \
                 const int e_ = lofs + i * RPAD + (j) * kTileRows;                                \
-                const uint32_t bias_ = f32_to_bf16((dv)[i]);                                     \
+                const uint32_t bias_ = f32_to_bf16(kI8 ? s_scale[r_] * (dv)[i] : (dv)[i]);      \
                 const uint32_t lb_ = f32_to_bf16(bf16_to_f32(s_base[e_]) + bf16_to_f32(bias_));  \
                 best[i] = max(best[i], local_key(lb_, r_));                                      \
                 s_logit[e_] = (uint16_t)lb_;                                                     \
             }                                                                                    \
         }                                                                                        \
     } while (0)
-            f32x4_t d[A > 0 ? A : 1];
+            // Register tiles two at a time, each pair's epilogue right after its
+            // MFMAs, so that few accumulators and widened operands are live.
+            // Tiles beyond nt_w hold other rows: multiplying them keeps the MFMA
+            // sequence free of branches, and their results are dropped.
 #pragma unroll
-            for (int j = 0; j < (A > 0 ? A : 1); ++j) d[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int j0 = 0; j0 < A; j0 += 2) {
+                f32x4_t d0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+                if constexpr (kI8) {
+                    // opaque every step, so that the widening to bf16 is not
+                    // hoisted out of the walk (that would hold twice the registers)
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+                    for (int j = j0; j < j0 + 2 && j < A; ++j)
 #pragma unroll
-                for (int j = 0; j < A; ++j)
-                    if (j < nt_w) d[j] = mfma_tile(a[kb], wr[j][kb], d[j]);
+                        for (int kb = 0; kb < 8; ++kb) pin_agpr(wr[j][kb]);
+                }
 #pragma unroll
-            for (int j = 0; j < A; ++j)
-                if (j < nt_w) DSW_EPI_MFMA(d[j], j);
+                for (int kb = 0; kb < 8; ++kb) {
+                    d0 = mfma_tile(a[kb], as_bf16x8(wr[j0][kb]), d0);
+                    if (j0 + 1 < A) d1 = mfma_tile(a[kb], as_bf16x8(wr[j0 + 1][kb]), d1);
+                }
+                if (j0 < nt_w) DSW_EPI_MFMA(d0, j0);
+                if (j0 + 1 < A && j0 + 1 < nt_w) DSW_EPI_MFMA(d1, j0 + 1);
+                __builtin_amdgcn_sched_barrier(0);  // keep the pairs apart
+            }
 #pragma unroll 1
             for (int j = A; j < M; ++j) {
                 if (j < nt_w) {
@@ -326,14 +366,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     if (j - A < LT) {
                         const int sb = (wave * LT + (j - A)) * 512 + lane;
 #pragma unroll
-                        for (int kb = 0; kb < 8; ++kb) dd = mfma_tile(a[kb], s_w[sb + kb * 64], dd);
+                        for (int kb = 0; kb < 8; ++kb) dd = mfma_tile(a[kb], as_bf16x8(s_wt[sb + kb * 64]), dd);
                     } else {
                         const int r = wrow0 + j * kTileRows + n;
                         const bool ok = r < nrows;
-                        const uint4* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks + g;
+                        const WT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks + g;
 #pragma unroll
-                        for (int kb = 0; kb < 8; ++kb)
-                            dd = mfma_tile(a[kb], ok ? src[kb * 4] : make_uint4(0u, 0u, 0u, 0u), dd);
+                        for (int kb = 0; kb < 8; ++kb) dd = mfma_tile(a[kb], as_bf16x8(ok ? src[kb * 4] : WT{}), dd);
                     }
                     DSW_EPI_MFMA(dd, j);
                 }
@@ -379,7 +418,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                                     if (NB == 1 || b < B) acc[b][s] = dot8(w4[q], s_u[b * US + c0 + q], acc[b][s]);
                         }
                     } else {
-                        const uint4* src = W2 + (size_t)(v0 + i) * kRowChunks;
+                        const WT* src = W2 + (size_t)(v0 + i) * kRowChunks;
 #pragma unroll 1
                         for (int c0 = 0; c0 < kRowChunks; c0 += kGrp) {
                             uint4 w4[kGrp];
@@ -679,5 +718,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 
 // (register tiles, tiles per wave) shapes of the MFMA engine, per batch tile
 #define DSW_MFMA_SHAPES(X) X(2, 2) X(4, 4) X(8, 8) X(8, 10) X(8, 16) X(0, 16)
+// the same for int8 weights (a tile row is half as large)
+#define DSW_MFMA_I8_SHAPES(X) X(4, 4) X(8, 8) X(16, 16) X(0, 16)
 
 }  // namespace dsw

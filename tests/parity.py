@@ -4,7 +4,8 @@ Rules (the walk is exact by definition; the GPU only sums in fp32 in another
 order):
   * logits: each GPU logit lies in [bf16(base + bf16(acc - E)), bf16(base + bf16(acc + E))]
     where acc is the exact dot product and E = g_r * sum_j |w_j u_j| bounds
-    any fp32 summation of r = 256 terms (g_r = r 2^-24 / (1 - r 2^-24)); and it
+    any fp32 summation of r = 256 terms (g_r = r 2^-24 / (1 - r 2^-24)), plus
+    2^-24 (|acc| + E) for int8 rows, whose fp32 sum is then scaled in fp32; and it
     is within one bf16 ulp of the oracle's logit (the ulp taken at the largest
     of |oracle logit|, |GPU logit| and |bias|, so that cancellation in
     base + bias cannot fake a miss), except where that fp32 interval itself
@@ -63,6 +64,8 @@ def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, s
             u = w.W1[prev]
             acc = w.W2 @ u
             E = GAMMA_R * (w.W2abs @ np.abs(u))
+            if w.Q is not None:  # the fp32 product scale * sum rounds once more
+                E = E + 2.0 ** -24 * (np.abs(acc) + E)
             bias = oracle.rne_bf16(acc)[0]
             lo = oracle.rne_bf16(acc - E)[0]
             hi = oracle.rne_bf16(acc + E)[0]

@@ -139,6 +139,27 @@ def test_planner_choices_on_mi355x_shapes(dsw):
     assert (v3.reg_slots, v3.lds_rows, v3.stream_rows) == (3, 202, 0)
 
 
+def test_planner_int8_rows(dsw):
+    d = fake_device(dsw)
+    pick = lambda p: (p.engine, p.tiles_per_wave, p.reg_tiles, p.lds_tiles, p.stream_rows)  # noqa: E731
+    # int8 rows take half the registers: V = 248,320 is fully resident at 16 tiles per wave
+    c3 = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8)
+    assert pick(c3) == (1, 16, 16, 0, 0) and c3.path == 0 and c3.w2_dtype == dsw.INT8
+    assert c3.onchip_bytes == 248_320 * 256 and c3.stream_bytes == 0
+    assert pick(dsw.plan(d, 248_320, 16, 16, w2_dtype=dsw.INT8)) == (1, 16, 16, 0, 0)
+    # smaller vocabularies take the smaller compiled shapes
+    assert dsw.plan(d, 60_000, 7, 4, w2_dtype=dsw.INT8).reg_tiles == 4
+    assert dsw.plan(d, 129_280, 7, 4, w2_dtype=dsw.INT8).reg_tiles == 8
+    # streaming everything works for int8 too
+    s = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=1)
+    assert (s.reg_rows, s.lds_rows, s.stream_rows, s.stream_bytes) == (0, 0, 970, 248_320 * 256)
+    # int8 has no VALU engine
+    with pytest.raises(dsw.DswError) as e:
+        dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=4)
+    assert e.value.code == -5
+    assert dsw.plan(d, 248_320, 16, 1).w2_dtype == dsw.BF16
+
+
 def test_planner_stream_fallback_on_small_devices(dsw):
     # 32 KiB of LDS beside the 4-request kernel's staging leaves no room for
     # the two LDS tiles per wave that V = 151,936 needs: those rows stream

@@ -41,9 +41,10 @@ def round_dev(inp):
             torch.from_numpy(inp["T"]).to(DEV), torch.from_numpy(inp["uniforms"]).to(DEV))
 
 
-def run(walker, W1d, W2d, inp, want_logits=True):
+def run(walker, W1d, W2d, inp, want_logits=True, scale=None):
     base, anchor, T, uni = round_dev(inp)
-    tokens, logits = walker.walk(W1d, W2d, base, anchor, T, uni, want_logits=want_logits)
+    tokens, logits = walker.walk(W1d, W2d, base, anchor, T, uni, w2_scale=scale,
+                                 want_logits=want_logits)
     torch.cuda.synchronize()
     st = walker.status()
     assert st == 0, f"device status {st}"
@@ -254,3 +255,70 @@ def test_every_mfma_shape(dsw, V, shape, B):
         toks, lg = run(walker, W1d, W2d, inp)
         rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg)
         say(temps, rep)
+
+
+# int8 rows + fp32 row scales: one vocabulary per compiled int8 shape, plus
+# ragged sizes; the harness quantizes once and both sides consume (q, scale).
+I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),
+             (248_320, (16, 16))]
+
+
+def int8_dev(Q, scale):
+    return torch.from_numpy(np.ascontiguousarray(Q)).to(DEV), torch.from_numpy(scale).to(DEV)
+
+
+@pytest.mark.parametrize("B", [1, 3, 13])
+@pytest.mark.parametrize("V,shape", I8_VOCABS)
+def test_int8_rows(dsw, V, shape, B):
+    say(f"int8 shape {shape} V={V} B={B}")
+    W1, W2 = workloads.weights(3, V=V)
+    Q, sc = workloads.quantize_int8(W2)
+    w = parity.Weights(W1, Q=Q, scale=sc)
+    walker = dsw.Walker(V, gamma_max=4, B_max=16, w2_dtype=dsw.INT8)
+    pl = walker.query_plan(B)
+    assert (pl.engine, pl.reg_tiles, pl.max_tiles, pl.stream_rows) == (1, *shape, 0)
+    W1d = bf16_dev(W1)
+    Qd, sd = int8_dev(Q, sc)
+    for temps in ("greedy", "mixed"):
+        inp = workloads.round_inputs(3, 11, B=B, gamma=3, V=V, temps=temps)
+        toks, lg = run(walker, W1d, Qd, inp, scale=sd)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg)
+        say(temps, rep)
+    walker.close()
+
+
+def test_int8_force_stream_is_bit_identical(dsw):
+    V = 100_003
+    say(f"int8 streamed vs resident V={V}")
+    W1, W2 = workloads.weights(3, V=V)
+    Q, sc = workloads.quantize_int8(W2)
+    W1d = bf16_dev(W1)
+    Qd, sd = int8_dev(Q, sc)
+    res = dsw.Walker(V, gamma_max=5, B_max=5, w2_dtype=dsw.INT8)
+    stm = dsw.Walker(V, gamma_max=5, B_max=5, w2_dtype=dsw.INT8, flags=dsw.FLAG_FORCE_STREAM)
+    assert stm.query_plan(5).stream_rows == stm.query_plan(5).rows_per_wg
+    for rnd in range(2):
+        inp = workloads.round_inputs(3, 30 + rnd, B=5, gamma=5, V=V, temps="mixed")
+        a = run(res, W1d, Qd, inp, scale=sd)
+        b = run(stm, W1d, Qd, inp, scale=sd)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_int8_full_size_large_vocab(dsw, B):
+    wl = workloads.WORKLOADS[3]
+    say(f"int8 full size {wl.name} B={B}")
+    W1, W2 = workloads.weights(3)
+    Q, sc = workloads.quantize_int8(W2)
+    w = parity.Weights(W1, Q=Q, scale=sc)
+    walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=B, w2_dtype=dsw.INT8)
+    say("plan", walker.query_plan(B).as_dict())
+    W1d = bf16_dev(W1)
+    Qd, sd = int8_dev(Q, sc)
+    for rnd in range(2):
+        inp = workloads.round_inputs(3, rnd, B=B, temps="cycle" if B == 1 else "mixed")
+        toks, lg = run(walker, W1d, Qd, inp, scale=sd)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 steps=[0, 1, wl.gamma - 1])
+        say("round", rnd, rep)
+    walker.close()
