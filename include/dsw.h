@@ -91,6 +91,10 @@ extern "C" {
 #define DSW_FLAG_MFMA_GEMV 8u    /* force the MFMA shard GEMV.  Without either flag
                                     one request per call takes the VALU engine and
                                     more take the MFMA engine (measured faster).     */
+#define DSW_FLAG_BATCHED 16u     /* use the batched kernel for every batch size.  It
+                                    serves B > 16 always: requests in groups of 16
+                                    on the MFMA engine, one owner workgroup per
+                                    request for the exchange                   */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -130,6 +134,8 @@ typedef struct dsw_plan_info {
     int max_tiles;           /* MFMA: compiled tiles-per-wave capacity          */
     int static_lds_bytes;    /* the kernel's static LDS (an upper bound)        */
     int w2_dtype;            /* DSW_BF16 or DSW_INT8 (int8: MFMA engine only)    */
+    int ring_slots;          /* batched kernel: LDS ring slots (groups in flight) */
+    int rows_pad;            /* batched kernel: shard rows padded to 128          */
 } dsw_plan_info;
 
 typedef struct dsw_handle* dsw_handle_t;
@@ -150,7 +156,7 @@ int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int
                      unsigned flags, dsw_plan_info* out);
 
 /* Create a handle for walks on `device` with vocabulary V, rank r (must be
- * 256), at most gamma_max steps and B_max requests per call, and W2 stored
+ * 256), at most gamma_max steps and B_max (1 .. 256) requests per call, and W2 stored
  * as w2_dtype.  Allocates and zeroes the device workspace (cross-workgroup
  * mailboxes, arrival counters, a round counter and a status word); the handle
  * owns it.  The calling thread's current device is left unchanged. */

@@ -35,6 +35,7 @@ FLAG_FORCE_STREAM = 1
 FLAG_COOPERATIVE = 2
 FLAG_VALU_GEMV = 4
 FLAG_MFMA_GEMV = 8
+FLAG_BATCHED = 16
 ENGINE_VALU, ENGINE_MFMA = 0, 1
 RANK = 256
 
@@ -67,7 +68,8 @@ class PlanInfo(ctypes.Structure):
                 ("engine", ctypes.c_int), ("tiles_per_wave", ctypes.c_int),
                 ("reg_tiles", ctypes.c_int), ("lds_tiles", ctypes.c_int),
                 ("max_tiles", ctypes.c_int), ("static_lds_bytes", ctypes.c_int),
-                ("w2_dtype", ctypes.c_int)]
+                ("w2_dtype", ctypes.c_int), ("ring_slots", ctypes.c_int),
+                ("rows_pad", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -13,11 +13,13 @@ extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile);
 extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs, or nullptr.
 const void* kernel_for(const dsw_plan_info& pl) {
     if (pl.engine == DSW_ENGINE_VALU) return dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile);
+    if (pl.batch_tile == dsw::kMaxBatch) return dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
     if (pl.w2_dtype == DSW_INT8) return dsw_internal_mfma_i8_kernel(pl.batch_tile, pl.reg_tiles, pl.max_tiles);
     if (pl.batch_tile == 4) return dsw_internal_mfma_kernel_b4(pl.reg_tiles, pl.max_tiles);
     if (pl.batch_tile == 16) return dsw_internal_mfma_kernel_b16(pl.reg_tiles, pl.max_tiles);
@@ -101,7 +103,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     if (w2_dtype != DSW_BF16 && w2_dtype != DSW_INT8) return DSW_ERR_DTYPE;
     if (V < 1) return DSW_ERR_VOCAB;
     if (gamma_max < 1) return DSW_ERR_GAMMA;
-    if (B_max < 1 || B_max > 16) return DSW_ERR_BATCH;
+    if (B_max < 1 || B_max > dsw::kMaxBatch) return DSW_ERR_BATCH;
     dsw_devinfo dev;
     int rc = dsw_device_info(device, &dev);
     if (rc) return rc;
@@ -135,6 +137,10 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.tok_mail = reinterpret_cast<unsigned long long*>(h->ws_mem + L.tok_mail);
     h->ws.round_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.round_ctr);
     h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.status);
+    h->ws.bkey = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bkey);
+    h->ws.bsum = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bsum);
+    h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
+    h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
     if (clear_workspace(h) != DSW_OK) {
         (void)hipFree(h->ws_mem);
         delete h;
@@ -231,6 +237,9 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     p.lds_rows = plan.lds_rows;
     p.tiles_per_wave = plan.tiles_per_wave;
     p.lds_tiles = plan.lds_tiles;
+    p.rows_pad = plan.rows_pad;
+    p.ring = plan.ring_slots;
+    p.aligned = (h->V % 8) == 0;
     p.spin_limit = kSpinLimit;
     p.trace = nullptr;
     if (h->trace != nullptr &&

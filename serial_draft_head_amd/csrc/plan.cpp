@@ -144,6 +144,89 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     return DSW_OK;
 }
 
+// ---- batched kernel (walk_batched.h) ---------------------------------------
+// (register tiles, tiles per wave); must match DSW_BATCHED_SHAPES and
+// DSW_BATCHED_I8_SHAPES.
+static const int kBShapes[][2] = {{4, 4}, {8, 8}, {8, 12}};
+static const int kBShapesI8[][2] = {{8, 8}, {8, 12}};
+static const int kBStreamShape[2] = {0, 12};
+static int batched_static_lds(int max_tiles, bool i8) {
+    const int rpad = max_tiles * 4 * kTileRows;
+    return 4 * kMaxBatch * 4 * 3 + 4 * kMaxBatch * 4 + kMaxGrid * 4 + kMaxBatch * 4 + 2 * rpad +
+           (i8 ? 4 * rpad : 0) + 512;
+}
+static int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+static int plan_batched(const dsw_devinfo* dev, int V, int B, unsigned flags, int grid, bool i8,
+                        dsw_plan_info* out) {
+    const int R = round_up((V + grid - 1) / grid, kTileRows);  // 16-row aligned shards
+    const int Rpad = round_up(R, 128);
+    const int tiles = R / kTileRows;
+    const int TW = ceil_div(tiles, 4);
+    const int tile_bytes = i8 ? kTileBytes / 2 : kTileBytes;
+    int reg_t = -1, max_t = -1;
+    if (flags & DSW_FLAG_FORCE_STREAM) {
+        reg_t = kBStreamShape[0];
+        max_t = kBStreamShape[1];
+    } else if (i8) {
+        for (const auto& sh : kBShapesI8)
+            if (sh[1] >= TW) {
+                reg_t = sh[0];
+                max_t = sh[1];
+                break;
+            }
+    } else {
+        for (const auto& sh : kBShapes)
+            if (sh[1] >= TW) {
+                reg_t = sh[0];
+                max_t = sh[1];
+                break;
+            }
+    }
+    if (max_t < TW) return DSW_ERR_VOCAB;
+    const int lds_static = batched_static_lds(max_t, i8);
+    const int avail = dev->max_lds_per_block - lds_static;
+    const int slot_bytes = 16 * kRowChunks * 16 + 16 * Rpad * 2;  // u rows + base of 16 requests
+    // LDS tiles first (4 waves x LT), then at least two ring slots
+    int LT = TW - reg_t;
+    if (LT < 0) LT = 0;
+    if (flags & DSW_FLAG_FORCE_STREAM) LT = 0;
+    while (LT > 0 && 4 * LT * tile_bytes + 2 * slot_bytes > avail) --LT;
+    int ring = (avail - 4 * LT * tile_bytes) / slot_bytes;
+    if (ring > 4) ring = 4;
+    if (ring < 2) return DSW_ERR_PLAN;
+
+    int reg_rows = 0, lds_rows = 0, stream_rows = 0;
+    for (int w = 0; w < 4; ++w)
+        for (int j = 0; j < TW; ++j) {
+            const int n = tile_rows(R, TW, w, j);
+            if (j < reg_t) reg_rows += n;
+            else if (j < reg_t + LT) lds_rows += n;
+            else stream_rows += n;
+        }
+    out->engine = DSW_ENGINE_MFMA;
+    out->path = stream_rows > 0 ? DSW_PATH_PARTIAL : DSW_PATH_RESIDENT;
+    out->grid = grid;
+    out->block = kBlock;
+    out->rows_per_wg = R;
+    out->reg_rows = reg_rows;
+    out->lds_rows = lds_rows;
+    out->stream_rows = stream_rows;
+    out->batch_tile = kMaxBatch;
+    int lds_bytes = 4 * LT * tile_bytes + ring * slot_bytes;
+    const int half = dev->lds_bytes_per_cu / 2 + 1024 - lds_static;  // one workgroup per CU
+    if (lds_bytes < half) lds_bytes = half < avail ? half : avail;
+    out->lds_bytes = lds_bytes;
+    out->tiles_per_wave = TW;
+    out->reg_tiles = reg_t;
+    out->lds_tiles = LT;
+    out->max_tiles = max_t;
+    out->static_lds_bytes = lds_static;
+    out->ring_slots = ring;
+    out->rows_pad = Rpad;
+    return DSW_OK;
+}
+
 static int plan_valu(const dsw_devinfo* dev, int B, unsigned flags, int grid, int R,
                      dsw_plan_info* out) {
     if (R > kMaxSlots * kBlock) return DSW_ERR_VOCAB;
@@ -198,7 +281,7 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (i8 && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_DTYPE;  // int8 runs on the MFMA engine
     if (V < 1 || V > (1 << 20)) return DSW_ERR_VOCAB;  // row ids live in 20 key bits
     if (gamma < 0) return DSW_ERR_GAMMA;
-    if (B < 0 || B > kMaxBatchPersistent) return DSW_ERR_BATCH;
+    if (B < 0 || B > kMaxBatch) return DSW_ERR_BATCH;
     if (dev->cu_count < 1 || dev->max_lds_per_block < 1) return DSW_ERR_DEVICE;
 
     const int grid = dev->cu_count < kMaxGrid ? dev->cu_count : kMaxGrid;
@@ -206,23 +289,28 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (rows > 4 * 16 * kTileRows) return DSW_ERR_VOCAB;  // 4 waves x 16 tiles x 16 rows
     if ((flags & DSW_FLAG_VALU_GEMV) && (flags & DSW_FLAG_MFMA_GEMV)) return DSW_ERR_ARG;
     const int R = (int)rows;
-    // engine: forced by a flag, else VALU for a single bf16 request, MFMA otherwise
+    // kernel: the batched one beyond 16 requests (or when asked for); else the
+    // engine forced by a flag, else VALU for a single bf16 request, MFMA otherwise
+    const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
+    if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
     if (!(flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV))) valu = B <= 1 && !i8;
-    const int rc = valu ? plan_valu(dev, B, flags, grid, R, out)
-                        : plan_mfma(dev, V, B, flags, grid, R, i8, out);
+    const int rc = batched ? plan_batched(dev, V, B, flags, grid, i8, out)
+                 : valu    ? plan_valu(dev, B, flags, grid, R, out)
+                           : plan_mfma(dev, V, B, flags, grid, R, i8, out);
     if (rc != DSW_OK) {
         memset(out, 0, sizeof(*out));
         return rc;
     }
     out->w2_dtype = w2_dtype;
     const int row_bytes = i8 ? kRank : kRank * 2;
+    const int Rs = out->rows_per_wg;  // the plan's shard size
     long long onchip = 0, streamed = 0;
     // every shard but the last is full; shards beyond V are empty
     for (int c = 0; c < grid; ++c) {
-        long long n = (long long)V - (long long)c * R;
+        long long n = (long long)V - (long long)c * Rs;
         if (n <= 0) break;
-        if (n > R) n = R;
+        if (n > Rs) n = Rs;
         // a short shard keeps its first rows in the same classes as the first shard
         long long on = out->reg_rows + out->lds_rows;
         if (out->engine == DSW_ENGINE_MFMA) {

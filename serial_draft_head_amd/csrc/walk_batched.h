@@ -1,0 +1,615 @@
+// walk_batched.h -- one persistent launch per round of DSpark's serial Markov
+// draft walk for large batches (up to 256 requests), on gfx950 (MI355X).
+//
+// The per-request computation is the one of walk_kernel.h ("Keeping the Draft
+// Walk on Chip", tie-pilot-qxw.github.io, section "The serial part of a
+// parallel drafter"; sampler of vLLM PR #64442, "Details").  What changes with
+// the batch size (section "B200: the bf16 table fits on chip": batching is
+// almost free for the matrix cores, everything around the GEMV grows):
+//
+// * GEMV: requests go through in groups of 16.  A weight tile is the A operand
+//   of v_mfma_f32_16x16x32_bf16 (16 rows x 32 latent values, the same register
+//   layout as walk_kernel.h) and the u vectors of the group are the B operand,
+//   so lane (n, g) ends with rows 4g .. 4g+3 of a tile for request n: four
+//   adjacent base logits, one 8-byte LDS read.
+// * Streaming: every step reads B * rows * 2 bytes of base logits per shard.
+//   The u rows and base logits of a group go straight from memory into a ring
+//   of LDS slots (global_load_lds_dwordx4), several groups ahead, while the
+//   matrix cores work on the current group; XOR swizzles keep the 16 lanes of
+//   one request column on distinct LDS banks.
+// * Exchange: an all-to-all of B keys per workgroup would read B * 2 KiB per
+//   workgroup and step.  Here request b is owned by workgroup b % G: every
+//   workgroup stores its B key words (and exp-sum words) in one row, the owner
+//   reads column b, and publishes the token (greedy) or the shard whose mass
+//   holds u*Z (sampled).  That shard recomputes its logits of request b (the
+//   weights are still in registers), finds the token, and publishes it.
+//   Greedy steps take two exchanges, sampled steps three.
+#pragma once
+#include "walk_kernel.h"
+
+namespace dsw {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt_vm_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
+
+// Wait until at most n vector-memory instructions of this wave are in flight.
+// No memory access moves across it (a load issued later must not be counted
+// as issued earlier).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    asm volatile("" ::: "memory");
+    switch (n < 0 ? 0 : (n > 31 ? 31 : n)) {
+#define DSW_W(i) \
+    case i: __builtin_amdgcn_s_waitcnt(waitcnt_vm_imm(i)); break;
+        DSW_W(0) DSW_W(1) DSW_W(2) DSW_W(3) DSW_W(4) DSW_W(5) DSW_W(6) DSW_W(7)
+        DSW_W(8) DSW_W(9) DSW_W(10) DSW_W(11) DSW_W(12) DSW_W(13) DSW_W(14) DSW_W(15)
+        DSW_W(16) DSW_W(17) DSW_W(18) DSW_W(19) DSW_W(20) DSW_W(21) DSW_W(22) DSW_W(23)
+        DSW_W(24) DSW_W(25) DSW_W(26) DSW_W(27) DSW_W(28) DSW_W(29) DSW_W(30) DSW_W(31)
+#undef DSW_W
+        default: break;
+    }
+}
+
+// Workgroup barrier that keeps vector-memory loads (and LDS DMA) in flight:
+// this wave's LDS accesses are complete, and the compiler moves no memory
+// access across it.  (__syncthreads would also wait for every outstanding
+// load, which would drain the prefetch ring at every group.)
+__device__ __forceinline__ void barrier_keep_vm() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8 KiB
+constexpr unsigned kDecPending = 1u << 20;             // decision: a shard, not a token
+
+template <int A, int M, int DT>
+__global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
+    constexpr bool kI8 = DT == 1;
+    using WT = typename std::conditional<kI8, uint2, uint4>::type;
+    static_assert(A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles && (A % 2) == 0, "shape");
+    constexpr int RPAD = M * 4 * kTileRows;  // shard rows, bound
+    constexpr int CHMAX = (RPAD + kBlock - 1) / kBlock;
+    extern __shared__ uint4 s_dyn[];  // [LDS weight tiles][ring slots]
+
+    __shared__ uint32_t s_rkey[4][kMaxBatch];  // per wave and request: local key
+    __shared__ float s_rm[4][kMaxBatch];       // per wave: max logit (sampled requests)
+    __shared__ float s_rs[4][kMaxBatch];       // per wave: exp-sum relative to s_rm
+    __shared__ int s_prev[kMaxBatch];
+    __shared__ int s_next[kMaxBatch];
+    __shared__ float s_T[kMaxBatch];
+    __shared__ unsigned s_dec[kMaxBatch];
+    __shared__ float s_S[kMaxGrid];
+    __shared__ uint16_t s_tl[RPAD];            // one request's recomputed shard logits
+    __shared__ float s_scale[kI8 ? RPAD : 1];
+    __shared__ int s_tasks[kMaxBatch];
+    __shared__ unsigned long long s_red64[4];
+    __shared__ float s_redf[4];
+    __shared__ int s_redi[4];
+    __shared__ int s_redj[4];
+    __shared__ int s_own;
+    __shared__ float s_pex;
+    __shared__ float s_tgt;
+    __shared__ int s_ntask;
+    __shared__ unsigned s_round;
+    __shared__ int s_abort;
+    __shared__ int s_any_samp;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // provably wave-uniform
+    const int g = lane >> 4;  // rows 4g .. 4g+3 of a tile
+    const int n = lane & 15;  // request column within a group
+    const int c = blockIdx.x;
+    const int G = gridDim.x;
+    const int V = p.V;
+    const int B = p.B;
+    const int gamma = p.gamma;
+    const int R = p.rows_per_wg;  // multiple of 16
+    const int Rpad = p.rows_pad;  // multiple of 128
+    const int CPR = Rpad >> 3;    // 16-byte chunks per request row of a base slot
+    const int v0 = c * R;
+    const int nrows = max(0, min(V, v0 + R) - v0);
+    const int TW = p.tiles_per_wave;
+    const int LT = p.lds_tiles;
+    const int wrow0 = wave * TW * kTileRows;
+    const int nt_w = max(0, min(TW, (nrows - wrow0 + kTileRows - 1) / kTileRows));
+    const int NG = (B + kGroup - 1) / kGroup;
+    const int D = p.ring;
+    const bool aligned = p.aligned != 0;
+    const int P = 2 + (aligned ? CPR / 16 : 0);  // DMA instructions per wave and group
+    const WT* __restrict__ W2 = reinterpret_cast<const WT*>(p.W2);
+    const uint4* __restrict__ W1 = reinterpret_cast<const uint4*>(p.W1);
+    const uint16_t* __restrict__ base = p.base;
+    unsigned* status = p.ws.status;
+    WT* s_wt = reinterpret_cast<WT*>(s_dyn);
+    char* ring = reinterpret_cast<char*>(s_dyn) + 4 * LT * 512 * (int)sizeof(WT);
+    const int slot_bytes = kSlotUBytes + kGroup * Rpad * 2;
+
+    if (t == 0) {
+        s_round = ld_agent(p.ws.round_ctr);
+        s_abort = 0;
+        s_any_samp = 0;
+    }
+    __syncthreads();
+    DSW_TRACE(gamma, 0);
+    if (t < B) {
+        int a = p.anchor[t];
+        float temp = p.T[t];
+        if (a < 0 || a >= V) {
+            if (c == 0) latch(status, kStatusToken);
+            a = 0;
+        }
+        if (temp > 0.0f && p.uniforms == nullptr) {
+            if (c == 0) latch(status, kStatusUniforms);
+            temp = 0.0f;
+        }
+        if (!(temp > 0.0f)) temp = 0.0f;
+        s_prev[t] = a;
+        s_T[t] = temp;
+        if (temp > 0.0f) s_any_samp = 1;
+    }
+
+    // ---- entry: this workgroup's shard on chip (as walk_kernel.h) --------
+    WT wr[A > 0 ? A : 1][8];
+#pragma unroll
+    for (int j = 0; j < A; ++j) {
+        const int row = min(v0 + wrow0 + j * kTileRows + n, V - 1);
+        const WT* src = W2 + (size_t)row * kRowChunks + g;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) pin_agpr(wr[j][kb]);
+    }
+    for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
+        WT v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int idx = i0 + q * kBlock + t;
+            const int s = idx >> 9, kb = (idx >> 6) & 7, ln = idx & 63;
+            const int ws = s / max(LT, 1);
+            const int j = A + (s - ws * LT);
+            const int r = ws * TW * kTileRows + j * kTileRows + (ln & 15);
+            v[q] = WT{};
+            if (idx < 4 * LT * 512 && j < TW && r < nrows)
+                v[q] = W2[(size_t)(v0 + r) * kRowChunks + kb * 4 + (ln >> 4)];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int idx = i0 + q * kBlock + t;
+            if (idx < 4 * LT * 512) s_wt[idx] = v[q];
+        }
+    }
+    if constexpr (kI8)
+        for (int r = t; r < RPAD; r += kBlock) s_scale[r] = r < nrows ? p.w2_scale[v0 + r] : 0.0f;
+    __syncthreads();
+    const unsigned round = s_round;
+    const bool any_samp = s_any_samp != 0;
+    const int CH = (nrows + kBlock - 1) / kBlock;
+
+    // MFMA over every tile of this wave with B operand ub[8]; EPI(d, j) gets
+    // the four results (rows 4g .. 4g+3 of tile j, request column n)
+#define DSW_TILES(EPI)                                                                           \
+    do {                                                                                         \
+        _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                                    \
+            f32x4_t d0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;                               \
+            if constexpr (kI8) {                                                                 \
+                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                               \
+                    pin_agpr(wr[j0][kb]);                                                        \
+                    pin_agpr(wr[j0 + 1][kb]);                                                    \
+                }                                                                                \
+            }                                                                                    \
+            _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                   \
+                d0 = mfma_tile(as_bf16x8(wr[j0][kb]), ub[kb], d0);                               \
+                d1 = mfma_tile(as_bf16x8(wr[j0 + 1][kb]), ub[kb], d1);                           \
+            }                                                                                    \
+            if (j0 < nt_w) EPI(d0, j0);                                                          \
+            if (j0 + 1 < nt_w) EPI(d1, j0 + 1);                                                  \
+            __builtin_amdgcn_sched_barrier(0);                                                   \
+        }                                                                                        \
+        _Pragma("unroll 1") for (int j = A; j < nt_w; ++j) {                                     \
+            f32x4_t dd = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                        \
+            if (j - A < LT) {                                                                    \
+                const int sb_ = (wave * LT + (j - A)) * 512 + lane;                              \
+                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
+                    dd = mfma_tile(as_bf16x8(s_wt[sb_ + kb * 64]), ub[kb], dd);                   \
+            } else {                                                                             \
+                const int row_ = min(v0 + wrow0 + j * kTileRows + n, V - 1);                     \
+                const WT* src_ = W2 + (size_t)row_ * kRowChunks + g;                             \
+                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
+                    dd = mfma_tile(as_bf16x8(src_[kb * 4]), ub[kb], dd);                          \
+            }                                                                                    \
+            EPI(dd, j);                                                                          \
+        }                                                                                        \
+    } while (0)
+
+    // ---- the walk --------------------------------------------------------
+    for (int k = 0; k < gamma; ++k) {
+        DSW_TRACE(k, kTrStepStart);
+        const unsigned seq = round * (unsigned)p.gamma_max + (unsigned)k;
+        const unsigned long long epoch = (unsigned long long)(seq % kEpochMod + 1u);
+        const int q = (int)(seq & 1u);
+        unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch;
+        unsigned long long* bsum = p.ws.bsum + (size_t)q * kMaxGrid * kMaxBatch;
+        unsigned long long* bdec = p.ws.bdec + (size_t)q * kMaxBatch;
+        unsigned long long* btok = p.ws.btok + (size_t)q * kMaxBatch;
+
+        // group gq's u rows and base logits into ring slot gq % D.  Each lane
+        // names its own source; the wave's 64 chunks land contiguously.
+#define DSW_ISSUE_GROUP(grp_)                                                                    \
+    do {                                                                                         \
+        const int gq_ = (grp_);                                                                  \
+        char* slot_ = ring + (gq_ % D) * slot_bytes;                                             \
+        _Pragma("unroll") for (int ii = 0; ii < 2; ++ii) {                                       \
+            const int inst_ = wave * 2 + ii;                                                     \
+            const int pos_ = inst_ * 64 + lane;                                                  \
+            const int nn_ = pos_ >> 5, pc_ = pos_ & 31;                                          \
+            const int b_ = min(gq_ * kGroup + nn_, B - 1);                                       \
+            __builtin_amdgcn_global_load_lds(                                                    \
+                (const void*)(W1 + (size_t)s_prev[b_] * kRowChunks + (pc_ ^ nn_)),              \
+                (lds_void_t*)(slot_ + inst_ * 1024), 16, 0, 0);                                  \
+        }                                                                                        \
+        if (aligned) {                                                                           \
+            const int per_ = CPR / 16;                                                           \
+            for (int ii = 0; ii < per_; ++ii) {                                                  \
+                const int inst_ = wave * per_ + ii;                                              \
+                const int pos_ = inst_ * 64 + lane;                                              \
+                const int nn_ = pos_ / CPR, pc_ = pos_ - nn_ * CPR;                              \
+                const int b_ = min(gq_ * kGroup + nn_, B - 1);                                   \
+                const int cr_ = min((v0 >> 3) + (pc_ ^ nn_), (V >> 3) - 1);                      \
+                const uint4* src_ = reinterpret_cast<const uint4*>(base) +                       \
+                                    ((size_t)b_ * gamma + k) * (size_t)(V >> 3) + cr_;           \
+                __builtin_amdgcn_global_load_lds((const void*)src_,                              \
+                                                 (lds_void_t*)(slot_ + kSlotUBytes + inst_ * 1024), \
+                                                 16, 0, 0);                                      \
+            }                                                                                    \
+        } else {                                                                                 \
+            uint16_t* sb_ = reinterpret_cast<uint16_t*>(slot_ + kSlotUBytes);                    \
+            for (int e_ = t; e_ < kGroup * Rpad; e_ += kBlock) {                                 \
+                const int nn_ = e_ / Rpad, r_ = e_ - nn_ * Rpad;                                 \
+                const int b_ = min(gq_ * kGroup + nn_, B - 1);                                   \
+                sb_[(nn_ * CPR + ((r_ >> 3) ^ nn_)) * 8 + (r_ & 7)] =                            \
+                    r_ < nrows ? base[((size_t)b_ * gamma + k) * V + v0 + r_] : (uint16_t)0;     \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
+
+        for (int gq = 0; gq < min(D - 1, NG); ++gq) DSW_ISSUE_GROUP(gq);
+
+        for (int grp = 0; grp < NG; ++grp) {
+            wait_vmcnt(P * min(D - 2, NG - 1 - grp));
+            barrier_keep_vm();
+            if (grp + D - 1 < NG) DSW_ISSUE_GROUP(grp + D - 1);
+            const char* slot = ring + (grp % D) * slot_bytes;
+            const uint4* su = reinterpret_cast<const uint4*>(slot);
+            uint16_t* sb = reinterpret_cast<uint16_t*>(const_cast<char*>(slot) + kSlotUBytes);
+            const int b = grp * kGroup + n;
+            const bool bval = b < B;
+            uint4 ub[8];
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) ub[kb] = su[n * kRowChunks + ((kb * 4 + g) ^ n)];
+            uint32_t best = 0u;
+            // logits land over the base values they came from (the sampled
+            // pass reads them back from there)
+#define DSW_EPI_G(dv, j)                                                                         \
+    do {                                                                                         \
+        const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
+        if (bval && rb_ < nrows) {                                                               \
+            uint2* e_ = reinterpret_cast<uint2*>(sb + (n * CPR + ((rb_ >> 3) ^ n)) * 8 + (rb_ & 7)); \
+            const uint2 bw_ = *e_;                                                               \
+            const uint32_t bb_[4] = {bw_.x & 0xFFFFu, bw_.x >> 16, bw_.y & 0xFFFFu, bw_.y >> 16}; \
+            uint32_t lb_[4];                                                                     \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+                const int r_ = rb_ + i;                                                          \
+                const uint32_t bias_ = f32_to_bf16(kI8 ? s_scale[r_] * (dv)[i] : (dv)[i]);       \
+                lb_[i] = f32_to_bf16(bf16_to_f32(bb_[i]) + bf16_to_f32(bias_));                  \
+                if (r_ < nrows) best = max(best, local_key(lb_[i], r_));                         \
+            }                                                                                    \
+            *e_ = make_uint2(lb_[0] | (lb_[1] << 16), lb_[2] | (lb_[3] << 16));                  \
+            if (p.logits != nullptr) {                                                           \
+                uint16_t* o_ = p.logits + ((size_t)b * gamma + k) * V + v0 + rb_;                \
+                if (aligned && rb_ + 3 < nrows) {                                                \
+                    *reinterpret_cast<uint2*>(o_) = *e_;                                         \
+                } else {                                                                         \
+                    _Pragma("unroll") for (int i = 0; i < 4; ++i) if (rb_ + i < nrows) o_[i] = (uint16_t)lb_[i]; \
+                }                                                                                \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
+            DSW_TILES(DSW_EPI_G);
+#undef DSW_EPI_G
+            // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
+            best = max(best, (uint32_t)__shfl_xor((int)best, 16));
+            best = max(best, (uint32_t)__shfl_xor((int)best, 32));
+            if (g == 0 && bval) s_rkey[wave][b] = best;
+            if (any_samp) {
+                const float Tb = bval ? s_T[b] : 0.0f;
+                const float mw = local_key_logit(best);
+                float sw = 0.0f;
+                if (Tb > 0.0f && best != 0u) {
+#pragma unroll
+                    for (int j = 0; j < M; ++j) {
+                        const int rb = wrow0 + j * kTileRows + 4 * g;
+                        if (j < nt_w && rb < nrows) {
+                            const uint2 lw = *reinterpret_cast<const uint2*>(sb + (n * CPR + ((rb >> 3) ^ n)) * 8 + (rb & 7));
+                            const uint32_t lv[4] = {lw.x & 0xFFFFu, lw.x >> 16, lw.y & 0xFFFFu, lw.y >> 16};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (rb + i < nrows) sw += __expf((bf16_to_f32(lv[i]) - mw) / Tb);
+                        }
+                    }
+                }
+                sw += __shfl_xor(sw, 16);
+                sw += __shfl_xor(sw, 32);
+                if (g == 0 && bval) {
+                    s_rm[wave][b] = mw;
+                    s_rs[wave][b] = sw;
+                }
+            }
+        }
+        __syncthreads();
+        DSW_TRACE(k, kTrGemvDone);
+
+        // ---- post: one key word (and exp-sum word) per request -----------
+        if (t < B) {
+            const uint32_t lk = max(max(s_rkey[0][t], s_rkey[1][t]), max(s_rkey[2][t], s_rkey[3][t]));
+            st_agent64(&bkey[(size_t)c * kMaxBatch + t], (global_key(lk, v0) << 28) | epoch);
+            if (s_T[t] > 0.0f) {
+                const float mc = local_key_logit(lk);
+                float sc = 0.0f;
+                for (int w = 0; w < 4; ++w)
+                    if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __expf((s_rm[w][t] - mc) / s_T[t]);
+                st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
+            }
+        }
+        DSW_TRACE(k, kTrPosted);
+
+        // read column b of every workgroup's row: kw, sw of shard t (t < G)
+#define DSW_READ_COLUMN(b_, kw_, sw_)                                                            \
+    do {                                                                                         \
+        kw_ = 0ull;                                                                              \
+        sw_ = 0.0f;                                                                              \
+        if (t < G) {                                                                             \
+            const bool samp_ = s_T[b_] > 0.0f;                                                   \
+            const unsigned long long* pk_ = &bkey[(size_t)t * kMaxBatch + (b_)];                 \
+            const unsigned long long* ps_ = &bsum[(size_t)t * kMaxBatch + (b_)];                 \
+            unsigned it_ = 0;                                                                    \
+            bool gotk_ = false, gots_ = !samp_;                                                  \
+            for (;;) {                                                                           \
+                if (!gotk_) {                                                                    \
+                    const unsigned long long w_ = ld_agent64(pk_);                               \
+                    if ((w_ & kEpochMod) == epoch) { kw_ = w_ >> 28; gotk_ = true; }             \
+                }                                                                                \
+                if (!gots_) {                                                                    \
+                    const unsigned long long w_ = ld_agent64(ps_);                               \
+                    if ((w_ & kEpochMod) == epoch) { sw_ = __uint_as_float((uint32_t)(w_ >> 32)); gots_ = true; } \
+                }                                                                                \
+                if (gotk_ && gots_) break;                                                       \
+                if (++it_ >= p.spin_limit) { latch(status, kStatusTimeout); s_abort = 1; break; } \
+                if ((it_ & 255u) == 0u && ld_agent(status) != 0u) { s_abort = 1; break; }        \
+                __builtin_amdgcn_s_sleep(1);                                                     \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
+
+        // shard masses S_t of sampled request b_ into s_S, then wave 0 finds
+        // the first shard with positive mass whose prefix exceeds u*Z (else the
+        // last with positive mass): s_own, s_pex (mass before it), s_tgt = u*Z.
+        // Every caller runs this same code on the same words: same results.
+#define DSW_OWNER_SHARD(b_, kw_, sw_, M_)                                                        \
+    do {                                                                                         \
+        s_S[t] = (t < G && kw_ != 0ull) ? sw_ * __expf((key_logit(kw_) - (M_)) / s_T[b_]) : 0.0f; \
+        __syncthreads();                                                                         \
+        if (wave == 0) {                                                                         \
+            const float4 m4_ = reinterpret_cast<const float4*>(s_S)[lane];                       \
+            const float q0_ = m4_.x, q1_ = q0_ + m4_.y, q2_ = q1_ + m4_.z, q3_ = q2_ + m4_.w;    \
+            const float incl_ = wave_incl_scan_dpp(q3_);                                         \
+            const float ex_ = incl_ - q3_;                                                       \
+            const float Z_ = __shfl(incl_, 63);                                                  \
+            const float tgt_ = p.uniforms[(size_t)(b_) * gamma + k] * Z_;                        \
+            const float c4_[4] = {ex_ + q0_, ex_ + q1_, ex_ + q2_, ex_ + q3_};                   \
+            const float w4_[4] = {m4_.x, m4_.y, m4_.z, m4_.w};                                   \
+            uint32_t first_ = 0u, lastp_ = 0u;                                                   \
+            _Pragma("unroll") for (int i = 3; i >= 0; --i) {                                     \
+                if (w4_[i] > 0.0f && c4_[i] > tgt_) first_ = (uint32_t)(4 * lane + i) + 1u;      \
+                if (lastp_ == 0u && w4_[i] > 0.0f) lastp_ = (uint32_t)(4 * lane + i) + 1u;       \
+            }                                                                                    \
+            const uint32_t fmin_ = wave_max_u32(first_ ? 0xFFFFFFFFu - first_ : 0u);             \
+            const uint32_t lmax_ = wave_max_u32(lastp_);                                         \
+            const int own_ = fmin_ ? (int)(0xFFFFFFFFu - fmin_) - 1 : (int)lmax_ - 1;            \
+            const int pj_ = max(own_ - 1, 0);                                                    \
+            const float cj_ = (pj_ & 3) == 0 ? c4_[0] : ((pj_ & 3) == 1 ? c4_[1] : ((pj_ & 3) == 2 ? c4_[2] : c4_[3])); \
+            const float pex_ = __shfl(cj_, pj_ >> 2);                                            \
+            if (lane == 0) {                                                                     \
+                s_own = own_;                                                                    \
+                s_pex = own_ > 0 ? pex_ : 0.0f;                                                  \
+                s_tgt = tgt_;                                                                    \
+            }                                                                                    \
+        }                                                                                        \
+        __syncthreads();                                                                         \
+    } while (0)
+
+        // workgroup max of kw_ into win_ (all threads)
+#define DSW_BLOCK_MAX64(kw_, win_)                                                               \
+    do {                                                                                         \
+        const unsigned long long m_ = wave_max_u64_dpp(kw_);                                     \
+        if (lane == 0) s_red64[wave] = m_;                                                       \
+        __syncthreads();                                                                         \
+        win_ = max(max(s_red64[0], s_red64[1]), max(s_red64[2], s_red64[3]));                    \
+    } while (0)
+
+        // ---- owners: the winner of every request this workgroup owns -------
+        for (int b = c; b < B; b += G) {
+            unsigned long long kw;
+            float sw;
+            DSW_READ_COLUMN(b, kw, sw);
+            unsigned long long win;
+            DSW_BLOCK_MAX64(kw, win);
+            if (s_abort) break;
+            if (!(s_T[b] > 0.0f)) {
+                if (t == 0) {
+                    const int tok = checked_token(key_index(win), V, status);
+                    st_agent64(&bdec[b], ((unsigned long long)(unsigned)tok << 28) | epoch);
+                }
+            } else {
+                DSW_OWNER_SHARD(b, kw, sw, key_logit(win));
+                if (t == 0)
+                    st_agent64(&bdec[b], ((unsigned long long)(kDecPending | (unsigned)max(s_own, 0)) << 28) | epoch);
+            }
+            __syncthreads();
+        }
+        __syncthreads();
+        if (s_abort) break;
+
+        // ---- decisions of every request ----------------------------------
+        if (t == 0) s_ntask = 0;
+        if (t < B) {
+            unsigned it = 0;
+            unsigned long long w = 0ull;
+            bool ok = true;
+            while (((w = ld_agent64(&bdec[t])) & kEpochMod) != epoch) {
+                if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
+                if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (!ok) s_abort = 1;
+            const unsigned d = ok ? (unsigned)(w >> 28) : 0u;
+            s_dec[t] = d;
+            if (!(d & kDecPending)) s_next[t] = checked_token((int)(d & 0xFFFFFu), V, status);
+        }
+        __syncthreads();
+        if (s_abort) break;
+        DSW_TRACE(k, kTrArrived);
+
+        // ---- sampled requests whose token lies in this shard --------------
+        if (any_samp) {
+            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] & 0xFFFFFu) == c)
+                s_tasks[atomicAdd(&s_ntask, 1)] = t;
+            __syncthreads();
+            const int ntask = s_ntask;
+            for (int i = 0; i < ntask; ++i) {
+                const int b = s_tasks[i];
+                const float Tb = s_T[b];
+                unsigned long long kw;
+                float sw;
+                DSW_READ_COLUMN(b, kw, sw);
+                unsigned long long win;
+                DSW_BLOCK_MAX64(kw, win);
+                if (s_abort) break;
+                const float Mg = key_logit(win);
+                DSW_OWNER_SHARD(b, kw, sw, Mg);
+                // this shard's logits of request b, recomputed in its column
+                const int nb = b & (kGroup - 1);
+                const uint4* urow = W1 + (size_t)s_prev[b] * kRowChunks;
+                uint4 ub[8];
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) ub[kb] = (n == nb) ? urow[kb * 4 + g] : make_uint4(0u, 0u, 0u, 0u);
+#define DSW_EPI_T(dv, j)                                                                         \
+    do {                                                                                         \
+        const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
+        if (n == nb) {                                                                           \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+                const int r_ = rb_ + i;                                                          \
+                if (r_ < nrows) {                                                                \
+                    const uint32_t bias_ = f32_to_bf16(kI8 ? s_scale[r_] * (dv)[i] : (dv)[i]);   \
+                    const uint32_t bb_ = base[((size_t)b * gamma + k) * V + v0 + r_];            \
+                    s_tl[r_] = (uint16_t)f32_to_bf16(bf16_to_f32(bb_) + bf16_to_f32(bias_));     \
+                }                                                                                \
+            }                                                                                    \
+        }                                                                                        \
+    } while (0)
+                DSW_TILES(DSW_EPI_T);
+#undef DSW_EPI_T
+                __syncthreads();
+                // rows in vocabulary order, CH consecutive rows per thread
+                const uint32_t lk = max(max(s_rkey[0][b], s_rkey[1][b]), max(s_rkey[2][b], s_rkey[3][b]));
+                const float ml = local_key_logit(lk);
+                const float scale = __expf((ml - Mg) / Tb);
+                float part = 0.0f;
+#pragma unroll
+                for (int rr = 0; rr < CHMAX; ++rr) {
+                    const int r = t * CH + rr;
+                    if (rr < CH && r < nrows) part += __expf((bf16_to_f32(s_tl[r]) - ml) / Tb);
+                }
+                const float incl = wave_incl_scan_dpp(part);
+                if (lane == 63) s_redf[wave] = incl;
+                __syncthreads();
+                float off = 0.0f;
+                for (int w = 0; w < wave; ++w) off += s_redf[w];
+                float run = off + (incl - part);
+                const float target = s_tgt, pexcl = s_pex;
+                uint32_t first = 0u, lastw = 0u;  // row + 1, 0 = none
+#pragma unroll
+                for (int rr = 0; rr < CHMAX; ++rr) {
+                    const int r = t * CH + rr;
+                    if (rr < CH && r < nrows) {
+                        const float w = __expf((bf16_to_f32(s_tl[r]) - ml) / Tb);
+                        run += w;
+                        if (first == 0u && pexcl + scale * run > target) first = (uint32_t)r + 1u;
+                        if (w > 0.0f) lastw = (uint32_t)r + 1u;
+                    }
+                }
+                const uint32_t fmin = wave_max_u32(first ? 0xFFFFFFFFu - first : 0u);
+                const uint32_t lmax = wave_max_u32(lastw);
+                if (lane == 0) {
+                    s_redi[wave] = (int)fmin;
+                    s_redj[wave] = (int)lmax;
+                }
+                __syncthreads();
+                uint32_t fm = 0u, lm = 0u;
+                for (int w = 0; w < 4; ++w) {
+                    fm = max(fm, (uint32_t)s_redi[w]);
+                    lm = max(lm, (uint32_t)s_redj[w]);
+                }
+                const int row = fm ? (int)(0xFFFFFFFFu - fm) - 1 : (lm ? (int)lm - 1 : -1);
+                const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
+                if (t == 0) {
+                    s_next[b] = tok;
+                    st_agent64(&btok[b], ((unsigned long long)(unsigned)tok << 28) | epoch);
+                }
+                __syncthreads();
+            }
+            // tokens found by other shards
+            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] & 0xFFFFFu) != c) {
+                unsigned it = 0;
+                unsigned long long w = 0ull;
+                bool ok = true;
+                while (((w = ld_agent64(&btok[t])) & kEpochMod) != epoch) {
+                    if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
+                    if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (!ok) s_abort = 1;
+                s_next[t] = ok ? checked_token((int)(w >> 28), V, status) : 0;
+            }
+            __syncthreads();
+            if (s_abort) break;
+        }
+
+        if (t < B) {
+            if (c == 0) p.tokens[(size_t)t * gamma + k] = s_next[t];
+            s_prev[t] = s_next[t];
+        }
+        __syncthreads();
+        DSW_TRACE(k, kTrSelected);
+        if (p.trace != nullptr && t == 0)
+            p.trace[((size_t)c * (gamma + 1) + k) * 8 + kTrReal] = __builtin_amdgcn_s_memrealtime();
+    }
+#undef DSW_ISSUE_GROUP
+#undef DSW_READ_COLUMN
+#undef DSW_OWNER_SHARD
+#undef DSW_BLOCK_MAX64
+#undef DSW_TILES
+
+    if (c == 0 && t == 0 && !s_abort)
+        __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// (register tiles, tiles per wave) shapes of the batched kernel
+#define DSW_BATCHED_SHAPES(X) X(4, 4) X(8, 8) X(8, 12) X(0, 12)
+#define DSW_BATCHED_I8_SHAPES(X) X(8, 8) X(8, 12) X(0, 12)
+
+}  // namespace dsw

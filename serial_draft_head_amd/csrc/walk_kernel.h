@@ -213,8 +213,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
+                // only tiles that exist in this shard have an LDS slot
                 const int idx = i0 + q * kBlock + t;
-                if (idx < 4 * LT * 512) s_wt[idx] = v[q];
+                const int s = idx >> 9;
+                const int ws = s / max(LT, 1);
+                const int j = A + (s - ws * LT);
+                if (idx < 4 * LT * 512 && j < TW && ws * TW * kTileRows + j * kTileRows < nrows) s_wt[idx] = v[q];
             }
         }
         if constexpr (kI8)

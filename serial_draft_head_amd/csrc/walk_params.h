@@ -21,13 +21,22 @@ constexpr int kMaxRegTiles = 8;     // weight tiles per wave in the 256 AGPRs
 // s into mail[s & 1][c], and readers wait until a word carries the epoch of
 // s.  Nothing needs clearing between steps, launches or graph replays.
 constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 16 exp-sum words
-constexpr int kMaxBatchPersistent = 16;
+constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
+constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
+constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
 constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // epochs live in the low 28 bits, never 0
 struct Workspace {
     unsigned long long* mail;      // [2][kMaxGrid][kMailWords]
     unsigned long long* tok_mail;  // [2][kMaxBatchPersistent] sampled token << 32 | epoch
     unsigned* round_ctr;           // [1]  launches so far (selects the step epochs)
     unsigned* status;              // [1]  latched kStatus* bits
+    // batched kernel (requests owned by workgroups): every workgroup posts one
+    // key word (and one exp-sum word) per request; the owner of request b
+    // reads column b and publishes a decision; a token shard publishes tokens
+    unsigned long long* bkey;      // [2][kMaxGrid][kMaxBatch]  key << 28 | epoch
+    unsigned long long* bsum;      // [2][kMaxGrid][kMaxBatch]  exp-sum bits << 32 | epoch
+    unsigned long long* bdec;      // [2][kMaxBatch]  decision << 28 | epoch
+    unsigned long long* btok;      // [2][kMaxBatch]  sampled token << 28 | epoch
 };
 
 // Status bits latched by the device (translated to DSW_ERR_DEV_* on the host).
@@ -37,7 +46,7 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, tok_mail, round_ctr, status, total;
+    size_t mail, tok_mail, round_ctr, status, bkey, bsum, bdec, btok, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -47,6 +56,10 @@ inline WorkspaceLayout workspace_layout() {
     L.tok_mail = o;  o = up(o + 2 * (size_t)kMaxBatchPersistent * 8);
     L.round_ctr = o; o = up(o + 4);
     L.status = o;    o = up(o + 4);
+    L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
+    L.bsum = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
+    L.bdec = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
+    L.btok = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
     L.total = o;
     return L;
 }
@@ -71,6 +84,9 @@ struct WalkParams {
     int lds_rows;            // rows per workgroup resident in LDS (after the register slots)
     int tiles_per_wave;      // MFMA engine: 16-row tiles per wave (contiguous rows)
     int lds_tiles;           // MFMA engine: tiles per wave held in LDS after the VGPR tiles
+    int rows_pad;            // batched kernel: shard rows rounded up to a multiple of 128
+    int ring;                // batched kernel: LDS slots for u rows and base logits of groups
+    int aligned;             // batched kernel: V % 8 == 0 (16-byte aligned base rows)
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };

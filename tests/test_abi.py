@@ -79,7 +79,7 @@ def shards_cover(V, grid, R):
     return covered == V
 
 
-ENGINES = {"mfma": 8, "valu": 4}   # flags forcing each shard-GEMV engine
+ENGINES = {"mfma": 8, "valu": 4, "batched": 16}   # flags forcing each kernel / engine
 
 
 @pytest.mark.parametrize("engine", list(ENGINES))
@@ -90,14 +90,16 @@ def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
     d = fake_device(dsw, cus=cus)
     flags = ENGINES[engine]
     rows = -(-V // min(cus, 256))
-    cap = 4 * 256 if engine == "valu" else 4 * 16 * 16
+    if engine == "batched":
+        rows = -(-rows // 16) * 16   # shards of whole 16-row tiles
+    cap = {"valu": 4 * 256, "mfma": 4 * 16 * 16, "batched": 4 * 12 * 16}[engine]
     if rows > cap:
         with pytest.raises(dsw.DswError) as e:
             dsw.plan(d, V, 7, B, flags=flags)
         assert e.value.code == -6
         return
     p = dsw.plan(d, V, 7, B, flags=flags)
-    assert p.engine == (1 if engine == "mfma" else 0)
+    assert p.engine == (0 if engine == "valu" else 1)
     assert p.grid == min(cus, 256) and p.block == 256
     assert p.rows_per_wg == rows
     assert shards_cover(V, p.grid, p.rows_per_wg)
@@ -108,7 +110,11 @@ def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
     assert p.lds_bytes + p.static_lds_bytes > d.lds_bytes_per_cu // 2   # one workgroup per CU
     assert p.onchip_bytes + p.stream_bytes == V * 512
     assert p.path == (1 if p.stream_rows > 0 else 0)
-    if engine == "mfma":
+    if engine == "batched":
+        assert p.batch_tile == 256 and 2 <= p.ring_slots <= 4
+        assert p.rows_pad % 128 == 0 and p.rows_pad >= rows
+        assert p.lds_bytes >= 4 * p.lds_tiles * 8192 + p.ring_slots * (8192 + 32 * p.rows_pad)
+    if engine != "valu":
         assert p.tiles_per_wave * 4 * 16 >= rows
         assert p.reg_tiles <= 8 and p.tiles_per_wave <= p.max_tiles
         assert p.reg_tiles + p.lds_tiles <= max(p.tiles_per_wave, p.reg_tiles)
@@ -137,6 +143,26 @@ def test_planner_choices_on_mi355x_shapes(dsw):
     assert (v1.engine, v1.reg_slots, v1.reg_rows, v1.lds_rows, v1.stream_rows) == (0, 3, 594, 0, 0)
     v3 = dsw.plan(d, 248_320, 16, 1, flags=4)
     assert (v3.reg_slots, v3.lds_rows, v3.stream_rows) == (3, 202, 0)
+
+
+def test_planner_batched_kernel(dsw):
+    d = fake_device(dsw)
+    # beyond 16 requests the batched kernel takes over, with 16-row aligned shards
+    c4 = dsw.plan(d, 129_280, 5, 253)
+    assert (c4.batch_tile, c4.rows_per_wg, c4.rows_pad, c4.tiles_per_wave, c4.reg_tiles) == (256, 512, 512, 8, 8)
+    assert c4.lds_tiles == 0 and c4.stream_rows == 0 and c4.ring_slots == 4
+    assert c4.onchip_bytes == 129_280 * 512
+    assert dsw.plan(d, 129_280, 5, 16).batch_tile == 16
+    assert dsw.plan(d, 129_280, 5, 16, flags=dsw.FLAG_BATCHED).batch_tile == 256
+    # V = 151,936 with 64 requests: two LDS tiles per wave beside the ring
+    c2 = dsw.plan(d, 151_936, 16, 64)
+    assert (c2.rows_per_wg, c2.tiles_per_wave, c2.reg_tiles, c2.lds_tiles, c2.stream_rows) == (608, 10, 8, 2, 0)
+    assert c2.ring_slots >= 2
+    i8 = dsw.plan(d, 129_280, 5, 64, w2_dtype=dsw.INT8)
+    assert (i8.reg_tiles, i8.max_tiles, i8.w2_dtype, i8.onchip_bytes) == (8, 8, dsw.INT8, 129_280 * 256)
+    with pytest.raises(dsw.DswError) as e:   # no VALU engine for the batched kernel
+        dsw.plan(d, 129_280, 5, 64, flags=dsw.FLAG_VALU_GEMV)
+    assert e.value.code == -11
 
 
 def test_planner_int8_rows(dsw):
@@ -185,7 +211,7 @@ def test_planner_force_stream_keeps_nothing_on_chip(dsw):
 def test_planner_rejects_bad_arguments(dsw):
     d = fake_device(dsw)
     for kw, code in [(dict(r=128), -4), (dict(w2_dtype=9), -5), (dict(V=0), -6),
-                     (dict(B=17), -2), (dict(gamma=-1), -3)]:
+                     (dict(B=257), -2), (dict(gamma=-1), -3)]:
         args = dict(V=1000, gamma=7, B=1)
         args.update(kw)
         r = args.pop("r", 256)

@@ -322,3 +322,120 @@ def test_int8_full_size_large_vocab(dsw, B):
                                  steps=[0, 1, wl.gamma - 1])
         say("round", rnd, rep)
     walker.close()
+
+
+# ---- the batched kernel (more than 16 requests, or FLAG_BATCHED) -----------
+
+def check_subset(w, inp, toks, lg, idx, steps=None):
+    """Parity of the requests `idx` only (requests are independent)."""
+    sub = lambda a: np.ascontiguousarray(a[idx])  # noqa: E731
+    return parity.check_round(w, sub(inp["base"]), sub(inp["anchor"]), sub(inp["T"]),
+                              sub(inp["uniforms"]), sub(toks), sub(lg), steps=steps)
+
+
+# aligned (V % 8 == 0: base rows stream straight into LDS) and unaligned vocabularies
+BATCHED_CASES = [(257, 17), (4_096, 40), (32_000, 64), (65_537, 33), (129_280, 24)]
+
+
+@pytest.mark.parametrize("temps", ["greedy", "mixed"])
+@pytest.mark.parametrize("V,B", BATCHED_CASES)
+def test_batched_parity(dsw, V, B, temps):
+    say(f"batched V={V} B={B} {temps}")
+    W1, W2 = workloads.weights(4, V=V)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(V, gamma_max=4, B_max=B)
+    pl = walker.query_plan(B)
+    say("plan", pl.as_dict())
+    assert pl.batch_tile == 256
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(4, 3, B=B, gamma=3, V=V, temps=temps)
+    toks, lg = run(walker, W1d, W2d, inp)
+    idx = np.unique(np.r_[0, B - 1, np.arange(0, B, 5)])
+    rep = check_subset(w, inp, toks, lg, idx)
+    say(rep)
+    walker.close()
+
+
+@pytest.mark.parametrize("B", [3, 16])
+def test_batched_kernel_at_small_batches(dsw, B):
+    V = 100_000
+    say(f"batched kernel forced at B={B}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(V, gamma_max=5, B_max=B, flags=dsw.FLAG_BATCHED)
+    assert walker.query_plan(B).batch_tile == 256
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 40 + rnd, B=B, gamma=5, V=V, temps="mixed")
+        toks, lg = run(walker, W1d, W2d, inp)
+        say(parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg))
+    walker.close()
+
+
+def test_batched_stream_logits_and_state(dsw):
+    V, B = 40_000, 37
+    say(f"batched streamed vs resident, logits optional, V={V} B={B}")
+    W1, W2 = workloads.weights(4, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    res = dsw.Walker(V, gamma_max=4, B_max=B)
+    stm = dsw.Walker(V, gamma_max=4, B_max=B, flags=dsw.FLAG_FORCE_STREAM)
+    assert stm.query_plan(B).stream_rows == stm.query_plan(B).rows_per_wg
+    for rnd in range(3):
+        inp = workloads.round_inputs(4, 50 + rnd, B=B, gamma=4, V=V, temps="mixed")
+        a = run(res, W1d, W2d, inp)
+        b = run(stm, W1d, W2d, inp)
+        c = run(res, W1d, W2d, inp, want_logits=False)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert np.array_equal(a[0], c[0])
+
+
+def test_batched_device_checks(dsw):
+    V, B = 20_000, 20
+    say("batched device status latch")
+    W1, W2 = workloads.weights(4, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    walker = dsw.Walker(V, gamma_max=3, B_max=B)
+    inp = workloads.round_inputs(4, 60, B=B, gamma=3, V=V, temps="mixed")
+    base, anchor, T, uni = round_dev(inp)
+    bad = anchor.clone()
+    bad[5] = V + 3
+    walker.walk(W1d, W2d, base, bad, T, uni)
+    assert walker.status() == -21
+    walker.walk(W1d, W2d, base, anchor, torch.ones_like(T), None)
+    assert walker.status() == -22
+    toks, lg = run(walker, W1d, W2d, inp)   # the next call is clean
+    parity.check_round(parity.Weights(W1, W2), inp["base"], inp["anchor"], inp["T"], inp["uniforms"],
+                       toks, lg)
+
+
+def test_batched_int8(dsw):
+    V, B = 129_280, 40
+    say(f"batched int8 V={V} B={B}")
+    W1, W2 = workloads.weights(4, V=V)
+    Q, sc = workloads.quantize_int8(W2)
+    w = parity.Weights(W1, Q=Q, scale=sc)
+    walker = dsw.Walker(V, gamma_max=3, B_max=B, w2_dtype=dsw.INT8)
+    assert walker.query_plan(B).batch_tile == 256
+    W1d = bf16_dev(W1)
+    Qd, sd = int8_dev(Q, sc)
+    inp = workloads.round_inputs(4, 70, B=B, gamma=3, V=V, temps="mixed")
+    toks, lg = run(walker, W1d, Qd, inp, scale=sd)
+    say(check_subset(w, inp, toks, lg, np.unique(np.r_[0, B - 1, np.arange(0, B, 4)])))
+    walker.close()
+
+
+@pytest.mark.parametrize("B", [64, 128, 253])
+def test_batched_full_size(dsw, B):
+    wl = workloads.WORKLOADS[4]
+    say(f"batched full size {wl.name} B={B}")
+    W1, W2 = workloads.weights(4)
+    w = parity.Weights(W1, W2)
+    walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=B)
+    say("plan", walker.query_plan(B).as_dict())
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(4, 0, B=B)
+    toks, lg = run(walker, W1d, W2d, inp)
+    rng = np.random.default_rng(B)
+    idx = np.unique(np.r_[0, B - 1, rng.choice(B, size=10, replace=False)])
+    say(check_subset(w, inp, toks, lg, idx, steps=[0, wl.gamma - 1]))
+    walker.close()
