@@ -11,7 +11,9 @@ rounds, bracketed by device synchronisation (lower is better).  Extra fields:
 per-launch kernel time from HIP events (the roofline's denominator), a
 cold-cache leg (L2 and the 256 MB Infinity Cache flushed before each round),
 gamma = 16 at the same vocabulary, the step-wise torch loop (the pages'
-default walk: gamma x {GEMV, add, argmax}) and the CPU oracle on a bounded
+default walk: gamma x {GEMV, add, argmax}), a short timing of every other
+checked configuration (more requests, gamma = 16, V = 248,320 in bf16 and
+int8, the batched kernel up to 253 requests) and the CPU oracle on a bounded
 sample of the same rounds.
 """
 from __future__ import annotations
@@ -166,6 +168,83 @@ def cpu_baseline(index, B, gamma, V, W1, W2, budget_s=15.0):
                       f"median wall time per round, binary64 C oracle with OpenMP"}
 
 
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+# Every configuration the walk is checked on, timed briefly after the headline
+# line's own measurements: (workload, requests, gamma, W2 storage).
+SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, "bf16"),
+         (3, 1, 16, "bf16"), (3, 1, 16, "int8"), (4, 64, 5, "bf16"), (4, 128, 5, "bf16"),
+         (4, 253, 5, "bf16")]
+
+
+def sweep_one(torch, dsw, index, B, gamma, dtype):
+    import workloads
+    wl = workloads.WORKLOADS[index]
+    V = wl.V
+    dev = torch.device("cuda", 0)
+    W1, W2 = workloads.weights(index)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W1d = bf(W1)
+    scale = None
+    if dtype == "int8":
+        Q, sc = workloads.quantize_int8(W2)
+        W2d = torch.from_numpy(Q).to(dev)
+        scale = torch.from_numpy(sc).to(dev)
+        w2_bytes = V * 256 + V * 4
+    else:
+        W2d = bf(W2)
+        w2_bytes = V * 256 * 2
+    big = B * gamma * V > 50_000_000
+    rounds = make_rounds(index, 3 if big else 8, B, gamma, V, wl.temps)
+    base, anchor, T, uni = to_device(rounds, torch, dev)
+    del rounds
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, w2_dtype=dsw.INT8 if dtype == "int8" else dsw.BF16)
+    plan = walker.query_plan(B)
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    n = base.shape[0]
+
+    def go(j):
+        walker.walk(W1d, W2d, base[j % n], anchor[j % n], T[j % n], uni[j % n], w2_scale=scale,
+                    tokens=tokens)
+    for j in range(5):
+        go(j)
+    torch.cuda.synchronize()
+    K = 30 if big else 200
+    t0 = time.perf_counter()
+    for j in range(K):
+        go(j)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / K * 1e6
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for j in range(K):
+        ev[j][0].record()
+        go(j)
+        ev[j][1].record()
+    torch.cuda.synchronize()
+    launch = statistics.fmean(a.elapsed_time(b) * 1e3 for a, b in ev)
+    st = walker.status()
+    walker.close()
+    abytes = algorithmic_bytes(V, B, gamma) - V * 256 * 2 + w2_bytes
+    stepwise = (gamma * w2_bytes + B * gamma * V * 2) / (HBM_PEAK_GBS * 1e9) * 1e6
+    flops = 2.0 * B * 256 * V * gamma
+    out = {"workload": wl.name, "B": B, "gamma": gamma, "w2": dtype, "temps": wl.temps,
+           "us_per_round": round(us, 2), "launch_us": round(launch, 2),
+           "kernel": "batched" if plan.batch_tile == 256 else
+                     ("valu" if plan.engine == dsw.ENGINE_VALU else "mfma"),
+           "path": "resident" if plan.stream_rows == 0 else f"partial ({plan.stream_rows} rows/wg streamed)",
+           "hbm_gbs": round(abytes / (launch * 1e-6) / 1e9, 1),
+           "hbm_frac": round(abytes / (launch * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "stepwise_bound_us": round(stepwise, 2),
+           "vs_stepwise_bound": round(us / stepwise, 3), "status": st}
+    if B >= 16:
+        tfs = flops / (launch * 1e-6) / 1e12
+        out["mfma_tfs"] = round(tfs, 1)
+        out["mfma_frac"] = round(tfs / MFMA_BF16_PEAK_TFS, 4)
+    del base, anchor, T, uni, W1d, W2d
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +257,7 @@ def main():
     ap.add_argument("--cold-rounds", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the timed walk (for profiling)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations")
     ap.add_argument("--pmc-mode", action="store_true",
                     help="for counter runs: 50 walks, then one 256 MiB device copy of known size")
     args = ap.parse_args()
@@ -290,10 +370,20 @@ def main():
         result["stepwise_torch_w2_gbs"] = round(gamma * w2_bytes / (sw * 1e-6) / 1e9, 1)
         log(f"step-wise torch: {sw:.2f} us/round")
 
+    walker.close()
+    del dev_rounds, W1d, W2d
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        result["configs"] = []
+        for (index, b, g, dt) in SWEEP:
+            log(f"sweep: workload {index} B={b} gamma={g} {dt}")
+            r = sweep_one(torch, dsw, index, b, g, dt)
+            log(r)
+            result["configs"].append(r)
+
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.workload, B, gamma, V, W1, W2)
-    walker.close()
     print(json.dumps(result), flush=True)
 
 

@@ -141,6 +141,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.bsum = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bsum);
     h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
     h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
+    h->ws.bext = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bext);
     if (clear_workspace(h) != DSW_OK) {
         (void)hipFree(h->ws_mem);
         delete h;

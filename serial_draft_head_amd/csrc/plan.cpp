@@ -153,7 +153,7 @@ static const int kBStreamShape[2] = {0, 12};
 static int batched_static_lds(int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
     return 4 * kMaxBatch * 4 * 3 + 4 * kMaxBatch * 4 + kMaxGrid * 4 + kMaxBatch * 4 + 2 * rpad +
-           (i8 ? 4 * rpad : 0) + 512;
+           (i8 ? 4 * rpad : 0) + 1024;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -161,6 +161,7 @@ static int plan_batched(const dsw_devinfo* dev, int V, int B, unsigned flags, in
                         dsw_plan_info* out) {
     const int R = round_up((V + grid - 1) / grid, kTileRows);  // 16-row aligned shards
     const int Rpad = round_up(R, 128);
+    if (Rpad > 1024) return DSW_ERR_VOCAB;  // the kernel's slot indexing assumes <= 1024
     const int tiles = R / kTileRows;
     const int TW = ceil_div(tiles, 4);
     const int tile_bytes = i8 ? kTileBytes / 2 : kTileBytes;

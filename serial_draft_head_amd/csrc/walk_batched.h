@@ -63,8 +63,25 @@ __device__ __forceinline__ void barrier_keep_vm() {
     asm volatile("" ::: "memory");
 }
 
+// 16 bytes from global memory straight into LDS: this lane's data lands at
+// lds_base + 16 * lane (lds_base is wave-uniform).  Written as inline assembly
+// so that the compiler does not treat every later LDS access as waiting on
+// it (it would drain the whole ring at each group); the kernel waits for
+// these loads itself with wait_vmcnt.  M0 needs one wait state before use.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
 constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8 KiB
-constexpr unsigned kDecPending = 1u << 20;             // decision: a shard, not a token
+// Decision payload: a token id (< 2^20), or kDecPending | shard << 21 |
+// ord16(max logit) for a sampled request whose token shard still has to find it.
+constexpr unsigned kDecPending = 1u << 20;
 
 template <int A, int M, int DT>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
@@ -86,6 +103,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ uint16_t s_tl[RPAD];            // one request's recomputed shard logits
     __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ int s_tasks[kMaxBatch];
+    __shared__ uint2 s_junk[64];               // epilogue writes of tiles beyond a wave's rows
     __shared__ unsigned long long s_red64[4];
     __shared__ float s_redf[4];
     __shared__ int s_redi[4];
@@ -121,6 +139,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const int D = p.ring;
     const bool aligned = p.aligned != 0;
     const int P = 2 + (aligned ? CPR / 16 : 0);  // DMA instructions per wave and group
+    // x / CPR as (x * cpr_mul) >> 20, exact for x < 16 * CPR (CPR <= 128: rows_pad <= 1024)
+    const unsigned cpr_mul = ((1u << 20) + (unsigned)CPR - 1u) / (unsigned)CPR;
     const WT* __restrict__ W2 = reinterpret_cast<const WT*>(p.W2);
     const uint4* __restrict__ W1 = reinterpret_cast<const uint4*>(p.W1);
     const uint16_t* __restrict__ base = p.base;
@@ -194,7 +214,28 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     // the four results (rows 4g .. 4g+3 of tile j, request column n)
 #define DSW_TILES(EPI)                                                                           \
     do {                                                                                         \
-        _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                                    \
+        if constexpr (!kI8) {                                                                    \
+            /* bf16: the MFMAs of a pair of tiles are issued before the epilogue of  */          \
+            /* the previous pair, whose VALU work then overlaps them                 */          \
+            f32x4_t p0_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, p1_ = p0_;                            \
+            _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                                \
+                f32x4_t c0_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, c1_ = c0_;                        \
+                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                               \
+                    c0_ = mfma_tile(as_bf16x8(wr[j0][kb]), ub[kb], c0_);                         \
+                    c1_ = mfma_tile(as_bf16x8(wr[j0 + 1][kb]), ub[kb], c1_);                     \
+                }                                                                                \
+                if (j0 > 0) {                                                                    \
+                    EPI(p0_, j0 - 2);                                                            \
+                    EPI(p1_, j0 - 1);                                                            \
+                }                                                                                \
+                p0_ = c0_;                                                                       \
+                p1_ = c1_;                                                                       \
+            }                                                                                    \
+            if (A > 0) {                                                                         \
+                EPI(p0_, A - 2);                                                                 \
+                EPI(p1_, A - 1);                                                                 \
+            }                                                                                    \
+        } else _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                             \
             f32x4_t d0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;                               \
             if constexpr (kI8) {                                                                 \
                 _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                               \
@@ -248,28 +289,25 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const int pos_ = inst_ * 64 + lane;                                                  \
             const int nn_ = pos_ >> 5, pc_ = pos_ & 31;                                          \
             const int b_ = min(gq_ * kGroup + nn_, B - 1);                                       \
-            __builtin_amdgcn_global_load_lds(                                                    \
-                (const void*)(W1 + (size_t)s_prev[b_] * kRowChunks + (pc_ ^ nn_)),              \
-                (lds_void_t*)(slot_ + inst_ * 1024), 16, 0, 0);                                  \
+            dma16(W1 + (size_t)s_prev[b_] * kRowChunks + (pc_ ^ nn_),                            \
+                  __builtin_amdgcn_readfirstlane(lds_addr(slot_ + inst_ * 1024)));               \
         }                                                                                        \
         if (aligned) {                                                                           \
             const int per_ = CPR / 16;                                                           \
             for (int ii = 0; ii < per_; ++ii) {                                                  \
                 const int inst_ = wave * per_ + ii;                                              \
                 const int pos_ = inst_ * 64 + lane;                                              \
-                const int nn_ = pos_ / CPR, pc_ = pos_ - nn_ * CPR;                              \
+                const int nn_ = (int)(((unsigned)pos_ * cpr_mul) >> 20), pc_ = pos_ - nn_ * CPR; \
                 const int b_ = min(gq_ * kGroup + nn_, B - 1);                                   \
                 const int cr_ = min((v0 >> 3) + (pc_ ^ nn_), (V >> 3) - 1);                      \
                 const uint4* src_ = reinterpret_cast<const uint4*>(base) +                       \
                                     ((size_t)b_ * gamma + k) * (size_t)(V >> 3) + cr_;           \
-                __builtin_amdgcn_global_load_lds((const void*)src_,                              \
-                                                 (lds_void_t*)(slot_ + kSlotUBytes + inst_ * 1024), \
-                                                 16, 0, 0);                                      \
+                dma16(src_, __builtin_amdgcn_readfirstlane(lds_addr(slot_ + kSlotUBytes + inst_ * 1024))); \
             }                                                                                    \
         } else {                                                                                 \
             uint16_t* sb_ = reinterpret_cast<uint16_t*>(slot_ + kSlotUBytes);                    \
             for (int e_ = t; e_ < kGroup * Rpad; e_ += kBlock) {                                 \
-                const int nn_ = e_ / Rpad, r_ = e_ - nn_ * Rpad;                                 \
+                const int nn_ = e_ / Rpad, r_ = e_ - nn_ * Rpad;  /* fallback path only */      \
                 const int b_ = min(gq_ * kGroup + nn_, B - 1);                                   \
                 sb_[(nn_ * CPR + ((r_ >> 3) ^ nn_)) * 8 + (r_ & 7)] =                            \
                     r_ < nrows ? base[((size_t)b_ * gamma + k) * V + v0 + r_] : (uint16_t)0;     \
@@ -291,36 +329,66 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             uint4 ub[8];
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) ub[kb] = su[n * kRowChunks + ((kb * 4 + g) ^ n)];
-            uint32_t best = 0u;
-            // logits land over the base values they came from (the sampled
-            // pass reads them back from there)
+            // lane's best (first) logit and row of request n; logits land over
+            // the base values they came from (the sampled pass reads them back)
+            float bestv = -__builtin_inff();
+            int bestr = -1;
+#define DSW_BEST(l_, r_, ok_)                                                                    \
+    do {                                                                                         \
+        const bool better_ = (ok_) && (l_) > bestv;                                              \
+        bestv = better_ ? (l_) : bestv;                                                          \
+        bestr = better_ ? (r_) : bestr;                                                          \
+    } while (0)
+// Branch-free, so that the matrix cores' work and this VALU work can be
+// interleaved: a register tile beyond this wave's rows writes to s_junk and
+// updates nothing.
 #define DSW_EPI_G(dv, j)                                                                         \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
-        if (bval && rb_ < nrows) {                                                               \
-            uint2* e_ = reinterpret_cast<uint2*>(sb + (n * CPR + ((rb_ >> 3) ^ n)) * 8 + (rb_ & 7)); \
-            const uint2 bw_ = *e_;                                                               \
-            const uint32_t bb_[4] = {bw_.x & 0xFFFFu, bw_.x >> 16, bw_.y & 0xFFFFu, bw_.y >> 16}; \
-            uint32_t lb_[4];                                                                     \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-                const int r_ = rb_ + i;                                                          \
-                const uint32_t bias_ = f32_to_bf16(kI8 ? s_scale[r_] * (dv)[i] : (dv)[i]);       \
-                lb_[i] = f32_to_bf16(bf16_to_f32(bb_[i]) + bf16_to_f32(bias_));                  \
-                if (r_ < nrows) best = max(best, local_key(lb_[i], r_));                         \
-            }                                                                                    \
-            *e_ = make_uint2(lb_[0] | (lb_[1] << 16), lb_[2] | (lb_[3] << 16));                  \
-            if (p.logits != nullptr) {                                                           \
-                uint16_t* o_ = p.logits + ((size_t)b * gamma + k) * V + v0 + rb_;                \
-                if (aligned && rb_ + 3 < nrows) {                                                \
-                    *reinterpret_cast<uint2*>(o_) = *e_;                                         \
-                } else {                                                                         \
-                    _Pragma("unroll") for (int i = 0; i < 4; ++i) if (rb_ + i < nrows) o_[i] = (uint16_t)lb_[i]; \
-                }                                                                                \
-            }                                                                                    \
+        const bool live_ = (j) < nt_w;                                                           \
+        uint2* e_ = live_ ? reinterpret_cast<uint2*>(sb + (n * CPR + ((rb_ >> 3) ^ n)) * 8 + (rb_ & 7)) \
+                          : &s_junk[lane];                                                       \
+        const uint2 bw_ = *e_;                                                                   \
+        float x0_ = (dv)[0], x1_ = (dv)[1], x2_ = (dv)[2], x3_ = (dv)[3];                        \
+        if constexpr (kI8) {                                                                     \
+            const int rs_ = live_ ? rb_ : 0;                                                     \
+            x0_ *= s_scale[rs_];                                                                 \
+            x1_ *= s_scale[rs_ + 1];                                                             \
+            x2_ *= s_scale[rs_ + 2];                                                             \
+            x3_ *= s_scale[rs_ + 3];                                                             \
         }                                                                                        \
+        const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);           \
+        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + bf16_lo(p01_), bf16_hi(bw_.x) + bf16_hi(p01_)); \
+        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + bf16_lo(p23_), bf16_hi(bw_.y) + bf16_hi(p23_)); \
+        *e_ = make_uint2(q01_, q23_);                                                            \
+        const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
+        DSW_BEST(bf16_lo(q01_), rb_, 0 < lim_);                                                  \
+        DSW_BEST(bf16_hi(q01_), rb_ + 1, 1 < lim_);                                              \
+        DSW_BEST(bf16_lo(q23_), rb_ + 2, 2 < lim_);                                              \
+        DSW_BEST(bf16_hi(q23_), rb_ + 3, 3 < lim_);                                              \
     } while (0)
             DSW_TILES(DSW_EPI_G);
 #undef DSW_EPI_G
+            uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
+            if (p.logits != nullptr) {
+                // the group's logits, out of the slot with whole-row stores
+                barrier_keep_vm();
+                for (int e = t; e < kGroup * CPR; e += kBlock) {
+                    const int nn = (int)(((unsigned)e * cpr_mul) >> 20), cr = e - nn * CPR;
+                    const int bq = grp * kGroup + nn, r0 = cr * 8;
+                    if (bq < B && r0 < nrows) {
+                        const uint4 w = *reinterpret_cast<const uint4*>(sb + (nn * CPR + (cr ^ nn)) * 8);
+                        uint16_t* o = p.logits + ((size_t)bq * gamma + k) * V + v0 + r0;
+                        if (aligned && r0 + 8 <= nrows) {
+                            *reinterpret_cast<uint4*>(o) = w;
+                        } else {
+                            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                            for (int i = 0; i < 8 && r0 + i < nrows; ++i)
+                                o[i] = (uint16_t)(ww[i >> 1] >> (16 * (i & 1)));
+                        }
+                    }
+                }
+            }
             // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
             best = max(best, (uint32_t)__shfl_xor((int)best, 16));
             best = max(best, (uint32_t)__shfl_xor((int)best, 32));
@@ -330,15 +398,19 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const float mw = local_key_logit(best);
                 float sw = 0.0f;
                 if (Tb > 0.0f && best != 0u) {
+                    const float sc = kLog2e / Tb;
 #pragma unroll
                     for (int j = 0; j < M; ++j) {
                         const int rb = wrow0 + j * kTileRows + 4 * g;
                         if (j < nt_w && rb < nrows) {
                             const uint2 lw = *reinterpret_cast<const uint2*>(sb + (n * CPR + ((rb >> 3) ^ n)) * 8 + (rb & 7));
-                            const uint32_t lv[4] = {lw.x & 0xFFFFu, lw.x >> 16, lw.y & 0xFFFFu, lw.y >> 16};
+                            const float lv[4] = {bf16_lo(lw.x), bf16_hi(lw.x), bf16_lo(lw.y), bf16_hi(lw.y)};
+                            const int lim = nrows - rb;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (rb + i < nrows) sw += __expf((bf16_to_f32(lv[i]) - mw) / Tb);
+                            for (int i = 0; i < 4; ++i) {
+                                const float e = __builtin_amdgcn_exp2f((lv[i] - mw) * sc);
+                                sw += i < lim ? e : 0.0f;
+                            }
                         }
                     }
                 }
@@ -360,8 +432,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             if (s_T[t] > 0.0f) {
                 const float mc = local_key_logit(lk);
                 float sc = 0.0f;
+                const float scl = kLog2e / s_T[t];
                 for (int w = 0; w < 4; ++w)
-                    if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __expf((s_rm[w][t] - mc) / s_T[t]);
+                    if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __builtin_amdgcn_exp2f((s_rm[w][t] - mc) * scl);
                 st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
             }
         }
@@ -401,7 +474,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         // Every caller runs this same code on the same words: same results.
 #define DSW_OWNER_SHARD(b_, kw_, sw_, M_)                                                        \
     do {                                                                                         \
-        s_S[t] = (t < G && kw_ != 0ull) ? sw_ * __expf((key_logit(kw_) - (M_)) / s_T[b_]) : 0.0f; \
+        s_S[t] = (t < G && kw_ != 0ull)                                                          \
+                     ? sw_ * __builtin_amdgcn_exp2f((key_logit(kw_) - (M_)) * (kLog2e / s_T[b_])) \
+                     : 0.0f;                                                                     \
         __syncthreads();                                                                         \
         if (wave == 0) {                                                                         \
             const float4 m4_ = reinterpret_cast<const float4*>(s_S)[lane];                       \
@@ -456,8 +531,14 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 }
             } else {
                 DSW_OWNER_SHARD(b, kw, sw, key_logit(win));
-                if (t == 0)
-                    st_agent64(&bdec[b], ((unsigned long long)(kDecPending | (unsigned)max(s_own, 0)) << 28) | epoch);
+                if (t == 0) {
+                    unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2;
+                    st_agent64(&ext[0], ((unsigned long long)__float_as_uint(s_pex) << 32) | epoch);
+                    st_agent64(&ext[1], ((unsigned long long)__float_as_uint(s_tgt) << 32) | epoch);
+                    const unsigned d = kDecPending | ((unsigned)max(s_own, 0) << 21) |
+                                       (uint32_t)((win >> kIdxBits) & 0xFFFFu);
+                    st_agent64(&bdec[b], ((unsigned long long)d << 28) | epoch);
+                }
             }
             __syncthreads();
         }
@@ -486,53 +567,71 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 
         // ---- sampled requests whose token lies in this shard --------------
         if (any_samp) {
-            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] & 0xFFFFFu) == c)
+            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] >> 21) == c)
                 s_tasks[atomicAdd(&s_ntask, 1)] = t;
             __syncthreads();
             const int ntask = s_ntask;
             for (int i = 0; i < ntask; ++i) {
                 const int b = s_tasks[i];
                 const float Tb = s_T[b];
-                unsigned long long kw;
-                float sw;
-                DSW_READ_COLUMN(b, kw, sw);
-                unsigned long long win;
-                DSW_BLOCK_MAX64(kw, win);
-                if (s_abort) break;
-                const float Mg = key_logit(win);
-                DSW_OWNER_SHARD(b, kw, sw, Mg);
+                const float sc2 = kLog2e / Tb;
+                // the owner's prefix before this shard and u*Z
+                if (t < 2) {
+                    const unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2 + t;
+                    unsigned it = 0;
+                    unsigned long long w = 0ull;
+                    while (((w = ld_agent64(ext)) & kEpochMod) != epoch) {
+                        if (++it >= p.spin_limit) { latch(status, kStatusTimeout); s_abort = 1; break; }
+                        if ((it & 255u) == 0u && ld_agent(status) != 0u) { s_abort = 1; break; }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    const float v = __uint_as_float((uint32_t)(w >> 32));
+                    if (t == 0) s_pex = v;
+                    else s_tgt = v;
+                }
+                const float Mg = bf16_to_f32(unord16(s_dec[b] & 0xFFFFu));
                 // this shard's logits of request b, recomputed in its column
                 const int nb = b & (kGroup - 1);
                 const uint4* urow = W1 + (size_t)s_prev[b] * kRowChunks;
                 uint4 ub[8];
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb) ub[kb] = (n == nb) ? urow[kb * 4 + g] : make_uint4(0u, 0u, 0u, 0u);
+    // the same arithmetic as the group loop, so the logits are the same bits
 #define DSW_EPI_T(dv, j)                                                                         \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
-        if (n == nb) {                                                                           \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-                const int r_ = rb_ + i;                                                          \
-                if (r_ < nrows) {                                                                \
-                    const uint32_t bias_ = f32_to_bf16(kI8 ? s_scale[r_] * (dv)[i] : (dv)[i]);   \
-                    const uint32_t bb_ = base[((size_t)b * gamma + k) * V + v0 + r_];            \
-                    s_tl[r_] = (uint16_t)f32_to_bf16(bf16_to_f32(bb_) + bf16_to_f32(bias_));     \
-                }                                                                                \
+        if (n == nb && (j) < nt_w && rb_ < nrows) {                                              \
+            const uint16_t* bp_ = base + ((size_t)b * gamma + k) * V + v0 + rb_;                 \
+            const int lim_ = nrows - rb_;                                                        \
+            uint32_t bb_[4];                                                                     \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) bb_[i] = i < lim_ ? bp_[i] : 0u;       \
+            float x0_ = (dv)[0], x1_ = (dv)[1], x2_ = (dv)[2], x3_ = (dv)[3];                    \
+            if constexpr (kI8) {                                                                 \
+                x0_ *= s_scale[rb_];                                                             \
+                x1_ *= s_scale[rb_ + 1];                                                         \
+                x2_ *= s_scale[rb_ + 2];                                                         \
+                x3_ *= s_scale[rb_ + 3];                                                         \
             }                                                                                    \
+            const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);       \
+            const uint32_t q01_ = pack_bf16_rne(bf16_to_f32(bb_[0]) + bf16_lo(p01_), bf16_to_f32(bb_[1]) + bf16_hi(p01_)); \
+            const uint32_t q23_ = pack_bf16_rne(bf16_to_f32(bb_[2]) + bf16_lo(p23_), bf16_to_f32(bb_[3]) + bf16_hi(p23_)); \
+            const uint32_t lb_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16};     \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) if (i < lim_) s_tl[rb_ + i] = (uint16_t)lb_[i]; \
         }                                                                                        \
     } while (0)
                 DSW_TILES(DSW_EPI_T);
 #undef DSW_EPI_T
                 __syncthreads();
                 // rows in vocabulary order, CH consecutive rows per thread
+                if (s_abort) break;
                 const uint32_t lk = max(max(s_rkey[0][b], s_rkey[1][b]), max(s_rkey[2][b], s_rkey[3][b]));
                 const float ml = local_key_logit(lk);
-                const float scale = __expf((ml - Mg) / Tb);
+                const float scale = __builtin_amdgcn_exp2f((ml - Mg) * sc2);
                 float part = 0.0f;
 #pragma unroll
                 for (int rr = 0; rr < CHMAX; ++rr) {
                     const int r = t * CH + rr;
-                    if (rr < CH && r < nrows) part += __expf((bf16_to_f32(s_tl[r]) - ml) / Tb);
+                    if (rr < CH && r < nrows) part += __builtin_amdgcn_exp2f((bf16_to_f32(s_tl[r]) - ml) * sc2);
                 }
                 const float incl = wave_incl_scan_dpp(part);
                 if (lane == 63) s_redf[wave] = incl;
@@ -546,7 +645,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 for (int rr = 0; rr < CHMAX; ++rr) {
                     const int r = t * CH + rr;
                     if (rr < CH && r < nrows) {
-                        const float w = __expf((bf16_to_f32(s_tl[r]) - ml) / Tb);
+                        const float w = __builtin_amdgcn_exp2f((bf16_to_f32(s_tl[r]) - ml) * sc2);
                         run += w;
                         if (first == 0u && pexcl + scale * run > target) first = (uint32_t)r + 1u;
                         if (w > 0.0f) lastw = (uint32_t)r + 1u;
@@ -573,7 +672,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 __syncthreads();
             }
             // tokens found by other shards
-            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] & 0xFFFFFu) != c) {
+            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] >> 21) != c) {
                 unsigned it = 0;
                 unsigned long long w = 0ull;
                 bool ok = true;

@@ -19,6 +19,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return u >> 16;
 }
 
+// Two fp32 values -> a bf16 pair (lo in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32.  It agrees bit for bit with f32_to_bf16 on finite
+// inputs, ties and denormals included (checked on the device).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
 __device__ __forceinline__ float dot8(const uint4 w, const uint4 u, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x),
                                           __builtin_bit_cast(bf16x2_t, u.x), acc, false);

@@ -37,6 +37,8 @@ struct Workspace {
     unsigned long long* bsum;      // [2][kMaxGrid][kMaxBatch]  exp-sum bits << 32 | epoch
     unsigned long long* bdec;      // [2][kMaxBatch]  decision << 28 | epoch
     unsigned long long* btok;      // [2][kMaxBatch]  sampled token << 28 | epoch
+    unsigned long long* bext;      // [2][kMaxBatch][2]  owner's prefix before the token
+                                   // shard and u*Z, fp32 bits << 32 | epoch
 };
 
 // Status bits latched by the device (translated to DSW_ERR_DEV_* on the host).
@@ -46,7 +48,7 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, tok_mail, round_ctr, status, bkey, bsum, bdec, btok, total;
+    size_t mail, tok_mail, round_ctr, status, bkey, bsum, bdec, btok, bext, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -60,6 +62,7 @@ inline WorkspaceLayout workspace_layout() {
     L.bsum = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bdec = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
     L.btok = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
+    L.bext = o;      o = up(o + 2 * (size_t)kMaxBatch * 2 * 8);
     L.total = o;
     return L;
 }
