@@ -156,6 +156,7 @@ static int batched_static_lds(int max_tiles, bool i8) {
            (i8 ? 4 * rpad : 0) + 1024;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
+static const int kBatchedFrom = 4;  // default: the batched kernel from this many requests
 
 static int plan_batched(const dsw_devinfo* dev, int V, int B, unsigned flags, int grid, bool i8,
                         dsw_plan_info* out) {
@@ -290,15 +291,29 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (rows > 4 * 16 * kTileRows) return DSW_ERR_VOCAB;  // 4 waves x 16 tiles x 16 rows
     if ((flags & DSW_FLAG_VALU_GEMV) && (flags & DSW_FLAG_MFMA_GEMV)) return DSW_ERR_ARG;
     const int R = (int)rows;
-    // kernel: the batched one beyond 16 requests (or when asked for); else the
-    // engine forced by a flag, else VALU for a single bf16 request, MFMA otherwise
+    // kernel: the batched one beyond 16 requests or when asked for; an engine
+    // flag forces the all-to-all kernel (up to 16 requests).  Otherwise, as
+    // measured on MI355X at V = 151,936: VALU for one bf16 request, the MFMA
+    // all-to-all kernel for 2-3 requests (and int8 at one), the batched kernel
+    // from 4 requests (falling back to the all-to-all kernel where it has no
+    // shape, e.g. int8 rows beyond 12 tiles per wave).
+    const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
-    if (!(flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV))) valu = B <= 1 && !i8;
-    const int rc = batched ? plan_batched(dev, V, B, flags, grid, i8, out)
-                 : valu    ? plan_valu(dev, B, flags, grid, R, out)
-                           : plan_mfma(dev, V, B, flags, grid, R, i8, out);
+    if (!forced) valu = B <= 1 && !i8;
+    int rc;
+    if (batched) {
+        rc = plan_batched(dev, V, B, flags, grid, i8, out);
+    } else if (!forced && B >= kBatchedFrom) {
+        rc = plan_batched(dev, V, B, flags, grid, i8, out);
+        if (rc != DSW_OK) {
+            memset(out, 0, sizeof(*out));
+            rc = plan_mfma(dev, V, B, flags, grid, R, i8, out);
+        }
+    } else {
+        rc = valu ? plan_valu(dev, B, flags, grid, R, out) : plan_mfma(dev, V, B, flags, grid, R, i8, out);
+    }
     if (rc != DSW_OK) {
         memset(out, 0, sizeof(*out));
         return rc;

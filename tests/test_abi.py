@@ -132,11 +132,13 @@ def test_planner_choices_on_mi355x_shapes(dsw):
     assert pick(dsw.plan(d, 32_000, 7, 1, flags=8)) == (125, 2, 2, 0, 0)
     c1 = dsw.plan(d, 151_936, 7, 1, flags=8)
     assert pick(c1) == (594, 10, 8, 2, 0) and c1.path == 0 and c1.onchip_bytes == 151_936 * 512
-    c2 = dsw.plan(d, 151_936, 16, 16)
+    c2 = dsw.plan(d, 151_936, 16, 16, flags=8)
     assert pick(c2) == (594, 10, 8, 2, 0) and c2.batch_tile == 16
+    # by default 2-3 requests take the all-to-all MFMA kernel, 4 and more the batched one
+    assert [dsw.plan(d, 151_936, 16, b).batch_tile for b in (2, 3, 4, 16)] == [4, 4, 256, 256]
     c3 = dsw.plan(d, 248_320, 16, 1, flags=8)
     assert c3.rows_per_wg == 970 and c3.tiles_per_wave == 16 and c3.path == 1 and c3.stream_rows > 0
-    c4 = dsw.plan(d, 129_280, 5, 16)
+    c4 = dsw.plan(d, 129_280, 5, 16, flags=8)
     assert pick(c4) == (505, 8, 8, 0, 0)
     # the VALU engine keeps whole 256-row groups per lane
     v1 = dsw.plan(d, 151_936, 7, 1, flags=4)
@@ -152,8 +154,10 @@ def test_planner_batched_kernel(dsw):
     assert (c4.batch_tile, c4.rows_per_wg, c4.rows_pad, c4.tiles_per_wave, c4.reg_tiles) == (256, 512, 512, 8, 8)
     assert c4.lds_tiles == 0 and c4.stream_rows == 0 and c4.ring_slots == 4
     assert c4.onchip_bytes == 129_280 * 512
-    assert dsw.plan(d, 129_280, 5, 16).batch_tile == 16
-    assert dsw.plan(d, 129_280, 5, 16, flags=dsw.FLAG_BATCHED).batch_tile == 256
+    assert dsw.plan(d, 129_280, 5, 16, flags=dsw.FLAG_MFMA_GEMV).batch_tile == 16
+    assert dsw.plan(d, 129_280, 5, 3, flags=dsw.FLAG_BATCHED).batch_tile == 256
+    # int8 rows beyond the batched shapes fall back to the all-to-all kernel
+    assert dsw.plan(d, 248_320, 16, 8, w2_dtype=dsw.INT8).batch_tile == 16
     # V = 151,936 with 64 requests: two LDS tiles per wave beside the ring
     c2 = dsw.plan(d, 151_936, 16, 64)
     assert (c2.rows_per_wg, c2.tiles_per_wave, c2.reg_tiles, c2.lds_tiles, c2.stream_rows) == (608, 10, 8, 2, 0)
@@ -174,8 +178,8 @@ def test_planner_int8_rows(dsw):
     assert c3.onchip_bytes == 248_320 * 256 and c3.stream_bytes == 0
     assert pick(dsw.plan(d, 248_320, 16, 16, w2_dtype=dsw.INT8)) == (1, 16, 16, 0, 0)
     # smaller vocabularies take the smaller compiled shapes
-    assert dsw.plan(d, 60_000, 7, 4, w2_dtype=dsw.INT8).reg_tiles == 4
-    assert dsw.plan(d, 129_280, 7, 4, w2_dtype=dsw.INT8).reg_tiles == 8
+    assert dsw.plan(d, 60_000, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 4
+    assert dsw.plan(d, 129_280, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 8
     # streaming everything works for int8 too
     s = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=1)
     assert (s.reg_rows, s.lds_rows, s.stream_rows, s.stream_bytes) == (0, 0, 970, 248_320 * 256)

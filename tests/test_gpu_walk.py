@@ -274,7 +274,7 @@ def test_int8_rows(dsw, V, shape, B):
     W1, W2 = workloads.weights(3, V=V)
     Q, sc = workloads.quantize_int8(W2)
     w = parity.Weights(W1, Q=Q, scale=sc)
-    walker = dsw.Walker(V, gamma_max=4, B_max=16, w2_dtype=dsw.INT8)
+    walker = dsw.Walker(V, gamma_max=4, B_max=16, w2_dtype=dsw.INT8, flags=dsw.FLAG_MFMA_GEMV)
     pl = walker.query_plan(B)
     assert (pl.engine, pl.reg_tiles, pl.max_tiles, pl.stream_rows) == (1, *shape, 0)
     W1d = bf16_dev(W1)
