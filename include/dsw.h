@@ -150,7 +150,9 @@ int dsw_device_info(int device, dsw_devinfo* out);
  * resident"); each shard is placed in VGPRs first, then LDS, and whatever is
  * left is streamed every step (section "V = 248,320: 62% on chip, the rest
  * streamed").  flags: DSW_FLAG_FORCE_STREAM and the engine flags.  int8 W2
- * always plans the MFMA engine (DSW_ERR_DTYPE with DSW_FLAG_VALU_GEMV).
+ * takes the VALU engine only for one request (rows widened to bf16 on chip,
+ * at most two register row groups per lane); DSW_FLAG_VALU_GEMV with int8 W2
+ * and B > 1 returns DSW_ERR_DTYPE.
  * Returns DSW_ERR_* on invalid sizes or when no plan fits. */
 int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int w2_dtype,
                      unsigned flags, dsw_plan_info* out);

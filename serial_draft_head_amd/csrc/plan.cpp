@@ -23,17 +23,22 @@ namespace dsw {
 
 // ---- VALU engine ----------------------------------------------------------
 // Largest number of VGPR row groups per lane a compiled kernel holds without
-// spilling to scratch (checked in the compiled code objects).
-static int valu_reg_slot_cap(int batch_tile) {
+// spilling to scratch (checked in the compiled code objects).  int8 rows are
+// widened to bf16 in registers; three widened groups beside the row scales
+// spill, so int8 stops at two.
+static int valu_reg_slot_cap(int batch_tile, bool i8) {
+    if (i8) return 2;
     switch (batch_tile) {
         case 1: return 3;
         case 4: return 2;
         default: return 1;
     }
 }
-// Upper bound of the VALU kernel's static LDS for a batch tile.
-static int valu_static_lds(int nb) {
-    return nb * ((kRowChunks + 1) * 16 + kMaxSlots * kBlock * 2 + 2 * 4 * kBlock + 144) + 1104;
+// Upper bound of the VALU kernel's static LDS for a batch tile (int8 rows add
+// their fp32 scales).
+static int valu_static_lds(int nb, bool i8) {
+    return nb * ((kRowChunks + 1) * 16 + kMaxSlots * kBlock * 2 + 2 * 4 * kBlock + 144) + 1104 +
+           (i8 ? 4 * kMaxSlots * kBlock : 0);
 }
 static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 
@@ -229,17 +234,18 @@ static int plan_batched(const dsw_devinfo* dev, int V, int B, unsigned flags, in
     return DSW_OK;
 }
 
-static int plan_valu(const dsw_devinfo* dev, int B, unsigned flags, int grid, int R,
+static int plan_valu(const dsw_devinfo* dev, int B, unsigned flags, int grid, int R, bool i8,
                      dsw_plan_info* out) {
     if (R > kMaxSlots * kBlock) return DSW_ERR_VOCAB;
     const int row_bytes = kRank * 2;
     const int tile = valu_tile_for(B);
     const int slots = ceil_div(R, kBlock);
-    int reg_slots = slots < valu_reg_slot_cap(tile) ? slots : valu_reg_slot_cap(tile);
+    const int cap = valu_reg_slot_cap(tile, i8);
+    int reg_slots = slots < cap ? slots : cap;
     if (flags & DSW_FLAG_FORCE_STREAM) reg_slots = 0;
     const int reg_rows = R < reg_slots * kBlock ? R : reg_slots * kBlock;
 
-    const int lds_static = valu_static_lds(tile);
+    const int lds_static = valu_static_lds(tile, i8);
     int lds_avail = dev->max_lds_per_block - lds_static;
     if (lds_avail < 0) lds_avail = 0;
     int lds_rows = R - reg_rows;
@@ -280,7 +286,7 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     if (r != kRank) return DSW_ERR_RANK;
     if (w2_dtype != DSW_BF16 && w2_dtype != DSW_INT8) return DSW_ERR_DTYPE;
     const bool i8 = w2_dtype == DSW_INT8;
-    if (i8 && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_DTYPE;  // int8 runs on the MFMA engine
+    if (i8 && (flags & DSW_FLAG_VALU_GEMV) && B > 1) return DSW_ERR_DTYPE;  // VALU int8: one request
     if (V < 1 || V > (1 << 20)) return DSW_ERR_VOCAB;  // row ids live in 20 key bits
     if (gamma < 0) return DSW_ERR_GAMMA;
     if (B < 0 || B > kMaxBatch) return DSW_ERR_BATCH;
@@ -293,15 +299,15 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const int R = (int)rows;
     // kernel: the batched one beyond 16 requests or when asked for; an engine
     // flag forces the all-to-all kernel (up to 16 requests).  Otherwise, as
-    // measured on MI355X at V = 151,936: VALU for one bf16 request, the MFMA
-    // all-to-all kernel for 2-3 requests (and int8 at one), the batched kernel
+    // measured on MI355X at V = 151,936: VALU for one request (int8 rows are
+    // widened to bf16 on chip), the MFMA all-to-all kernel for 2-3, the batched kernel
     // from 4 requests (falling back to the all-to-all kernel where it has no
     // shape, e.g. int8 rows beyond 12 tiles per wave).
     const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
-    if (!forced) valu = B <= 1 && !i8;
+    if (!forced) valu = B <= 1;
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);
@@ -312,7 +318,7 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
             rc = plan_mfma(dev, V, B, flags, grid, R, i8, out);
         }
     } else {
-        rc = valu ? plan_valu(dev, B, flags, grid, R, out) : plan_mfma(dev, V, B, flags, grid, R, i8, out);
+        rc = valu ? plan_valu(dev, B, flags, grid, R, i8, out) : plan_mfma(dev, V, B, flags, grid, R, i8, out);
     }
     if (rc != DSW_OK) {
         memset(out, 0, sizeof(*out));

@@ -93,9 +93,10 @@ template <int ENGINE, int A, int M, int NB, int DT = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
     constexpr bool kI8 = DT == 1;  // int8 rows + fp32 row scales
-    static_assert(!kI8 || kMfma, "int8 weights run on the MFMA engine");
-    // one K block of 8 weights of a lane's tile row (MFMA), or 16 bytes of a row (VALU)
-    using WT = typename std::conditional<kI8, uint2, uint4>::type;
+    static_assert(!kI8 || kMfma || NB == 1, "int8 rows on the VALU engine: one request");
+    // one K block of 8 weights of a lane's tile row (MFMA), or 16 bytes of a row
+    // (VALU; int8 rows are widened to bf16 once, at entry)
+    using WT = typename std::conditional<kI8 && kMfma, uint2, uint4>::type;
     static_assert(NB == 1 || NB == 4 || NB == 16, "batch tile");
     static_assert(!kMfma || (NB >= 4 && A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles), "MFMA shape");
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
@@ -236,6 +237,37 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int idx = i0 + q * kBlock + t;
                 if (idx < NB * RPAD) s_base[idx] = v[q];
             }
+        }
+    } else if constexpr (kI8) {
+        // int8 rows: HBM carries half the bytes; each row is widened to bf16
+        // once (exact) and the walk then runs the bf16 dot products
+        const uint4* __restrict__ Wq = reinterpret_cast<const uint4*>(p.W2);  // 16 codes per uint4
+        // slot by slot: one slot's codes in flight, then widened (holding every
+        // slot's codes at once would not fit beside the widened rows)
+#pragma unroll
+        for (int s = 0; s < A; ++s) {
+            const int row = min(v0 + s * kBlock + t, V - 1);  // rows past the shard: any valid row
+            uint4 qv[kRowChunks / 2];
+#pragma unroll
+            for (int c2 = 0; c2 < kRowChunks / 2; ++c2) qv[c2] = Wq[(size_t)row * (kRowChunks / 2) + c2];
+#pragma unroll
+            for (int c2 = 0; c2 < kRowChunks / 2; ++c2) {
+                wr[s][2 * c2] = as_bf16x8(make_uint2(qv[c2].x, qv[c2].y));
+                wr[s][2 * c2 + 1] = as_bf16x8(make_uint2(qv[c2].z, qv[c2].w));
+            }
+        }
+        for (int j = t; j < lds_rows * (kRowChunks / 2); j += kBlock) {
+            const int il = j >> 4, c2 = j & 15;
+            const uint4 qv = Wq[(size_t)(v0 + reg_cap + il) * (kRowChunks / 2) + c2];
+            s_w[il * kRowChunks + ((2 * c2) ^ (il & 31))] = as_bf16x8(make_uint2(qv.x, qv.y));
+            s_w[il * kRowChunks + ((2 * c2 + 1) ^ (il & 31))] = as_bf16x8(make_uint2(qv.z, qv.w));
+        }
+        // row scales in LDS: four more registers per lane would spill the widest shape
+        for (int r = t; r < RPAD; r += kBlock) s_scale[r] = r < nrows ? p.w2_scale[v0 + r] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < kMaxSlots; ++s) {
+            const int i = s * kBlock + t;
+            bs[0][s] = (B > 0 && i < nrows) ? (uint32_t)base[v0 + i] : 0u;
         }
     } else {
         // no pin here: A = 3 needs 384 registers, more than the 256 VGPRs a "v"
@@ -423,11 +455,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                         }
                     } else {
                         const WT* src = W2 + (size_t)(v0 + i) * kRowChunks;
+                        const uint2* srcq = reinterpret_cast<const uint2*>(p.W2) + (size_t)(v0 + i) * kRowChunks;
 #pragma unroll 1
                         for (int c0 = 0; c0 < kRowChunks; c0 += kGrp) {
                             uint4 w4[kGrp];
 #pragma unroll
-                            for (int q = 0; q < kGrp; ++q) w4[q] = src[c0 + q];
+                            for (int q = 0; q < kGrp; ++q) {
+                                if constexpr (kI8) w4[q] = as_bf16x8(srcq[c0 + q]);
+                                else w4[q] = src[c0 + q];
+                            }
 #pragma unroll
                             for (int q = 0; q < kGrp; ++q)
 #pragma unroll
@@ -437,13 +473,18 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     }
                 }
             }
+            // int8: the scale reads stay after the dot products (issued earlier,
+            // they would be live across the GEMV and spill the widest shape)
+            if constexpr (kI8) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
 #pragma unroll
                 for (int s = 0; s < kMaxSlots; ++s) {
                     const int i = s * kBlock + t;
                     if ((NB == 1 || b < B) && i < nrows) {
-                        const uint32_t bias = f32_to_bf16(acc[b][s]);
+                        float a = acc[b][s];
+                        if constexpr (kI8) a *= s_scale[i];
+                        const uint32_t bias = f32_to_bf16(a);
                         const uint32_t lbits = f32_to_bf16(bf16_to_f32(bs[b][s]) + bf16_to_f32(bias));
                         best[b] = max(best[b], local_key(lbits, i));
                         s_logit[b * RPAD + i] = (uint16_t)lbits;

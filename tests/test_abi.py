@@ -173,19 +173,27 @@ def test_planner_int8_rows(dsw):
     d = fake_device(dsw)
     pick = lambda p: (p.engine, p.tiles_per_wave, p.reg_tiles, p.lds_tiles, p.stream_rows)  # noqa: E731
     # int8 rows take half the registers: V = 248,320 is fully resident at 16 tiles per wave
-    c3 = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8)
+    c3 = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=dsw.FLAG_MFMA_GEMV)
     assert pick(c3) == (1, 16, 16, 0, 0) and c3.path == 0 and c3.w2_dtype == dsw.INT8
     assert c3.onchip_bytes == 248_320 * 256 and c3.stream_bytes == 0
     assert pick(dsw.plan(d, 248_320, 16, 16, w2_dtype=dsw.INT8)) == (1, 16, 16, 0, 0)
+    # one request takes the VALU engine: two widened register groups, LDS rows
+    # (bf16, 512 bytes each) and the rest streamed as int8 every step
+    v = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8)
+    assert (v.engine, v.reg_slots, v.reg_rows) == (0, 2, 512) and v.path == 1
+    assert v.lds_rows == (v.lds_bytes // 512) and v.lds_rows + v.stream_rows == 970 - 512
+    assert v.stream_bytes == 256 * v.stream_rows * 256 and v.onchip_bytes + v.stream_bytes == 248_320 * 256
+    # small vocabularies fit in the two register groups
+    assert dsw.plan(d, 100_000, 7, 1, w2_dtype=dsw.INT8).path == 0
     # smaller vocabularies take the smaller compiled shapes
     assert dsw.plan(d, 60_000, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 4
     assert dsw.plan(d, 129_280, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 8
     # streaming everything works for int8 too
     s = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=1)
     assert (s.reg_rows, s.lds_rows, s.stream_rows, s.stream_bytes) == (0, 0, 970, 248_320 * 256)
-    # int8 has no VALU engine
+    # the VALU engine takes int8 rows for one request only
     with pytest.raises(dsw.DswError) as e:
-        dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=4)
+        dsw.plan(d, 248_320, 16, 2, w2_dtype=dsw.INT8, flags=4)
     assert e.value.code == -5
     assert dsw.plan(d, 248_320, 16, 1).w2_dtype == dsw.BF16
 

@@ -287,6 +287,47 @@ def test_int8_rows(dsw, V, shape, B):
     walker.close()
 
 
+# one request: int8 rows widened to bf16 on chip (VALU engine), including the
+# vocabulary whose shard overflows registers and LDS (int8 rows streamed)
+@pytest.mark.parametrize("V", [257, 4097, 60_000, 129_280, 248_320])
+def test_int8_rows_valu(dsw, V):
+    say(f"int8 valu V={V}")
+    W1, W2 = workloads.weights(3, V=V)
+    Q, sc = workloads.quantize_int8(W2)
+    w = parity.Weights(W1, Q=Q, scale=sc)
+    walker = dsw.Walker(V, gamma_max=4, B_max=1, w2_dtype=dsw.INT8, flags=dsw.FLAG_VALU_GEMV)
+    pl = walker.query_plan(1)
+    say("plan", pl.as_dict())
+    assert pl.engine == 0 and pl.reg_slots <= 2
+    assert (pl.stream_rows > 0) == (V == 248_320)
+    W1d = bf16_dev(W1)
+    Qd, sd = int8_dev(Q, sc)
+    for rnd, temps in enumerate(("greedy", "cycle", "cycle", "cycle")):
+        inp = workloads.round_inputs(3, 40 + rnd, B=1, gamma=4, V=V, temps=temps)
+        toks, lg = run(walker, W1d, Qd, inp, scale=sd)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg)
+        say(temps, inp["T"], rep)
+    walker.close()
+
+
+def test_int8_valu_force_stream_is_bit_identical(dsw):
+    V = 100_003
+    say(f"int8 valu streamed vs resident V={V}")
+    W1, W2 = workloads.weights(3, V=V)
+    Q, sc = workloads.quantize_int8(W2)
+    W1d = bf16_dev(W1)
+    Qd, sd = int8_dev(Q, sc)
+    res = dsw.Walker(V, gamma_max=5, B_max=1, w2_dtype=dsw.INT8, flags=dsw.FLAG_VALU_GEMV)
+    stm = dsw.Walker(V, gamma_max=5, B_max=1, w2_dtype=dsw.INT8,
+                     flags=dsw.FLAG_VALU_GEMV | dsw.FLAG_FORCE_STREAM)
+    assert stm.query_plan(1).stream_rows == stm.query_plan(1).rows_per_wg
+    for rnd in range(3):
+        inp = workloads.round_inputs(3, 50 + rnd, B=1, gamma=5, V=V, temps="cycle")
+        a = run(res, W1d, Qd, inp, scale=sd)
+        b = run(stm, W1d, Qd, inp, scale=sd)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_int8_force_stream_is_bit_identical(dsw):
     V = 100_003
     say(f"int8 streamed vs resident V={V}")
