@@ -199,10 +199,13 @@ int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out);
 /* Diagnostics: record per-workgroup, per-step phase timestamps of later
  * dsw_walk calls into `trace`, a device buffer of `bytes` bytes owned by the
  * caller (NULL disables).  Layout: uint64 [grid][gamma+1][8]; row k < gamma
- * holds s_memtime counts at: step start, inputs staged, GEMV done, workgroup
- * argmax known, key posted, all workgroups arrived, tokens known, and (slot 7)
- * s_memrealtime (100 MHz) at the end of the step; row gamma slot 0 is the
- * kernel's start.  Calls whose trace would not fit in `bytes` record nothing. */
+ * holds device-wide 100 MHz clock (s_memrealtime) readings at: step start,
+ * inputs staged, GEMV done, workgroup argmax known, key posted, all
+ * workgroups arrived, tokens known, and (slot 7) the core-clock counter
+ * (s_memtime) at the end of the step; row gamma slot 0 is the kernel's start.
+ * Only the first 16 steps are recorded (the timestamps are kept on chip and
+ * written once, when the walk ends).  Calls whose trace would not fit in
+ * `bytes` record nothing. */
 int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes);
 
 /* Free the workspace and the handle.  NULL is accepted. */

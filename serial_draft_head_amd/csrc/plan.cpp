@@ -21,6 +21,9 @@
 
 namespace dsw {
 
+// LDS of the phase trace's timestamps (kTraceSteps + 1 rows of 8 u64), in every kernel.
+static const int kTraceLds = (kTraceSteps + 1) * 8 * 8;
+
 // ---- VALU engine ----------------------------------------------------------
 // Largest number of VGPR row groups per lane a compiled kernel holds without
 // spilling to scratch (checked in the compiled code objects).  int8 rows are
@@ -38,7 +41,7 @@ static int valu_reg_slot_cap(int batch_tile, bool i8) {
 // their fp32 scales).
 static int valu_static_lds(int nb, bool i8) {
     return nb * ((kRowChunks + 1) * 16 + kMaxSlots * kBlock * 2 + 2 * 4 * kBlock + 144) + 1104 +
-           (i8 ? 4 * kMaxSlots * kBlock : 0);
+           (i8 ? 4 * kMaxSlots * kBlock : 0) + kTraceLds;
 }
 static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 
@@ -54,7 +57,8 @@ static int mfma_tile_for(int B) { return B <= 4 ? 4 : 16; }
 // wave, int8 rows with their fp32 scales).
 static int mfma_static_lds(int nb, int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
-    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0);
+    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0) +
+           kTraceLds;
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -158,7 +162,7 @@ static const int kBStreamShape[2] = {0, 12};
 static int batched_static_lds(int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
     return 4 * kMaxBatch * 4 * 3 + 4 * kMaxBatch * 4 + kMaxGrid * 4 + kMaxBatch * 4 + 2 * rpad +
-           (i8 ? 4 * rpad : 0) + 1024;
+           (i8 ? 4 * rpad : 0) + 1024 + kTraceLds;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 static const int kBatchedFrom = 4;  // default: the batched kernel from this many requests

@@ -114,6 +114,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ int s_ntask;
     __shared__ unsigned s_round;
     __shared__ int s_abort;
+    DSW_TRACE_DECL;
     __shared__ int s_any_samp;
 
     const int t = threadIdx.x;
@@ -694,8 +695,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }
         __syncthreads();
         DSW_TRACE(k, kTrSelected);
-        if (p.trace != nullptr && t == 0)
-            p.trace[((size_t)c * (gamma + 1) + k) * 8 + kTrReal] = __builtin_amdgcn_s_memrealtime();
+        DSW_TRACE_REAL(k);
     }
 #undef DSW_ISSUE_GROUP
 #undef DSW_READ_COLUMN
@@ -703,6 +703,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #undef DSW_BLOCK_MAX64
 #undef DSW_TILES
 
+    DSW_TRACE_FLUSH();
     if (c == 0 && t == 0 && !s_abort)
         __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

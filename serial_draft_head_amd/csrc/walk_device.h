@@ -193,11 +193,29 @@ __device__ __forceinline__ uint32_t unord16(uint32_t ord) {
     return (ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu);
 }
 
-// Phase timestamp into the optional trace buffer (thread 0 of each workgroup).
-#define DSW_TRACE(k, ph)                                                                    \
+// Phase timestamps of the optional trace (thread 0 of each workgroup).  They
+// are kept in LDS during the walk and written out once at the end, so that
+// tracing adds no global stores (and no waits on them) inside the steps.
+// Steps beyond kTraceSteps are not recorded; row kTraceSteps holds the kernel
+// start, written out as step `gamma`.
+#define DSW_TRACE_DECL __shared__ unsigned long long s_trace[kTraceSteps + 1][8]
+#define DSW_TRACE_AT(k, ph, clock)                                                          \
     do {                                                                                    \
-        if (p.trace != nullptr && t == 0)                                                   \
-            p.trace[((size_t)c * (gamma + 1) + (k)) * 8 + (ph)] = __builtin_amdgcn_s_memtime(); \
+        if (p.trace != nullptr && t == 0) {                                                 \
+            const int kk_ = (k) >= gamma ? kTraceSteps : ((k) < kTraceSteps ? (k) : -1);    \
+            if (kk_ >= 0) s_trace[kk_][ph] = clock;                                         \
+        }                                                                                   \
+    } while (0)
+#define DSW_TRACE(k, ph) DSW_TRACE_AT(k, ph, __builtin_amdgcn_s_memrealtime())
+#define DSW_TRACE_REAL(k) DSW_TRACE_AT(k, kTrReal, __builtin_amdgcn_s_memtime())
+#define DSW_TRACE_FLUSH()                                                                   \
+    do {                                                                                    \
+        if (p.trace != nullptr && t == 0) {                                                 \
+            for (int k_ = 0; k_ < gamma && k_ < kTraceSteps; ++k_)                          \
+                for (int ph_ = 0; ph_ < 8; ++ph_)                                           \
+                    p.trace[((size_t)c * (gamma + 1) + k_) * 8 + ph_] = s_trace[k_][ph_];   \
+            p.trace[((size_t)c * (gamma + 1) + gamma) * 8] = s_trace[kTraceSteps][0];       \
+        }                                                                                   \
     } while (0)
 
 }  // namespace dsw

@@ -127,6 +127,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     __shared__ int s_prev[NB];
     __shared__ unsigned s_round;
     __shared__ int s_abort;
+    DSW_TRACE_DECL;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -421,14 +422,34 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #pragma unroll
                 for (int s = 0; s < kMaxSlots; ++s) acc[b][s] = 0.0f;
             if (A > 0) {
+                if constexpr (NB == 1) {
+                    // u read kUPre chunks ahead of its dot products: each LDS read
+                    // is in flight while earlier chunks are multiplied (the
+                    // scheduling barriers keep the compiler from sinking the
+                    // reads back next to their use)
+                    constexpr int kUPre = 2;
+                    uint4 ub[kUPre + 1];
 #pragma unroll
-                for (int ch = 0; ch < kRowChunks; ++ch) {
+                    for (int q = 0; q < kUPre; ++q) ub[q] = s_u[q];
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        if (NB == 1 || b < B) {
-                            const uint4 u4 = s_u[b * US + ch];
+                    for (int ch = 0; ch < kRowChunks; ++ch) {
+                        if (ch + kUPre < kRowChunks) ub[(ch + kUPre) % (kUPre + 1)] = s_u[ch + kUPre];
+                        __builtin_amdgcn_sched_barrier(0);
+                        const uint4 u4 = ub[ch % (kUPre + 1)];
 #pragma unroll
-                            for (int s = 0; s < A; ++s) acc[b][s] = dot8(wr[s][ch], u4, acc[b][s]);
+                        for (int s = 0; s < A; ++s) acc[0][s] = dot8(wr[s][ch], u4, acc[0][s]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+#pragma unroll
+                    for (int ch = 0; ch < kRowChunks; ++ch) {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            if (b < B) {
+                                const uint4 u4 = s_u[b * US + ch];
+#pragma unroll
+                                for (int s = 0; s < A; ++s) acc[b][s] = dot8(wr[s][ch], u4, acc[b][s]);
+                            }
                         }
                     }
                 }
@@ -578,6 +599,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                            ((unsigned long long)__float_as_uint(s_tot[lane]) << 32) | epoch);
         }
         DSW_TRACE(k, kTrPosted);
+        // the previous step's tokens, stored while this step's rendezvous is in
+        // flight (a store at the end of a step would hold up the next gather)
+        if (c == 0 && k > 0 && t < B) p.tokens[(size_t)t * gamma + k - 1] = DSW_TOKEN(t);
         if (p.logits != nullptr) {  // the exact values the tokens are selected from
             for (int b = 0; b < B; ++b) {
                 uint16_t* dst = p.logits + ((size_t)b * gamma + k) * V + v0;
@@ -592,35 +616,74 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             sw[b] = 0.0f;
         }
         if (t < G) {
+            // Up to 4 requests: two polls in flight, each check waiting only for
+            // the older load, so a word that lands is seen about half a round
+            // trip sooner than with one poll at a time.  16 requests: one poll at
+            // a time (a second set of words would not fit in registers).
+            constexpr int kDepth = NB <= 4 ? 2 : 1;
             const unsigned long long* box = mail_q + (size_t)t * kMailWords;
+            unsigned long long pa[kDepth == 2 ? NB : 1][2], pb[kDepth == 2 ? NB : 1][2];
+#define DSW_POLL(w)                                                                        \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                       \
+        if (NB == 1 || b < B) {                                                            \
+            w[b][0] = ld_agent64(&box[b]);                                                 \
+            if (s_T[b] > 0.0f) w[b][1] = ld_agent64(&box[kMaxBatchPersistent + b]);        \
+        }                                                                                  \
+    }
+#define DSW_READY(w, ready)                                                                \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                       \
+        if (NB == 1 || b < B) {                                                            \
+            if ((w[b][0] & kEpochMod) == epoch) kw[b] = w[b][0] >> 28;                     \
+            else ready = false;                                                            \
+            if (s_T[b] > 0.0f) {                                                           \
+                if ((w[b][1] & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(w[b][1] >> 32)); \
+                else ready = false;                                                        \
+            }                                                                              \
+        }                                                                                  \
+    }
             unsigned it = 0;
+            if constexpr (kDepth == 2) DSW_POLL(pa);
             for (;;) {
-                bool ready = true;
+                if constexpr (kDepth == 2) {
+                    DSW_POLL(pb);
+                    bool ready = true;
+                    DSW_READY(pa, ready);
+                    if (ready) break;
+                    __builtin_amdgcn_s_sleep(1);
+                    DSW_POLL(pa);
+                    ready = true;
+                    DSW_READY(pb, ready);
+                    if (ready) break;
+                } else {
+                    bool ready = true;
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (NB == 1 || b < B) {
-                        const unsigned long long wk = ld_agent64(&box[b]);
-                        if ((wk & kEpochMod) == epoch) kw[b] = wk >> 28;
-                        else ready = false;
-                        if (s_T[b] > 0.0f) {
-                            const unsigned long long ws = ld_agent64(&box[kMaxBatchPersistent + b]);
-                            if ((ws & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(ws >> 32));
+                    for (int b = 0; b < NB; ++b) {
+                        if (b < B) {
+                            const unsigned long long wk = ld_agent64(&box[b]);
+                            if ((wk & kEpochMod) == epoch) kw[b] = wk >> 28;
                             else ready = false;
+                            if (s_T[b] > 0.0f) {
+                                const unsigned long long ws = ld_agent64(&box[kMaxBatchPersistent + b]);
+                                if ((ws & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(ws >> 32));
+                                else ready = false;
+                            }
                         }
                     }
+                    if (ready) break;
                 }
-                if (ready) break;
                 if (++it >= p.spin_limit) {
                     latch(status, kStatusTimeout);
                     s_abort = 1;
                     break;
                 }
-                if ((it & 255u) == 0u && ld_agent(status) != 0u) {
+                if ((it & 127u) == 0u && ld_agent(status) != 0u) {
                     s_abort = 1;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
+#undef DSW_POLL
+#undef DSW_READY
         }
         DSW_TRACE(k, kTrArrived);
 #pragma unroll
@@ -750,13 +813,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             __syncthreads();
             if (s_abort) break;
         }
-        if (c == 0 && t < B) p.tokens[(size_t)t * gamma + k] = DSW_TOKEN(t);
         DSW_TRACE(k, kTrSelected);
-        if (p.trace != nullptr && t == 0)
-            p.trace[((size_t)c * (gamma + 1) + k) * 8 + kTrReal] = __builtin_amdgcn_s_memrealtime();
+        DSW_TRACE_REAL(k);
     }
+    if (c == 0 && t < B && !s_abort && gamma > 0) p.tokens[(size_t)t * gamma + gamma - 1] = DSW_TOKEN(t);
 #undef DSW_TOKEN
 
+    DSW_TRACE_FLUSH();
     if (c == 0 && t == 0 && !s_abort)
         __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -15,6 +15,7 @@ constexpr int kLdsWork = 16384;     // LDS bytes reserved for u vectors and redu
 constexpr int kTileRows = 16;       // MFMA engine: vocabulary rows per 16x16x32 tile
 constexpr int kTileBytes = kTileRows * kRank * 2;   // 8 KiB of bf16 weights per tile
 constexpr int kMaxRegTiles = 8;     // weight tiles per wave in the 256 AGPRs
+constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 
 // Device workspace.  Cross-workgroup traffic goes through per-workgroup
 // mailboxes tagged with a step epoch: workgroup c writes its words for step
@@ -95,7 +96,8 @@ struct WalkParams {
 };
 
 // Phase timestamps recorded per workgroup and step when a trace buffer is set
-// (s_memtime core-clock counts; slot 7 holds s_memrealtime at 100 MHz).
+// (s_memrealtime, the device-wide 100 MHz clock, so that workgroups on
+// different XCDs compare; slot 7 holds the core-clock counter s_memtime).
 enum TracePhase {
     kTrStepStart = 0,   // top of the step
     kTrGathered = 1,    // u and the base logits staged (after the barrier)
@@ -104,7 +106,7 @@ enum TracePhase {
     kTrPosted = 4,      // key posted and arrival counted
     kTrArrived = 5,     // every workgroup has arrived
     kTrSelected = 6,    // tokens known (end of step)
-    kTrReal = 7,        // s_memrealtime at the end of the step
+    kTrReal = 7,        // s_memtime (core clock) at the end of the step
 };
 
 }  // namespace dsw
