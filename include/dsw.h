@@ -89,8 +89,9 @@ extern "C" {
                                     DSW_ERR_DEV_TIMEOUT; the kernel never hangs.    */
 #define DSW_FLAG_VALU_GEMV 4u    /* force the VALU shard GEMV                        */
 #define DSW_FLAG_MFMA_GEMV 8u    /* force the MFMA shard GEMV.  Without either flag
-                                    one request per call takes the VALU engine and
-                                    more take the MFMA engine (measured faster).     */
+                                    bf16 rows take the MFMA engine and one int8
+                                    request takes the VALU engine (measured
+                                    faster on MI355X).                             */
 #define DSW_FLAG_BATCHED 16u     /* use the batched kernel for every batch size.  It
                                     serves B > 16 always: requests in groups of 16
                                     on the MFMA engine, one owner workgroup per

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libdsw.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b4.hip", "walk_mfma_b16.hip", "walk_mfma_i8.hip", "walk_batched.hip"]
+HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b1.hip", "walk_mfma_b4.hip", "walk_mfma_b16.hip", "walk_mfma_i8.hip", "walk_batched.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 # Packed-fp32 VALU forms are kept out of every code object.

@@ -10,6 +10,7 @@
 #include "walk_params.h"
 
 extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile, int w2_dtype);
+extern "C" const void* dsw_internal_mfma_kernel_b1(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
@@ -21,6 +22,7 @@ const void* kernel_for(const dsw_plan_info& pl) {
     if (pl.engine == DSW_ENGINE_VALU) return dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile, pl.w2_dtype);
     if (pl.batch_tile == dsw::kMaxBatch) return dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
     if (pl.w2_dtype == DSW_INT8) return dsw_internal_mfma_i8_kernel(pl.batch_tile, pl.reg_tiles, pl.max_tiles);
+    if (pl.batch_tile == 1) return dsw_internal_mfma_kernel_b1(pl.reg_tiles, pl.max_tiles);
     if (pl.batch_tile == 4) return dsw_internal_mfma_kernel_b4(pl.reg_tiles, pl.max_tiles);
     if (pl.batch_tile == 16) return dsw_internal_mfma_kernel_b16(pl.reg_tiles, pl.max_tiles);
     return nullptr;

@@ -49,10 +49,12 @@ static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 // (register tiles, tiles per wave) shapes compiled for each batch tile; must
 // match DSW_MFMA_SHAPES in walk_kernel.h.
 static const int kShapes[][2] = {{2, 2}, {4, 4}, {8, 8}, {8, 10}, {8, 16}};
+// one request (DSW_MFMA_ONE_SHAPES): AGPR tiles, then up to kMaxVgprTiles VGPR tiles
+static const int kShapesOne[][2] = {{2, 2}, {4, 4}, {8, 8}, {10, 10}, {12, 12}, {12, 16}};
 // int8 rows (DSW_MFMA_I8_SHAPES): a tile row takes half the registers
 static const int kShapesI8[][2] = {{4, 4}, {8, 8}, {16, 16}};
 static const int kStreamShape[2] = {0, 16};
-static int mfma_tile_for(int B) { return B <= 4 ? 4 : 16; }
+static int mfma_tile_for(int B, bool i8) { return (B <= 1 && !i8) ? 1 : (B <= 4 ? 4 : 16); }
 // Upper bound of the MFMA kernel's static LDS for (batch tile, tiles per
 // wave, int8 rows with their fp32 scales).
 static int mfma_static_lds(int nb, int max_tiles, bool i8) {
@@ -86,6 +88,13 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
                 max_t = sh[1];
                 break;
             }
+    } else if (mfma_tile_for(B, i8) == 1) {
+        for (const auto& sh : kShapesOne)
+            if (sh[1] >= TW) {
+                reg_t = sh[0];
+                max_t = sh[1];
+                break;
+            }
     } else {
         for (const auto& sh : kShapes)
             if (sh[1] >= TW) {
@@ -95,7 +104,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
             }
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
-    const int nb = mfma_tile_for(B);
+    const int nb = mfma_tile_for(B, i8);
     const int lds_static = mfma_static_lds(nb, max_t, i8);
     int avail = dev->max_lds_per_block - lds_static;
     if (avail < 0) return DSW_ERR_PLAN;
@@ -303,15 +312,16 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const int R = (int)rows;
     // kernel: the batched one beyond 16 requests or when asked for; an engine
     // flag forces the all-to-all kernel (up to 16 requests).  Otherwise, as
-    // measured on MI355X at V = 151,936: VALU for one request (int8 rows are
-    // widened to bf16 on chip), the MFMA all-to-all kernel for 2-3, the batched kernel
-    // from 4 requests (falling back to the all-to-all kernel where it has no
-    // shape, e.g. int8 rows beyond 12 tiles per wave).
+    // measured on MI355X: one bf16 request on the MFMA engine (V = 151,936,
+    // gamma = 7: 39.7 against 42.5 us per round on VALU), one int8 request on
+    // VALU (rows widened to bf16 on chip), the MFMA all-to-all kernel for 2-3,
+    // the batched kernel from 4 requests (falling back to the all-to-all kernel
+    // where it has no shape, e.g. int8 rows beyond 12 tiles per wave).
     const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
-    if (!forced) valu = B <= 1;
+    if (!forced) valu = B <= 1 && i8;
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);

@@ -57,6 +57,13 @@ __device__ __forceinline__ f32x4_t mfma_tile(const uint4 a, const uint4 b, f32x4
                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
+// MFMA engine: the 8-latent chunk that lane group gg (lanes 16gg .. 16gg+15)
+// supplies in K block kb.  Chunks are dealt so that each lane's 8 K blocks are
+// 8 consecutive chunks of its row (128 contiguous bytes of bf16 weights), not
+// every fourth chunk; A (u) and B (W2) use the same map, so the contraction
+// covers every latent once.
+#define DSW_KC(kb, gg) ((gg) * 8 + (kb))
+
 // Workgroup-local 32-bit key: {order-preserving bf16 logit, ~row in shard}.
 __device__ __forceinline__ uint32_t local_key(uint32_t lbits, int r) {
     return (ord16(lbits) << 16) | (0xFFFFu - (uint32_t)r);
@@ -75,6 +82,21 @@ __device__ __forceinline__ void pin_agpr(uint4& v) {
     asm volatile("" : "+a"(v.x), "+a"(v.y), "+a"(v.z), "+a"(v.w));
 }
 __device__ __forceinline__ void pin_agpr(uint2& v) { asm volatile("" : "+a"(v.x), "+a"(v.y)); }
+__device__ __forceinline__ void pin_vgpr(uint4& v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void pin_vgpr(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+
+// One request on the MFMA engine: tile j's 16 results sit in lanes 0..15 of
+// its accumulator's first register.  Two permlane16 swaps and one permlane32
+// swap gather four tiles into one register, lane l holding row l%16 of tile
+// l/16, i.e. the 64 consecutive rows of the four tiles.
+__device__ __forceinline__ float combine4(float t0, float t1, float t2, float t3) {
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t0), __float_as_uint(t1), false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t2), __float_as_uint(t3), false, false);
+    const auto s = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+    return __uint_as_float(s[0]);
+}
 
 // One K block of a lane's tile row as the MFMA's 8 bf16 values.
 __device__ __forceinline__ uint4 as_bf16x8(const uint4& w) { return w; }
@@ -98,16 +120,22 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // (VALU; int8 rows are widened to bf16 once, at entry)
     using WT = typename std::conditional<kI8 && kMfma, uint2, uint4>::type;
     static_assert(NB == 1 || NB == 4 || NB == 16, "batch tile");
-    static_assert(!kMfma || (NB >= 4 && A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles), "MFMA shape");
+    // one request on the MFMA engine: tiles gathered four at a time, up to
+    // kMaxRegTiles tiles per wave in AGPRs and kMaxVgprTiles more in VGPRs
+    constexpr bool kOne = kMfma && NB == 1;
+    static_assert(!kMfma || (A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles + (kOne ? kMaxVgprTiles : 0)),
+                  "MFMA shape");
+    static_assert(!kOne || !kI8, "one-request MFMA engine: bf16 rows");
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
     constexpr int RPAD = kMfma ? M * 4 * kTileRows : kMaxSlots * kBlock;  // rows per shard, bound
     constexpr int CHMAX = (RPAD + kBlock - 1) / kBlock;                    // scan rows per thread
     constexpr int US = kRowChunks + 1;                                     // padded u row (uint4)
-    constexpr int KPL = kMfma ? 4 : NB;                                    // request keys per lane
+    constexpr int KPL = (kMfma && !kOne) ? 4 : NB;                         // request keys per lane
+    constexpr int NQ = kOne ? (M + 3) / 4 : 1;                             // 4-tile groups per wave
     extern __shared__ uint4 s_w[];  // LDS-resident weights (engine-specific layout)
 
     __shared__ uint4 s_u[NB * US];
-    __shared__ uint16_t s_base[kMfma ? NB * RPAD : 1];
+    __shared__ uint16_t s_base[kMfma && !kOne ? NB * RPAD : 1];
     __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ uint16_t s_logit[NB * RPAD];
     __shared__ uint32_t s_wbest[4][NB];
@@ -186,17 +214,28 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // ---- entry: this workgroup's shard on chip -------------------------
     WT wr[A > 0 ? A : 1][kMfma ? 8 : kRowChunks];
     uint32_t bs[kMfma ? 1 : NB][kMfma ? 1 : kMaxSlots];  // VALU: base logits of the lane's rows
+    uint32_t bq[NQ];  // one request, MFMA: base logits of rows wrow0 + 64q + lane
+    // one request, MFMA: does group q's row for this lane exist in the shard
+#define DSW_ONE_ROW_OK(q) ((4 * (q) + (lane >> 4)) < nt_w && wrow0 + 64 * (q) + lane < nrows)
     if constexpr (kMfma) {
 #pragma unroll
         for (int j = 0; j < A; ++j) {
             // rows outside the shard load some valid row instead (no second,
             // zeroed copy of the registers); their results are never used
             const int row = min(v0 + wrow0 + j * kTileRows + n, V - 1);
-            const WT* src = W2 + (size_t)row * kRowChunks + g;
+            const WT* src = W2 + (size_t)row * kRowChunks;
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
+            for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[DSW_KC(kb, g)];
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) pin_agpr(wr[j][kb]);
+            for (int kb = 0; kb < 8; ++kb) {
+                if (j < kMaxRegTiles) pin_agpr(wr[j][kb]);
+                else pin_vgpr(wr[j][kb]);
+            }
+        }
+        if constexpr (kOne) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                bq[q] = (B > 0 && DSW_ONE_ROW_OK(q)) ? (uint32_t)base[v0 + wrow0 + 64 * q + lane] : 0u;
         }
         // LDS tiles: 8 loads per thread in flight before their stores; only
         // tiles that exist in this shard have an LDS slot
@@ -211,7 +250,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int r = ws * TW * kTileRows + j * kTileRows + (ln & 15);
                 v[q] = WT{};
                 if (idx < 4 * LT * 512 && j < TW && r < nrows)
-                    v[q] = W2[(size_t)(v0 + r) * kRowChunks + kb * 4 + (ln >> 4)];
+                    v[q] = W2[(size_t)(v0 + r) * kRowChunks + DSW_KC(kb, ln >> 4)];
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -225,7 +264,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         }
         if constexpr (kI8)
             for (int r = t; r < RPAD; r += kBlock) s_scale[r] = r < nrows ? p.w2_scale[v0 + r] : 0.0f;
-        for (int i0 = 0; i0 < NB * RPAD; i0 += 8 * kBlock) {
+        for (int i0 = 0; i0 < (kOne ? 0 : NB * RPAD); i0 += 8 * kBlock) {
             uint16_t v[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -322,7 +361,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         const int q = (int)(seq & 1u);
         unsigned long long* mail_q = p.ws.mail + (size_t)q * kMaxGrid * kMailWords;
 
-        if constexpr (kMfma) {
+        if constexpr (kMfma && !kOne) {
             if (k > 0) {  // this step's base logits for the shard, loads batched
                 for (int b = 0; b < B; ++b) {
                     const uint16_t* src = base + ((size_t)b * gamma + k) * V + v0;
@@ -357,7 +396,59 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             // A operand: lane l carries u of request l%16, latent 8*(l/16).. of each K block
             uint4 a[8];
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) a[kb] = (n < B) ? s_u[n * US + kb * 4 + g] : make_uint4(0u, 0u, 0u, 0u);
+            for (int kb = 0; kb < 8; ++kb) a[kb] = (n < B) ? s_u[n * US + DSW_KC(kb, g)] : make_uint4(0u, 0u, 0u, 0u);
+          if constexpr (kOne) {
+            // Groups of four tiles: four independent MFMA chains, gathered into
+            // one register, then one 64-lane epilogue.  Register tiles are
+            // multiplied even beyond nt_w (they hold valid rows; results are
+            // masked), LDS and streamed tiles only where they exist.
+#pragma unroll
+            for (int gq = 0; gq < NQ; ++gq) {
+                if (4 * gq < nt_w) {
+                    f32x4_t d[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int j = 4 * gq + jj;
+                        d[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                        if (j < A) {
+#pragma unroll
+                            for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], wr[j < A ? j : 0][kb], d[jj]);
+                        } else if (j < M && j < nt_w) {
+                            if (j - A < LT) {
+                                const int sb = (wave * LT + (j - A)) * 512 + lane;
+#pragma unroll
+                                for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
+                            } else {
+                                const int r = wrow0 + j * kTileRows + n;
+                                const bool ok = r < nrows;
+                                const uint4* src = reinterpret_cast<const uint4*>(p.W2) +
+                                                   (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
+#pragma unroll
+                                for (int kb = 0; kb < 8; ++kb)
+                                    d[jj] = mfma_tile(a[kb], ok ? src[DSW_KC(kb, g)] : make_uint4(0u, 0u, 0u, 0u),
+                                                      d[jj]);
+                            }
+                        }
+                    }
+                    const float acc1 = combine4(d[0][0], d[1][0], d[2][0], d[3][0]);
+                    if (DSW_ONE_ROW_OK(gq)) {
+                        const int r = wrow0 + 64 * gq + lane;
+                        const uint32_t bias = f32_to_bf16(acc1);
+                        const uint32_t lbits = f32_to_bf16(bf16_to_f32(bq[gq]) + bf16_to_f32(bias));
+                        best[0] = max(best[0], local_key(lbits, r));
+                        s_logit[r] = (uint16_t)lbits;
+                    }
+                }
+            }
+            // the next step's base logits land while the rendezvous is in flight
+            if (k + 1 < gamma) {
+#pragma unroll
+                for (int gq = 0; gq < NQ; ++gq)
+                    bq[gq] = DSW_ONE_ROW_OK(gq)
+                                 ? (uint32_t)base[(size_t)(k + 1) * V + v0 + wrow0 + 64 * gq + lane]
+                                 : 0u;
+            }
+          } else {
             const int lofs = 4 * g * RPAD + wrow0 + n;
 #define DSW_EPI_MFMA(dv, j)                                                                      \
     do {                                                                                         \
@@ -407,14 +498,16 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     } else {
                         const int r = wrow0 + j * kTileRows + n;
                         const bool ok = r < nrows;
-                        const WT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks + g;
+                        const WT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
 #pragma unroll
-                        for (int kb = 0; kb < 8; ++kb) dd = mfma_tile(a[kb], as_bf16x8(ok ? src[kb * 4] : WT{}), dd);
+                        for (int kb = 0; kb < 8; ++kb)
+                            dd = mfma_tile(a[kb], as_bf16x8(ok ? src[DSW_KC(kb, g)] : WT{}), dd);
                     }
                     DSW_EPI_MFMA(dd, j);
                 }
             }
 #undef DSW_EPI_MFMA
+          }
         } else {
             float acc[NB][kMaxSlots];
 #pragma unroll
@@ -528,7 +621,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         DSW_TRACE(k, kTrGemvDone);
 
         // workgroup argmax per request: DPP within the wave, then 4 waves via LDS
-        if constexpr (kMfma) {
+        if constexpr (kMfma && !kOne) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) best[i] = row16_max_u32(best[i]);
             if (n == 0) {
@@ -818,6 +911,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     }
     if (c == 0 && t < B && !s_abort && gamma > 0) p.tokens[(size_t)t * gamma + gamma - 1] = DSW_TOKEN(t);
 #undef DSW_TOKEN
+#undef DSW_ONE_ROW_OK
 
     DSW_TRACE_FLUSH();
     if (c == 0 && t == 0 && !s_abort)
@@ -828,5 +922,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #define DSW_MFMA_SHAPES(X) X(2, 2) X(4, 4) X(8, 8) X(8, 10) X(8, 16) X(0, 16)
 // the same for int8 weights (a tile row is half as large)
 #define DSW_MFMA_I8_SHAPES(X) X(4, 4) X(8, 8) X(16, 16) X(0, 16)
+// one request: up to kMaxRegTiles AGPR tiles plus kMaxVgprTiles VGPR tiles per wave
+#define DSW_MFMA_ONE_SHAPES(X) X(2, 2) X(4, 4) X(8, 8) X(10, 10) X(12, 12) X(12, 16) X(0, 16)
 
 }  // namespace dsw

@@ -1,0 +1,14 @@
+// walk_mfma_b1.hip -- MFMA-engine walk kernels (walk_kernel.h) for one request
+// per launch: register tiles in AGPRs and VGPRs, four tiles' results gathered
+// into one register per epilogue.
+#include "walk_kernel.h"
+
+// Host-side lookup used by the launcher: the kernel for (register tiles,
+// tiles per wave) at batch tile 1, or nullptr when that shape is not compiled.
+extern "C" const void* dsw_internal_mfma_kernel_b1(int reg_tiles, int max_tiles) {
+#define DSW_PICK(R, M) \
+    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_kernel<dsw::kEngineMfma, (R), (M), 1>;
+    DSW_MFMA_ONE_SHAPES(DSW_PICK)
+#undef DSW_PICK
+    return nullptr;
+}

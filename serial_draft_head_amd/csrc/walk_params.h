@@ -15,6 +15,7 @@ constexpr int kLdsWork = 16384;     // LDS bytes reserved for u vectors and redu
 constexpr int kTileRows = 16;       // MFMA engine: vocabulary rows per 16x16x32 tile
 constexpr int kTileBytes = kTileRows * kRank * 2;   // 8 KiB of bf16 weights per tile
 constexpr int kMaxRegTiles = 8;     // weight tiles per wave in the 256 AGPRs
+constexpr int kMaxVgprTiles = 4;    // one request, MFMA engine: further tiles per wave in VGPRs
 constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 
 // Device workspace.  Cross-workgroup traffic goes through per-workgroup

@@ -116,7 +116,8 @@ def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
         assert p.lds_bytes >= 4 * p.lds_tiles * 8192 + p.ring_slots * (8192 + 32 * p.rows_pad)
     if engine != "valu":
         assert p.tiles_per_wave * 4 * 16 >= rows
-        assert p.reg_tiles <= 8 and p.tiles_per_wave <= p.max_tiles
+        # one request keeps up to 4 more tiles per wave in VGPRs
+        assert p.reg_tiles <= (12 if p.batch_tile == 1 else 8) and p.tiles_per_wave <= p.max_tiles
         assert p.reg_tiles + p.lds_tiles <= max(p.tiles_per_wave, p.reg_tiles)
         assert p.lds_bytes >= p.lds_rows * 512
     else:
@@ -127,16 +128,27 @@ def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
 def test_planner_choices_on_mi355x_shapes(dsw):
     d = fake_device(dsw)
     pick = lambda p: (p.rows_per_wg, p.tiles_per_wave, p.reg_tiles, p.lds_tiles, p.stream_rows)
-    # by default one request takes the VALU engine, more take the MFMA engine
-    assert dsw.plan(d, 151_936, 7, 1).engine == 0 and dsw.plan(d, 151_936, 7, 2).engine == 1
+    # by default bf16 rows take the MFMA engine (one request: batch tile 1),
+    # one int8 request the VALU engine
+    assert dsw.plan(d, 151_936, 7, 1).engine == 1 and dsw.plan(d, 151_936, 7, 1).batch_tile == 1
+    assert dsw.plan(d, 151_936, 7, 2).engine == 1
+    assert dsw.plan(d, 151_936, 7, 1, w2_dtype=dsw.INT8).engine == 0
     assert pick(dsw.plan(d, 32_000, 7, 1, flags=8)) == (125, 2, 2, 0, 0)
+    # one request on the MFMA engine: 10 tiles per wave all in registers (8 AGPR + 2 VGPR)
     c1 = dsw.plan(d, 151_936, 7, 1, flags=8)
-    assert pick(c1) == (594, 10, 8, 2, 0) and c1.path == 0 and c1.onchip_bytes == 151_936 * 512
+    assert pick(c1) == (594, 10, 10, 0, 0) and c1.path == 0 and c1.onchip_bytes == 151_936 * 512
+    assert c1.batch_tile == 1
+    # V = 248,320: 12 register tiles and 4 LDS tiles per wave, nothing streamed
+    c3 = dsw.plan(d, 248_320, 16, 1, flags=8)
+    assert pick(c3) == (970, 16, 12, 4, 0) and c3.batch_tile == 1
+    # two requests: the 4-request tile with 8 AGPR tiles and 2 LDS tiles
+    assert pick(dsw.plan(d, 151_936, 7, 2, flags=8)) == (594, 10, 8, 2, 0)
     c2 = dsw.plan(d, 151_936, 16, 16, flags=8)
     assert pick(c2) == (594, 10, 8, 2, 0) and c2.batch_tile == 16
     # by default 2-3 requests take the all-to-all MFMA kernel, 4 and more the batched one
     assert [dsw.plan(d, 151_936, 16, b).batch_tile for b in (2, 3, 4, 16)] == [4, 4, 256, 256]
-    c3 = dsw.plan(d, 248_320, 16, 1, flags=8)
+    # 4 requests at V = 248,320: 8 AGPR tiles per wave, LDS for some, the rest streamed
+    c3 = dsw.plan(d, 248_320, 16, 4, flags=8)
     assert c3.rows_per_wg == 970 and c3.tiles_per_wave == 16 and c3.path == 1 and c3.stream_rows > 0
     c4 = dsw.plan(d, 129_280, 5, 16, flags=8)
     assert pick(c4) == (505, 8, 8, 0, 0)
