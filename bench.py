@@ -170,6 +170,32 @@ def cpu_baseline(index, B, gamma, V, W1, W2, budget_s=15.0):
 
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
 
+
+def gamma_sweep(torch, dsw, W1d, W2d, V, gammas=(1, 4, 7, 10, 16), rounds=60, K=200):
+    """Walk time against gamma, fitted as t = entry + gamma * step by least
+    squares, once with the shard resident and once with nothing on chip
+    (DSW_FLAG_FORCE_STREAM: W2 re-read every step inside the one launch).
+    The resident entry is the one-time shard load; the difference between the
+    two per-step costs is what residency saves on each step."""
+    out = {}
+    for name, flags in (("resident", 0), ("streamed", dsw.FLAG_FORCE_STREAM)):
+        walker = dsw.Walker(V, gamma_max=max(gammas), B_max=1, flags=flags)
+        pts = []
+        for g in gammas:
+            d = to_device(make_rounds(1, rounds, 1, g, V, "greedy"), torch, W1d.device)
+            us, _ = time_walk(torch, walker, W1d, W2d, d, K, 10)
+            pts.append((g, us))
+            del d
+        st = walker.status()
+        walker.close()
+        x = np.array([p[0] for p in pts], dtype=np.float64)
+        y = np.array([p[1] for p in pts], dtype=np.float64)
+        step, entry = np.polyfit(x, y, 1)
+        out[name] = {"us_per_round": {int(g): round(u, 2) for g, u in pts},
+                     "entry_us": round(float(entry), 2), "us_per_step": round(float(step), 3),
+                     "status": st}
+    return out
+
 # Every configuration the walk is checked on, timed briefly after the headline
 # line's own measurements: (workload, requests, gamma, W2 storage).
 SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, "bf16"),
@@ -260,6 +286,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations")
     ap.add_argument("--pmc-mode", action="store_true",
                     help="for counter runs: 50 walks, then one 256 MiB device copy of known size")
+    ap.add_argument("--stepwise-only", action="store_true",
+                    help="for counter runs: only the step-wise library-op loop, then the same copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -287,6 +315,16 @@ def main():
     plan = walker.query_plan(B).as_dict()
     log("plan", plan)
 
+    if args.stepwise_only:
+        sw = stepwise_torch(torch, W1d, W2d, dev_rounds, 20)
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"stepwise_only": True, "rounds": 23, "us_per_round": round(sw, 3),
+                          "copy_bytes": COPY_BYTES}))
+        return
     if args.pmc_mode:
         base, anchor, T, uni = dev_rounds
         for i in range(50):
@@ -371,7 +409,13 @@ def main():
         log(f"step-wise torch: {sw:.2f} us/round")
 
     walker.close()
-    del dev_rounds, W1d, W2d
+    del dev_rounds
+    torch.cuda.empty_cache()
+    # gamma sweep at this vocabulary: one-time entry vs per-step cost, resident vs streamed
+    if B == 1 and V == 151_936 and not args.no_sweep:
+        result["gamma_sweep"] = gamma_sweep(torch, dsw, W1d, W2d, V)
+        log("gamma sweep", result["gamma_sweep"])
+    del W1d, W2d
     torch.cuda.empty_cache()
     if not args.no_sweep:
         result["configs"] = []
