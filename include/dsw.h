@@ -161,8 +161,11 @@ int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int
 /* Create a handle for walks on `device` with vocabulary V, rank r (must be
  * 256), at most gamma_max steps and B_max (1 .. 256) requests per call, and W2 stored
  * as w2_dtype.  Allocates and zeroes the device workspace (cross-workgroup
- * mailboxes, arrival counters, a round counter and a status word); the handle
- * owns it.  The calling thread's current device is left unchanged. */
+ * mailboxes, arrival counters, a round counter and a status word), and, when
+ * the handle can run the batched kernel (B_max >= 4 or DSW_FLAG_BATCHED),
+ * B_max * V * 2 bytes where that kernel keeps the current step's logits of its
+ * sampled requests for the shard that draws their token; the handle owns
+ * both.  The calling thread's current device is left unchanged. */
 int dsw_create(dsw_handle_t* h, int device, int V, int r, int gamma_max, int B_max,
                int w2_dtype, unsigned flags);
 

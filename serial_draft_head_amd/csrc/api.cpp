@@ -36,6 +36,7 @@ struct dsw_handle {
     dsw_devinfo dev;
     char* ws_mem;
     size_t ws_bytes;
+    uint16_t* blog_mem;  // batched kernel: logits of sampled requests, [B_max][V] bf16
     dsw::Workspace ws;
     unsigned long long* trace;  // optional device trace buffer (caller-owned)
     long long trace_bytes;
@@ -144,8 +145,20 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
     h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
     h->ws.bext = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bext);
+    // the batched kernel keeps the current step's logits of its sampled
+    // requests here for the token shards (B_max * V * 2 bytes)
+    h->blog_mem = nullptr;
+    if (B_max >= dsw::kBatchedFrom || (flags & DSW_FLAG_BATCHED)) {
+        if (hipMalloc(&h->blog_mem, (size_t)B_max * (size_t)V * 2) != hipSuccess) {
+            (void)hipFree(h->ws_mem);
+            delete h;
+            return DSW_ERR_HIP;
+        }
+    }
+    h->ws.blog = h->blog_mem;
     if (clear_workspace(h) != DSW_OK) {
         (void)hipFree(h->ws_mem);
+        if (h->blog_mem) (void)hipFree(h->blog_mem);
         delete h;
         return DSW_ERR_HIP;
     }
@@ -168,6 +181,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         if (!ok) {
             (void)hipGetLastError();
             (void)hipFree(h->ws_mem);
+            if (h->blog_mem) (void)hipFree(h->blog_mem);
             delete h;
             return prc != DSW_OK ? prc : DSW_ERR_LAUNCH;
         }
@@ -291,6 +305,7 @@ extern "C" int dsw_destroy(dsw_handle_t h) {
             (void)hipDeviceSynchronize();
             (void)hipFree(h->ws_mem);
         }
+        if (h->blog_mem) (void)hipFree(h->blog_mem);
     }
     delete h;
     return DSW_OK;

@@ -170,11 +170,10 @@ static const int kBShapesI8[][2] = {{8, 8}, {8, 12}};
 static const int kBStreamShape[2] = {0, 12};
 static int batched_static_lds(int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
-    return 4 * kMaxBatch * 4 * 3 + 4 * kMaxBatch * 4 + kMaxGrid * 4 + kMaxBatch * 4 + 2 * rpad +
+    return 4 * kMaxBatch * 4 * 3 + 4 * kMaxBatch * 4 + kMaxGrid * 4 + kMaxBatch * 4 +
            (i8 ? 4 * rpad : 0) + 1024 + kTraceLds;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
-static const int kBatchedFrom = 4;  // default: the batched kernel from this many requests
 
 static int plan_batched(const dsw_devinfo* dev, int V, int B, unsigned flags, int grid, bool i8,
                         dsw_plan_info* out) {

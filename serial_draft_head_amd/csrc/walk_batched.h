@@ -21,9 +21,10 @@
 //   workgroup and step.  Here request b is owned by workgroup b % G: every
 //   workgroup stores its B key words (and exp-sum words) in one row, the owner
 //   reads column b, and publishes the token (greedy) or the shard whose mass
-//   holds u*Z (sampled).  That shard recomputes its logits of request b (the
-//   weights are still in registers), finds the token, and publishes it.
-//   Greedy steps take two exchanges, sampled steps three.
+//   holds u*Z (sampled).  That shard scans its logits of request b (written
+//   out during the step: to `logits` if the caller wants them, else to the
+//   workspace), finds the token, and publishes it.  Greedy steps take two
+//   exchanges, sampled steps three.
 #pragma once
 #include "walk_kernel.h"
 
@@ -89,7 +90,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
     static_assert(A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles && (A % 2) == 0, "shape");
     constexpr int RPAD = M * 4 * kTileRows;  // shard rows, bound
-    constexpr int CHMAX = (RPAD + kBlock - 1) / kBlock;
     extern __shared__ uint4 s_dyn[];  // [LDS weight tiles][ring slots]
 
     __shared__ uint32_t s_rkey[4][kMaxBatch];  // per wave and request: local key
@@ -100,14 +100,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ float s_T[kMaxBatch];
     __shared__ unsigned s_dec[kMaxBatch];
     __shared__ float s_S[kMaxGrid];
-    __shared__ uint16_t s_tl[RPAD];            // one request's recomputed shard logits
     __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ int s_tasks[kMaxBatch];
     __shared__ uint2 s_junk[64];               // epilogue writes of tiles beyond a wave's rows
     __shared__ unsigned long long s_red64[4];
-    __shared__ float s_redf[4];
-    __shared__ int s_redi[4];
-    __shared__ int s_redj[4];
     __shared__ int s_own;
     __shared__ float s_pex;
     __shared__ float s_tgt;
@@ -132,6 +128,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const int CPR = Rpad >> 3;    // 16-byte chunks per request row of a base slot
     const int v0 = c * R;
     const int nrows = max(0, min(V, v0 + R) - v0);
+    // register slots beyond the shard load its last row (a cache hit), never
+    // another shard's rows (extra HBM reads); an empty shard loads row V - 1
+    const int last_row = nrows > 0 ? v0 + nrows - 1 : V - 1;
     const int TW = p.tiles_per_wave;
     const int LT = p.lds_tiles;
     const int wrow0 = wave * TW * kTileRows;
@@ -178,7 +177,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     WT wr[A > 0 ? A : 1][8];
 #pragma unroll
     for (int j = 0; j < A; ++j) {
-        const int row = min(v0 + wrow0 + j * kTileRows + n, V - 1);
+        const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
         const WT* src = W2 + (size_t)row * kRowChunks + g;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
@@ -209,7 +208,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __syncthreads();
     const unsigned round = s_round;
     const bool any_samp = s_any_samp != 0;
-    const int CH = (nrows + kBlock - 1) / kBlock;
 
     // MFMA over every tile of this wave with B operand ub[8]; EPI(d, j) gets
     // the four results (rows 4g .. 4g+3 of tile j, request column n)
@@ -259,7 +257,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
                     dd = mfma_tile(as_bf16x8(s_wt[sb_ + kb * 64]), ub[kb], dd);                   \
             } else {                                                                             \
-                const int row_ = min(v0 + wrow0 + j * kTileRows + n, V - 1);                     \
+                const int row_ = min(v0 + wrow0 + j * kTileRows + n, last_row);                  \
                 const WT* src_ = W2 + (size_t)row_ * kRowChunks + g;                             \
                 _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
                     dd = mfma_tile(as_bf16x8(src_[kb * 4]), ub[kb], dd);                          \
@@ -371,15 +369,19 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             DSW_TILES(DSW_EPI_G);
 #undef DSW_EPI_G
             uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
-            if (p.logits != nullptr) {
-                // the group's logits, out of the slot with whole-row stores
+            if (p.logits != nullptr || any_samp) {
+                // the group's logits, out of the slot with whole-row stores: to
+                // `logits` when asked for, and for sampled requests in any case
+                // (to the workspace otherwise), where the token shard reads them
                 barrier_keep_vm();
                 for (int e = t; e < kGroup * CPR; e += kBlock) {
                     const int nn = (int)(((unsigned)e * cpr_mul) >> 20), cr = e - nn * CPR;
                     const int bq = grp * kGroup + nn, r0 = cr * 8;
-                    if (bq < B && r0 < nrows) {
+                    if (bq < B && r0 < nrows && (p.logits != nullptr || s_T[bq] > 0.0f)) {
                         const uint4 w = *reinterpret_cast<const uint4*>(sb + (nn * CPR + (cr ^ nn)) * 8);
-                        uint16_t* o = p.logits + ((size_t)bq * gamma + k) * V + v0 + r0;
+                        uint16_t* o = (p.logits != nullptr ? p.logits + ((size_t)bq * gamma + k) * V
+                                                           : p.ws.blog + (size_t)bq * V) +
+                                      v0 + r0;
                         if (aligned && r0 + 8 <= nrows) {
                             *reinterpret_cast<uint4*>(o) = w;
                         } else {
@@ -567,111 +569,74 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         DSW_TRACE(k, kTrArrived);
 
         // ---- sampled requests whose token lies in this shard --------------
+        // Their logits of this shard were written out in the group loop; each
+        // wave takes every fourth task and scans the shard's rows in vocabulary
+        // order (RL consecutive rows per lane) for the first cumulative mass
+        // above u*Z, from the owner's prefix before this shard.
         if (any_samp) {
             if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] >> 21) == c)
                 s_tasks[atomicAdd(&s_ntask, 1)] = t;
             __syncthreads();
             const int ntask = s_ntask;
-            for (int i = 0; i < ntask; ++i) {
+            constexpr int RLMAX = (RPAD + 63) / 64;  // rows per lane, bound
+            const int RL = (nrows + 63) / 64;
+            for (int i = wave; i < ntask; i += 4) {
                 const int b = s_tasks[i];
-                const float Tb = s_T[b];
-                const float sc2 = kLog2e / Tb;
-                // the owner's prefix before this shard and u*Z
-                if (t < 2) {
-                    const unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2 + t;
+                const float sc2 = kLog2e / s_T[b];
+                // the owner's prefix before this shard (lane 0) and u*Z (lane 1)
+                float ev = 0.0f;
+                bool ok = true;
+                if (lane < 2) {
+                    const unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2 + lane;
                     unsigned it = 0;
                     unsigned long long w = 0ull;
                     while (((w = ld_agent64(ext)) & kEpochMod) != epoch) {
-                        if (++it >= p.spin_limit) { latch(status, kStatusTimeout); s_abort = 1; break; }
-                        if ((it & 255u) == 0u && ld_agent(status) != 0u) { s_abort = 1; break; }
+                        if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
+                        if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
                         __builtin_amdgcn_s_sleep(1);
                     }
-                    const float v = __uint_as_float((uint32_t)(w >> 32));
-                    if (t == 0) s_pex = v;
-                    else s_tgt = v;
+                    ev = __uint_as_float((uint32_t)(w >> 32));
                 }
+                if (!ok) s_abort = 1;
+                const float pexcl = __shfl(ev, 0), target = __shfl(ev, 1);
                 const float Mg = bf16_to_f32(unord16(s_dec[b] & 0xFFFFu));
-                // this shard's logits of request b, recomputed in its column
-                const int nb = b & (kGroup - 1);
-                const uint4* urow = W1 + (size_t)s_prev[b] * kRowChunks;
-                uint4 ub[8];
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb) ub[kb] = (n == nb) ? urow[kb * 4 + g] : make_uint4(0u, 0u, 0u, 0u);
-    // the same arithmetic as the group loop, so the logits are the same bits
-#define DSW_EPI_T(dv, j)                                                                         \
-    do {                                                                                         \
-        const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
-        if (n == nb && (j) < nt_w && rb_ < nrows) {                                              \
-            const uint16_t* bp_ = base + ((size_t)b * gamma + k) * V + v0 + rb_;                 \
-            const int lim_ = nrows - rb_;                                                        \
-            uint32_t bb_[4];                                                                     \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) bb_[i] = i < lim_ ? bp_[i] : 0u;       \
-            float x0_ = (dv)[0], x1_ = (dv)[1], x2_ = (dv)[2], x3_ = (dv)[3];                    \
-            if constexpr (kI8) {                                                                 \
-                x0_ *= s_scale[rb_];                                                             \
-                x1_ *= s_scale[rb_ + 1];                                                         \
-                x2_ *= s_scale[rb_ + 2];                                                         \
-                x3_ *= s_scale[rb_ + 3];                                                         \
-            }                                                                                    \
-            const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);       \
-            const uint32_t q01_ = pack_bf16_rne(bf16_to_f32(bb_[0]) + bf16_lo(p01_), bf16_to_f32(bb_[1]) + bf16_hi(p01_)); \
-            const uint32_t q23_ = pack_bf16_rne(bf16_to_f32(bb_[2]) + bf16_lo(p23_), bf16_to_f32(bb_[3]) + bf16_hi(p23_)); \
-            const uint32_t lb_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16};     \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) if (i < lim_) s_tl[rb_ + i] = (uint16_t)lb_[i]; \
-        }                                                                                        \
-    } while (0)
-                DSW_TILES(DSW_EPI_T);
-#undef DSW_EPI_T
-                __syncthreads();
-                // rows in vocabulary order, CH consecutive rows per thread
-                if (s_abort) break;
                 const uint32_t lk = max(max(s_rkey[0][b], s_rkey[1][b]), max(s_rkey[2][b], s_rkey[3][b]));
                 const float ml = local_key_logit(lk);
                 const float scale = __builtin_amdgcn_exp2f((ml - Mg) * sc2);
+                const uint16_t* lrow = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V
+                                                            : p.ws.blog + (size_t)b * V) + v0;
+                float wv[RLMAX];
                 float part = 0.0f;
 #pragma unroll
-                for (int rr = 0; rr < CHMAX; ++rr) {
-                    const int r = t * CH + rr;
-                    if (rr < CH && r < nrows) part += __builtin_amdgcn_exp2f((bf16_to_f32(s_tl[r]) - ml) * sc2);
+                for (int rr = 0; rr < RLMAX; ++rr) {
+                    const int r = lane * RL + rr;
+                    wv[rr] = (rr < RL && r < nrows) ? __builtin_amdgcn_exp2f((bf16_to_f32(lrow[r]) - ml) * sc2) : 0.0f;
+                    part += wv[rr];
                 }
                 const float incl = wave_incl_scan_dpp(part);
-                if (lane == 63) s_redf[wave] = incl;
-                __syncthreads();
-                float off = 0.0f;
-                for (int w = 0; w < wave; ++w) off += s_redf[w];
-                float run = off + (incl - part);
-                const float target = s_tgt, pexcl = s_pex;
+                float run = incl - part;
                 uint32_t first = 0u, lastw = 0u;  // row + 1, 0 = none
 #pragma unroll
-                for (int rr = 0; rr < CHMAX; ++rr) {
-                    const int r = t * CH + rr;
-                    if (rr < CH && r < nrows) {
-                        const float w = __builtin_amdgcn_exp2f((bf16_to_f32(s_tl[r]) - ml) * sc2);
-                        run += w;
+                for (int rr = 0; rr < RLMAX; ++rr) {
+                    const int r = lane * RL + rr;
+                    if (rr < RL && r < nrows) {
+                        run += wv[rr];
                         if (first == 0u && pexcl + scale * run > target) first = (uint32_t)r + 1u;
-                        if (w > 0.0f) lastw = (uint32_t)r + 1u;
+                        if (wv[rr] > 0.0f) lastw = (uint32_t)r + 1u;
                     }
                 }
                 const uint32_t fmin = wave_max_u32(first ? 0xFFFFFFFFu - first : 0u);
                 const uint32_t lmax = wave_max_u32(lastw);
+                // no crossing row (rounding): the last row with positive mass
+                const int row = fmin ? (int)(0xFFFFFFFFu - fmin) - 1 : (lmax ? (int)lmax - 1 : -1);
                 if (lane == 0) {
-                    s_redi[wave] = (int)fmin;
-                    s_redj[wave] = (int)lmax;
-                }
-                __syncthreads();
-                uint32_t fm = 0u, lm = 0u;
-                for (int w = 0; w < 4; ++w) {
-                    fm = max(fm, (uint32_t)s_redi[w]);
-                    lm = max(lm, (uint32_t)s_redj[w]);
-                }
-                const int row = fm ? (int)(0xFFFFFFFFu - fm) - 1 : (lm ? (int)lm - 1 : -1);
-                const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
-                if (t == 0) {
+                    const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
                     s_next[b] = tok;
                     st_agent64(&btok[b], ((unsigned long long)(unsigned)tok << 28) | epoch);
                 }
-                __syncthreads();
             }
+            __syncthreads();
+            if (s_abort) break;
             // tokens found by other shards
             if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] >> 21) != c) {
                 unsigned it = 0;

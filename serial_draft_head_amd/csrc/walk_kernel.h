@@ -169,6 +169,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     const int gamma = p.gamma;
     const int v0 = c * p.rows_per_wg;
     const int nrows = max(0, min(V, v0 + p.rows_per_wg) - v0);
+    // register slots beyond the shard load its last row (a cache hit), never
+    // another shard's rows (extra HBM reads); an empty shard loads row V - 1
+    const int last_row = nrows > 0 ? v0 + nrows - 1 : V - 1;
     const WT* __restrict__ W2 = reinterpret_cast<const WT*>(p.W2);
     WT* s_wt = reinterpret_cast<WT*>(s_w);
     const uint4* __restrict__ W1 = reinterpret_cast<const uint4*>(p.W1);
@@ -220,9 +223,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     if constexpr (kMfma) {
 #pragma unroll
         for (int j = 0; j < A; ++j) {
-            // rows outside the shard load some valid row instead (no second,
-            // zeroed copy of the registers); their results are never used
-            const int row = min(v0 + wrow0 + j * kTileRows + n, V - 1);
+            // rows outside the shard load the shard's last row instead (no
+            // second, zeroed copy of the registers); their results are never used
+            const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
             const WT* src = W2 + (size_t)row * kRowChunks;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[DSW_KC(kb, g)];
@@ -286,7 +289,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         // slot's codes at once would not fit beside the widened rows)
 #pragma unroll
         for (int s = 0; s < A; ++s) {
-            const int row = min(v0 + s * kBlock + t, V - 1);  // rows past the shard: any valid row
+            const int row = min(v0 + s * kBlock + t, last_row);  // rows past the shard: its last row
             uint4 qv[kRowChunks / 2];
 #pragma unroll
             for (int c2 = 0; c2 < kRowChunks / 2; ++c2) qv[c2] = Wq[(size_t)row * (kRowChunks / 2) + c2];

@@ -26,6 +26,7 @@ constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 
 constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
+constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests
 constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // epochs live in the low 28 bits, never 0
 struct Workspace {
     unsigned long long* mail;      // [2][kMaxGrid][kMailWords]
@@ -41,6 +42,10 @@ struct Workspace {
     unsigned long long* btok;      // [2][kMaxBatch]  sampled token << 28 | epoch
     unsigned long long* bext;      // [2][kMaxBatch][2]  owner's prefix before the token
                                    // shard and u*Z, fp32 bits << 32 | epoch
+    uint16_t* blog;                // [B_max][V] batched kernel: this step's logits of the
+                                   // sampled requests (when the caller wants none written),
+                                   // read back by the token shards; NULL if the handle
+                                   // never runs the batched kernel
 };
 
 // Status bits latched by the device (translated to DSW_ERR_DEV_* on the host).
