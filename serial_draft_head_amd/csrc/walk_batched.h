@@ -138,6 +138,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const int NG = (B + kGroup - 1) / kGroup;
     const int D = p.ring;
     const bool aligned = p.aligned != 0;
+    const bool al4 = (V & 3) == 0;  // 8-byte stores of 4 logits (rows 4g .. 4g+3)
     const int P = 2 + (aligned ? CPR / 16 : 0);  // DMA instructions per wave and group
     // x / CPR as (x * cpr_mul) >> 20, exact for x < 16 * CPR (CPR <= 128: rows_pad <= 1024)
     const unsigned cpr_mul = ((1u << 20) + (unsigned)CPR - 1u) / (unsigned)CPR;
@@ -361,37 +362,29 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + bf16_lo(p23_), bf16_hi(bw_.y) + bf16_hi(p23_)); \
         *e_ = make_uint2(q01_, q23_);                                                            \
         const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
+        if (lout != nullptr && lim_ > 0) {                                                       \
+            if (al4 && lim_ >= 4) {                                                              \
+                *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);                  \
+            } else {                                                                             \
+                const uint32_t l4_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16}; \
+                _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                  \
+                    if (i_ < lim_) lout[rb_ + i_] = (uint16_t)l4_[i_];                            \
+            }                                                                                    \
+        }                                                                                        \
         DSW_BEST(bf16_lo(q01_), rb_, 0 < lim_);                                                  \
         DSW_BEST(bf16_hi(q01_), rb_ + 1, 1 < lim_);                                              \
         DSW_BEST(bf16_lo(q23_), rb_ + 2, 2 < lim_);                                              \
         DSW_BEST(bf16_hi(q23_), rb_ + 3, 3 < lim_);                                              \
     } while (0)
+            // this lane's logits go out straight from the epilogue: to `logits`
+            // when asked for, and for sampled requests in any case (to the
+            // workspace otherwise), where the token shard reads them back
+            uint16_t* lout = nullptr;
+            if (bval && (p.logits != nullptr || s_T[b] > 0.0f))
+                lout = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V : p.ws.blog + (size_t)b * V) + v0;
             DSW_TILES(DSW_EPI_G);
 #undef DSW_EPI_G
             uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
-            if (p.logits != nullptr || any_samp) {
-                // the group's logits, out of the slot with whole-row stores: to
-                // `logits` when asked for, and for sampled requests in any case
-                // (to the workspace otherwise), where the token shard reads them
-                barrier_keep_vm();
-                for (int e = t; e < kGroup * CPR; e += kBlock) {
-                    const int nn = (int)(((unsigned)e * cpr_mul) >> 20), cr = e - nn * CPR;
-                    const int bq = grp * kGroup + nn, r0 = cr * 8;
-                    if (bq < B && r0 < nrows && (p.logits != nullptr || s_T[bq] > 0.0f)) {
-                        const uint4 w = *reinterpret_cast<const uint4*>(sb + (nn * CPR + (cr ^ nn)) * 8);
-                        uint16_t* o = (p.logits != nullptr ? p.logits + ((size_t)bq * gamma + k) * V
-                                                           : p.ws.blog + (size_t)bq * V) +
-                                      v0 + r0;
-                        if (aligned && r0 + 8 <= nrows) {
-                            *reinterpret_cast<uint4*>(o) = w;
-                        } else {
-                            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-                            for (int i = 0; i < 8 && r0 + i < nrows; ++i)
-                                o[i] = (uint16_t)(ww[i >> 1] >> (16 * (i & 1)));
-                        }
-                    }
-                }
-            }
             // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
             best = max(best, (uint32_t)__shfl_xor((int)best, 16));
             best = max(best, (uint32_t)__shfl_xor((int)best, 32));
@@ -583,6 +576,16 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             for (int i = wave; i < ntask; i += 4) {
                 const int b = s_tasks[i];
                 const float sc2 = kLog2e / s_T[b];
+                // this shard's logits of request b, requested before the owner's
+                // words are polled (both round trips overlap)
+                const uint16_t* lrow = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V
+                                                            : p.ws.blog + (size_t)b * V) + v0;
+                uint32_t lb[RLMAX];
+#pragma unroll
+                for (int rr = 0; rr < RLMAX; ++rr) {
+                    const int r = lane * RL + rr;
+                    lb[rr] = (rr < RL && r < nrows) ? (uint32_t)lrow[r] : 0u;
+                }
                 // the owner's prefix before this shard (lane 0) and u*Z (lane 1)
                 float ev = 0.0f;
                 bool ok = true;
@@ -603,14 +606,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const uint32_t lk = max(max(s_rkey[0][b], s_rkey[1][b]), max(s_rkey[2][b], s_rkey[3][b]));
                 const float ml = local_key_logit(lk);
                 const float scale = __builtin_amdgcn_exp2f((ml - Mg) * sc2);
-                const uint16_t* lrow = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V
-                                                            : p.ws.blog + (size_t)b * V) + v0;
                 float wv[RLMAX];
                 float part = 0.0f;
 #pragma unroll
                 for (int rr = 0; rr < RLMAX; ++rr) {
                     const int r = lane * RL + rr;
-                    wv[rr] = (rr < RL && r < nrows) ? __builtin_amdgcn_exp2f((bf16_to_f32(lrow[r]) - ml) * sc2) : 0.0f;
+                    wv[rr] = (rr < RL && r < nrows) ? __builtin_amdgcn_exp2f((bf16_to_f32(lb[rr]) - ml) * sc2) : 0.0f;
                     part += wv[rr];
                 }
                 const float incl = wave_incl_scan_dpp(part);
