@@ -362,6 +362,32 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + bf16_lo(p23_), bf16_hi(bw_.y) + bf16_hi(p23_)); \
         *e_ = make_uint2(q01_, q23_);                                                            \
         const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
+        DSW_BEST(bf16_lo(q01_), rb_, 0 < lim_);                                                  \
+        DSW_BEST(bf16_hi(q01_), rb_ + 1, 1 < lim_);                                              \
+        DSW_BEST(bf16_lo(q23_), rb_ + 2, 2 < lim_);                                              \
+        DSW_BEST(bf16_hi(q23_), rb_ + 3, 3 < lim_);                                              \
+    } while (0)
+// As DSW_EPI_G, and this lane's four logits go out with one 8-byte store.
+#define DSW_EPI_GS(dv, j)                                                                         \
+    do {                                                                                         \
+        const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
+        const bool live_ = (j) < nt_w;                                                           \
+        uint2* e_ = live_ ? reinterpret_cast<uint2*>(sb + (n * CPR + ((rb_ >> 3) ^ n)) * 8 + (rb_ & 7)) \
+                          : &s_junk[lane];                                                       \
+        const uint2 bw_ = *e_;                                                                   \
+        float x0_ = (dv)[0], x1_ = (dv)[1], x2_ = (dv)[2], x3_ = (dv)[3];                        \
+        if constexpr (kI8) {                                                                     \
+            const int rs_ = live_ ? rb_ : 0;                                                     \
+            x0_ *= s_scale[rs_];                                                                 \
+            x1_ *= s_scale[rs_ + 1];                                                             \
+            x2_ *= s_scale[rs_ + 2];                                                             \
+            x3_ *= s_scale[rs_ + 3];                                                             \
+        }                                                                                        \
+        const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);           \
+        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + bf16_lo(p01_), bf16_hi(bw_.x) + bf16_hi(p01_)); \
+        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + bf16_lo(p23_), bf16_hi(bw_.y) + bf16_hi(p23_)); \
+        *e_ = make_uint2(q01_, q23_);                                                            \
+        const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
         if (lout != nullptr && lim_ > 0) {                                                       \
             if (al4 && lim_ >= 4) {                                                              \
                 *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);                  \
@@ -376,14 +402,21 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         DSW_BEST(bf16_lo(q23_), rb_ + 2, 2 < lim_);                                              \
         DSW_BEST(bf16_hi(q23_), rb_ + 3, 3 < lim_);                                              \
     } while (0)
-            // this lane's logits go out straight from the epilogue: to `logits`
-            // when asked for, and for sampled requests in any case (to the
-            // workspace otherwise), where the token shard reads them back
+            // Logits go out straight from the epilogue: to `logits` when asked
+            // for, and for sampled requests in any case (to the workspace
+            // otherwise), where the token shard reads them back.  A group with
+            // nothing to store runs the epilogue without the stores (their
+            // branches cost a greedy batch ~12% even when no lane stores).
             uint16_t* lout = nullptr;
             if (bval && (p.logits != nullptr || s_T[b] > 0.0f))
                 lout = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V : p.ws.blog + (size_t)b * V) + v0;
-            DSW_TILES(DSW_EPI_G);
+            if (__builtin_amdgcn_ballot_w64(lout != nullptr) != 0ull) {
+                DSW_TILES(DSW_EPI_GS);
+            } else {
+                DSW_TILES(DSW_EPI_G);
+            }
 #undef DSW_EPI_G
+#undef DSW_EPI_GS
             uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
             // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
             best = max(best, (uint32_t)__shfl_xor((int)best, 16));
