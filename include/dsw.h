@@ -96,6 +96,13 @@ extern "C" {
                                     serves B > 16 always: requests in groups of 16
                                     on the MFMA engine, one owner workgroup per
                                     request for the exchange                   */
+#define DSW_FLAG_SINGLE_ROUND 32u /* round once: logit = bf16(base + fp32 dot)
+                                    instead of the default walk's
+                                    bf16(base + bf16(dot)) -- the rounding of the
+                                    pages' H100 int8 kernel ("Keeping the Draft
+                                    Walk on Chip", section "Correctness", Fig. 7)
+                                    and of vLLM PR #64442 ("Details").  Applies
+                                    to every walk of the handle.              */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -197,7 +204,9 @@ int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sca
  * workspace is re-zeroed so that the next call starts clean. */
 int dsw_status(dsw_handle_t h);
 
-/* The plan dsw_walk uses for batch size B on this handle. */
+/* The plan dsw_walk uses for batch size B on this handle, for a walk of
+ * gamma_max steps (one bf16 request walking up to 3 steps takes the VALU
+ * engine instead: see dsw_plan_compute with the walk's own gamma). */
 int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out);
 
 /* Diagnostics: record per-workgroup, per-step phase timestamps of later

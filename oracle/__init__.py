@@ -55,11 +55,11 @@ def _load():
     lib.oracle_rne_bf16_array.restype = None
     lib.oracle_rne_bf16_array.argtypes = [P, P, P, ctypes.c_long]
     lib.oracle_step.restype = i
-    lib.oracle_step.argtypes = [i, i, P, P, P, P, P, f, f, P]
+    lib.oracle_step.argtypes = [i, i, P, P, P, P, P, f, f, P, i]
     lib.oracle_sample.restype = i
     lib.oracle_sample.argtypes = [i, P, f, f]
     lib.oracle_walk.restype = i
-    lib.oracle_walk.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_walk.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, P, P, P, i]
     lib.oracle_threads.restype = i
     lib.oracle_threads.argtypes = []
     lib.oracle_set_threads.restype = None
@@ -99,8 +99,12 @@ def bf16_bits_to_f64(bits):
     return b.view(np.float32).astype(np.float64)
 
 
-def step(u_bits, base_bits, T, uniform, W2_bits=None, Q=None, scale=None):
-    """One step for one request.  Returns (token, logits_bits[V])."""
+SINGLE_ROUND = 1  # mode bit: logit = bf16(base + dot), rounded once
+
+
+def step(u_bits, base_bits, T, uniform, W2_bits=None, Q=None, scale=None, single_round=False):
+    """One step for one request.  Returns (token, logits_bits[V]).  single_round:
+    the sum base + dot is rounded to bf16 once (default: the dot first, then the sum)."""
     u_bits = _c(u_bits, np.uint16)
     base_bits = _c(base_bits, np.uint16)
     W2_bits, Q, scale = _c(W2_bits, np.uint16), _c(Q, np.int8), _c(scale, np.float32)
@@ -108,7 +112,8 @@ def step(u_bits, base_bits, T, uniform, W2_bits=None, Q=None, scale=None):
     r = u_bits.shape[0]
     out = np.empty(V, dtype=np.uint16)
     tok = _load().oracle_step(V, r, _ptr(u_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
-                              _ptr(base_bits), float(T), float(uniform), _ptr(out))
+                              _ptr(base_bits), float(T), float(uniform), _ptr(out),
+                              SINGLE_ROUND if single_round else 0)
     if tok < 0:
         raise RuntimeError(f"oracle_step failed with {tok}")
     return tok, out
@@ -124,7 +129,7 @@ def sample(logits_bits, T, uniform) -> int:
 
 
 def walk(W1_bits, base_bits, anchor, T, uniforms=None, W2_bits=None, Q=None, scale=None,
-         forced=None, want_logits=True):
+         forced=None, want_logits=True, single_round=False):
     """The whole walk.  Shapes: W1 [V,r] u16, W2 [V,r] u16 (or Q [V,r] i8 + scale [V] f32),
     base [B,gamma,V] u16, anchor [B] i32, T [B] f32, uniforms [B,gamma] f32 or None,
     forced [B,gamma] i32 or None (teacher forcing: step k>0 uses forced[:,k-1] as prev).
@@ -144,7 +149,8 @@ def walk(W1_bits, base_bits, anchor, T, uniforms=None, W2_bits=None, Q=None, sca
     logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
     rc = _load().oracle_walk(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
                              _ptr(base_bits), _ptr(anchor), _ptr(T), _ptr(uniforms),
-                             _ptr(forced), _ptr(tokens), _ptr(logits))
+                             _ptr(forced), _ptr(tokens), _ptr(logits),
+                             SINGLE_ROUND if single_round else 0)
     if rc != 0:
         raise RuntimeError(f"oracle_walk failed with {rc}")
     return tokens, logits

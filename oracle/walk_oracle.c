@@ -23,6 +23,11 @@
  *   int8:      acc_v = scale_v * sum_j q[v, j] * u_j
  *   bias_v   = RNE_bf16(acc_v)        rounded straight from f64
  *   logit_v  = RNE_bf16(base_v + bias_v)  (the f64 sum of two bf16 is exact)
+ *   single-rounding mode (ORACLE_SINGLE_ROUND): logit_v = RNE_bf16(base_v + acc_v),
+ *            the sum rounded once, as the pages' H100 int8 kernel does ("Keeping
+ *            the Draft Walk on Chip", section "Correctness", and the caption of
+ *            Fig. 7) and as vLLM PR #64442 ("Details") writes its fp32 sum to
+ *            the cache
  *   T == 0 : tok = smallest v with logit_v == max_w logit_w
  *   T  > 0 : M = max logit, w_v = exp((logit_v - M) / T), C_v = sum_{j<=v} w_j,
  *            Z = C_{V-1}, t = uniform * Z, tok = smallest v with C_v > t
@@ -49,6 +54,9 @@ static double bf16_value(uint16_t h) {
     memcpy(&f, &bits, sizeof f);
     return (double)f;
 }
+
+/* Mode bits of oracle_step / oracle_walk. */
+#define ORACLE_SINGLE_ROUND 1
 
 /* Round x to the nearest bf16 value (8 significant bits, exponent range of
  * binary32), ties to even, directly from binary64.  The result is returned as
@@ -138,7 +146,8 @@ static int sample_inverse_cdf(const double* logit, int V, double T, double unifo
 static int oracle_step_impl(int V, int r, const uint16_t* u_bits,
                             const uint16_t* W2, const int8_t* Q, const float* scale,
                             const uint16_t* base, float T, float uniform,
-                            uint16_t* logits, double* lg) {
+                            uint16_t* logits, double* lg, int mode) {
+    const int single = (mode & ORACLE_SINGLE_ROUND) != 0;
     double* u = (double*)malloc(sizeof(double) * (size_t)r);
     if (!u) return -3;
     for (int j = 0; j < r; ++j) u[j] = bf16_value(u_bits[j]);
@@ -156,8 +165,9 @@ static int oracle_step_impl(int V, int r, const uint16_t* u_bits,
             for (int j = 0; j < r; ++j) dot += (double)row[j] * u[j];
             acc = (double)scale[v] * dot;
         }
-        double bias = oracle_rne_bf16(acc);
-        double logit = oracle_rne_bf16(bf16_value(base[v]) + bias);
+        /* double rounding: the bias is rounded to bf16 first; single: the sum once */
+        double logit = single ? oracle_rne_bf16(bf16_value(base[v]) + acc)
+                              : oracle_rne_bf16(bf16_value(base[v]) + oracle_rne_bf16(acc));
         if (!isfinite(logit)) bad = 1;
         lg[v] = logit;
         if (logits) logits[v] = oracle_bf16_bits(logit);
@@ -177,11 +187,11 @@ static int oracle_step_impl(int V, int r, const uint16_t* u_bits,
 /* Public single step (see oracle_step_impl). */
 int oracle_step(int V, int r, const uint16_t* u_bits, const uint16_t* W2,
                 const int8_t* Q, const float* scale, const uint16_t* base,
-                float T, float uniform, uint16_t* logits) {
+                float T, float uniform, uint16_t* logits, int mode) {
     if (V <= 0 || r <= 0 || !u_bits || !base || (!W2 && (!Q || !scale))) return -1;
     double* lg = (double*)malloc(sizeof(double) * (size_t)V);
     if (!lg) return -3;
-    int tok = oracle_step_impl(V, r, u_bits, W2, Q, scale, base, T, uniform, logits, lg);
+    int tok = oracle_step_impl(V, r, u_bits, W2, Q, scale, base, T, uniform, logits, lg, mode);
     free(lg);
     return tok;
 }
@@ -211,6 +221,7 @@ int oracle_sample(int V, const uint16_t* logits, float T, float uniform) {
  *              (teacher forcing, so each step can be judged on its own).
  *   tokens   : [B][gamma] out
  *   logits   : [B][gamma][V] bf16 bits out, or NULL
+ *   mode     : 0, or ORACLE_SINGLE_ROUND
  * Returns 0, or a negative error (-1 bad argument, -2 non-finite logit,
  * -3 out of memory).
  */
@@ -218,7 +229,7 @@ int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
                 const uint16_t* W2, const int8_t* Q, const float* scale,
                 const uint16_t* base, const int32_t* anchor, const float* T,
                 const float* uniforms, const int32_t* forced, int32_t* tokens,
-                uint16_t* logits) {
+                uint16_t* logits, int mode) {
     if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !base || !anchor || !T ||
         !tokens || (!W2 && (!Q || !scale)))
         return -1;
@@ -237,7 +248,7 @@ int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
             uint16_t* out = logits ? logits + ((size_t)b * gamma + k) * (size_t)V : NULL;
             float uni = uniforms ? uniforms[(size_t)b * gamma + k] : 0.0f;
             int tok = oracle_step_impl(V, r, W1 + (size_t)prev * (size_t)r, W2, Q, scale,
-                                       base_k, T[b], uni, out, lg);
+                                       base_k, T[b], uni, out, lg, mode);
             if (tok < 0) { free(lg); return tok; }
             tokens[(size_t)b * gamma + k] = tok;
             prev = tok;

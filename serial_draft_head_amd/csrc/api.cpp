@@ -163,10 +163,14 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         return DSW_ERR_HIP;
     }
     // Residency: every batch size this handle serves must fit one workgroup
-    // on each CU within the LDS limit, and the grid must not exceed the CUs.
-    for (int B = 1; B <= B_max; ++B) {
+    // on each CU within the LDS limit, and the grid must not exceed the CUs;
+    // short walks (up to 3 steps) may plan another kernel, so they are checked too.
+    const int n_g = gamma_max > 3 ? 2 : 1;
+    for (int i = 0; i < B_max * n_g; ++i) {
+        const int B = 1 + i / n_g;
+        const int gm = (i % n_g) == 0 ? gamma_max : 3;
         dsw_plan_info pl;
-        int prc = dsw_plan_compute(&dev, V, r, gamma_max, B, w2_dtype, flags, &pl);
+        int prc = dsw_plan_compute(&dev, V, r, gm, B, w2_dtype, flags, &pl);
         const void* fn = prc == DSW_OK ? kernel_for(pl) : nullptr;
         hipFuncAttributes attr;
         int per_cu = 0;
@@ -258,6 +262,7 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     p.ring = plan.ring_slots;
     p.aligned = (h->V % 8) == 0;
     p.spin_limit = kSpinLimit;
+    p.single_round = (h->flags & DSW_FLAG_SINGLE_ROUND) ? 1 : 0;
     p.trace = nullptr;
     if (h->trace != nullptr &&
         (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)

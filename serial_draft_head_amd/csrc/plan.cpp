@@ -320,7 +320,10 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
-    if (!forced) valu = B <= 1 && i8;
+    // one bf16 request: the MFMA engine's step is ~1 us shorter, but its shard
+    // load ~3 us longer (measured at V = 151,936), so walks of up to 3 steps
+    // take the VALU engine
+    if (!forced) valu = B <= 1 && (i8 || gamma <= 3);
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);

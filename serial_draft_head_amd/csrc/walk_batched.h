@@ -357,9 +357,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             x2_ *= s_scale[rs_ + 2];                                                             \
             x3_ *= s_scale[rs_ + 3];                                                             \
         }                                                                                        \
-        const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);           \
-        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + bf16_lo(p01_), bf16_hi(bw_.x) + bf16_hi(p01_)); \
-        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + bf16_lo(p23_), bf16_hi(bw_.y) + bf16_hi(p23_)); \
+        if (!p.single_round) {  /* double rounding: the bias to bf16 first */                 \
+            const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);       \
+            x0_ = bf16_lo(p01_);                                                                 \
+            x1_ = bf16_hi(p01_);                                                                 \
+            x2_ = bf16_lo(p23_);                                                                 \
+            x3_ = bf16_hi(p23_);                                                                 \
+        }                                                                                        \
+        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + x0_, bf16_hi(bw_.x) + x1_);         \
+        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
         *e_ = make_uint2(q01_, q23_);                                                            \
         const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
         DSW_BEST(bf16_lo(q01_), rb_, 0 < lim_);                                                  \
@@ -383,9 +389,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             x2_ *= s_scale[rs_ + 2];                                                             \
             x3_ *= s_scale[rs_ + 3];                                                             \
         }                                                                                        \
-        const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);           \
-        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + bf16_lo(p01_), bf16_hi(bw_.x) + bf16_hi(p01_)); \
-        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + bf16_lo(p23_), bf16_hi(bw_.y) + bf16_hi(p23_)); \
+        if (!p.single_round) {  /* double rounding: the bias to bf16 first */                 \
+            const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);       \
+            x0_ = bf16_lo(p01_);                                                                 \
+            x1_ = bf16_hi(p01_);                                                                 \
+            x2_ = bf16_lo(p23_);                                                                 \
+            x3_ = bf16_hi(p23_);                                                                 \
+        }                                                                                        \
+        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + x0_, bf16_hi(bw_.x) + x1_);         \
+        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
         *e_ = make_uint2(q01_, q23_);                                                            \
         const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
         if (lout != nullptr && lim_ > 0) {                                                       \

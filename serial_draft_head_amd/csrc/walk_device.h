@@ -19,6 +19,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return u >> 16;
 }
 
+// The bias as the epilogue adds it: rounded to bf16 (dbl = ~0u, the default
+// walk's double rounding) or kept in fp32 (dbl = 0, single rounding of the
+// sum).  Branch-free with a uniform mask, so it costs no extra registers.
+__device__ __forceinline__ float bias_round(float a, uint32_t dbl) {
+    uint32_t u = __float_as_uint(a);
+    u += (0x7FFFu + ((u >> 16) & 1u)) & dbl;
+    return __uint_as_float(u & (0xFFFF0000u | ~dbl));
+}
+
 // Two fp32 values -> a bf16 pair (lo in the low half), round to nearest even:
 // one v_cvt_pk_bf16_f32.  It agrees bit for bit with f32_to_bf16 on finite
 // inputs, ties and denormals included (checked on the device).

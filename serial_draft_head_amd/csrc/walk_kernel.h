@@ -168,6 +168,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     const int B = p.B;
     const int gamma = p.gamma;
     const int v0 = c * p.rows_per_wg;
+    const uint32_t dbl_round = p.single_round ? 0u : 0xFFFFFFFFu;  // see bias_round
     const int nrows = max(0, min(V, v0 + p.rows_per_wg) - v0);
     // register slots beyond the shard load its last row (a cache hit), never
     // another shard's rows (extra HBM reads); an empty shard loads row V - 1
@@ -436,8 +437,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     const float acc1 = combine4(d[0][0], d[1][0], d[2][0], d[3][0]);
                     if (DSW_ONE_ROW_OK(gq)) {
                         const int r = wrow0 + 64 * gq + lane;
-                        const uint32_t bias = f32_to_bf16(acc1);
-                        const uint32_t lbits = f32_to_bf16(bf16_to_f32(bq[gq]) + bf16_to_f32(bias));
+                        const float bias = bias_round(acc1, dbl_round);
+                        const uint32_t lbits = f32_to_bf16(bf16_to_f32(bq[gq]) + bias);
                         best[0] = max(best[0], local_key(lbits, r));
                         s_logit[r] = (uint16_t)lbits;
                     }
@@ -459,8 +460,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
             if (4 * g + i < B && r_ < nrows) {                                                   \
                 const int e_ = lofs + i * RPAD + (j) * kTileRows;                                \
-                const uint32_t bias_ = f32_to_bf16(kI8 ? s_scale[r_] * (dv)[i] : (dv)[i]);      \
-                const uint32_t lb_ = f32_to_bf16(bf16_to_f32(s_base[e_]) + bf16_to_f32(bias_));  \
+                const float a_ = kI8 ? s_scale[r_] * (dv)[i] : (dv)[i];                          \
+                const float bias_ = bias_round(a_, dbl_round);                                   \
+                const uint32_t lb_ = f32_to_bf16(bf16_to_f32(s_base[e_]) + bias_);               \
                 best[i] = max(best[i], local_key(lb_, r_));                                      \
                 s_logit[e_] = (uint16_t)lb_;                                                     \
             }                                                                                    \
@@ -601,8 +603,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     if ((NB == 1 || b < B) && i < nrows) {
                         float a = acc[b][s];
                         if constexpr (kI8) a *= s_scale[i];
-                        const uint32_t bias = f32_to_bf16(a);
-                        const uint32_t lbits = f32_to_bf16(bf16_to_f32(bs[b][s]) + bf16_to_f32(bias));
+                        // double rounding (the default walk's), or one rounding of the sum
+                        const float bias = bias_round(a, dbl_round);
+                        const uint32_t lbits = f32_to_bf16(bf16_to_f32(bs[b][s]) + bias);
                         best[b] = max(best[b], local_key(lbits, i));
                         s_logit[b * RPAD + i] = (uint16_t)lbits;
                     }

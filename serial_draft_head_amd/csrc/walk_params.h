@@ -98,6 +98,7 @@ struct WalkParams {
     int ring;                // batched kernel: LDS slots for u rows and base logits of groups
     int aligned;             // batched kernel: V % 8 == 0 (16-byte aligned base rows)
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
+    int single_round;        // 1: logit = bf16(base + fp32 dot), rounded once
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };
 

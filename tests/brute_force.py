@@ -20,12 +20,17 @@ def bias_exact(W2, u, v, Q=None, scale=None):
     return Fraction(float(scale[v])) * dot
 
 
-def step_logits(W2, u, base_row, Q=None, scale=None):
+def step_logits(W2, u, base_row, Q=None, scale=None, single=False):
+    """bf16 logit bits of one step: bf16(base + bf16(dot)), or bf16(base + dot)
+    rounded once when `single`."""
     V = len(base_row)
     out = []
     for v in range(V):
-        b = rne_bits(bias_exact(W2, u, v, Q, scale))
-        out.append(rne_bits(value(base_row[v]) + value(b)))
+        dot = bias_exact(W2, u, v, Q, scale)
+        if single:
+            out.append(rne_bits(value(base_row[v]) + dot))
+        else:
+            out.append(rne_bits(value(base_row[v]) + value(rne_bits(dot))))
     return out
 
 
@@ -55,14 +60,14 @@ def sample_exact(logit_bits, T, uniform):
     return tok, float(margin)
 
 
-def walk(W1, W2, base, anchor, T=0.0, uniforms=None, Q=None, scale=None):
+def walk(W1, W2, base, anchor, T=0.0, uniforms=None, Q=None, scale=None, single=False):
     """Greedy or sampled walk of one request.  Returns (tokens, logits bits, min sampling margin)."""
     gamma = base.shape[0]
     prev = int(anchor)
     toks, logits, margin = [], [], 1.0
     for k in range(gamma):
         u = [value(W1[prev, j]) for j in range(W1.shape[1])]
-        lb = step_logits(W2, u, base[k], Q, scale)
+        lb = step_logits(W2, u, base[k], Q, scale, single)
         if T == 0.0:
             tok = argmax_lowest(lb)
         else:

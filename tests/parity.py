@@ -21,6 +21,10 @@ order):
     wherever u Z is farther than d from every boundary.
 Step k uses prev = the GPU's token k-1 (teacher forcing), so every step is
 judged on its own.
+
+Single-rounding mode (logit = bf16(base + fp32 dot)): the interval becomes
+[bf16(base + acc - E'), bf16(base + acc + E')] with E' = E + 2^-24 (|base + acc| + E),
+the fp32 addition rounding once more before the one rounding to bf16.
 """
 from __future__ import annotations
 
@@ -51,11 +55,12 @@ class Weights:
         self.W2abs = np.abs(self.W2)
 
 
-def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, steps=None):
+def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, steps=None,
+                single_round=False):
     """Assert the parity rules for one round; return a small report dict."""
     B, gamma, V = base.shape
     or_tok, or_lg = oracle.walk(w.W1_bits, base, anchor, T, uniforms, W2_bits=w.W2_bits, Q=w.Q,
-                                scale=w.scale, forced=gpu_tokens)
+                                scale=w.scale, forced=gpu_tokens, single_round=single_round)
     rep = {"steps": 0, "exact_logits": 0, "logits": 0, "near_ties": 0, "token_match": 0,
            "sampled": 0, "sampled_exact_checked": 0}
     for b in range(B):
@@ -67,11 +72,16 @@ def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, s
             if w.Q is not None:  # the fp32 product scale * sum rounds once more
                 E = E + 2.0 ** -24 * (np.abs(acc) + E)
             bias = oracle.rne_bf16(acc)[0]
-            lo = oracle.rne_bf16(acc - E)[0]
-            hi = oracle.rne_bf16(acc + E)[0]
             bse = oracle.bf16_bits_to_f64(base[b, k])
-            Llo = oracle.rne_bf16(bse + lo)[0]
-            Lhi = oracle.rne_bf16(bse + hi)[0]
+            if single_round:
+                E1 = E + 2.0 ** -24 * (np.abs(bse + acc) + E)
+                Llo = oracle.rne_bf16(bse + acc - E1)[0]
+                Lhi = oracle.rne_bf16(bse + acc + E1)[0]
+            else:
+                lo = oracle.rne_bf16(acc - E)[0]
+                hi = oracle.rne_bf16(acc + E)[0]
+                Llo = oracle.rne_bf16(bse + lo)[0]
+                Lhi = oracle.rne_bf16(bse + hi)[0]
             g = oracle.bf16_bits_to_f64(gpu_logits[b, k])
             o = oracle.bf16_bits_to_f64(or_lg[b, k])
             bad = np.nonzero((g < Llo) | (g > Lhi))[0]

@@ -133,6 +133,8 @@ def test_planner_choices_on_mi355x_shapes(dsw):
     assert dsw.plan(d, 151_936, 7, 1).engine == 1 and dsw.plan(d, 151_936, 7, 1).batch_tile == 1
     assert dsw.plan(d, 151_936, 7, 2).engine == 1
     assert dsw.plan(d, 151_936, 7, 1, w2_dtype=dsw.INT8).engine == 0
+    # short walks of one bf16 request take the VALU engine (its shard load is shorter)
+    assert dsw.plan(d, 151_936, 3, 1).engine == 0 and dsw.plan(d, 151_936, 4, 1).engine == 1
     assert pick(dsw.plan(d, 32_000, 7, 1, flags=8)) == (125, 2, 2, 0, 0)
     # one request on the MFMA engine: 10 tiles per wave all in registers (8 AGPR + 2 VGPR)
     c1 = dsw.plan(d, 151_936, 7, 1, flags=8)

@@ -257,6 +257,41 @@ def test_every_mfma_shape(dsw, V, shape, B):
         say(temps, rep)
 
 
+# single rounding (logit = bf16(base + fp32 dot)) on every kernel and engine
+SINGLE_CASES = [  # (V, B, gamma, temps, flags, w2 dtype)
+    (32_000, 1, 5, "greedy", 0, "bf16"),         # MFMA, one request
+    (100_003, 1, 4, "cycle", 4, "bf16"),         # VALU
+    (60_000, 3, 4, "mixed", 8, "bf16"),          # MFMA, 4-request tile
+    (129_280, 20, 3, "mixed", 0, "bf16"),        # batched
+    (60_000, 1, 4, "cycle", 0, "int8"),          # VALU int8
+    (60_000, 3, 3, "mixed", 8, "int8"),          # MFMA int8
+]
+
+
+@pytest.mark.parametrize("V,B,gamma,temps,flags,dt", SINGLE_CASES)
+def test_single_rounding(dsw, V, B, gamma, temps, flags, dt):
+    say(f"single rounding V={V} B={B} gamma={gamma} temps={temps} flags={flags} {dt}")
+    W1, W2 = workloads.weights(4, V=V)
+    W1d = bf16_dev(W1)
+    if dt == "int8":
+        Q, sc = workloads.quantize_int8(W2)
+        w = parity.Weights(W1, Q=Q, scale=sc)
+        W2d, sd = int8_dev(Q, sc)
+    else:
+        w = parity.Weights(W1, W2)
+        W2d, sd = bf16_dev(W2), None
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, flags=flags | dsw.FLAG_SINGLE_ROUND,
+                        w2_dtype=dsw.INT8 if dt == "int8" else dsw.BF16)
+    say("plan", walker.query_plan(B).as_dict())
+    for rnd in range(3):
+        inp = workloads.round_inputs(4, 70 + rnd, B=B, gamma=gamma, V=V, temps=temps)
+        toks, lg = run(walker, W1d, W2d, inp, scale=sd)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 single_round=True)
+        say(rnd, rep)
+    walker.close()
+
+
 # int8 rows + fp32 row scales: one vocabulary per compiled int8 shape, plus
 # ragged sizes; the harness quantizes once and both sides consume (q, scale).
 I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),

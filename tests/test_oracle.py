@@ -99,6 +99,18 @@ def test_hand_worked_walk(oracle_mod):
     assert logits[0].tolist() == want
 
 
+def test_hand_worked_walk_single_rounding(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_walk_v4_r2_single.json")) as f:
+        g = json.load(f)
+    W1 = bits_of(np.ravel(g["W1"])).reshape(g["V"], g["r"])
+    W2 = bits_of(np.ravel(g["W2"])).reshape(g["V"], g["r"])
+    base = bits_of(np.ravel(g["base"])).reshape(1, g["gamma"], g["V"])
+    toks, logits = oracle_mod.walk(W1, base, [g["anchor"]], [g["T"]], W2_bits=W2, single_round=True)
+    assert toks[0].tolist() == g["expected_tokens"]
+    want = [[int(x, 16) for x in row] for row in g["expected_logits_bits"]]
+    assert logits[0].tolist() == want
+
+
 def test_hand_worked_sampler(oracle_mod):
     with open(os.path.join(GOLDEN, "hand_sampler.json")) as f:
         g = json.load(f)
@@ -167,6 +179,61 @@ def test_brute_force_sampled(oracle_mod, seed):
         assert logits[0].tolist() == bl
         if margin > 1e-12:
             assert toks[0].tolist() == bt
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_brute_force_single_rounding(oracle_mod, seed):
+    d = workloads.toy(seed + 400, V=12, r=4, B=12, gamma=3, w2_std=0.5, base_std=1.0)
+    anchors = np.arange(12, dtype=np.int32)
+    T = np.zeros(12, dtype=np.float32)
+    toks, logits = oracle_mod.walk(d["W1"], d["base"], anchors, T, W2_bits=d["W2"], single_round=True)
+    for b in range(12):
+        bt, bl, _ = bf.walk(d["W1"], d["W2"], d["base"][b], anchors[b], single=True)
+        assert toks[b].tolist() == bt
+        assert logits[b].tolist() == bl
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_brute_force_single_rounding_int8_and_sampled(oracle_mod, seed):
+    d = workloads.toy(seed + 500, V=12, r=4, B=12, gamma=3, w2_std=0.5, base_std=0.2)
+    Q, scale = workloads.quantize_int8(d["W2"])
+    anchors = np.arange(12, dtype=np.int32)
+    toks, logits = oracle_mod.walk(d["W1"], d["base"], anchors, np.zeros(12, np.float32), Q=Q,
+                                   scale=scale, single_round=True)
+    for b in range(12):
+        bt, bl, _ = bf.walk(d["W1"], None, d["base"][b], anchors[b], Q=Q, scale=scale, single=True)
+        assert toks[b].tolist() == bt and logits[b].tolist() == bl
+    e = workloads.toy(seed + 600, V=12, r=4, B=1, gamma=3, base_std=1.5)
+    for T in (0.6, 1.0):
+        toks, logits = oracle_mod.walk(e["W1"], e["base"], e["anchor"], [T], uniforms=e["uniforms"],
+                                       W2_bits=e["W2"], single_round=True)
+        bt, bl, margin = bf.walk(e["W1"], e["W2"], e["base"][0], e["anchor"][0], T=T,
+                                 uniforms=e["uniforms"][0], single=True)
+        assert logits[0].tolist() == bl
+        if margin > 1e-12:
+            assert toks[0].tolist() == bt
+
+
+def test_single_rounding_special_cases(oracle_mod):
+    # base = 0: both modes round the dot product once, so they agree (and equal
+    # the rounding of a numpy matmul); W2 = 0: both give the base logits
+    V, r = 500, 256
+    W1, W2 = workloads.weights(0, V=V, r=r)
+    base0 = np.zeros((1, 5, V), dtype=np.uint16)
+    t1, l1 = oracle_mod.walk(W1, base0, [3], [0.0], W2_bits=W2)
+    t2, l2 = oracle_mod.walk(W1, base0, [3], [0.0], W2_bits=W2, single_round=True)
+    assert np.array_equal(l1, l2) and np.array_equal(t1, t2)
+    d = workloads.toy(9, V=V, r=r, B=4, gamma=3)
+    Wz = np.zeros((V, r), dtype=np.uint16)
+    for sr in (False, True):
+        toks, logits = oracle_mod.walk(d["W1"], d["base"], d["anchor"], np.zeros(4, np.float32),
+                                       W2_bits=Wz, single_round=sr)
+        assert np.array_equal(logits, d["base"])
+    # the two modes differ somewhere on ordinary inputs (the flag is not a no-op)
+    e = workloads.toy(11, V=V, r=r, B=1, gamma=4, base_std=2.0)
+    _, la = oracle_mod.walk(e["W1"], e["base"], e["anchor"], [0.0], W2_bits=e["W2"])
+    _, lb = oracle_mod.walk(e["W1"], e["base"], e["anchor"], [0.0], W2_bits=e["W2"], single_round=True)
+    assert not np.array_equal(la, lb)
 
 
 # ------------------------------------------------------------- special cases
