@@ -209,6 +209,24 @@ int dsw_status(dsw_handle_t h);
  * engine instead: see dsw_plan_compute with the walk's own gamma). */
 int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out);
 
+/* Device-drawn uniforms.  With enable != 0, later dsw_walk calls that pass
+ * uniforms == NULL draw the uniform of request b at step k on the device:
+ * the top 24 bits of word 0 of Philox-4x32-10 (Salmon et al., "Parallel
+ * Random Numbers: As Easy as 1, 2, 3", SC 2011) with counter
+ * (k, b, round counter, 0x44535721) and key (seed low word, seed high word),
+ * times 2^-24.  The round counter is the handle's device counter of completed
+ * walks (dsw_round_counter), so every launch or graph replay draws fresh
+ * uniforms -- the pages' kernel keys its noise by (seed, row, step, round
+ * counter): "Keeping the Draft Walk on Chip", section "The idea: make the
+ * walk resident".  Walks that pass uniforms use them.  enable = 0 restores
+ * the default (T > 0 with uniforms == NULL is DSW_ERR_DEV_UNIFORMS). */
+int dsw_set_seed(dsw_handle_t h, unsigned long long seed, int enable);
+
+/* The handle's device round counter: waits for the device, then reads it.
+ * It starts at 0 and counts the walks that completed without a device error;
+ * walk n (from 0) draws its device uniforms with round counter n. */
+int dsw_round_counter(dsw_handle_t h, unsigned* out);
+
 /* Diagnostics: record per-workgroup, per-step phase timestamps of later
  * dsw_walk calls into `trace`, a device buffer of `bytes` bytes owned by the
  * caller (NULL disables).  Layout: uint64 [grid][gamma+1][8]; row k < gamma

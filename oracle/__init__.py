@@ -61,6 +61,10 @@ def _load():
     lib.oracle_walk.restype = i
     lib.oracle_walk.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, P, P, P, i]
     lib.oracle_threads.restype = i
+    lib.oracle_philox4x32_10.argtypes = [P, P, P]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_device_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i, i, P]
+    lib.oracle_device_uniforms.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [i]
@@ -154,3 +158,21 @@ def walk(W1_bits, base_bits, anchor, T, uniforms=None, W2_bits=None, Q=None, sca
     if rc != 0:
         raise RuntimeError(f"oracle_walk failed with {rc}")
     return tokens, logits
+
+
+def philox4x32_10(ctr, key):
+    """Philox-4x32-10 of a 4-word counter and a 2-word key (4 output words)."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def device_uniforms(seed: int, round_counter: int, B: int, gamma: int):
+    """[B, gamma] f32: the uniforms a walk draws on the device from `seed`
+    when the handle's round counter is `round_counter`."""
+    out = np.empty((B, gamma), dtype=np.float32)
+    _load().oracle_device_uniforms(int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF,
+                                   int(B), int(gamma), _ptr(out))
+    return out

@@ -257,3 +257,58 @@ int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
     free(lg);
     return 0;
 }
+
+/*
+ * Counter-based uniforms, for walks that draw their uniforms on the device.
+ * Philox-4x32 with 10 rounds, as defined in Salmon, Moraes, Dror and Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011): each round
+ * multiplies counter words 0 and 2 by the two round constants, keeps the high
+ * and low halves of the 64-bit products, mixes the high halves with the
+ * other two counter words and the key, and the key advances by the two Weyl
+ * constants between rounds.
+ */
+static void mulhilo32(uint32_t a, uint32_t b, uint32_t* hi, uint32_t* lo) {
+    const uint64_t p = (uint64_t)a * (uint64_t)b;
+    *hi = (uint32_t)(p >> 32);
+    *lo = (uint32_t)p;
+}
+
+void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint32_t hi0, lo0, hi1, lo1;
+        mulhilo32(0xD2511F53u, c[0], &hi0, &lo0);
+        mulhilo32(0xCD9E8D57u, c[2], &hi1, &lo1);
+        const uint32_t n0 = hi1 ^ c[1] ^ k0;
+        const uint32_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+    out[0] = c[0];
+    out[1] = c[1];
+    out[2] = c[2];
+    out[3] = c[3];
+}
+
+/* The uniform of request b at step k of the walk whose device round counter
+ * was `round`: counter (k, b, round, 0x44535721), key (seed low, seed high),
+ * the first output word's top 24 bits as a multiple of 2^-24 in [0, 1). */
+float oracle_device_uniform(uint64_t seed, uint32_t round, int b, int k) {
+    const uint32_t ctr[4] = {(uint32_t)k, (uint32_t)b, round, 0x44535721u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return (float)(out[0] >> 8) * (1.0f / 16777216.0f);
+}
+
+void oracle_device_uniforms(uint64_t seed, uint32_t round, int B, int gamma, float* out) {
+    for (int b = 0; b < B; ++b)
+        for (int k = 0; k < gamma; ++k) out[(size_t)b * gamma + k] = oracle_device_uniform(seed, round, b, k);
+}

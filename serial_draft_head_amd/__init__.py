@@ -101,8 +101,11 @@ def lib():
         L.dsw_destroy.argtypes = [P]
         L.dsw_strerror.argtypes = [I]
         L.dsw_strerror.restype = ctypes.c_char_p
+        L.dsw_set_seed.argtypes = [P, ctypes.c_ulonglong, I]
+        L.dsw_round_counter.argtypes = [P, ctypes.POINTER(ctypes.c_uint)]
+        L.dsw_set_trace.argtypes = [P, P, ctypes.c_longlong]
         for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_status",
-                  "dsw_query_plan", "dsw_destroy"):
+                  "dsw_query_plan", "dsw_destroy", "dsw_set_seed", "dsw_round_counter", "dsw_set_trace"):
             getattr(L, f).restype = I
         _lib = L
         return L
@@ -168,6 +171,17 @@ class Walker:
         _check(lib().dsw_query_plan(self._h, int(B), ctypes.byref(out)), "dsw_query_plan")
         return out
 
+    def set_seed(self, seed: int, enable: bool = True) -> None:
+        """Walks with uniforms=None draw their uniforms on the device (dsw_set_seed)."""
+        _check(lib().dsw_set_seed(self._h, ctypes.c_ulonglong(int(seed) & (2 ** 64 - 1)), int(bool(enable))),
+               "dsw_set_seed")
+
+    def round_counter(self) -> int:
+        """The device round counter (waits for the device)."""
+        out = ctypes.c_uint(0)
+        _check(lib().dsw_round_counter(self._h, ctypes.byref(out)), "dsw_round_counter")
+        return int(out.value)
+
     def status(self) -> int:
         """Wait for the device; return (and clear) the latched device status code."""
         return lib().dsw_status(self._h)
@@ -177,7 +191,7 @@ class Walker:
         """One round.  Tensors live on this handle's device:
         W1 bf16 [V,256]; W2 bf16 [V,256] (or int8 + w2_scale f32 [V]);
         base bf16 [B,gamma,V]; anchor int32 [B]; T float32 [B] (0 = greedy);
-        uniforms float32 [B,gamma] or None when every T is 0.
+        uniforms float32 [B,gamma], or None when every T is 0 or after set_seed (drawn on the device).
         Returns (tokens int32 [B,gamma], logits bf16 [B,gamma,V] or None)."""
         import torch
         dev = torch.device("cuda", self.device)

@@ -38,6 +38,8 @@ struct dsw_handle {
     size_t ws_bytes;
     uint16_t* blog_mem;  // batched kernel: logits of sampled requests, [B_max][V] bf16
     dsw::Workspace ws;
+    unsigned long long seed;    // key of device-drawn uniforms (when seeded)
+    int seeded;
     unsigned long long* trace;  // optional device trace buffer (caller-owned)
     long long trace_bytes;
     std::mutex mu;  // guards the per-kernel attribute cache below
@@ -127,6 +129,8 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->dev = dev;
     h->trace = nullptr;
     h->trace_bytes = 0;
+    h->seed = 0ull;
+    h->seeded = 0;
     memset(h->lds_configured, 0, sizeof(h->lds_configured));
     memset(h->lds_configured_bytes, 0, sizeof(h->lds_configured_bytes));
     h->n_configured = 0;
@@ -263,6 +267,8 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     p.aligned = (h->V % 8) == 0;
     p.spin_limit = kSpinLimit;
     p.single_round = (h->flags & DSW_FLAG_SINGLE_ROUND) ? 1 : 0;
+    p.seeded = h->seeded;
+    p.seed = h->seed;
     p.trace = nullptr;
     if (h->trace != nullptr &&
         (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)
@@ -277,6 +283,22 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
                             static_cast<hipStream_t>(stream));
     if (e == hipErrorCooperativeLaunchTooLarge) return DSW_ERR_LAUNCH;
     return e == hipSuccess ? DSW_OK : DSW_ERR_HIP;
+}
+
+extern "C" int dsw_set_seed(dsw_handle_t h, unsigned long long seed, int enable) {
+    if (!h) return DSW_ERR_NULL;
+    h->seed = seed;
+    h->seeded = enable ? 1 : 0;
+    return DSW_OK;
+}
+
+extern "C" int dsw_round_counter(dsw_handle_t h, unsigned* out) {
+    if (!h || !out) return DSW_ERR_NULL;
+    DeviceGuard g(h->device);
+    if (!g.ok) return DSW_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return DSW_ERR_HIP;
+    if (hipMemcpy(out, h->ws.round_ctr, sizeof *out, hipMemcpyDeviceToHost) != hipSuccess) return DSW_ERR_HIP;
+    return DSW_OK;
 }
 
 extern "C" int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes) {

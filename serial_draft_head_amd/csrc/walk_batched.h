@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             if (c == 0) latch(status, kStatusToken);
             a = 0;
         }
-        if (temp > 0.0f && p.uniforms == nullptr) {
+        if (temp > 0.0f && p.uniforms == nullptr && !p.seeded) {
             if (c == 0) latch(status, kStatusUniforms);
             temp = 0.0f;
         }
@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const float incl_ = wave_incl_scan_dpp(q3_);                                         \
             const float ex_ = incl_ - q3_;                                                       \
             const float Z_ = __shfl(incl_, 63);                                                  \
-            const float tgt_ = p.uniforms[(size_t)(b_) * gamma + k] * Z_;                        \
+            const float tgt_ = walk_uniform(p, (b_), k, gamma, round) * Z_;                      \
             const float c4_[4] = {ex_ + q0_, ex_ + q1_, ex_ + q2_, ex_ + q3_};                   \
             const float w4_[4] = {m4_.x, m4_.y, m4_.z, m4_.w};                                   \
             uint32_t first_ = 0u, lastp_ = 0u;                                                   \

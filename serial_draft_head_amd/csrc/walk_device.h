@@ -52,6 +52,41 @@ __device__ __forceinline__ float dot8(const uint4 w, const uint4 u, float acc) {
     return acc;
 }
 
+// ------------------------------------------------------ device uniforms
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC 2011): per round, counter words 0 and 2 are
+// multiplied by the round constants; the high halves of the products are mixed
+// with words 3 and 1 and the key, the low halves carried over; the key
+// advances by the Weyl constants between rounds.  Returns output word 0.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t h0 = __umulhi(0xD2511F53u, c0), l0 = 0xD2511F53u * c0;
+        const uint32_t h1 = __umulhi(0xCD9E8D57u, c2), l1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = l1;
+        c2 = n2;
+        c3 = l0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+
+// The uniform of request b at step k: supplied by the caller, or drawn on the
+// device, keyed by (seed, request, step, round counter) as the pages' kernel
+// keys its noise ("Keeping the Draft Walk on Chip", section "The idea: make
+// the walk resident"), so every launch and graph replay draws fresh values:
+// the top 24 bits of Philox word 0, as a multiple of 2^-24 in [0, 1).
+__device__ __forceinline__ float walk_uniform(const WalkParams& p, int b, int k, int gamma, unsigned round) {
+    if (p.uniforms != nullptr) return p.uniforms[(size_t)b * gamma + k];
+    const uint32_t w = philox_word0((uint32_t)k, (uint32_t)b, round, 0x44535721u, (uint32_t)p.seed,
+                                    (uint32_t)(p.seed >> 32));
+    return (float)(w >> 8) * (1.0f / 16777216.0f);
+}
+
 // Selection key (36 bits): order-preserving bits of the bf16 logit, then the
 // inverted row index (rows < 2^20).  Larger key = larger logit, then smaller id.
 constexpr int kIdxBits = 20;

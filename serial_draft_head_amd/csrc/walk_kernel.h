@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 if (c == 0) latch(status, kStatusToken);
                 a = 0;
             }
-            if (temp > 0.0f && p.uniforms == nullptr) {
+            if (temp > 0.0f && p.uniforms == nullptr && !p.seeded) {
                 if (c == 0) latch(status, kStatusUniforms);
                 temp = 0.0f;
             }
@@ -819,7 +819,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const float incl = wave_incl_scan_dpp(q3);
                 const float ex = incl - q3;
                 const float Z = __shfl(incl, 63);
-                const float target = p.uniforms[(size_t)b * gamma + k] * Z;
+                const float target = walk_uniform(p, b, k, gamma, round) * Z;
                 const float c4[4] = {ex + q0, ex + q1, ex + q2, ex + q3};
                 const float w4[4] = {m4.x, m4.y, m4.z, m4.w};
                 uint32_t first = 0u, lastp = 0u;  // shard + 1, 0 = none

@@ -99,6 +99,8 @@ struct WalkParams {
     int aligned;             // batched kernel: V % 8 == 0 (16-byte aligned base rows)
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
     int single_round;        // 1: logit = bf16(base + fp32 dot), rounded once
+    int seeded;              // 1: uniforms == NULL draws them on the device from seed
+    unsigned long long seed; // key of the device-drawn uniforms
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };
 

@@ -292,6 +292,48 @@ def test_single_rounding(dsw, V, B, gamma, temps, flags, dt):
     walker.close()
 
 
+# uniforms drawn on the device (Philox keyed by seed, request, step and the
+# handle's round counter), checked against the oracle's own Philox
+@pytest.mark.parametrize("V,B,gamma,flags", [(32_000, 1, 6, 0), (60_000, 1, 3, 4), (60_000, 3, 4, 8),
+                                             (129_280, 20, 3, 0)])
+def test_device_uniforms(dsw, V, B, gamma, flags):
+    import oracle
+    say(f"device uniforms V={V} B={B} gamma={gamma} flags={flags}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, flags=flags)
+    seed = 0x5EED_0000_0000 + V
+    walker.set_seed(seed)
+    seen = []
+    for rnd in range(3):
+        inp = workloads.round_inputs(2, 80 + rnd, B=B, gamma=gamma, V=V, temps="cycle" if B == 1 else "mixed")
+        if B == 1:
+            inp["T"][:] = 1.0
+        ctr = walker.round_counter()
+        base, anchor, T, _ = round_dev(inp)
+        tokens, logits = walker.walk(W1d, W2d, base, anchor, T, None, want_logits=True)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        uni = oracle.device_uniforms(seed, ctr, B, gamma)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], uni, toks, lg)
+        say(rnd, "round counter", ctr, rep)
+        assert walker.round_counter() == ctr + 1
+        seen.append(ctr)
+    assert len(set(seen)) == 3
+    # without a seed, a sampled request with no uniforms is a latched device error
+    walker.set_seed(seed, enable=False)
+    inp = workloads.round_inputs(2, 90, B=B, gamma=gamma, V=V, temps="cycle")
+    inp["T"][:] = 1.0
+    base, anchor, T, _ = round_dev(inp)
+    walker.walk(W1d, W2d, base, anchor, T, None)
+    torch.cuda.synchronize()
+    assert walker.status() == -22
+    walker.close()
+
+
 # int8 rows + fp32 row scales: one vocabulary per compiled int8 shape, plus
 # ragged sizes; the harness quantizes once and both sides consume (q, scale).
 I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),

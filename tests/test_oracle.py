@@ -111,6 +111,33 @@ def test_hand_worked_walk_single_rounding(oracle_mod):
     assert logits[0].tolist() == want
 
 
+def test_philox_known_answers(oracle_mod):
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        g = json.load(f)
+    for v in g["vectors"]:
+        ctr = [int(x, 16) for x in v["ctr"]]
+        key = [int(x, 16) for x in v["key"]]
+        assert [int(x) for x in oracle_mod.philox4x32_10(ctr, key)] == [int(x, 16) for x in v["out"]]
+
+
+def test_device_uniforms_follow_their_definition(oracle_mod):
+    # u(b, k) = top 24 bits of word 0 of Philox(counter (k, b, round, tag), key = seed) / 2^24
+    seed, rnd, B, gamma = 0x0123456789ABCDEF, 77, 5, 9
+    u = oracle_mod.device_uniforms(seed, rnd, B, gamma)
+    for b in range(B):
+        for k in range(gamma):
+            w = int(oracle_mod.philox4x32_10([k, b, rnd, 0x44535721], [seed & 0xFFFFFFFF, seed >> 32])[0])
+            assert u[b, k] == np.float32((w >> 8) / 2.0 ** 24)
+    big = oracle_mod.device_uniforms(7, 3, 256, 64).ravel()
+    assert big.min() >= 0.0 and big.max() < 1.0
+    # 16 equal bins over 16,384 draws: each within 5 sigma of 1,024
+    counts = np.bincount((big * 16).astype(int), minlength=16)
+    assert np.all(np.abs(counts - 1024) < 5 * math.sqrt(1024 * 15 / 16))
+    # a new round or seed gives new uniforms
+    assert not np.array_equal(oracle_mod.device_uniforms(7, 4, 256, 64).ravel(), big)
+    assert not np.array_equal(oracle_mod.device_uniforms(8, 3, 256, 64).ravel(), big)
+
+
 def test_hand_worked_sampler(oracle_mod):
     with open(os.path.join(GOLDEN, "hand_sampler.json")) as f:
         g = json.load(f)
