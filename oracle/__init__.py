@@ -14,7 +14,9 @@ What it computes (see the header of walk_oracle.c for the passages followed):
 "The serial part of a parallel drafter": ``u = W1[prev]``,
 ``logit = bf16(base + bf16(W2 @ u))``, argmax or a sample of
 ``softmax(logit / T)``, ``prev = tok``; the sampler is the inverse CDF of
-vLLM PR #64442, section "Details".
+vLLM PR #64442, section "Details", or (the ``gumbel`` mode) Gumbel-max from
+counter-based noise, the pages' small-batch sampler (section "The idea: make
+the walk resident").
 """
 from __future__ import annotations
 
@@ -60,6 +62,15 @@ def _load():
     lib.oracle_sample.argtypes = [i, P, f, f]
     lib.oracle_walk.restype = i
     lib.oracle_walk.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, P, P, P, i]
+    lib.oracle_walk_ex.restype = i
+    lib.oracle_walk_ex.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, P, P, P, i,
+                                   ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_gumbel_uniform.restype = ctypes.c_double
+    lib.oracle_gumbel_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, i, i, i]
+    lib.oracle_gumbel_scores.restype = i
+    lib.oracle_gumbel_scores.argtypes = [i, P, f, ctypes.c_uint64, ctypes.c_uint32, i, i, P]
+    lib.oracle_gumbel_from_uniforms.restype = i
+    lib.oracle_gumbel_from_uniforms.argtypes = [i, P, ctypes.c_double, P]
     lib.oracle_threads.restype = i
     lib.oracle_philox4x32_10.argtypes = [P, P, P]
     lib.oracle_philox4x32_10.restype = None
@@ -104,6 +115,7 @@ def bf16_bits_to_f64(bits):
 
 
 SINGLE_ROUND = 1  # mode bit: logit = bf16(base + dot), rounded once
+GUMBEL = 2        # mode bit: sampled requests draw by Gumbel-max from counter-based noise
 
 
 def step(u_bits, base_bits, T, uniform, W2_bits=None, Q=None, scale=None, single_round=False):
@@ -133,10 +145,12 @@ def sample(logits_bits, T, uniform) -> int:
 
 
 def walk(W1_bits, base_bits, anchor, T, uniforms=None, W2_bits=None, Q=None, scale=None,
-         forced=None, want_logits=True, single_round=False):
+         forced=None, want_logits=True, single_round=False, gumbel=False, seed=0, round_counter=0):
     """The whole walk.  Shapes: W1 [V,r] u16, W2 [V,r] u16 (or Q [V,r] i8 + scale [V] f32),
     base [B,gamma,V] u16, anchor [B] i32, T [B] f32, uniforms [B,gamma] f32 or None,
     forced [B,gamma] i32 or None (teacher forcing: step k>0 uses forced[:,k-1] as prev).
+    gumbel: sampled requests draw by Gumbel-max from the noise of `seed` and the
+    device round counter `round_counter` (uniforms are then not used).
 
     Returns (tokens [B,gamma] i32, logits [B,gamma,V] u16 or None)."""
     W1_bits = _c(W1_bits, np.uint16)
@@ -151,10 +165,11 @@ def walk(W1_bits, base_bits, anchor, T, uniforms=None, W2_bits=None, Q=None, sca
     assert base_bits.shape[2] == V
     tokens = np.empty((B, gamma), dtype=np.int32)
     logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
-    rc = _load().oracle_walk(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
-                             _ptr(base_bits), _ptr(anchor), _ptr(T), _ptr(uniforms),
-                             _ptr(forced), _ptr(tokens), _ptr(logits),
-                             SINGLE_ROUND if single_round else 0)
+    mode = (SINGLE_ROUND if single_round else 0) | (GUMBEL if gumbel else 0)
+    rc = _load().oracle_walk_ex(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+                                _ptr(base_bits), _ptr(anchor), _ptr(T), _ptr(uniforms),
+                                _ptr(forced), _ptr(tokens), _ptr(logits), mode,
+                                int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF)
     if rc != 0:
         raise RuntimeError(f"oracle_walk failed with {rc}")
     return tokens, logits
@@ -176,3 +191,30 @@ def device_uniforms(seed: int, round_counter: int, B: int, gamma: int):
     _load().oracle_device_uniforms(int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF,
                                    int(B), int(gamma), _ptr(out))
     return out
+
+
+def gumbel_uniform(seed: int, round_counter: int, b: int, k: int, v: int) -> float:
+    """The Gumbel-max noise uniform U in (0, 1) of vocabulary row v, request b, step k."""
+    return _load().oracle_gumbel_uniform(int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF,
+                                         int(b), int(k), int(v))
+
+
+def gumbel_scores(logits_bits, T, seed: int, round_counter: int, b: int, k: int):
+    """f64 perturbed scores logit / T - ln(-ln U) of one request and step, for given bf16 logits."""
+    lb = _c(logits_bits, np.uint16)
+    out = np.empty(lb.shape[0], dtype=np.float64)
+    rc = _load().oracle_gumbel_scores(lb.shape[0], _ptr(lb), float(T), int(seed) & (2 ** 64 - 1),
+                                      int(round_counter) & 0xFFFFFFFF, int(b), int(k), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gumbel_scores failed with {rc}")
+    return out
+
+
+def gumbel_from_uniforms(logits, T, U) -> int:
+    """Gumbel-max draw over f64 logits with given uniforms U in (0, 1)."""
+    lg = _c(logits, np.float64)
+    u = _c(U, np.float64)
+    tok = _load().oracle_gumbel_from_uniforms(lg.shape[0], _ptr(lg), float(T), _ptr(u))
+    if tok < 0:
+        raise RuntimeError(f"oracle_gumbel_from_uniforms failed with {tok}")
+    return tok

@@ -32,6 +32,12 @@
  *   T  > 0 : M = max logit, w_v = exp((logit_v - M) / T), C_v = sum_{j<=v} w_j,
  *            Z = C_{V-1}, t = uniform * Z, tok = smallest v with C_v > t
  *            (if rounding leaves none, the largest v with w_v > 0).
+ *   Gumbel-max mode (ORACLE_GUMBEL, T > 0): tok = smallest v maximising
+ *            logit_v / T - ln(-ln U_v), one counter-based uniform U_v in (0, 1)
+ *            per request, step and vocabulary row (the pages' in-kernel sampler
+ *            for small batches: "Keeping the Draft Walk on Chip", section
+ *            "The idea: make the walk resident"; argmax of the perturbed
+ *            logits is an exact draw from softmax(logit / T)).
  *   prev     = tok for the next step.
  *
  * Parallelism: OpenMP over vocabulary rows inside one GEMV.  Each row's sum
@@ -57,6 +63,9 @@ static double bf16_value(uint16_t h) {
 
 /* Mode bits of oracle_step / oracle_walk. */
 #define ORACLE_SINGLE_ROUND 1
+#define ORACLE_GUMBEL 2
+
+static int sample_gumbel(const double* logit, int V, double T, uint64_t seed, uint32_t round, int b, int k);
 
 /* Round x to the nearest bf16 value (8 significant bits, exponent range of
  * binary32), ties to even, directly from binary64.  The result is returned as
@@ -105,6 +114,14 @@ void oracle_set_threads(int n) {
 #endif
 }
 
+/* The smallest index holding the largest of V values (ties go to the smallest id). */
+static int first_argmax(const double* x, int V) {
+    int best = 0;
+    for (int v = 1; v < V; ++v)
+        if (x[v] > x[best]) best = v;   /* strict: the first maximum wins */
+    return best;
+}
+
 /* Inverse-CDF draw over softmax(logit / T) from one uniform in [0, 1).
  * logit holds V finite values.  Returns the chosen token id. */
 static int sample_inverse_cdf(const double* logit, int V, double T, double uniform) {
@@ -146,7 +163,8 @@ static int sample_inverse_cdf(const double* logit, int V, double T, double unifo
 static int oracle_step_impl(int V, int r, const uint16_t* u_bits,
                             const uint16_t* W2, const int8_t* Q, const float* scale,
                             const uint16_t* base, float T, float uniform,
-                            uint16_t* logits, double* lg, int mode) {
+                            uint16_t* logits, double* lg, int mode,
+                            uint64_t seed, uint32_t round, int b, int k) {
     const int single = (mode & ORACLE_SINGLE_ROUND) != 0;
     double* u = (double*)malloc(sizeof(double) * (size_t)r);
     if (!u) return -3;
@@ -175,23 +193,20 @@ static int oracle_step_impl(int V, int r, const uint16_t* u_bits,
     free(u);
     if (bad) return -2;
 
-    if (T == 0.0f) {
-        int best = 0;
-        for (int v = 1; v < V; ++v)
-            if (lg[v] > lg[best]) best = v;   /* strict: the first maximum wins */
-        return best;
-    }
+    if (T == 0.0f) return first_argmax(lg, V);
+    if (mode & ORACLE_GUMBEL) return sample_gumbel(lg, V, (double)T, seed, round, b, k);
     return sample_inverse_cdf(lg, V, (double)T, (double)uniform);
 }
 
-/* Public single step (see oracle_step_impl). */
+/* Public single step (see oracle_step_impl; inverse-CDF sampling). */
 int oracle_step(int V, int r, const uint16_t* u_bits, const uint16_t* W2,
                 const int8_t* Q, const float* scale, const uint16_t* base,
                 float T, float uniform, uint16_t* logits, int mode) {
     if (V <= 0 || r <= 0 || !u_bits || !base || (!W2 && (!Q || !scale))) return -1;
     double* lg = (double*)malloc(sizeof(double) * (size_t)V);
     if (!lg) return -3;
-    int tok = oracle_step_impl(V, r, u_bits, W2, Q, scale, base, T, uniform, logits, lg, mode);
+    int tok = oracle_step_impl(V, r, u_bits, W2, Q, scale, base, T, uniform, logits, lg,
+                               mode & ORACLE_SINGLE_ROUND, 0, 0, 0, 0);
     free(lg);
     return tok;
 }
@@ -221,20 +236,23 @@ int oracle_sample(int V, const uint16_t* logits, float T, float uniform) {
  *              (teacher forcing, so each step can be judged on its own).
  *   tokens   : [B][gamma] out
  *   logits   : [B][gamma][V] bf16 bits out, or NULL
- *   mode     : 0, or ORACLE_SINGLE_ROUND
+ *   mode     : 0, or ORACLE_SINGLE_ROUND, ORACLE_GUMBEL (or both)
+ *   seed, round : Gumbel-max mode only: the key and the device round counter
+ *              of the uniforms (see oracle_gumbel_uniform)
  * Returns 0, or a negative error (-1 bad argument, -2 non-finite logit,
  * -3 out of memory).
  */
-int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
-                const uint16_t* W2, const int8_t* Q, const float* scale,
-                const uint16_t* base, const int32_t* anchor, const float* T,
-                const float* uniforms, const int32_t* forced, int32_t* tokens,
-                uint16_t* logits, int mode) {
+int oracle_walk_ex(int V, int r, int B, int gamma, const uint16_t* W1,
+                   const uint16_t* W2, const int8_t* Q, const float* scale,
+                   const uint16_t* base, const int32_t* anchor, const float* T,
+                   const float* uniforms, const int32_t* forced, int32_t* tokens,
+                   uint16_t* logits, int mode, uint64_t seed, uint32_t round) {
     if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !base || !anchor || !T ||
         !tokens || (!W2 && (!Q || !scale)))
         return -1;
+    if ((mode & ORACLE_GUMBEL) && B > 256) return -1;  /* request ids live in 8 counter bits */
     for (int b = 0; b < B; ++b) {
-        if (T[b] != 0.0f && !uniforms) return -1;
+        if (T[b] != 0.0f && !uniforms && !(mode & ORACLE_GUMBEL)) return -1;
         if (anchor[b] < 0 || anchor[b] >= V) return -1;
     }
     double* lg = (double*)malloc(sizeof(double) * (size_t)V);
@@ -248,7 +266,7 @@ int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
             uint16_t* out = logits ? logits + ((size_t)b * gamma + k) * (size_t)V : NULL;
             float uni = uniforms ? uniforms[(size_t)b * gamma + k] : 0.0f;
             int tok = oracle_step_impl(V, r, W1 + (size_t)prev * (size_t)r, W2, Q, scale,
-                                       base_k, T[b], uni, out, lg, mode);
+                                       base_k, T[b], uni, out, lg, mode, seed, round, b, k);
             if (tok < 0) { free(lg); return tok; }
             tokens[(size_t)b * gamma + k] = tok;
             prev = tok;
@@ -256,6 +274,16 @@ int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
     }
     free(lg);
     return 0;
+}
+
+/* The walk with inverse-CDF sampling (oracle_walk_ex without Gumbel-max). */
+int oracle_walk(int V, int r, int B, int gamma, const uint16_t* W1,
+                const uint16_t* W2, const int8_t* Q, const float* scale,
+                const uint16_t* base, const int32_t* anchor, const float* T,
+                const float* uniforms, const int32_t* forced, int32_t* tokens,
+                uint16_t* logits, int mode) {
+    return oracle_walk_ex(V, r, B, gamma, W1, W2, Q, scale, base, anchor, T, uniforms, forced,
+                          tokens, logits, mode & ORACLE_SINGLE_ROUND, 0, 0);
 }
 
 /*
@@ -311,4 +339,66 @@ float oracle_device_uniform(uint64_t seed, uint32_t round, int b, int k) {
 void oracle_device_uniforms(uint64_t seed, uint32_t round, int B, int gamma, float* out) {
     for (int b = 0; b < B; ++b)
         for (int k = 0; k < gamma; ++k) out[(size_t)b * gamma + k] = oracle_device_uniform(seed, round, b, k);
+}
+
+/*
+ * Gumbel-max sampling.  The noise of vocabulary row v for request b at step k
+ * of the walk whose device round counter was `round`: Philox-4x32-10 of the
+ * counter (v / 4, 256 k + b, round, 0x47554D42) under the key (seed low, seed
+ * high), output word v mod 4 (four consecutive rows share one call), mapped to
+ * the odd multiple (2 (w >> 9) + 1) 2^-24 of 2^-24, which lies strictly inside
+ * (0, 1) and is exact in binary32.  The Gumbel variate is -ln(-ln U).
+ */
+double oracle_gumbel_uniform(uint64_t seed, uint32_t round, int b, int k, int v) {
+    const uint32_t ctr[4] = {(uint32_t)v >> 2, ((uint32_t)k << 8) | ((uint32_t)b & 0xFFu), round, 0x47554D42u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return (double)(2u * (out[v & 3] >> 9) + 1u) * (1.0 / 16777216.0);
+}
+
+/* Perturbed scores logit_v / T - ln(-ln U_v) of one request and step. */
+static void gumbel_scores(const double* logit, int V, double T, uint64_t seed, uint32_t round, int b, int k,
+                          double* score) {
+    for (int v = 0; v < V; ++v) {
+        const double U = oracle_gumbel_uniform(seed, round, b, k, v);
+        score[v] = logit[v] / T - log(-log(U));
+    }
+}
+
+/* Gumbel-max draw: the smallest v with the largest perturbed score. */
+static int sample_gumbel(const double* logit, int V, double T, uint64_t seed, uint32_t round, int b, int k) {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!sc) return -3;
+    gumbel_scores(logit, V, T, seed, round, b, k, sc);
+    const int best = first_argmax(sc, V);
+    free(sc);
+    return best;
+}
+
+/* The perturbed scores for given bf16 logits (used to judge GPU tokens on the
+ * GPU's own emitted logits); T > 0. */
+int oracle_gumbel_scores(int V, const uint16_t* logits, float T, uint64_t seed, uint32_t round, int b, int k,
+                         double* score) {
+    if (V <= 0 || !logits || !score || !(T > 0.0f)) return -1;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!lg) return -3;
+    for (int v = 0; v < V; ++v) lg[v] = bf16_value(logits[v]);
+    gumbel_scores(lg, V, (double)T, seed, round, b, k, score);
+    free(lg);
+    return 0;
+}
+
+/* Gumbel-max draw from given uniforms (no counter-based generator): the
+ * definition of the sampler on its own, for worked examples. */
+int oracle_gumbel_from_uniforms(int V, const double* logit, double T, const double* U) {
+    if (V <= 0 || !logit || !U || !(T > 0.0)) return -1;
+    for (int v = 0; v < V; ++v)
+        if (!(U[v] > 0.0 && U[v] < 1.0)) return -1;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!sc) return -3;
+    for (int v = 0; v < V; ++v) sc[v] = logit[v] / T - log(-log(U[v]));
+    const int best = first_argmax(sc, V);
+    free(sc);
+    return best;
 }

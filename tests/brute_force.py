@@ -77,3 +77,26 @@ def walk(W1, W2, base, anchor, T=0.0, uniforms=None, Q=None, scale=None, single=
         logits.append(lb)
         prev = tok
     return toks, logits, margin
+
+
+def gumbel_uniform(philox_words, v):
+    """U of vocabulary row v from the four Philox words of its group of four rows:
+    the odd multiple (2 (w >> 9) + 1) 2^-24 of 2^-24, as an exact rational."""
+    w = int(philox_words[v % 4])
+    return Fraction(2 * (w >> 9) + 1, 2 ** 24)
+
+
+def gumbel_exact(logit_bits, T, U):
+    """Gumbel-max at 60 digits: (token, gap between the two largest scores)."""
+    sc = []
+    for x, u in zip(logit_bits, U):
+        l = mpmath.mpf(value(x).numerator) / value(x).denominator
+        uu = mpmath.mpf(u.numerator) / u.denominator
+        sc.append(l / mpmath.mpf(float(T)) - mpmath.log(-mpmath.log(uu)))
+    best = 0
+    for v in range(1, len(sc)):
+        if sc[v] > sc[best]:
+            best = v
+    rest = [s for v, s in enumerate(sc) if v != best]
+    gap = float(sc[best] - max(rest)) if rest else 1.0
+    return best, gap

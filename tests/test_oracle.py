@@ -138,6 +138,112 @@ def test_device_uniforms_follow_their_definition(oracle_mod):
     assert not np.array_equal(oracle_mod.device_uniforms(8, 3, 256, 64).ravel(), big)
 
 
+def test_hand_worked_gumbel(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_gumbel.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert oracle_mod.gumbel_from_uniforms(c["logits"], c["T"], c["U"]) == c["token"], c
+
+
+def test_gumbel_uniforms_follow_their_definition(oracle_mod):
+    # U(b, k, v) = (2 (w >> 9) + 1) / 2^24, w = word v % 4 of
+    # Philox(counter (v / 4, 256 k + b, round, tag), key = seed)
+    seed, rnd = 0xFEDCBA9876543210, 1234
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        b, k, v = int(rng.integers(0, 256)), int(rng.integers(0, 64)), int(rng.integers(0, 1 << 20))
+        w = oracle_mod.philox4x32_10([v >> 2, (k << 8) | b, rnd, 0x47554D42],
+                                     [seed & 0xFFFFFFFF, seed >> 32])
+        want = bf.gumbel_uniform(w, v)
+        got = oracle_mod.gumbel_uniform(seed, rnd, b, k, v)
+        assert Fraction(got) == want
+        assert 0.0 < got < 1.0
+        assert float(np.float32(got)) == got  # exact in binary32
+    # neighbouring rows, requests, steps and rounds draw different noise
+    u0 = oracle_mod.gumbel_uniform(seed, rnd, 3, 2, 100)
+    for args in ((seed, rnd, 3, 2, 101), (seed, rnd, 4, 2, 100), (seed, rnd, 3, 3, 100),
+                 (seed, rnd + 1, 3, 2, 100), (seed + 1, rnd, 3, 2, 100)):
+        assert oracle_mod.gumbel_uniform(*args) != u0
+
+
+def test_gumbel_max_draws_follow_softmax(oracle_mod):
+    # the argmax of logit / T + G is a draw from softmax(logit / T): frequencies
+    # over 40,000 rounds of noise within 5 sigma of the softmax probabilities
+    logits = [0.0, 1.0, -0.5, 2.0, 0.25]
+    lb = bits_of(logits)
+    for T in (0.7, 1.6):
+        N = 40000
+        counts = np.zeros(len(logits))
+        for rnd in range(N):
+            counts[int(np.argmax(oracle_mod.gumbel_scores(lb, T, 99, rnd, 1, 2)))] += 1
+        p = np.exp(np.array(logits) / T)
+        p /= p.sum()
+        sigma = np.sqrt(N * p * (1 - p))
+        assert np.all(np.abs(counts - N * p) < 5 * sigma), (T, counts, N * p)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_gumbel(oracle_mod, seed):
+    V, gamma, B = 12, 3, 3
+    d = workloads.toy(seed + 700, V=V, r=4, B=B, gamma=gamma, base_std=1.5)
+    key, rnd = 1000 + seed, 17 * seed + 3
+    for T in (0.6, 1.0, 2.5):
+        Tv = np.full(B, T, np.float32)
+        toks, logits = oracle_mod.walk(d["W1"], d["base"], d["anchor"], Tv, W2_bits=d["W2"],
+                                       gumbel=True, seed=key, round_counter=rnd)
+        for b in range(B):
+            prev = int(d["anchor"][b])
+            for k in range(gamma):
+                u = [value(d["W1"][prev, j]) for j in range(4)]
+                lb = bf.step_logits(d["W2"], u, d["base"][b, k])
+                assert logits[b, k].tolist() == lb
+                U = [bf.gumbel_uniform(oracle_mod.philox4x32_10(
+                    [v >> 2, (k << 8) | b, rnd, 0x47554D42], [key & 0xFFFFFFFF, key >> 32]), v)
+                    for v in range(V)]
+                tok, gap = bf.gumbel_exact(lb, T, U)
+                if gap > 1e-12:
+                    assert toks[b, k] == tok
+                prev = int(toks[b, k])
+
+
+def test_gumbel_walk_small_temperature_is_greedy(oracle_mod):
+    V = 2000
+    W1, W2 = workloads.weights(0, V=V)
+    inp = workloads.round_inputs(0, 5, B=2, gamma=6, V=V)
+    t0, lg0 = oracle_mod.walk(W1, inp["base"], inp["anchor"], [0.0, 0.0], W2_bits=W2)
+    t1, lg1 = oracle_mod.walk(W1, inp["base"], inp["anchor"], [1e-4, 1e-4], W2_bits=W2, forced=t0,
+                              gumbel=True, seed=3, round_counter=9)
+    assert np.array_equal(lg0, lg1)
+    # G lies in [-ln(-ln 2^-25), -ln(-ln(1 - 2^-25))] = [-2.9, 17.3]: a logit gap
+    # above 0.01 is worth 100 at T = 1e-4, more than any difference of noise
+    for b in range(2):
+        for k in range(6):
+            lv = np.sort(oracle_mod.bf16_bits_to_f64(lg1[b, k]))
+            if lv[-1] - lv[-2] > 0.01:
+                assert t1[b, k] == t0[b, k]
+
+
+def test_gumbel_walk_uses_its_own_request_step_and_round(oracle_mod):
+    # the walk's token at (b, k) is the argmax of the scores of (b, k, round) on
+    # its own logits; greedy requests in the same batch are unaffected
+    V = 1500
+    W1, W2 = workloads.weights(2, V=V)
+    inp = workloads.round_inputs(3, 0, B=3, gamma=5, V=V)
+    T = np.array([0.8, 0.0, 1.2], np.float32)
+    toks, lg = oracle_mod.walk(W1, inp["base"], inp["anchor"], T, W2_bits=W2, gumbel=True, seed=11,
+                               round_counter=40)
+    for b in (0, 2):
+        for k in range(5):
+            sc = oracle_mod.gumbel_scores(lg[b, k], T[b], 11, 40, b, k)
+            assert toks[b, k] == int(np.argmax(sc))
+    tg, _ = oracle_mod.walk(W1, inp["base"][1:2], inp["anchor"][1:2], [0.0], W2_bits=W2)
+    assert np.array_equal(toks[1], tg[0])
+    # another round counter draws other tokens somewhere
+    t2, _ = oracle_mod.walk(W1, inp["base"], inp["anchor"], T, W2_bits=W2, gumbel=True, seed=11,
+                            round_counter=41)
+    assert not np.array_equal(t2[[0, 2]], toks[[0, 2]])
+
+
 def test_hand_worked_sampler(oracle_mod):
     with open(os.path.join(GOLDEN, "hand_sampler.json")) as f:
         g = json.load(f)
