@@ -211,10 +211,12 @@ def gamma_sweep(torch, dsw, W1d, W2d, V, gammas=(1, 4, 7, 10, 16), rounds=60, K=
 # line's own measurements: (workload, requests, gamma, W2 storage).
 SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, "bf16"),
          (3, 1, 16, "bf16"), (3, 1, 16, "int8"), (4, 64, 5, "bf16"), (4, 128, 5, "bf16"),
-         (4, 253, 5, "bf16")]
+         (4, 253, 5, "bf16"),
+         # the mixed-temperature walks again, sampled by Gumbel-max (DSW_FLAG_GUMBEL)
+         (2, 1, 16, "bf16", "gumbel"), (2, 4, 16, "bf16", "gumbel"), (2, 16, 16, "bf16", "gumbel")]
 
 
-def sweep_one(torch, dsw, index, B, gamma, dtype):
+def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf"):
     import workloads
     wl = workloads.WORKLOADS[index]
     V = wl.V
@@ -235,7 +237,10 @@ def sweep_one(torch, dsw, index, B, gamma, dtype):
     rounds = make_rounds(index, 3 if big else 8, B, gamma, V, wl.temps)
     base, anchor, T, uni = to_device(rounds, torch, dev)
     del rounds
-    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, w2_dtype=dsw.INT8 if dtype == "int8" else dsw.BF16)
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, w2_dtype=dsw.INT8 if dtype == "int8" else dsw.BF16,
+                        flags=dsw.FLAG_GUMBEL if sampler == "gumbel" else 0)
+    if sampler == "gumbel":
+        walker.set_seed(0x5EED + index)
     plan = walker.query_plan(B)
     tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
     n = base.shape[0]
@@ -264,7 +269,7 @@ def sweep_one(torch, dsw, index, B, gamma, dtype):
     abytes = algorithmic_bytes(V, B, gamma) - V * 256 * 2 + w2_bytes
     stepwise = (gamma * w2_bytes + B * gamma * V * 2) / (HBM_PEAK_GBS * 1e9) * 1e6
     flops = 2.0 * B * 256 * V * gamma
-    out = {"workload": wl.name, "B": B, "gamma": gamma, "w2": dtype, "temps": wl.temps,
+    out = {"workload": wl.name, "B": B, "gamma": gamma, "w2": dtype, "temps": wl.temps, "sampler": sampler,
            "us_per_round": round(us, 2), "launch_us": round(launch, 2),
            "kernel": "batched" if plan.batch_tile == 256 else
                      ("valu" if plan.engine == dsw.ENGINE_VALU else "mfma"),
@@ -430,9 +435,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_sweep:
         result["configs"] = []
-        for (index, b, g, dt) in SWEEP:
-            log(f"sweep: workload {index} B={b} gamma={g} {dt}")
-            r = sweep_one(torch, dsw, index, b, g, dt)
+        for (index, b, g, dt, *smp) in SWEEP:
+            log(f"sweep: workload {index} B={b} gamma={g} {dt} {smp}")
+            r = sweep_one(torch, dsw, index, b, g, dt, *smp)
             log(r)
             result["configs"].append(r)
 

@@ -103,6 +103,23 @@ extern "C" {
                                     Walk on Chip", section "Correctness", Fig. 7)
                                     and of vLLM PR #64442 ("Details").  Applies
                                     to every walk of the handle.              */
+#define DSW_FLAG_GUMBEL 64u      /* sampled requests draw by Gumbel-max instead of
+                                    the inverse CDF: the token is the smallest id
+                                    maximising logit / T - ln(-ln U), one noise
+                                    uniform U per request, step and vocabulary
+                                    row -- the pages' small-batch sampler
+                                    ("Keeping the Draft Walk on Chip", section
+                                    "The idea: make the walk resident").  U of
+                                    row v, request b, step k: Philox-4x32-10 of
+                                    counter (v / 4, 256 k + b, round counter,
+                                    0x47554D42) under the key of dsw_set_seed,
+                                    word v mod 4, as (2 (w >> 9) + 1) 2^-24.
+                                    The uniforms argument is not used.  Needs a
+                                    seed: dsw_walk returns DSW_ERR_ARG until
+                                    dsw_set_seed(h, seed, 1).  Served by the
+                                    all-to-all kernel only: with
+                                    DSW_FLAG_BATCHED or B_max > 16, dsw_create
+                                    returns DSW_ERR_ARG.                       */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */

@@ -37,6 +37,7 @@ FLAG_VALU_GEMV = 4
 FLAG_MFMA_GEMV = 8
 FLAG_BATCHED = 16
 FLAG_SINGLE_ROUND = 32
+FLAG_GUMBEL = 64
 ENGINE_VALU, ENGINE_MFMA = 0, 1
 RANK = 256
 

@@ -13,7 +13,11 @@ LIB = os.path.join(HERE, "libdsw.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b1.hip", "walk_mfma_b4.hip", "walk_mfma_b16.hip", "walk_mfma_i8.hip", "walk_batched.hip"]
+HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b1.hip", "walk_mfma_b4.hip", "walk_mfma_b16.hip", "walk_mfma_i8.hip",
+               "walk_batched.hip",
+               # the all-to-all kernels again, with Gumbel-max sampling
+               "walk_valu_gumbel.hip", "walk_mfma_b1_gumbel.hip", "walk_mfma_b4_gumbel.hip",
+               "walk_mfma_b16_gumbel.hip", "walk_mfma_i8_gumbel.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 # Packed-fp32 VALU forms are kept out of every code object.

@@ -15,16 +15,34 @@ extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles)
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles);
+// the same all-to-all kernels with Gumbel-max sampling
+extern "C" const void* dsw_internal_walk_kernel_gumbel(int reg_slots, int batch_tile, int w2_dtype);
+extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b4_gumbel(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b16_gumbel(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_i8_kernel_gumbel(int batch_tile, int reg_tiles, int max_tiles);
 
 namespace {
-// The compiled kernel a plan runs, or nullptr.
-const void* kernel_for(const dsw_plan_info& pl) {
-    if (pl.engine == DSW_ENGINE_VALU) return dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile, pl.w2_dtype);
-    if (pl.batch_tile == dsw::kMaxBatch) return dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
-    if (pl.w2_dtype == DSW_INT8) return dsw_internal_mfma_i8_kernel(pl.batch_tile, pl.reg_tiles, pl.max_tiles);
-    if (pl.batch_tile == 1) return dsw_internal_mfma_kernel_b1(pl.reg_tiles, pl.max_tiles);
-    if (pl.batch_tile == 4) return dsw_internal_mfma_kernel_b4(pl.reg_tiles, pl.max_tiles);
-    if (pl.batch_tile == 16) return dsw_internal_mfma_kernel_b16(pl.reg_tiles, pl.max_tiles);
+// The compiled kernel a plan runs (with Gumbel-max sampling when `gumbel`), or
+// nullptr.  The planner never gives a Gumbel-max handle the batched kernel.
+const void* kernel_for(const dsw_plan_info& pl, bool gumbel) {
+    if (pl.batch_tile == dsw::kMaxBatch)
+        return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
+    if (pl.engine == DSW_ENGINE_VALU)
+        return gumbel ? dsw_internal_walk_kernel_gumbel(pl.reg_slots, pl.batch_tile, pl.w2_dtype)
+                      : dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile, pl.w2_dtype);
+    if (pl.w2_dtype == DSW_INT8)
+        return gumbel ? dsw_internal_mfma_i8_kernel_gumbel(pl.batch_tile, pl.reg_tiles, pl.max_tiles)
+                      : dsw_internal_mfma_i8_kernel(pl.batch_tile, pl.reg_tiles, pl.max_tiles);
+    if (pl.batch_tile == 1)
+        return gumbel ? dsw_internal_mfma_kernel_b1_gumbel(pl.reg_tiles, pl.max_tiles)
+                      : dsw_internal_mfma_kernel_b1(pl.reg_tiles, pl.max_tiles);
+    if (pl.batch_tile == 4)
+        return gumbel ? dsw_internal_mfma_kernel_b4_gumbel(pl.reg_tiles, pl.max_tiles)
+                      : dsw_internal_mfma_kernel_b4(pl.reg_tiles, pl.max_tiles);
+    if (pl.batch_tile == 16)
+        return gumbel ? dsw_internal_mfma_kernel_b16_gumbel(pl.reg_tiles, pl.max_tiles)
+                      : dsw_internal_mfma_kernel_b16(pl.reg_tiles, pl.max_tiles);
     return nullptr;
 }
 }  // namespace
@@ -175,7 +193,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         const int gm = (i % n_g) == 0 ? gamma_max : 3;
         dsw_plan_info pl;
         int prc = dsw_plan_compute(&dev, V, r, gm, B, w2_dtype, flags, &pl);
-        const void* fn = prc == DSW_OK ? kernel_for(pl) : nullptr;
+        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0) : nullptr;
         hipFuncAttributes attr;
         int per_cu = 0;
         bool ok = fn != nullptr && hipFuncGetAttributes(&attr, fn) == hipSuccess &&
@@ -215,11 +233,12 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     if (h->dtype == DSW_INT8 && w2_scale == nullptr) return DSW_ERR_DTYPE;
     if (B == 0 || gamma == 0) return DSW_OK;
     if (!W1 || !W2 || !base || !anchor || !T || !tokens) return DSW_ERR_NULL;
+    if ((h->flags & DSW_FLAG_GUMBEL) && !h->seeded) return DSW_ERR_ARG;  // the noise needs a seed
 
     dsw_plan_info plan;
     int rc = dsw_plan_compute(&h->dev, h->V, h->r, gamma, B, h->dtype, h->flags, &plan);
     if (rc) return rc;
-    const void* fn = kernel_for(plan);
+    const void* fn = kernel_for(plan, (h->flags & DSW_FLAG_GUMBEL) != 0);
     if (!fn) return DSW_ERR_PLAN;
 
     DeviceGuard g(h->device);

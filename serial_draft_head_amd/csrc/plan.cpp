@@ -37,11 +37,13 @@ static int valu_reg_slot_cap(int batch_tile, bool i8) {
         default: return 1;
     }
 }
+// Gumbel-max kernels of up to 4 requests keep one step's noise per row in LDS.
+static int gumbel_noise_lds(int nb, int rpad, bool gum) { return gum && nb <= 4 ? nb * rpad * 4 : 0; }
 // Upper bound of the VALU kernel's static LDS for a batch tile (int8 rows add
 // their fp32 scales).
-static int valu_static_lds(int nb, bool i8) {
+static int valu_static_lds(int nb, bool i8, bool gum) {
     return nb * ((kRowChunks + 1) * 16 + kMaxSlots * kBlock * 2 + 2 * 4 * kBlock + 144) + 1104 +
-           (i8 ? 4 * kMaxSlots * kBlock : 0) + kTraceLds;
+           (i8 ? 4 * kMaxSlots * kBlock : 0) + kTraceLds + gumbel_noise_lds(nb, kMaxSlots * kBlock, gum);
 }
 static int valu_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 
@@ -57,10 +59,10 @@ static const int kStreamShape[2] = {0, 16};
 static int mfma_tile_for(int B, bool i8) { return (B <= 1 && !i8) ? 1 : (B <= 4 ? 4 : 16); }
 // Upper bound of the MFMA kernel's static LDS for (batch tile, tiles per
 // wave, int8 rows with their fp32 scales).
-static int mfma_static_lds(int nb, int max_tiles, bool i8) {
+static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum) {
     const int rpad = max_tiles * 4 * kTileRows;
     return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0) +
-           kTraceLds;
+           kTraceLds + gumbel_noise_lds(nb, rpad, gum);
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -105,7 +107,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
     const int nb = mfma_tile_for(B, i8);
-    const int lds_static = mfma_static_lds(nb, max_t, i8);
+    const int lds_static = mfma_static_lds(nb, max_t, i8, (flags & DSW_FLAG_GUMBEL) != 0);
     int avail = dev->max_lds_per_block - lds_static;
     if (avail < 0) return DSW_ERR_PLAN;
 
@@ -257,7 +259,7 @@ static int plan_valu(const dsw_devinfo* dev, int B, unsigned flags, int grid, in
     if (flags & DSW_FLAG_FORCE_STREAM) reg_slots = 0;
     const int reg_rows = R < reg_slots * kBlock ? R : reg_slots * kBlock;
 
-    const int lds_static = valu_static_lds(tile, i8);
+    const int lds_static = valu_static_lds(tile, i8, (flags & DSW_FLAG_GUMBEL) != 0);
     int lds_avail = dev->max_lds_per_block - lds_static;
     if (lds_avail < 0) lds_avail = 0;
     int lds_rows = R - reg_rows;
@@ -319,6 +321,9 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
+    // Gumbel-max is the small-batch sampler: the all-to-all kernel, up to 16 requests
+    const bool gumbel = (flags & DSW_FLAG_GUMBEL) != 0;
+    if (batched && gumbel) return DSW_ERR_ARG;
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
     // one bf16 request: the MFMA engine's step is ~1 us shorter, but its shard
     // load ~3 us longer (measured at V = 151,936), so walks of up to 3 steps
@@ -327,7 +332,7 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);
-    } else if (!forced && B >= kBatchedFrom) {
+    } else if (!forced && !gumbel && B >= kBatchedFrom) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);
         if (rc != DSW_OK) {
             memset(out, 0, sizeof(*out));

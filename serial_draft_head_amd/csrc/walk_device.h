@@ -58,21 +58,26 @@ __device__ __forceinline__ float dot8(const uint4 w, const uint4 u, float acc) {
 // multiplied by the round constants; the high halves of the products are mixed
 // with words 3 and 1 and the key, the low halves carried over; the key
 // advances by the Weyl constants between rounds.  Returns output word 0.
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                                 uint32_t k0, uint32_t k1) {
+// All four output words, in place of the counter.
+__device__ __forceinline__ void philox4(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
-        const uint32_t h0 = __umulhi(0xD2511F53u, c0), l0 = 0xD2511F53u * c0;
-        const uint32_t h1 = __umulhi(0xCD9E8D57u, c2), l1 = 0xCD9E8D57u * c2;
-        const uint32_t n0 = h1 ^ c1 ^ k0, n2 = h0 ^ c3 ^ k1;
-        c0 = n0;
-        c1 = l1;
-        c2 = n2;
-        c3 = l0;
+        const uint32_t h0 = __umulhi(0xD2511F53u, c[0]), l0 = 0xD2511F53u * c[0];
+        const uint32_t h1 = __umulhi(0xCD9E8D57u, c[2]), l1 = 0xCD9E8D57u * c[2];
+        const uint32_t n0 = h1 ^ c[1] ^ k0, n2 = h0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = l1;
+        c[2] = n2;
+        c[3] = l0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
-    return c0;
+}
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+    uint32_t c[4] = {c0, c1, c2, c3};
+    philox4(c, k0, k1);
+    return c[0];
 }
 
 // The uniform of request b at step k: supplied by the caller, or drawn on the
@@ -85,6 +90,28 @@ __device__ __forceinline__ float walk_uniform(const WalkParams& p, int b, int k,
     const uint32_t w = philox_word0((uint32_t)k, (uint32_t)b, round, 0x44535721u, (uint32_t)p.seed,
                                     (uint32_t)(p.seed >> 32));
     return (float)(w >> 8) * (1.0f / 16777216.0f);
+}
+
+// Gumbel-max noise ("Keeping the Draft Walk on Chip", section "The idea: make
+// the walk resident": small batches sample by per-row Gumbel-max from Philox
+// noise keyed by seed, row, step and round counter).  Vocabulary rows 4m ..
+// 4m+3 of request b at step k share the call on counter (m, 256 k + b, round,
+// 0x47554D42); word e maps to U = (2 (w >> 9) + 1) 2^-24, strictly inside
+// (0, 1) and exact in fp32.  Returns the variate G = -ln(-ln U).  -ln U is
+// taken as -log1p(U - 1) on [0.5, 1), where U - 1 is exact, so that U close
+// to 1 (the rows with the largest G) keeps its relative precision.
+__device__ __forceinline__ float gumbel_of_word(uint32_t w) {
+    const float U = (float)(2u * (w >> 9) + 1u) * (1.0f / 16777216.0f);
+    const float e = -0.69314718f * __builtin_amdgcn_logf(U);
+    return -0.69314718f * __builtin_amdgcn_logf(e);
+}
+
+// Order-preserving 32-bit image of an fp32 score (-0 maps like +0; every
+// finite score maps above 0, so a zero key never wins).
+__device__ __forceinline__ uint32_t ord32(float s) {
+    uint32_t b = __float_as_uint(s);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 // Selection key (36 bits): order-preserving bits of the bf16 logit, then the

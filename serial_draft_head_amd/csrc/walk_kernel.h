@@ -38,7 +38,12 @@
 // counter, so nothing is cleared between steps, launches or graph replays.
 // Sampling scans shard masses in vocabulary order; the owner shard of u*Z finds
 // the token and publishes it through a token mailbox (vLLM PR #64442,
-// "Details": block masses, then a token inside the block).
+// "Details": block masses, then a token inside the block).  The GUM = 1
+// instantiations sample by Gumbel-max instead (section "The idea: make the
+// walk resident": per-row Gumbel-max for small batches): each workgroup posts
+// its best {l / T + G, ~id} in the two words, and the largest such key across
+// the grid names the token, with no owner hop; up to 4 requests, the noise G
+// of the next step is drawn while the current step's words travel.
 #pragma once
 #include <type_traits>
 
@@ -111,7 +116,9 @@ __device__ __forceinline__ uint4 as_bf16x8(const uint2& q) {
                       bf16_pair(i8_at(q.y, 0), i8_at(q.y, 1)), bf16_pair(i8_at(q.y, 2), i8_at(q.y, 3)));
 }
 
-template <int ENGINE, int A, int M, int NB, int DT = 0>
+// GUM = 1: sampled requests draw by Gumbel-max instead of the inverse CDF (a
+// separate instantiation, so that the default kernels carry none of its code)
+template <int ENGINE, int A, int M, int NB, int DT = 0, int GUM = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
     constexpr bool kI8 = DT == 1;  // int8 rows + fp32 row scales
@@ -138,10 +145,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     __shared__ uint16_t s_base[kMfma && !kOne ? NB * RPAD : 1];
     __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ uint16_t s_logit[NB * RPAD];
+    // Gumbel-max, up to 4 requests: the noise G of the shard's rows for the
+    // coming step, drawn while the previous rendezvous is in flight
+    constexpr bool kPreG = GUM != 0 && NB <= 4;
+    __shared__ float s_G[kPreG ? NB * RPAD : 1];
     __shared__ uint32_t s_wbest[4][NB];
     __shared__ unsigned long long s_red64[4][NB];
     __shared__ float s_redf[4][NB];
-    __shared__ float s_S[NB * kBlock];
+    // shard masses (inverse CDF); Gumbel-max: the waves' best {score, ~id} keys
+    __shared__ __attribute__((aligned(16))) float s_S[NB * kBlock];
     __shared__ int s_own[NB];
     __shared__ float s_pex[NB];
     __shared__ float s_tgt[NB];
@@ -169,6 +181,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     const int gamma = p.gamma;
     const int v0 = c * p.rows_per_wg;
     const uint32_t dbl_round = p.single_round ? 0u : 0xFFFFFFFFu;  // see bias_round
+    constexpr bool gum = GUM != 0;  // sampled requests: Gumbel-max instead of the inverse CDF
     const int nrows = max(0, min(V, v0 + p.rows_per_wg) - v0);
     // register slots beyond the shard load its last row (a cache hit), never
     // another shard's rows (extra HBM reads); an empty shard loads row V - 1
@@ -348,10 +361,34 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     for (int b = 0; b < NB; ++b) any_samp |= (b < B) && (s_T[b] > 0.0f);
     const int CH = (nrows + kBlock - 1) / kBlock;  // rows per thread in vocabulary-order scans
 
+    // Gumbel-max noise of step kk for every sampled request: rows in aligned
+    // groups of four ids, one Philox call per group (see gumbel_of_word)
+    const int m0 = v0 >> 2;
+    const int ng = nrows > 0 ? ((v0 + nrows - 1) >> 2) - m0 + 1 : 0;
+    auto draw_noise = [&](int kk) {
+#pragma unroll 1
+        for (int b = 0; b < B; ++b) {
+            if (!(s_T[b] > 0.0f)) continue;
+#pragma unroll 1
+            for (int gi = t; gi < ng; gi += kBlock) {
+                uint32_t w[4] = {(uint32_t)(m0 + gi), ((uint32_t)kk << 8) | (uint32_t)b, round, 0x47554D42u};
+                philox4(w, (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * (m0 + gi) + e - v0;
+                    if (r >= 0 && r < nrows) s_G[b * RPAD + r] = gumbel_of_word(w[e]);
+                }
+            }
+        }
+    };
+    if constexpr (kPreG) {
+        if (any_samp && gamma > 0) draw_noise(0);  // read after the first step's barriers
+    }
+
     // token of request b at the end of the current step (after the winner
     // reduction and, for sampled requests, the owner's publication)
 #define DSW_TOKEN(b)                                                                             \
-    ((s_T[b] > 0.0f)                                                                             \
+    ((s_T[b] > 0.0f && !gum)                                                                     \
          ? s_prev[b]                                                                             \
          : checked_token(key_index(max(max(s_red64[0][b], s_red64[1][b]),                        \
                                        max(s_red64[2][b], s_red64[3][b]))),                      \
@@ -645,9 +682,49 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         __syncthreads();
         DSW_TRACE(k, kTrReduced);
 
+        // Gumbel-max (sampled requests): the shard's best key {ord32(l / T + G),
+        // ~id}, rows in aligned groups of four ids, one Philox call per group
+        unsigned long long* s_gk = reinterpret_cast<unsigned long long*>(s_S);  // [4][NB]
+        if (any_samp && gum) {
+#pragma unroll 1
+            for (int b = 0; b < B; ++b) {
+                if (!(s_T[b] > 0.0f)) continue;
+                const float invT = 1.0f / s_T[b];
+                unsigned long long bk = 0ull;
+                if constexpr (kPreG) {  // the noise is already in LDS
+#pragma unroll 1
+                    for (int r = t; r < nrows; r += kBlock) {
+                        const float sc = bf16_to_f32(s_logit[b * RPAD + r]) * invT + s_G[b * RPAD + r];
+                        const unsigned long long key = ((unsigned long long)ord32(sc) << kIdxBits) |
+                                                       (unsigned long long)(kIdxMask - (uint32_t)(v0 + r));
+                        bk = key > bk ? key : bk;
+                    }
+                }
+#pragma unroll 1
+                for (int gi = t; gi < (kPreG ? 0 : ng); gi += kBlock) {
+                    uint32_t w[4] = {(uint32_t)(m0 + gi), ((uint32_t)k << 8) | (uint32_t)b, round, 0x47554D42u};
+                    philox4(w, (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 4 * (m0 + gi) + e;
+                        const int r = v - v0;
+                        if (r >= 0 && r < nrows) {
+                            const float sc = bf16_to_f32(s_logit[b * RPAD + r]) * invT + gumbel_of_word(w[e]);
+                            const unsigned long long key =
+                                ((unsigned long long)ord32(sc) << kIdxBits) | (unsigned long long)(kIdxMask - (uint32_t)v);
+                            bk = key > bk ? key : bk;
+                        }
+                    }
+                }
+                bk = wave_max_u64_dpp(bk);
+                if (lane == 0) s_gk[wave * NB + b] = bk;
+            }
+            __syncthreads();
+        }
+
         // sampled requests: masses w = exp((l - m_c) / T) of the shard's rows in
         // vocabulary order, CH consecutive rows per thread
-        if (any_samp) {
+        if (any_samp && !gum) {
             float part[NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -692,10 +769,18 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         if (wave == 0 && lane < B) {
             const uint32_t lk = max(max(s_wbest[0][lane], s_wbest[1][lane]), max(s_wbest[2][lane], s_wbest[3][lane]));
             unsigned long long* box = mail_q + (size_t)c * kMailWords;
-            st_agent64(&box[lane], (global_key(lk, v0) << 28) | epoch);
-            if (s_T[lane] > 0.0f)
-                st_agent64(&box[kMaxBatchPersistent + lane],
-                           ((unsigned long long)__float_as_uint(s_tot[lane]) << 32) | epoch);
+            if (gum && s_T[lane] > 0.0f) {
+                // Gumbel-max: {score, epoch} and {~id, epoch}
+                const unsigned long long gk = max(max(s_gk[lane], s_gk[NB + lane]),
+                                                  max(s_gk[2 * NB + lane], s_gk[3 * NB + lane]));
+                st_agent64(&box[lane], ((gk >> kIdxBits) << 32) | epoch);
+                st_agent64(&box[kMaxBatchPersistent + lane], ((gk & kIdxMask) << 32) | epoch);
+            } else {
+                st_agent64(&box[lane], (global_key(lk, v0) << 28) | epoch);
+                if (s_T[lane] > 0.0f)
+                    st_agent64(&box[kMaxBatchPersistent + lane],
+                               ((unsigned long long)__float_as_uint(s_tot[lane]) << 32) | epoch);
+            }
         }
         DSW_TRACE(k, kTrPosted);
         // the previous step's tokens, stored while this step's rendezvous is in
@@ -707,12 +792,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 for (int r = t; r < nrows; r += kBlock) dst[r] = s_logit[b * RPAD + r];
             }
         }
+        if constexpr (kPreG) {
+            // the next step's noise, while this step's words travel (this
+            // step's noise was last read before the barrier ahead of the post)
+            if (any_samp && k + 1 < gamma) draw_noise(k + 1);
+        }
         unsigned long long kw[NB];
-        float sw[NB];
+        uint32_t sw[NB];  // the second word's payload: exp-sum bits, or ~id (Gumbel-max)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             kw[b] = 0ull;
-            sw[b] = 0.0f;
+            sw[b] = 0u;
         }
         if (t < G) {
             // Up to 4 requests: two polls in flight, each check waiting only for
@@ -735,7 +825,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             if ((w[b][0] & kEpochMod) == epoch) kw[b] = w[b][0] >> 28;                     \
             else ready = false;                                                            \
             if (s_T[b] > 0.0f) {                                                           \
-                if ((w[b][1] & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(w[b][1] >> 32)); \
+                if ((w[b][1] & kEpochMod) == epoch) sw[b] = (uint32_t)(w[b][1] >> 32);          \
                 else ready = false;                                                        \
             }                                                                              \
         }                                                                                  \
@@ -763,7 +853,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                             else ready = false;
                             if (s_T[b] > 0.0f) {
                                 const unsigned long long ws = ld_agent64(&box[kMaxBatchPersistent + b]);
-                                if ((ws & kEpochMod) == epoch) sw[b] = __uint_as_float((uint32_t)(ws >> 32));
+                                if ((ws & kEpochMod) == epoch) sw[b] = (uint32_t)(ws >> 32);
                                 else ready = false;
                             }
                         }
@@ -785,6 +875,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #undef DSW_READY
         }
         DSW_TRACE(k, kTrArrived);
+        if (any_samp && gum) {
+            // Gumbel-max keys {score (32), ~id (20)}: ~id is decoded like a greedy key's
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if ((NB == 1 || b < B) && s_T[b] > 0.0f) kw[b] = ((kw[b] >> 4) << kIdxBits) | sw[b];
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const unsigned long long m = wave_max_u64_dpp(kw[b]);
@@ -796,7 +892,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         // ---- sampled requests: owner shard of u*Z ------------------------
         // Every workgroup derives the same owner from the same mailbox words
         // with the same code, so they agree without another exchange.
-        if (any_samp) {
+        if (any_samp && !gum) {
             // shard masses S_c = s_c * exp((m_c - M) / T), one request per row of s_S
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
@@ -804,7 +900,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     const unsigned long long win =
                         max(max(s_red64[0][b], s_red64[1][b]), max(s_red64[2][b], s_red64[3][b]));
                     float S = 0.0f;
-                    if (t < G && kw[b] != 0ull) S = sw[b] * __expf((key_logit(kw[b]) - key_logit(win)) / s_T[b]);
+                    if (t < G && kw[b] != 0ull) S = __uint_as_float(sw[b]) * __expf((key_logit(kw[b]) - key_logit(win)) / s_T[b]);
                     s_S[b * kBlock + t] = S;
                 }
             }

@@ -100,7 +100,7 @@ struct WalkParams {
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
     int single_round;        // 1: logit = bf16(base + fp32 dot), rounded once
     int seeded;              // 1: uniforms == NULL draws them on the device from seed
-    unsigned long long seed; // key of the device-drawn uniforms
+    unsigned long long seed; // key of the device-drawn uniforms and of the Gumbel noise
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };
 

@@ -19,6 +19,14 @@ order):
   * sampled tokens: from the GPU's own logits in binary64, C_{t-1} - d <= u Z < C_t + d
     with d = 1e-5 Z, and the token equals the oracle's draw on those logits
     wherever u Z is farther than d from every boundary.
+  * Gumbel-max tokens (flag DSW_FLAG_GUMBEL): with the binary64 scores
+    S_v = l_v / T - ln(-ln U_v) of the GPU's own logits and the oracle's noise,
+    S_tok >= max S - d with d = 1e-4, and the token equals the oracle's
+    argmax wherever the top two scores are more than 2 d apart.  d covers the
+    GPU's fp32 score: l * fp32(1/T) (2 roundings of a value below 2^6), two
+    fp32 logarithms of relative error ~2^-23 (-ln U near 1 is taken with
+    log1p, so its relative error stays small), and the final sum; together
+    well under 1e-5 for |S| < 64.
 Step k uses prev = the GPU's token k-1 (teacher forcing), so every step is
 judged on its own.
 
@@ -35,6 +43,7 @@ import oracle
 R = 256
 GAMMA_R = R * 2.0 ** -24 / (1 - R * 2.0 ** -24)
 SAMPLE_TOL = 1e-5
+GUMBEL_TOL = 1e-4
 
 
 def bf16_ulp(x):
@@ -56,11 +65,14 @@ class Weights:
 
 
 def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, steps=None,
-                single_round=False):
-    """Assert the parity rules for one round; return a small report dict."""
+                single_round=False, gumbel=None):
+    """Assert the parity rules for one round; return a small report dict.
+    gumbel: (seed, round counter) of a Gumbel-max walk, else None."""
     B, gamma, V = base.shape
+    g_seed, g_round = gumbel if gumbel is not None else (0, 0)
     or_tok, or_lg = oracle.walk(w.W1_bits, base, anchor, T, uniforms, W2_bits=w.W2_bits, Q=w.Q,
-                                scale=w.scale, forced=gpu_tokens, single_round=single_round)
+                                scale=w.scale, forced=gpu_tokens, single_round=single_round,
+                                gumbel=gumbel is not None, seed=g_seed, round_counter=g_round)
     rep = {"steps": 0, "exact_logits": 0, "logits": 0, "near_ties": 0, "token_match": 0,
            "sampled": 0, "sampled_exact_checked": 0}
     for b in range(B):
@@ -113,6 +125,16 @@ def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, s
                     rep["near_ties"] += 1
                     assert o[tok] >= omax - 2 * bf16_ulp(omax)
                     rep["token_match"] += int(tok == int(or_tok[b, k]))
+            elif gumbel is not None:
+                rep["sampled"] += 1
+                S = oracle.gumbel_scores(gpu_logits[b, k], T[b], g_seed, g_round, b, k)
+                top = int(np.argmax(S))
+                assert S[tok] >= S[top] - GUMBEL_TOL, \
+                    f"b={b} k={k}: Gumbel-max token {tok} scores {S[tok]}, best {top} scores {S[top]}"
+                second = np.delete(S, top).max() if V > 1 else -np.inf
+                if S[top] - second > 2 * GUMBEL_TOL:
+                    assert tok == top, f"b={b} k={k}: Gumbel-max token {tok} vs oracle {top}"
+                    rep["sampled_exact_checked"] += 1
             else:
                 rep["sampled"] += 1
                 Tb = float(np.float32(T[b]))

@@ -334,6 +334,76 @@ def test_device_uniforms(dsw, V, B, gamma, flags):
     walker.close()
 
 
+# Gumbel-max sampling (DSW_FLAG_GUMBEL): every all-to-all kernel family, ragged
+# and full sizes; the oracle draws the same Philox noise from (seed, round counter)
+GUMBEL_CASES = [  # (V, B, gamma, flags, w2 dtype)
+    (32_000, 1, 6, 0, "bf16"),        # one-request MFMA engine
+    (60_001, 1, 3, 0, "bf16"),        # short walk: VALU engine, ragged vocabulary
+    (4_097, 3, 5, 0, "bf16"),         # MFMA, batch tile 4, ragged
+    (151_936, 1, 7, 0, "bf16"),       # the headline shape
+    (248_320, 1, 4, 0, "bf16"),       # 12 register + 4 LDS tiles per wave
+    (151_936, 16, 3, 0, "bf16"),      # MFMA, batch tile 16 (no batched kernel with the flag)
+    (60_000, 4, 4, 4, "bf16"),        # VALU, batch tile 4
+    (129_280, 1, 4, 0, "int8"),       # int8 rows, VALU
+    (60_000, 4, 3, 0, "int8"),        # int8 rows, MFMA
+]
+
+
+@pytest.mark.parametrize("V,B,gamma,flags,dt", GUMBEL_CASES)
+def test_gumbel_max(dsw, V, B, gamma, flags, dt):
+    say(f"gumbel-max V={V} B={B} gamma={gamma} flags={flags} {dt}")
+    W1, W2 = workloads.weights(2, V=V)
+    W1d = bf16_dev(W1)
+    if dt == "int8":
+        Q, sc = workloads.quantize_int8(W2)
+        w = parity.Weights(W1, Q=Q, scale=sc)
+        W2d, sd = int8_dev(Q, sc)
+    else:
+        w = parity.Weights(W1, W2)
+        W2d, sd = bf16_dev(W2), None
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, flags=flags | dsw.FLAG_GUMBEL,
+                        w2_dtype=dsw.INT8 if dt == "int8" else dsw.BF16)
+    say("plan", walker.query_plan(B).as_dict())
+    seed = 0x6A6B_0000_0000 + V + B
+    walker.set_seed(seed)
+    checked = 0
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 40 + rnd, B=B, gamma=gamma, V=V, temps="mixed")
+        if B == 1:
+            inp["T"][:] = (1.0, 0.6)[rnd]
+        ctr = walker.round_counter()
+        base, anchor, T, uni = round_dev(inp)
+        # the uniforms argument is not used by Gumbel-max
+        tokens, logits = walker.walk(W1d, W2d, base, anchor, T, uni if rnd else None, w2_scale=sd,
+                                     want_logits=True)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], None, toks, lg,
+                                 gumbel=(seed, ctr))
+        say(rnd, "round counter", ctr, rep)
+        checked += rep["sampled_exact_checked"]
+        assert walker.round_counter() == ctr + 1
+    assert checked > 0
+    walker.close()
+
+
+def test_gumbel_max_needs_a_seed_and_a_small_batch(dsw):
+    V = 4_096
+    W1, W2 = workloads.weights(2, V=V)
+    walker = dsw.Walker(V, gamma_max=3, B_max=2, flags=dsw.FLAG_GUMBEL)
+    inp = workloads.round_inputs(2, 1, B=2, gamma=3, V=V, temps="mixed")
+    base, anchor, T, _ = round_dev(inp)
+    with pytest.raises(dsw.DswError) as e:   # no seed yet
+        walker.walk(bf16_dev(W1), bf16_dev(W2), base, anchor, T, None)
+    assert e.value.code == -11
+    walker.close()
+    with pytest.raises(dsw.DswError) as e:   # beyond 16 requests the batched kernel has no Gumbel-max
+        dsw.Walker(V, gamma_max=3, B_max=17, flags=dsw.FLAG_GUMBEL)
+    assert e.value.code == -11
+
+
 # int8 rows + fp32 row scales: one vocabulary per compiled int8 shape, plus
 # ragged sizes; the harness quantizes once and both sides consume (q, scale).
 I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),
