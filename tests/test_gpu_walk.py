@@ -404,6 +404,60 @@ def test_gumbel_max_needs_a_seed_and_a_small_batch(dsw):
     assert e.value.code == -11
 
 
+# HIP graph replays: nothing is cleared between replays (epochs come from the
+# device round counter) and device-drawn noise is keyed by that counter, so
+# each replay must be a correct walk with fresh noise.  Eager copies and
+# synchronisations run between the replays.
+@pytest.mark.parametrize("B,flags,temps", [(1, 0, "cycle"), (3, 64, "mixed"), (20, 0, "mixed")])
+def test_graph_replays_are_fresh_walks(dsw, B, flags, temps):
+    import oracle
+    say(f"graph replays B={B} flags={flags} {temps}")
+    V, gamma = 32_000, 4
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, flags=flags)
+    seed = 0xC0FFEE + B
+    walker.set_seed(seed)
+    inp = workloads.round_inputs(2, 300, B=B, gamma=gamma, V=V, temps=temps)
+    base, anchor, T, _ = round_dev(inp)  # the graph's static inputs
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=DEV)
+    logits = torch.empty((B, gamma, V), dtype=torch.bfloat16, device=DEV)
+    walker.walk(W1d, W2d, base, anchor, T, None, tokens=tokens, logits=logits)  # eager warm-up
+    torch.cuda.synchronize()
+    assert walker.status() == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        walker.walk(W1d, W2d, base, anchor, T, None, tokens=tokens, logits=logits)
+    torch.cuda.synchronize()
+    seen = []
+    for r in range(4):
+        inp = workloads.round_inputs(2, 301 + r, B=B, gamma=gamma, V=V, temps=temps)
+        nb, na, nt, _ = round_dev(inp)
+        base.copy_(nb)
+        anchor.copy_(na)
+        T.copy_(nt)
+        torch.cuda.synchronize()
+        ctr = walker.round_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        if flags & dsw.FLAG_GUMBEL:
+            rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], None, toks, lg,
+                                     gumbel=(seed, ctr))
+        else:
+            uni = oracle.device_uniforms(seed, ctr, B, gamma)
+            rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], uni, toks, lg)
+        say(r, "round counter", ctr, rep)
+        assert walker.round_counter() == ctr + 1
+        seen.append(ctr)
+    assert len(set(seen)) == 4
+    del g
+    walker.close()
+
+
 # int8 rows + fp32 row scales: one vocabulary per compiled int8 shape, plus
 # ragged sizes; the harness quantizes once and both sides consume (q, scale).
 I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),
