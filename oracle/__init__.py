@@ -16,7 +16,9 @@ What it computes (see the header of walk_oracle.c for the passages followed):
 ``softmax(logit / T)``, ``prev = tok``; the sampler is the inverse CDF of
 vLLM PR #64442, section "Details", or (the ``gumbel`` mode) Gumbel-max from
 counter-based noise, the pages' small-batch sampler (section "The idea: make
-the walk resident").
+the walk resident").  ``walk_gru`` is the GRU serial head (section "Beyond
+DSpark: other serial heads"): the state goes through a standard GRU cell fed
+with ``W1[prev]`` and the vocabulary matrix reads ``bf16(h)``.
 """
 from __future__ import annotations
 
@@ -71,6 +73,10 @@ def _load():
     lib.oracle_gumbel_scores.argtypes = [i, P, f, ctypes.c_uint64, ctypes.c_uint32, i, i, P]
     lib.oracle_gumbel_from_uniforms.restype = i
     lib.oracle_gumbel_from_uniforms.argtypes = [i, P, ctypes.c_double, P]
+    lib.oracle_gru_cell.restype = None
+    lib.oracle_gru_cell.argtypes = [i, P, P, P, P, P, P, P]
+    lib.oracle_walk_gru.restype = i
+    lib.oracle_walk_gru.argtypes = [i, i, i, i] + [P] * 18 + [i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_threads.restype = i
     lib.oracle_philox4x32_10.argtypes = [P, P, P]
     lib.oracle_philox4x32_10.restype = None
@@ -218,3 +224,49 @@ def gumbel_from_uniforms(logits, T, U) -> int:
     if tok < 0:
         raise RuntimeError(f"oracle_gumbel_from_uniforms failed with {tok}")
     return tok
+
+
+def gru_cell(x, h, Wih_bits, Whh_bits, bih, bhh):
+    """One GRU cell in binary64: x, h [r] -> h' [r]; Wih, Whh [3r, r] bf16 bits
+    (gates r, z, n), bih, bhh [3r] f32."""
+    x = _c(x, np.float64)
+    h = _c(h, np.float64)
+    r = x.shape[0]
+    Wih_bits, Whh_bits = _c(Wih_bits, np.uint16), _c(Whh_bits, np.uint16)
+    bih, bhh = _c(bih, np.float32), _c(bhh, np.float32)
+    assert Wih_bits.shape == (3 * r, r) and Whh_bits.shape == (3 * r, r) and h.shape == (r,)
+    out = np.empty(r, dtype=np.float64)
+    _load().oracle_gru_cell(r, _ptr(x), _ptr(h), _ptr(Wih_bits), _ptr(Whh_bits), _ptr(bih), _ptr(bhh),
+                            _ptr(out))
+    return out
+
+
+def walk_gru(W1_bits, base_bits, anchor, T, cell, h0, uniforms=None, W2_bits=None, Q=None, scale=None,
+             forced=None, forced_h=None, want_logits=True, single_round=False, gumbel=False, seed=0,
+             round_counter=0):
+    """The GRU head's walk.  cell = (Wih [3r,r] u16, Whh [3r,r] u16, bih [3r] f32, bhh [3r] f32);
+    h0 [B,r] f32; forced_h [B,gamma,r] f32 or None (teacher forcing of the state).
+    Returns (tokens [B,gamma] i32, logits [B,gamma,V] u16 or None, states [B,gamma,r] f64)."""
+    W1_bits = _c(W1_bits, np.uint16)
+    W2_bits, Q, scale = _c(W2_bits, np.uint16), _c(Q, np.int8), _c(scale, np.float32)
+    Wih, Whh, bih, bhh = _c(cell[0], np.uint16), _c(cell[1], np.uint16), _c(cell[2], np.float32), \
+        _c(cell[3], np.float32)
+    h0 = _c(h0, np.float32)
+    base_bits = _c(base_bits, np.uint16)
+    anchor, T = _c(anchor, np.int32), _c(T, np.float32)
+    uniforms, forced, forced_h = _c(uniforms, np.float32), _c(forced, np.int32), _c(forced_h, np.float32)
+    V, r = W1_bits.shape
+    B, gamma = base_bits.shape[0], base_bits.shape[1]
+    assert base_bits.shape[2] == V and h0.shape == (B, r)
+    tokens = np.empty((B, gamma), dtype=np.int32)
+    logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
+    states = np.empty((B, gamma, r), dtype=np.float64)
+    mode = (SINGLE_ROUND if single_round else 0) | (GUMBEL if gumbel else 0)
+    rc = _load().oracle_walk_gru(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+                                 _ptr(Wih), _ptr(Whh), _ptr(bih), _ptr(bhh), _ptr(h0), _ptr(base_bits),
+                                 _ptr(anchor), _ptr(T), _ptr(uniforms), _ptr(forced), _ptr(forced_h),
+                                 _ptr(tokens), _ptr(logits), _ptr(states), mode,
+                                 int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF)
+    if rc != 0:
+        raise RuntimeError(f"oracle_walk_gru failed with {rc}")
+    return tokens, logits, states

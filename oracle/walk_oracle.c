@@ -40,6 +40,21 @@
  *            logits is an exact draw from softmax(logit / T)).
  *   prev     = tok for the next step.
  *
+ * GRU head (oracle_gru_cell, oracle_walk_gru): a serial head whose state is
+ * updated by a gated recurrent cell ("Keeping the Draft Walk on Chip",
+ * section "Beyond DSpark: other serial heads": DeLS-Spec corrects its block
+ * with a GRU, and every such head ends in the same vocabulary-wide matrix).
+ * The cell is the standard GRU (Cho et al. 2014, "Learning Phrase
+ * Representations using RNN Encoder-Decoder"), in the common form where the
+ * reset gate scales the recurrent term after its matrix product; gates in the
+ * order (r, z, n):
+ *   r = sigmoid(Wir x + bir + Whr h + bhr)
+ *   z = sigmoid(Wiz x + biz + Whz h + bhz)
+ *   n = tanh(Win x + bin + r * (Whn h + bhn))
+ *   h' = (1 - z) * n + z * h
+ * with x = W1[prev] (the previous token's row of the rank-r table) and the
+ * vocabulary matrix applied to u = bf16(h'):  logit = bf16(base + bf16(W2 u)).
+ *
  * Parallelism: OpenMP over vocabulary rows inside one GEMV.  Each row's sum
  * is formed by one thread in a fixed order, so results do not depend on the
  * thread count.
@@ -401,4 +416,89 @@ int oracle_gumbel_from_uniforms(int V, const double* logit, double T, const doub
     const int best = first_argmax(sc, V);
     free(sc);
     return best;
+}
+
+/*
+ * One GRU cell in binary64 (see the header).  x, h: r values; Wih, Whh:
+ * [3r][r] bf16 bits, gate blocks (r, z, n); bih, bhh: [3r] f32; out: r values.
+ */
+void oracle_gru_cell(int r, const double* x, const double* h, const uint16_t* Wih, const uint16_t* Whh,
+                     const float* bih, const float* bhh, double* out) {
+    for (int j = 0; j < r; ++j) {
+        double gi[3], gh[3];
+        for (int g = 0; g < 3; ++g) {
+            const int row = g * r + j;
+            double si = 0.0, sh = 0.0;
+            for (int i = 0; i < r; ++i) {
+                si += bf16_value(Wih[(size_t)row * r + i]) * x[i];
+                sh += bf16_value(Whh[(size_t)row * r + i]) * h[i];
+            }
+            gi[g] = si + (double)bih[row];
+            gh[g] = sh + (double)bhh[row];
+        }
+        const double rg = 1.0 / (1.0 + exp(-(gi[0] + gh[0])));
+        const double zg = 1.0 / (1.0 + exp(-(gi[1] + gh[1])));
+        const double ng = tanh(gi[2] + rg * gh[2]);
+        out[j] = (1.0 - zg) * ng + zg * h[j];
+    }
+}
+
+/*
+ * The GRU head's walk for B independent requests (free running, or teacher
+ * forced).  Arguments as oracle_walk_ex, plus
+ *   Wih, Whh, bih, bhh : the cell (see oracle_gru_cell)
+ *   h0       : [B][r] initial states (f32)
+ *   forced_h : [B][gamma][r] f32 or NULL.  When given, step k > 0 of request b
+ *              starts from forced_h[b][k-1] instead of the oracle's own state.
+ *   states   : [B][gamma][r] out, the states h_k in binary64 (may be NULL)
+ * The GEMV operand of step k is bf16(h_k), rounded from binary64.
+ */
+int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
+                    const uint16_t* W2, const int8_t* Q, const float* scale,
+                    const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
+                    const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
+                    const float* uniforms, const int32_t* forced, const float* forced_h,
+                    int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
+                    uint32_t round) {
+    if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !Wih || !Whh || !bih || !bhh || !h0 || !base ||
+        !anchor || !T || !tokens || (!W2 && (!Q || !scale)))
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        if (T[b] != 0.0f && !uniforms && !(mode & ORACLE_GUMBEL)) return -1;
+        if (anchor[b] < 0 || anchor[b] >= V) return -1;
+    }
+    double* lg = (double*)malloc(sizeof(double) * (size_t)V);
+    double* x = (double*)malloc(sizeof(double) * (size_t)r);
+    double* h = (double*)malloc(sizeof(double) * (size_t)r);
+    double* hn = (double*)malloc(sizeof(double) * (size_t)r);
+    uint16_t* ub = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)r);
+    int rc = 0;
+    if (!lg || !x || !h || !hn || !ub) rc = -3;
+    for (int b = 0; b < B && rc == 0; ++b) {
+        int prev = anchor[b];
+        for (int i = 0; i < r; ++i) h[i] = (double)h0[(size_t)b * r + i];
+        for (int k = 0; k < gamma && rc == 0; ++k) {
+            if (forced && k > 0) prev = forced[(size_t)b * gamma + (k - 1)];
+            if (forced_h && k > 0)
+                for (int i = 0; i < r; ++i) h[i] = (double)forced_h[((size_t)b * gamma + (k - 1)) * r + i];
+            if (prev < 0 || prev >= V) { rc = -1; break; }
+            for (int i = 0; i < r; ++i) x[i] = bf16_value(W1[(size_t)prev * r + i]);
+            oracle_gru_cell(r, x, h, Wih, Whh, bih, bhh, hn);
+            for (int i = 0; i < r; ++i) {
+                h[i] = hn[i];
+                ub[i] = oracle_bf16_bits(oracle_rne_bf16(hn[i]));
+                if (states) states[((size_t)b * gamma + k) * r + i] = hn[i];
+            }
+            const uint16_t* base_k = base + ((size_t)b * gamma + k) * (size_t)V;
+            uint16_t* out = logits ? logits + ((size_t)b * gamma + k) * (size_t)V : NULL;
+            float uni = uniforms ? uniforms[(size_t)b * gamma + k] : 0.0f;
+            int tok = oracle_step_impl(V, r, ub, W2, Q, scale, base_k, T[b], uni, out, lg, mode, seed, round,
+                                       b, k);
+            if (tok < 0) { rc = tok; break; }
+            tokens[(size_t)b * gamma + k] = tok;
+            prev = tok;
+        }
+    }
+    free(lg); free(x); free(h); free(hn); free(ub);
+    return rc;
 }

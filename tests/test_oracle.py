@@ -244,6 +244,98 @@ def test_gumbel_walk_uses_its_own_request_step_and_round(oracle_mod):
     assert not np.array_equal(t2[[0, 2]], toks[[0, 2]])
 
 
+# ------------------------------------------------------------ GRU serial head
+def test_hand_worked_gru(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_gru_r1.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        r = c["r"]
+        Wih = bits_of(np.asarray(c["Wih"], dtype=np.float64).ravel()).reshape(3 * r, r)
+        Whh = bits_of(np.asarray(c["Whh"], dtype=np.float64).ravel()).reshape(3 * r, r)
+        out = oracle_mod.gru_cell(c["x"], c["h"], Wih, Whh, c["bih"], c["bhh"])
+        assert np.allclose(out, c["out"], rtol=0, atol=1e-14), (c, out)
+
+
+def _torch_gru(r, x, h, Wih, Whh, bih, bhh):
+    import torch
+    cell = torch.nn.GRUCell(r, r).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(value_f64(Wih)))
+        cell.weight_hh.copy_(torch.from_numpy(value_f64(Whh)))
+        cell.bias_ih.copy_(torch.from_numpy(np.asarray(bih, np.float64)))
+        cell.bias_hh.copy_(torch.from_numpy(np.asarray(bhh, np.float64)))
+        return cell(torch.from_numpy(np.asarray(x, np.float64))[None],
+                    torch.from_numpy(np.asarray(h, np.float64))[None])[0].numpy()
+
+
+def value_f64(bits):
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("r", [1, 8, 256])
+def test_gru_cell_matches_torch_grucell(oracle_mod, r):
+    # torch.nn.GRUCell in float64 is an independent implementation of the same cell
+    Wih, Whh, bih, bhh = workloads.gru_cell_weights(r, r=r)
+    rng = np.random.default_rng(r)
+    for _ in range(5):
+        x = value_f64(workloads.to_bf16_bits(rng.standard_normal(r)))
+        h = np.tanh(rng.standard_normal(r))
+        want = _torch_gru(r, x, h, Wih, Whh, bih, bhh)
+        got = oracle_mod.gru_cell(x, h, Wih, Whh, bih, bhh)
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_gru_walk_brute_force(oracle_mod, seed):
+    # V = 12, r = 4: states from torch's GRUCell, the operand bf16(h) by the exact
+    # bit-pattern search, the logits as exact rationals
+    V, r, gamma, B = 12, 4, 3, 3
+    d = workloads.toy(seed + 800, V=V, r=r, B=B, gamma=gamma, w2_std=0.5, base_std=0.5)
+    cell = workloads.gru_cell_weights(seed, r=r)
+    h0 = workloads.gru_h0(seed, 0, B, r=r)
+    T = np.zeros(B, np.float32)
+    toks, logits, states = oracle_mod.walk_gru(d["W1"], d["base"], d["anchor"], T, cell, h0, W2_bits=d["W2"])
+    for b in range(B):
+        prev, h = int(d["anchor"][b]), h0[b].astype(np.float64)
+        for k in range(gamma):
+            x = value_f64(d["W1"][prev])
+            h = _torch_gru(r, x, h, *cell)
+            assert np.allclose(states[b, k], h, rtol=0, atol=1e-13)
+            u = [value(rne_bits(Fraction(float(v)))) for v in states[b, k]]
+            lb = bf.step_logits(d["W2"], u, d["base"][b, k])
+            assert logits[b, k].tolist() == lb
+            assert toks[b, k] == bf.argmax_lowest(lb)
+            prev = int(toks[b, k])
+
+
+def test_gru_walk_teacher_forcing_and_zero_cell(oracle_mod):
+    V, r = 2000, 256
+    W1, W2 = workloads.weights(0, V=V)
+    inp = workloads.round_inputs(1, 4, B=2, gamma=5, V=V, temps="mixed")
+    cell = workloads.gru_cell_weights(0)
+    h0 = workloads.gru_h0(0, 4, 2)
+    t0, l0, s0 = oracle_mod.walk_gru(W1, inp["base"], inp["anchor"], inp["T"], cell, h0,
+                                     uniforms=inp["uniforms"], W2_bits=W2)
+    # forcing the oracle's own tokens and (f32-exact) states reproduces the walk
+    s32 = s0.astype(np.float32)
+    t1, l1, s1 = oracle_mod.walk_gru(W1, inp["base"], inp["anchor"], inp["T"], cell, h0,
+                                     uniforms=inp["uniforms"], W2_bits=W2, forced=t0, forced_h=s32)
+    assert np.array_equal(t0[:, 0], t1[:, 0]) and np.array_equal(l0[:, 0], l1[:, 0])
+    # each step is the plain walk's step with the operand bf16(h_k)
+    for b in range(2):
+        for k in range(5):
+            ub = oracle_mod.rne_bf16(s0[b, k])[1]
+            tok, lg = oracle_mod.step(ub, inp["base"][b, k], inp["T"][b], inp["uniforms"][b, k], W2_bits=W2)
+            assert np.array_equal(lg, l0[b, k]) and tok == t0[b, k]
+    # a zero cell halves the state every step: h_k = h0 / 2^(k+1)
+    z = (np.zeros((3 * r, r), np.uint16), np.zeros((3 * r, r), np.uint16), np.zeros(3 * r, np.float32),
+         np.zeros(3 * r, np.float32))
+    _, _, sz = oracle_mod.walk_gru(W1, inp["base"], inp["anchor"], [0.0, 0.0], z, h0, W2_bits=W2)
+    for k in range(5):
+        assert np.array_equal(sz[:, k], h0.astype(np.float64) / 2.0 ** (k + 1))
+
+
 def test_hand_worked_sampler(oracle_mod):
     with open(os.path.join(GOLDEN, "hand_sampler.json")) as f:
         g = json.load(f)

@@ -120,3 +120,22 @@ def toy(seed: int, V: int = 12, r: int = 4, B: int = 1, gamma: int = 3, w2_std: 
     T = temperatures(rng, B, temps, seed)
     uniforms = rng.random((B, gamma), dtype=np.float32)
     return {"W1": W1, "W2": W2, "base": base, "anchor": anchor, "T": T, "uniforms": uniforms}
+
+
+def gru_cell_weights(index: int, r: int = R):
+    """Synthetic GRU cell for the GRU serial head (the pages measure such heads on
+    synthetic weights): Wih, Whh [3r, r] bf16 bits and bih, bhh [3r] f32, all
+    N(0, 1/r), the scale of the usual uniform(-1/sqrt(r), 1/sqrt(r)) init."""
+    rng = np.random.Generator(np.random.PCG64(7_000 + index))
+    sd = 1.0 / np.sqrt(r)
+    Wih = to_bf16_bits(sd * rng.standard_normal((3 * r, r), dtype=np.float32))
+    Whh = to_bf16_bits(sd * rng.standard_normal((3 * r, r), dtype=np.float32))
+    bih = (sd * rng.standard_normal(3 * r)).astype(np.float32)
+    bhh = (sd * rng.standard_normal(3 * r)).astype(np.float32)
+    return Wih, Whh, bih, bhh
+
+
+def gru_h0(index: int, round_index: int, B: int, r: int = R):
+    """Initial GRU states [B, r] f32 in (-1, 1): tanh of N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(8_000_000 + 1000 * index + round_index))
+    return np.tanh(rng.standard_normal((B, r))).astype(np.float32)
