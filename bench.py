@@ -213,10 +213,12 @@ SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, 
          (3, 1, 16, "bf16"), (3, 1, 16, "int8"), (4, 64, 5, "bf16"), (4, 128, 5, "bf16"),
          (4, 253, 5, "bf16"),
          # the mixed-temperature walks again, sampled by Gumbel-max (DSW_FLAG_GUMBEL)
-         (2, 1, 16, "bf16", "gumbel"), (2, 4, 16, "bf16", "gumbel"), (2, 16, 16, "bf16", "gumbel")]
+         (2, 1, 16, "bf16", "gumbel"), (2, 4, 16, "bf16", "gumbel"), (2, 16, 16, "bf16", "gumbel"),
+         # the GRU serial head (DSW_FLAG_GRU) on the headline and the long walk
+         (1, 1, 7, "bf16", "inverse_cdf", "gru"), (2, 1, 16, "bf16", "inverse_cdf", "gru")]
 
 
-def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf"):
+def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="markov"):
     import workloads
     wl = workloads.WORKLOADS[index]
     V = wl.V
@@ -238,14 +240,24 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf"):
     base, anchor, T, uni = to_device(rounds, torch, dev)
     del rounds
     walker = dsw.Walker(V, gamma_max=gamma, B_max=B, w2_dtype=dsw.INT8 if dtype == "int8" else dsw.BF16,
-                        flags=dsw.FLAG_GUMBEL if sampler == "gumbel" else 0)
+                        flags=(dsw.FLAG_GUMBEL if sampler == "gumbel" else 0) |
+                              (dsw.FLAG_GRU if head == "gru" else 0))
     if sampler == "gumbel":
         walker.set_seed(0x5EED + index)
     plan = walker.query_plan(B)
     tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
     n = base.shape[0]
 
+    if head == "gru":  # synthetic cell and initial state (no checkpoint uses this head)
+        cw = workloads.gru_cell_weights(index)
+        celld = (bf(cw[0]), bf(cw[1]), torch.from_numpy(cw[2]).to(dev), torch.from_numpy(cw[3]).to(dev))
+        h0 = torch.from_numpy(workloads.gru_h0(index, 0, 1)[0]).to(dev)
+
     def go(j):
+        if head == "gru":
+            walker.walk_gru(W1d, W2d, celld, h0, base[j % n], anchor[j % n], T[j % n], uni[j % n],
+                            tokens=tokens)
+            return
         walker.walk(W1d, W2d, base[j % n], anchor[j % n], T[j % n], uni[j % n], w2_scale=scale,
                     tokens=tokens)
     for j in range(5):
@@ -270,6 +282,7 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf"):
     stepwise = (gamma * w2_bytes + B * gamma * V * 2) / (HBM_PEAK_GBS * 1e9) * 1e6
     flops = 2.0 * B * 256 * V * gamma
     out = {"workload": wl.name, "B": B, "gamma": gamma, "w2": dtype, "temps": wl.temps, "sampler": sampler,
+           "head": head,
            "us_per_round": round(us, 2), "launch_us": round(launch, 2),
            "kernel": "batched" if plan.batch_tile == 256 else
                      ("valu" if plan.engine == dsw.ENGINE_VALU else "mfma"),

@@ -120,6 +120,13 @@ extern "C" {
                                     all-to-all kernel only: with
                                     DSW_FLAG_BATCHED or B_max > 16, dsw_create
                                     returns DSW_ERR_ARG.                       */
+#define DSW_FLAG_GRU 128u        /* the GRU serial head ("Keeping the Draft Walk on
+                                    Chip", section "Beyond DSpark: other serial
+                                    heads"): walks go through dsw_walk_gru.
+                                    One bf16 request (B_max = 1); not with
+                                    DSW_FLAG_GUMBEL, DSW_FLAG_BATCHED or
+                                    DSW_FLAG_VALU_GEMV (DSW_ERR_ARG) or int8
+                                    rows (DSW_ERR_DTYPE).                      */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -215,6 +222,34 @@ int dsw_create(dsw_handle_t* h, int device, int V, int r, int gamma_max, int B_m
 int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale,
              const void* base, const int32_t* anchor, const float* T, const float* uniforms,
              int32_t* tokens, void* logits, int B, int gamma, void* stream);
+
+/* One round of the GRU serial head ("Keeping the Draft Walk on Chip", section
+ * "Beyond DSpark: other serial heads": the walk with a recurrent state, each
+ * head supplying only its state update; DeLS-Spec's head is a GRU).  Handle
+ * created with DSW_FLAG_GRU (dsw_walk on it returns DSW_ERR_ARG, and this call
+ * on another handle too).  For k < gamma, with prev = anchor, then the
+ * previous token, and h = h0, then the previous state:
+ *   x  = W1[prev]
+ *   r  = sigmoid(Wih[0:r] x + bih[0:r] + Whh[0:r] h + bhh[0:r])
+ *   z  = sigmoid(Wih[r:2r] x + bih[r:2r] + Whh[r:2r] h + bhh[r:2r])
+ *   n  = tanh(Wih[2r:3r] x + bih[2r:3r] + r * (Whh[2r:3r] h + bhh[2r:3r]))
+ *   h  = (1 - z) * n + z * h                 (fp32, the standard GRU cell)
+ *   logit = bf16(base_k + bf16(W2 bf16(h))), tok as in dsw_walk.
+ * Arguments as dsw_walk (B must be 0 or 1; bf16 W2, w2_scale NULL), plus
+ * (device pointers):
+ *   Wih, Whh  bf16 [3r][r]   the cell's input and recurrent weights, gate
+ *                            blocks in the order (r, z, n)
+ *   bih, bhh  f32 [3r]       their biases
+ *   h0        f32 [r]        the initial state
+ *   states    f32 [gamma][r] out, or NULL: the state after every step (the
+ *                            last one continues the next round)
+ * The state is spread over the workgroups (each updates r / grid elements
+ * with its rows of the cell held in LDS) and gathered by every workgroup once
+ * per step through epoch-tagged mailboxes.  Asynchronous; allocates nothing. */
+int dsw_walk_gru(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
+                 const float* bih, const float* bhh, const float* h0, const void* base,
+                 const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
+                 void* logits, float* states, int B, int gamma, void* stream);
 
 /* Wait for the handle's device, then return and clear the status word that
  * the device latches (0 or a DSW_ERR_DEV_* code).  After a device error the

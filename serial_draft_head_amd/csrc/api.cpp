@@ -21,11 +21,17 @@ extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max
 extern "C" const void* dsw_internal_mfma_kernel_b4_gumbel(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16_gumbel(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel_gumbel(int batch_tile, int reg_tiles, int max_tiles);
+// the one-request kernels for the GRU serial head
+extern "C" const void* dsw_internal_mfma_kernel_b1_gru(int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs (with Gumbel-max sampling when `gumbel`), or
 // nullptr.  The planner never gives a Gumbel-max handle the batched kernel.
-const void* kernel_for(const dsw_plan_info& pl, bool gumbel) {
+const void* kernel_for(const dsw_plan_info& pl, bool gumbel, bool gru) {
+    if (gru)  // the planner gives the GRU head only the one-request MFMA engine
+        return pl.engine == DSW_ENGINE_MFMA && pl.batch_tile == 1 && pl.w2_dtype == DSW_BF16
+                   ? dsw_internal_mfma_kernel_b1_gru(pl.reg_tiles, pl.max_tiles)
+                   : nullptr;
     if (pl.batch_tile == dsw::kMaxBatch)
         return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
     if (pl.engine == DSW_ENGINE_VALU)
@@ -193,7 +199,9 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         const int gm = (i % n_g) == 0 ? gamma_max : 3;
         dsw_plan_info pl;
         int prc = dsw_plan_compute(&dev, V, r, gm, B, w2_dtype, flags, &pl);
-        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0) : nullptr;
+        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0,
+                                                    (flags & DSW_FLAG_GRU) != 0)
+                                        : nullptr;
         hipFuncAttributes attr;
         int per_cu = 0;
         bool ok = fn != nullptr && hipFuncGetAttributes(&attr, fn) == hipSuccess &&
@@ -222,10 +230,20 @@ extern "C" int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out) {
     return dsw_plan_compute(&h->dev, h->V, h->r, h->gamma_max, B, h->dtype, h->flags, out);
 }
 
-extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale,
-                        const void* base, const int32_t* anchor, const float* T,
-                        const float* uniforms, int32_t* tokens, void* logits, int B, int gamma,
-                        void* stream) {
+namespace {
+// The GRU head's extra arguments (dsw_walk_gru).
+struct GruArgs {
+    const uint16_t* wih;
+    const uint16_t* whh;
+    const float* bih;
+    const float* bhh;
+    const float* h0;
+    float* states;
+};
+
+int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale, const void* base,
+              const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens, void* logits,
+              int B, int gamma, void* stream, const GruArgs* gru) {
     if (!h) return DSW_ERR_NULL;
     if (B < 0 || B > h->B_max) return DSW_ERR_BATCH;
     if (gamma < 0 || gamma > h->gamma_max) return DSW_ERR_GAMMA;
@@ -238,7 +256,7 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     dsw_plan_info plan;
     int rc = dsw_plan_compute(&h->dev, h->V, h->r, gamma, B, h->dtype, h->flags, &plan);
     if (rc) return rc;
-    const void* fn = kernel_for(plan, (h->flags & DSW_FLAG_GUMBEL) != 0);
+    const void* fn = kernel_for(plan, (h->flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr);
     if (!fn) return DSW_ERR_PLAN;
 
     DeviceGuard g(h->device);
@@ -288,6 +306,12 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
     p.single_round = (h->flags & DSW_FLAG_SINGLE_ROUND) ? 1 : 0;
     p.seeded = h->seeded;
     p.seed = h->seed;
+    p.gru_wih = gru ? gru->wih : nullptr;
+    p.gru_whh = gru ? gru->whh : nullptr;
+    p.gru_bih = gru ? gru->bih : nullptr;
+    p.gru_bhh = gru ? gru->bhh : nullptr;
+    p.h0 = gru ? gru->h0 : nullptr;
+    p.states = gru ? gru->states : nullptr;
     p.trace = nullptr;
     if (h->trace != nullptr &&
         (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)
@@ -302,6 +326,26 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
                             static_cast<hipStream_t>(stream));
     if (e == hipErrorCooperativeLaunchTooLarge) return DSW_ERR_LAUNCH;
     return e == hipSuccess ? DSW_OK : DSW_ERR_HIP;
+}
+}  // namespace
+
+extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale,
+                        const void* base, const int32_t* anchor, const float* T,
+                        const float* uniforms, int32_t* tokens, void* logits, int B, int gamma,
+                        void* stream) {
+    if (h && (h->flags & DSW_FLAG_GRU)) return DSW_ERR_ARG;  // dsw_walk_gru serves these handles
+    return walk_impl(h, W1, W2, w2_scale, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, nullptr);
+}
+
+extern "C" int dsw_walk_gru(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
+                            const float* bih, const float* bhh, const float* h0, const void* base,
+                            const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
+                            void* logits, float* states, int B, int gamma, void* stream) {
+    if (!h) return DSW_ERR_NULL;
+    if (!(h->flags & DSW_FLAG_GRU)) return DSW_ERR_ARG;
+    if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
+    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states};
+    return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
 }
 
 extern "C" int dsw_set_seed(dsw_handle_t h, unsigned long long seed, int enable) {

@@ -9,12 +9,16 @@
 #define DSW_SAMPLER 0
 #define DSW_LOOKUP dsw_internal_mfma_kernel_b1
 #endif
+// DSW_CELL 0: the Markov head; 1: the GRU head (walk_mfma_b1_gru.hip)
+#ifndef DSW_CELL
+#define DSW_CELL 0
+#endif
 
 // Host-side lookup used by the launcher: the kernel for (register tiles,
 // tiles per wave) at batch tile 1, or nullptr when that shape is not compiled.
 extern "C" const void* DSW_LOOKUP(int reg_tiles, int max_tiles) {
 #define DSW_PICK(R, M) \
-    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_kernel<dsw::kEngineMfma, (R), (M), 1, 0, DSW_SAMPLER>;
+    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_kernel<dsw::kEngineMfma, (R), (M), 1, 0, DSW_SAMPLER, DSW_CELL>;
     DSW_MFMA_ONE_SHAPES(DSW_PICK)
 #undef DSW_PICK
     return nullptr;

@@ -24,6 +24,7 @@ constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 // s.  Nothing needs clearing between steps, launches or graph replays.
 constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 16 exp-sum words
 constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
+constexpr int kGruMaxPerWg = 4;    // GRU head: state elements per workgroup (one per wave; grid >= 64)
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
 constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests
@@ -101,6 +102,15 @@ struct WalkParams {
     int single_round;        // 1: logit = bf16(base + fp32 dot), rounded once
     int seeded;              // 1: uniforms == NULL draws them on the device from seed
     unsigned long long seed; // key of the device-drawn uniforms and of the Gumbel noise
+    // GRU serial head (kernels with CELL = 1; one request): the cell's weights
+    // [3r][r] bf16 and biases [3r] f32 (gates r, z, n), the initial state [r]
+    // f32, and an optional [gamma][r] f32 output of every step's state
+    const uint16_t* gru_wih;
+    const uint16_t* gru_whh;
+    const float* gru_bih;
+    const float* gru_bhh;
+    const float* h0;
+    float* states;
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };
 

@@ -65,20 +65,33 @@ class Weights:
 
 
 def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, steps=None,
-                single_round=False, gumbel=None):
+                single_round=False, gumbel=None, latents=None):
     """Assert the parity rules for one round; return a small report dict.
-    gumbel: (seed, round counter) of a Gumbel-max walk, else None."""
+    gumbel: (seed, round counter) of a Gumbel-max walk, else None.
+    latents: [B, gamma, r] bf16 bits of the GEMV operand of every step (the GRU
+    head's bf16(h)), else None (the Markov head's W1[prev])."""
     B, gamma, V = base.shape
     g_seed, g_round = gumbel if gumbel is not None else (0, 0)
-    or_tok, or_lg = oracle.walk(w.W1_bits, base, anchor, T, uniforms, W2_bits=w.W2_bits, Q=w.Q,
-                                scale=w.scale, forced=gpu_tokens, single_round=single_round,
-                                gumbel=gumbel is not None, seed=g_seed, round_counter=g_round)
+    if latents is None:
+        or_tok, or_lg = oracle.walk(w.W1_bits, base, anchor, T, uniforms, W2_bits=w.W2_bits, Q=w.Q,
+                                    scale=w.scale, forced=gpu_tokens, single_round=single_round,
+                                    gumbel=gumbel is not None, seed=g_seed, round_counter=g_round)
+    else:  # one oracle step per (request, step) on the given operand
+        assert gumbel is None
+        or_tok = np.empty((B, gamma), np.int32)
+        or_lg = np.empty((B, gamma, V), np.uint16)
+        for b in range(B):
+            for k in range(gamma) if steps is None else steps:
+                uk = 0.0 if uniforms is None else uniforms[b, k]
+                or_tok[b, k], or_lg[b, k] = oracle.step(latents[b, k], base[b, k], T[b], uk,
+                                                        W2_bits=w.W2_bits, Q=w.Q, scale=w.scale,
+                                                        single_round=single_round)
     rep = {"steps": 0, "exact_logits": 0, "logits": 0, "near_ties": 0, "token_match": 0,
            "sampled": 0, "sampled_exact_checked": 0}
     for b in range(B):
         for k in range(gamma) if steps is None else steps:
             prev = int(anchor[b]) if k == 0 else int(gpu_tokens[b, k - 1])
-            u = w.W1[prev]
+            u = w.W1[prev] if latents is None else oracle.bf16_bits_to_f64(latents[b, k])
             acc = w.W2 @ u
             E = GAMMA_R * (w.W2abs @ np.abs(u))
             if w.Q is not None:  # the fp32 product scale * sum rounds once more
@@ -152,3 +165,46 @@ def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, s
                     assert tok == want, f"b={b} k={k}: sampled {tok} vs oracle {want}"
                     rep["sampled_exact_checked"] += 1
     return rep
+
+
+# ---------------------------------------------------------------- GRU head
+F32_EPS = 2.0 ** -24
+
+
+def check_gru_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states):
+    """The GPU's state after every step against the oracle's binary64 GRU cell
+    applied to the GPU's previous state (teacher forcing), within a bound of
+    the fp32 evaluation: each of the six dot products (r bf16 x bf16 or bf16 x
+    fp32 terms, fma) and its bias adds err <= g_(r+4) (sum |w v| + |b|) with
+    g_n = n 2^-24 / (1 - n 2^-24); sigmoid' <= 1/4, tanh' <= 1; each fp32
+    exp/divide/tanh adds 4 ulps of its result, the final blend 3 ulps.
+    Returns (steps checked, largest error, largest error / bound)."""
+    Wih, Whh, bih, bhh = cell
+    Wi, Wh = oracle.bf16_bits_to_f64(Wih), oracle.bf16_bits_to_f64(Whh)
+    r = Wi.shape[1]
+    gam = (r + 4) * F32_EPS / (1 - (r + 4) * F32_EPS)
+    gamma = gpu_states.shape[0]
+    worst, worst_ratio = 0.0, 0.0
+    for k in range(gamma):
+        prev = int(anchor) if k == 0 else int(gpu_tokens[k - 1])
+        x = oracle.bf16_bits_to_f64(W1_bits[prev])
+        h = h0.astype(np.float64) if k == 0 else gpu_states[k - 1].astype(np.float64)
+        want = oracle.gru_cell(x, h, Wih, Whh, bih, bhh)
+        gi = Wi @ x + bih
+        gh = Wh @ h + bhh
+        Ei = gam * (np.abs(Wi) @ np.abs(x) + np.abs(bih))
+        Eh = gam * (np.abs(Wh) @ np.abs(h) + np.abs(bhh))
+        gi, gh, Ei, Eh = (a.reshape(3, r) for a in (gi, gh, Ei, Eh))
+        rg = 1 / (1 + np.exp(-(gi[0] + gh[0])))
+        zg = 1 / (1 + np.exp(-(gi[1] + gh[1])))
+        ng = np.tanh(gi[2] + rg * gh[2])
+        e_r = 0.25 * (Ei[0] + Eh[0]) + 4 * F32_EPS * rg
+        e_z = 0.25 * (Ei[1] + Eh[1]) + 4 * F32_EPS * zg
+        e_n = Ei[2] + rg * Eh[2] + e_r * np.abs(gh[2]) + 4 * F32_EPS * (np.abs(ng) + np.abs(gi[2] + rg * gh[2]))
+        bound = e_z * np.abs(ng - h) + (1 - zg) * e_n + 3 * F32_EPS * (np.abs(ng) + np.abs(h))
+        bound = 2 * bound + 1e-9
+        err = np.abs(gpu_states[k].astype(np.float64) - want)
+        assert np.all(err <= bound), f"k={k}: state error {err.max()} above its bound at {np.argmax(err - bound)}"
+        worst = max(worst, float(err.max()))
+        worst_ratio = max(worst_ratio, float((err / bound).max()))
+    return gamma, worst, worst_ratio

@@ -59,6 +59,7 @@ def test_null_and_argument_errors_without_a_device(dsw):
     assert L.dsw_create(ctypes.byref(h), 0, 0, 256, 7, 1, 0, 0) == -6        # vocab
     assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 0, 1, 0, 0) == -3      # gamma
     assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 7, 0, 0, 0) == -2      # batch
+    assert L.dsw_walk_gru(None, *([None] * 14), 1, 1, None) == -1
 
 
 def fake_device(dsw, cus=256, lds_cu=160 * 1024, lds_blk=160 * 1024):
@@ -203,6 +204,30 @@ def test_planner_gumbel_max_stays_on_the_all_to_all_kernel(dsw):
         with pytest.raises(dsw.DswError) as e:
             dsw.plan(d, 129_280, 5, B, flags=flags)
         assert e.value.code == -11
+
+
+def test_planner_gru_head(dsw):
+    d = fake_device(dsw)
+    R = dsw.FLAG_GRU
+    # one bf16 request on the one-request MFMA engine, also for short walks
+    for gamma in (1, 3, 16):
+        p = dsw.plan(d, 151_936, gamma, 1, flags=R)
+        assert (p.engine, p.batch_tile, p.reg_tiles, p.max_tiles) == (1, 1, 10, 10)
+        q = dsw.plan(d, 151_936, 16, 1)
+        # the state, the cell rows and the recurrent pre-activations take LDS
+        assert p.static_lds_bytes == q.static_lds_bytes + 256 * 4 + 4 * 6 * (512 + 4) + 4 * 3 * 4
+    assert dsw.plan(d, 248_320, 16, 1, flags=R).max_tiles == 16
+    for B, flags, dt, code in ((2, R, dsw.BF16, -11), (1, R | dsw.FLAG_GUMBEL, dsw.BF16, -11),
+                               (1, R | dsw.FLAG_BATCHED, dsw.BF16, -11), (1, R | dsw.FLAG_VALU_GEMV, dsw.BF16, -11),
+                               (1, R, dsw.INT8, -5)):
+        with pytest.raises(dsw.DswError) as e:
+            dsw.plan(d, 151_936, 7, B, w2_dtype=dt, flags=flags)
+        assert e.value.code == code
+    # the state is spread over at most 4 elements per workgroup: 64 CUs at least
+    assert dsw.plan(fake_device(dsw, cus=64), 32_000, 7, 1, flags=R).grid == 64
+    with pytest.raises(dsw.DswError) as e:
+        dsw.plan(fake_device(dsw, cus=63), 32_000, 7, 1, flags=R)
+    assert e.value.code == -10
 
 
 def test_planner_int8_rows(dsw):

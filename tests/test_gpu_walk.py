@@ -458,6 +458,76 @@ def test_graph_replays_are_fresh_walks(dsw, B, flags, temps):
     walker.close()
 
 
+# The GRU serial head: the state after every step against the oracle's cell
+# on the GPU's previous state, and the logits / tokens of every step against
+# the oracle's step on the GPU's operand bf16(h) (both teacher forced).
+GRU_CASES = [  # (V, gamma, temps)
+    (4_097, 5, "greedy"), (32_000, 7, "cycle"), (151_936, 16, "greedy"), (151_936, 8, "hot"),
+    (248_320, 4, "greedy")]
+
+
+@pytest.mark.parametrize("V,gamma,temps", GRU_CASES)
+def test_gru_head(dsw, V, gamma, temps):
+    import oracle
+    say(f"gru head V={V} gamma={gamma} {temps}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    cell = workloads.gru_cell_weights(1)
+    celld = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+             torch.from_numpy(cell[3]).to(DEV))
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_GRU)
+    say("plan", walker.query_plan(1).as_dict())
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 500 + rnd, B=1, gamma=gamma, V=V,
+                                     temps="cycle" if temps == "hot" else temps)
+        if temps == "hot":
+            inp["T"][:] = 1.0
+        h0 = workloads.gru_h0(1, rnd, 1)
+        base, anchor, T, uni = round_dev(inp)
+        tokens, logits, states = walker.walk_gru(W1d, W2d, celld, torch.from_numpy(h0[0]).to(DEV), base,
+                                                 anchor, T, uni, want_logits=True, want_states=True)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        st = states.cpu().numpy()
+        n, worst, ratio = parity.check_gru_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+        ub = oracle.rne_bf16(st.astype(np.float64))[1][None]
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 latents=ub)
+        say(rnd, f"states: {n} steps, largest error {worst:.3g} ({ratio:.3f} of its bound)", rep)
+        # the same walk without the optional outputs gives the same tokens
+        t2, _, _ = walker.walk_gru(W1d, W2d, celld, torch.from_numpy(h0[0]).to(DEV), base, anchor, T, uni)
+        torch.cuda.synchronize()
+        assert walker.status() == 0 and np.array_equal(t2.cpu().numpy(), toks)
+    walker.close()
+
+
+def test_gru_head_argument_errors(dsw):
+    V = 4_096
+    W1, W2 = workloads.weights(2, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(2, 1, B=1, gamma=3, V=V)
+    base, anchor, T, uni = round_dev(inp)
+    g = dsw.Walker(V, gamma_max=3, B_max=1, flags=dsw.FLAG_GRU)
+    with pytest.raises(dsw.DswError) as e:   # a GRU handle takes dsw_walk_gru only
+        g.walk(W1d, W2d, base, anchor, T, uni)
+    assert e.value.code == -11
+    g.close()
+    m = dsw.Walker(V, gamma_max=3, B_max=1)
+    cell = workloads.gru_cell_weights(1)
+    celld = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+             torch.from_numpy(cell[3]).to(DEV))
+    with pytest.raises(dsw.DswError) as e:   # and a Markov handle refuses it
+        m.walk_gru(W1d, W2d, celld, torch.zeros(256, device=DEV), base, anchor, T, uni)
+    assert e.value.code == -11
+    m.close()
+    with pytest.raises(dsw.DswError) as e:
+        dsw.Walker(V, gamma_max=3, B_max=2, flags=dsw.FLAG_GRU)
+    assert e.value.code == -11
+
+
 # int8 rows + fp32 row scales: one vocabulary per compiled int8 shape, plus
 # ragged sizes; the harness quantizes once and both sides consume (q, scale).
 I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),
