@@ -319,7 +319,7 @@ def main():
                     help="for counter runs: only the step-wise library-op loop, then the same copy")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the walk runs on one GPU; --gpus must be 1 (the multi-GPU split is a design, not built)"}))
         sys.exit(2)
 
     import torch
