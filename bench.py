@@ -215,15 +215,18 @@ SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, 
          # the mixed-temperature walks again, sampled by Gumbel-max (DSW_FLAG_GUMBEL)
          (2, 1, 16, "bf16", "gumbel"), (2, 4, 16, "bf16", "gumbel"), (2, 16, 16, "bf16", "gumbel"),
          # the GRU serial head (DSW_FLAG_GRU) on the headline and the long walk
-         (1, 1, 7, "bf16", "inverse_cdf", "gru"), (2, 1, 16, "bf16", "inverse_cdf", "gru")]
+         (1, 1, 7, "bf16", "inverse_cdf", "gru"), (2, 1, 16, "bf16", "inverse_cdf", "gru"),
+         # one GPU's share of a two-GPU vocabulary split (the kernel at its real shape;
+         # the cross-GPU exchange is not built): half of V = 151,936 and of V = 248,320
+         (1, 1, 7, "bf16", "inverse_cdf", "markov", 75_968), (3, 1, 16, "bf16", "inverse_cdf", "markov", 124_160)]
 
 
-def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="markov"):
+def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="markov", V=None):
     import workloads
     wl = workloads.WORKLOADS[index]
-    V = wl.V
+    V = wl.V if V is None else V
     dev = torch.device("cuda", 0)
-    W1, W2 = workloads.weights(index)
+    W1, W2 = workloads.weights(index, V=V)
     bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     W1d = bf(W1)
     scale = None
@@ -281,7 +284,7 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="m
     abytes = algorithmic_bytes(V, B, gamma) - V * 256 * 2 + w2_bytes
     stepwise = (gamma * w2_bytes + B * gamma * V * 2) / (HBM_PEAK_GBS * 1e9) * 1e6
     flops = 2.0 * B * 256 * V * gamma
-    out = {"workload": wl.name, "B": B, "gamma": gamma, "w2": dtype, "temps": wl.temps, "sampler": sampler,
+    out = {"workload": wl.name, "V": V, "B": B, "gamma": gamma, "w2": dtype, "temps": wl.temps, "sampler": sampler,
            "head": head,
            "us_per_round": round(us, 2), "launch_us": round(launch, 2),
            "kernel": "batched" if plan.batch_tile == 256 else

@@ -182,9 +182,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const WT* src = W2 + (size_t)row * kRowChunks + g;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
+    }
+    // pinned once every tile's loads are in flight (a pin waits for its registers)
+#pragma unroll
+    for (int j = 0; j < A; ++j)
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) pin_agpr(wr[j][kb]);
-    }
     for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
         WT v[8];
 #pragma unroll

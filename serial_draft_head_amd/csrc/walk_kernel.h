@@ -280,12 +280,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             const WT* src = W2 + (size_t)row * kRowChunks;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[DSW_KC(kb, g)];
+        }
+        // pinned only once every tile's loads are in flight: a pin waits for
+        // its registers, so pinning tile by tile would turn the shard load
+        // into one memory round trip per tile
+#pragma unroll
+        for (int j = 0; j < A; ++j)
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
                 if (j < kMaxRegTiles) pin_agpr(wr[j][kb]);
                 else pin_vgpr(wr[j][kb]);
             }
-        }
         if constexpr (kOne) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
