@@ -646,7 +646,8 @@ def check_subset(w, inp, toks, lg, idx, steps=None):
 
 
 # aligned (V % 8 == 0: base rows stream straight into LDS) and unaligned vocabularies
-BATCHED_CASES = [(257, 17), (4_096, 40), (32_000, 64), (65_537, 33), (129_280, 24)]
+# V = 151,936 keeps two tiles per wave in LDS beside the ring
+BATCHED_CASES = [(257, 17), (4_096, 40), (32_000, 64), (65_537, 33), (129_280, 24), (151_936, 20)]
 
 
 @pytest.mark.parametrize("temps", ["greedy", "mixed"])
@@ -659,6 +660,7 @@ def test_batched_parity(dsw, V, B, temps):
     pl = walker.query_plan(B)
     say("plan", pl.as_dict())
     assert pl.batch_tile == 256
+    assert (pl.lds_tiles > 0) == (V == 151_936)
     W1d, W2d = bf16_dev(W1), bf16_dev(W2)
     inp = workloads.round_inputs(4, 3, B=B, gamma=3, V=V, temps=temps)
     toks, lg = run(walker, W1d, W2d, inp)
