@@ -441,21 +441,26 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const float Tb = bval ? s_T[b] : 0.0f;
                 const float mw = local_key_logit(best);
                 float sw = 0.0f;
-                if (Tb > 0.0f && best != 0u) {
-                    const float sc = kLog2e / Tb;
+                // every tile's four logits are read first (all reads in flight,
+                // rows clamped into the slot), then the exps; lanes of greedy or
+                // empty columns compute theirs and drop them
+                const bool on = Tb > 0.0f && best != 0u;
+                const float sc = on ? kLog2e / Tb : 0.0f;
+                uint2 lw[M];
 #pragma unroll
-                    for (int j = 0; j < M; ++j) {
-                        const int rb = wrow0 + j * kTileRows + 4 * g;
-                        if (j < nt_w && rb < nrows) {
-                            const uint2 lw = *reinterpret_cast<const uint2*>(sb + (n * CPR + ((rb >> 3) ^ n)) * 8 + (rb & 7));
-                            const float lv[4] = {bf16_lo(lw.x), bf16_hi(lw.x), bf16_lo(lw.y), bf16_hi(lw.y)};
-                            const int lim = nrows - rb;
+                for (int j = 0; j < M; ++j) {
+                    const int rb = min(wrow0 + j * kTileRows + 4 * g, Rpad - 4);
+                    lw[j] = *reinterpret_cast<const uint2*>(sb + (n * CPR + ((rb >> 3) ^ n)) * 8 + (rb & 7));
+                }
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float e = __builtin_amdgcn_exp2f((lv[i] - mw) * sc);
-                                sw += i < lim ? e : 0.0f;
-                            }
-                        }
+                for (int j = 0; j < M; ++j) {
+                    const int rb = wrow0 + j * kTileRows + 4 * g;
+                    const int lim = (on && j < nt_w) ? nrows - rb : 0;
+                    const float lv[4] = {bf16_lo(lw[j].x), bf16_hi(lw[j].x), bf16_lo(lw[j].y), bf16_hi(lw[j].y)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = __builtin_amdgcn_exp2f((lv[i] - mw) * sc);
+                        sw += i < lim ? e : 0.0f;
                     }
                 }
                 sw += __shfl_xor(sw, 16);
