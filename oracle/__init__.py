@@ -77,6 +77,10 @@ def _load():
     lib.oracle_gru_cell.argtypes = [i, P, P, P, P, P, P, P]
     lib.oracle_walk_gru.restype = i
     lib.oracle_walk_gru.argtypes = [i, i, i, i] + [P] * 18 + [i, ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_rnn_cell.restype = None
+    lib.oracle_rnn_cell.argtypes = [i, P, P, P, P, P, P, P]
+    lib.oracle_walk_rnn.restype = i
+    lib.oracle_walk_rnn.argtypes = [i, i, i, i] + [P] * 18 + [i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_threads.restype = i
     lib.oracle_philox4x32_10.argtypes = [P, P, P]
     lib.oracle_philox4x32_10.restype = None
@@ -241,9 +245,29 @@ def gru_cell(x, h, Wih_bits, Whh_bits, bih, bhh):
     return out
 
 
+def rnn_cell(x, h, Wih_bits, Whh_bits, bih, bhh):
+    """One tanh RNN cell in binary64: x, h [r] -> tanh(Wih x + bih + Whh h + bhh) [r];
+    Wih, Whh [r, r] bf16 bits, bih, bhh [r] f32."""
+    x = _c(x, np.float64)
+    h = _c(h, np.float64)
+    r = x.shape[0]
+    Wih_bits, Whh_bits = _c(Wih_bits, np.uint16), _c(Whh_bits, np.uint16)
+    bih, bhh = _c(bih, np.float32), _c(bhh, np.float32)
+    assert Wih_bits.shape == (r, r) and Whh_bits.shape == (r, r) and h.shape == (r,)
+    out = np.empty(r, dtype=np.float64)
+    _load().oracle_rnn_cell(r, _ptr(x), _ptr(h), _ptr(Wih_bits), _ptr(Whh_bits), _ptr(bih), _ptr(bhh),
+                            _ptr(out))
+    return out
+
+
+def walk_rnn(W1_bits, base_bits, anchor, T, cell, h0, **kw):
+    """The RNN head's walk: as walk_gru with cell = (Wih [r,r] u16, Whh [r,r] u16, bih [r], bhh [r])."""
+    return walk_gru(W1_bits, base_bits, anchor, T, cell, h0, _fn="oracle_walk_rnn", **kw)
+
+
 def walk_gru(W1_bits, base_bits, anchor, T, cell, h0, uniforms=None, W2_bits=None, Q=None, scale=None,
              forced=None, forced_h=None, want_logits=True, single_round=False, gumbel=False, seed=0,
-             round_counter=0):
+             round_counter=0, _fn="oracle_walk_gru"):
     """The GRU head's walk.  cell = (Wih [3r,r] u16, Whh [3r,r] u16, bih [3r] f32, bhh [3r] f32);
     h0 [B,r] f32; forced_h [B,gamma,r] f32 or None (teacher forcing of the state).
     Returns (tokens [B,gamma] i32, logits [B,gamma,V] u16 or None, states [B,gamma,r] f64)."""
@@ -262,11 +286,11 @@ def walk_gru(W1_bits, base_bits, anchor, T, cell, h0, uniforms=None, W2_bits=Non
     logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
     states = np.empty((B, gamma, r), dtype=np.float64)
     mode = (SINGLE_ROUND if single_round else 0) | (GUMBEL if gumbel else 0)
-    rc = _load().oracle_walk_gru(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+    rc = getattr(_load(), _fn)(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
                                  _ptr(Wih), _ptr(Whh), _ptr(bih), _ptr(bhh), _ptr(h0), _ptr(base_bits),
                                  _ptr(anchor), _ptr(T), _ptr(uniforms), _ptr(forced), _ptr(forced_h),
                                  _ptr(tokens), _ptr(logits), _ptr(states), mode,
                                  int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF)
     if rc != 0:
-        raise RuntimeError(f"oracle_walk_gru failed with {rc}")
+        raise RuntimeError(f"{_fn} failed with {rc}")
     return tokens, logits, states

@@ -54,6 +54,9 @@
  *   h' = (1 - z) * n + z * h
  * with x = W1[prev] (the previous token's row of the rank-r table) and the
  * vocabulary matrix applied to u = bf16(h'):  logit = bf16(base + bf16(W2 u)).
+ * RNN head (oracle_rnn_cell, oracle_walk_rnn; DSpark's own RNN head, read as
+ * the standard tanh RNN cell): h' = tanh(Wih x + bih + Whh h + bhh), otherwise
+ * the same walk.
  *
  * Parallelism: OpenMP over vocabulary rows inside one GEMV.  Each row's sum
  * is formed by one thread in a fixed order, so results do not depend on the
@@ -444,22 +447,38 @@ void oracle_gru_cell(int r, const double* x, const double* h, const uint16_t* Wi
 }
 
 /*
- * The GRU head's walk for B independent requests (free running, or teacher
- * forced).  Arguments as oracle_walk_ex, plus
- *   Wih, Whh, bih, bhh : the cell (see oracle_gru_cell)
+ * One tanh RNN cell in binary64: h' = tanh(Wih x + bih + Whh h + bhh).
+ * Wih, Whh: [r][r] bf16 bits; bih, bhh: [r] f32.
+ */
+void oracle_rnn_cell(int r, const double* x, const double* h, const uint16_t* Wih, const uint16_t* Whh,
+                     const float* bih, const float* bhh, double* out) {
+    for (int j = 0; j < r; ++j) {
+        double si = 0.0, sh = 0.0;
+        for (int i = 0; i < r; ++i) {
+            si += bf16_value(Wih[(size_t)j * r + i]) * x[i];
+            sh += bf16_value(Whh[(size_t)j * r + i]) * h[i];
+        }
+        out[j] = tanh((si + (double)bih[j]) + (sh + (double)bhh[j]));
+    }
+}
+
+/*
+ * A recurrent head's walk for B independent requests (free running, or teacher
+ * forced); kind 1 = GRU, 2 = tanh RNN.  Arguments as oracle_walk_ex, plus
+ *   Wih, Whh, bih, bhh : the cell (see oracle_gru_cell, oracle_rnn_cell)
  *   h0       : [B][r] initial states (f32)
  *   forced_h : [B][gamma][r] f32 or NULL.  When given, step k > 0 of request b
  *              starts from forced_h[b][k-1] instead of the oracle's own state.
  *   states   : [B][gamma][r] out, the states h_k in binary64 (may be NULL)
  * The GEMV operand of step k is bf16(h_k), rounded from binary64.
  */
-int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
-                    const uint16_t* W2, const int8_t* Q, const float* scale,
-                    const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
-                    const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
-                    const float* uniforms, const int32_t* forced, const float* forced_h,
-                    int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
-                    uint32_t round) {
+static int walk_cell(int kind, int V, int r, int B, int gamma, const uint16_t* W1,
+                     const uint16_t* W2, const int8_t* Q, const float* scale,
+                     const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
+                     const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
+                     const float* uniforms, const int32_t* forced, const float* forced_h,
+                     int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
+                     uint32_t round) {
     if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !Wih || !Whh || !bih || !bhh || !h0 || !base ||
         !anchor || !T || !tokens || (!W2 && (!Q || !scale)))
         return -1;
@@ -483,7 +502,8 @@ int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
                 for (int i = 0; i < r; ++i) h[i] = (double)forced_h[((size_t)b * gamma + (k - 1)) * r + i];
             if (prev < 0 || prev >= V) { rc = -1; break; }
             for (int i = 0; i < r; ++i) x[i] = bf16_value(W1[(size_t)prev * r + i]);
-            oracle_gru_cell(r, x, h, Wih, Whh, bih, bhh, hn);
+            if (kind == 1) oracle_gru_cell(r, x, h, Wih, Whh, bih, bhh, hn);
+            else oracle_rnn_cell(r, x, h, Wih, Whh, bih, bhh, hn);
             for (int i = 0; i < r; ++i) {
                 h[i] = hn[i];
                 ub[i] = oracle_bf16_bits(oracle_rne_bf16(hn[i]));
@@ -501,4 +521,29 @@ int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
     }
     free(lg); free(x); free(h); free(hn); free(ub);
     return rc;
+}
+
+/* The GRU head's walk (see walk_cell). */
+int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
+                    const uint16_t* W2, const int8_t* Q, const float* scale,
+                    const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
+                    const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
+                    const float* uniforms, const int32_t* forced, const float* forced_h,
+                    int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
+                    uint32_t round) {
+    return walk_cell(1, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, h0, base, anchor, T, uniforms,
+                     forced, forced_h, tokens, logits, states, mode, seed, round);
+}
+
+/* The RNN head's walk: as oracle_walk_gru with the tanh RNN cell, Wih, Whh
+ * [r][r], bih, bhh [r]. */
+int oracle_walk_rnn(int V, int r, int B, int gamma, const uint16_t* W1,
+                    const uint16_t* W2, const int8_t* Q, const float* scale,
+                    const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
+                    const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
+                    const float* uniforms, const int32_t* forced, const float* forced_h,
+                    int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
+                    uint32_t round) {
+    return walk_cell(2, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, h0, base, anchor, T, uniforms,
+                     forced, forced_h, tokens, logits, states, mode, seed, round);
 }

@@ -309,6 +309,61 @@ def test_gru_walk_brute_force(oracle_mod, seed):
             prev = int(toks[b, k])
 
 
+def test_hand_worked_rnn(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_rnn_r1.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        r = c["r"]
+        Wih = bits_of(np.asarray(c["Wih"], dtype=np.float64).ravel()).reshape(r, r)
+        Whh = bits_of(np.asarray(c["Whh"], dtype=np.float64).ravel()).reshape(r, r)
+        out = oracle_mod.rnn_cell(c["x"], c["h"], Wih, Whh, c["bih"], c["bhh"])
+        assert np.allclose(out, c["out"], rtol=0, atol=1e-14), (c, out)
+
+
+def _torch_rnn(r, x, h, Wih, Whh, bih, bhh):
+    import torch
+    cell = torch.nn.RNNCell(r, r, nonlinearity="tanh").double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(value_f64(Wih)))
+        cell.weight_hh.copy_(torch.from_numpy(value_f64(Whh)))
+        cell.bias_ih.copy_(torch.from_numpy(np.asarray(bih, np.float64)))
+        cell.bias_hh.copy_(torch.from_numpy(np.asarray(bhh, np.float64)))
+        return cell(torch.from_numpy(np.asarray(x, np.float64))[None],
+                    torch.from_numpy(np.asarray(h, np.float64))[None])[0].numpy()
+
+
+@pytest.mark.parametrize("r", [1, 8, 256])
+def test_rnn_cell_matches_torch_rnncell(oracle_mod, r):
+    Wih, Whh, bih, bhh = workloads.rnn_cell_weights(r, r=r)
+    rng = np.random.default_rng(100 + r)
+    for _ in range(5):
+        x = value_f64(workloads.to_bf16_bits(rng.standard_normal(r)))
+        h = np.tanh(rng.standard_normal(r))
+        want = _torch_rnn(r, x, h, Wih, Whh, bih, bhh)
+        got = oracle_mod.rnn_cell(x, h, Wih, Whh, bih, bhh)
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_rnn_walk_brute_force(oracle_mod, seed):
+    V, r, gamma, B = 12, 4, 3, 3
+    d = workloads.toy(seed + 900, V=V, r=r, B=B, gamma=gamma, w2_std=0.5, base_std=0.5)
+    cell = workloads.rnn_cell_weights(seed, r=r)
+    h0 = workloads.gru_h0(seed, 1, B, r=r)
+    toks, logits, states = oracle_mod.walk_rnn(d["W1"], d["base"], d["anchor"], np.zeros(B, np.float32), cell,
+                                               h0, W2_bits=d["W2"])
+    for b in range(B):
+        prev, h = int(d["anchor"][b]), h0[b].astype(np.float64)
+        for k in range(gamma):
+            h = _torch_rnn(r, value_f64(d["W1"][prev]), h, *cell)
+            assert np.allclose(states[b, k], h, rtol=0, atol=1e-13)
+            u = [value(rne_bits(Fraction(float(v)))) for v in states[b, k]]
+            lb = bf.step_logits(d["W2"], u, d["base"][b, k])
+            assert logits[b, k].tolist() == lb
+            assert toks[b, k] == bf.argmax_lowest(lb)
+            prev = int(toks[b, k])
+
+
 def test_gru_walk_teacher_forcing_and_zero_cell(oracle_mod):
     V, r = 2000, 256
     W1, W2 = workloads.weights(0, V=V)

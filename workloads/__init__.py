@@ -122,17 +122,23 @@ def toy(seed: int, V: int = 12, r: int = 4, B: int = 1, gamma: int = 3, w2_std: 
     return {"W1": W1, "W2": W2, "base": base, "anchor": anchor, "T": T, "uniforms": uniforms}
 
 
-def gru_cell_weights(index: int, r: int = R):
-    """Synthetic GRU cell for the GRU serial head (the pages measure such heads on
-    synthetic weights): Wih, Whh [3r, r] bf16 bits and bih, bhh [3r] f32, all
-    N(0, 1/r), the scale of the usual uniform(-1/sqrt(r), 1/sqrt(r)) init."""
-    rng = np.random.Generator(np.random.PCG64(7_000 + index))
+def gru_cell_weights(index: int, r: int = R, gates: int = 3):
+    """Synthetic cell for the recurrent serial heads (the pages measure such heads
+    on synthetic weights): Wih, Whh [gates * r, r] bf16 bits and bih, bhh
+    [gates * r] f32, all N(0, 1/r), the scale of the usual
+    uniform(-1/sqrt(r), 1/sqrt(r)) init.  gates = 3: the GRU, 1: the RNN."""
+    rng = np.random.Generator(np.random.PCG64(7_000 + 10 * index + gates))
     sd = 1.0 / np.sqrt(r)
-    Wih = to_bf16_bits(sd * rng.standard_normal((3 * r, r), dtype=np.float32))
-    Whh = to_bf16_bits(sd * rng.standard_normal((3 * r, r), dtype=np.float32))
-    bih = (sd * rng.standard_normal(3 * r)).astype(np.float32)
-    bhh = (sd * rng.standard_normal(3 * r)).astype(np.float32)
+    Wih = to_bf16_bits(sd * rng.standard_normal((gates * r, r), dtype=np.float32))
+    Whh = to_bf16_bits(sd * rng.standard_normal((gates * r, r), dtype=np.float32))
+    bih = (sd * rng.standard_normal(gates * r)).astype(np.float32)
+    bhh = (sd * rng.standard_normal(gates * r)).astype(np.float32)
     return Wih, Whh, bih, bhh
+
+
+def rnn_cell_weights(index: int, r: int = R):
+    """Synthetic tanh RNN cell: Wih, Whh [r, r] bf16 bits, bih, bhh [r] f32."""
+    return gru_cell_weights(index, r=r, gates=1)
 
 
 def gru_h0(index: int, round_index: int, B: int, r: int = R):
