@@ -127,6 +127,10 @@ extern "C" {
                                     DSW_FLAG_GUMBEL, DSW_FLAG_BATCHED or
                                     DSW_FLAG_VALU_GEMV (DSW_ERR_ARG) or int8
                                     rows (DSW_ERR_DTYPE).                      */
+#define DSW_FLAG_RNN 256u        /* the RNN serial head (same section; DSpark's
+                                    RNN head, read as the tanh RNN cell):
+                                    walks go through dsw_walk_rnn.  The same
+                                    limits as DSW_FLAG_GRU, and not with it. */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -226,8 +230,8 @@ int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sca
 /* One round of the GRU serial head ("Keeping the Draft Walk on Chip", section
  * "Beyond DSpark: other serial heads": the walk with a recurrent state, each
  * head supplying only its state update; DeLS-Spec's head is a GRU).  Handle
- * created with DSW_FLAG_GRU (dsw_walk on it returns DSW_ERR_ARG, and this call
- * on another handle too).  For k < gamma, with prev = anchor, then the
+ * created with DSW_FLAG_GRU (dsw_walk or dsw_walk_rnn on it returns
+ * DSW_ERR_ARG, and this call on another handle too).  For k < gamma, with prev = anchor, then the
  * previous token, and h = h0, then the previous state:
  *   x  = W1[prev]
  *   r  = sigmoid(Wih[0:r] x + bih[0:r] + Whh[0:r] h + bhh[0:r])
@@ -247,6 +251,16 @@ int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sca
  * with its rows of the cell held in LDS) and gathered by every workgroup once
  * per step through epoch-tagged mailboxes.  Asynchronous; allocates nothing. */
 int dsw_walk_gru(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
+                 const float* bih, const float* bhh, const float* h0, const void* base,
+                 const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
+                 void* logits, float* states, int B, int gamma, void* stream);
+
+/* One round of the RNN serial head ("Keeping the Draft Walk on Chip", section
+ * "Beyond DSpark: other serial heads": DSpark's own RNN head).  Handle created
+ * with DSW_FLAG_RNN.  As dsw_walk_gru with the tanh RNN cell
+ *   h = tanh(Wih x + bih + Whh h + bhh)      (fp32, x = W1[prev])
+ * and Wih, Whh bf16 [r][r], bih, bhh f32 [r]. */
+int dsw_walk_rnn(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
                  const float* bih, const float* bhh, const float* h0, const void* base,
                  const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
                  void* logits, float* states, int B, int gamma, void* stream);

@@ -39,6 +39,7 @@ FLAG_BATCHED = 16
 FLAG_SINGLE_ROUND = 32
 FLAG_GUMBEL = 64
 FLAG_GRU = 128
+FLAG_RNN = 256
 ENGINE_VALU, ENGINE_MFMA = 0, 1
 RANK = 256
 
@@ -99,6 +100,7 @@ def lib():
         L.dsw_create.argtypes = [ctypes.POINTER(P), I, I, I, I, I, I, U]
         L.dsw_walk.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, P]
         L.dsw_walk_gru.argtypes = [P] * 15 + [I, I, P]
+        L.dsw_walk_rnn.argtypes = [P] * 15 + [I, I, P]
         L.dsw_status.argtypes = [P]
         L.dsw_query_plan.argtypes = [P, I, ctypes.POINTER(PlanInfo)]
         L.dsw_destroy.argtypes = [P]
@@ -107,7 +109,7 @@ def lib():
         L.dsw_set_seed.argtypes = [P, ctypes.c_ulonglong, I]
         L.dsw_round_counter.argtypes = [P, ctypes.POINTER(ctypes.c_uint)]
         L.dsw_set_trace.argtypes = [P, P, ctypes.c_longlong]
-        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_status",
+        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn", "dsw_status",
                   "dsw_query_plan", "dsw_destroy", "dsw_set_seed", "dsw_round_counter", "dsw_set_trace"):
             getattr(L, f).restype = I
         _lib = L
@@ -235,14 +237,26 @@ class Walker:
         cell = (Wih bf16 [3r,r], Whh bf16 [3r,r], bih f32 [3r], bhh f32 [3r]); h0 f32 [r];
         other tensors as walk().  Returns (tokens [B,gamma], logits or None,
         states f32 [gamma, r] or None)."""
+        return self._walk_cell(3, "dsw_walk_gru", W1, W2, cell, h0, base, anchor, T, uniforms, tokens,
+                               logits, states, want_logits, want_states, stream)
+
+    def walk_rnn(self, W1, W2, cell, h0, base, anchor, T, uniforms=None, tokens=None, logits=None,
+                 states=None, want_logits=False, want_states=False, stream=None):
+        """One round of the RNN serial head (handle made with FLAG_RNN; one request).
+        cell = (Wih bf16 [r,r], Whh bf16 [r,r], bih f32 [r], bhh f32 [r]); as walk_gru otherwise."""
+        return self._walk_cell(1, "dsw_walk_rnn", W1, W2, cell, h0, base, anchor, T, uniforms, tokens,
+                               logits, states, want_logits, want_states, stream)
+
+    def _walk_cell(self, gates, fname, W1, W2, cell, h0, base, anchor, T, uniforms, tokens, logits,
+                   states, want_logits, want_states, stream):
         import torch
         dev = torch.device("cuda", self.device)
         B, gamma, V = (int(x) for x in base.shape)
         r = self.r
         Wih, Whh, bih, bhh = cell
         need = [(W1, torch.bfloat16, (self.V, r), "W1"), (W2, torch.bfloat16, (self.V, r), "W2"),
-                (Wih, torch.bfloat16, (3 * r, r), "Wih"), (Whh, torch.bfloat16, (3 * r, r), "Whh"),
-                (bih, torch.float32, (3 * r,), "bih"), (bhh, torch.float32, (3 * r,), "bhh"),
+                (Wih, torch.bfloat16, (gates * r, r), "Wih"), (Whh, torch.bfloat16, (gates * r, r), "Whh"),
+                (bih, torch.float32, (gates * r,), "bih"), (bhh, torch.float32, (gates * r,), "bhh"),
                 (h0, torch.float32, (r,), "h0"), (base, torch.bfloat16, (B, gamma, self.V), "base"),
                 (anchor, torch.int32, (B,), "anchor"), (T, torch.float32, (B,), "T")]
         if uniforms is not None:
@@ -263,10 +277,10 @@ class Walker:
                 raise ValueError(f"{name}: want {dt} {shape} contiguous on {dev}, got "
                                  f"{t.dtype} {tuple(t.shape)} on {t.device}")
         ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
-        rc = lib().dsw_walk_gru(self._h, ptr(W1), ptr(W2), ptr(Wih), ptr(Whh), ptr(bih), ptr(bhh), ptr(h0),
-                                ptr(base), ptr(anchor), ptr(T), ptr(uniforms), ptr(tokens), ptr(logits),
-                                ptr(states), B, gamma, _stream_handle(torch, dev, stream))
-        _check(rc, "dsw_walk_gru")
+        rc = getattr(lib(), fname)(self._h, ptr(W1), ptr(W2), ptr(Wih), ptr(Whh), ptr(bih), ptr(bhh), ptr(h0),
+                                   ptr(base), ptr(anchor), ptr(T), ptr(uniforms), ptr(tokens), ptr(logits),
+                                   ptr(states), B, gamma, _stream_handle(torch, dev, stream))
+        _check(rc, fname)
         return tokens, logits, states
 
 

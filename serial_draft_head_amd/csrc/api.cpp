@@ -21,16 +21,22 @@ extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max
 extern "C" const void* dsw_internal_mfma_kernel_b4_gumbel(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16_gumbel(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel_gumbel(int batch_tile, int reg_tiles, int max_tiles);
-// the one-request kernels for the GRU serial head
+// the one-request kernels for the GRU and RNN serial heads
 extern "C" const void* dsw_internal_mfma_kernel_b1_gru(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b1_rnn(int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs (with Gumbel-max sampling when `gumbel`), or
 // nullptr.  The planner never gives a Gumbel-max handle the batched kernel.
-const void* kernel_for(const dsw_plan_info& pl, bool gumbel, bool gru) {
-    if (gru)  // the planner gives the GRU head only the one-request MFMA engine
+// The head a handle's flags select: 0 the Markov head, 1 the GRU head, 2 the RNN head.
+int cell_of(unsigned flags) { return (flags & DSW_FLAG_GRU) ? 1 : ((flags & DSW_FLAG_RNN) ? 2 : 0); }
+
+// cell: 0 the Markov head, 1 the GRU head, 2 the RNN head
+const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell) {
+    if (cell)  // the planner gives the recurrent heads only the one-request MFMA engine
         return pl.engine == DSW_ENGINE_MFMA && pl.batch_tile == 1 && pl.w2_dtype == DSW_BF16
-                   ? dsw_internal_mfma_kernel_b1_gru(pl.reg_tiles, pl.max_tiles)
+                   ? (cell == 1 ? dsw_internal_mfma_kernel_b1_gru : dsw_internal_mfma_kernel_b1_rnn)(
+                         pl.reg_tiles, pl.max_tiles)
                    : nullptr;
     if (pl.batch_tile == dsw::kMaxBatch)
         return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
@@ -199,8 +205,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         const int gm = (i % n_g) == 0 ? gamma_max : 3;
         dsw_plan_info pl;
         int prc = dsw_plan_compute(&dev, V, r, gm, B, w2_dtype, flags, &pl);
-        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0,
-                                                    (flags & DSW_FLAG_GRU) != 0)
+        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0, cell_of(flags))
                                         : nullptr;
         hipFuncAttributes attr;
         int per_cu = 0;
@@ -231,7 +236,7 @@ extern "C" int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out) {
 }
 
 namespace {
-// The GRU head's extra arguments (dsw_walk_gru).
+// A recurrent head's extra arguments (dsw_walk_gru, dsw_walk_rnn).
 struct GruArgs {
     const uint16_t* wih;
     const uint16_t* whh;
@@ -256,7 +261,7 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     dsw_plan_info plan;
     int rc = dsw_plan_compute(&h->dev, h->V, h->r, gamma, B, h->dtype, h->flags, &plan);
     if (rc) return rc;
-    const void* fn = kernel_for(plan, (h->flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr);
+    const void* fn = kernel_for(plan, (h->flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr ? cell_of(h->flags) : 0);
     if (!fn) return DSW_ERR_PLAN;
 
     DeviceGuard g(h->device);
@@ -333,7 +338,7 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
                         const void* base, const int32_t* anchor, const float* T,
                         const float* uniforms, int32_t* tokens, void* logits, int B, int gamma,
                         void* stream) {
-    if (h && (h->flags & DSW_FLAG_GRU)) return DSW_ERR_ARG;  // dsw_walk_gru serves these handles
+    if (h && cell_of(h->flags)) return DSW_ERR_ARG;  // dsw_walk_gru / dsw_walk_rnn serve these handles
     return walk_impl(h, W1, W2, w2_scale, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, nullptr);
 }
 
@@ -342,7 +347,18 @@ extern "C" int dsw_walk_gru(dsw_handle_t h, const void* W1, const void* W2, cons
                             const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
                             void* logits, float* states, int B, int gamma, void* stream) {
     if (!h) return DSW_ERR_NULL;
-    if (!(h->flags & DSW_FLAG_GRU)) return DSW_ERR_ARG;
+    if (cell_of(h->flags) != 1) return DSW_ERR_ARG;
+    if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
+    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states};
+    return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
+}
+
+extern "C" int dsw_walk_rnn(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
+                            const float* bih, const float* bhh, const float* h0, const void* base,
+                            const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
+                            void* logits, float* states, int B, int gamma, void* stream) {
+    if (!h) return DSW_ERR_NULL;
+    if (cell_of(h->flags) != 2) return DSW_ERR_ARG;
     if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
     const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states};
     return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);

@@ -59,14 +59,19 @@ static const int kStreamShape[2] = {0, 16};
 static int mfma_tile_for(int B, bool i8) { return (B <= 1 && !i8) ? 1 : (B <= 4 ? 4 : 16); }
 // Upper bound of the MFMA kernel's static LDS for (batch tile, tiles per
 // wave, int8 rows with their fp32 scales).
-// The GRU head keeps its state (r floats) and its cell rows (6 bf16 rows and 6
-// biases per owned state element, and the recurrent pre-activations of the
-// coming step) in LDS.
-static int gru_lds(bool gru) { return gru ? kRank * 4 + kGruMaxPerWg * 6 * (kRank * 2 + 4) + kGruMaxPerWg * 3 * 4 : 0; }
-static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum, bool gru) {
+// A recurrent head keeps its state (r floats) and its cell rows in LDS: per
+// owned state element 2 x gates bf16 rows and biases, and the gates' recurrent
+// pre-activations of the coming step (GRU: 3 gates, RNN: 1).
+static int cell_lds(int gates) {
+    return gates ? kRank * 4 + kCellMaxPerWg * 2 * gates * (kRank * 2 + 4) + kCellMaxPerWg * gates * 4 : 0;
+}
+static int cell_gates(unsigned flags) {
+    return (flags & DSW_FLAG_GRU) ? 3 : ((flags & DSW_FLAG_RNN) ? 1 : 0);
+}
+static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum, int gates) {
     const int rpad = max_tiles * 4 * kTileRows;
     return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0) +
-           kTraceLds + gumbel_noise_lds(nb, rpad, gum) + gru_lds(gru);
+           kTraceLds + gumbel_noise_lds(nb, rpad, gum) + cell_lds(gates);
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -111,8 +116,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
     const int nb = mfma_tile_for(B, i8);
-    const int lds_static = mfma_static_lds(nb, max_t, i8, (flags & DSW_FLAG_GUMBEL) != 0,
-                                           (flags & DSW_FLAG_GRU) != 0);
+    const int lds_static = mfma_static_lds(nb, max_t, i8, (flags & DSW_FLAG_GUMBEL) != 0, cell_gates(flags));
     int avail = dev->max_lds_per_block - lds_static;
     if (avail < 0) return DSW_ERR_PLAN;
 
@@ -329,19 +333,20 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     // Gumbel-max is the small-batch sampler: the all-to-all kernel, up to 16 requests
     const bool gumbel = (flags & DSW_FLAG_GUMBEL) != 0;
     if (batched && gumbel) return DSW_ERR_ARG;
-    // the GRU head: one bf16 request on the one-request MFMA engine, and a grid
-    // of at least r / kGruMaxPerWg workgroups to hold the state
-    const bool gru = (flags & DSW_FLAG_GRU) != 0;
-    if (gru) {
+    // the recurrent heads: one bf16 request on the one-request MFMA engine, and
+    // a grid of at least r / kCellMaxPerWg workgroups to hold the state
+    const bool cell = (flags & (DSW_FLAG_GRU | DSW_FLAG_RNN)) != 0;
+    if ((flags & DSW_FLAG_GRU) && (flags & DSW_FLAG_RNN)) return DSW_ERR_ARG;
+    if (cell) {
         if (B > 1 || batched || gumbel || (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
         if (i8) return DSW_ERR_DTYPE;
-        if (grid * kGruMaxPerWg < kRank) return DSW_ERR_PLAN;
+        if (grid * kCellMaxPerWg < kRank) return DSW_ERR_PLAN;
     }
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
     // one bf16 request: the MFMA engine's step is ~1 us shorter, but its shard
     // load ~3 us longer (measured at V = 151,936), so walks of up to 3 steps
     // take the VALU engine
-    if (!forced) valu = B <= 1 && (i8 || gamma <= 3) && !gru;
+    if (!forced) valu = B <= 1 && (i8 || gamma <= 3) && !cell;
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);

@@ -118,14 +118,15 @@ __device__ __forceinline__ uint4 as_bf16x8(const uint2& q) {
 
 // GUM = 1: sampled requests draw by Gumbel-max instead of the inverse CDF (a
 // separate instantiation, so that the default kernels carry none of its code).
-// CELL = 1: the GRU serial head ("Keeping the Draft Walk on Chip", section
-// "Beyond DSpark: other serial heads": the same walk with a recurrent state
+// CELL = 1, 2: recurrent serial heads ("Keeping the Draft Walk on Chip",
+// section "Beyond DSpark: other serial heads": the same walk with a state
 // update; the state is spread across the workgroups and gathered once per
-// step).  The state h goes through the standard GRU cell (Cho et al. 2014;
-// gates r, z, n; the reset gate scales Whn h + bhn) fed with x = W1[prev], and
-// the vocabulary matrix reads bf16(h).  Workgroup c updates state elements
-// c, c + G, ... (one per wave), posts them with the step's epoch, and every
-// workgroup gathers all r of them before its GEMV.  One request.
+// step).  The state h goes through a standard cell fed with x = W1[prev] --
+// CELL = 1 the GRU (Cho et al. 2014; gates r, z, n; the reset gate scales
+// Whn h + bhn), CELL = 2 the tanh RNN, h' = tanh(Wih x + bih + Whh h + bhh) --
+// and the vocabulary matrix reads bf16(h).  Workgroup c updates state
+// elements c, c + G, ... (one per wave), posts them with the step's epoch, and
+// every workgroup gathers all r of them before its GEMV.  One request.
 template <int ENGINE, int A, int M, int NB, int DT = 0, int GUM = 0, int CELL = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
@@ -142,9 +143,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                   "MFMA shape");
     static_assert(!kOne || !kI8, "one-request MFMA engine: bf16 rows");
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
+    constexpr bool kCell = CELL != 0;                           // a recurrent head
     constexpr bool kGru = CELL == 1;
-    static_assert(!kGru || (kOne && GUM == 0), "GRU head: the one-request MFMA engine");
-    static_assert(!kGru || kBlock == kRank, "GRU head: one state element per thread in the gather");
+    constexpr int kGates = CELL == 1 ? 3 : 1;                    // cell rows per input, per element
+    static_assert(CELL >= 0 && CELL <= 2, "cell");
+    static_assert(!kCell || (kOne && GUM == 0), "recurrent heads: the one-request MFMA engine");
+    static_assert(!kCell || kBlock == kRank, "recurrent heads: one state element per thread in the gather");
     constexpr int RPAD = kMfma ? M * 4 * kTileRows : kMaxSlots * kBlock;  // rows per shard, bound
     constexpr int CHMAX = (RPAD + kBlock - 1) / kBlock;                    // scan rows per thread
     constexpr int US = kRowChunks + 1;                                     // padded u row (uint4)
@@ -160,14 +164,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // coming step, drawn while the previous rendezvous is in flight
     constexpr bool kPreG = GUM != 0 && NB <= 4;
     __shared__ float s_G[kPreG ? NB * RPAD : 1];
-    // GRU head: the state h (r floats), and this workgroup's rows of the cell
-    // (per owned element: Wir, Wiz, Win, Whr, Whz, Whn) with their biases
-    __shared__ float s_h[kGru ? kRank : 1];
-    __shared__ uint16_t s_cw[kGru ? kGruMaxPerWg * 6 * kRank : 1];
-    __shared__ float s_cb[kGru ? kGruMaxPerWg * 6 : 1];
-    // GRU head: Whh h + bhh of the owned elements for the coming step, formed
-    // while the previous step's keys travel
-    __shared__ float s_gh[kGru ? kGruMaxPerWg * 3 : 1];
+    // recurrent heads: the state h (r floats), and this workgroup's rows of the
+    // cell (per owned element: the kGates rows of Wih, then those of Whh --
+    // GRU Wir, Wiz, Win, Whr, Whz, Whn) with their biases
+    __shared__ float s_h[kCell ? kRank : 1];
+    __shared__ uint16_t s_cw[kCell ? kCellMaxPerWg * 2 * kGates * kRank : 1];
+    __shared__ float s_cb[kCell ? kCellMaxPerWg * 2 * kGates : 1];
+    // recurrent heads: Whh h + bhh of the owned elements for the coming step,
+    // formed while the previous step's keys travel
+    __shared__ float s_gh[kCell ? kCellMaxPerWg * kGates : 1];
     __shared__ uint32_t s_wbest[4][NB];
     __shared__ unsigned long long s_red64[4][NB];
     __shared__ float s_redf[4][NB];
@@ -246,22 +251,23 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         s_T[t] = temp;
     }
     for (int j = t; j < NB * US; j += kBlock) s_u[j] = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (kGru) {
-        // h0, and the cell rows of state elements c + i G (i < kGruMaxPerWg)
+    if constexpr (kCell) {
+        // h0, and the cell rows of state elements c + i G (i < kCellMaxPerWg)
+        constexpr int kRows = 2 * kGates;
         for (int m = t; m < kRank; m += kBlock) s_h[m] = p.h0[m];
-        for (int e = t; e < kGruMaxPerWg * 6 * kRank; e += kBlock) {
-            const int i = e / (6 * kRank), q = (e / kRank) % 6, m = e % kRank;
+        for (int e = t; e < kCellMaxPerWg * kRows * kRank; e += kBlock) {
+            const int i = e / (kRows * kRank), q = (e / kRank) % kRows, m = e % kRank;
             const int j = c + i * G;
             uint16_t wv = 0;
             if (j < kRank) {
-                const uint16_t* W = q < 3 ? p.gru_wih : p.gru_whh;
-                wv = W[(size_t)((q % 3) * kRank + j) * kRank + m];
+                const uint16_t* W = q < kGates ? p.gru_wih : p.gru_whh;
+                wv = W[(size_t)((q % kGates) * kRank + j) * kRank + m];
             }
             s_cw[e] = wv;
         }
-        if (t < kGruMaxPerWg * 6) {
-            const int i = t / 6, q = t % 6, j = c + i * G;
-            s_cb[t] = j < kRank ? (q < 3 ? p.gru_bih : p.gru_bhh)[(q % 3) * kRank + j] : 0.0f;
+        if (t < kCellMaxPerWg * kRows) {
+            const int i = t / kRows, q = t % kRows, j = c + i * G;
+            s_cb[t] = j < kRank ? (q < kGates ? p.gru_bih : p.gru_bhh)[(q % kGates) * kRank + j] : 0.0f;
         }
     }
 
@@ -427,30 +433,32 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         if (any_samp && gamma > 0) draw_noise(0);  // read after the first step's barriers
     }
 
-    // GRU head: wave i forms Whh h + bhh for its element c + i G from the state
-    // in s_h (three dot products of r terms), for the cell of the coming step
+    // recurrent heads: wave i forms Whh h + bhh for its element c + i G from
+    // the state in s_h (kGates dot products of r terms), for the coming step
     constexpr int kCellUnroll = A <= 10 ? 4 : 1;  // the widest shapes have no registers to spare
-    auto gru_recurrent = [&]() {
+    auto cell_recurrent = [&]() {
         const int j = c + wave * G;
-        if (wave < kGruMaxPerWg && j < kRank) {
-            float acc[3] = {0.0f, 0.0f, 0.0f};
+        if (wave < kCellMaxPerWg && j < kRank) {
+            float acc[kGates];
+#pragma unroll
+            for (int q = 0; q < kGates; ++q) acc[q] = 0.0f;
 #pragma unroll kCellUnroll
             for (int mm = 0; mm < kRank / 64; ++mm) {
                 const int m = mm * 64 + lane;
                 const float hv = s_h[m];
 #pragma unroll
-                for (int q = 0; q < 3; ++q)
-                    acc[q] = fmaf(bf16_to_f32(s_cw[(wave * 6 + 3 + q) * kRank + m]), hv, acc[q]);
+                for (int q = 0; q < kGates; ++q)
+                    acc[q] = fmaf(bf16_to_f32(s_cw[(wave * 2 * kGates + kGates + q) * kRank + m]), hv, acc[q]);
             }
 #pragma unroll
-            for (int q = 0; q < 3; ++q) {
+            for (int q = 0; q < kGates; ++q) {
                 const float tot = __shfl(wave_incl_scan_dpp(acc[q]), 63);
-                if (lane == 0) s_gh[wave * 3 + q] = tot + s_cb[wave * 6 + 3 + q];
+                if (lane == 0) s_gh[wave * kGates + q] = tot + s_cb[wave * 2 * kGates + kGates + q];
             }
         }
     };
-    if constexpr (kGru) {
-        if (gamma > 0) gru_recurrent();  // from h0; read by the same wave in step 0
+    if constexpr (kCell) {
+        if (gamma > 0) cell_recurrent();  // from h0; read by the same wave in step 0
     }
 
     // token of request b at the end of the current step (after the winner
@@ -495,30 +503,37 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             s_u[b * US + ch] = W1[(size_t)prev * kRowChunks + ch];
         }
         __syncthreads();
-        if constexpr (kGru) {
-            // ---- GRU cell: wave i updates state element c + i G ---------------
+        if constexpr (kCell) {
+            // ---- the cell: wave i updates state element c + i G ---------------
             const uint16_t* s_x = reinterpret_cast<const uint16_t*>(s_u);  // x = W1[prev]
             const int j = c + wave * G;
             unsigned long long* box = mail_q + (size_t)c * kMailWords;
-            if (wave < kGruMaxPerWg && j < kRank) {
+            if (wave < kCellMaxPerWg && j < kRank) {
                 // Wih x + bih (the recurrent half was formed ahead, in s_gh)
-                float acc[3] = {0.0f, 0.0f, 0.0f};
+                float acc[kGates];
+#pragma unroll
+                for (int q = 0; q < kGates; ++q) acc[q] = 0.0f;
 #pragma unroll kCellUnroll
                 for (int mm = 0; mm < kRank / 64; ++mm) {
                     const int m = mm * 64 + lane;
                     const float xv = bf16_to_f32(s_x[m]);
 #pragma unroll
-                    for (int q = 0; q < 3; ++q)
-                        acc[q] = fmaf(bf16_to_f32(s_cw[(wave * 6 + q) * kRank + m]), xv, acc[q]);
+                    for (int q = 0; q < kGates; ++q)
+                        acc[q] = fmaf(bf16_to_f32(s_cw[(wave * 2 * kGates + q) * kRank + m]), xv, acc[q]);
                 }
 #pragma unroll
-                for (int q = 0; q < 3; ++q) acc[q] = __shfl(wave_incl_scan_dpp(acc[q]), 63);
-                const float* cb = s_cb + wave * 6;
-                const float* gh = s_gh + wave * 3;
-                const float rg = 1.0f / (1.0f + expf(-((acc[0] + cb[0]) + gh[0])));
-                const float zg = 1.0f / (1.0f + expf(-((acc[1] + cb[1]) + gh[1])));
-                const float ng = tanhf((acc[2] + cb[2]) + rg * gh[2]);
-                const float hn = (1.0f - zg) * ng + zg * s_h[j];
+                for (int q = 0; q < kGates; ++q) acc[q] = __shfl(wave_incl_scan_dpp(acc[q]), 63);
+                const float* cb = s_cb + wave * 2 * kGates;
+                const float* gh = s_gh + wave * kGates;
+                float hn;
+                if constexpr (kGru) {
+                    const float rg = 1.0f / (1.0f + expf(-((acc[0] + cb[0]) + gh[0])));
+                    const float zg = 1.0f / (1.0f + expf(-((acc[1] + cb[1]) + gh[1])));
+                    const float ng = tanhf((acc[2] + cb[2]) + rg * gh[2]);
+                    hn = (1.0f - zg) * ng + zg * s_h[j];
+                } else {
+                    hn = tanhf((acc[0] + cb[0]) + gh[0]);
+                }
                 if (lane == 0) {
                     st_agent64(&box[1 + wave], ((unsigned long long)__float_as_uint(hn) << 32) | epoch);
                     if (p.states != nullptr) p.states[(size_t)k * kRank + j] = hn;
@@ -922,9 +937,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             // step's noise was last read before the barrier ahead of the post)
             if (any_samp && k + 1 < gamma) draw_noise(k + 1);
         }
-        if constexpr (kGru) {
+        if constexpr (kCell) {
             // the next step's recurrent half from this step's state, while the keys travel
-            if (k + 1 < gamma) gru_recurrent();
+            if (k + 1 < gamma) cell_recurrent();
         }
         unsigned long long kw[NB];
         uint32_t sw[NB];  // the second word's payload: exp-sum bits, or ~id (Gumbel-max)

@@ -24,7 +24,7 @@ constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 // s.  Nothing needs clearing between steps, launches or graph replays.
 constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 16 exp-sum words
 constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
-constexpr int kGruMaxPerWg = 4;    // GRU head: state elements per workgroup (one per wave; grid >= 64)
+constexpr int kCellMaxPerWg = 4;   // recurrent heads: state elements per workgroup (one per wave; grid >= 64)
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
 constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests

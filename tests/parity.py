@@ -208,3 +208,28 @@ def check_gru_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states):
         worst = max(worst, float(err.max()))
         worst_ratio = max(worst_ratio, float((err / bound).max()))
     return gamma, worst, worst_ratio
+
+
+def check_rnn_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states):
+    """As check_gru_states for the tanh RNN cell: the error of the fp32
+    pre-activation (two dot products and biases, g_(r+4) sum |w v|) passes
+    through tanh' <= 1; tanh and the adds add 4 ulps of the result and 2 of the
+    pre-activation.  Returns (steps checked, largest error, largest error / bound)."""
+    Wih, Whh, bih, bhh = cell
+    Wi, Wh = oracle.bf16_bits_to_f64(Wih), oracle.bf16_bits_to_f64(Whh)
+    r = Wi.shape[1]
+    gam = (r + 4) * F32_EPS / (1 - (r + 4) * F32_EPS)
+    worst, worst_ratio = 0.0, 0.0
+    for k in range(gpu_states.shape[0]):
+        prev = int(anchor) if k == 0 else int(gpu_tokens[k - 1])
+        x = oracle.bf16_bits_to_f64(W1_bits[prev])
+        h = h0.astype(np.float64) if k == 0 else gpu_states[k - 1].astype(np.float64)
+        want = oracle.rnn_cell(x, h, Wih, Whh, bih, bhh)
+        pre = Wi @ x + bih + Wh @ h + bhh
+        E = gam * (np.abs(Wi) @ np.abs(x) + np.abs(bih) + np.abs(Wh) @ np.abs(h) + np.abs(bhh))
+        bound = 2 * (E + 4 * F32_EPS * np.abs(want) + 2 * F32_EPS * np.abs(pre)) + 1e-9
+        err = np.abs(gpu_states[k].astype(np.float64) - want)
+        assert np.all(err <= bound), f"k={k}: state error {err.max()} above its bound at {np.argmax(err - bound)}"
+        worst = max(worst, float(err.max()))
+        worst_ratio = max(worst_ratio, float((err / bound).max()))
+    return gpu_states.shape[0], worst, worst_ratio

@@ -60,6 +60,7 @@ def test_null_and_argument_errors_without_a_device(dsw):
     assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 0, 1, 0, 0) == -3      # gamma
     assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 7, 0, 0, 0) == -2      # batch
     assert L.dsw_walk_gru(None, *([None] * 14), 1, 1, None) == -1
+    assert L.dsw_walk_rnn(None, *([None] * 14), 1, 1, None) == -1
 
 
 def fake_device(dsw, cus=256, lds_cu=160 * 1024, lds_blk=160 * 1024):
@@ -223,6 +224,13 @@ def test_planner_gru_head(dsw):
         with pytest.raises(dsw.DswError) as e:
             dsw.plan(d, 151_936, 7, B, w2_dtype=dt, flags=flags)
         assert e.value.code == code
+    # the RNN head: the same plan, one gate instead of three in LDS
+    n = dsw.plan(d, 151_936, 7, 1, flags=dsw.FLAG_RNN)
+    assert (n.engine, n.batch_tile, n.reg_tiles) == (1, 1, 10)
+    assert n.static_lds_bytes == dsw.plan(d, 151_936, 16, 1).static_lds_bytes + 256 * 4 + 4 * 2 * (512 + 4) + 4 * 4
+    with pytest.raises(dsw.DswError) as e:
+        dsw.plan(d, 151_936, 7, 1, flags=R | dsw.FLAG_RNN)
+    assert e.value.code == -11
     # the state is spread over at most 4 elements per workgroup: 64 CUs at least
     assert dsw.plan(fake_device(dsw, cus=64), 32_000, 7, 1, flags=R).grid == 64
     with pytest.raises(dsw.DswError) as e:

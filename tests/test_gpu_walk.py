@@ -504,6 +504,45 @@ def test_gru_head(dsw, V, gamma, temps):
     walker.close()
 
 
+RNN_CASES = [(4_097, 5, "greedy"), (32_000, 7, "cycle"), (151_936, 16, "greedy")]
+
+
+@pytest.mark.parametrize("V,gamma,temps", RNN_CASES)
+def test_rnn_head(dsw, V, gamma, temps):
+    import oracle
+    say(f"rnn head V={V} gamma={gamma} {temps}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    cell = workloads.rnn_cell_weights(1)
+    celld = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+             torch.from_numpy(cell[3]).to(DEV))
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_RNN)
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 600 + rnd, B=1, gamma=gamma, V=V, temps=temps)
+        h0 = workloads.gru_h0(2, rnd, 1)
+        base, anchor, T, uni = round_dev(inp)
+        tokens, logits, states = walker.walk_rnn(W1d, W2d, celld, torch.from_numpy(h0[0]).to(DEV), base,
+                                                 anchor, T, uni, want_logits=True, want_states=True)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        st = states.cpu().numpy()
+        n, worst, ratio = parity.check_rnn_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+        ub = oracle.rne_bf16(st.astype(np.float64))[1][None]
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 latents=ub)
+        say(rnd, f"states: {n} steps, largest error {worst:.3g} ({ratio:.3f} of its bound)", rep)
+    # a GRU handle refuses the RNN call
+    g = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_GRU)
+    with pytest.raises(dsw.DswError) as e:
+        g.walk_rnn(W1d, W2d, celld, torch.zeros(256, device=DEV), base, anchor, T, uni)
+    assert e.value.code == -11
+    g.close()
+    walker.close()
+
+
 def test_gru_head_argument_errors(dsw):
     V = 4_096
     W1, W2 = workloads.weights(2, V=V)
