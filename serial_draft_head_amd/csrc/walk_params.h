@@ -102,9 +102,10 @@ struct WalkParams {
     int single_round;        // 1: logit = bf16(base + fp32 dot), rounded once
     int seeded;              // 1: uniforms == NULL draws them on the device from seed
     unsigned long long seed; // key of the device-drawn uniforms and of the Gumbel noise
-    // GRU serial head (kernels with CELL = 1; one request): the cell's weights
-    // [3r][r] bf16 and biases [3r] f32 (gates r, z, n), the initial state [r]
-    // f32, and an optional [gamma][r] f32 output of every step's state
+    // Recurrent serial heads (one request): the cell's weights [g*r][r] bf16
+    // and biases [g*r] f32 -- g = 3 for the GRU (CELL = 1; gates r, z, n),
+    // g = 1 for the tanh RNN (CELL = 2) -- the initial state [r] f32, and an
+    // optional [gamma][r] f32 output of every step's state
     const uint16_t* gru_wih;
     const uint16_t* gru_whh;
     const float* gru_bih;
