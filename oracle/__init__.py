@@ -18,7 +18,10 @@ vLLM PR #64442, section "Details", or (the ``gumbel`` mode) Gumbel-max from
 counter-based noise, the pages' small-batch sampler (section "The idea: make
 the walk resident").  ``walk_gru`` is the GRU serial head (section "Beyond
 DSpark: other serial heads"): the state goes through a standard GRU cell fed
-with ``W1[prev]`` and the vocabulary matrix reads ``bf16(h)``.
+with ``W1[prev]`` and the vocabulary matrix reads ``bf16(h)``; ``walk_rnn``
+the tanh RNN head and ``walk_gated`` DSpark's gated head (read as a convex gate
+between the state and ``W1[prev]``, the gate computed from the state by one
+int8 matrix).
 """
 from __future__ import annotations
 
@@ -81,6 +84,10 @@ def _load():
     lib.oracle_rnn_cell.argtypes = [i, P, P, P, P, P, P, P]
     lib.oracle_walk_rnn.restype = i
     lib.oracle_walk_rnn.argtypes = [i, i, i, i] + [P] * 18 + [i, ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_gated_cell.restype = None
+    lib.oracle_gated_cell.argtypes = [i, P, P, P, P, P, P]
+    lib.oracle_walk_gated.restype = i
+    lib.oracle_walk_gated.argtypes = [i, i, i, i] + [P] * 17 + [i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_threads.restype = i
     lib.oracle_philox4x32_10.argtypes = [P, P, P]
     lib.oracle_philox4x32_10.restype = None
@@ -258,6 +265,48 @@ def rnn_cell(x, h, Wih_bits, Whh_bits, bih, bhh):
     _load().oracle_rnn_cell(r, _ptr(x), _ptr(h), _ptr(Wih_bits), _ptr(Whh_bits), _ptr(bih), _ptr(bhh),
                             _ptr(out))
     return out
+
+
+def gated_cell(x, h, Gq, gs, gb):
+    """One step of the gated head in binary64: x, h [r] -> g h + (1 - g) x with
+    g = sigmoid(gs * (Gq @ h) + gb); Gq [r, r] int8 codes, gs, gb [r] f32."""
+    x = _c(x, np.float64)
+    h = _c(h, np.float64)
+    r = x.shape[0]
+    Gq, gs, gb = _c(Gq, np.int8), _c(gs, np.float32), _c(gb, np.float32)
+    assert Gq.shape == (r, r) and gs.shape == (r,) and gb.shape == (r,) and h.shape == (r,)
+    out = np.empty(r, dtype=np.float64)
+    _load().oracle_gated_cell(r, _ptr(x), _ptr(h), _ptr(Gq), _ptr(gs), _ptr(gb), _ptr(out))
+    return out
+
+
+def walk_gated(W1_bits, base_bits, anchor, T, gate, h0, uniforms=None, W2_bits=None, Q=None, scale=None,
+               forced=None, forced_h=None, want_logits=True, single_round=False, gumbel=False, seed=0,
+               round_counter=0):
+    """The gated head's walk.  gate = (Gq [r,r] int8, gs [r] f32, gb [r] f32); the
+    other arguments and the result as walk_gru."""
+    W1_bits = _c(W1_bits, np.uint16)
+    W2_bits, Q, scale = _c(W2_bits, np.uint16), _c(Q, np.int8), _c(scale, np.float32)
+    Gq, gs, gb = _c(gate[0], np.int8), _c(gate[1], np.float32), _c(gate[2], np.float32)
+    h0 = _c(h0, np.float32)
+    base_bits = _c(base_bits, np.uint16)
+    anchor, T = _c(anchor, np.int32), _c(T, np.float32)
+    uniforms, forced, forced_h = _c(uniforms, np.float32), _c(forced, np.int32), _c(forced_h, np.float32)
+    V, r = W1_bits.shape
+    B, gamma = base_bits.shape[0], base_bits.shape[1]
+    assert base_bits.shape[2] == V and h0.shape == (B, r) and Gq.shape == (r, r)
+    tokens = np.empty((B, gamma), dtype=np.int32)
+    logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
+    states = np.empty((B, gamma, r), dtype=np.float64)
+    mode = (SINGLE_ROUND if single_round else 0) | (GUMBEL if gumbel else 0)
+    rc = _load().oracle_walk_gated(V, r, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+                                   _ptr(Gq), _ptr(gs), _ptr(gb), _ptr(h0), _ptr(base_bits),
+                                   _ptr(anchor), _ptr(T), _ptr(uniforms), _ptr(forced), _ptr(forced_h),
+                                   _ptr(tokens), _ptr(logits), _ptr(states), mode,
+                                   int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF)
+    if rc != 0:
+        raise RuntimeError(f"oracle_walk_gated failed with {rc}")
+    return tokens, logits, states
 
 
 def walk_rnn(W1_bits, base_bits, anchor, T, cell, h0, **kw):

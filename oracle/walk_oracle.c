@@ -57,6 +57,16 @@
  * RNN head (oracle_rnn_cell, oracle_walk_rnn; DSpark's own RNN head, read as
  * the standard tanh RNN cell): h' = tanh(Wih x + bih + Whh h + bhh), otherwise
  * the same walk.
+ * Gated head (oracle_gated_cell, oracle_walk_gated; DSpark's own gated head).
+ * The pages fix only its shape: one r x r matrix, small enough in int8 for
+ * every CTA to apply it itself, so the update needs no state exchange.  They
+ * give no equation; the reading taken here is the plainest single-matrix gated
+ * update, a convex gate between the carried state and the new token's row:
+ *   g  = sigmoid(s * (Gq h) + b)       Gq int8 codes [r][r], s, b per row
+ *   h' = g * h + (1 - g) * x           x = W1[prev]
+ * and the vocabulary matrix reads u = bf16(h') as for the other heads.  With
+ * b -> -inf the gate closes (g = 0) and the walk is the Markov walk; with
+ * b -> +inf the state never moves.
  *
  * Parallelism: OpenMP over vocabulary rows inside one GEMV.  Each row's sum
  * is formed by one thread in a fixed order, so results do not depend on the
@@ -463,9 +473,26 @@ void oracle_rnn_cell(int r, const double* x, const double* h, const uint16_t* Wi
 }
 
 /*
+ * One step of the gated head in binary64 (see the header): per element j,
+ * g_j = sigmoid(s_j * sum_i Gq[j][i] h_i + b_j), h'_j = g_j h_j + (1 - g_j) x_j.
+ * Gq: [r][r] int8 codes; s, b: [r] f32.
+ */
+void oracle_gated_cell(int r, const double* x, const double* h, const int8_t* Gq, const float* s,
+                       const float* b, double* out) {
+    for (int j = 0; j < r; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < r; ++i) acc += (double)Gq[(size_t)j * r + i] * h[i];
+        const double g = 1.0 / (1.0 + exp(-((double)s[j] * acc + (double)b[j])));
+        out[j] = g * h[j] + (1.0 - g) * x[j];
+    }
+}
+
+/*
  * A recurrent head's walk for B independent requests (free running, or teacher
- * forced); kind 1 = GRU, 2 = tanh RNN.  Arguments as oracle_walk_ex, plus
+ * forced); kind 1 = GRU, 2 = tanh RNN, 3 = gated head.  Arguments as
+ * oracle_walk_ex, plus
  *   Wih, Whh, bih, bhh : the cell (see oracle_gru_cell, oracle_rnn_cell)
+ *   Gq, gs, gb : the gated head's matrix, row scales and biases (kind 3)
  *   h0       : [B][r] initial states (f32)
  *   forced_h : [B][gamma][r] f32 or NULL.  When given, step k > 0 of request b
  *              starts from forced_h[b][k-1] instead of the oracle's own state.
@@ -475,13 +502,15 @@ void oracle_rnn_cell(int r, const double* x, const double* h, const uint16_t* Wi
 static int walk_cell(int kind, int V, int r, int B, int gamma, const uint16_t* W1,
                      const uint16_t* W2, const int8_t* Q, const float* scale,
                      const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
+                     const int8_t* Gq, const float* gs, const float* gb,
                      const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
                      const float* uniforms, const int32_t* forced, const float* forced_h,
                      int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
                      uint32_t round) {
-    if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !Wih || !Whh || !bih || !bhh || !h0 || !base ||
-        !anchor || !T || !tokens || (!W2 && (!Q || !scale)))
+    if (V <= 0 || r <= 0 || B < 0 || gamma < 0 || !W1 || !h0 || !base || !anchor || !T || !tokens ||
+        (!W2 && (!Q || !scale)))
         return -1;
+    if (kind == 3 ? (!Gq || !gs || !gb) : (!Wih || !Whh || !bih || !bhh)) return -1;
     for (int b = 0; b < B; ++b) {
         if (T[b] != 0.0f && !uniforms && !(mode & ORACLE_GUMBEL)) return -1;
         if (anchor[b] < 0 || anchor[b] >= V) return -1;
@@ -503,7 +532,8 @@ static int walk_cell(int kind, int V, int r, int B, int gamma, const uint16_t* W
             if (prev < 0 || prev >= V) { rc = -1; break; }
             for (int i = 0; i < r; ++i) x[i] = bf16_value(W1[(size_t)prev * r + i]);
             if (kind == 1) oracle_gru_cell(r, x, h, Wih, Whh, bih, bhh, hn);
-            else oracle_rnn_cell(r, x, h, Wih, Whh, bih, bhh, hn);
+            else if (kind == 2) oracle_rnn_cell(r, x, h, Wih, Whh, bih, bhh, hn);
+            else oracle_gated_cell(r, x, h, Gq, gs, gb, hn);
             for (int i = 0; i < r; ++i) {
                 h[i] = hn[i];
                 ub[i] = oracle_bf16_bits(oracle_rne_bf16(hn[i]));
@@ -531,8 +561,8 @@ int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
                     const float* uniforms, const int32_t* forced, const float* forced_h,
                     int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
                     uint32_t round) {
-    return walk_cell(1, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, h0, base, anchor, T, uniforms,
-                     forced, forced_h, tokens, logits, states, mode, seed, round);
+    return walk_cell(1, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, h0, base, anchor,
+                     T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
 }
 
 /* The RNN head's walk: as oracle_walk_gru with the tanh RNN cell, Wih, Whh
@@ -544,6 +574,19 @@ int oracle_walk_rnn(int V, int r, int B, int gamma, const uint16_t* W1,
                     const float* uniforms, const int32_t* forced, const float* forced_h,
                     int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
                     uint32_t round) {
-    return walk_cell(2, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, h0, base, anchor, T, uniforms,
-                     forced, forced_h, tokens, logits, states, mode, seed, round);
+    return walk_cell(2, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, h0, base, anchor,
+                     T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
+}
+
+/* The gated head's walk: as oracle_walk_gru with the gated update, Gq [r][r]
+ * int8 codes, gs, gb [r] f32 (see oracle_gated_cell). */
+int oracle_walk_gated(int V, int r, int B, int gamma, const uint16_t* W1,
+                      const uint16_t* W2, const int8_t* Q, const float* scale,
+                      const int8_t* Gq, const float* gs, const float* gb,
+                      const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
+                      const float* uniforms, const int32_t* forced, const float* forced_h,
+                      int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
+                      uint32_t round) {
+    return walk_cell(3, V, r, B, gamma, W1, W2, Q, scale, NULL, NULL, NULL, NULL, Gq, gs, gb, h0, base, anchor,
+                     T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
 }

@@ -364,6 +364,99 @@ def test_rnn_walk_brute_force(oracle_mod, seed):
             prev = int(toks[b, k])
 
 
+# ---------------------------------------------------------------- gated head
+def test_hand_worked_gated(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_gated.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        r = c["r"]
+        out = oracle_mod.gated_cell(c["x"], c["h"], np.asarray(c["Gq"], np.int8).reshape(r, r),
+                                    np.asarray(c["gs"], np.float32), np.asarray(c["gb"], np.float32))
+        # s and b are f32: ln 3 rounds to f32 (relative error <= 2^-24), which moves h' by < 1e-7
+        assert np.allclose(out, c["out"], rtol=0, atol=1e-6), (c, out)
+
+
+def _mp_gated(x, h, Gq, gs, gb):
+    """The gated update in 50-digit arithmetic (mpmath), element by element."""
+    import mpmath
+    mpmath.mp.dps = 50
+    out = []
+    for j in range(len(x)):
+        acc = mpmath.fsum(mpmath.mpf(int(Gq[j, i])) * mpmath.mpf(float(h[i])) for i in range(len(x)))
+        g = 1 / (1 + mpmath.exp(-(mpmath.mpf(float(gs[j])) * acc + mpmath.mpf(float(gb[j])))))
+        out.append(float(g * mpmath.mpf(float(h[j])) + (1 - g) * mpmath.mpf(float(x[j]))))
+    return np.asarray(out)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_gated_walk_brute_force(oracle_mod, seed):
+    V, r, gamma, B = 12, 4, 3, 3
+    d = workloads.toy(seed + 950, V=V, r=r, B=B, gamma=gamma, w2_std=0.5, base_std=0.5)
+    gate = workloads.gated_weights(seed, r=r)
+    h0 = workloads.gru_h0(seed, 2, B, r=r)
+    toks, logits, states = oracle_mod.walk_gated(d["W1"], d["base"], d["anchor"], np.zeros(B, np.float32), gate,
+                                                 h0, W2_bits=d["W2"])
+    for b in range(B):
+        prev, h = int(d["anchor"][b]), h0[b].astype(np.float64)
+        for k in range(gamma):
+            h = _mp_gated(value_f64(d["W1"][prev]), h, *gate)
+            assert np.allclose(states[b, k], h, rtol=0, atol=1e-13)
+            u = [value(rne_bits(Fraction(float(v)))) for v in states[b, k]]
+            lb = bf.step_logits(d["W2"], u, d["base"][b, k])
+            assert logits[b, k].tolist() == lb
+            assert toks[b, k] == bf.argmax_lowest(lb)
+            prev = int(toks[b, k])
+
+
+def test_gated_walk_limits_and_invariants(oracle_mod):
+    V, r, B, gamma = 2000, 256, 2, 5
+    W1, W2 = workloads.weights(0, V=V)
+    inp = workloads.round_inputs(1, 4, B=B, gamma=gamma, V=V, temps="mixed")
+    Gq, gs, gb = workloads.gated_weights(0)
+    h0 = workloads.gru_h0(0, 4, B)
+    args = (W1, inp["base"], inp["anchor"], inp["T"])
+    # a closed gate (g = 0 exactly: exp(1e4) overflows) is the Markov walk
+    t0, l0, s0 = oracle_mod.walk_gated(*args, (Gq, gs, np.full(r, -1e4, np.float32)), h0,
+                                       uniforms=inp["uniforms"], W2_bits=W2)
+    tm, lm = oracle_mod.walk(*args, uniforms=inp["uniforms"], W2_bits=W2)
+    assert np.array_equal(t0, tm) and np.array_equal(l0, lm)
+    for b in range(B):
+        prev = int(inp["anchor"][b])
+        for k in range(gamma):
+            assert np.array_equal(s0[b, k], value_f64(W1[prev]))
+            prev = int(t0[b, k])
+    # an open gate (g = 1 exactly) keeps h0: every step is the plain step on bf16(h0)
+    t1, l1, s1 = oracle_mod.walk_gated(*args, (Gq, gs, np.full(r, 1e4, np.float32)), h0,
+                                       uniforms=inp["uniforms"], W2_bits=W2)
+    for b in range(B):
+        ub = oracle_mod.rne_bf16(h0[b].astype(np.float64))[1]
+        for k in range(gamma):
+            assert np.array_equal(s1[b, k], h0[b].astype(np.float64))
+            tok, lg = oracle_mod.step(ub, inp["base"][b, k], inp["T"][b], inp["uniforms"][b, k], W2_bits=W2)
+            assert np.array_equal(lg, l1[b, k]) and tok == t1[b, k]
+    # the synthetic gate: each new state lies between the old state and x (a
+    # convex blend), the gate is not saturated, and (-Gq, -s) is the same gate
+    t2, l2, s2 = oracle_mod.walk_gated(*args, (Gq, gs, gb), h0, uniforms=inp["uniforms"], W2_bits=W2)
+    t3, l3, s3 = oracle_mod.walk_gated(*args, (-Gq, -gs, gb), h0, uniforms=inp["uniforms"], W2_bits=W2)
+    assert np.array_equal(t2, t3) and np.array_equal(l2, l3) and np.array_equal(s2, s3)
+    for b in range(B):
+        prev, h = int(inp["anchor"][b]), h0[b].astype(np.float64)
+        for k in range(gamma):
+            x = value_f64(W1[prev])
+            lo, hi = np.minimum(h, x), np.maximum(h, x)
+            assert np.all(s2[b, k] >= lo - 1e-15) and np.all(s2[b, k] <= hi + 1e-15)
+            w = np.where(np.abs(x - h) > 1e-3, (s2[b, k] - x) / np.where(np.abs(x - h) > 1e-3, h - x, 1.0), 0.5)
+            assert 0.02 < np.median(w) < 0.98 and np.ptp(w) > 0.3  # gates spread over (0, 1)
+            h, prev = s2[b, k], int(t2[b, k])
+    # the gate reads the state: moving h0 alone changes the gates of step 0
+    _, _, s4 = oracle_mod.walk_gated(*args, (Gq, gs, gb), -h0, uniforms=inp["uniforms"], W2_bits=W2)
+    x0 = value_f64(W1[int(inp["anchor"][0])])
+    ok = (np.abs(h0[0] - x0) > 0.05) & (np.abs(-h0[0] - x0) > 0.05)
+    g_a = (s2[0, 0] - x0)[ok] / (h0[0] - x0)[ok]
+    g_b = (s4[0, 0] - x0)[ok] / (-h0[0] - x0)[ok]
+    assert ok.sum() > 100 and np.median(np.abs(g_a - g_b)) > 0.05
+
+
 def test_gru_walk_teacher_forcing_and_zero_cell(oracle_mod):
     V, r = 2000, 256
     W1, W2 = workloads.weights(0, V=V)

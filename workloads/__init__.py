@@ -141,6 +141,17 @@ def rnn_cell_weights(index: int, r: int = R):
     return gru_cell_weights(index, r=r, gates=1)
 
 
+def gated_weights(index: int, r: int = R):
+    """Synthetic gated head: the r x r gate matrix drawn N(0, 1/r), quantised
+    like int8 W2 rows (Gq [r, r] int8 codes, gs [r] f32 row scales), and a gate
+    bias gb [r] f32 drawn N(0, 1), so that the gates spread over (0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(7_500 + index))
+    G = to_bf16_bits((1.0 / np.sqrt(r)) * rng.standard_normal((r, r), dtype=np.float32))
+    Gq, gs = quantize_int8(G)
+    gb = rng.standard_normal(r).astype(np.float32)
+    return Gq, gs, gb
+
+
 def gru_h0(index: int, round_index: int, B: int, r: int = R):
     """Initial GRU states [B, r] f32 in (-1, 1): tanh of N(0, 1)."""
     rng = np.random.Generator(np.random.PCG64(8_000_000 + 1000 * index + round_index))
