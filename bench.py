@@ -217,6 +217,8 @@ SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, 
          # the GRU serial head (DSW_FLAG_GRU) on the headline and the long walk
          (1, 1, 7, "bf16", "inverse_cdf", "gru"), (2, 1, 16, "bf16", "inverse_cdf", "gru"),
          (1, 1, 7, "bf16", "inverse_cdf", "rnn"),
+         # DSpark's gated head (DSW_FLAG_GATED) on the headline and the long walk
+         (1, 1, 7, "bf16", "inverse_cdf", "gated"), (2, 1, 16, "bf16", "inverse_cdf", "gated"),
          # one GPU's share of a two-GPU vocabulary split (the kernel at its real shape;
          # the cross-GPU exchange is not built): half of V = 151,936 and of V = 248,320
          (1, 1, 7, "bf16", "inverse_cdf", "markov", 75_968), (3, 1, 16, "bf16", "inverse_cdf", "markov", 124_160)]
@@ -245,7 +247,8 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="m
     del rounds
     walker = dsw.Walker(V, gamma_max=gamma, B_max=B, w2_dtype=dsw.INT8 if dtype == "int8" else dsw.BF16,
                         flags=(dsw.FLAG_GUMBEL if sampler == "gumbel" else 0) |
-                              (dsw.FLAG_GRU if head == "gru" else 0) | (dsw.FLAG_RNN if head == "rnn" else 0))
+                              (dsw.FLAG_GRU if head == "gru" else 0) | (dsw.FLAG_RNN if head == "rnn" else 0) |
+                              (dsw.FLAG_GATED if head == "gated" else 0))
     if sampler == "gumbel":
         walker.set_seed(0x5EED + index)
     plan = walker.query_plan(B)
@@ -256,8 +259,15 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="m
         cw = workloads.gru_cell_weights(index, gates=3 if head == "gru" else 1)
         celld = (bf(cw[0]), bf(cw[1]), torch.from_numpy(cw[2]).to(dev), torch.from_numpy(cw[3]).to(dev))
         h0 = torch.from_numpy(workloads.gru_h0(index, 0, 1)[0]).to(dev)
+    if head == "gated":
+        gw = workloads.gated_weights(index)
+        gated = tuple(torch.from_numpy(a).to(dev) for a in gw)
+        h0 = torch.from_numpy(workloads.gru_h0(index, 0, 1)[0]).to(dev)
 
     def go(j):
+        if head == "gated":
+            walker.walk_gated(W1d, W2d, gated, h0, base[j % n], anchor[j % n], T[j % n], uni[j % n], tokens=tokens)
+            return
         if head in ("gru", "rnn"):
             (walker.walk_gru if head == "gru" else walker.walk_rnn)(
                 W1d, W2d, celld, h0, base[j % n], anchor[j % n], T[j % n], uni[j % n], tokens=tokens)

@@ -131,6 +131,10 @@ extern "C" {
                                     RNN head, read as the tanh RNN cell):
                                     walks go through dsw_walk_rnn.  The same
                                     limits as DSW_FLAG_GRU, and not with it. */
+#define DSW_FLAG_GATED 512u      /* DSpark's gated serial head (same section):
+                                    walks go through dsw_walk_gated.  The same
+                                    limits as DSW_FLAG_GRU, and not with it
+                                    or DSW_FLAG_RNN.                           */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -264,6 +268,30 @@ int dsw_walk_rnn(dsw_handle_t h, const void* W1, const void* W2, const void* Wih
                  const float* bih, const float* bhh, const float* h0, const void* base,
                  const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
                  void* logits, float* states, int B, int gamma, void* stream);
+
+/* One round of DSpark's gated serial head ("Keeping the Draft Walk on Chip",
+ * section "Beyond DSpark: other serial heads": one r x r matrix that fits in
+ * int8 beside the shard, so every CTA applies it itself and the state needs no
+ * exchange).  The pages give no equation; this entry point takes a convex gate
+ * between the state and the new token's row, the gate read from the state:
+ *   x  = W1[prev]
+ *   g  = sigmoid(gate_scale * (Gq h) + gate_bias)   (per element, fp32)
+ *   h  = g * h + (1 - g) * x
+ *   logit = bf16(base_k + bf16(W2 bf16(h))), tok as in dsw_walk.
+ * Handle created with DSW_FLAG_GATED (dsw_walk, dsw_walk_gru and dsw_walk_rnn
+ * on it return DSW_ERR_ARG, and this call on another handle too).  Arguments
+ * as dsw_walk_gru, with the cell replaced by (device pointers):
+ *   Gq          int8 [r][r]  the gate matrix's codes, row-major, 16-byte
+ *                            aligned (else DSW_ERR_ARG)
+ *   gate_scale  f32 [r]      the codes' row scales
+ *   gate_bias   f32 [r]      the gate biases
+ * Every workgroup holds Gq (64 KiB) in LDS and updates the whole state; the
+ * gates of step k + 1 are formed while step k's keys travel.  Asynchronous;
+ * allocates nothing. */
+int dsw_walk_gated(dsw_handle_t h, const void* W1, const void* W2, const void* Gq, const float* gate_scale,
+                   const float* gate_bias, const float* h0, const void* base, const int32_t* anchor,
+                   const float* T, const float* uniforms, int32_t* tokens, void* logits, float* states,
+                   int B, int gamma, void* stream);
 
 /* Wait for the handle's device, then return and clear the status word that
  * the device latches (0 or a DSW_ERR_DEV_* code).  After a device error the

@@ -40,6 +40,7 @@ FLAG_SINGLE_ROUND = 32
 FLAG_GUMBEL = 64
 FLAG_GRU = 128
 FLAG_RNN = 256
+FLAG_GATED = 512
 ENGINE_VALU, ENGINE_MFMA = 0, 1
 RANK = 256
 
@@ -101,6 +102,7 @@ def lib():
         L.dsw_walk.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, P]
         L.dsw_walk_gru.argtypes = [P] * 15 + [I, I, P]
         L.dsw_walk_rnn.argtypes = [P] * 15 + [I, I, P]
+        L.dsw_walk_gated.argtypes = [P] * 14 + [I, I, P]
         L.dsw_status.argtypes = [P]
         L.dsw_query_plan.argtypes = [P, I, ctypes.POINTER(PlanInfo)]
         L.dsw_destroy.argtypes = [P]
@@ -109,7 +111,8 @@ def lib():
         L.dsw_set_seed.argtypes = [P, ctypes.c_ulonglong, I]
         L.dsw_round_counter.argtypes = [P, ctypes.POINTER(ctypes.c_uint)]
         L.dsw_set_trace.argtypes = [P, P, ctypes.c_longlong]
-        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn", "dsw_status",
+        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn", "dsw_walk_gated",
+                  "dsw_status",
                   "dsw_query_plan", "dsw_destroy", "dsw_set_seed", "dsw_round_counter", "dsw_set_trace"):
             getattr(L, f).restype = I
         _lib = L
@@ -237,26 +240,42 @@ class Walker:
         cell = (Wih bf16 [3r,r], Whh bf16 [3r,r], bih f32 [3r], bhh f32 [3r]); h0 f32 [r];
         other tensors as walk().  Returns (tokens [B,gamma], logits or None,
         states f32 [gamma, r] or None)."""
-        return self._walk_cell(3, "dsw_walk_gru", W1, W2, cell, h0, base, anchor, T, uniforms, tokens,
-                               logits, states, want_logits, want_states, stream)
+        return self._walk_cell(self._cell_spec(cell, 3), "dsw_walk_gru", W1, W2, cell, h0, base, anchor, T,
+                               uniforms, tokens, logits, states, want_logits, want_states, stream)
 
     def walk_rnn(self, W1, W2, cell, h0, base, anchor, T, uniforms=None, tokens=None, logits=None,
                  states=None, want_logits=False, want_states=False, stream=None):
         """One round of the RNN serial head (handle made with FLAG_RNN; one request).
         cell = (Wih bf16 [r,r], Whh bf16 [r,r], bih f32 [r], bhh f32 [r]); as walk_gru otherwise."""
-        return self._walk_cell(1, "dsw_walk_rnn", W1, W2, cell, h0, base, anchor, T, uniforms, tokens,
+        return self._walk_cell(self._cell_spec(cell, 1), "dsw_walk_rnn", W1, W2, cell, h0, base, anchor, T,
+                               uniforms, tokens, logits, states, want_logits, want_states, stream)
+
+    def walk_gated(self, W1, W2, gate, h0, base, anchor, T, uniforms=None, tokens=None, logits=None,
+                   states=None, want_logits=False, want_states=False, stream=None):
+        """One round of DSpark's gated serial head (handle made with FLAG_GATED; one
+        request).  gate = (Gq int8 [r,r], gate_scale f32 [r], gate_bias f32 [r]):
+        g = sigmoid(gate_scale * (Gq h) + gate_bias), h = g h + (1 - g) W1[prev];
+        as walk_gru otherwise."""
+        import torch
+        r = self.r
+        spec = [(gate[0], torch.int8, (r, r), "Gq"), (gate[1], torch.float32, (r,), "gate_scale"),
+                (gate[2], torch.float32, (r,), "gate_bias")]
+        return self._walk_cell(spec, "dsw_walk_gated", W1, W2, gate, h0, base, anchor, T, uniforms, tokens,
                                logits, states, want_logits, want_states, stream)
 
-    def _walk_cell(self, gates, fname, W1, W2, cell, h0, base, anchor, T, uniforms, tokens, logits,
+    def _cell_spec(self, cell, gates):
+        import torch
+        r = self.r
+        return [(cell[0], torch.bfloat16, (gates * r, r), "Wih"), (cell[1], torch.bfloat16, (gates * r, r), "Whh"),
+                (cell[2], torch.float32, (gates * r,), "bih"), (cell[3], torch.float32, (gates * r,), "bhh")]
+
+    def _walk_cell(self, spec, fname, W1, W2, cell, h0, base, anchor, T, uniforms, tokens, logits,
                    states, want_logits, want_states, stream):
         import torch
         dev = torch.device("cuda", self.device)
         B, gamma, V = (int(x) for x in base.shape)
         r = self.r
-        Wih, Whh, bih, bhh = cell
-        need = [(W1, torch.bfloat16, (self.V, r), "W1"), (W2, torch.bfloat16, (self.V, r), "W2"),
-                (Wih, torch.bfloat16, (gates * r, r), "Wih"), (Whh, torch.bfloat16, (gates * r, r), "Whh"),
-                (bih, torch.float32, (gates * r,), "bih"), (bhh, torch.float32, (gates * r,), "bhh"),
+        need = [(W1, torch.bfloat16, (self.V, r), "W1"), (W2, torch.bfloat16, (self.V, r), "W2")] + spec + [
                 (h0, torch.float32, (r,), "h0"), (base, torch.bfloat16, (B, gamma, self.V), "base"),
                 (anchor, torch.int32, (B,), "anchor"), (T, torch.float32, (B,), "T")]
         if uniforms is not None:
@@ -277,7 +296,7 @@ class Walker:
                 raise ValueError(f"{name}: want {dt} {shape} contiguous on {dev}, got "
                                  f"{t.dtype} {tuple(t.shape)} on {t.device}")
         ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
-        rc = getattr(lib(), fname)(self._h, ptr(W1), ptr(W2), ptr(Wih), ptr(Whh), ptr(bih), ptr(bhh), ptr(h0),
+        rc = getattr(lib(), fname)(self._h, ptr(W1), ptr(W2), *[ptr(t[0]) for t in spec], ptr(h0),
                                    ptr(base), ptr(anchor), ptr(T), ptr(uniforms), ptr(tokens), ptr(logits),
                                    ptr(states), B, gamma, _stream_handle(torch, dev, stream))
         _check(rc, fname)

@@ -24,20 +24,25 @@ extern "C" const void* dsw_internal_mfma_i8_kernel_gumbel(int batch_tile, int re
 // the one-request kernels for the GRU and RNN serial heads
 extern "C" const void* dsw_internal_mfma_kernel_b1_gru(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b1_rnn(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b1_gated(int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs (with Gumbel-max sampling when `gumbel`), or
 // nullptr.  The planner never gives a Gumbel-max handle the batched kernel.
-// The head a handle's flags select: 0 the Markov head, 1 the GRU head, 2 the RNN head.
-int cell_of(unsigned flags) { return (flags & DSW_FLAG_GRU) ? 1 : ((flags & DSW_FLAG_RNN) ? 2 : 0); }
+// The head a handle's flags select: 0 the Markov head, 1 the GRU head, 2 the
+// RNN head, 3 the gated head.
+int cell_of(unsigned flags) {
+    return (flags & DSW_FLAG_GRU) ? 1 : ((flags & DSW_FLAG_RNN) ? 2 : ((flags & DSW_FLAG_GATED) ? 3 : 0));
+}
 
-// cell: 0 the Markov head, 1 the GRU head, 2 the RNN head
+// cell: as cell_of
 const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell) {
-    if (cell)  // the planner gives the recurrent heads only the one-request MFMA engine
-        return pl.engine == DSW_ENGINE_MFMA && pl.batch_tile == 1 && pl.w2_dtype == DSW_BF16
-                   ? (cell == 1 ? dsw_internal_mfma_kernel_b1_gru : dsw_internal_mfma_kernel_b1_rnn)(
-                         pl.reg_tiles, pl.max_tiles)
-                   : nullptr;
+    if (cell) {  // the planner gives the recurrent heads only the one-request MFMA engine
+        if (pl.engine != DSW_ENGINE_MFMA || pl.batch_tile != 1 || pl.w2_dtype != DSW_BF16) return nullptr;
+        return (cell == 1 ? dsw_internal_mfma_kernel_b1_gru
+                          : (cell == 2 ? dsw_internal_mfma_kernel_b1_rnn : dsw_internal_mfma_kernel_b1_gated))(
+            pl.reg_tiles, pl.max_tiles);
+    }
     if (pl.batch_tile == dsw::kMaxBatch)
         return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
     if (pl.engine == DSW_ENGINE_VALU)
@@ -236,7 +241,8 @@ extern "C" int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out) {
 }
 
 namespace {
-// A recurrent head's extra arguments (dsw_walk_gru, dsw_walk_rnn).
+// A recurrent head's extra arguments (dsw_walk_gru, dsw_walk_rnn: the cell;
+// dsw_walk_gated: the gate matrix, its scales and biases).
 struct GruArgs {
     const uint16_t* wih;
     const uint16_t* whh;
@@ -244,6 +250,9 @@ struct GruArgs {
     const float* bhh;
     const float* h0;
     float* states;
+    const int8_t* gq;
+    const float* gs;
+    const float* gb;
 };
 
 int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale, const void* base,
@@ -317,6 +326,9 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     p.gru_bhh = gru ? gru->bhh : nullptr;
     p.h0 = gru ? gru->h0 : nullptr;
     p.states = gru ? gru->states : nullptr;
+    p.gate_q = gru ? gru->gq : nullptr;
+    p.gate_scale = gru ? gru->gs : nullptr;
+    p.gate_bias = gru ? gru->gb : nullptr;
     p.trace = nullptr;
     if (h->trace != nullptr &&
         (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)
@@ -338,7 +350,7 @@ extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const fl
                         const void* base, const int32_t* anchor, const float* T,
                         const float* uniforms, int32_t* tokens, void* logits, int B, int gamma,
                         void* stream) {
-    if (h && cell_of(h->flags)) return DSW_ERR_ARG;  // dsw_walk_gru / dsw_walk_rnn serve these handles
+    if (h && cell_of(h->flags)) return DSW_ERR_ARG;  // the heads' own entry points serve these handles
     return walk_impl(h, W1, W2, w2_scale, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, nullptr);
 }
 
@@ -349,7 +361,8 @@ extern "C" int dsw_walk_gru(dsw_handle_t h, const void* W1, const void* W2, cons
     if (!h) return DSW_ERR_NULL;
     if (cell_of(h->flags) != 1) return DSW_ERR_ARG;
     if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
-    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states};
+    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states,
+                    nullptr, nullptr, nullptr};
     return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
 }
 
@@ -360,7 +373,23 @@ extern "C" int dsw_walk_rnn(dsw_handle_t h, const void* W1, const void* W2, cons
     if (!h) return DSW_ERR_NULL;
     if (cell_of(h->flags) != 2) return DSW_ERR_ARG;
     if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
-    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states};
+    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states,
+                    nullptr, nullptr, nullptr};
+    return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
+}
+
+extern "C" int dsw_walk_gated(dsw_handle_t h, const void* W1, const void* W2, const void* Gq,
+                              const float* gate_scale, const float* gate_bias, const float* h0, const void* base,
+                              const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens,
+                              void* logits, float* states, int B, int gamma, void* stream) {
+    if (!h) return DSW_ERR_NULL;
+    if (cell_of(h->flags) != 3) return DSW_ERR_ARG;
+    if (B > 0 && gamma > 0) {
+        if (!Gq || !gate_scale || !gate_bias || !h0) return DSW_ERR_NULL;
+        if (reinterpret_cast<uintptr_t>(Gq) % 16 != 0) return DSW_ERR_ARG;  // read as 16-byte words
+    }
+    const GruArgs g{nullptr, nullptr, nullptr, nullptr, h0, states, static_cast<const int8_t*>(Gq), gate_scale,
+                    gate_bias};
     return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
 }
 

@@ -62,16 +62,18 @@ static int mfma_tile_for(int B, bool i8) { return (B <= 1 && !i8) ? 1 : (B <= 4 
 // A recurrent head keeps its state (r floats) and its cell rows in LDS: per
 // owned state element 2 x gates bf16 rows and biases, and the gates' recurrent
 // pre-activations of the coming step (GRU: 3 gates, RNN: 1).
-static int cell_lds(int gates) {
+// The gated head holds its whole r x r matrix (widened to bf16), the row
+// scales and biases, the state, its two low bf16 pieces and the coming
+// step's gates.
+static int cell_lds(unsigned flags) {
+    if (flags & DSW_FLAG_GATED) return kRank * kRank * 2 + 4 * kRank * 4 + 2 * kRank * 2;
+    const int gates = (flags & DSW_FLAG_GRU) ? 3 : ((flags & DSW_FLAG_RNN) ? 1 : 0);
     return gates ? kRank * 4 + kCellMaxPerWg * 2 * gates * (kRank * 2 + 4) + kCellMaxPerWg * gates * 4 : 0;
 }
-static int cell_gates(unsigned flags) {
-    return (flags & DSW_FLAG_GRU) ? 3 : ((flags & DSW_FLAG_RNN) ? 1 : 0);
-}
-static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum, int gates) {
+static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum, unsigned flags) {
     const int rpad = max_tiles * 4 * kTileRows;
     return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0) +
-           kTraceLds + gumbel_noise_lds(nb, rpad, gum) + cell_lds(gates);
+           kTraceLds + gumbel_noise_lds(nb, rpad, gum) + cell_lds(flags);
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -116,7 +118,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
     const int nb = mfma_tile_for(B, i8);
-    const int lds_static = mfma_static_lds(nb, max_t, i8, (flags & DSW_FLAG_GUMBEL) != 0, cell_gates(flags));
+    const int lds_static = mfma_static_lds(nb, max_t, i8, (flags & DSW_FLAG_GUMBEL) != 0, flags);
     int avail = dev->max_lds_per_block - lds_static;
     if (avail < 0) return DSW_ERR_PLAN;
 
@@ -334,13 +336,15 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const bool gumbel = (flags & DSW_FLAG_GUMBEL) != 0;
     if (batched && gumbel) return DSW_ERR_ARG;
     // the recurrent heads: one bf16 request on the one-request MFMA engine, and
-    // a grid of at least r / kCellMaxPerWg workgroups to hold the state
-    const bool cell = (flags & (DSW_FLAG_GRU | DSW_FLAG_RNN)) != 0;
-    if ((flags & DSW_FLAG_GRU) && (flags & DSW_FLAG_RNN)) return DSW_ERR_ARG;
+    // (GRU, RNN) a grid of at least r / kCellMaxPerWg workgroups to hold the
+    // state; the gated head keeps the whole state in every workgroup
+    const unsigned heads = flags & (DSW_FLAG_GRU | DSW_FLAG_RNN | DSW_FLAG_GATED);
+    const bool cell = heads != 0;
+    if (heads & (heads - 1)) return DSW_ERR_ARG;  // one head per handle
     if (cell) {
         if (B > 1 || batched || gumbel || (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
         if (i8) return DSW_ERR_DTYPE;
-        if (grid * kCellMaxPerWg < kRank) return DSW_ERR_PLAN;
+        if (!(flags & DSW_FLAG_GATED) && grid * kCellMaxPerWg < kRank) return DSW_ERR_PLAN;
     }
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
     // one bf16 request: the MFMA engine's step is ~1 us shorter, but its shard

@@ -126,7 +126,10 @@ __device__ __forceinline__ uint4 as_bf16x8(const uint2& q) {
 // Whn h + bhn), CELL = 2 the tanh RNN, h' = tanh(Wih x + bih + Whh h + bhh) --
 // and the vocabulary matrix reads bf16(h).  Workgroup c updates state
 // elements c, c + G, ... (one per wave), posts them with the step's epoch, and
-// every workgroup gathers all r of them before its GEMV.  One request.
+// every workgroup gathers all r of them before its GEMV.  CELL = 3: DSpark's
+// gated head, whose one r x r matrix is small enough in int8 for every
+// workgroup to hold it and update the whole state itself (no state exchange):
+// g = sigmoid(s (Gq h) + b) from the state, h' = g h + (1 - g) x.  One request.
 template <int ENGINE, int A, int M, int NB, int DT = 0, int GUM = 0, int CELL = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
@@ -145,8 +148,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
     constexpr bool kCell = CELL != 0;                           // a recurrent head
     constexpr bool kGru = CELL == 1;
+    constexpr bool kGated = CELL == 3;                          // the whole state in every workgroup
+    constexpr bool kShard = kCell && !kGated;                   // the state spread over the workgroups
     constexpr int kGates = CELL == 1 ? 3 : 1;                    // cell rows per input, per element
-    static_assert(CELL >= 0 && CELL <= 2, "cell");
+    static_assert(CELL >= 0 && CELL <= 3, "cell");
     static_assert(!kCell || (kOne && GUM == 0), "recurrent heads: the one-request MFMA engine");
     static_assert(!kCell || kBlock == kRank, "recurrent heads: one state element per thread in the gather");
     constexpr int RPAD = kMfma ? M * 4 * kTileRows : kMaxSlots * kBlock;  // rows per shard, bound
@@ -168,11 +173,21 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // cell (per owned element: the kGates rows of Wih, then those of Whh --
     // GRU Wir, Wiz, Win, Whr, Whz, Whn) with their biases
     __shared__ float s_h[kCell ? kRank : 1];
-    __shared__ uint16_t s_cw[kCell ? kCellMaxPerWg * 2 * kGates * kRank : 1];
-    __shared__ float s_cb[kCell ? kCellMaxPerWg * 2 * kGates : 1];
+    __shared__ uint16_t s_cw[kShard ? kCellMaxPerWg * 2 * kGates * kRank : 1];
+    __shared__ float s_cb[kShard ? kCellMaxPerWg * 2 * kGates : 1];
     // recurrent heads: Whh h + bhh of the owned elements for the coming step,
     // formed while the previous step's keys travel
-    __shared__ float s_gh[kCell ? kCellMaxPerWg * kGates : 1];
+    __shared__ float s_gh[kShard ? kCellMaxPerWg * kGates : 1];
+    // gated head: the matrix widened once from int8 to bf16 (exact), as 16
+    // MFMA B-operand tiles of 16 rows in the order [tile][K block][lane]; the
+    // row scales and biases; the gates of the coming step; and the state's
+    // three bf16 pieces hi, lo, lo2 (h = hi + lo + lo2 exactly; hi = bf16(h)
+    // is also the vocabulary GEMV's operand in s_u)
+    __shared__ uint4 s_gw[kGated ? (kRank / kTileRows) * 8 * 64 : 1];
+    __shared__ float s_gs[kGated ? kRank : 1];
+    __shared__ float s_gb[kGated ? kRank : 1];
+    __shared__ float s_gg[kGated ? kRank : 1];
+    __shared__ uint4 s_hp[kGated ? 3 * kRowChunks : 1];
     __shared__ uint32_t s_wbest[4][NB];
     __shared__ unsigned long long s_red64[4][NB];
     __shared__ float s_redf[4][NB];
@@ -251,7 +266,54 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         s_T[t] = temp;
     }
     for (int j = t; j < NB * US; j += kBlock) s_u[j] = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (kCell) {
+    // gated head: the exact split h = hi + lo + lo2 into bf16 pieces (fp32 h
+    // has 24 significant bits, each piece takes the next 8), stored by thread m
+    auto split_state = [&](int m, float hv) {
+        uint16_t* s_x = reinterpret_cast<uint16_t*>(s_u);
+        uint16_t* s_lo = reinterpret_cast<uint16_t*>(s_hp);
+        const uint32_t hi = f32_to_bf16(hv);
+        const float r1 = hv - bf16_to_f32(hi);
+        const uint32_t lo = f32_to_bf16(r1);
+        s_x[m] = (uint16_t)hi;
+        s_lo[m] = (uint16_t)hi;
+        s_lo[kRank + m] = (uint16_t)lo;
+        s_lo[2 * kRank + m] = (uint16_t)f32_to_bf16(r1 - bf16_to_f32(lo));
+    };
+    if constexpr (kGated) {
+        // h0 and the whole gate matrix (every workgroup updates the whole state)
+        __syncthreads();  // s_u is zeroed by other threads just above
+        for (int m = t; m < kRank; m += kBlock) {
+            const float hv = p.h0[m];
+            s_h[m] = hv;
+            split_state(m, hv);  // the first gates read it (s_u is zero until the first gather)
+            s_gs[m] = p.gate_scale[m];
+            s_gb[m] = p.gate_bias[m];
+        }
+        // B-operand entry (tile * 8 + kb) * 64 + lane holds the codes of chunk
+        // KC(kb, g) = 8 g + kb of row 16 tile + n (n = lane % 16, g = lane / 16),
+        // widened to bf16: item (tile, lane) is the 64 contiguous codes 64 g ..
+        // of that row, K blocks 0..7.  Every load is issued before any is used.
+        const uint4* gq = reinterpret_cast<const uint4*>(p.gate_q);
+        constexpr int kItems = (kRank / kTileRows) * 64 / kBlock;
+        uint4 raw[kItems][4];
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = t + it * kBlock, ln = i & 63;
+            const int m = (i >> 6) * kTileRows + (ln & 15);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) raw[it][q] = gq[m * (kRank / 16) + 4 * (ln >> 4) + q];
+        }
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = t + it * kBlock, ln = i & 63, tile = i >> 6;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s_gw[(tile * 8 + 2 * q) * 64 + ln] = as_bf16x8(make_uint2(raw[it][q].x, raw[it][q].y));
+                s_gw[(tile * 8 + 2 * q + 1) * 64 + ln] = as_bf16x8(make_uint2(raw[it][q].z, raw[it][q].w));
+            }
+        }
+    }
+    if constexpr (kShard) {
         // h0, and the cell rows of state elements c + i G (i < kCellMaxPerWg)
         constexpr int kRows = 2 * kGates;
         for (int m = t; m < kRank; m += kBlock) s_h[m] = p.h0[m];
@@ -457,8 +519,62 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             }
         }
     };
-    if constexpr (kCell) {
+    if constexpr (kShard) {
         if (gamma > 0) cell_recurrent();  // from h0; read by the same wave in step 0
+    }
+    // gated head: wave w forms the gates of state elements 64 w .. 64 w + 63 for
+    // the coming step on the matrix cores.  A-operand rows 0, 1, 2 carry the
+    // state's three bf16 pieces, so row i of the result is the gate matrix
+    // times piece i: products exact, sums in fp32, and their sum is the
+    // matrix times the fp32 state.
+    // Rows 3..15 of A repeat lo2: their results are never read.  K block
+    // kb + 1's operands are read from LDS before block kb's products are
+    // issued.  (KT tiles per pass: the widest shapes have no registers for
+    // four accumulators.)
+    auto gate_update = [&]() {
+        constexpr int KT = A <= 10 ? 4 : 1;
+        const uint4* ap = s_hp + min(lane & 15, 2) * kRowChunks + DSW_KC(0, lane >> 4);
+#pragma unroll 1
+        for (int t0 = 0; t0 < 4; t0 += KT) {
+            const uint4* bp = s_gw + (wave * 4 + t0) * 8 * 64 + lane;
+            f32x4_t d[KT];
+            uint4 a = ap[0], b[KT];
+#pragma unroll
+            for (int tl = 0; tl < KT; ++tl) {
+                d[tl] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                b[tl] = bp[tl * 8 * 64];
+            }
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                uint4 a2 = a, b2[KT];
+#pragma unroll
+                for (int tl = 0; tl < KT; ++tl) b2[tl] = b[tl];
+                if (kb + 1 < 8) {
+                    a2 = ap[kb + 1];  // DSW_KC(kb + 1, g) = DSW_KC(0, g) + kb + 1
+#pragma unroll
+                    for (int tl = 0; tl < KT; ++tl) b2[tl] = bp[tl * 8 * 64 + (kb + 1) * 64];
+                }
+                __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of the products
+#pragma unroll
+                for (int tl = 0; tl < KT; ++tl) d[tl] = mfma_tile(a, b[tl], d[tl]);
+                __builtin_amdgcn_sched_barrier(0);
+                a = a2;
+#pragma unroll
+                for (int tl = 0; tl < KT; ++tl) b[tl] = b2[tl];
+            }
+            if (lane < kTileRows) {
+#pragma unroll
+                for (int tl = 0; tl < KT; ++tl) {
+                    const int m = (wave * 4 + t0 + tl) * kTileRows + lane;
+                    const float dot = (d[tl][0] + d[tl][1]) + d[tl][2];
+                    s_gg[m] = 1.0f / (1.0f + expf(-(s_gs[m] * dot + s_gb[m])));
+                }
+            }
+        }
+    };
+    if constexpr (kGated) {
+        if (gamma > 0) gate_update();  // from h0; read after the first gather's barrier
+        __syncthreads();               // every wave has read bf16(h0) before the gather replaces it
     }
 
     // token of request b at the end of the current step (after the winner
@@ -503,7 +619,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             s_u[b * US + ch] = W1[(size_t)prev * kRowChunks + ch];
         }
         __syncthreads();
-        if constexpr (kCell) {
+        if constexpr (kGated) {
+            // ---- the gated update, one state element per thread ---------------
+            const uint16_t* s_x = reinterpret_cast<const uint16_t*>(s_u);  // x = W1[prev]
+            const float gg = s_gg[t];
+            const float hn = gg * s_h[t] + (1.0f - gg) * bf16_to_f32(s_x[t]);
+            s_h[t] = hn;
+            split_state(t, hn);  // bf16(h') replaces x as the GEMV operand
+            if (c == 0 && p.states != nullptr) p.states[(size_t)k * kRank + t] = hn;
+            __syncthreads();
+        }
+        if constexpr (kShard) {
             // ---- the cell: wave i updates state element c + i G ---------------
             const uint16_t* s_x = reinterpret_cast<const uint16_t*>(s_u);  // x = W1[prev]
             const int j = c + wave * G;
@@ -937,9 +1063,31 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             // step's noise was last read before the barrier ahead of the post)
             if (any_samp && k + 1 < gamma) draw_noise(k + 1);
         }
-        if constexpr (kCell) {
+        if constexpr (kShard) {
             // the next step's recurrent half from this step's state, while the keys travel
             if (k + 1 < gamma) cell_recurrent();
+        }
+        // Up to 4 requests: two polls in flight, each check waiting only for the
+        // older load, so a word that lands is seen about half a round trip
+        // sooner than with one poll at a time.  16 requests: one poll at a time
+        // (a second set of words would not fit in registers).  Thread t < G
+        // reads workgroup t's mailbox.
+        constexpr int kDepth = NB <= 4 ? 2 : 1;
+        const unsigned long long* box = mail_q + (size_t)t * kMailWords;
+        unsigned long long pa[kDepth == 2 ? NB : 1][2], pb[kDepth == 2 ? NB : 1][2];
+#define DSW_POLL(w)                                                                        \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                       \
+        if (NB == 1 || b < B) {                                                            \
+            w[b][0] = ld_agent64(&box[b]);                                                 \
+            if (s_T[b] > 0.0f) w[b][1] = ld_agent64(&box[kMaxBatchPersistent + b]);        \
+        }                                                                                  \
+    }
+        if constexpr (kGated) {
+            // the first polls go out, then the next step's gates are formed while
+            // the keys travel
+            static_assert(kDepth == 2, "gated head: one request");
+            if (t < G) DSW_POLL(pa);
+            if (k + 1 < gamma) gate_update();
         }
         unsigned long long kw[NB];
         uint32_t sw[NB];  // the second word's payload: exp-sum bits, or ~id (Gumbel-max)
@@ -949,20 +1097,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             sw[b] = 0u;
         }
         if (t < G) {
-            // Up to 4 requests: two polls in flight, each check waiting only for
-            // the older load, so a word that lands is seen about half a round
-            // trip sooner than with one poll at a time.  16 requests: one poll at
-            // a time (a second set of words would not fit in registers).
-            constexpr int kDepth = NB <= 4 ? 2 : 1;
-            const unsigned long long* box = mail_q + (size_t)t * kMailWords;
-            unsigned long long pa[kDepth == 2 ? NB : 1][2], pb[kDepth == 2 ? NB : 1][2];
-#define DSW_POLL(w)                                                                        \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                       \
-        if (NB == 1 || b < B) {                                                            \
-            w[b][0] = ld_agent64(&box[b]);                                                 \
-            if (s_T[b] > 0.0f) w[b][1] = ld_agent64(&box[kMaxBatchPersistent + b]);        \
-        }                                                                                  \
-    }
 #define DSW_READY(w, ready)                                                                \
     _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                       \
         if (NB == 1 || b < B) {                                                            \
@@ -975,7 +1109,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         }                                                                                  \
     }
             unsigned it = 0;
-            if constexpr (kDepth == 2) DSW_POLL(pa);
+            if constexpr (kDepth == 2 && !kGated) DSW_POLL(pa);  // (the gated head polled above)
             for (;;) {
                 if constexpr (kDepth == 2) {
                     DSW_POLL(pb);

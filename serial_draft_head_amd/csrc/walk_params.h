@@ -112,6 +112,11 @@ struct WalkParams {
     const float* gru_bhh;
     const float* h0;
     float* states;
+    // gated head (CELL = 3): the r x r gate matrix as int8 codes (row-major,
+    // 16-byte aligned) with fp32 row scales and biases; h0 and states as above
+    const int8_t* gate_q;
+    const float* gate_scale;
+    const float* gate_bias;
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };
 

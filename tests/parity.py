@@ -210,6 +210,35 @@ def check_gru_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states):
     return gamma, worst, worst_ratio
 
 
+def check_gated_states(W1_bits, gate, h0, gpu_tokens, anchor, gpu_states):
+    """As check_gru_states for the gated head, g = sigmoid(s (Gq h) + b),
+    h' = g h + (1 - g) x: the fp32 pre-activation errs by at most
+    g_(r+4) (|s| sum |q h| + |b|) (exact int8 x fp32 products, fp32 sums, the
+    scale and the bias), which passes through sigmoid' <= 1/4; exp, add and
+    divide add 4 ulps of g; the blend errs by |dg| |h - x| plus 3 ulps of
+    |h| + |x|.  Returns (steps checked, largest error, largest error / bound)."""
+    Gq, gs, gb = gate
+    Q = np.asarray(Gq, np.float64)
+    s = np.asarray(gs, np.float64)
+    b = np.asarray(gb, np.float64)
+    r = Q.shape[1]
+    gam = (r + 4) * F32_EPS / (1 - (r + 4) * F32_EPS)
+    worst, worst_ratio = 0.0, 0.0
+    for k in range(gpu_states.shape[0]):
+        prev = int(anchor) if k == 0 else int(gpu_tokens[k - 1])
+        x = oracle.bf16_bits_to_f64(W1_bits[prev])
+        h = h0.astype(np.float64) if k == 0 else gpu_states[k - 1].astype(np.float64)
+        want = oracle.gated_cell(x, h, Gq, gs, gb)
+        g = 1 / (1 + np.exp(-(s * (Q @ h) + b)))
+        e_g = 0.25 * gam * (np.abs(s) * (np.abs(Q) @ np.abs(h)) + np.abs(b)) + 4 * F32_EPS * g
+        bound = 2 * (e_g * np.abs(h - x) + 3 * F32_EPS * (np.abs(h) + np.abs(x))) + 1e-9
+        err = np.abs(gpu_states[k].astype(np.float64) - want)
+        assert np.all(err <= bound), f"k={k}: state error {err.max()} above its bound at {np.argmax(err - bound)}"
+        worst = max(worst, float(err.max()))
+        worst_ratio = max(worst_ratio, float((err / bound).max()))
+    return gpu_states.shape[0], worst, worst_ratio
+
+
 def check_rnn_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states):
     """As check_gru_states for the tanh RNN cell: the error of the fp32
     pre-activation (two dot products and biases, g_(r+4) sum |w v|) passes

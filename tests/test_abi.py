@@ -61,6 +61,7 @@ def test_null_and_argument_errors_without_a_device(dsw):
     assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 7, 0, 0, 0) == -2      # batch
     assert L.dsw_walk_gru(None, *([None] * 14), 1, 1, None) == -1
     assert L.dsw_walk_rnn(None, *([None] * 14), 1, 1, None) == -1
+    assert L.dsw_walk_gated(None, *([None] * 13), 1, 1, None) == -1
 
 
 def fake_device(dsw, cus=256, lds_cu=160 * 1024, lds_blk=160 * 1024):
@@ -236,6 +237,30 @@ def test_planner_gru_head(dsw):
     with pytest.raises(dsw.DswError) as e:
         dsw.plan(fake_device(dsw, cus=63), 32_000, 7, 1, flags=R)
     assert e.value.code == -10
+
+
+def test_planner_gated_head(dsw):
+    d = fake_device(dsw)
+    Q = dsw.FLAG_GATED
+    # the one-request MFMA engine; the whole gate matrix (widened to bf16), its
+    # scales and biases, the state, its low pieces and the gates take 133 KiB of LDS
+    p = dsw.plan(d, 151_936, 7, 1, flags=Q)
+    q = dsw.plan(d, 151_936, 16, 1)
+    assert (p.engine, p.batch_tile, p.reg_tiles, p.max_tiles, p.stream_rows) == (1, 1, 10, 10, 0)
+    assert p.static_lds_bytes == q.static_lds_bytes + 256 * 256 * 2 + 4 * 256 * 4 + 2 * 256 * 2
+    # V = 248,320: the matrix displaces LDS tiles of the shard, which then streams part of its rows
+    full, gated = dsw.plan(d, 248_320, 16, 1), dsw.plan(d, 248_320, 16, 1, flags=Q)
+    assert full.stream_rows == 0 and gated.stream_rows > 0 and gated.lds_tiles < full.lds_tiles
+    assert gated.static_lds_bytes + gated.lds_bytes <= 160 * 1024
+    # no state exchange, so no lower bound on the grid
+    assert dsw.plan(fake_device(dsw, cus=32), 32_000, 7, 1, flags=Q).grid == 32
+    for B, flags, dt, code in ((2, Q, dsw.BF16, -11), (1, Q | dsw.FLAG_GUMBEL, dsw.BF16, -11),
+                               (1, Q | dsw.FLAG_BATCHED, dsw.BF16, -11), (1, Q | dsw.FLAG_VALU_GEMV, dsw.BF16, -11),
+                               (1, Q | dsw.FLAG_GRU, dsw.BF16, -11), (1, Q | dsw.FLAG_RNN, dsw.BF16, -11),
+                               (1, Q, dsw.INT8, -5)):
+        with pytest.raises(dsw.DswError) as e:
+            dsw.plan(d, 151_936, 7, B, w2_dtype=dt, flags=flags)
+        assert e.value.code == code
 
 
 def test_planner_int8_rows(dsw):

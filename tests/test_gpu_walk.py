@@ -543,6 +543,105 @@ def test_rnn_head(dsw, V, gamma, temps):
     walker.close()
 
 
+GATED_CASES = [(4_097, 5, "greedy"), (32_000, 7, "cycle"), (151_936, 16, "greedy"), (248_320, 16, "cycle")]
+
+
+@pytest.mark.parametrize("V,gamma,temps", GATED_CASES)
+def test_gated_head(dsw, V, gamma, temps):
+    import oracle
+    say(f"gated head V={V} gamma={gamma} {temps}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    gate = workloads.gated_weights(1)
+    gated = (torch.from_numpy(gate[0]).to(DEV), torch.from_numpy(gate[1]).to(DEV),
+             torch.from_numpy(gate[2]).to(DEV))
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_GATED)
+    say("plan", walker.query_plan(1).as_dict())
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 700 + rnd, B=1, gamma=gamma, V=V, temps=temps)
+        h0 = workloads.gru_h0(2, rnd, 1)
+        base, anchor, T, uni = round_dev(inp)
+        tokens, logits, states = walker.walk_gated(W1d, W2d, gated, torch.from_numpy(h0[0]).to(DEV), base,
+                                                   anchor, T, uni, want_logits=True, want_states=True)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        st = states.cpu().numpy()
+        n, worst, ratio = parity.check_gated_states(W1, gate, h0[0], toks[0], inp["anchor"][0], st)
+        ub = oracle.rne_bf16(st.astype(np.float64))[1][None]
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 latents=ub)
+        say(rnd, f"states: {n} steps, largest error {worst:.3g} ({ratio:.3f} of its bound)", rep)
+    walker.close()
+
+
+def test_gated_head_closed_gate_is_the_markov_walk(dsw):
+    # gate bias -1e4: g = 1 / (1 + inf) = 0 exactly, so h = x = W1[prev] and the
+    # operand bf16(h) is the Markov walk's; tokens and logits agree bit for bit
+    V, gamma = 32_000, 7
+    say(f"gated head, closed gate, V={V} gamma={gamma}")
+    W1, W2 = workloads.weights(2, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    Gq, gs, _ = workloads.gated_weights(1)
+    gated = (torch.from_numpy(Gq).to(DEV), torch.from_numpy(gs).to(DEV),
+             torch.full((256,), -1e4, dtype=torch.float32, device=DEV))
+    wg = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_GATED)
+    wm = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_MFMA_GEMV)
+    for rnd in range(3):
+        inp = workloads.round_inputs(2, 800 + rnd, B=1, gamma=gamma, V=V, temps="cycle")
+        base, anchor, T, uni = round_dev(inp)
+        h0 = torch.from_numpy(workloads.gru_h0(2, rnd, 1)[0]).to(DEV)
+        tg, lgg, st = wg.walk_gated(W1d, W2d, gated, h0, base, anchor, T, uni, want_logits=True, want_states=True)
+        tm, lgm = wm.walk(W1d, W2d, base, anchor, T, uni, want_logits=True)
+        torch.cuda.synchronize()
+        assert wg.status() == 0 and wm.status() == 0
+        assert torch.equal(tg, tm) and torch.equal(lgg.view(torch.int16), lgm.view(torch.int16))
+        prevs = [int(inp["anchor"][0])] + tg[0, :-1].cpu().tolist()
+        want = torch.from_numpy(oracle_rows_f32(W1, prevs)).to(DEV)
+        assert torch.equal(st, want)
+    wg.close()
+    wm.close()
+
+
+def oracle_rows_f32(W1_bits, rows):
+    """W1 rows as exact f32 values (bf16 bits shifted into the high half)."""
+    return (np.asarray(W1_bits[rows], np.uint32) << 16).view(np.float32)
+
+
+def test_gated_head_argument_errors(dsw):
+    V, gamma = 4_096, 3
+    W1, W2 = workloads.weights(2, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(2, 1, B=1, gamma=gamma, V=V)
+    base, anchor, T, uni = round_dev(inp)
+    Gq, gs, gb = workloads.gated_weights(1)
+    Gqd, gsd, gbd = torch.from_numpy(Gq).to(DEV), torch.from_numpy(gs).to(DEV), torch.from_numpy(gb).to(DEV)
+    h0 = torch.zeros(256, device=DEV)
+    g = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_GATED)
+    # a matrix that is not 16-byte aligned
+    buf = torch.zeros(256 * 256 + 16, dtype=torch.int8, device=DEV)
+    bad = buf[1:1 + 256 * 256].view(256, 256)
+    with pytest.raises(dsw.DswError) as e:
+        g.walk_gated(W1d, W2d, (bad, gsd, gbd), h0, base, anchor, T, uni)
+    assert e.value.code == -11
+    # the Markov, GRU and RNN calls refuse a gated handle; the gated call refuses a GRU handle
+    with pytest.raises(dsw.DswError) as e:
+        g.walk(W1d, W2d, base, anchor, T, uni)
+    assert e.value.code == -11
+    r = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_GRU)
+    with pytest.raises(dsw.DswError) as e:
+        r.walk_gated(W1d, W2d, (Gqd, gsd, gbd), h0, base, anchor, T, uni)
+    assert e.value.code == -11
+    r.close()
+    # the handle still walks after the refused calls
+    tokens, _, _ = g.walk_gated(W1d, W2d, (Gqd, gsd, gbd), h0, base, anchor, T, uni)
+    torch.cuda.synchronize()
+    assert g.status() == 0 and tokens.shape == (1, gamma)
+    g.close()
+
+
 def test_gru_head_argument_errors(dsw):
     V = 4_096
     W1, W2 = workloads.weights(2, V=V)
