@@ -285,9 +285,11 @@ int dsw_walk_rnn(dsw_handle_t h, const void* W1, const void* W2, const void* Wih
  *                            aligned (else DSW_ERR_ARG)
  *   gate_scale  f32 [r]      the codes' row scales
  *   gate_bias   f32 [r]      the gate biases
- * Every workgroup holds Gq (64 KiB) in LDS and updates the whole state; the
- * gates of step k + 1 are formed while step k's keys travel.  Asynchronous;
- * allocates nothing. */
+ * Every workgroup holds Gq in LDS (widened once to bf16, which is exact: 128
+ * KiB) and updates the whole state; the gates of step k + 1 are formed on the
+ * matrix cores while step k's keys travel.  With V > 196,608 the matrix
+ * leaves no LDS for the shard, whose rows beyond the registers then stream
+ * every step.  Asynchronous; allocates nothing. */
 int dsw_walk_gated(dsw_handle_t h, const void* W1, const void* W2, const void* Gq, const float* gate_scale,
                    const float* gate_bias, const float* h0, const void* base, const int32_t* anchor,
                    const float* T, const float* uniforms, int32_t* tokens, void* logits, float* states,
