@@ -87,6 +87,10 @@ def _load():
     lib.oracle_gated_cell.restype = None
     lib.oracle_gated_cell.argtypes = [i, P, P, P, P, P, P]
     lib.oracle_walk_gated.restype = i
+    lib.oracle_gru_cell_in.restype = None
+    lib.oracle_gru_cell_in.argtypes = [i, i, P, P, P, P, P, P, P]
+    lib.oracle_walk_domino.restype = i
+    lib.oracle_walk_domino.argtypes = [i, i, i, i, i] + [P] * 19 + [i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_walk_gated.argtypes = [i, i, i, i] + [P] * 17 + [i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_threads.restype = i
     lib.oracle_philox4x32_10.argtypes = [P, P, P]
@@ -306,6 +310,55 @@ def walk_gated(W1_bits, base_bits, anchor, T, gate, h0, uniforms=None, W2_bits=N
                                    int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF)
     if rc != 0:
         raise RuntimeError(f"oracle_walk_gated failed with {rc}")
+    return tokens, logits, states
+
+
+def gru_cell_in(x, h, Wih_bits, Whh_bits, bih, bhh):
+    """The GRU cell with an input wider than the state: x [in], h [r];
+    Wih [3r, in], Whh [3r, r] bf16 bits, bih, bhh [3r] f32."""
+    x = _c(x, np.float64)
+    h = _c(h, np.float64)
+    r, n_in = h.shape[0], x.shape[0]
+    Wih_bits, Whh_bits = _c(Wih_bits, np.uint16), _c(Whh_bits, np.uint16)
+    bih, bhh = _c(bih, np.float32), _c(bhh, np.float32)
+    assert Wih_bits.shape == (3 * r, n_in) and Whh_bits.shape == (3 * r, r)
+    out = np.empty(r, dtype=np.float64)
+    _load().oracle_gru_cell_in(r, n_in, _ptr(x), _ptr(h), _ptr(Wih_bits), _ptr(Whh_bits), _ptr(bih), _ptr(bhh),
+                               _ptr(out))
+    return out
+
+
+def walk_domino(W1_bits, base_bits, anchor, T, cell, H_bits, h0, uniforms=None, W2_bits=None, Q=None,
+                scale=None, forced=None, forced_h=None, want_logits=True, single_round=False, gumbel=False,
+                seed=0, round_counter=0):
+    """Domino's head: the GRU walk with the drafter's hidden states appended to
+    every step's input.  cell = (Wih [3r, r+d] u16, Whh [3r, r] u16, bih, bhh
+    [3r] f32); H_bits [B, gamma, d] bf16 bits; otherwise as walk_gru."""
+    W1_bits = _c(W1_bits, np.uint16)
+    W2_bits, Q, scale = _c(W2_bits, np.uint16), _c(Q, np.int8), _c(scale, np.float32)
+    Wih, Whh, bih, bhh = _c(cell[0], np.uint16), _c(cell[1], np.uint16), _c(cell[2], np.float32), \
+        _c(cell[3], np.float32)
+    H_bits = _c(H_bits, np.uint16)
+    h0 = _c(h0, np.float32)
+    base_bits = _c(base_bits, np.uint16)
+    anchor, T = _c(anchor, np.int32), _c(T, np.float32)
+    uniforms, forced, forced_h = _c(uniforms, np.float32), _c(forced, np.int32), _c(forced_h, np.float32)
+    V, r = W1_bits.shape
+    B, gamma = base_bits.shape[0], base_bits.shape[1]
+    d = H_bits.shape[2]
+    assert base_bits.shape[2] == V and h0.shape == (B, r) and H_bits.shape[:2] == (B, gamma)
+    assert Wih.shape == (3 * r, r + d)
+    tokens = np.empty((B, gamma), dtype=np.int32)
+    logits = np.empty((B, gamma, V), dtype=np.uint16) if want_logits else None
+    states = np.empty((B, gamma, r), dtype=np.float64)
+    mode = (SINGLE_ROUND if single_round else 0) | (GUMBEL if gumbel else 0)
+    rc = _load().oracle_walk_domino(V, r, d, B, gamma, _ptr(W1_bits), _ptr(W2_bits), _ptr(Q), _ptr(scale),
+                                    _ptr(Wih), _ptr(Whh), _ptr(bih), _ptr(bhh), _ptr(H_bits), _ptr(h0),
+                                    _ptr(base_bits), _ptr(anchor), _ptr(T), _ptr(uniforms), _ptr(forced),
+                                    _ptr(forced_h), _ptr(tokens), _ptr(logits), _ptr(states), mode,
+                                    int(seed) & (2 ** 64 - 1), int(round_counter) & 0xFFFFFFFF)
+    if rc != 0:
+        raise RuntimeError(f"oracle_walk_domino failed with {rc}")
     return tokens, logits, states
 
 

@@ -67,6 +67,11 @@
  * and the vocabulary matrix reads u = bf16(h') as for the other heads.  With
  * b -> -inf the gate closes (g = 0) and the walk is the Markov walk; with
  * b -> +inf the state never moves.
+ * Domino's head (oracle_walk_domino): a GRU cell that also reads the drafter's
+ * hidden states (same section).  Read here as the GRU above whose input at
+ * step k is the concatenation x = [W1[prev]; H_k] of the previous token's row
+ * and the drafter's hidden state H_k (d values) at block position k, so Wih
+ * is [3r][r + d].
  *
  * Parallelism: OpenMP over vocabulary rows inside one GEMV.  Each row's sum
  * is formed by one thread in a fixed order, so results do not depend on the
@@ -435,17 +440,15 @@ int oracle_gumbel_from_uniforms(int V, const double* logit, double T, const doub
  * One GRU cell in binary64 (see the header).  x, h: r values; Wih, Whh:
  * [3r][r] bf16 bits, gate blocks (r, z, n); bih, bhh: [3r] f32; out: r values.
  */
-void oracle_gru_cell(int r, const double* x, const double* h, const uint16_t* Wih, const uint16_t* Whh,
-                     const float* bih, const float* bhh, double* out) {
+void oracle_gru_cell_in(int r, int in, const double* x, const double* h, const uint16_t* Wih,
+                        const uint16_t* Whh, const float* bih, const float* bhh, double* out) {
     for (int j = 0; j < r; ++j) {
         double gi[3], gh[3];
         for (int g = 0; g < 3; ++g) {
             const int row = g * r + j;
             double si = 0.0, sh = 0.0;
-            for (int i = 0; i < r; ++i) {
-                si += bf16_value(Wih[(size_t)row * r + i]) * x[i];
-                sh += bf16_value(Whh[(size_t)row * r + i]) * h[i];
-            }
+            for (int i = 0; i < in; ++i) si += bf16_value(Wih[(size_t)row * in + i]) * x[i];
+            for (int i = 0; i < r; ++i) sh += bf16_value(Whh[(size_t)row * r + i]) * h[i];
             gi[g] = si + (double)bih[row];
             gh[g] = sh + (double)bhh[row];
         }
@@ -454,6 +457,12 @@ void oracle_gru_cell(int r, const double* x, const double* h, const uint16_t* Wi
         const double ng = tanh(gi[2] + rg * gh[2]);
         out[j] = (1.0 - zg) * ng + zg * h[j];
     }
+}
+
+/* The GRU cell with an input as wide as the state (Wih [3r][r]). */
+void oracle_gru_cell(int r, const double* x, const double* h, const uint16_t* Wih, const uint16_t* Whh,
+                     const float* bih, const float* bhh, double* out) {
+    oracle_gru_cell_in(r, r, x, h, Wih, Whh, bih, bhh, out);
 }
 
 /*
@@ -493,6 +502,8 @@ void oracle_gated_cell(int r, const double* x, const double* h, const int8_t* Gq
  * oracle_walk_ex, plus
  *   Wih, Whh, bih, bhh : the cell (see oracle_gru_cell, oracle_rnn_cell)
  *   Gq, gs, gb : the gated head's matrix, row scales and biases (kind 3)
+ *   H, d     : kind 4 (Domino): the drafter's hidden states [B][gamma][d] bf16,
+ *              the GRU's input is [W1[prev]; H[b][k]] and Wih is [3r][r + d]
  *   h0       : [B][r] initial states (f32)
  *   forced_h : [B][gamma][r] f32 or NULL.  When given, step k > 0 of request b
  *              starts from forced_h[b][k-1] instead of the oracle's own state.
@@ -502,7 +513,7 @@ void oracle_gated_cell(int r, const double* x, const double* h, const int8_t* Gq
 static int walk_cell(int kind, int V, int r, int B, int gamma, const uint16_t* W1,
                      const uint16_t* W2, const int8_t* Q, const float* scale,
                      const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
-                     const int8_t* Gq, const float* gs, const float* gb,
+                     const int8_t* Gq, const float* gs, const float* gb, const uint16_t* H, int d,
                      const float* h0, const uint16_t* base, const int32_t* anchor, const float* T,
                      const float* uniforms, const int32_t* forced, const float* forced_h,
                      int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
@@ -511,12 +522,14 @@ static int walk_cell(int kind, int V, int r, int B, int gamma, const uint16_t* W
         (!W2 && (!Q || !scale)))
         return -1;
     if (kind == 3 ? (!Gq || !gs || !gb) : (!Wih || !Whh || !bih || !bhh)) return -1;
+    if (kind == 4 && (!H || d <= 0)) return -1;
+    const int in = kind == 4 ? r + d : r;  /* the cell's input width */
     for (int b = 0; b < B; ++b) {
         if (T[b] != 0.0f && !uniforms && !(mode & ORACLE_GUMBEL)) return -1;
         if (anchor[b] < 0 || anchor[b] >= V) return -1;
     }
     double* lg = (double*)malloc(sizeof(double) * (size_t)V);
-    double* x = (double*)malloc(sizeof(double) * (size_t)r);
+    double* x = (double*)malloc(sizeof(double) * (size_t)in);
     double* h = (double*)malloc(sizeof(double) * (size_t)r);
     double* hn = (double*)malloc(sizeof(double) * (size_t)r);
     uint16_t* ub = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)r);
@@ -531,7 +544,8 @@ static int walk_cell(int kind, int V, int r, int B, int gamma, const uint16_t* W
                 for (int i = 0; i < r; ++i) h[i] = (double)forced_h[((size_t)b * gamma + (k - 1)) * r + i];
             if (prev < 0 || prev >= V) { rc = -1; break; }
             for (int i = 0; i < r; ++i) x[i] = bf16_value(W1[(size_t)prev * r + i]);
-            if (kind == 1) oracle_gru_cell(r, x, h, Wih, Whh, bih, bhh, hn);
+            for (int i = r; i < in; ++i) x[i] = bf16_value(H[((size_t)b * gamma + k) * (size_t)d + (i - r)]);
+            if (kind == 1 || kind == 4) oracle_gru_cell_in(r, in, x, h, Wih, Whh, bih, bhh, hn);
             else if (kind == 2) oracle_rnn_cell(r, x, h, Wih, Whh, bih, bhh, hn);
             else oracle_gated_cell(r, x, h, Gq, gs, gb, hn);
             for (int i = 0; i < r; ++i) {
@@ -561,8 +575,8 @@ int oracle_walk_gru(int V, int r, int B, int gamma, const uint16_t* W1,
                     const float* uniforms, const int32_t* forced, const float* forced_h,
                     int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
                     uint32_t round) {
-    return walk_cell(1, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, h0, base, anchor,
-                     T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
+    return walk_cell(1, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, NULL, 0, h0, base,
+                     anchor, T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
 }
 
 /* The RNN head's walk: as oracle_walk_gru with the tanh RNN cell, Wih, Whh
@@ -574,8 +588,8 @@ int oracle_walk_rnn(int V, int r, int B, int gamma, const uint16_t* W1,
                     const float* uniforms, const int32_t* forced, const float* forced_h,
                     int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
                     uint32_t round) {
-    return walk_cell(2, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, h0, base, anchor,
-                     T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
+    return walk_cell(2, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, NULL, 0, h0, base,
+                     anchor, T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
 }
 
 /* The gated head's walk: as oracle_walk_gru with the gated update, Gq [r][r]
@@ -587,6 +601,19 @@ int oracle_walk_gated(int V, int r, int B, int gamma, const uint16_t* W1,
                       const float* uniforms, const int32_t* forced, const float* forced_h,
                       int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
                       uint32_t round) {
-    return walk_cell(3, V, r, B, gamma, W1, W2, Q, scale, NULL, NULL, NULL, NULL, Gq, gs, gb, h0, base, anchor,
-                     T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
+    return walk_cell(3, V, r, B, gamma, W1, W2, Q, scale, NULL, NULL, NULL, NULL, Gq, gs, gb, NULL, 0, h0, base,
+                     anchor, T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
+}
+
+/* Domino's head: as oracle_walk_gru with Wih [3r][r + d] and the drafter's
+ * hidden states H [B][gamma][d] bf16 appended to every step's input. */
+int oracle_walk_domino(int V, int r, int d, int B, int gamma, const uint16_t* W1,
+                       const uint16_t* W2, const int8_t* Q, const float* scale,
+                       const uint16_t* Wih, const uint16_t* Whh, const float* bih, const float* bhh,
+                       const uint16_t* H, const float* h0, const uint16_t* base, const int32_t* anchor,
+                       const float* T, const float* uniforms, const int32_t* forced, const float* forced_h,
+                       int32_t* tokens, uint16_t* logits, double* states, int mode, uint64_t seed,
+                       uint32_t round) {
+    return walk_cell(4, V, r, B, gamma, W1, W2, Q, scale, Wih, Whh, bih, bhh, NULL, NULL, NULL, H, d, h0, base,
+                     anchor, T, uniforms, forced, forced_h, tokens, logits, states, mode, seed, round);
 }

@@ -457,6 +457,87 @@ def test_gated_walk_limits_and_invariants(oracle_mod):
     assert ok.sum() > 100 and np.median(np.abs(g_a - g_b)) > 0.05
 
 
+# ---------------------------------------------------------------- Domino's head
+def test_hand_worked_domino(oracle_mod):
+    with open(os.path.join(GOLDEN, "hand_domino.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        r, d = c["r"], c["d"]
+        Wih = bits_of(np.asarray(c["Wih"], dtype=np.float64).ravel()).reshape(3 * r, r + d)
+        Whh = bits_of(np.asarray(c["Whh"], dtype=np.float64).ravel()).reshape(3 * r, r)
+        out = oracle_mod.gru_cell_in(c["x"] + c["H"], c["h"], Wih, Whh, c["bih"], c["bhh"])
+        assert np.allclose(out, c["out"], rtol=0, atol=1e-14), (c, out)
+
+
+def _torch_gru_in(r, n_in, x, h, Wih, Whh, bih, bhh):
+    import torch
+    cell = torch.nn.GRUCell(n_in, r).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(value_f64(Wih)))
+        cell.weight_hh.copy_(torch.from_numpy(value_f64(Whh)))
+        cell.bias_ih.copy_(torch.from_numpy(np.asarray(bih, np.float64)))
+        cell.bias_hh.copy_(torch.from_numpy(np.asarray(bhh, np.float64)))
+        return cell(torch.from_numpy(np.asarray(x, np.float64))[None],
+                    torch.from_numpy(np.asarray(h, np.float64))[None])[0].numpy()
+
+
+@pytest.mark.parametrize("r,d", [(1, 1), (8, 5), (256, 2560)])
+def test_domino_cell_matches_torch_grucell(oracle_mod, r, d):
+    Wih, Whh, bih, bhh = workloads.domino_cell_weights(r + d, d=d, r=r)
+    rng = np.random.default_rng(300 + r)
+    for _ in range(3):
+        x = value_f64(workloads.to_bf16_bits(rng.standard_normal(r + d)))
+        h = np.tanh(rng.standard_normal(r))
+        want = _torch_gru_in(r, r + d, x, h, Wih, Whh, bih, bhh)
+        got = oracle_mod.gru_cell_in(x, h, Wih, Whh, bih, bhh)
+        assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_domino_walk_brute_force(oracle_mod, seed):
+    V, r, d, gamma, B = 12, 4, 3, 3, 3
+    dd = workloads.toy(seed + 970, V=V, r=r, B=B, gamma=gamma, w2_std=0.5, base_std=0.5)
+    cell = workloads.domino_cell_weights(seed, d=d, r=r)
+    H = workloads.domino_hidden(seed, 0, B, gamma, d=d)
+    h0 = workloads.gru_h0(seed, 3, B, r=r)
+    toks, logits, states = oracle_mod.walk_domino(dd["W1"], dd["base"], dd["anchor"], np.zeros(B, np.float32),
+                                                  cell, H, h0, W2_bits=dd["W2"])
+    for b in range(B):
+        prev, h = int(dd["anchor"][b]), h0[b].astype(np.float64)
+        for k in range(gamma):
+            x = np.concatenate([value_f64(dd["W1"][prev]), value_f64(H[b, k])])
+            h = _torch_gru_in(r, r + d, x, h, *cell)
+            assert np.allclose(states[b, k], h, rtol=0, atol=1e-13)
+            u = [value(rne_bits(Fraction(float(v)))) for v in states[b, k]]
+            lb = bf.step_logits(dd["W2"], u, dd["base"][b, k])
+            assert logits[b, k].tolist() == lb
+            assert toks[b, k] == bf.argmax_lowest(lb)
+            prev = int(toks[b, k])
+
+
+def test_domino_walk_reduces_to_the_gru_walk(oracle_mod):
+    # zero hidden states (or zero hidden columns of Wih) leave the GRU walk on Wih[:, :r]
+    V, r, d, B, gamma = 2000, 256, 64, 2, 5
+    W1, W2 = workloads.weights(0, V=V)
+    inp = workloads.round_inputs(1, 5, B=B, gamma=gamma, V=V, temps="mixed")
+    Wih, Whh, bih, bhh = workloads.domino_cell_weights(1, d=d)
+    h0 = workloads.gru_h0(0, 5, B)
+    args = (W1, inp["base"], inp["anchor"], inp["T"])
+    tg, lg, sg = oracle_mod.walk_gru(*args, (np.ascontiguousarray(Wih[:, :r]), Whh, bih, bhh), h0,
+                                     uniforms=inp["uniforms"], W2_bits=W2)
+    zH = np.zeros((B, gamma, d), np.uint16)
+    t0, l0, s0 = oracle_mod.walk_domino(*args, (Wih, Whh, bih, bhh), zH, h0, uniforms=inp["uniforms"], W2_bits=W2)
+    assert np.array_equal(t0, tg) and np.array_equal(l0, lg) and np.array_equal(s0, sg)
+    H = workloads.domino_hidden(1, 5, B, gamma, d=d)
+    Wz = Wih.copy()
+    Wz[:, r:] = 0
+    t1, l1, s1 = oracle_mod.walk_domino(*args, (Wz, Whh, bih, bhh), H, h0, uniforms=inp["uniforms"], W2_bits=W2)
+    assert np.array_equal(t1, tg) and np.array_equal(s1, sg)
+    # and the hidden states do move the walk
+    t2, _, s2 = oracle_mod.walk_domino(*args, (Wih, Whh, bih, bhh), H, h0, uniforms=inp["uniforms"], W2_bits=W2)
+    assert np.abs(s2[:, 0] - sg[:, 0]).max() > 0.05
+
+
 def test_gru_walk_teacher_forcing_and_zero_cell(oracle_mod):
     V, r = 2000, 256
     W1, W2 = workloads.weights(0, V=V)

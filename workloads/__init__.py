@@ -152,6 +152,28 @@ def gated_weights(index: int, r: int = R):
     return Gq, gs, gb
 
 
+DOMINO_D = 2560  # the drafter's hidden width (the Qwen3-4B target the pages' Domino runs use)
+
+
+def domino_cell_weights(index: int, d: int = DOMINO_D, r: int = R):
+    """Synthetic Domino cell: a GRU whose input is [W1[prev]; H_k], Wih [3r, r + d]
+    bf16 bits drawn N(0, 1/(r + d)) so that the wide input keeps the gates in
+    range, Whh [3r, r] bf16 bits and both biases N(0, 1/r)."""
+    rng = np.random.Generator(np.random.PCG64(7_700 + index))
+    Wih = to_bf16_bits((1.0 / np.sqrt(r + d)) * rng.standard_normal((3 * r, r + d), dtype=np.float32))
+    sd = 1.0 / np.sqrt(r)
+    Whh = to_bf16_bits(sd * rng.standard_normal((3 * r, r), dtype=np.float32))
+    bih = (sd * rng.standard_normal(3 * r)).astype(np.float32)
+    bhh = (sd * rng.standard_normal(3 * r)).astype(np.float32)
+    return Wih, Whh, bih, bhh
+
+
+def domino_hidden(index: int, round_index: int, B: int, gamma: int, d: int = DOMINO_D):
+    """The drafter's hidden states of one round, [B, gamma, d] bf16 bits, N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(9_000_000 + 1000 * index + round_index))
+    return to_bf16_bits(rng.standard_normal((B, gamma, d), dtype=np.float32))
+
+
 def gru_h0(index: int, round_index: int, B: int, r: int = R):
     """Initial GRU states [B, r] f32 in (-1, 1): tanh of N(0, 1)."""
     rng = np.random.Generator(np.random.PCG64(8_000_000 + 1000 * index + round_index))
