@@ -219,6 +219,8 @@ SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, 
          (1, 1, 7, "bf16", "inverse_cdf", "rnn"),
          # DSpark's gated head (DSW_FLAG_GATED) on the headline and the long walk
          (1, 1, 7, "bf16", "inverse_cdf", "gated"), (2, 1, 16, "bf16", "inverse_cdf", "gated"),
+         # Domino's head (DSW_FLAG_DOMINO; hidden width 2560) on the headline and the long walk
+         (1, 1, 7, "bf16", "inverse_cdf", "domino"), (2, 1, 16, "bf16", "inverse_cdf", "domino"),
          # one GPU's share of a two-GPU vocabulary split (the kernel at its real shape;
          # the cross-GPU exchange is not built): half of V = 151,936 and of V = 248,320
          (1, 1, 7, "bf16", "inverse_cdf", "markov", 75_968), (3, 1, 16, "bf16", "inverse_cdf", "markov", 124_160)]
@@ -248,7 +250,8 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="m
     walker = dsw.Walker(V, gamma_max=gamma, B_max=B, w2_dtype=dsw.INT8 if dtype == "int8" else dsw.BF16,
                         flags=(dsw.FLAG_GUMBEL if sampler == "gumbel" else 0) |
                               (dsw.FLAG_GRU if head == "gru" else 0) | (dsw.FLAG_RNN if head == "rnn" else 0) |
-                              (dsw.FLAG_GATED if head == "gated" else 0))
+                              (dsw.FLAG_GATED if head == "gated" else 0) |
+                              (dsw.FLAG_DOMINO if head == "domino" else 0))
     if sampler == "gumbel":
         walker.set_seed(0x5EED + index)
     plan = walker.query_plan(B)
@@ -259,12 +262,21 @@ def sweep_one(torch, dsw, index, B, gamma, dtype, sampler="inverse_cdf", head="m
         cw = workloads.gru_cell_weights(index, gates=3 if head == "gru" else 1)
         celld = (bf(cw[0]), bf(cw[1]), torch.from_numpy(cw[2]).to(dev), torch.from_numpy(cw[3]).to(dev))
         h0 = torch.from_numpy(workloads.gru_h0(index, 0, 1)[0]).to(dev)
+    if head == "domino":
+        cw = workloads.domino_cell_weights(index)
+        celld = (bf(cw[0]), bf(cw[1]), torch.from_numpy(cw[2]).to(dev), torch.from_numpy(cw[3]).to(dev))
+        hid = bf(workloads.domino_hidden(index, 0, 1, gamma)[0])
+        h0 = torch.from_numpy(workloads.gru_h0(index, 0, 1)[0]).to(dev)
     if head == "gated":
         gw = workloads.gated_weights(index)
         gated = tuple(torch.from_numpy(a).to(dev) for a in gw)
         h0 = torch.from_numpy(workloads.gru_h0(index, 0, 1)[0]).to(dev)
 
     def go(j):
+        if head == "domino":
+            walker.walk_domino(W1d, W2d, celld, hid, h0, base[j % n], anchor[j % n], T[j % n], uni[j % n],
+                               tokens=tokens)
+            return
         if head == "gated":
             walker.walk_gated(W1d, W2d, gated, h0, base[j % n], anchor[j % n], T[j % n], uni[j % n], tokens=tokens)
             return

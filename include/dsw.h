@@ -135,6 +135,12 @@ extern "C" {
                                     walks go through dsw_walk_gated.  The same
                                     limits as DSW_FLAG_GRU, and not with it
                                     or DSW_FLAG_RNN.                           */
+#define DSW_FLAG_DOMINO 1024u    /* Domino's serial head (same section): walks
+                                    go through dsw_walk_domino.  The limits of
+                                    DSW_FLAG_GRU, one head flag per handle,
+                                    gamma_max <= 16 (DSW_ERR_GAMMA) and a grid
+                                    of r workgroups (DSW_ERR_PLAN on a device
+                                    with fewer CUs).                           */
 
 /* Device description the planner works from.  dsw_device_info() fills it
  * from the HIP runtime; tests may pass invented devices to dsw_plan_compute. */
@@ -294,6 +300,26 @@ int dsw_walk_gated(dsw_handle_t h, const void* W1, const void* W2, const void* G
                    const float* gate_bias, const float* h0, const void* base, const int32_t* anchor,
                    const float* T, const float* uniforms, int32_t* tokens, void* logits, float* states,
                    int B, int gamma, void* stream);
+
+/* One round of Domino's serial head ("Keeping the Draft Walk on Chip",
+ * section "Beyond DSpark: other serial heads": a GRU cell that also reads the
+ * drafter's hidden states).  Read here as dsw_walk_gru whose input at step k
+ * is the concatenation x = [W1[prev]; H[k]] of the previous token's row and
+ * the drafter's hidden state at block position k.  Handle created with
+ * DSW_FLAG_DOMINO (the other walk calls refuse it with DSW_ERR_ARG, and this
+ * call refuses other handles).  Arguments as dsw_walk_gru except (device
+ * pointers):
+ *   Wih  bf16 [3r][r + d]  input weights, gate blocks (r, z, n), 16-byte aligned
+ *   H    bf16 [gamma][d]   the drafter's hidden states, 16-byte aligned
+ *   d                      hidden width: 8 <= d <= 4096, d % 8 == 0
+ * (DSW_ERR_ARG otherwise).  Each workgroup forms the hidden states' part of
+ * its state element's gate pre-activations for all gamma steps when the walk
+ * starts; every step then runs the GRU head's step with that part added.
+ * Asynchronous; allocates nothing. */
+int dsw_walk_domino(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
+                    const float* bih, const float* bhh, const float* h0, const void* H, int d,
+                    const void* base, const int32_t* anchor, const float* T, const float* uniforms,
+                    int32_t* tokens, void* logits, float* states, int B, int gamma, void* stream);
 
 /* Wait for the handle's device, then return and clear the status word that
  * the device latches (0 or a DSW_ERR_DEV_* code).  After a device error the

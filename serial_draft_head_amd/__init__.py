@@ -41,6 +41,7 @@ FLAG_GUMBEL = 64
 FLAG_GRU = 128
 FLAG_RNN = 256
 FLAG_GATED = 512
+FLAG_DOMINO = 1024
 ENGINE_VALU, ENGINE_MFMA = 0, 1
 RANK = 256
 
@@ -103,6 +104,7 @@ def lib():
         L.dsw_walk_gru.argtypes = [P] * 15 + [I, I, P]
         L.dsw_walk_rnn.argtypes = [P] * 15 + [I, I, P]
         L.dsw_walk_gated.argtypes = [P] * 14 + [I, I, P]
+        L.dsw_walk_domino.argtypes = [P] * 9 + [I] + [P] * 7 + [I, I, P]
         L.dsw_status.argtypes = [P]
         L.dsw_query_plan.argtypes = [P, I, ctypes.POINTER(PlanInfo)]
         L.dsw_destroy.argtypes = [P]
@@ -111,7 +113,7 @@ def lib():
         L.dsw_set_seed.argtypes = [P, ctypes.c_ulonglong, I]
         L.dsw_round_counter.argtypes = [P, ctypes.POINTER(ctypes.c_uint)]
         L.dsw_set_trace.argtypes = [P, P, ctypes.c_longlong]
-        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn", "dsw_walk_gated",
+        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn", "dsw_walk_gated", "dsw_walk_domino",
                   "dsw_status",
                   "dsw_query_plan", "dsw_destroy", "dsw_set_seed", "dsw_round_counter", "dsw_set_trace"):
             getattr(L, f).restype = I
@@ -263,6 +265,21 @@ class Walker:
         return self._walk_cell(spec, "dsw_walk_gated", W1, W2, gate, h0, base, anchor, T, uniforms, tokens,
                                logits, states, want_logits, want_states, stream)
 
+    def walk_domino(self, W1, W2, cell, H, h0, base, anchor, T, uniforms=None, tokens=None, logits=None,
+                    states=None, want_logits=False, want_states=False, stream=None):
+        """One round of Domino's serial head (handle made with FLAG_DOMINO; one
+        request): the GRU head whose input at step k is [W1[prev]; H[k]].
+        cell = (Wih bf16 [3r, r+d], Whh bf16 [3r, r], bih f32 [3r], bhh f32 [3r]);
+        H bf16 [gamma, d]; as walk_gru otherwise."""
+        import torch
+        r = self.r
+        gamma, d = int(base.shape[1]), int(H.shape[-1])
+        spec = [(cell[0], torch.bfloat16, (3 * r, r + d), "Wih"), (cell[1], torch.bfloat16, (3 * r, r), "Whh"),
+                (cell[2], torch.float32, (3 * r,), "bih"), (cell[3], torch.float32, (3 * r,), "bhh")]
+        return self._walk_cell(spec, "dsw_walk_domino", W1, W2, cell, h0, base, anchor, T, uniforms, tokens,
+                               logits, states, want_logits, want_states, stream,
+                               after_h0=[(H, torch.bfloat16, (gamma, d), "H")], after_h0_ints=[d])
+
     def _cell_spec(self, cell, gates):
         import torch
         r = self.r
@@ -270,13 +287,14 @@ class Walker:
                 (cell[2], torch.float32, (gates * r,), "bih"), (cell[3], torch.float32, (gates * r,), "bhh")]
 
     def _walk_cell(self, spec, fname, W1, W2, cell, h0, base, anchor, T, uniforms, tokens, logits,
-                   states, want_logits, want_states, stream):
+                   states, want_logits, want_states, stream, after_h0=(), after_h0_ints=()):
         import torch
         dev = torch.device("cuda", self.device)
         B, gamma, V = (int(x) for x in base.shape)
         r = self.r
         need = [(W1, torch.bfloat16, (self.V, r), "W1"), (W2, torch.bfloat16, (self.V, r), "W2")] + spec + [
-                (h0, torch.float32, (r,), "h0"), (base, torch.bfloat16, (B, gamma, self.V), "base"),
+                (h0, torch.float32, (r,), "h0")] + list(after_h0) + [
+                (base, torch.bfloat16, (B, gamma, self.V), "base"),
                 (anchor, torch.int32, (B,), "anchor"), (T, torch.float32, (B,), "T")]
         if uniforms is not None:
             need.append((uniforms, torch.float32, (B, gamma), "uniforms"))
@@ -297,7 +315,7 @@ class Walker:
                                  f"{t.dtype} {tuple(t.shape)} on {t.device}")
         ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
         rc = getattr(lib(), fname)(self._h, ptr(W1), ptr(W2), *[ptr(t[0]) for t in spec], ptr(h0),
-                                   ptr(base), ptr(anchor), ptr(T), ptr(uniforms), ptr(tokens), ptr(logits),
+                                   *[ptr(t[0]) for t in after_h0], *after_h0_ints, ptr(base), ptr(anchor), ptr(T), ptr(uniforms), ptr(tokens), ptr(logits),
                                    ptr(states), B, gamma, _stream_handle(torch, dev, stream))
         _check(rc, fname)
         return tokens, logits, states

@@ -25,23 +25,28 @@ extern "C" const void* dsw_internal_mfma_i8_kernel_gumbel(int batch_tile, int re
 extern "C" const void* dsw_internal_mfma_kernel_b1_gru(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b1_rnn(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b1_gated(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b1_domino(int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs (with Gumbel-max sampling when `gumbel`), or
 // nullptr.  The planner never gives a Gumbel-max handle the batched kernel.
 // The head a handle's flags select: 0 the Markov head, 1 the GRU head, 2 the
-// RNN head, 3 the gated head.
+// RNN head, 3 the gated head, 4 Domino's head.
 int cell_of(unsigned flags) {
-    return (flags & DSW_FLAG_GRU) ? 1 : ((flags & DSW_FLAG_RNN) ? 2 : ((flags & DSW_FLAG_GATED) ? 3 : 0));
+    if (flags & DSW_FLAG_GRU) return 1;
+    if (flags & DSW_FLAG_RNN) return 2;
+    if (flags & DSW_FLAG_GATED) return 3;
+    return (flags & DSW_FLAG_DOMINO) ? 4 : 0;
 }
 
 // cell: as cell_of
 const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell) {
     if (cell) {  // the planner gives the recurrent heads only the one-request MFMA engine
         if (pl.engine != DSW_ENGINE_MFMA || pl.batch_tile != 1 || pl.w2_dtype != DSW_BF16) return nullptr;
-        return (cell == 1 ? dsw_internal_mfma_kernel_b1_gru
-                          : (cell == 2 ? dsw_internal_mfma_kernel_b1_rnn : dsw_internal_mfma_kernel_b1_gated))(
-            pl.reg_tiles, pl.max_tiles);
+        const void* (*const lookup[])(int, int) = {dsw_internal_mfma_kernel_b1_gru, dsw_internal_mfma_kernel_b1_rnn,
+                                                   dsw_internal_mfma_kernel_b1_gated,
+                                                   dsw_internal_mfma_kernel_b1_domino};
+        return cell <= 4 ? lookup[cell - 1](pl.reg_tiles, pl.max_tiles) : nullptr;
     }
     if (pl.batch_tile == dsw::kMaxBatch)
         return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
@@ -253,6 +258,8 @@ struct GruArgs {
     const int8_t* gq;
     const float* gs;
     const float* gb;
+    const uint16_t* hidden;  // Domino's head: H [gamma][d]
+    int d;
 };
 
 int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale, const void* base,
@@ -329,6 +336,9 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     p.gate_q = gru ? gru->gq : nullptr;
     p.gate_scale = gru ? gru->gs : nullptr;
     p.gate_bias = gru ? gru->gb : nullptr;
+    p.hidden = gru ? gru->hidden : nullptr;
+    p.hidden_d = gru ? gru->d : 0;
+    p.cell_in = dsw::kRank + p.hidden_d;
     p.trace = nullptr;
     if (h->trace != nullptr &&
         (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)
@@ -362,7 +372,7 @@ extern "C" int dsw_walk_gru(dsw_handle_t h, const void* W1, const void* W2, cons
     if (cell_of(h->flags) != 1) return DSW_ERR_ARG;
     if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
     const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states,
-                    nullptr, nullptr, nullptr};
+                    nullptr, nullptr, nullptr, nullptr, 0};
     return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
 }
 
@@ -374,7 +384,7 @@ extern "C" int dsw_walk_rnn(dsw_handle_t h, const void* W1, const void* W2, cons
     if (cell_of(h->flags) != 2) return DSW_ERR_ARG;
     if (B > 0 && gamma > 0 && (!Wih || !Whh || !bih || !bhh || !h0)) return DSW_ERR_NULL;
     const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states,
-                    nullptr, nullptr, nullptr};
+                    nullptr, nullptr, nullptr, nullptr, 0};
     return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
 }
 
@@ -389,7 +399,25 @@ extern "C" int dsw_walk_gated(dsw_handle_t h, const void* W1, const void* W2, co
         if (reinterpret_cast<uintptr_t>(Gq) % 16 != 0) return DSW_ERR_ARG;  // read as 16-byte words
     }
     const GruArgs g{nullptr, nullptr, nullptr, nullptr, h0, states, static_cast<const int8_t*>(Gq), gate_scale,
-                    gate_bias};
+                    gate_bias, nullptr, 0};
+    return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
+}
+
+extern "C" int dsw_walk_domino(dsw_handle_t h, const void* W1, const void* W2, const void* Wih, const void* Whh,
+                               const float* bih, const float* bhh, const float* h0, const void* H, int d,
+                               const void* base, const int32_t* anchor, const float* T, const float* uniforms,
+                               int32_t* tokens, void* logits, float* states, int B, int gamma, void* stream) {
+    if (!h) return DSW_ERR_NULL;
+    if (cell_of(h->flags) != 4) return DSW_ERR_ARG;
+    if (d < 8 || d > dsw::kDominoMaxD || d % 8 != 0) return DSW_ERR_ARG;
+    if (B > 0 && gamma > 0) {
+        if (!Wih || !Whh || !bih || !bhh || !h0 || !H) return DSW_ERR_NULL;
+        // read as 16-byte words
+        if (reinterpret_cast<uintptr_t>(Wih) % 16 != 0 || reinterpret_cast<uintptr_t>(H) % 16 != 0)
+            return DSW_ERR_ARG;
+    }
+    const GruArgs g{static_cast<const uint16_t*>(Wih), static_cast<const uint16_t*>(Whh), bih, bhh, h0, states,
+                    nullptr, nullptr, nullptr, static_cast<const uint16_t*>(H), d};
     return walk_impl(h, W1, W2, nullptr, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, &g);
 }
 

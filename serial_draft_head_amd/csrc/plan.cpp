@@ -67,8 +67,10 @@ static int mfma_tile_for(int B, bool i8) { return (B <= 1 && !i8) ? 1 : (B <= 4 
 // step's gates.
 static int cell_lds(unsigned flags) {
     if (flags & DSW_FLAG_GATED) return kRank * kRank * 2 + 4 * kRank * 4 + 2 * kRank * 2;
-    const int gates = (flags & DSW_FLAG_GRU) ? 3 : ((flags & DSW_FLAG_RNN) ? 1 : 0);
-    return gates ? kRank * 4 + kCellMaxPerWg * 2 * gates * (kRank * 2 + 4) + kCellMaxPerWg * gates * 4 : 0;
+    const int gates = (flags & (DSW_FLAG_GRU | DSW_FLAG_DOMINO)) ? 3 : ((flags & DSW_FLAG_RNN) ? 1 : 0);
+    // Domino's head: the hidden states' pre-activations of every step and their partial sums
+    const int domino = (flags & DSW_FLAG_DOMINO) ? 5 * kDominoMaxGamma * 3 * 4 : 0;
+    return gates ? kRank * 4 + kCellMaxPerWg * 2 * gates * (kRank * 2 + 4) + kCellMaxPerWg * gates * 4 + domino : 0;
 }
 static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum, unsigned flags) {
     const int rpad = max_tiles * 4 * kTileRows;
@@ -338,13 +340,16 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     // the recurrent heads: one bf16 request on the one-request MFMA engine, and
     // (GRU, RNN) a grid of at least r / kCellMaxPerWg workgroups to hold the
     // state; the gated head keeps the whole state in every workgroup
-    const unsigned heads = flags & (DSW_FLAG_GRU | DSW_FLAG_RNN | DSW_FLAG_GATED);
+    const unsigned heads = flags & (DSW_FLAG_GRU | DSW_FLAG_RNN | DSW_FLAG_GATED | DSW_FLAG_DOMINO);
     const bool cell = heads != 0;
     if (heads & (heads - 1)) return DSW_ERR_ARG;  // one head per handle
     if (cell) {
         if (B > 1 || batched || gumbel || (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
         if (i8) return DSW_ERR_DTYPE;
         if (!(flags & DSW_FLAG_GATED) && grid * kCellMaxPerWg < kRank) return DSW_ERR_PLAN;
+        // Domino's head: one state element per workgroup, its drafters' block length
+        if ((flags & DSW_FLAG_DOMINO) && grid < kRank) return DSW_ERR_PLAN;
+        if ((flags & DSW_FLAG_DOMINO) && gamma > kDominoMaxGamma) return DSW_ERR_GAMMA;
     }
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
     // one bf16 request: the MFMA engine's step is ~1 us shorter, but its shard

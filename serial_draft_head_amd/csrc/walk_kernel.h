@@ -147,11 +147,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     static_assert(!kOne || !kI8, "one-request MFMA engine: bf16 rows");
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
     constexpr bool kCell = CELL != 0;                           // a recurrent head
-    constexpr bool kGru = CELL == 1;
+    constexpr bool kDomino = CELL == 4;                         // the GRU reading the drafter's hidden states
+    constexpr bool kGru = CELL == 1 || kDomino;
     constexpr bool kGated = CELL == 3;                          // the whole state in every workgroup
     constexpr bool kShard = kCell && !kGated;                   // the state spread over the workgroups
-    constexpr int kGates = CELL == 1 ? 3 : 1;                    // cell rows per input, per element
-    static_assert(CELL >= 0 && CELL <= 3, "cell");
+    constexpr int kGates = kGru ? 3 : 1;                         // cell rows per input, per element
+    static_assert(CELL >= 0 && CELL <= 4, "cell");
     static_assert(!kCell || (kOne && GUM == 0), "recurrent heads: the one-request MFMA engine");
     static_assert(!kCell || kBlock == kRank, "recurrent heads: one state element per thread in the gather");
     constexpr int RPAD = kMfma ? M * 4 * kTileRows : kMaxSlots * kBlock;  // rows per shard, bound
@@ -178,6 +179,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // recurrent heads: Whh h + bhh of the owned elements for the coming step,
     // formed while the previous step's keys travel
     __shared__ float s_gh[kShard ? kCellMaxPerWg * kGates : 1];
+    // Domino's head (one state element per workgroup): the hidden states' part
+    // of the element's three input pre-activations for every step, and the
+    // waves' partial sums that form it
+    __shared__ float s_P[kDomino ? kDominoMaxGamma * 3 : 1];
+    __shared__ float s_pp[kDomino ? 4 * kDominoMaxGamma * 3 : 1];
     // gated head: the matrix widened once from int8 to bf16 (exact), as 16
     // MFMA B-operand tiles of 16 rows in the order [tile][K block][lane]; the
     // row scales and biases; the gates of the coming step; and the state's
@@ -323,7 +329,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             uint16_t wv = 0;
             if (j < kRank) {
                 const uint16_t* W = q < kGates ? p.gru_wih : p.gru_whh;
-                wv = W[(size_t)((q % kGates) * kRank + j) * kRank + m];
+                wv = W[(size_t)((q % kGates) * kRank + j) * (q < kGates ? p.cell_in : kRank) + m];
             }
             s_cw[e] = wv;
         }
@@ -331,6 +337,56 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             const int i = t / kRows, q = t % kRows, j = c + i * G;
             s_cb[t] = j < kRank ? (q < kGates ? p.gru_bih : p.gru_bhh)[(q % kGates) * kRank + j] : 0.0f;
         }
+    }
+    if constexpr (kDomino) {
+        // P[k][q] = Wih[q r + c][r .. r + d) . H[k]: thread t takes the 16-byte
+        // slices t and t + kBlock of the d hidden columns (d <= 2 * 8 * kBlock),
+        // eight steps' hidden states loaded at a time; fp32 sums of exact
+        // products, reduced over each wave and then over the four waves
+        const int d8 = p.hidden_d / 8, in8 = p.cell_in / 8;
+        const uint4* Wr = reinterpret_cast<const uint4*>(p.gru_wih);
+        const uint4* Hh = reinterpret_cast<const uint4*>(p.hidden);
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+        auto dot8 = [](const uint4 a, const uint4 b, float acc) {
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = fmaf(bf16_to_f32(aw[i] & 0xFFFFu), bf16_to_f32(bw[i] & 0xFFFFu), acc);
+                acc = fmaf(bf16_to_f32(aw[i] >> 16), bf16_to_f32(bw[i] >> 16), acc);
+            }
+            return acc;
+        };
+        uint4 wq[3][2];
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int e8 = t + s * kBlock;
+                wq[q][s] = e8 < d8 ? Wr[(size_t)(q * kRank + c) * in8 + kRank / 8 + e8] : z4;
+            }
+#pragma unroll 1
+        for (int k0 = 0; k0 < gamma; k0 += 8) {
+            uint4 hv[8][2];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int e8 = t + s * kBlock;
+                    hv[kk][s] = (k0 + kk < gamma && e8 < d8) ? Hh[(size_t)(k0 + kk) * d8 + e8] : z4;
+                }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    const float part = dot8(wq[q][1], hv[kk][1], dot8(wq[q][0], hv[kk][0], 0.0f));
+                    const float tot = __shfl(wave_incl_scan_dpp(part), 63);
+                    if (lane == 0) s_pp[(wave * kDominoMaxGamma + k0 + kk) * 3 + q] = tot;
+                }
+        }
+        __syncthreads();
+        if (t < kDominoMaxGamma * 3)
+            s_P[t] = (s_pp[t] + s_pp[kDominoMaxGamma * 3 + t]) +
+                     (s_pp[2 * kDominoMaxGamma * 3 + t] + s_pp[3 * kDominoMaxGamma * 3 + t]);
     }
 
     // ---- entry: this workgroup's shard on chip -------------------------
@@ -649,6 +705,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 }
 #pragma unroll
                 for (int q = 0; q < kGates; ++q) acc[q] = __shfl(wave_incl_scan_dpp(acc[q]), 63);
+                if constexpr (kDomino) {  // the hidden states' part of the input (one element, wave 0)
+#pragma unroll
+                    for (int q = 0; q < kGates; ++q) acc[q] += s_P[k * 3 + q];
+                }
                 const float* cb = s_cb + wave * 2 * kGates;
                 const float* gh = s_gh + wave * kGates;
                 float hn;

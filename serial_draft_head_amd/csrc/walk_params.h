@@ -25,6 +25,8 @@ constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 16 exp-sum words
 constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
 constexpr int kCellMaxPerWg = 4;   // recurrent heads: state elements per workgroup (one per wave; grid >= 64)
+constexpr int kDominoMaxGamma = 16;  // Domino's head: steps per round (its drafters' blocks)
+constexpr int kDominoMaxD = 4096;    // Domino's head: the drafter's hidden width, bound
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
 constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests
@@ -106,7 +108,7 @@ struct WalkParams {
     // and biases [g*r] f32 -- g = 3 for the GRU (CELL = 1; gates r, z, n),
     // g = 1 for the tanh RNN (CELL = 2) -- the initial state [r] f32, and an
     // optional [gamma][r] f32 output of every step's state
-    const uint16_t* gru_wih;
+    const uint16_t* gru_wih;         // rows of cell_in values (r, or r + d for Domino's head)
     const uint16_t* gru_whh;
     const float* gru_bih;
     const float* gru_bhh;
@@ -117,6 +119,11 @@ struct WalkParams {
     const int8_t* gate_q;
     const float* gate_scale;
     const float* gate_bias;
+    // Domino's head (CELL = 4; the GRU with the drafter's hidden states appended
+    // to its input): hidden states [gamma][hidden_d] bf16, 16-byte aligned
+    const uint16_t* hidden;
+    int hidden_d;
+    int cell_in;             // Wih row length: r, or r + hidden_d
     unsigned long long* trace;  // optional [grid][gamma+1][8] phase timestamps, or null
 };
 

@@ -171,25 +171,30 @@ def check_round(w: Weights, base, anchor, T, uniforms, gpu_tokens, gpu_logits, s
 F32_EPS = 2.0 ** -24
 
 
-def check_gru_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states):
+def check_gru_states(W1_bits, cell, h0, gpu_tokens, anchor, gpu_states, hidden=None):
     """The GPU's state after every step against the oracle's binary64 GRU cell
     applied to the GPU's previous state (teacher forcing), within a bound of
     the fp32 evaluation: each of the six dot products (r bf16 x bf16 or bf16 x
     fp32 terms, fma) and its bias adds err <= g_(r+4) (sum |w v| + |b|) with
     g_n = n 2^-24 / (1 - n 2^-24); sigmoid' <= 1/4, tanh' <= 1; each fp32
     exp/divide/tanh adds 4 ulps of its result, the final blend 3 ulps.
+    hidden: [gamma, d] bf16 bits of Domino's head, appended to every step's
+    input (Wih is then [3r, r + d] and the dot products have r + d terms).
     Returns (steps checked, largest error, largest error / bound)."""
     Wih, Whh, bih, bhh = cell
     Wi, Wh = oracle.bf16_bits_to_f64(Wih), oracle.bf16_bits_to_f64(Whh)
-    r = Wi.shape[1]
-    gam = (r + 4) * F32_EPS / (1 - (r + 4) * F32_EPS)
+    r = Wh.shape[1]
+    n_in = Wi.shape[1]
+    gam = (n_in + 4) * F32_EPS / (1 - (n_in + 4) * F32_EPS)
     gamma = gpu_states.shape[0]
     worst, worst_ratio = 0.0, 0.0
     for k in range(gamma):
         prev = int(anchor) if k == 0 else int(gpu_tokens[k - 1])
         x = oracle.bf16_bits_to_f64(W1_bits[prev])
+        if hidden is not None:
+            x = np.concatenate([x, oracle.bf16_bits_to_f64(hidden[k])])
         h = h0.astype(np.float64) if k == 0 else gpu_states[k - 1].astype(np.float64)
-        want = oracle.gru_cell(x, h, Wih, Whh, bih, bhh)
+        want = oracle.gru_cell_in(x, h, Wih, Whh, bih, bhh)
         gi = Wi @ x + bih
         gh = Wh @ h + bhh
         Ei = gam * (np.abs(Wi) @ np.abs(x) + np.abs(bih))

@@ -62,6 +62,7 @@ def test_null_and_argument_errors_without_a_device(dsw):
     assert L.dsw_walk_gru(None, *([None] * 14), 1, 1, None) == -1
     assert L.dsw_walk_rnn(None, *([None] * 14), 1, 1, None) == -1
     assert L.dsw_walk_gated(None, *([None] * 13), 1, 1, None) == -1
+    assert L.dsw_walk_domino(None, *([None] * 8), 64, *([None] * 7), 1, 1, None) == -1
 
 
 def fake_device(dsw, cus=256, lds_cu=160 * 1024, lds_blk=160 * 1024):
@@ -261,6 +262,27 @@ def test_planner_gated_head(dsw):
         with pytest.raises(dsw.DswError) as e:
             dsw.plan(d, 151_936, 7, B, w2_dtype=dt, flags=flags)
         assert e.value.code == code
+
+
+def test_planner_domino_head(dsw):
+    d = fake_device(dsw)
+    D = dsw.FLAG_DOMINO
+    p, g = dsw.plan(d, 151_936, 16, 1, flags=D), dsw.plan(d, 151_936, 16, 1, flags=dsw.FLAG_GRU)
+    assert (p.engine, p.batch_tile, p.reg_tiles) == (1, 1, 10)
+    # the GRU head's LDS and the hidden states' pre-activations of 16 steps with their partial sums
+    assert p.static_lds_bytes == g.static_lds_bytes + 5 * 16 * 3 * 4
+    for B, flags, dt, code in ((2, D, dsw.BF16, -11), (1, D | dsw.FLAG_GRU, dsw.BF16, -11),
+                               (1, D | dsw.FLAG_GATED, dsw.BF16, -11), (1, D, dsw.INT8, -5)):
+        with pytest.raises(dsw.DswError) as e:
+            dsw.plan(d, 151_936, 7, B, w2_dtype=dt, flags=flags)
+        assert e.value.code == code
+    with pytest.raises(dsw.DswError) as e:
+        dsw.plan(d, 151_936, 17, 1, flags=D)
+    assert e.value.code == -3
+    # one state element per workgroup: r workgroups
+    with pytest.raises(dsw.DswError) as e:
+        dsw.plan(fake_device(dsw, cus=128), 32_000, 7, 1, flags=D)
+    assert e.value.code == -10
 
 
 def test_planner_int8_rows(dsw):

@@ -642,6 +642,77 @@ def test_gated_head_argument_errors(dsw):
     g.close()
 
 
+DOMINO_CASES = [(4_097, 5, "greedy", 2560), (32_000, 15, "cycle", 2560), (151_936, 16, "greedy", 4096),
+                (151_936, 7, "greedy", 8)]
+
+
+@pytest.mark.parametrize("V,gamma,temps,d", DOMINO_CASES)
+def test_domino_head(dsw, V, gamma, temps, d):
+    import oracle
+    say(f"domino head V={V} gamma={gamma} {temps} d={d}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    cell = workloads.domino_cell_weights(1, d=d)
+    celld = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+             torch.from_numpy(cell[3]).to(DEV))
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_DOMINO)
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 900 + rnd, B=1, gamma=gamma, V=V, temps=temps)
+        h0 = workloads.gru_h0(2, rnd, 1)
+        H = workloads.domino_hidden(2, rnd, 1, gamma, d=d)
+        base, anchor, T, uni = round_dev(inp)
+        tokens, logits, states = walker.walk_domino(W1d, W2d, celld, bf16_dev(H[0]), torch.from_numpy(h0[0]).to(DEV),
+                                                    base, anchor, T, uni, want_logits=True, want_states=True)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        st = states.cpu().numpy()
+        n, worst, ratio = parity.check_gru_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st, hidden=H[0])
+        ub = oracle.rne_bf16(st.astype(np.float64))[1][None]
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 latents=ub)
+        say(rnd, f"states: {n} steps, largest error {worst:.3g} ({ratio:.3f} of its bound)", rep)
+    walker.close()
+
+
+def test_domino_head_argument_errors(dsw):
+    V, gamma, d = 4_096, 3, 64
+    W1, W2 = workloads.weights(2, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    inp = workloads.round_inputs(2, 1, B=1, gamma=gamma, V=V)
+    base, anchor, T, uni = round_dev(inp)
+    cell = workloads.domino_cell_weights(1, d=d)
+    celld = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+             torch.from_numpy(cell[3]).to(DEV))
+    H = bf16_dev(workloads.domino_hidden(2, 1, 1, gamma, d=d)[0])
+    h0 = torch.zeros(256, device=DEV)
+    g = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=dsw.FLAG_DOMINO)
+    # hidden width not a multiple of 8, and misaligned hidden states
+    c12 = workloads.domino_cell_weights(1, d=12)
+    c12d = (bf16_dev(c12[0]), celld[1], celld[2], celld[3])
+    with pytest.raises(dsw.DswError) as e:
+        g.walk_domino(W1d, W2d, c12d, bf16_dev(workloads.domino_hidden(2, 1, 1, gamma, d=12)[0]), h0, base,
+                      anchor, T, uni)
+    assert e.value.code == -11
+    buf = torch.zeros(gamma * d + 8, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(dsw.DswError) as e:
+        g.walk_domino(W1d, W2d, celld, buf[1:1 + gamma * d].view(gamma, d), h0, base, anchor, T, uni)
+    assert e.value.code == -11
+    # the other heads' calls refuse the handle; more than 16 steps are refused at creation
+    with pytest.raises(dsw.DswError) as e:
+        g.walk(W1d, W2d, base, anchor, T, uni)
+    assert e.value.code == -11
+    with pytest.raises(dsw.DswError) as e:
+        dsw.Walker(V, gamma_max=17, B_max=1, flags=dsw.FLAG_DOMINO)
+    assert e.value.code == -3
+    tokens, _, _ = g.walk_domino(W1d, W2d, celld, H, h0, base, anchor, T, uni)
+    torch.cuda.synchronize()
+    assert g.status() == 0 and tokens.shape == (1, gamma)
+    g.close()
+
+
 def test_gru_head_argument_errors(dsw):
     V = 4_096
     W1, W2 = workloads.weights(2, V=V)
