@@ -713,6 +713,71 @@ def test_domino_head_argument_errors(dsw):
     g.close()
 
 
+@pytest.mark.parametrize("head", ["gru", "rnn", "gated", "domino"])
+def test_recurrent_heads_single_rounding_and_device_uniforms(dsw, head):
+    # every recurrent head with DSW_FLAG_SINGLE_ROUND and sampled steps whose
+    # uniforms the device draws from the seed (T = 1 at every step)
+    import oracle
+    V, gamma, d = 32_000, 9, 256
+    say(f"{head} head, single rounding, device uniforms, V={V} gamma={gamma}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    flag = {"gru": dsw.FLAG_GRU, "rnn": dsw.FLAG_RNN, "gated": dsw.FLAG_GATED, "domino": dsw.FLAG_DOMINO}[head]
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=flag | dsw.FLAG_SINGLE_ROUND)
+    seed = 0x5EED_1234 + flag
+    walker.set_seed(seed)
+    if head in ("gru", "rnn"):
+        cell = workloads.gru_cell_weights(3, gates=3 if head == "gru" else 1)
+    elif head == "domino":
+        cell = workloads.domino_cell_weights(3, d=d)
+    else:
+        cell = workloads.gated_weights(3)
+    if head == "gated":
+        dev_cell = tuple(torch.from_numpy(a).to(DEV) for a in cell)
+    else:
+        dev_cell = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+                    torch.from_numpy(cell[3]).to(DEV))
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 950 + rnd, B=1, gamma=gamma, V=V, temps="cycle")
+        inp["T"][:] = 1.0
+        h0 = workloads.gru_h0(3, rnd, 1)
+        h0d = torch.from_numpy(h0[0]).to(DEV)
+        base, anchor, T, _ = round_dev(inp)
+        ctr = walker.round_counter()
+        kw = dict(want_logits=True, want_states=True)
+        if head == "gru":
+            tokens, logits, states = walker.walk_gru(W1d, W2d, dev_cell, h0d, base, anchor, T, None, **kw)
+        elif head == "rnn":
+            tokens, logits, states = walker.walk_rnn(W1d, W2d, dev_cell, h0d, base, anchor, T, None, **kw)
+        elif head == "gated":
+            tokens, logits, states = walker.walk_gated(W1d, W2d, dev_cell, h0d, base, anchor, T, None, **kw)
+        else:
+            H = workloads.domino_hidden(3, rnd, 1, gamma, d=d)
+            tokens, logits, states = walker.walk_domino(W1d, W2d, dev_cell, bf16_dev(H[0]), h0d, base, anchor, T,
+                                                        None, **kw)
+        torch.cuda.synchronize()
+        assert walker.status() == 0 and walker.round_counter() == ctr + 1
+        toks = tokens.cpu().numpy()
+        lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+        st = states.cpu().numpy()
+        if head == "gru":
+            n, worst, ratio = parity.check_gru_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+        elif head == "rnn":
+            n, worst, ratio = parity.check_rnn_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+        elif head == "gated":
+            n, worst, ratio = parity.check_gated_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+        else:
+            n, worst, ratio = parity.check_gru_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st, hidden=H[0])
+        ub = oracle.rne_bf16(st.astype(np.float64))[1][None]
+        uni = oracle.device_uniforms(seed, ctr, 1, gamma)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], uni, toks, lg, latents=ub,
+                                 single_round=True)
+        assert rep["sampled"] == gamma
+        say(rnd, f"states: {n} steps, largest error {worst:.3g} ({ratio:.3f} of its bound)", rep)
+    walker.close()
+
+
 def test_gru_head_argument_errors(dsw):
     V = 4_096
     W1, W2 = workloads.weights(2, V=V)
