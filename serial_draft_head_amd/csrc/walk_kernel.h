@@ -129,7 +129,11 @@ __device__ __forceinline__ uint4 as_bf16x8(const uint2& q) {
 // every workgroup gathers all r of them before its GEMV.  CELL = 3: DSpark's
 // gated head, whose one r x r matrix is small enough in int8 for every
 // workgroup to hold it and update the whole state itself (no state exchange):
-// g = sigmoid(s (Gq h) + b) from the state, h' = g h + (1 - g) x.  One request.
+// g = sigmoid(s (Gq h) + b) from the state, h' = g h + (1 - g) x.  CELL = 4:
+// Domino's head, the GRU of CELL = 1 whose input also carries the drafter's
+// hidden state H_k of block position k, x = [W1[prev]; H_k]; the hidden
+// states' part of the input pre-activations is formed for every step when the
+// kernel starts (one state element per workgroup).  One request.
 template <int ENGINE, int A, int M, int NB, int DT = 0, int GUM = 0, int CELL = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
