@@ -778,6 +778,56 @@ def test_recurrent_heads_single_rounding_and_device_uniforms(dsw, head):
     walker.close()
 
 
+def _random_configs(n, seed=2026):
+    """Seeded random walks over the planner's paths: ragged vocabularies, any
+    batch, 1..16 steps, bf16 or int8 rows, engine, streaming, rounding and
+    sampler flags (combinations the planner refuses are drawn again)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        V = int(rng.integers(1_000, 160_000))
+        B = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 40]))
+        gamma = int(rng.integers(1, 17))
+        gamma = max(1, min(gamma, 3_000_000 // (V * B)))  # the oracle's share stays small
+        dt = "int8" if rng.random() < 0.25 else "bf16"
+        opts = [0, 8, 4, 8 | 1, 64] if B <= 16 else [0, 16]
+        flags = int(rng.choice(opts)) | (32 if rng.random() < 0.3 else 0)
+        if dt == "int8" and (flags & 4) and B > 1:
+            continue  # int8 rows on the VALU engine: one request
+        temps = "greedy" if rng.random() < 0.3 else "mixed"
+        out.append((V, B, gamma, dt, flags, temps))
+    return out
+
+
+@pytest.mark.parametrize("V,B,gamma,dt,flags,temps", _random_configs(12))
+def test_random_walks(dsw, V, B, gamma, dt, flags, temps):
+    import oracle  # noqa: F401  (parity loads it)
+    say(f"random walk V={V} B={B} gamma={gamma} {dt} flags={flags} {temps}")
+    W1, W2 = workloads.weights(2, V=V)
+    W1d = bf16_dev(W1)
+    if dt == "int8":
+        Q, sc = workloads.quantize_int8(W2)
+        w = parity.Weights(W1, Q=Q, scale=sc)
+        W2d, sd = int8_dev(Q, sc)
+    else:
+        w = parity.Weights(W1, W2)
+        W2d, sd = bf16_dev(W2), None
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=B, flags=flags,
+                        w2_dtype=dsw.INT8 if dt == "int8" else dsw.BF16)
+    seed = 0xABCD_0000 + V
+    if flags & 64:
+        walker.set_seed(seed)
+    say("plan", walker.query_plan(B).as_dict())
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 1000 + rnd, B=B, gamma=gamma, V=V, temps=temps)
+        ctr = walker.round_counter()
+        toks, lg = run(walker, W1d, W2d, inp, scale=sd)
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg,
+                                 single_round=bool(flags & 32), gumbel=(seed, ctr) if flags & 64 else None)
+        say(rnd, rep)
+    walker.close()
+
+
 def test_gru_head_argument_errors(dsw):
     V = 4_096
     W1, W2 = workloads.weights(2, V=V)
