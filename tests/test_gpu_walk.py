@@ -828,6 +828,63 @@ def test_random_walks(dsw, V, B, gamma, dt, flags, temps):
     walker.close()
 
 
+def _random_head_configs(n, seed=2027):
+    rng = np.random.default_rng(seed)
+    heads = ["gru", "rnn", "gated", "domino"]
+    return [(heads[i % 4], int(rng.integers(1_000, 200_000)), int(rng.integers(1, 17)),
+             "greedy" if rng.random() < 0.4 else "cycle", bool(rng.random() < 0.4), 8 * int(rng.integers(1, 513)))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("head,V,gamma,temps,single,d", _random_head_configs(8))
+def test_random_recurrent_walks(dsw, head, V, gamma, temps, single, d):
+    import oracle
+    say(f"random {head} walk V={V} gamma={gamma} {temps} single={single} d={d}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    flag = {"gru": dsw.FLAG_GRU, "rnn": dsw.FLAG_RNN, "gated": dsw.FLAG_GATED, "domino": dsw.FLAG_DOMINO}[head]
+    walker = dsw.Walker(V, gamma_max=gamma, B_max=1, flags=flag | (dsw.FLAG_SINGLE_ROUND if single else 0))
+    if head == "gated":
+        cell = workloads.gated_weights(V % 7)
+        dev_cell = tuple(torch.from_numpy(a).to(DEV) for a in cell)
+    else:
+        cell = (workloads.domino_cell_weights(V % 7, d=d) if head == "domino"
+                else workloads.gru_cell_weights(V % 7, gates=3 if head == "gru" else 1))
+        dev_cell = (bf16_dev(cell[0]), bf16_dev(cell[1]), torch.from_numpy(cell[2]).to(DEV),
+                    torch.from_numpy(cell[3]).to(DEV))
+    inp = workloads.round_inputs(2, 1100 + gamma, B=1, gamma=gamma, V=V, temps=temps)
+    h0 = workloads.gru_h0(V % 5, gamma, 1)
+    h0d = torch.from_numpy(h0[0]).to(DEV)
+    base, anchor, T, uni = round_dev(inp)
+    kw = dict(want_logits=True, want_states=True)
+    H = None
+    if head == "domino":
+        H = workloads.domino_hidden(V % 5, gamma, 1, gamma, d=d)
+        tokens, logits, states = walker.walk_domino(W1d, W2d, dev_cell, bf16_dev(H[0]), h0d, base, anchor, T, uni,
+                                                    **kw)
+    else:
+        fn = {"gru": walker.walk_gru, "rnn": walker.walk_rnn, "gated": walker.walk_gated}[head]
+        tokens, logits, states = fn(W1d, W2d, dev_cell, h0d, base, anchor, T, uni, **kw)
+    torch.cuda.synchronize()
+    assert walker.status() == 0
+    toks = tokens.cpu().numpy()
+    lg = logits.view(torch.int16).cpu().numpy().view(np.uint16)
+    st = states.cpu().numpy()
+    if head == "rnn":
+        n, worst, ratio = parity.check_rnn_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+    elif head == "gated":
+        n, worst, ratio = parity.check_gated_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st)
+    else:
+        n, worst, ratio = parity.check_gru_states(W1, cell, h0[0], toks[0], inp["anchor"][0], st,
+                                                  hidden=None if H is None else H[0])
+    ub = oracle.rne_bf16(st.astype(np.float64))[1][None]
+    rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg, latents=ub,
+                             single_round=single)
+    say(f"states: {n} steps, largest error {worst:.3g} ({ratio:.3f} of its bound)", rep)
+    walker.close()
+
+
 def test_gru_head_argument_errors(dsw):
     V = 4_096
     W1, W2 = workloads.weights(2, V=V)
