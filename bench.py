@@ -341,6 +341,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations")
     ap.add_argument("--pmc-mode", action="store_true",
                     help="for counter runs: 50 walks, then one 256 MiB device copy of known size")
+    ap.add_argument("--heads-only", action="store_true",
+                    help="only the recurrent heads' configurations of the sweep (for profiling)")
     ap.add_argument("--stepwise-only", action="store_true",
                     help="for counter runs: only the step-wise library-op loop, then the same copy")
     args = ap.parse_args()
@@ -352,6 +354,11 @@ def main():
 
     import serial_draft_head_amd as dsw
     import workloads
+
+    if args.heads_only:
+        heads = [sweep_one(torch, dsw, *cfg) for cfg in SWEEP if len(cfg) > 5 and cfg[5] != "markov"]
+        print(json.dumps({"heads_only": True, "configs": heads}))
+        return
 
     wl = workloads.WORKLOADS[args.workload]
     B = args.B if args.B is not None else wl.batches[0]
