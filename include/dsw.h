@@ -204,13 +204,20 @@ int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int
                      unsigned flags, dsw_plan_info* out);
 
 /* Create a handle for walks on `device` with vocabulary V, rank r (must be
- * 256), at most gamma_max steps and B_max (1 .. 256) requests per call, and W2 stored
- * as w2_dtype.  Allocates and zeroes the device workspace (cross-workgroup
- * mailboxes, arrival counters, a round counter and a status word), and, when
- * the handle can run the batched kernel (B_max >= 4 or DSW_FLAG_BATCHED),
- * B_max * V * 2 bytes where that kernel keeps the current step's logits of its
- * sampled requests for the shard that draws their token; the handle owns
- * both.  The calling thread's current device is left unchanged. */
+ * 256), at most gamma_max (1 .. 4096) steps and B_max (1 .. 256) requests per
+ * call, and W2 stored as w2_dtype.  The handle holds what the pages' resident
+ * kernel keeps between replays ("Keeping the Draft Walk on Chip", section "The
+ * idea: make the walk resident": every CTA posts into a shared exchange area,
+ * and a round parity lets graph replays run without a memset): it allocates
+ * and zeroes the device workspace (per-workgroup mailboxes for both step
+ * parities, per-kernel-family launch counters that select the step epochs, a
+ * round counter and a status word), and, when the handle can run the batched
+ * kernel (B_max >= 4 or DSW_FLAG_BATCHED), B_max * V * 2 bytes where that
+ * kernel keeps the current step's logits of its sampled requests for the shard
+ * that draws their token; the handle owns both.  It also checks, with the
+ * occupancy API, that every kernel the handle can run fits one workgroup per
+ * CU (DSW_ERR_LAUNCH otherwise).  The calling thread's current device is left
+ * unchanged. */
 int dsw_create(dsw_handle_t* h, int device, int V, int r, int gamma_max, int B_max,
                int w2_dtype, unsigned flags);
 
@@ -322,13 +329,21 @@ int dsw_walk_domino(dsw_handle_t h, const void* W1, const void* W2, const void* 
                     int32_t* tokens, void* logits, float* states, int B, int gamma, void* stream);
 
 /* Wait for the handle's device, then return and clear the status word that
- * the device latches (0 or a DSW_ERR_DEV_* code).  After a device error the
- * workspace is re-zeroed so that the next call starts clean. */
+ * the device latches (0 or a DSW_ERR_DEV_* code).  The pages' kernel bounds
+ * every cross-CTA wait ("Keeping the Draft Walk on Chip", section "The idea:
+ * make the walk resident": CTAs poll the arrival count); here a wait that
+ * exceeds its bound latches DSW_ERR_DEV_TIMEOUT and every workgroup exits.
+ * While a device error is latched, later walks on the handle return at once
+ * without touching their outputs; after a device error this call re-zeroes
+ * the workspace (counters included) so that the next walk starts clean. */
 int dsw_status(dsw_handle_t h);
 
 /* The plan dsw_walk uses for batch size B on this handle, for a walk of
  * gamma_max steps (one bf16 request walking up to 3 steps takes the VALU
- * engine instead: see dsw_plan_compute with the walk's own gamma). */
+ * engine instead: see dsw_plan_compute with the walk's own gamma): the
+ * slice-per-CTA split and its on-chip / streamed rows of "Keeping the Draft
+ * Walk on Chip", sections "The idea: make the walk resident" and "V = 248,320:
+ * 62% on chip, the rest streamed".  Host only. */
 int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out);
 
 /* Device-drawn uniforms.  With enable != 0, later dsw_walk calls that pass
@@ -361,7 +376,35 @@ int dsw_round_counter(dsw_handle_t h, unsigned* out);
  * `bytes` record nothing. */
 int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes);
 
-/* Free the workspace and the handle.  NULL is accepted. */
+/* Diagnostics and tests of the exchange ("Keeping the Draft Walk on Chip",
+ * section "The idea: make the walk resident": CTAs post, then poll until
+ * every CTA has arrived).  spin_limit: polls before a device wait gives up
+ * (0 restores the default, about 2^20); a small value makes the waits give
+ * up, which latches DSW_ERR_DEV_TIMEOUT while every workgroup still exits.
+ * skew (0 .. 64, else DSW_ERR_ARG): 0, or before each post every workgroup
+ * sleeps a pseudo-random 0..7 times skew units of ~8k clocks, so that the
+ * workgroups reach each rendezvous in a scrambled order.  Later walks on
+ * the handle use both. */
+int dsw_set_debug(dsw_handle_t h, unsigned spin_limit, unsigned skew);
+
+/* Test hook: waits for the device, then sets the round counter and both
+ * kernel families' launch counters to `value` (e.g. just below a 32-bit
+ * wrap of the step sequence numbers). */
+int dsw_set_round_counter(dsw_handle_t h, unsigned value);
+
+/* The epoch a mailbox word carries at step sequence number seq (gamma_max
+ * times the family's launch count plus the step, mod 2^32): (seq mod 2^27)
+ * + 1.  Host only. */
+unsigned dsw_debug_epoch(unsigned seq);
+
+/* Diagnostics: out[i] = the Gumbel variate -ln(-ln U) the kernels compute for
+ * U = (2 i + 1) 2^-24, for every i < 2^23 (every U of DSW_FLAG_GUMBEL's
+ * noise).  out: device buffer of 2^23 floats on the current device; runs
+ * asynchronously on `stream`. */
+int dsw_debug_gumbel_table(float* out, void* stream);
+
+/* Wait for the handle's device, then free the workspace and the handle (the
+ * end of the handle's exchange area, see dsw_create).  NULL is accepted. */
 int dsw_destroy(dsw_handle_t h);
 
 /* Static description of a DSW_* code. */

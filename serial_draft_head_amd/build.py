@@ -20,7 +20,9 @@ HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b1.hip", "walk_mfma_b4.hip", "walk_mf
                "walk_mfma_b16_gumbel.hip", "walk_mfma_i8_gumbel.hip",
                # the one-request kernels for the recurrent serial heads (GRU, RNN, gated, Domino)
                "walk_mfma_b1_gru.hip", "walk_mfma_b1_rnn.hip", "walk_mfma_b1_gated.hip",
-               "walk_mfma_b1_domino.hip"]
+               "walk_mfma_b1_domino.hip",
+               # diagnostics
+               "walk_debug.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 # Packed-fp32 VALU forms are kept out of every code object.

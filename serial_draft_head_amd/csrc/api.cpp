@@ -82,6 +82,8 @@ struct dsw_handle {
     int seeded;
     unsigned long long* trace;  // optional device trace buffer (caller-owned)
     long long trace_bytes;
+    unsigned spin_limit;        // polls before a device wait gives up
+    unsigned skew;              // diagnostics: pseudo-random delays before posts (0 = none)
     std::mutex mu;  // guards the per-kernel attribute cache below
     const void* lds_configured[64];  // kernels whose dynamic-LDS ceiling was raised
     int lds_configured_bytes[64];
@@ -147,7 +149,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     if (r != dsw::kRank) return DSW_ERR_RANK;
     if (w2_dtype != DSW_BF16 && w2_dtype != DSW_INT8) return DSW_ERR_DTYPE;
     if (V < 1) return DSW_ERR_VOCAB;
-    if (gamma_max < 1) return DSW_ERR_GAMMA;
+    if (gamma_max < 1 || gamma_max > dsw::kMaxGammaMax) return DSW_ERR_GAMMA;
     if (B_max < 1 || B_max > dsw::kMaxBatch) return DSW_ERR_BATCH;
     dsw_devinfo dev;
     int rc = dsw_device_info(device, &dev);
@@ -169,6 +171,8 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->dev = dev;
     h->trace = nullptr;
     h->trace_bytes = 0;
+    h->spin_limit = kSpinLimit;
+    h->skew = 0u;
     h->seed = 0ull;
     h->seeded = 0;
     memset(h->lds_configured, 0, sizeof(h->lds_configured));
@@ -181,8 +185,8 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws_bytes = L.total;
     if (hipMalloc(&h->ws_mem, L.total) != hipSuccess) { delete h; return DSW_ERR_HIP; }
     h->ws.mail = reinterpret_cast<unsigned long long*>(h->ws_mem + L.mail);
-    h->ws.tok_mail = reinterpret_cast<unsigned long long*>(h->ws_mem + L.tok_mail);
     h->ws.round_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.round_ctr);
+    h->ws.fam_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.fam_ctr);
     h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.status);
     h->ws.bkey = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bkey);
     h->ws.bsum = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bsum);
@@ -323,7 +327,8 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     p.rows_pad = plan.rows_pad;
     p.ring = plan.ring_slots;
     p.aligned = (h->V % 8) == 0;
-    p.spin_limit = kSpinLimit;
+    p.spin_limit = h->spin_limit;
+    p.skew = h->skew;
     p.single_round = (h->flags & DSW_FLAG_SINGLE_ROUND) ? 1 : 0;
     p.seeded = h->seeded;
     p.seed = h->seed;
@@ -435,6 +440,33 @@ extern "C" int dsw_round_counter(dsw_handle_t h, unsigned* out) {
     if (hipDeviceSynchronize() != hipSuccess) return DSW_ERR_HIP;
     if (hipMemcpy(out, h->ws.round_ctr, sizeof *out, hipMemcpyDeviceToHost) != hipSuccess) return DSW_ERR_HIP;
     return DSW_OK;
+}
+
+extern "C" int dsw_set_debug(dsw_handle_t h, unsigned spin_limit, unsigned skew) {
+    if (!h) return DSW_ERR_NULL;
+    if (skew > 64u) return DSW_ERR_ARG;
+    h->spin_limit = spin_limit ? spin_limit : kSpinLimit;
+    h->skew = skew;
+    return DSW_OK;
+}
+
+extern "C" int dsw_set_round_counter(dsw_handle_t h, unsigned value) {
+    if (!h) return DSW_ERR_NULL;
+    DeviceGuard g(h->device);
+    if (!g.ok) return DSW_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return DSW_ERR_HIP;
+    const unsigned v[3] = {value, value, value};
+    if (hipMemcpy(h->ws.round_ctr, &v[0], sizeof v[0], hipMemcpyHostToDevice) != hipSuccess) return DSW_ERR_HIP;
+    if (hipMemcpy(h->ws.fam_ctr, &v[1], 2 * sizeof v[0], hipMemcpyHostToDevice) != hipSuccess) return DSW_ERR_HIP;
+    return DSW_OK;
+}
+
+extern "C" unsigned dsw_debug_epoch(unsigned seq) { return dsw::epoch_of(seq); }
+
+extern "C" int dsw_internal_gumbel_table(float* out, void* stream);
+extern "C" int dsw_debug_gumbel_table(float* out, void* stream) {
+    if (!out) return DSW_ERR_NULL;
+    return dsw_internal_gumbel_table(out, stream) == 0 ? DSW_OK : DSW_ERR_HIP;
 }
 
 extern "C" int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes) {

@@ -109,6 +109,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ float s_tgt;
     __shared__ int s_ntask;
     __shared__ unsigned s_round;
+    __shared__ unsigned s_fam;
     __shared__ int s_abort;
     DSW_TRACE_DECL;
     __shared__ int s_any_samp;
@@ -152,10 +153,29 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 
     if (t == 0) {
         s_round = ld_agent(p.ws.round_ctr);
-        s_abort = 0;
+        s_fam = ld_agent(p.ws.fam_ctr + kFamBatched);
+        // a device error latched by an earlier launch stands until dsw_status
+        // clears the workspace: this launch then does nothing
+        s_abort = ld_agent(status) != 0u;
         s_any_samp = 0;
     }
+    // every word this workgroup posts in this launch, both parities, starts at
+    // 0 (the barriers before the first post order these stores first): its row
+    // of keys, exp-sums and tokens, and the decision words of the requests it owns
+    for (int i = t; i < 2 * p.B_max; i += kBlock) {
+        const size_t o = ((size_t)(i / p.B_max) * kMaxGrid + c) * kMaxBatch + i % p.B_max;
+        st_agent64(p.ws.bkey + o, 0ull);
+        st_agent64(p.ws.bsum + o, 0ull);
+        st_agent64(p.ws.btok + o, 0ull);
+    }
+    for (int b = c + (t >> 1) * G; b < p.B_max; b += (kBlock >> 1) * G) {
+        const int par = t & 1;
+        st_agent64(p.ws.bdec + (size_t)par * kMaxBatch + b, 0ull);
+        st_agent64(p.ws.bext + ((size_t)par * kMaxBatch + b) * 2, 0ull);
+        st_agent64(p.ws.bext + ((size_t)par * kMaxBatch + b) * 2 + 1, 0ull);
+    }
     __syncthreads();
+    if (s_abort) return;  // uniform: read after the barrier
     DSW_TRACE(gamma, 0);
     if (t < B) {
         int a = p.anchor[t];
@@ -211,6 +231,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         for (int r = t; r < RPAD; r += kBlock) s_scale[r] = r < nrows ? p.w2_scale[v0 + r] : 0.0f;
     __syncthreads();
     const unsigned round = s_round;
+    const unsigned fam = s_fam;
     const bool any_samp = s_any_samp != 0;
 
     // MFMA over every tile of this wave with B operand ub[8]; EPI(d, j) gets
@@ -273,13 +294,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     // ---- the walk --------------------------------------------------------
     for (int k = 0; k < gamma; ++k) {
         DSW_TRACE(k, kTrStepStart);
-        const unsigned seq = round * (unsigned)p.gamma_max + (unsigned)k;
-        const unsigned long long epoch = (unsigned long long)(seq % kEpochMod + 1u);
+        const unsigned seq = fam * (unsigned)p.gamma_max + (unsigned)k;
+        const unsigned long long epoch = epoch_of(seq);
         const int q = (int)(seq & 1u);
         unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch;
         unsigned long long* bsum = p.ws.bsum + (size_t)q * kMaxGrid * kMaxBatch;
         unsigned long long* bdec = p.ws.bdec + (size_t)q * kMaxBatch;
-        unsigned long long* btok = p.ws.btok + (size_t)q * kMaxBatch;
+        unsigned long long* btok = p.ws.btok + (size_t)q * kMaxGrid * kMaxBatch;  // [shard][request]
 
         // group gq's u rows and base logits into ring slot gq % D.  Each lane
         // names its own source; the wave's 64 chunks land contiguously.
@@ -475,6 +496,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         DSW_TRACE(k, kTrGemvDone);
 
         // ---- post: one key word (and exp-sum word) per request -----------
+        walk_skew(p, c, k, 0);
         if (t < B) {
             const uint32_t lk = max(max(s_rkey[0][t], s_rkey[1][t]), max(s_rkey[2][t], s_rkey[3][t]));
             st_agent64(&bkey[(size_t)c * kMaxBatch + t], (global_key(lk, v0) << 28) | epoch);
@@ -576,11 +598,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             if (!(s_T[b] > 0.0f)) {
                 if (t == 0) {
                     const int tok = checked_token(key_index(win), V, status);
+                    walk_skew(p, c, k, 1);
                     st_agent64(&bdec[b], ((unsigned long long)(unsigned)tok << 28) | epoch);
                 }
             } else {
                 DSW_OWNER_SHARD(b, kw, sw, key_logit(win));
                 if (t == 0) {
+                    walk_skew(p, c, k, 1);
                     unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2;
                     st_agent64(&ext[0], ((unsigned long long)__float_as_uint(s_pex) << 32) | epoch);
                     st_agent64(&ext[1], ((unsigned long long)__float_as_uint(s_tgt) << 32) | epoch);
@@ -686,7 +710,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 if (lane == 0) {
                     const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
                     s_next[b] = tok;
-                    st_agent64(&btok[b], ((unsigned long long)(unsigned)tok << 28) | epoch);
+                    walk_skew(p, c, k, 2);
+                    st_agent64(&btok[(size_t)c * kMaxBatch + b], ((unsigned long long)(unsigned)tok << 28) | epoch);
                 }
             }
             __syncthreads();
@@ -696,7 +721,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 unsigned it = 0;
                 unsigned long long w = 0ull;
                 bool ok = true;
-                while (((w = ld_agent64(&btok[t])) & kEpochMod) != epoch) {
+                const unsigned long long* tw = &btok[(size_t)(s_dec[t] >> 21) * kMaxBatch + t];
+                while (((w = ld_agent64(tw)) & kEpochMod) != epoch) {
                     if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
                     if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
                     __builtin_amdgcn_s_sleep(1);
@@ -723,8 +749,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #undef DSW_TILES
 
     DSW_TRACE_FLUSH();
-    if (c == 0 && t == 0 && !s_abort)
+    if (c == 0 && t == 0 && !s_abort) {
         __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.ws.fam_ctr + kFamBatched, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // (register tiles, tiles per wave) shapes of the batched kernel

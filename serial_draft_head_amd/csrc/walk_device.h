@@ -97,9 +97,11 @@ __device__ __forceinline__ float walk_uniform(const WalkParams& p, int b, int k,
 // noise keyed by seed, row, step and round counter).  Vocabulary rows 4m ..
 // 4m+3 of request b at step k share the call on counter (m, 256 k + b, round,
 // 0x47554D42); word e maps to U = (2 (w >> 9) + 1) 2^-24, strictly inside
-// (0, 1) and exact in fp32.  Returns the variate G = -ln(-ln U).  -ln U is
-// taken as -log1p(U - 1) on [0.5, 1), where U - 1 is exact, so that U close
-// to 1 (the rows with the largest G) keeps its relative precision.
+// (0, 1) and exact in fp32.  Returns the variate G = -ln(-ln U), both
+// logarithms taken with the hardware base-2 logarithm (v_log_f32) times ln 2,
+// straight on U.  Over all 2^23 values U can take, -ln U stays within 2e-7
+// relative and G within 2e-6 absolute of binary64 (a GPU test evaluates this
+// function on every one of them, dsw_debug_gumbel_table).
 __device__ __forceinline__ float gumbel_of_word(uint32_t w) {
     const float U = (float)(2u * (w >> 9) + 1u) * (1.0f / 16777216.0f);
     const float e = -0.69314718f * __builtin_amdgcn_logf(U);
@@ -159,6 +161,21 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
         if (lane >= off) x += y;
     }
     return x;
+}
+
+// Diagnostics (dsw_set_debug): with p.skew > 0, the calling wave sleeps
+// before a post for a pseudo-random number (0..7, from the workgroup, step and
+// call site) of p.skew units of s_sleep 127 (~8k clocks each), so that
+// workgroups reach the rendezvous in a scrambled order.  Bounded; never runs
+// with p.skew == 0.
+__device__ __forceinline__ void walk_skew(const WalkParams& p, int c, int k, int site) {
+    if (p.skew == 0u) return;
+    uint32_t h = (uint32_t)c * 0x9E3779B1u ^ ((uint32_t)k * 0x85EBCA77u + (uint32_t)site * 0xC2B2AE3Du);
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    const uint32_t n = (h & 7u) * p.skew;
+    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
 // A token id that will index W1: out-of-range ids latch kStatusToken and

@@ -215,6 +215,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     __shared__ int s_anchor[NB];
     __shared__ int s_prev[NB];
     __shared__ unsigned s_round;
+    __shared__ unsigned s_fam;
     __shared__ int s_abort;
     DSW_TRACE_DECL;
 
@@ -252,8 +253,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 
     if (t == 0) {
         s_round = ld_agent(p.ws.round_ctr);
-        s_abort = 0;
+        s_fam = ld_agent(p.ws.fam_ctr + kFamAll);
+        // a device error latched by an earlier launch stands until dsw_status
+        // clears the workspace: this launch then does nothing
+        s_abort = ld_agent(status) != 0u;
     }
+    // every word this workgroup posts in this launch, both parities, starts
+    // at 0 (the barriers before the first post order these stores first)
+    if (t < 2 * kMailWords)
+        st_agent64(p.ws.mail + ((size_t)(t / kMailWords) * kMaxGrid + c) * kMailWords + t % kMailWords, 0ull);
     DSW_TRACE(gamma, 0);
     if (t < NB) {
         int a = 0;
@@ -525,7 +533,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             }
     }
     __syncthreads();
+    if (s_abort) return;  // uniform: read after the barrier
     const unsigned round = s_round;
+    const unsigned fam = s_fam;
     bool any_samp = false;
 #pragma unroll
     for (int b = 0; b < NB; ++b) any_samp |= (b < B) && (s_T[b] > 0.0f);
@@ -649,8 +659,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // ---- the walk --------------------------------------------------------
     for (int k = 0; k < gamma; ++k) {
         DSW_TRACE(k, kTrStepStart);
-        const unsigned seq = round * (unsigned)p.gamma_max + (unsigned)k;
-        const unsigned long long epoch = (unsigned long long)(seq % kEpochMod + 1u);
+        const unsigned seq = fam * (unsigned)p.gamma_max + (unsigned)k;
+        const unsigned long long epoch = epoch_of(seq);
         const int q = (int)(seq & 1u);
         unsigned long long* mail_q = p.ws.mail + (size_t)q * kMaxGrid * kMailWords;
 
@@ -1096,6 +1106,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         }
 
         // ---- rendezvous: post, write the logits out, read every mailbox ------
+        if (wave == 0) walk_skew(p, c, k, 0);
         if (wave == 0 && lane < B) {
             const uint32_t lk = max(max(s_wbest[0][lane], s_wbest[1][lane]), max(s_wbest[2][lane], s_wbest[3][lane]));
             unsigned long long* box = mail_q + (size_t)c * kMailWords;
@@ -1103,12 +1114,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 // Gumbel-max: {score, epoch} and {~id, epoch}
                 const unsigned long long gk = max(max(s_gk[lane], s_gk[NB + lane]),
                                                   max(s_gk[2 * NB + lane], s_gk[3 * NB + lane]));
-                st_agent64(&box[lane], ((gk >> kIdxBits) << 32) | epoch);
-                st_agent64(&box[kMaxBatchPersistent + lane], ((gk & kIdxMask) << 32) | epoch);
+                st_agent64(&box[kMailKeys + lane], ((gk >> kIdxBits) << 32) | epoch);
+                st_agent64(&box[kMailSums + lane], ((gk & kIdxMask) << 32) | epoch);
             } else {
-                st_agent64(&box[lane], (global_key(lk, v0) << 28) | epoch);
+                st_agent64(&box[kMailKeys + lane], (global_key(lk, v0) << 28) | epoch);
                 if (s_T[lane] > 0.0f)
-                    st_agent64(&box[kMaxBatchPersistent + lane],
+                    st_agent64(&box[kMailSums + lane],
                                ((unsigned long long)__float_as_uint(s_tot[lane]) << 32) | epoch);
             }
         }
@@ -1142,8 +1153,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #define DSW_POLL(w)                                                                        \
     _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                       \
         if (NB == 1 || b < B) {                                                            \
-            w[b][0] = ld_agent64(&box[b]);                                                 \
-            if (s_T[b] > 0.0f) w[b][1] = ld_agent64(&box[kMaxBatchPersistent + b]);        \
+            w[b][0] = ld_agent64(&box[kMailKeys + b]);                                     \
+            if (s_T[b] > 0.0f) w[b][1] = ld_agent64(&box[kMailSums + b]);                  \
         }                                                                                  \
     }
         if constexpr (kGated) {
@@ -1190,11 +1201,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         if (b < B) {
-                            const unsigned long long wk = ld_agent64(&box[b]);
+                            const unsigned long long wk = ld_agent64(&box[kMailKeys + b]);
                             if ((wk & kEpochMod) == epoch) kw[b] = wk >> 28;
                             else ready = false;
                             if (s_T[b] > 0.0f) {
-                                const unsigned long long ws = ld_agent64(&box[kMaxBatchPersistent + b]);
+                                const unsigned long long ws = ld_agent64(&box[kMailSums + b]);
                                 if ((ws & kEpochMod) == epoch) sw[b] = (uint32_t)(ws >> 32);
                                 else ready = false;
                             }
@@ -1320,15 +1331,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int row = fm ? (int)(0xFFFFFFFFu - fm) - 1 : (lm ? (int)lm - 1 : -1);
                 const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
                 __syncthreads();
-                if (t == 0) {
-                    s_prev[b] = tok;
-                    st_agent64(p.ws.tok_mail + (size_t)q * kMaxBatchPersistent + b,
+                if (t == 0) s_prev[b] = tok;
+                if (t == b) {  // into this workgroup's own mailbox region
+                    st_agent64(mail_q + (size_t)c * kMailWords + kMailToks + b,
                                ((unsigned long long)(unsigned)tok << 32) | epoch);
                 }
             }
-            // every other sampled request: thread b reads its token mailbox
+            // every other sampled request: thread b reads its owner's token word
             if (t < B && s_T[t] > 0.0f && s_own[t] != c) {
-                const unsigned long long* tbox = p.ws.tok_mail + (size_t)q * kMaxBatchPersistent + t;
+                // (an owner of -1, no shard with mass, cannot occur: the winner's
+                // shard always has mass >= 1; the clamp keeps the read in bounds)
+                const unsigned long long* tbox = mail_q + (size_t)max(s_own[t], 0) * kMailWords + kMailToks + t;
                 unsigned it = 0;
                 unsigned long long v = 0ull;
                 bool ok = true;
@@ -1358,8 +1371,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #undef DSW_ONE_ROW_OK
 
     DSW_TRACE_FLUSH();
-    if (c == 0 && t == 0 && !s_abort)
+    if (c == 0 && t == 0 && !s_abort) {
         __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.ws.fam_ctr + kFamAll, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // (register tiles, tiles per wave) shapes of the MFMA engine, per batch tile

@@ -21,8 +21,22 @@ constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 // Device workspace.  Cross-workgroup traffic goes through per-workgroup
 // mailboxes tagged with a step epoch: workgroup c writes its words for step
 // s into mail[s & 1][c], and readers wait until a word carries the epoch of
-// s.  Nothing needs clearing between steps, launches or graph replays.
-constexpr int kMailWords = 32;      // per workgroup and parity: 16 key words + 16 exp-sum words
+// s.  The host clears nothing between steps, launches or graph replays.
+//
+// Epochs.  Step k of a launch has sequence number s = n * gamma_max + k
+// (mod 2^32), n the launch count of the kernel family that owns the region
+// (the all-to-all kernels and the batched kernel keep separate counts), and
+// epoch(s) = (s mod 2^27) + 1: never 0, and since 2^27 divides 2^32 two steps
+// share an epoch only if their sequence numbers are 2^27 apart, also across
+// the 32-bit wrap.  At entry every workgroup zeroes each word it will post in
+// this launch (both parities), before its first post and behind a barrier, so
+// a word a reader polls holds 0, a post of this launch or a post of the
+// family's previous launch -- fewer than 2 gamma_max steps from the current
+// one, never a full period.  Every word has one writing workgroup.
+constexpr int kMailKeys = 0;        // word b: request b's key (or Gumbel score)
+constexpr int kMailSums = 16;       // word 16 + b: its exp-sum (or Gumbel ~id)
+constexpr int kMailToks = 32;       // word 32 + b: its sampled token, posted by the owner shard
+constexpr int kMailWords = 48;      // per workgroup and parity
 constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
 constexpr int kCellMaxPerWg = 4;   // recurrent heads: state elements per workgroup (one per wave; grid >= 64)
 constexpr int kDominoMaxGamma = 16;  // Domino's head: steps per round (its drafters' blocks)
@@ -30,11 +44,16 @@ constexpr int kDominoMaxD = 4096;    // Domino's head: the drafter's hidden widt
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
 constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests
-constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // epochs live in the low 28 bits, never 0
+constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // the 28-bit epoch field of a mailbox word
+constexpr unsigned kEpochPeriod = 1u << 27;   // epochs repeat after this many steps
+constexpr int kMaxGammaMax = 4096;            // gamma_max bound: 2 gamma_max stays far below the period
+constexpr int kFamAll = 0;                    // family counter of the all-to-all kernels
+constexpr int kFamBatched = 1;                // family counter of the batched kernel
+constexpr unsigned epoch_of(unsigned seq) { return (seq & (kEpochPeriod - 1u)) + 1u; }
 struct Workspace {
     unsigned long long* mail;      // [2][kMaxGrid][kMailWords]
-    unsigned long long* tok_mail;  // [2][kMaxBatchPersistent] sampled token << 32 | epoch
-    unsigned* round_ctr;           // [1]  launches so far (selects the step epochs)
+    unsigned* round_ctr;           // [1]  completed launches (keys the device-drawn noise)
+    unsigned* fam_ctr;             // [2]  completed launches per kernel family (the epochs)
     unsigned* status;              // [1]  latched kStatus* bits
     // batched kernel (requests owned by workgroups): every workgroup posts one
     // key word (and one exp-sum word) per request; the owner of request b
@@ -42,7 +61,8 @@ struct Workspace {
     unsigned long long* bkey;      // [2][kMaxGrid][kMaxBatch]  key << 28 | epoch
     unsigned long long* bsum;      // [2][kMaxGrid][kMaxBatch]  exp-sum bits << 32 | epoch
     unsigned long long* bdec;      // [2][kMaxBatch]  decision << 28 | epoch
-    unsigned long long* btok;      // [2][kMaxBatch]  sampled token << 28 | epoch
+    unsigned long long* btok;      // [2][kMaxGrid][kMaxBatch]  sampled token << 28 | epoch,
+                                   // in the row of the shard that found it
     unsigned long long* bext;      // [2][kMaxBatch][2]  owner's prefix before the token
                                    // shard and u*Z, fp32 bits << 32 | epoch
     uint16_t* blog;                // [B_max][V] batched kernel: this step's logits of the
@@ -58,20 +78,20 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, tok_mail, round_ctr, status, bkey, bsum, bdec, btok, bext, total;
+    size_t mail, round_ctr, fam_ctr, status, bkey, bsum, bdec, btok, bext, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     WorkspaceLayout L;
     size_t o = 0;
     L.mail = o;      o = up(o + 2 * (size_t)kMaxGrid * kMailWords * 8);
-    L.tok_mail = o;  o = up(o + 2 * (size_t)kMaxBatchPersistent * 8);
     L.round_ctr = o; o = up(o + 4);
+    L.fam_ctr = o;   o = up(o + 8);
     L.status = o;    o = up(o + 4);
     L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bsum = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bdec = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
-    L.btok = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
+    L.btok = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bext = o;      o = up(o + 2 * (size_t)kMaxBatch * 2 * 8);
     L.total = o;
     return L;
@@ -101,6 +121,8 @@ struct WalkParams {
     int ring;                // batched kernel: LDS slots for u rows and base logits of groups
     int aligned;             // batched kernel: V % 8 == 0 (16-byte aligned base rows)
     unsigned spin_limit;     // polls before a wait gives up and latches kStatusTimeout
+    unsigned skew;           // diagnostics: 0, or each workgroup sleeps a pseudo-random
+                             // multiple of this many s_sleep units before it posts
     int single_round;        // 1: logit = bf16(base + fp32 dot), rounded once
     int seeded;              // 1: uniforms == NULL draws them on the device from seed
     unsigned long long seed; // key of the device-drawn uniforms and of the Gumbel noise
