@@ -65,6 +65,50 @@ def test_null_and_argument_errors_without_a_device(dsw):
     assert L.dsw_walk_domino(None, *([None] * 8), 64, *([None] * 7), 1, 1, None) == -1
 
 
+def test_debug_and_test_hooks_without_a_handle(dsw):
+    L = dsw.lib()
+    assert L.dsw_set_debug(None, 1, 0) == -1
+    assert L.dsw_set_round_counter(None, 5) == -1
+    assert L.dsw_debug_gumbel_table(None, None) == -1
+    h = ctypes.c_void_p()
+    assert L.dsw_create(ctypes.byref(h), 0, 100, 256, 4097, 1, 0, 0) == -3  # gamma_max above 4096
+
+
+EPOCH_PERIOD = 1 << 27
+
+
+def test_epoch_range_and_period(dsw):
+    """Epochs lie in [1, 2^27] (never the 0 of a cleared word) and repeat with
+    period 2^27 in the step sequence number, which divides 2^32: the same
+    sequence number mod 2^27 gives the same epoch, also across the 32-bit wrap."""
+    rng = __import__("numpy").random.default_rng(7)
+    seqs = [0, 1, EPOCH_PERIOD - 1, EPOCH_PERIOD, 2 ** 32 - 1, 2 ** 32 - 16, 2 ** 31] + \
+        [int(x) for x in rng.integers(0, 2 ** 32, 200)]
+    for s in seqs:
+        e = dsw.debug_epoch(s)
+        assert 1 <= e <= EPOCH_PERIOD, (s, e)
+        assert e == (s % EPOCH_PERIOD) + 1
+        assert dsw.debug_epoch((s + EPOCH_PERIOD) % 2 ** 32) == e
+        assert dsw.debug_epoch((s + 1) % 2 ** 32) != e
+
+
+@pytest.mark.parametrize("gamma_max", [1, 7, 16, 5, 4096])
+def test_epochs_distinct_across_the_wrap(dsw, gamma_max):
+    """Steps of consecutive launches around the 32-bit wrap of the sequence
+    number s = n * gamma_max + k, and around the wrap of the counter n itself,
+    carry pairwise distinct epochs (the reads of one launch only ever meet
+    words of that launch or of the one before)."""
+    for n0 in ((2 ** 32) // gamma_max - 2, 2 ** 32 - 2, 2 ** 28 - 2, 0):
+        epochs = []
+        for n in range(n0, n0 + 4):
+            for k in range(gamma_max if gamma_max <= 64 else 64):
+                epochs.append(dsw.debug_epoch(((n % 2 ** 32) * gamma_max + k) % 2 ** 32))
+        # consecutive launches: 2 gamma_max steps never share an epoch
+        for i in range(len(epochs)):
+            window = epochs[i:i + 2 * min(gamma_max, 64)]
+            assert len(set(window)) == len(window), (gamma_max, n0, i)
+
+
 def fake_device(dsw, cus=256, lds_cu=160 * 1024, lds_blk=160 * 1024):
     d = dsw.DevInfo()
     d.cu_count, d.simds_per_cu, d.wave_size, d.vgprs_per_simd_lane = cus, 4, 64, 512
