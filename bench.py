@@ -48,10 +48,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload_name, B, gamma):
-    """HBM bytes per launch from the committed counter record, if it was taken
-    on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"counters_{workload_name}_b{B}_g{gamma}.json")
+def recorded_traffic(workload_name, B, gamma, cold=False):
+    """HBM bytes per launch from the committed counter record (warm, or with L2
+    and the Infinity Cache flushed before each launch), if it was taken on the
+    current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"counters_{workload_name}_b{B}_g{gamma}{'_cold' if cold else ''}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -158,25 +159,53 @@ def stepwise_torch(torch, W1d, W2d, dev_rounds, K):
     return (time.perf_counter() - t0) / K * 1e6
 
 
-def cpu_baseline(index, B, gamma, V, W1, W2, budget_s=15.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(index, B, gamma, V, W1, W2, n_rounds=1000, budget_s=30.0, one_thread_s=10.0):
+    """The oracle as it stands, on the host cores: the same seeded rounds as
+    the workload (all n_rounds of them unless the budget runs out first),
+    median wall time per round with every OpenMP thread, then a shorter
+    sample with one thread."""
     import oracle
     import workloads
-    times = []
-    t_start = time.perf_counter()
-    r = 0
-    while True:
-        inp = workloads.round_inputs(index, r, B=B, gamma=gamma, V=V)
-        t0 = time.perf_counter()
-        oracle.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2,
-                    want_logits=False)
-        times.append(time.perf_counter() - t0)
-        r += 1
-        if time.perf_counter() - t_start > budget_s or r >= 1000:
-            break
-    return {"value": statistics.median(times) * 1e6, "unit": "us/round", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"{r} rounds of the same workload (seeded rounds 0..{r - 1}), "
-                      f"median wall time per round, binary64 C oracle with OpenMP"}
+
+    def timed(limit_s, max_rounds):
+        times = []
+        t_start = time.perf_counter()
+        r = 0
+        while r < max_rounds:
+            inp = workloads.round_inputs(index, r, B=B, gamma=gamma, V=V)
+            t0 = time.perf_counter()
+            oracle.walk(W1, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], W2_bits=W2,
+                        want_logits=False)
+            times.append(time.perf_counter() - t0)
+            r += 1
+            if time.perf_counter() - t_start > limit_s:
+                break
+        return times
+
+    n_threads = oracle.threads()
+    times = timed(budget_s, n_rounds)
+    oracle.set_threads(1)
+    try:
+        one = timed(one_thread_s, n_rounds)
+    finally:
+        oracle.set_threads(n_threads)
+    return {"value": statistics.median(times) * 1e6, "unit": "us/round", "cores": n_threads,
+            "kind": "oracle", "cpu_model": cpu_model(), "rounds": len(times),
+            "one_thread_us": statistics.median(one) * 1e6, "one_thread_rounds": len(one),
+            "sample": f"{len(times)} of the workload's {n_rounds} seeded rounds (rounds 0..{len(times) - 1}) with "
+                      f"{n_threads} OpenMP threads, then rounds 0..{len(one) - 1} with one thread; median wall "
+                      f"time per round of the binary64 C oracle"}
 
 
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
@@ -206,6 +235,28 @@ def gamma_sweep(torch, dsw, W1d, W2d, V, gammas=(1, 4, 7, 10, 16), rounds=60, K=
                      "entry_us": round(float(entry), 2), "us_per_step": round(float(step), 3),
                      "status": st}
     return out
+
+def cold_gamma_sweep(torch, dsw, W1d, W2d, V, flush, gammas=(1, 4, 7, 10, 16), rounds=30):
+    """The resident walk with L2 and the Infinity Cache flushed before each
+    round (outside the events), against gamma, fitted as entry + gamma * step:
+    the entry is then the shard load from HBM."""
+    walker = dsw.Walker(V, gamma_max=max(gammas), B_max=1)
+    try:
+        pts = []
+        for g in gammas:
+            d = to_device(make_rounds(1, rounds, 1, g, V, "greedy"), torch, W1d.device)
+            mean, durs = time_walk(torch, walker, W1d, W2d, d, rounds, 2, flush=flush)
+            pts.append((g, statistics.median(durs)))
+            del d
+        st = walker.status()
+    finally:
+        walker.close()
+    x = np.array([p[0] for p in pts], dtype=np.float64)
+    y = np.array([p[1] for p in pts], dtype=np.float64)
+    step, entry = np.polyfit(x, y, 1)
+    return {"us_per_round_median": {int(g): round(u, 2) for g, u in pts}, "entry_us": round(float(entry), 2),
+            "us_per_step": round(float(step), 3), "status": st}
+
 
 # Every configuration the walk is checked on, timed briefly after the headline
 # line's own measurements: (workload, requests, gamma, W2 storage).
@@ -340,7 +391,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the timed walk (for profiling)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations")
     ap.add_argument("--pmc-mode", action="store_true",
-                    help="for counter runs: 50 walks, then one 256 MiB device copy of known size")
+                    help="for counter runs: --pmc-walks walks, then one 256 MiB device copy of known size")
+    ap.add_argument("--pmc-walks", type=int, default=50)
+    ap.add_argument("--pmc-cold", action="store_true", help="with --pmc-mode: a 1 GiB flush before each walk")
     ap.add_argument("--heads-only", action="store_true",
                     help="only the recurrent heads' configurations of the sweep (for profiling)")
     ap.add_argument("--stepwise-only", action="store_true",
@@ -374,6 +427,43 @@ def main():
     dev_rounds = to_device(rounds, torch, dev)
     del rounds
     walker = dsw.Walker(V, gamma_max=max(gamma, 16), B_max=B)
+    try:
+        result = headline(args, torch, dsw, wl, walker, W1d, W2d, dev_rounds, B, gamma, V, n_rounds)
+    finally:
+        walker.close()   # every path: no handle outlives main()
+    if result is None:
+        return
+    del dev_rounds
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        extras(args, torch, dsw, result, W1d, W2d, B, V)
+        del W1d, W2d
+        torch.cuda.empty_cache()
+        if not args.no_sweep:
+            result["configs"] = []
+            for (index, b, g, dt, *smp) in SWEEP:
+                log(f"sweep: workload {index} B={b} gamma={g} {dt} {smp}")
+                r = sweep_one(torch, dsw, index, b, g, dt, *smp)
+                log(r)
+                result["configs"].append(r)
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle)")
+            result["cpu_baseline"] = cpu_baseline(args.workload, B, gamma, V, W1, W2)
+    print(json.dumps(result), flush=True)
+
+
+def flusher(torch, dev):
+    """A write of 1 GiB that evicts L2 and the 256 MB Infinity Cache."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        scratch.zero_()
+    return flush
+
+
+def headline(args, torch, dsw, wl, walker, W1d, W2d, dev_rounds, B, gamma, V, n_rounds):
+    """The timed walk and its roofline; None for the profiling-only modes."""
+    dev = W1d.device
     plan = walker.query_plan(B).as_dict()
     log("plan", plan)
 
@@ -386,11 +476,16 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"stepwise_only": True, "rounds": 23, "us_per_round": round(sw, 3),
                           "copy_bytes": COPY_BYTES}))
-        return
+        return None
     if args.pmc_mode:
+        # counter runs: args.pmc_walks walks (each after a 1 GiB flush with
+        # --pmc-cold), then one device copy of known size to calibrate the counters
         base, anchor, T, uni = dev_rounds
-        for i in range(50):
+        flush = flusher(torch, dev) if args.pmc_cold else None
+        for i in range(args.pmc_walks):
             j = i % base.shape[0]
+            if flush is not None:
+                flush()
             walker.walk(W1d, W2d, base[j], anchor[j], T[j], uni[j])
         torch.cuda.synchronize()
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -398,9 +493,10 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_mode": True, "walks": 50, "copy_bytes": COPY_BYTES,
-                          "kernel_source_hash": kernel_source_hash(), "status": walker.status()}))
-        return
+        print(json.dumps({"pmc_mode": True, "walks": args.pmc_walks, "cold": bool(args.pmc_cold),
+                          "copy_bytes": COPY_BYTES, "kernel_source_hash": kernel_source_hash(),
+                          "status": walker.status()}))
+        return None
     us_round, _ = time_walk(torch, walker, W1d, W2d, dev_rounds, args.steps, args.warmup)
     st = walker.status()
     if st != 0:
@@ -415,8 +511,7 @@ def main():
                    "temps": wl.temps, "rounds_resident": n_rounds, "w2": "bf16"},
     }
     if args.no_extras:
-        print(json.dumps(result), flush=True)
-        return
+        return result
 
     # per-launch kernel time (HIP events on the launch stream)
     k_launch = min(args.steps, 300)
@@ -440,18 +535,24 @@ def main():
     log(f"per launch {mean_launch:.2f} us, {achieved:.0f} GB/s algorithmic")
 
     # cold: flush L2 + Infinity Cache before each round (outside the events)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
-    def flush():
-        scratch.zero_()
+    flush = flusher(torch, dev)
     kc = min(args.cold_rounds, n_rounds)
     cold_mean, cold = time_walk(torch, walker, W1d, W2d, dev_rounds, kc, 2, flush=flush)
     cold.sort()
-    result["cold_us_per_round"] = {"median": round(statistics.median(cold), 3),
-                                   "p10": round(cold[len(cold) // 10], 3),
+    cold_med = statistics.median(cold)
+    result["cold_us_per_round"] = {"median": round(cold_med, 3), "p10": round(cold[len(cold) // 10], 3),
                                    "p90": round(cold[(9 * len(cold)) // 10], 3), "rounds": kc}
-    del scratch
+    cold_ach = abytes / (cold_med * 1e-6) / 1e9
+    result["roofline"].update({"cold_launch_us_median": round(cold_med, 3), "cold_achieved": round(cold_ach, 1),
+                               "cold_frac": round(cold_ach / HBM_PEAK_GBS, 4),
+                               "cold_traffic": recorded_traffic(wl.name, B, gamma, cold=True)})
+    result["cold_frac_of_stepwise_bound"] = round(cold_med / stepwise_bound, 4)
     log("cold", result["cold_us_per_round"])
+    if B == 1 and V == 151_936 and not args.no_sweep:
+        result["cold_gamma_sweep"] = cold_gamma_sweep(torch, dsw, W1d, W2d, V, flush)
+        log("cold gamma sweep", result["cold_gamma_sweep"])
+    del flush
+    torch.cuda.empty_cache()
 
     # gamma = 16 at the same vocabulary (the metric's second walk length)
     if gamma != 16 and V == 151_936:
@@ -469,29 +570,14 @@ def main():
         result["stepwise_torch_us_per_round"] = round(sw, 3)
         result["stepwise_torch_w2_gbs"] = round(gamma * w2_bytes / (sw * 1e-6) / 1e9, 1)
         log(f"step-wise torch: {sw:.2f} us/round")
+    return result
 
-    walker.close()
-    del dev_rounds
-    torch.cuda.empty_cache()
+
+def extras(args, torch, dsw, result, W1d, W2d, B, V):
     # gamma sweep at this vocabulary: one-time entry vs per-step cost, resident vs streamed
     if B == 1 and V == 151_936 and not args.no_sweep:
         result["gamma_sweep"] = gamma_sweep(torch, dsw, W1d, W2d, V)
         log("gamma sweep", result["gamma_sweep"])
-    del W1d, W2d
-    torch.cuda.empty_cache()
-    if not args.no_sweep:
-        result["configs"] = []
-        for (index, b, g, dt, *smp) in SWEEP:
-            log(f"sweep: workload {index} B={b} gamma={g} {dt} {smp}")
-            r = sweep_one(torch, dsw, index, b, g, dt, *smp)
-            log(r)
-            result["configs"].append(r)
-
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(args.workload, B, gamma, V, W1, W2)
-    print(json.dumps(result), flush=True)
-
 
 if __name__ == "__main__":
     main()

@@ -15,9 +15,12 @@ driven by ``uniforms[:, k]``, and ``prev = tok``.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
 import threading
+import weakref
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsw.so")
@@ -113,9 +116,15 @@ def lib():
         L.dsw_set_seed.argtypes = [P, ctypes.c_ulonglong, I]
         L.dsw_round_counter.argtypes = [P, ctypes.POINTER(ctypes.c_uint)]
         L.dsw_set_trace.argtypes = [P, P, ctypes.c_longlong]
-        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn", "dsw_walk_gated", "dsw_walk_domino",
-                  "dsw_status",
-                  "dsw_query_plan", "dsw_destroy", "dsw_set_seed", "dsw_round_counter", "dsw_set_trace"):
+        L.dsw_set_debug.argtypes = [P, U, U]
+        L.dsw_set_round_counter.argtypes = [P, U]
+        L.dsw_debug_epoch.argtypes = [U]
+        L.dsw_debug_epoch.restype = U
+        L.dsw_debug_gumbel_table.argtypes = [P, P]
+        for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn",
+                  "dsw_walk_gated", "dsw_walk_domino", "dsw_status", "dsw_query_plan", "dsw_destroy", "dsw_set_seed",
+                  "dsw_round_counter", "dsw_set_trace", "dsw_set_debug", "dsw_set_round_counter",
+                  "dsw_debug_gumbel_table"):
             getattr(L, f).restype = I
         _lib = L
         return L
@@ -152,6 +161,40 @@ def _stream_handle(torch, device, stream):
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
+def debug_epoch(seq: int) -> int:
+    """The epoch a mailbox word carries at step sequence number seq (host only)."""
+    return int(lib().dsw_debug_epoch(ctypes.c_uint(int(seq) & 0xFFFFFFFF)))
+
+
+def debug_gumbel_table(out, stream=None) -> None:
+    """out: float32 device tensor of 2^23 elements; fills it with the kernels'
+    Gumbel variate -ln(-ln U) for U = (2 i + 1) 2^-24 (dsw_debug_gumbel_table)."""
+    import torch
+    if out.dtype != torch.float32 or out.numel() != 1 << 23 or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out: want a contiguous float32 device tensor of 2^23 elements")
+    _check(lib().dsw_debug_gumbel_table(ctypes.c_void_p(out.data_ptr()),
+                                        _stream_handle(torch, out.device, stream)), "dsw_debug_gumbel_table")
+
+
+# Handles still open when the interpreter exits are destroyed by an atexit
+# hook, which runs before the HIP runtime (and any profiler attached to the
+# process) is torn down; finalizers that run later, during interpreter
+# shutdown, do nothing.
+_open_walkers = weakref.WeakSet()
+
+
+def _close_all():
+    for w in list(_open_walkers):
+        try:
+            w.close()
+        except Exception:
+            pass
+    _walkers.clear()
+
+
+atexit.register(_close_all)
+
+
 class Walker:
     """A handle of the library: workspace for walks of vocabulary V with at
     most gamma_max steps and B_max requests on one device."""
@@ -164,17 +207,42 @@ class Walker:
         _check(lib().dsw_create(ctypes.byref(h), self.device, self.V, int(r), self.gamma_max,
                                 self.B_max, self.w2_dtype, int(flags)), "dsw_create")
         self._h = h
+        _open_walkers.add(self)
 
     def close(self):
+        """Destroy the handle (waits for its device).  Idempotent."""
         if getattr(self, "_h", None):
-            lib().dsw_destroy(self._h)
-            self._h = None
+            h, self._h = self._h, None
+            lib().dsw_destroy(h)
+        _open_walkers.discard(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
     def __del__(self):
+        # during interpreter shutdown the atexit hook has already closed every
+        # handle; never call into the runtime from a late finalizer
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
             pass
+
+    def set_debug(self, spin_limit: int = 0, skew: int = 0) -> None:
+        """Diagnostics (dsw_set_debug): polls before a device wait gives up (0 =
+        the default), and pseudo-random delays before every post (0 = none)."""
+        _check(lib().dsw_set_debug(self._h, ctypes.c_uint(int(spin_limit)), ctypes.c_uint(int(skew))),
+               "dsw_set_debug")
+
+    def set_round_counter(self, value: int) -> None:
+        """Test hook (dsw_set_round_counter): waits for the device, then sets the
+        round counter and the launch counters of both kernel families."""
+        _check(lib().dsw_set_round_counter(self._h, ctypes.c_uint(int(value) & 0xFFFFFFFF)),
+               "dsw_set_round_counter")
 
     def query_plan(self, B: int) -> PlanInfo:
         out = PlanInfo()
@@ -325,12 +393,16 @@ _walkers = {}
 
 
 def walk(W1, W2, base, anchor, T, uniforms=None, w2_scale=None, want_logits=False, stream=None):
-    """Functional form: one round with a cached handle per (device, V, dtype)."""
+    """Functional form: one round with a cached handle per (device, V, dtype,
+    stream).  A handle serves one stream at a time (its workspace and counters
+    are not shared between concurrent walks), so walks on different streams
+    get different handles."""
     import torch
     B, gamma, V = (int(x) for x in base.shape)
     device = W1.device.index if W1.device.index is not None else torch.cuda.current_device()
     dtype = INT8 if W2.dtype == torch.int8 else BF16
-    key = (device, V, dtype)
+    sid = int((stream if stream is not None else torch.cuda.current_stream(device)).cuda_stream)
+    key = (device, V, dtype, sid)
     w = _walkers.get(key)
     if w is None or w.gamma_max < gamma or w.B_max < B:
         if w is not None:
