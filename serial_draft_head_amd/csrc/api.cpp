@@ -7,6 +7,7 @@
 #include <new>
 
 #include "../../include/dsw.h"
+#include "launch.h"
 #include "walk_params.h"
 
 extern "C" const void* dsw_internal_walk_kernel(int reg_slots, int batch_tile, int w2_dtype);
@@ -84,10 +85,6 @@ struct dsw_handle {
     long long trace_bytes;
     unsigned spin_limit;        // polls before a device wait gives up
     unsigned skew;              // diagnostics: pseudo-random delays before posts (0 = none)
-    std::mutex mu;  // guards the per-kernel attribute cache below
-    const void* lds_configured[64];  // kernels whose dynamic-LDS ceiling was raised
-    int lds_configured_bytes[64];
-    int n_configured;
 };
 
 namespace {
@@ -111,8 +108,6 @@ int clear_workspace(dsw_handle* h) {
     if (hipDeviceSynchronize() != hipSuccess) return DSW_ERR_HIP;
     return DSW_OK;
 }
-
-constexpr unsigned kSpinLimit = 1u << 20;  // polls; each costs well over 100 ns
 
 }  // namespace
 
@@ -171,13 +166,10 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->dev = dev;
     h->trace = nullptr;
     h->trace_bytes = 0;
-    h->spin_limit = kSpinLimit;
+    h->spin_limit = dsw::kSpinLimit;
     h->skew = 0u;
     h->seed = 0ull;
     h->seeded = 0;
-    memset(h->lds_configured, 0, sizeof(h->lds_configured));
-    memset(h->lds_configured_bytes, 0, sizeof(h->lds_configured_bytes));
-    h->n_configured = 0;
 
     DeviceGuard g(device);
     if (!g.ok) { delete h; return DSW_ERR_DEVICE; }
@@ -250,21 +242,50 @@ extern "C" int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out) {
 }
 
 namespace {
-// A recurrent head's extra arguments (dsw_walk_gru, dsw_walk_rnn: the cell;
-// dsw_walk_gated: the gate matrix, its scales and biases).
-struct GruArgs {
-    const uint16_t* wih;
-    const uint16_t* whh;
-    const float* bih;
-    const float* bhh;
-    const float* h0;
-    float* states;
-    const int8_t* gq;
-    const float* gs;
-    const float* gb;
-    const uint16_t* hidden;  // Domino's head: H [gamma][d]
-    int d;
+using dsw::GruArgs;
+
+// Kernels whose dynamic-LDS ceiling was raised, per device (process-wide).
+std::mutex g_lds_mu;
+struct LdsEntry {
+    const void* fn;
+    int device;
+    int bytes;
 };
+LdsEntry g_lds[256];
+int g_n_lds = 0;
+
+void raise_lds_ceiling(const void* fn, int device, int bytes) {
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    int slot = -1;
+    for (int i = 0; i < g_n_lds; ++i)
+        if (g_lds[i].fn == fn && g_lds[i].device == device) slot = i;
+    if (slot >= 0 && g_lds[slot].bytes >= bytes) return;
+    // Raises the dynamic-LDS ceiling where the runtime enforces one; a
+    // failure here surfaces as a launch error.
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    (void)hipGetLastError();
+    if (slot < 0 && g_n_lds < 256) slot = g_n_lds++;
+    if (slot >= 0) g_lds[slot] = LdsEntry{fn, device, bytes};
+}
+
+dsw::LaunchCtx ctx_of(const dsw_handle* h) {
+    dsw::LaunchCtx x;
+    x.device = h->device;
+    x.V = h->V;
+    x.gamma_max = h->gamma_max;
+    x.B_max = h->B_max;
+    x.dtype = h->dtype;
+    x.flags = h->flags;
+    x.dev = &h->dev;
+    x.ws = h->ws;
+    x.spin_limit = h->spin_limit;
+    x.skew = h->skew;
+    x.seeded = h->seeded;
+    x.seed = h->seed;
+    x.trace = h->trace;
+    x.trace_bytes = h->trace_bytes;
+    return x;
+}
 
 int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale, const void* base,
               const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens, void* logits,
@@ -272,39 +293,36 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     if (!h) return DSW_ERR_NULL;
     if (B < 0 || B > h->B_max) return DSW_ERR_BATCH;
     if (gamma < 0 || gamma > h->gamma_max) return DSW_ERR_GAMMA;
-    if (h->dtype == DSW_BF16 && w2_scale != nullptr) return DSW_ERR_DTYPE;
-    if (h->dtype == DSW_INT8 && w2_scale == nullptr) return DSW_ERR_DTYPE;
+    const dsw::LaunchCtx x = ctx_of(h);
+    return dsw::launch_walk(x, W1, W2, w2_scale, base, anchor, T, uniforms, tokens, logits, B, gamma, stream, gru,
+                            nullptr);
+}
+}  // namespace
+
+namespace dsw {
+
+int launch_walk(const LaunchCtx& x, const void* W1, const void* W2, const float* w2_scale, const void* base,
+                const int32_t* anchor, const float* T, const float* uniforms, int32_t* tokens, void* logits,
+                int B, int gamma, void* stream, const GruArgs* gru, dsw_plan_info* plan_out) {
+    if (x.dtype == DSW_BF16 && w2_scale != nullptr) return DSW_ERR_DTYPE;
+    if (x.dtype == DSW_INT8 && w2_scale == nullptr) return DSW_ERR_DTYPE;
     if (B == 0 || gamma == 0) return DSW_OK;
     if (!W1 || !W2 || !base || !anchor || !T || !tokens) return DSW_ERR_NULL;
-    if ((h->flags & DSW_FLAG_GUMBEL) && !h->seeded) return DSW_ERR_ARG;  // the noise needs a seed
+    if ((x.flags & DSW_FLAG_GUMBEL) && !x.seeded) return DSW_ERR_ARG;  // the noise needs a seed
 
     dsw_plan_info plan;
-    int rc = dsw_plan_compute(&h->dev, h->V, h->r, gamma, B, h->dtype, h->flags, &plan);
+    int rc = dsw_plan_compute(x.dev, x.V, kRank, gamma, B, x.dtype, x.flags, &plan);
     if (rc) return rc;
-    const void* fn = kernel_for(plan, (h->flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr ? cell_of(h->flags) : 0);
+    if (plan_out) *plan_out = plan;
+    const void* fn = kernel_for(plan, (x.flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr ? cell_of(x.flags) : 0);
     if (!fn) return DSW_ERR_PLAN;
+    if (plan.batch_tile == kMaxBatch && x.ws.blog == nullptr) return DSW_ERR_PLAN;
 
-    DeviceGuard g(h->device);
+    DeviceGuard g(x.device);
     if (!g.ok) return DSW_ERR_DEVICE;
-    {
-        std::lock_guard<std::mutex> lock(h->mu);
-        int slot = -1;
-        for (int i = 0; i < h->n_configured; ++i)
-            if (h->lds_configured[i] == fn) slot = i;
-        if (slot < 0 || h->lds_configured_bytes[slot] < plan.lds_bytes) {
-            // Raises the dynamic-LDS ceiling where the runtime enforces one;
-            // a failure here surfaces as a launch error below.
-            (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes);
-            (void)hipGetLastError();
-            if (slot < 0 && h->n_configured < 64) slot = h->n_configured++;
-            if (slot >= 0) {
-                h->lds_configured[slot] = fn;
-                h->lds_configured_bytes[slot] = plan.lds_bytes;
-            }
-        }
-    }
+    raise_lds_ceiling(fn, x.device, plan.lds_bytes);
 
-    dsw::WalkParams p;
+    WalkParams p;
     p.W1 = static_cast<const uint16_t*>(W1);
     p.W2 = W2;
     p.w2_scale = w2_scale;
@@ -314,24 +332,24 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     p.uniforms = uniforms;
     p.tokens = tokens;
     p.logits = static_cast<uint16_t*>(logits);
-    p.ws = h->ws;
-    p.V = h->V;
+    p.ws = x.ws;
+    p.V = x.V;
     p.B = B;
     p.gamma = gamma;
-    p.gamma_max = h->gamma_max;
-    p.B_max = h->B_max;
+    p.gamma_max = x.gamma_max;
+    p.B_max = x.B_max;
     p.rows_per_wg = plan.rows_per_wg;
     p.lds_rows = plan.lds_rows;
     p.tiles_per_wave = plan.tiles_per_wave;
     p.lds_tiles = plan.lds_tiles;
     p.rows_pad = plan.rows_pad;
     p.ring = plan.ring_slots;
-    p.aligned = (h->V % 8) == 0;
-    p.spin_limit = h->spin_limit;
-    p.skew = h->skew;
-    p.single_round = (h->flags & DSW_FLAG_SINGLE_ROUND) ? 1 : 0;
-    p.seeded = h->seeded;
-    p.seed = h->seed;
+    p.aligned = (x.V % 8) == 0;
+    p.spin_limit = x.spin_limit;
+    p.skew = x.skew;
+    p.single_round = (x.flags & DSW_FLAG_SINGLE_ROUND) ? 1 : 0;
+    p.seeded = x.seeded;
+    p.seed = x.seed;
     p.gru_wih = gru ? gru->wih : nullptr;
     p.gru_whh = gru ? gru->whh : nullptr;
     p.gru_bih = gru ? gru->bih : nullptr;
@@ -343,14 +361,12 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     p.gate_bias = gru ? gru->gb : nullptr;
     p.hidden = gru ? gru->hidden : nullptr;
     p.hidden_d = gru ? gru->d : 0;
-    p.cell_in = dsw::kRank + p.hidden_d;
+    p.cell_in = kRank + p.hidden_d;
     p.trace = nullptr;
-    if (h->trace != nullptr &&
-        (long long)plan.grid * (gamma + 1) * 8 * 8 <= h->trace_bytes)
-        p.trace = h->trace;
+    if (x.trace != nullptr && (long long)plan.grid * (gamma + 1) * 8 * 8 <= x.trace_bytes) p.trace = x.trace;
     void* args[] = {&p};
     hipError_t e;
-    if (h->flags & DSW_FLAG_COOPERATIVE)
+    if (x.flags & DSW_FLAG_COOPERATIVE)
         e = hipLaunchCooperativeKernel(fn, dim3(plan.grid), dim3(plan.block), args,
                                        (unsigned)plan.lds_bytes, static_cast<hipStream_t>(stream));
     else
@@ -359,7 +375,8 @@ int walk_impl(dsw_handle_t h, const void* W1, const void* W2, const float* w2_sc
     if (e == hipErrorCooperativeLaunchTooLarge) return DSW_ERR_LAUNCH;
     return e == hipSuccess ? DSW_OK : DSW_ERR_HIP;
 }
-}  // namespace
+
+}  // namespace dsw
 
 extern "C" int dsw_walk(dsw_handle_t h, const void* W1, const void* W2, const float* w2_scale,
                         const void* base, const int32_t* anchor, const float* T,
@@ -445,7 +462,7 @@ extern "C" int dsw_round_counter(dsw_handle_t h, unsigned* out) {
 extern "C" int dsw_set_debug(dsw_handle_t h, unsigned spin_limit, unsigned skew) {
     if (!h) return DSW_ERR_NULL;
     if (skew > 64u) return DSW_ERR_ARG;
-    h->spin_limit = spin_limit ? spin_limit : kSpinLimit;
+    h->spin_limit = spin_limit ? spin_limit : dsw::kSpinLimit;
     h->skew = skew;
     return DSW_OK;
 }
