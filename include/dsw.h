@@ -53,6 +53,8 @@ extern "C" {
 #define DSW_ERR_DEVICE -9        /* no such device                                   */
 #define DSW_ERR_PLAN -10         /* no execution plan fits the request              */
 #define DSW_ERR_ARG -11          /* another invalid argument                         */
+#define DSW_ERR_SCRATCH -12      /* dsw_walk_static: the walk needs more workspace than
+                                    its static scratch array holds                  */
 /* latched by the device, reported by dsw_status() */
 #define DSW_ERR_DEV_TIMEOUT -20  /* a cross-workgroup wait exceeded its bound        */
 #define DSW_ERR_DEV_TOKEN -21    /* an anchor or token id was outside [0, V)        */
@@ -406,6 +408,45 @@ int dsw_debug_gumbel_table(float* out, void* stream);
 /* Wait for the handle's device, then free the workspace and the handle (the
  * end of the handle's exchange area, see dsw_create).  NULL is accepted. */
 int dsw_destroy(dsw_handle_t h);
+
+/* ---- the allocation-free entry point ------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * dsw_walk_static is dsw_walk without a handle: the same plan, kernels and
+ * results for the same (V, dtype, flags, B, gamma), with the workspace in a
+ * file-scope device array of the library (36 MiB per GPU, held until the
+ * process ends: 4 MiB of mailboxes, counters and status, and 32 MiB where the
+ * batched kernel keeps the current step's logits of its sampled requests when
+ * `logits` is NULL).  It allocates nothing (no hipMalloc, hipFree or
+ * allocating library call) and never waits for the device.
+ *   device    the GPU the pointers live on; the call launches there
+ *   V, w2_dtype, flags   as dsw_create; flags: DSW_FLAG_FORCE_STREAM,
+ *             DSW_FLAG_COOPERATIVE, DSW_FLAG_VALU_GEMV, DSW_FLAG_MFMA_GEMV,
+ *             DSW_FLAG_BATCHED, DSW_FLAG_SINGLE_ROUND (others: DSW_ERR_ARG;
+ *             sampled requests need `uniforms`)
+ *   the tensors, B (0 .. 256), gamma (0 .. 256) and stream   as dsw_walk
+ * Errors as dsw_walk, and DSW_ERR_SCRATCH when the planner picks the batched
+ * kernel (4 or more requests by default), logits is NULL and B * V * 2
+ * exceeds 32 MiB (pass logits, or split the batch).  Every call on a GPU
+ * shares that GPU's array and leaves its contents for the next (no clearing
+ * is needed between calls): calls that overlap on one GPU race, so issue
+ * them one at a time per GPU.  The first call on a device (or
+ * dsw_static_init) looks up the array's device address and zero-fills its
+ * workspace part with a kernel on the call's stream. */
+int dsw_walk_static(int device, int V, int w2_dtype, unsigned flags, const void* W1, const void* W2,
+                    const float* w2_scale, const void* base, const int32_t* anchor, const float* T,
+                    const float* uniforms, int32_t* tokens, void* logits, int B, int gamma, void* stream);
+
+/* Optional set-up of dsw_walk_static on `device` (call it outside any graph
+ * capture): the array's device address and its zero fill, waited for.
+ * Allocates nothing. */
+int dsw_static_init(int device);
+
+/* dsw_status for dsw_walk_static on `device`: waits for the device, returns
+ * and clears the latched device status (0 or a DSW_ERR_DEV_* code); after an
+ * error it zero-fills the workspace so that the next call starts clean.
+ * Until then later calls on the device return at once, as with a handle. */
+int dsw_static_status(int device);
 
 /* Static description of a DSW_* code. */
 const char* dsw_strerror(int code);

@@ -29,7 +29,7 @@ OK = 0
 ERR = {
     -1: "DSW_ERR_NULL", -2: "DSW_ERR_BATCH", -3: "DSW_ERR_GAMMA", -4: "DSW_ERR_RANK",
     -5: "DSW_ERR_DTYPE", -6: "DSW_ERR_VOCAB", -7: "DSW_ERR_LAUNCH", -8: "DSW_ERR_HIP",
-    -9: "DSW_ERR_DEVICE", -10: "DSW_ERR_PLAN", -11: "DSW_ERR_ARG",
+    -9: "DSW_ERR_DEVICE", -10: "DSW_ERR_PLAN", -11: "DSW_ERR_ARG", -12: "DSW_ERR_SCRATCH",
     -20: "DSW_ERR_DEV_TIMEOUT", -21: "DSW_ERR_DEV_TOKEN", -22: "DSW_ERR_DEV_UNIFORMS",
 }
 BF16, INT8 = 0, 1
@@ -121,10 +121,13 @@ def lib():
         L.dsw_debug_epoch.argtypes = [U]
         L.dsw_debug_epoch.restype = U
         L.dsw_debug_gumbel_table.argtypes = [P, P]
+        L.dsw_walk_static.argtypes = [I, I, I, U] + [P] * 9 + [I, I, P]
+        L.dsw_static_init.argtypes = [I]
+        L.dsw_static_status.argtypes = [I]
         for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn",
                   "dsw_walk_gated", "dsw_walk_domino", "dsw_status", "dsw_query_plan", "dsw_destroy", "dsw_set_seed",
                   "dsw_round_counter", "dsw_set_trace", "dsw_set_debug", "dsw_set_round_counter",
-                  "dsw_debug_gumbel_table"):
+                  "dsw_debug_gumbel_table", "dsw_walk_static", "dsw_static_init", "dsw_static_status"):
             getattr(L, f).restype = I
         _lib = L
         return L
@@ -390,6 +393,56 @@ class Walker:
 
 
 _walkers = {}
+
+
+def walk_static(W1, W2, base, anchor, T, uniforms=None, w2_scale=None, tokens=None, logits=None,
+                want_logits=False, flags=0, stream=None):
+    """One round through dsw_walk_static: no handle, no allocation in the
+    library (its workspace is a static device array; outputs that are None
+    are allocated here, by torch).  Tensors and results as Walker.walk; the
+    device is W1's.  Calls on one GPU must not overlap."""
+    import torch
+    dev = W1.device
+    B, gamma, V = (int(x) for x in base.shape)
+    dtype = INT8 if W2.dtype == torch.int8 else BF16
+    need = [(W1, torch.bfloat16, (V, RANK), "W1"), (base, torch.bfloat16, (B, gamma, V), "base"),
+            (anchor, torch.int32, (B,), "anchor"), (T, torch.float32, (B,), "T")]
+    if dtype == BF16:
+        need.append((W2, torch.bfloat16, (V, RANK), "W2"))
+    else:
+        need.append((W2, torch.int8, (V, RANK), "W2"))
+        need.append((w2_scale, torch.float32, (V,), "w2_scale"))
+    if uniforms is not None:
+        need.append((uniforms, torch.float32, (B, gamma), "uniforms"))
+    if tokens is None:
+        tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    need.append((tokens, torch.int32, (B, gamma), "tokens"))
+    if logits is None and want_logits:
+        logits = torch.empty((B, gamma, V), dtype=torch.bfloat16, device=dev)
+    if logits is not None:
+        need.append((logits, torch.bfloat16, (B, gamma, V), "logits"))
+    for t, dt, shape, name in need:
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name}: want {dt} {shape} contiguous on {dev}, got "
+                             f"{t.dtype} {tuple(t.shape)} on {t.device}")
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    rc = lib().dsw_walk_static(int(dev.index or 0), V, dtype, int(flags), ptr(W1), ptr(W2), ptr(w2_scale),
+                               ptr(base), ptr(anchor), ptr(T), ptr(uniforms), ptr(tokens), ptr(logits), B, gamma,
+                               _stream_handle(torch, dev, stream))
+    _check(rc, "dsw_walk_static")
+    return tokens, logits
+
+
+def static_init(device: int = 0) -> None:
+    """dsw_static_init: set up dsw_walk_static on `device` (outside graph capture)."""
+    _check(lib().dsw_static_init(int(device)), "dsw_static_init")
+
+
+def static_status(device: int = 0) -> int:
+    """dsw_static_status: wait, then return and clear the latched device status of dsw_walk_static."""
+    return lib().dsw_static_status(int(device))
 
 
 def walk(W1, W2, base, anchor, T, uniforms=None, w2_scale=None, want_logits=False, stream=None):

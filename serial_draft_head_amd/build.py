@@ -22,7 +22,9 @@ HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b1.hip", "walk_mfma_b4.hip", "walk_mf
                "walk_mfma_b1_gru.hip", "walk_mfma_b1_rnn.hip", "walk_mfma_b1_gated.hip",
                "walk_mfma_b1_domino.hip",
                # diagnostics
-               "walk_debug.hip"]
+               "walk_debug.hip",
+               # the allocation-free entry point and its static workspace
+               "walk_static.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 # Packed-fp32 VALU forms are kept out of every code object.

@@ -537,6 +537,7 @@ extern "C" const char* dsw_strerror(int code) {
         case DSW_ERR_DEVICE: return "no such device";
         case DSW_ERR_PLAN: return "no execution plan fits";
         case DSW_ERR_ARG: return "invalid argument";
+        case DSW_ERR_SCRATCH: return "the walk needs more workspace than the static scratch array holds";
         case DSW_ERR_DEV_TIMEOUT: return "device: a cross-workgroup wait exceeded its bound";
         case DSW_ERR_DEV_TOKEN: return "device: token id outside [0, V)";
         case DSW_ERR_DEV_UNIFORMS: return "device: T > 0 but uniforms is NULL";
