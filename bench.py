@@ -258,6 +258,56 @@ def cold_gamma_sweep(torch, dsw, W1d, W2d, V, flush, gammas=(1, 4, 7, 10, 16), r
             "us_per_step": round(float(step), 3), "status": st}
 
 
+def grid_sweep(torch, dsw, grids=(8, 16, 32, 64, 128, 256), rounds=20, K=200):
+    """The rendezvous against the number of workgroups (dsw_set_grid): at
+    V = 2,048 (shards of 8 to 256 rows, so that the GEMV stays small) the
+    per-step cost of a greedy walk, fitted over gamma in {1, 9, 17}, is the
+    exchange, the gather and a few MFMA tiles; then the V = 32,000 walk
+    (gamma = 7) at the grids whose shards fit on chip."""
+    import workloads
+    dev = torch.device("cuda", 0)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    out = {"exchange_v2048": {}, "toy_v32000_g7": {}}
+    V = 2048
+    W1, W2 = workloads.weights(0, V=V)
+    W1d, W2d = bf(W1), bf(W2)
+    for G in grids:
+        walker = dsw.Walker(V, gamma_max=17, B_max=1)
+        try:
+            walker.set_grid(G)
+            pts = []
+            for g in (1, 9, 17):
+                d = to_device(make_rounds(0, rounds, 1, g, V, "greedy"), torch, dev)
+                us, _ = time_walk(torch, walker, W1d, W2d, d, K, 10)
+                pts.append((g, us))
+            st = walker.status()
+        finally:
+            walker.close()
+        step, entry = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
+        out["exchange_v2048"][G] = {"us_per_round": {g: round(u, 2) for g, u in pts},
+                                    "us_per_step": round(float(step), 3), "entry_us": round(float(entry), 2),
+                                    "status": st}
+        log("grid", G, out["exchange_v2048"][G])
+    V = 32_000
+    W1, W2 = workloads.weights(0, V=V)
+    W1d, W2d = bf(W1), bf(W2)
+    d = to_device(make_rounds(0, rounds, 1, 7, V, "greedy"), torch, dev)
+    for G in grids:
+        if -(-V // G) > 1024:  # more rows than the compiled shapes hold on chip
+            continue
+        walker = dsw.Walker(V, gamma_max=7, B_max=1)
+        try:
+            walker.set_grid(G)
+            us, _ = time_walk(torch, walker, W1d, W2d, d, K, 10)
+            out["toy_v32000_g7"][G] = {"us_per_round": round(us, 2), "status": walker.status(),
+                                       "plan": {k: v for k, v in walker.query_plan(1).as_dict().items()
+                                                if k in ("rows_per_wg", "reg_tiles", "max_tiles", "lds_tiles")}}
+        finally:
+            walker.close()
+        log("toy grid", G, out["toy_v32000_g7"][G])
+    return out
+
+
 # Every configuration the walk is checked on, timed briefly after the headline
 # line's own measurements: (workload, requests, gamma, W2 storage).
 SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, "bf16"),
@@ -398,6 +448,8 @@ def main():
                     help="only the recurrent heads' configurations of the sweep (for profiling)")
     ap.add_argument("--stepwise-only", action="store_true",
                     help="for counter runs: only the step-wise library-op loop, then the same copy")
+    ap.add_argument("--grid-sweep", action="store_true",
+                    help="only the rendezvous cost against the number of workgroups (8 .. 256)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the walk runs on one GPU; --gpus must be 1 (the multi-GPU split is a design, not built)"}))
@@ -408,6 +460,9 @@ def main():
     import serial_draft_head_amd as dsw
     import workloads
 
+    if args.grid_sweep:
+        print(json.dumps({"grid_sweep": grid_sweep(torch, dsw)}))
+        return
     if args.heads_only:
         heads = [sweep_one(torch, dsw, *cfg) for cfg in SWEEP if len(cfg) > 5 and cfg[5] != "markov"]
         print(json.dumps({"heads_only": True, "configs": heads}))

@@ -66,7 +66,10 @@ extern "C" {
                                     bias = bf16(scale[v] * fp32 sum_j q[v][j] u[j])
                                     (the int8 table with one fp32 scale per row of
                                     section "V = 248,320: 62% on chip, the rest
-                                    streamed"); always on the MFMA engine      */
+                                    streamed").  One request: the rows are
+                                    widened to bf16 on chip when the shard is
+                                    loaded (exact); more requests keep the codes
+                                    and widen them every step               */
 
 /* shard GEMV engines */
 #define DSW_ENGINE_VALU 0        /* v_dot2 per lane, one row per lane                */
@@ -197,10 +200,10 @@ int dsw_device_info(int device, dsw_devinfo* out);
  * each CTA one slice of vocabulary rows (section "The idea: make the walk
  * resident"); each shard is placed in VGPRs first, then LDS, and whatever is
  * left is streamed every step (section "V = 248,320: 62% on chip, the rest
- * streamed").  flags: DSW_FLAG_FORCE_STREAM and the engine flags.  int8 W2
- * takes the VALU engine only for one request (rows widened to bf16 on chip,
- * at most two register row groups per lane); DSW_FLAG_VALU_GEMV with int8 W2
- * and B > 1 returns DSW_ERR_DTYPE.
+ * streamed").  flags: DSW_FLAG_FORCE_STREAM and the engine flags.  One
+ * request walking up to 3 steps takes the VALU engine, longer walks the MFMA
+ * engine; both keep int8 rows widened to bf16 on chip.  DSW_FLAG_VALU_GEMV
+ * with int8 W2 and B > 1 returns DSW_ERR_DTYPE.
  * Returns DSW_ERR_* on invalid sizes or when no plan fits. */
 int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int w2_dtype,
                      unsigned flags, dsw_plan_info* out);
@@ -383,11 +386,23 @@ int dsw_set_trace(dsw_handle_t h, void* trace, long long bytes);
  * every CTA has arrived).  spin_limit: polls before a device wait gives up
  * (0 restores the default, about 2^20); a small value makes the waits give
  * up, which latches DSW_ERR_DEV_TIMEOUT while every workgroup still exits.
- * skew (0 .. 64, else DSW_ERR_ARG): 0, or before each post every workgroup
- * sleeps a pseudo-random 0..7 times skew units of ~8k clocks, so that the
- * workgroups reach each rendezvous in a scrambled order.  Later walks on
- * the handle use both. */
+ * skew (0 or 1, else DSW_ERR_ARG): 1 makes every workgroup sleep a
+ * pseudo-random 0..7 units of ~8k clocks, so that the workgroups reach the
+ * rendezvous in a scrambled order: before its first post in the one-kernel
+ * exchange (a hook in that kernel's step loop slows every step even when
+ * off), before each post of each step in the batched kernel.  Later walks
+ * on the handle use both. */
 int dsw_set_debug(dsw_handle_t h, unsigned spin_limit, unsigned skew);
+
+/* Tuning: later walks on the handle use `grid` workgroups (1 .. the device's
+ * CU count; 0 restores one per CU), so that each owns ceil(V / grid) rows:
+ * fewer, larger shards mean fewer participants in every rendezvous and more
+ * rows per workgroup (the pages measure their exchange at 0.97 us per step
+ * even with 8 CTAs: "Keeping the Draft Walk on Chip", section "B200: the
+ * bf16 table fits on chip").  Walks whose shards then exceed the compiled
+ * shapes return the planner's error (DSW_ERR_VOCAB); the recurrent heads
+ * need a grid of r / 4 (Domino's head: r) workgroups (DSW_ERR_PLAN). */
+int dsw_set_grid(dsw_handle_t h, int grid);
 
 /* Test hook: waits for the device, then sets the round counter and both
  * kernel families' launch counters to `value` (e.g. just below a 32-bit

@@ -118,6 +118,7 @@ def lib():
         L.dsw_set_trace.argtypes = [P, P, ctypes.c_longlong]
         L.dsw_set_debug.argtypes = [P, U, U]
         L.dsw_set_round_counter.argtypes = [P, U]
+        L.dsw_set_grid.argtypes = [P, I]
         L.dsw_debug_epoch.argtypes = [U]
         L.dsw_debug_epoch.restype = U
         L.dsw_debug_gumbel_table.argtypes = [P, P]
@@ -126,7 +127,7 @@ def lib():
         L.dsw_static_status.argtypes = [I]
         for f in ("dsw_device_info", "dsw_plan_compute", "dsw_create", "dsw_walk", "dsw_walk_gru", "dsw_walk_rnn",
                   "dsw_walk_gated", "dsw_walk_domino", "dsw_status", "dsw_query_plan", "dsw_destroy", "dsw_set_seed",
-                  "dsw_round_counter", "dsw_set_trace", "dsw_set_debug", "dsw_set_round_counter",
+                  "dsw_round_counter", "dsw_set_trace", "dsw_set_debug", "dsw_set_round_counter", "dsw_set_grid",
                   "dsw_debug_gumbel_table", "dsw_walk_static", "dsw_static_init", "dsw_static_status"):
             getattr(L, f).restype = I
         _lib = L
@@ -240,6 +241,10 @@ class Walker:
         the default), and pseudo-random delays before every post (0 = none)."""
         _check(lib().dsw_set_debug(self._h, ctypes.c_uint(int(spin_limit)), ctypes.c_uint(int(skew))),
                "dsw_set_debug")
+
+    def set_grid(self, grid: int) -> None:
+        """dsw_set_grid: later walks use `grid` workgroups (0 = one per CU)."""
+        _check(lib().dsw_set_grid(self._h, int(grid)), "dsw_set_grid")
 
     def set_round_counter(self, value: int) -> None:
         """Test hook (dsw_set_round_counter): waits for the device, then sets the

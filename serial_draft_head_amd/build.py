@@ -21,6 +21,8 @@ HIP_SOURCES = ["walk_valu.hip", "walk_mfma_b1.hip", "walk_mfma_b4.hip", "walk_mf
                # the one-request kernels for the recurrent serial heads (GRU, RNN, gated, Domino)
                "walk_mfma_b1_gru.hip", "walk_mfma_b1_rnn.hip", "walk_mfma_b1_gated.hip",
                "walk_mfma_b1_domino.hip",
+               # one request with int8 rows (widened once), with either sampler
+               "walk_mfma_b1_i8.hip", "walk_mfma_b1_i8_gumbel.hip",
                # diagnostics
                "walk_debug.hip",
                # the allocation-free entry point and its static workspace

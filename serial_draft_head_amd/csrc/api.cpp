@@ -15,7 +15,7 @@ extern "C" const void* dsw_internal_mfma_kernel_b1(int reg_tiles, int max_tiles)
 extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
-extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round);
 // the same all-to-all kernels with Gumbel-max sampling
 extern "C" const void* dsw_internal_walk_kernel_gumbel(int reg_slots, int batch_tile, int w2_dtype);
 extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max_tiles);
@@ -27,6 +27,9 @@ extern "C" const void* dsw_internal_mfma_kernel_b1_gru(int reg_tiles, int max_ti
 extern "C" const void* dsw_internal_mfma_kernel_b1_rnn(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b1_gated(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b1_domino(int reg_tiles, int max_tiles);
+// one request with int8 rows widened to bf16 at entry
+extern "C" const void* dsw_internal_mfma_kernel_b1_i8(int reg_tiles, int max_tiles);
+extern "C" const void* dsw_internal_mfma_kernel_b1_i8_gumbel(int reg_tiles, int max_tiles);
 
 namespace {
 // The compiled kernel a plan runs (with Gumbel-max sampling when `gumbel`), or
@@ -40,8 +43,9 @@ int cell_of(unsigned flags) {
     return (flags & DSW_FLAG_DOMINO) ? 4 : 0;
 }
 
-// cell: as cell_of
-const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell) {
+// cell: as cell_of; single: DSW_FLAG_SINGLE_ROUND (the batched kernel is
+// compiled for each rounding)
+const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell, bool single) {
     if (cell) {  // the planner gives the recurrent heads only the one-request MFMA engine
         if (pl.engine != DSW_ENGINE_MFMA || pl.batch_tile != 1 || pl.w2_dtype != DSW_BF16) return nullptr;
         const void* (*const lookup[])(int, int) = {dsw_internal_mfma_kernel_b1_gru, dsw_internal_mfma_kernel_b1_rnn,
@@ -50,10 +54,13 @@ const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell) {
         return cell <= 4 ? lookup[cell - 1](pl.reg_tiles, pl.max_tiles) : nullptr;
     }
     if (pl.batch_tile == dsw::kMaxBatch)
-        return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles);
+        return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single);
     if (pl.engine == DSW_ENGINE_VALU)
         return gumbel ? dsw_internal_walk_kernel_gumbel(pl.reg_slots, pl.batch_tile, pl.w2_dtype)
                       : dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile, pl.w2_dtype);
+    if (pl.w2_dtype == DSW_INT8 && pl.batch_tile == 1)
+        return gumbel ? dsw_internal_mfma_kernel_b1_i8_gumbel(pl.reg_tiles, pl.max_tiles)
+                      : dsw_internal_mfma_kernel_b1_i8(pl.reg_tiles, pl.max_tiles);
     if (pl.w2_dtype == DSW_INT8)
         return gumbel ? dsw_internal_mfma_i8_kernel_gumbel(pl.batch_tile, pl.reg_tiles, pl.max_tiles)
                       : dsw_internal_mfma_i8_kernel(pl.batch_tile, pl.reg_tiles, pl.max_tiles);
@@ -75,6 +82,7 @@ struct dsw_handle {
     int V, r, gamma_max, B_max, dtype;
     unsigned flags;
     dsw_devinfo dev;
+    dsw_devinfo pdev;  // what the planner sees: dev, with the workgroup count capped by dsw_set_grid
     char* ws_mem;
     size_t ws_bytes;
     uint16_t* blog_mem;  // batched kernel: logits of sampled requests, [B_max][V] bf16
@@ -164,6 +172,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->dtype = w2_dtype;
     h->flags = flags;
     h->dev = dev;
+    h->pdev = dev;
     h->trace = nullptr;
     h->trace_bytes = 0;
     h->spin_limit = dsw::kSpinLimit;
@@ -177,9 +186,10 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws_bytes = L.total;
     if (hipMalloc(&h->ws_mem, L.total) != hipSuccess) { delete h; return DSW_ERR_HIP; }
     h->ws.mail = reinterpret_cast<unsigned long long*>(h->ws_mem + L.mail);
-    h->ws.round_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.round_ctr);
-    h->ws.fam_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.fam_ctr);
-    h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.status);
+    h->ws.tokw = reinterpret_cast<unsigned long long*>(h->ws_mem + L.tokw);
+    h->ws.round_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.ctl) + dsw::kCtlRound;
+    h->ws.fam_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.ctl) + dsw::kCtlFam;
+    h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.ctl) + dsw::kCtlStatus;
     h->ws.bkey = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bkey);
     h->ws.bsum = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bsum);
     h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
@@ -211,7 +221,8 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         const int gm = (i % n_g) == 0 ? gamma_max : 3;
         dsw_plan_info pl;
         int prc = dsw_plan_compute(&dev, V, r, gm, B, w2_dtype, flags, &pl);
-        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0, cell_of(flags))
+        const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0, cell_of(flags),
+                                                    (flags & DSW_FLAG_SINGLE_ROUND) != 0)
                                         : nullptr;
         hipFuncAttributes attr;
         int per_cu = 0;
@@ -238,7 +249,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
 extern "C" int dsw_query_plan(dsw_handle_t h, int B, dsw_plan_info* out) {
     if (!h || !out) return DSW_ERR_NULL;
     if (B < 0 || B > h->B_max) return DSW_ERR_BATCH;
-    return dsw_plan_compute(&h->dev, h->V, h->r, h->gamma_max, B, h->dtype, h->flags, out);
+    return dsw_plan_compute(&h->pdev, h->V, h->r, h->gamma_max, B, h->dtype, h->flags, out);
 }
 
 namespace {
@@ -276,7 +287,7 @@ dsw::LaunchCtx ctx_of(const dsw_handle* h) {
     x.B_max = h->B_max;
     x.dtype = h->dtype;
     x.flags = h->flags;
-    x.dev = &h->dev;
+    x.dev = &h->pdev;
     x.ws = h->ws;
     x.spin_limit = h->spin_limit;
     x.skew = h->skew;
@@ -314,7 +325,8 @@ int launch_walk(const LaunchCtx& x, const void* W1, const void* W2, const float*
     int rc = dsw_plan_compute(x.dev, x.V, kRank, gamma, B, x.dtype, x.flags, &plan);
     if (rc) return rc;
     if (plan_out) *plan_out = plan;
-    const void* fn = kernel_for(plan, (x.flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr ? cell_of(x.flags) : 0);
+    const void* fn = kernel_for(plan, (x.flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr ? cell_of(x.flags) : 0,
+                                (x.flags & DSW_FLAG_SINGLE_ROUND) != 0);
     if (!fn) return DSW_ERR_PLAN;
     if (plan.batch_tile == kMaxBatch && x.ws.blog == nullptr) return DSW_ERR_PLAN;
 
@@ -461,9 +473,17 @@ extern "C" int dsw_round_counter(dsw_handle_t h, unsigned* out) {
 
 extern "C" int dsw_set_debug(dsw_handle_t h, unsigned spin_limit, unsigned skew) {
     if (!h) return DSW_ERR_NULL;
-    if (skew > 64u) return DSW_ERR_ARG;
+    if (skew > 1u) return DSW_ERR_ARG;
     h->spin_limit = spin_limit ? spin_limit : dsw::kSpinLimit;
     h->skew = skew;
+    return DSW_OK;
+}
+
+extern "C" int dsw_set_grid(dsw_handle_t h, int grid) {
+    if (!h) return DSW_ERR_NULL;
+    if (grid < 0 || grid > h->dev.cu_count) return DSW_ERR_ARG;
+    h->pdev = h->dev;
+    if (grid > 0) h->pdev.cu_count = grid;
     return DSW_OK;
 }
 

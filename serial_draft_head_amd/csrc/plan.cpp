@@ -56,7 +56,8 @@ static const int kShapesOne[][2] = {{2, 2}, {4, 4}, {8, 8}, {10, 10}, {12, 12}, 
 // int8 rows (DSW_MFMA_I8_SHAPES): a tile row takes half the registers
 static const int kShapesI8[][2] = {{4, 4}, {8, 8}, {16, 16}};
 static const int kStreamShape[2] = {0, 16};
-static int mfma_tile_for(int B, bool i8) { return (B <= 1 && !i8) ? 1 : (B <= 4 ? 4 : 16); }
+// one request (bf16 or int8 rows widened at entry), or 4 / 16 requests
+static int mfma_tile_for(int B) { return B <= 1 ? 1 : (B <= 4 ? 4 : 16); }
 // Upper bound of the MFMA kernel's static LDS for (batch tile, tiles per
 // wave, int8 rows with their fp32 scales).
 // A recurrent head keeps its state (r floats) and its cell rows in LDS: per
@@ -91,20 +92,22 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
                      dsw_plan_info* out) {
     const int tiles = ceil_div(R, kTileRows);
     const int TW = ceil_div(tiles, 4);
-    const int tile_bytes = i8 ? kTileBytes / 2 : kTileBytes;
+    const int nb = mfma_tile_for(B);
+    // one request keeps int8 rows widened to bf16 on chip; more requests keep the codes
+    const int tile_bytes = (i8 && nb != 1) ? kTileBytes / 2 : kTileBytes;
     int reg_t = -1, max_t = -1;
     if (flags & DSW_FLAG_FORCE_STREAM) {
         reg_t = kStreamShape[0];
         max_t = kStreamShape[1];
-    } else if (i8) {
-        for (const auto& sh : kShapesI8)
+    } else if (nb == 1) {
+        for (const auto& sh : kShapesOne)
             if (sh[1] >= TW) {
                 reg_t = sh[0];
                 max_t = sh[1];
                 break;
             }
-    } else if (mfma_tile_for(B, i8) == 1) {
-        for (const auto& sh : kShapesOne)
+    } else if (i8) {
+        for (const auto& sh : kShapesI8)
             if (sh[1] >= TW) {
                 reg_t = sh[0];
                 max_t = sh[1];
@@ -119,7 +122,6 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
             }
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
-    const int nb = mfma_tile_for(B, i8);
     const int lds_static = mfma_static_lds(nb, max_t, i8, (flags & DSW_FLAG_GUMBEL) != 0, flags);
     int avail = dev->max_lds_per_block - lds_static;
     if (avail < 0) return DSW_ERR_PLAN;
@@ -185,8 +187,11 @@ static const int kBShapesI8[][2] = {{8, 8}, {8, 12}};
 static const int kBStreamShape[2] = {0, 12};
 static int batched_static_lds(int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
+    // per-request keys, maxima, exp-sums, tasks and decisions; the shard
+    // masses; int8 row scales; the -inf base rows of dead tiles (4 waves x 64
+    // lanes x 8 bytes) and a few scalars; the trace
     return 4 * kMaxBatch * 4 * 3 + 4 * kMaxBatch * 4 + kMaxGrid * 4 + kMaxBatch * 4 +
-           (i8 ? 4 * rpad : 0) + 1024 + kTraceLds;
+           (i8 ? 4 * rpad : 0) + 4 * 64 * 8 + 1024 + kTraceLds;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -326,9 +331,9 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const int R = (int)rows;
     // kernel: the batched one beyond 16 requests or when asked for; an engine
     // flag forces the all-to-all kernel (up to 16 requests).  Otherwise, as
-    // measured on MI355X: one bf16 request on the MFMA engine (V = 151,936,
-    // gamma = 7: 39.7 against 42.5 us per round on VALU), one int8 request on
-    // VALU (rows widened to bf16 on chip), the MFMA all-to-all kernel for 2-3,
+    // measured on MI355X: one request on the MFMA engine (V = 151,936,
+    // gamma = 7: 39.7 against 42.5 us per round on VALU; int8 rows widened to
+    // bf16 on chip when the shard is loaded), the MFMA all-to-all kernel for 2-3,
     // the batched kernel from 4 requests (falling back to the all-to-all kernel
     // where it has no shape, e.g. int8 rows beyond 12 tiles per wave).
     const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
@@ -352,10 +357,10 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
         if ((flags & DSW_FLAG_DOMINO) && gamma > kDominoMaxGamma) return DSW_ERR_GAMMA;
     }
     bool valu = (flags & DSW_FLAG_VALU_GEMV) != 0;
-    // one bf16 request: the MFMA engine's step is ~1 us shorter, but its shard
-    // load ~3 us longer (measured at V = 151,936), so walks of up to 3 steps
-    // take the VALU engine
-    if (!forced) valu = B <= 1 && (i8 || gamma <= 3) && !cell;
+    // one request: the MFMA engine's step is ~1 us shorter, but its shard load
+    // ~3 us longer (measured at V = 151,936 in bf16), so walks of up to 3 steps
+    // take the VALU engine; both widen int8 rows to bf16 once, at entry
+    if (!forced) valu = B <= 1 && gamma <= 3 && !cell;
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);

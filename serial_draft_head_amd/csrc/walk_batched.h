@@ -84,7 +84,8 @@ constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8
 // ord16(max logit) for a sampled request whose token shard still has to find it.
 constexpr unsigned kDecPending = 1u << 20;
 
-template <int A, int M, int DT>
+// SR = 1: single rounding (logit = bf16(base + fp32 dot)), DSW_FLAG_SINGLE_ROUND.
+template <int A, int M, int DT, int SR>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
@@ -102,7 +103,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ float s_S[kMaxGrid];
     __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ int s_tasks[kMaxBatch];
-    __shared__ uint2 s_junk[64];               // epilogue writes of tiles beyond a wave's rows
+    __shared__ uint2 s_junk[4][64];            // base logits (-inf) of tiles beyond a wave's rows
     __shared__ unsigned long long s_red64[4];
     __shared__ int s_own;
     __shared__ float s_pex;
@@ -151,14 +152,21 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     char* ring = reinterpret_cast<char*>(s_dyn) + 4 * LT * 512 * (int)sizeof(WT);
     const int slot_bytes = kSlotUBytes + kGroup * Rpad * 2;
 
-    if (t == 0) {
-        s_round = ld_agent(p.ws.round_ctr);
-        s_fam = ld_agent(p.ws.fam_ctr + kFamBatched);
-        // a device error latched by an earlier launch stands until dsw_status
-        // clears the workspace: this launch then does nothing
-        s_abort = ld_agent(status) != 0u;
-        s_any_samp = 0;
+    // The control block (round counter, family counters, status word) and this
+    // thread's anchor and temperature are requested first and used only after
+    // the shard's loads have been issued, so that their round trip overlaps the
+    // shard load.  A plain load: the previous launch's updates are visible at
+    // a kernel boundary.
+    uint4 ctl = make_uint4(0u, 0u, 0u, 0u);
+    if (t == 0) ctl = *reinterpret_cast<const uint4*>(p.ws.round_ctr);
+    int a_in = 0;
+    float t_in = 0.0f;
+    if (t < B) {
+        a_in = p.anchor[t];
+        t_in = p.T[t];
     }
+    if (t == 0) s_any_samp = 0;
+    s_junk[t >> 6][t & 63] = make_uint2(0xFF80FF80u, 0xFF80FF80u);  // -inf base logits
     // every word this workgroup posts in this launch, both parities, starts at
     // 0 (the barriers before the first post order these stores first): its row
     // of keys, exp-sums and tokens, and the decision words of the requests it owns
@@ -174,25 +182,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         st_agent64(p.ws.bext + ((size_t)par * kMaxBatch + b) * 2, 0ull);
         st_agent64(p.ws.bext + ((size_t)par * kMaxBatch + b) * 2 + 1, 0ull);
     }
-    __syncthreads();
-    if (s_abort) return;  // uniform: read after the barrier
+    __syncthreads();  // s_any_samp and s_junk set (LDS only: no wait for the loads above)
     DSW_TRACE(gamma, 0);
-    if (t < B) {
-        int a = p.anchor[t];
-        float temp = p.T[t];
-        if (a < 0 || a >= V) {
-            if (c == 0) latch(status, kStatusToken);
-            a = 0;
-        }
-        if (temp > 0.0f && p.uniforms == nullptr && !p.seeded) {
-            if (c == 0) latch(status, kStatusUniforms);
-            temp = 0.0f;
-        }
-        if (!(temp > 0.0f)) temp = 0.0f;
-        s_prev[t] = a;
-        s_T[t] = temp;
-        if (temp > 0.0f) s_any_samp = 1;
-    }
 
     // ---- entry: this workgroup's shard on chip (as walk_kernel.h) --------
     WT wr[A > 0 ? A : 1][8];
@@ -229,7 +220,31 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     }
     if constexpr (kI8)
         for (int r = t; r < RPAD; r += kBlock) s_scale[r] = r < nrows ? p.w2_scale[v0 + r] : 0.0f;
+    if (t == 0) {
+        s_round = ctl.x;
+        s_fam = ctl.z;  // the batched family's counter
+        // a device error latched by an earlier launch stands until dsw_status
+        // clears the workspace: this launch then does nothing
+        s_abort = ctl.w != 0u;
+    }
+    if (t < B) {
+        int a = a_in;
+        float temp = t_in;
+        if (a < 0 || a >= V) {
+            if (c == 0) latch(status, kStatusToken);
+            a = 0;
+        }
+        if (temp > 0.0f && p.uniforms == nullptr && !p.seeded) {
+            if (c == 0) latch(status, kStatusUniforms);
+            temp = 0.0f;
+        }
+        if (!(temp > 0.0f)) temp = 0.0f;
+        s_prev[t] = a;
+        s_T[t] = temp;
+        if (temp > 0.0f) s_any_samp = 1;
+    }
     __syncthreads();
+    if (s_abort) return;  // uniform: read after the barrier
     const unsigned round = s_round;
     const unsigned fam = s_fam;
     const bool any_samp = s_any_samp != 0;
@@ -241,23 +256,28 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         if constexpr (!kI8) {                                                                    \
             /* bf16: the MFMAs of a pair of tiles are issued before the epilogue of  */          \
             /* the previous pair, whose VALU work then overlaps them                 */          \
+            /* their base logits are read from LDS with the MFMAs, a pair ahead     */          \
             f32x4_t p0_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, p1_ = p0_;                            \
+            uint2 pb0_ = make_uint2(0u, 0u), pb1_ = pb0_;                                        \
             _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                                \
+                const uint2 nb0_ = *DSW_BASE_PTR(j0), nb1_ = *DSW_BASE_PTR(j0 + 1);              \
                 f32x4_t c0_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, c1_ = c0_;                        \
                 _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                               \
                     c0_ = mfma_tile(as_bf16x8(wr[j0][kb]), ub[kb], c0_);                         \
                     c1_ = mfma_tile(as_bf16x8(wr[j0 + 1][kb]), ub[kb], c1_);                     \
                 }                                                                                \
                 if (j0 > 0) {                                                                    \
-                    EPI(p0_, j0 - 2);                                                            \
-                    EPI(p1_, j0 - 1);                                                            \
+                    EPI(p0_, j0 - 2, pb0_);                                                      \
+                    EPI(p1_, j0 - 1, pb1_);                                                      \
                 }                                                                                \
                 p0_ = c0_;                                                                       \
                 p1_ = c1_;                                                                       \
+                pb0_ = nb0_;                                                                     \
+                pb1_ = nb1_;                                                                     \
             }                                                                                    \
             if (A > 0) {                                                                         \
-                EPI(p0_, A - 2);                                                                 \
-                EPI(p1_, A - 1);                                                                 \
+                EPI(p0_, A - 2, pb0_);                                                           \
+                EPI(p1_, A - 1, pb1_);                                                           \
             }                                                                                    \
         } else _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                             \
             f32x4_t d0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;                               \
@@ -271,8 +291,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 d0 = mfma_tile(as_bf16x8(wr[j0][kb]), ub[kb], d0);                               \
                 d1 = mfma_tile(as_bf16x8(wr[j0 + 1][kb]), ub[kb], d1);                           \
             }                                                                                    \
-            if (j0 < nt_w) EPI(d0, j0);                                                          \
-            if (j0 + 1 < nt_w) EPI(d1, j0 + 1);                                                  \
+            if (j0 < nt_w) EPI(d0, j0, *DSW_BASE_PTR(j0));                                       \
+            if (j0 + 1 < nt_w) EPI(d1, j0 + 1, *DSW_BASE_PTR(j0 + 1));                           \
             __builtin_amdgcn_sched_barrier(0);                                                   \
         }                                                                                        \
         _Pragma("unroll 1") for (int j = A; j < nt_w; ++j) {                                     \
@@ -287,7 +307,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
                     dd = mfma_tile(as_bf16x8(src_[kb * 4]), ub[kb], dd);                          \
             }                                                                                    \
-            EPI(dd, j);                                                                          \
+            EPI(dd, j, *DSW_BASE_PTR(j));                                                        \
         }                                                                                        \
     } while (0)
 
@@ -353,26 +373,41 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             uint4 ub[8];
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) ub[kb] = su[n * kRowChunks + ((kb * 4 + g) ^ n)];
-            // lane's best (first) logit and row of request n; logits land over
-            // the base values they came from (the sampled pass reads them back)
+            // The partial tile of the vocabulary's last shard: base rows past the
+            // vocabulary read -inf, so that their logits lose every max and add
+            // nothing to an exp-sum.  Only the wave whose tiles hold them fills
+            // them, after the group's DMA has landed and before it reads them.
+            if (nt_w > 0 && nrows < wrow0 + nt_w * kTileRows) {
+                const int nfill = wrow0 + nt_w * kTileRows - nrows;  // 1 .. 15 rows
+                for (int e = lane; e < kGroup * nfill; e += 64) {
+                    const int nn = e & (kGroup - 1), r = nrows + (e >> 4);
+                    sb[(nn * CPR + ((r >> 3) ^ nn)) * 8 + (r & 7)] = (uint16_t)0xFF80u;
+                }
+            }
+            // Lane's best (first) logit of request n: the tile whose four logits
+            // hold the largest value first (tiles in row order, a strictly larger
+            // maximum replaces it), that tile's logits, and after the tiles the
+            // first of its four rows with that value.
             float bestv = -__builtin_inff();
-            int bestr = -1;
-#define DSW_BEST(l_, r_, ok_)                                                                    \
-    do {                                                                                         \
-        const bool better_ = (ok_) && (l_) > bestv;                                              \
-        bestv = better_ ? (l_) : bestv;                                                          \
-        bestr = better_ ? (r_) : bestr;                                                          \
-    } while (0)
+            int bestj = -1;
+            uint32_t bq01 = 0u, bq23 = 0u;
+// Base logits of tile j for this lane: the slot, or s_junk (-inf) for a
+// register tile beyond this wave's rows.
+#define DSW_BASE_PTR(j)                                                                          \
+    (((j) < nt_w) ? reinterpret_cast<uint2*>(sb + (n * CPR + (((wrow0 + (j) * kTileRows + 4 * g) >> 3) ^ n)) * 8 + \
+                                             ((wrow0 + (j) * kTileRows + 4 * g) & 7))            \
+                  : &s_junk[wave][lane])
 // Branch-free, so that the matrix cores' work and this VALU work can be
-// interleaved: a register tile beyond this wave's rows writes to s_junk and
-// updates nothing.
-#define DSW_EPI_G(dv, j)                                                                         \
+// interleaved; a tile beyond this wave's rows has -inf base logits and its
+// logits lose every max.  bw: the tile's four base logits.  STORE (a
+// constant): the logits go back into the slot over the base logits (the
+// sampled requests' exp-sum pass reads them there) and out to `lout`, with one
+// 8-byte store per lane where the vocabulary allows.
+#define DSW_EPI(dv, j, bw, STORE)                                                                \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
         const bool live_ = (j) < nt_w;                                                           \
-        uint2* e_ = live_ ? reinterpret_cast<uint2*>(sb + (n * CPR + ((rb_ >> 3) ^ n)) * 8 + (rb_ & 7)) \
-                          : &s_junk[lane];                                                       \
-        const uint2 bw_ = *e_;                                                                   \
+        const uint2 bw_ = (bw);                                                                  \
         float x0_ = (dv)[0], x1_ = (dv)[1], x2_ = (dv)[2], x3_ = (dv)[3];                        \
         if constexpr (kI8) {                                                                     \
             const int rs_ = live_ ? rb_ : 0;                                                     \
@@ -381,7 +416,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             x2_ *= s_scale[rs_ + 2];                                                             \
             x3_ *= s_scale[rs_ + 3];                                                             \
         }                                                                                        \
-        if (!p.single_round) {  /* double rounding: the bias to bf16 first */                 \
+        if constexpr (!SR) {  /* double rounding: the bias to bf16 first */                    \
             const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);       \
             x0_ = bf16_lo(p01_);                                                                 \
             x1_ = bf16_hi(p01_);                                                                 \
@@ -390,54 +425,28 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }                                                                                        \
         const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + x0_, bf16_hi(bw_.x) + x1_);         \
         const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
-        *e_ = make_uint2(q01_, q23_);                                                            \
-        const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
-        DSW_BEST(bf16_lo(q01_), rb_, 0 < lim_);                                                  \
-        DSW_BEST(bf16_hi(q01_), rb_ + 1, 1 < lim_);                                              \
-        DSW_BEST(bf16_lo(q23_), rb_ + 2, 2 < lim_);                                              \
-        DSW_BEST(bf16_hi(q23_), rb_ + 3, 3 < lim_);                                              \
-    } while (0)
-// As DSW_EPI_G, and this lane's four logits go out with one 8-byte store.
-#define DSW_EPI_GS(dv, j)                                                                         \
-    do {                                                                                         \
-        const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
-        const bool live_ = (j) < nt_w;                                                           \
-        uint2* e_ = live_ ? reinterpret_cast<uint2*>(sb + (n * CPR + ((rb_ >> 3) ^ n)) * 8 + (rb_ & 7)) \
-                          : &s_junk[lane];                                                       \
-        const uint2 bw_ = *e_;                                                                   \
-        float x0_ = (dv)[0], x1_ = (dv)[1], x2_ = (dv)[2], x3_ = (dv)[3];                        \
-        if constexpr (kI8) {                                                                     \
-            const int rs_ = live_ ? rb_ : 0;                                                     \
-            x0_ *= s_scale[rs_];                                                                 \
-            x1_ *= s_scale[rs_ + 1];                                                             \
-            x2_ *= s_scale[rs_ + 2];                                                             \
-            x3_ *= s_scale[rs_ + 3];                                                             \
-        }                                                                                        \
-        if (!p.single_round) {  /* double rounding: the bias to bf16 first */                 \
-            const uint32_t p01_ = pack_bf16_rne(x0_, x1_), p23_ = pack_bf16_rne(x2_, x3_);       \
-            x0_ = bf16_lo(p01_);                                                                 \
-            x1_ = bf16_hi(p01_);                                                                 \
-            x2_ = bf16_lo(p23_);                                                                 \
-            x3_ = bf16_hi(p23_);                                                                 \
-        }                                                                                        \
-        const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + x0_, bf16_hi(bw_.x) + x1_);         \
-        const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
-        *e_ = make_uint2(q01_, q23_);                                                            \
-        const int lim_ = (bval && live_) ? nrows - rb_ : 0;                                      \
-        if (lout != nullptr && lim_ > 0) {                                                       \
-            if (al4 && lim_ >= 4) {                                                              \
-                *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);                  \
-            } else {                                                                             \
-                const uint32_t l4_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16}; \
-                _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                  \
-                    if (i_ < lim_) lout[rb_ + i_] = (uint16_t)l4_[i_];                            \
+        if (STORE) {                                                                             \
+            *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                           \
+            const int lim_ = live_ ? nrows - rb_ : 0;                                            \
+            if (lout != nullptr && lim_ > 0) {                                                   \
+                if (al4 && lim_ >= 4) {                                                          \
+                    *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);              \
+                } else {                                                                         \
+                    const uint32_t l4_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16}; \
+                    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                              \
+                        if (i_ < lim_) lout[rb_ + i_] = (uint16_t)l4_[i_];                        \
+                }                                                                                \
             }                                                                                    \
         }                                                                                        \
-        DSW_BEST(bf16_lo(q01_), rb_, 0 < lim_);                                                  \
-        DSW_BEST(bf16_hi(q01_), rb_ + 1, 1 < lim_);                                              \
-        DSW_BEST(bf16_lo(q23_), rb_ + 2, 2 < lim_);                                              \
-        DSW_BEST(bf16_hi(q23_), rb_ + 3, 3 < lim_);                                              \
+        const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
+        const bool gt_ = tm_ > bestv;                                                            \
+        bestv = gt_ ? tm_ : bestv;                                                               \
+        bestj = gt_ ? (j) : bestj;                                                               \
+        bq01 = gt_ ? q01_ : bq01;                                                                \
+        bq23 = gt_ ? q23_ : bq23;                                                                \
     } while (0)
+#define DSW_EPI_G(dv, j, bw) DSW_EPI(dv, j, bw, 0)
+#define DSW_EPI_GS(dv, j, bw) DSW_EPI(dv, j, bw, 1)
             // Logits go out straight from the epilogue: to `logits` when asked
             // for, and for sampled requests in any case (to the workspace
             // otherwise), where the token shard reads them back.  A group with
@@ -453,20 +462,26 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             }
 #undef DSW_EPI_G
 #undef DSW_EPI_GS
+#undef DSW_EPI
+#undef DSW_BASE_PTR
+            // the first of the best tile's four rows with the best value
+            const int bi = bf16_lo(bq01) == bestv ? 0 : (bf16_hi(bq01) == bestv ? 1 : (bf16_lo(bq23) == bestv ? 2 : 3));
+            const int bestr = bestj >= 0 ? wrow0 + bestj * kTileRows + 4 * g + bi : -1;
             uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
             // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
             best = max(best, (uint32_t)__shfl_xor((int)best, 16));
             best = max(best, (uint32_t)__shfl_xor((int)best, 32));
             if (g == 0 && bval) s_rkey[wave][b] = best;
-            if (any_samp) {
-                const float Tb = bval ? s_T[b] : 0.0f;
+            const float Tb = bval ? s_T[b] : 0.0f;
+            const bool on = Tb > 0.0f && best != 0u;
+            if (any_samp && __builtin_amdgcn_ballot_w64(on) != 0ull) {
+                // exp-sum of this wave's logits of request n relative to its
+                // maximum: every live tile's four logits are read first (all
+                // reads in flight), then the exps; rows past the vocabulary hold
+                // -inf (exp 0); lanes of greedy or empty columns drop theirs
                 const float mw = local_key_logit(best);
-                float sw = 0.0f;
-                // every tile's four logits are read first (all reads in flight,
-                // rows clamped into the slot), then the exps; lanes of greedy or
-                // empty columns compute theirs and drop them
-                const bool on = Tb > 0.0f && best != 0u;
                 const float sc = on ? kLog2e / Tb : 0.0f;
+                float sw4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four independent sums
                 uint2 lw[M];
 #pragma unroll
                 for (int j = 0; j < M; ++j) {
@@ -475,15 +490,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 }
 #pragma unroll
                 for (int j = 0; j < M; ++j) {
-                    const int rb = wrow0 + j * kTileRows + 4 * g;
-                    const int lim = (on && j < nt_w) ? nrows - rb : 0;
-                    const float lv[4] = {bf16_lo(lw[j].x), bf16_hi(lw[j].x), bf16_lo(lw[j].y), bf16_hi(lw[j].y)};
+                    if (j < nt_w) {  // wave-uniform
+                        const float lv[4] = {bf16_lo(lw[j].x), bf16_hi(lw[j].x), bf16_lo(lw[j].y), bf16_hi(lw[j].y)};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = __builtin_amdgcn_exp2f((lv[i] - mw) * sc);
-                        sw += i < lim ? e : 0.0f;
+                        for (int i = 0; i < 4; ++i) sw4[i] += __builtin_amdgcn_exp2f((lv[i] - mw) * sc);
                     }
                 }
+                float sw = on ? (sw4[0] + sw4[1]) + (sw4[2] + sw4[3]) : 0.0f;
                 sw += __shfl_xor(sw, 16);
                 sw += __shfl_xor(sw, 32);
                 if (g == 0 && bval) {

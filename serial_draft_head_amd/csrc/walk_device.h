@@ -163,19 +163,29 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
     return x;
 }
 
-// Diagnostics (dsw_set_debug): with p.skew > 0, the calling wave sleeps
+// Diagnostics (dsw_set_debug): with p.skew != 0, the calling wave sleeps
 // before a post for a pseudo-random number (0..7, from the workgroup, step and
-// call site) of p.skew units of s_sleep 127 (~8k clocks each), so that
-// workgroups reach the rendezvous in a scrambled order.  Bounded; never runs
-// with p.skew == 0.
+// call site) of units of s_sleep 127 (~8k clocks each), so that workgroups
+// reach the rendezvous in a scrambled order.  No loop: three fixed sleeps
+// guarded by the bits of the count (a loop nested in the step loop measurably
+// slowed the walk even when it never ran).
 __device__ __forceinline__ void walk_skew(const WalkParams& p, int c, int k, int site) {
     if (p.skew == 0u) return;
     uint32_t h = (uint32_t)c * 0x9E3779B1u ^ ((uint32_t)k * 0x85EBCA77u + (uint32_t)site * 0xC2B2AE3Du);
     h ^= h >> 15;
     h *= 0x2C1B3C6Du;
     h ^= h >> 12;
-    const uint32_t n = (h & 7u) * p.skew;
-    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
+    if (h & 1u) __builtin_amdgcn_s_sleep(127);
+    if (h & 2u) {
+        __builtin_amdgcn_s_sleep(127);
+        __builtin_amdgcn_s_sleep(127);
+    }
+    if (h & 4u) {
+        __builtin_amdgcn_s_sleep(127);
+        __builtin_amdgcn_s_sleep(127);
+        __builtin_amdgcn_s_sleep(127);
+        __builtin_amdgcn_s_sleep(127);
+    }
 }
 
 // A token id that will index W1: out-of-range ids latch kStatusToken and

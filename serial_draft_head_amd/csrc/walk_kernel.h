@@ -139,16 +139,19 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kMfma = ENGINE == kEngineMfma;
     constexpr bool kI8 = DT == 1;  // int8 rows + fp32 row scales
     static_assert(!kI8 || kMfma || NB == 1, "int8 rows on the VALU engine: one request");
-    // one K block of 8 weights of a lane's tile row (MFMA), or 16 bytes of a row
-    // (VALU; int8 rows are widened to bf16 once, at entry)
-    using WT = typename std::conditional<kI8 && kMfma, uint2, uint4>::type;
     static_assert(NB == 1 || NB == 4 || NB == 16, "batch tile");
     // one request on the MFMA engine: tiles gathered four at a time, up to
     // kMaxRegTiles tiles per wave in AGPRs and kMaxVgprTiles more in VGPRs
     constexpr bool kOne = kMfma && NB == 1;
-    static_assert(!kMfma || (A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles + (kOne ? kMaxVgprTiles : 0)),
+    // MT: one K block of 8 weights of a lane's tile row as stored in memory
+    // (MFMA: 8 int8 codes or 8 bf16), or 16 bytes of a row (VALU).  WT: the
+    // same on chip -- the MFMA engine with up to 16 requests keeps int8 codes
+    // and widens them every step; one request keeps rows widened to bf16 once,
+    // at entry (exact: |q| <= 127), as does the VALU engine
+    using MT = typename std::conditional<kI8 && kMfma, uint2, uint4>::type;
+    using WT = typename std::conditional<kI8 && kMfma && !kOne, uint2, uint4>::type;
+    static_assert(!kMfma || (A <= M && A <= (kI8 && !kOne ? 2 : 1) * kMaxRegTiles + (kOne ? kMaxVgprTiles : 0)),
                   "MFMA shape");
-    static_assert(!kOne || !kI8, "one-request MFMA engine: bf16 rows");
     static_assert(kMfma || (A >= 0 && A <= kMaxSlots), "VALU shape");
     constexpr bool kCell = CELL != 0;                           // a recurrent head
     constexpr bool kDomino = CELL == 4;                         // the GRU reading the drafter's hidden states
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // register slots beyond the shard load its last row (a cache hit), never
     // another shard's rows (extra HBM reads); an empty shard loads row V - 1
     const int last_row = nrows > 0 ? v0 + nrows - 1 : V - 1;
-    const WT* __restrict__ W2 = reinterpret_cast<const WT*>(p.W2);
+    const MT* __restrict__ W2 = reinterpret_cast<const MT*>(p.W2);
     WT* s_wt = reinterpret_cast<WT*>(s_w);
     const uint4* __restrict__ W1 = reinterpret_cast<const uint4*>(p.W1);
     const uint16_t* __restrict__ base = p.base;
@@ -251,38 +254,29 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     const int wrow0 = wave * TW * kTileRows;
     const int nt_w = kMfma ? max(0, min(TW, (nrows - wrow0 + kTileRows - 1) / kTileRows)) : 0;
 
-    if (t == 0) {
-        s_round = ld_agent(p.ws.round_ctr);
-        s_fam = ld_agent(p.ws.fam_ctr + kFamAll);
-        // a device error latched by an earlier launch stands until dsw_status
-        // clears the workspace: this launch then does nothing
-        s_abort = ld_agent(status) != 0u;
+    // The control block (round counter, family counters, status word) and this
+    // thread's anchor and temperature are requested first and used only after
+    // the shard's loads have been issued, so that their round trip overlaps the
+    // shard load.  A plain load: the previous launch's updates are visible at
+    // a kernel boundary.
+    uint4 ctl = make_uint4(0u, 0u, 0u, 0u);
+    if (t == 0) ctl = *reinterpret_cast<const uint4*>(p.ws.round_ctr);
+    int a_in = 0;
+    float t_in = 0.0f;
+    if (t < NB && t < B) {
+        a_in = p.anchor[t];
+        t_in = p.T[t];
     }
     // every word this workgroup posts in this launch, both parities, starts
     // at 0 (the barriers before the first post order these stores first)
     if (t < 2 * kMailWords)
         st_agent64(p.ws.mail + ((size_t)(t / kMailWords) * kMaxGrid + c) * kMailWords + t % kMailWords, 0ull);
-    DSW_TRACE(gamma, 0);
-    if (t < NB) {
-        int a = 0;
-        float temp = 0.0f;
-        if (t < B) {
-            a = p.anchor[t];
-            temp = p.T[t];
-            if (a < 0 || a >= V) {
-                if (c == 0) latch(status, kStatusToken);
-                a = 0;
-            }
-            if (temp > 0.0f && p.uniforms == nullptr && !p.seeded) {
-                if (c == 0) latch(status, kStatusUniforms);
-                temp = 0.0f;
-            }
-            if (!(temp > 0.0f)) temp = 0.0f;
-        }
-        s_anchor[t] = a;
-        s_prev[t] = a;
-        s_T[t] = temp;
+    else if (t < 2 * kMailWords + 2 * kMaxBatchPersistent) {
+        const int i = t - 2 * kMailWords;
+        st_agent64(p.ws.tokw + ((size_t)(i / kMaxBatchPersistent) * kMaxGrid + c) * kMaxBatchPersistent +
+                       i % kMaxBatchPersistent, 0ull);
     }
+    DSW_TRACE(gamma, 0);
     for (int j = t; j < NB * US; j += kBlock) s_u[j] = make_uint4(0u, 0u, 0u, 0u);
     // gated head: the exact split h = hi + lo + lo2 into bf16 pieces (fp32 h
     // has 24 significant bits, each piece takes the next 8), stored by thread m
@@ -407,13 +401,51 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     uint32_t bq[NQ];  // one request, MFMA: base logits of rows wrow0 + 64q + lane
     // one request, MFMA: does group q's row for this lane exist in the shard
 #define DSW_ONE_ROW_OK(q) ((4 * (q) + (lane >> 4)) < nt_w && wrow0 + 64 * (q) + lane < nrows)
-    if constexpr (kMfma) {
+    if constexpr (kMfma && kOne && kI8) {
+        // int8 codes widened to bf16 on chip, in two passes (the AGPR tiles,
+        // then the VGPR tiles) so that the codes in flight and the widened
+        // tiles fit in the registers together; within a pass every load is
+        // issued before the first widening
+        constexpr int P1 = A < kMaxRegTiles ? A : kMaxRegTiles;
+        {
+            uint2 raw[P1 > 0 ? P1 : 1][8];
+#pragma unroll
+            for (int j = 0; j < P1; ++j) {
+                const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) raw[j][kb] = W2[(size_t)row * kRowChunks + DSW_KC(kb, g)];
+            }
+#pragma unroll
+            for (int j = 0; j < P1; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    wr[j][kb] = as_bf16x8(raw[j][kb]);
+                    pin_agpr(wr[j][kb]);
+                }
+        }
+        if constexpr (A > kMaxRegTiles) {
+            uint2 raw[A - P1][8];
+#pragma unroll
+            for (int j = P1; j < A; ++j) {
+                const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) raw[j - P1][kb] = W2[(size_t)row * kRowChunks + DSW_KC(kb, g)];
+            }
+#pragma unroll
+            for (int j = P1; j < A; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    wr[j][kb] = as_bf16x8(raw[j - P1][kb]);
+                    pin_vgpr(wr[j][kb]);
+                }
+        }
+    } else if constexpr (kMfma) {
 #pragma unroll
         for (int j = 0; j < A; ++j) {
             // rows outside the shard load the shard's last row instead (no
             // second, zeroed copy of the registers); their results are never used
             const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
-            const WT* src = W2 + (size_t)row * kRowChunks;
+            const MT* src = W2 + (size_t)row * kRowChunks;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[DSW_KC(kb, g)];
         }
@@ -427,6 +459,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 if (j < kMaxRegTiles) pin_agpr(wr[j][kb]);
                 else pin_vgpr(wr[j][kb]);
             }
+    }
+    if constexpr (kMfma) {
         if constexpr (kOne) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
@@ -435,7 +469,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         // LDS tiles: 8 loads per thread in flight before their stores; only
         // tiles that exist in this shard have an LDS slot
         for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
-            WT v[8];
+            MT v[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int idx = i0 + q * kBlock + t;
@@ -443,7 +477,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int ws = s / max(LT, 1);
                 const int j = A + (s - ws * LT);
                 const int r = ws * TW * kTileRows + j * kTileRows + (ln & 15);
-                v[q] = WT{};
+                v[q] = MT{};
                 if (idx < 4 * LT * 512 && j < TW && r < nrows)
                     v[q] = W2[(size_t)(v0 + r) * kRowChunks + DSW_KC(kb, ln >> 4)];
             }
@@ -454,7 +488,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int s = idx >> 9;
                 const int ws = s / max(LT, 1);
                 const int j = A + (s - ws * LT);
-                if (idx < 4 * LT * 512 && j < TW && ws * TW * kTileRows + j * kTileRows < nrows) s_wt[idx] = v[q];
+                if (idx < 4 * LT * 512 && j < TW && ws * TW * kTileRows + j * kTileRows < nrows) {
+                    if constexpr (kOne && kI8) s_wt[idx] = as_bf16x8(v[q]);  // widened once
+                    else s_wt[idx] = v[q];
+                }
             }
         }
         if constexpr (kI8)
@@ -511,7 +548,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         for (int s = 0; s < A; ++s) {
             const int i = s * kBlock + t;
             if (i < reg_rows) {
-                const WT* src = W2 + (size_t)(v0 + i) * kRowChunks;
+                const MT* src = W2 + (size_t)(v0 + i) * kRowChunks;
 #pragma unroll
                 for (int ch = 0; ch < kRowChunks; ++ch) wr[s][ch] = src[ch];
             } else {
@@ -532,8 +569,37 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 bs[b][s] = (b < B && i < nrows) ? (uint32_t)base[((size_t)b * gamma) * V + v0 + i] : 0u;
             }
     }
+    if (t == 0) {
+        s_round = ctl.x;
+        s_fam = (kFamAll == 0 ? ctl.y : ctl.z);
+        // a device error latched by an earlier launch stands until dsw_status
+        // clears the workspace: this launch then does nothing
+        s_abort = ctl.w != 0u;
+    }
+    if (t < NB) {
+        int a = a_in;
+        float temp = t_in;
+        if (t < B) {
+            if (a < 0 || a >= V) {
+                if (c == 0) latch(status, kStatusToken);
+                a = 0;
+            }
+            if (temp > 0.0f && p.uniforms == nullptr && !p.seeded) {
+                if (c == 0) latch(status, kStatusUniforms);
+                temp = 0.0f;
+            }
+            if (!(temp > 0.0f)) temp = 0.0f;
+        }
+        s_anchor[t] = a;
+        s_prev[t] = a;
+        s_T[t] = temp;
+    }
     __syncthreads();
     if (s_abort) return;  // uniform: read after the barrier
+    // diagnostics: a pseudo-random delay per workgroup before the walk, so that
+    // the workgroups reach the first rendezvous in a scrambled order (a hook
+    // inside the step loop measurably slowed every step, even when off)
+    walk_skew(p, c, 0, 0);
     const unsigned round = s_round;
     const unsigned fam = s_fam;
     bool any_samp = false;
@@ -802,11 +868,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                             } else {
                                 const int r = wrow0 + j * kTileRows + n;
                                 const bool ok = r < nrows;
-                                const uint4* src = reinterpret_cast<const uint4*>(p.W2) +
-                                                   (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
+                                const MT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
 #pragma unroll
                                 for (int kb = 0; kb < 8; ++kb)
-                                    d[jj] = mfma_tile(a[kb], ok ? src[DSW_KC(kb, g)] : make_uint4(0u, 0u, 0u, 0u),
+                                    d[jj] = mfma_tile(a[kb], ok ? as_bf16x8(src[DSW_KC(kb, g)]) : make_uint4(0u, 0u, 0u, 0u),
                                                       d[jj]);
                             }
                         }
@@ -814,7 +879,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     const float acc1 = combine4(d[0][0], d[1][0], d[2][0], d[3][0]);
                     if (DSW_ONE_ROW_OK(gq)) {
                         const int r = wrow0 + 64 * gq + lane;
-                        const float bias = bias_round(acc1, dbl_round);
+                        const float bias = bias_round(kI8 ? s_scale[r] * acc1 : acc1, dbl_round);
                         const uint32_t lbits = f32_to_bf16(bf16_to_f32(bq[gq]) + bias);
                         best[0] = max(best[0], local_key(lbits, r));
                         s_logit[r] = (uint16_t)lbits;
@@ -880,10 +945,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     } else {
                         const int r = wrow0 + j * kTileRows + n;
                         const bool ok = r < nrows;
-                        const WT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
+                        const MT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
 #pragma unroll
                         for (int kb = 0; kb < 8; ++kb)
-                            dd = mfma_tile(a[kb], as_bf16x8(ok ? src[DSW_KC(kb, g)] : WT{}), dd);
+                            dd = mfma_tile(a[kb], as_bf16x8(ok ? src[DSW_KC(kb, g)] : MT{}), dd);
                     }
                     DSW_EPI_MFMA(dd, j);
                 }
@@ -950,7 +1015,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                                     if (NB == 1 || b < B) acc[b][s] = dot8(w4[q], s_u[b * US + c0 + q], acc[b][s]);
                         }
                     } else {
-                        const WT* src = W2 + (size_t)(v0 + i) * kRowChunks;
+                        const MT* src = W2 + (size_t)(v0 + i) * kRowChunks;
                         const uint2* srcq = reinterpret_cast<const uint2*>(p.W2) + (size_t)(v0 + i) * kRowChunks;
 #pragma unroll 1
                         for (int c0 = 0; c0 < kRowChunks; c0 += kGrp) {
@@ -1106,7 +1171,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         }
 
         // ---- rendezvous: post, write the logits out, read every mailbox ------
-        if (wave == 0) walk_skew(p, c, k, 0);
         if (wave == 0 && lane < B) {
             const uint32_t lk = max(max(s_wbest[0][lane], s_wbest[1][lane]), max(s_wbest[2][lane], s_wbest[3][lane]));
             unsigned long long* box = mail_q + (size_t)c * kMailWords;
@@ -1332,8 +1396,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
                 __syncthreads();
                 if (t == 0) s_prev[b] = tok;
-                if (t == b) {  // into this workgroup's own mailbox region
-                    st_agent64(mail_q + (size_t)c * kMailWords + kMailToks + b,
+                if (t == b) {  // into this workgroup's own row of token words
+                    st_agent64(p.ws.tokw + ((size_t)q * kMaxGrid + c) * kMaxBatchPersistent + b,
                                ((unsigned long long)(unsigned)tok << 32) | epoch);
                 }
             }
@@ -1341,7 +1405,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             if (t < B && s_T[t] > 0.0f && s_own[t] != c) {
                 // (an owner of -1, no shard with mass, cannot occur: the winner's
                 // shard always has mass >= 1; the clamp keeps the read in bounds)
-                const unsigned long long* tbox = mail_q + (size_t)max(s_own[t], 0) * kMailWords + kMailToks + t;
+                const unsigned long long* tbox =
+                    p.ws.tokw + ((size_t)q * kMaxGrid + max(s_own[t], 0)) * kMaxBatchPersistent + t;
                 unsigned it = 0;
                 unsigned long long v = 0ull;
                 bool ok = true;

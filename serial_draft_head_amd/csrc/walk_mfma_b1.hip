@@ -15,12 +15,16 @@
 #ifndef DSW_CELL
 #define DSW_CELL 0
 #endif
+// DSW_DT 0: bf16 rows; 1: int8 rows with fp32 row scales (walk_mfma_b1_i8.hip)
+#ifndef DSW_DT
+#define DSW_DT 0
+#endif
 
 // Host-side lookup used by the launcher: the kernel for (register tiles,
 // tiles per wave) at batch tile 1, or nullptr when that shape is not compiled.
 extern "C" const void* DSW_LOOKUP(int reg_tiles, int max_tiles) {
 #define DSW_PICK(R, M) \
-    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_kernel<dsw::kEngineMfma, (R), (M), 1, 0, DSW_SAMPLER, DSW_CELL>;
+    if (reg_tiles == (R) && max_tiles == (M)) return (const void*)dsw::walk_kernel<dsw::kEngineMfma, (R), (M), 1, DSW_DT, DSW_SAMPLER, DSW_CELL>;
     DSW_MFMA_ONE_SHAPES(DSW_PICK)
 #undef DSW_PICK
     return nullptr;

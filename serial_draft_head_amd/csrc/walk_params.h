@@ -35,8 +35,8 @@ constexpr int kTraceSteps = 16;    // steps the optional phase trace records
 // one, never a full period.  Every word has one writing workgroup.
 constexpr int kMailKeys = 0;        // word b: request b's key (or Gumbel score)
 constexpr int kMailSums = 16;       // word 16 + b: its exp-sum (or Gumbel ~id)
-constexpr int kMailToks = 32;       // word 32 + b: its sampled token, posted by the owner shard
-constexpr int kMailWords = 48;      // per workgroup and parity
+constexpr int kMailWords = 32;      // per workgroup and parity (256 bytes: measured faster to
+                                    // poll than a 384-byte stride)
 constexpr int kMaxBatchPersistent = 16;  // requests per launch of the all-to-all kernel
 constexpr int kCellMaxPerWg = 4;   // recurrent heads: state elements per workgroup (one per wave; grid >= 64)
 constexpr int kDominoMaxGamma = 16;  // Domino's head: steps per round (its drafters' blocks)
@@ -50,11 +50,17 @@ constexpr int kMaxGammaMax = 4096;            // gamma_max bound: 2 gamma_max st
 constexpr int kFamAll = 0;                    // family counter of the all-to-all kernels
 constexpr int kFamBatched = 1;                // family counter of the batched kernel
 constexpr unsigned epoch_of(unsigned seq) { return (seq & (kEpochPeriod - 1u)) + 1u; }
+// The control block: one 16-byte aligned line that a kernel reads with a single
+// load when it starts (a kernel boundary makes the previous launch's updates
+// visible): {round counter, family counters [2], status word}.
+constexpr int kCtlRound = 0, kCtlFam = 1, kCtlStatus = 3;
 struct Workspace {
     unsigned long long* mail;      // [2][kMaxGrid][kMailWords]
-    unsigned* round_ctr;           // [1]  completed launches (keys the device-drawn noise)
-    unsigned* fam_ctr;             // [2]  completed launches per kernel family (the epochs)
-    unsigned* status;              // [1]  latched kStatus* bits
+    unsigned long long* tokw;      // [2][kMaxGrid][kMaxBatchPersistent]  sampled token << 32 | epoch,
+                                   // in the row of the shard that found it
+    unsigned* round_ctr;           // ctl[0]  completed launches (keys the device-drawn noise)
+    unsigned* fam_ctr;             // ctl[1..2]  completed launches per kernel family (the epochs)
+    unsigned* status;              // ctl[3]  latched kStatus* bits
     // batched kernel (requests owned by workgroups): every workgroup posts one
     // key word (and one exp-sum word) per request; the owner of request b
     // reads column b and publishes a decision; a token shard publishes tokens
@@ -78,16 +84,15 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, round_ctr, fam_ctr, status, bkey, bsum, bdec, btok, bext, total;
+    size_t mail, tokw, ctl, bkey, bsum, bdec, btok, bext, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     WorkspaceLayout L;
     size_t o = 0;
     L.mail = o;      o = up(o + 2 * (size_t)kMaxGrid * kMailWords * 8);
-    L.round_ctr = o; o = up(o + 4);
-    L.fam_ctr = o;   o = up(o + 8);
-    L.status = o;    o = up(o + 4);
+    L.tokw = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatchPersistent * 8);
+    L.ctl = o;       o = up(o + 16);
     L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bsum = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bdec = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);

@@ -94,9 +94,10 @@ dsw::Workspace workspace_at(unsigned char* base) {
     const dsw::WorkspaceLayout L = dsw::workspace_layout();
     dsw::Workspace ws;
     ws.mail = reinterpret_cast<unsigned long long*>(base + L.mail);
-    ws.round_ctr = reinterpret_cast<unsigned*>(base + L.round_ctr);
-    ws.fam_ctr = reinterpret_cast<unsigned*>(base + L.fam_ctr);
-    ws.status = reinterpret_cast<unsigned*>(base + L.status);
+    ws.tokw = reinterpret_cast<unsigned long long*>(base + L.tokw);
+    ws.round_ctr = reinterpret_cast<unsigned*>(base + L.ctl) + dsw::kCtlRound;
+    ws.fam_ctr = reinterpret_cast<unsigned*>(base + L.ctl) + dsw::kCtlFam;
+    ws.status = reinterpret_cast<unsigned*>(base + L.ctl) + dsw::kCtlStatus;
     ws.bkey = reinterpret_cast<unsigned long long*>(base + L.bkey);
     ws.bsum = reinterpret_cast<unsigned long long*>(base + L.bsum);
     ws.bdec = reinterpret_cast<unsigned long long*>(base + L.bdec);

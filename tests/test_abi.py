@@ -176,11 +176,12 @@ def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
 def test_planner_choices_on_mi355x_shapes(dsw):
     d = fake_device(dsw)
     pick = lambda p: (p.rows_per_wg, p.tiles_per_wave, p.reg_tiles, p.lds_tiles, p.stream_rows)
-    # by default bf16 rows take the MFMA engine (one request: batch tile 1),
-    # one int8 request the VALU engine
+    # by default one request takes the MFMA engine with batch tile 1, bf16 or
+    # int8 rows (widened on chip)
     assert dsw.plan(d, 151_936, 7, 1).engine == 1 and dsw.plan(d, 151_936, 7, 1).batch_tile == 1
     assert dsw.plan(d, 151_936, 7, 2).engine == 1
-    assert dsw.plan(d, 151_936, 7, 1, w2_dtype=dsw.INT8).engine == 0
+    i1 = dsw.plan(d, 151_936, 7, 1, w2_dtype=dsw.INT8)
+    assert (i1.engine, i1.batch_tile, i1.reg_tiles, i1.max_tiles) == (1, 1, 10, 10)
     # short walks of one bf16 request take the VALU engine (its shard load is shorter)
     assert dsw.plan(d, 151_936, 3, 1).engine == 0 and dsw.plan(d, 151_936, 4, 1).engine == 1
     assert pick(dsw.plan(d, 32_000, 7, 1, flags=8)) == (125, 2, 2, 0, 0)
@@ -332,19 +333,27 @@ def test_planner_domino_head(dsw):
 def test_planner_int8_rows(dsw):
     d = fake_device(dsw)
     pick = lambda p: (p.engine, p.tiles_per_wave, p.reg_tiles, p.lds_tiles, p.stream_rows)  # noqa: E731
-    # int8 rows take half the registers: V = 248,320 is fully resident at 16 tiles per wave
-    c3 = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=dsw.FLAG_MFMA_GEMV)
+    # with more than one request int8 codes take half the registers: V = 248,320
+    # is fully resident at 16 tiles per wave
+    c3 = dsw.plan(d, 248_320, 16, 2, w2_dtype=dsw.INT8, flags=dsw.FLAG_MFMA_GEMV)
     assert pick(c3) == (1, 16, 16, 0, 0) and c3.path == 0 and c3.w2_dtype == dsw.INT8
     assert c3.onchip_bytes == 248_320 * 256 and c3.stream_bytes == 0
     assert pick(dsw.plan(d, 248_320, 16, 16, w2_dtype=dsw.INT8)) == (1, 16, 16, 0, 0)
-    # one request takes the VALU engine: two widened register groups, LDS rows
-    # (bf16, 512 bytes each) and the rest streamed as int8 every step
-    v = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8)
+    # one request takes the one-request MFMA engine: rows widened to bf16 on
+    # chip, 12 register and 4 LDS tiles per wave as in bf16, nothing streamed
+    one = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8)
+    assert pick(one) == (1, 16, 12, 4, 0) and one.batch_tile == 1 and one.path == 0
+    assert one.onchip_bytes == 248_320 * 256 and one.stream_bytes == 0
+    # forced onto the VALU engine: two widened register groups, LDS rows (bf16,
+    # 512 bytes each) and the rest streamed as int8 every step
+    v = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=dsw.FLAG_VALU_GEMV)
     assert (v.engine, v.reg_slots, v.reg_rows) == (0, 2, 512) and v.path == 1
     assert v.lds_rows == (v.lds_bytes // 512) and v.lds_rows + v.stream_rows == 970 - 512
     assert v.stream_bytes == 256 * v.stream_rows * 256 and v.onchip_bytes + v.stream_bytes == 248_320 * 256
     # small vocabularies fit in the two register groups
-    assert dsw.plan(d, 100_000, 7, 1, w2_dtype=dsw.INT8).path == 0
+    assert dsw.plan(d, 100_000, 7, 1, w2_dtype=dsw.INT8, flags=dsw.FLAG_VALU_GEMV).path == 0
+    # short walks of one int8 request take the VALU engine, like bf16
+    assert dsw.plan(d, 100_000, 3, 1, w2_dtype=dsw.INT8).engine == 0
     # smaller vocabularies take the smaller compiled shapes
     assert dsw.plan(d, 60_000, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 4
     assert dsw.plan(d, 129_280, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 8

@@ -913,6 +913,7 @@ def test_gru_head_argument_errors(dsw):
 # ragged sizes; the harness quantizes once and both sides consume (q, scale).
 I8_VOCABS = [(257, (4, 4)), (4097, (4, 4)), (60_000, (4, 4)), (129_280, (8, 8)),
              (248_320, (16, 16))]
+I8_ONE_SHAPES = {257: (2, 2), 4097: (2, 2), 60_000: (4, 4), 129_280: (8, 8), 248_320: (12, 16)}
 
 
 def int8_dev(Q, scale):
@@ -928,6 +929,8 @@ def test_int8_rows(dsw, V, shape, B):
     w = parity.Weights(W1, Q=Q, scale=sc)
     walker = dsw.Walker(V, gamma_max=4, B_max=16, w2_dtype=dsw.INT8, flags=dsw.FLAG_MFMA_GEMV)
     pl = walker.query_plan(B)
+    if B == 1:  # one request: rows widened to bf16 on chip, the bf16 one-request shapes
+        shape = I8_ONE_SHAPES[V]
     assert (pl.engine, pl.reg_tiles, pl.max_tiles, pl.stream_rows) == (1, *shape, 0)
     W1d = bf16_dev(W1)
     Qd, sd = int8_dev(Q, sc)
