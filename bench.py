@@ -62,6 +62,84 @@ def recorded_traffic(workload_name, B, gamma, cold=False):
     return rec.get("hbm_bytes_per_launch")
 
 
+READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+
+
+def summarize_counters(outdir, workload_name, V, B, gamma, cold, dest_dir=PROFILES):
+    """The counter record of one workload from rocprofv3 --pmc CSV output
+    under `outdir` (any number of runs of --pmc-mode, each with some of
+    READ_COUNTERS / WRITE_COUNTERS): per-dispatch means for the walk kernel
+    and for the 256 MiB calibration copy, and the bytes they stand for.
+
+    L2-to-fabric requests: reads of 32 B (RDREQ_32B), 128 B (BUBBLE) and
+    64 B (the rest); writes of 64 B (WRREQ_64B) and 32 B (the rest).  Each
+    direction is scaled by what the same sum reads for the copy of known
+    size.  With L2 and the Infinity Cache flushed before each launch these
+    are HBM bytes; warm they count L2 misses, some of which the Infinity
+    Cache serves."""
+    import csv
+    import glob
+    walk_names, w_vals, cp = set(), {}, {}  # walk: counter -> [per dispatch]; copy: counter -> value
+    for path in glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True):
+        disp = {}  # dispatch id -> (kernel, {counter: value summed over rows})
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                d = disp.setdefault(int(row["Dispatch_Id"]), (row["Kernel_Name"], {}))[1]
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        for kname, d in disp.values():
+            if "dsw::walk_" in kname:
+                walk_names.add(kname)
+                for c, v in d.items():
+                    w_vals.setdefault(c, []).append(v)
+        # the calibration copy: the last copy dispatch of real size in this run
+        # (earlier ones upload the inputs, a later tiny one reads the status back)
+        big = [i for i, (kname, d) in disp.items()
+               if "copy" in kname.lower() and "dsw::" not in kname and sum(d.values()) > 10_000]
+        if big:
+            cp.update(disp[max(big)][1])
+    if len(walk_names) != 1 or not cp:
+        raise SystemExit(f"expected one walk kernel and the calibration copy, found {sorted(walk_names)}")
+    w = {c: sum(v) / len(v) for c, v in w_vals.items()}
+
+    def rd(m):
+        if not all(c in m for c in READ_COUNTERS):
+            return None
+        req, r32, r128 = (m[c] for c in READ_COUNTERS)
+        return r32 * 32 + r128 * 128 + (req - r32 - r128) * 64
+
+    def wr(m):
+        if not all(c in m for c in WRITE_COUNTERS):
+            return None
+        req, w64 = (m[c] for c in WRITE_COUNTERS)
+        return w64 * 64 + (req - w64) * 32
+
+    rec = {"kernel": walk_names.pop(), "workload": workload_name, "B": B, "gamma": gamma, "cold": bool(cold),
+           "kernel_source_hash": kernel_source_hash(), "dispatches": {c: len(v) for c, v in w_vals.items()},
+           "walk_counters_per_dispatch": {c: round(v, 1) for c, v in sorted(w.items())},
+           "copy_bytes": COPY_BYTES,
+           "copy_counters": {c: round(v, 1) for c, v in sorted(cp.items())},
+           "algorithmic_bytes_per_launch": algorithmic_bytes(V, B, gamma)}
+    total = 0.0
+    for name, f in (("read", rd), ("write", wr)):
+        raw, ref = f(w), f(cp)
+        if raw is None or not ref:
+            rec[name + "_bytes_per_launch"] = None
+            continue
+        scale = COPY_BYTES / ref
+        rec[name + "_bytes_raw"] = round(raw)
+        rec[name + "_scale"] = round(scale, 4)
+        rec[name + "_bytes_per_launch"] = round(raw * scale)
+        total += raw * scale
+    if rec["read_bytes_per_launch"] is not None and rec["write_bytes_per_launch"] is not None:
+        rec["hbm_bytes_per_launch"] = round(total)
+    path = os.path.join(dest_dir, f"counters_{workload_name}_b{B}_g{gamma}{'_cold' if cold else ''}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -448,12 +526,23 @@ def main():
                     help="only the recurrent heads' configurations of the sweep (for profiling)")
     ap.add_argument("--stepwise-only", action="store_true",
                     help="for counter runs: only the step-wise library-op loop, then the same copy")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write the counter record of --workload/--B/--gamma (cold with --pmc-cold) "
+                         "from the rocprofv3 --pmc CSV output under DIR; no GPU")
     ap.add_argument("--grid-sweep", action="store_true",
                     help="only the rendezvous cost against the number of workgroups (8 .. 256)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the walk runs on one GPU; --gpus must be 1 (the multi-GPU split is a design, not built)"}))
         sys.exit(2)
+
+    if args.summarize_counters:
+        import workloads
+        wl = workloads.WORKLOADS[args.workload]
+        B = args.B if args.B is not None else wl.batches[0]
+        gamma = args.gamma if args.gamma is not None else wl.gamma
+        print(json.dumps(summarize_counters(args.summarize_counters, wl.name, wl.V, B, gamma, args.pmc_cold)))
+        return
 
     import torch
 
@@ -507,12 +596,19 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def flusher(torch, dev):
-    """A write of 1 GiB that evicts L2 and the 256 MB Infinity Cache."""
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+def flusher(torch, dev, write=False):
+    """Evicts L2 and the 256 MB Infinity Cache before a launch: a read of
+    1 GiB (a sum over it), which leaves the caches holding clean lines of
+    another buffer.  write=True zeroes the 1 GiB instead, which also evicts
+    them but leaves up to the caches' size in dirty lines whose write-back
+    the next launch pays for."""
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     def flush():
-        scratch.zero_()
+        if write:
+            scratch.zero_()
+        else:
+            scratch.sum()
     return flush
 
 
@@ -603,6 +699,11 @@ def headline(args, torch, dsw, wl, walker, W1d, W2d, dev_rounds, B, gamma, V, n_
                                "cold_traffic": recorded_traffic(wl.name, B, gamma, cold=True)})
     result["cold_frac_of_stepwise_bound"] = round(cold_med / stepwise_bound, 4)
     log("cold", result["cold_us_per_round"])
+    wflush = flusher(torch, dev, write=True)
+    _, cold_w = time_walk(torch, walker, W1d, W2d, dev_rounds, min(kc, 40), 2, flush=wflush)
+    result["cold_after_write_flush_us"] = round(statistics.median(cold_w), 3)
+    log("cold after a write flush", result["cold_after_write_flush_us"])
+    del wflush
     if B == 1 and V == 151_936 and not args.no_sweep:
         result["cold_gamma_sweep"] = cold_gamma_sweep(torch, dsw, W1d, W2d, V, flush)
         log("cold gamma sweep", result["cold_gamma_sweep"])

@@ -187,6 +187,11 @@ typedef struct dsw_plan_info {
     int w2_dtype;            /* DSW_BF16 or DSW_INT8 (int8: MFMA engine only)    */
     int ring_slots;          /* batched kernel: LDS ring slots (groups in flight) */
     int rows_pad;            /* batched kernel: shard rows padded to 128          */
+    int prefetch_tiles;      /* MFMA, one bf16 request: streamed tiles per wave
+                                whose rows for the next step are loaded into LDS
+                                while the step's keys are exchanged ("Keeping
+                                the Draft Walk on Chip", section "V = 248,320:
+                                62% on chip, the rest streamed")                */
 } dsw_plan_info;
 
 typedef struct dsw_handle* dsw_handle_t;

@@ -78,7 +78,7 @@ class PlanInfo(ctypes.Structure):
                 ("reg_tiles", ctypes.c_int), ("lds_tiles", ctypes.c_int),
                 ("max_tiles", ctypes.c_int), ("static_lds_bytes", ctypes.c_int),
                 ("w2_dtype", ctypes.c_int), ("ring_slots", ctypes.c_int),
-                ("rows_pad", ctypes.c_int)]
+                ("rows_pad", ctypes.c_int), ("prefetch_tiles", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -226,10 +226,12 @@ class Walker:
     def __exit__(self, *exc):
         self.close()
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # during interpreter shutdown the atexit hook has already closed every
-        # handle; never call into the runtime from a late finalizer
-        if sys.is_finalizing():
+        # handle; never call into the runtime from a late finalizer (the
+        # default argument keeps the check usable after module globals are
+        # cleared)
+        if _finalizing():
             return
         try:
             self.close()

@@ -354,6 +354,7 @@ int launch_walk(const LaunchCtx& x, const void* W1, const void* W2, const float*
     p.lds_rows = plan.lds_rows;
     p.tiles_per_wave = plan.tiles_per_wave;
     p.lds_tiles = plan.lds_tiles;
+    p.pf_tiles = plan.prefetch_tiles;
     p.rows_pad = plan.rows_pad;
     p.ring = plan.ring_slots;
     p.aligned = (x.V % 8) == 0;

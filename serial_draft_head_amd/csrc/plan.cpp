@@ -154,11 +154,22 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
             else stream_rows += n;
         }
 
+    // one bf16 request in the shape without register tiles: LDS left over
+    // takes the first streamed tiles of every wave one step ahead (their
+    // slots follow the 4 x LT slots of LDS tiles)
+    int PF = 0;
+    if (nb == 1 && !i8 && reg_t == 0 && stream_rows > 0) {  // the kernel has it only without register tiles
+        const int streamed = TW - reg_t - LT;
+        const int room = (avail - 4 * LT * tile_bytes) / (4 * tile_bytes);
+        PF = streamed < room ? streamed : room;
+        if (PF < 0) PF = 0;
+    }
     int lds_bytes = slots(LT) * tile_bytes;
     const int half = dev->lds_bytes_per_cu / 2 + 1024 - lds_static;  // one workgroup per CU
     if (lds_bytes < half) lds_bytes = half;
+    if (PF > 0 && lds_bytes < 4 * (LT + PF) * tile_bytes) lds_bytes = 4 * (LT + PF) * tile_bytes;
     if (lds_bytes > avail) lds_bytes = avail;
-    if (lds_bytes < slots(LT) * tile_bytes) return DSW_ERR_PLAN;
+    if (lds_bytes < slots(LT) * tile_bytes || lds_bytes < 4 * (LT + PF) * tile_bytes * (PF > 0)) return DSW_ERR_PLAN;
 
     out->engine = DSW_ENGINE_MFMA;
     out->path = stream_rows > 0 ? DSW_PATH_PARTIAL : DSW_PATH_RESIDENT;
@@ -176,6 +187,7 @@ static int plan_mfma(const dsw_devinfo* dev, int V, int B, unsigned flags, int g
     out->lds_tiles = LT;
     out->max_tiles = max_t;
     out->static_lds_bytes = lds_static;
+    out->prefetch_tiles = PF;
     return DSW_OK;
 }
 

@@ -1,5 +1,6 @@
 // walk_device.h -- device helpers shared by the walk kernels: bf16 rounding,
-// the selection key, device-coherent mailbox I/O and wave reductions.
+// the selection key, device-coherent mailbox I/O, wave reductions, and
+// loads from global memory straight into LDS.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -315,5 +316,55 @@ __device__ __forceinline__ uint32_t unord16(uint32_t ord) {
             p.trace[((size_t)c * (gamma + 1) + gamma) * 8] = s_trace[kTraceSteps][0];       \
         }                                                                                   \
     } while (0)
+
+// ------------------------------------------- vector-memory waits, LDS DMA
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt_vm_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
+
+// Wait until at most n vector-memory instructions of this wave are in flight.
+// No memory access moves across it (a load issued later must not be counted
+// as issued earlier).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    asm volatile("" ::: "memory");
+    switch (n < 0 ? 0 : (n > 31 ? 31 : n)) {
+#define DSW_W(i) \
+    case i: __builtin_amdgcn_s_waitcnt(waitcnt_vm_imm(i)); break;
+        DSW_W(0) DSW_W(1) DSW_W(2) DSW_W(3) DSW_W(4) DSW_W(5) DSW_W(6) DSW_W(7)
+        DSW_W(8) DSW_W(9) DSW_W(10) DSW_W(11) DSW_W(12) DSW_W(13) DSW_W(14) DSW_W(15)
+        DSW_W(16) DSW_W(17) DSW_W(18) DSW_W(19) DSW_W(20) DSW_W(21) DSW_W(22) DSW_W(23)
+        DSW_W(24) DSW_W(25) DSW_W(26) DSW_W(27) DSW_W(28) DSW_W(29) DSW_W(30) DSW_W(31)
+#undef DSW_W
+        default: break;
+    }
+}
+
+// Workgroup barrier that keeps vector-memory loads (and LDS DMA) in flight:
+// this wave's LDS accesses are complete, and the compiler moves no memory
+// access across it.  (__syncthreads would also wait for every outstanding
+// load, which would drain the prefetch ring at every group.)
+__device__ __forceinline__ void barrier_keep_vm() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes from global memory straight into LDS: this lane's data lands at
+// lds_base + 16 * lane (lds_base is wave-uniform).  Written as inline assembly
+// so that the compiler does not treat every later LDS access as waiting on
+// it (it would drain the whole ring at each group); the kernel waits for
+// these loads itself with wait_vmcnt.  M0 needs one wait state before use.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
 
 }  // namespace dsw

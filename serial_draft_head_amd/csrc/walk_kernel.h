@@ -251,6 +251,14 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // MFMA layout
     const int TW = kMfma ? p.tiles_per_wave : 0;
     const int LT = kMfma ? p.lds_tiles : 0;
+    // one bf16 request, no register tiles (the shape that streams): streamed
+    // tiles LT .. LT + PF - 1 of this wave come from LDS slots after the LDS
+    // tiles', filled one step ahead while the previous step's keys travel
+    // ("Keeping the Draft Walk on Chip", section "V = 248,320: 62% on chip,
+    // the rest streamed": the ring keeps refilling across steps).  Only in
+    // that shape is LDS left over; elsewhere the code would cost registers.
+    constexpr bool kPf = kMfma && kOne && !kI8 && A == 0;
+    const int PF = kPf ? p.pf_tiles : 0;
     const int wrow0 = wave * TW * kTileRows;
     const int nt_w = kMfma ? max(0, min(TW, (nrows - wrow0 + kTileRows - 1) / kTileRows)) : 0;
 
@@ -600,6 +608,21 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     // the workgroups reach the first rendezvous in a scrambled order (a hook
     // inside the step loop measurably slowed every step, even when off)
     walk_skew(p, c, 0, 0);
+    // this wave's prefetched tiles for the next step, straight into its LDS
+    // slots (wave-local: the same wave reads them after its next gather);
+    // rows past the shard load its last row, whose results are dropped
+    auto prefetch_streamed = [&]() {
+        if constexpr (kPf) {
+            for (int i = 0; i < PF; ++i) {
+                const int row = min(v0 + wrow0 + (A + LT + i) * kTileRows + n, last_row);
+                const uint4* src = reinterpret_cast<const uint4*>(p.W2) + (size_t)row * kRowChunks;
+                const uint32_t dst = lds_addr(s_w + (size_t)(4 * LT + wave * PF + i) * 512);
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) dma16(src + DSW_KC(kb, g), dst + kb * 64 * 16);
+            }
+        }
+    };
+    prefetch_streamed();
     const unsigned round = s_round;
     const unsigned fam = s_fam;
     bool any_samp = false;
@@ -754,6 +777,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             const int prev = (k == 0) ? s_anchor[b] : DSW_TOKEN(b);
             s_u[b * US + ch] = W1[(size_t)prev * kRowChunks + ch];
         }
+        if (PF > 0) wait_vmcnt(0);  // the prefetched tiles are in LDS (issued a step ago)
         __syncthreads();
         if constexpr (kGated) {
             // ---- the gated update, one state element per thread ---------------
@@ -863,6 +887,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                         } else if (j < M && j < nt_w) {
                             if (j - A < LT) {
                                 const int sb = (wave * LT + (j - A)) * 512 + lane;
+#pragma unroll
+                                for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
+                            } else if (j - A - LT < PF) {
+                                const int sb = (4 * LT + wave * PF + (j - A - LT)) * 512 + lane;
 #pragma unroll
                                 for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
                             } else {
@@ -1188,6 +1216,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             }
         }
         DSW_TRACE(k, kTrPosted);
+        if (k + 1 < gamma) prefetch_streamed();  // the next step's, while the keys travel
         // the previous step's tokens, stored while this step's rendezvous is in
         // flight (a store at the end of a step would hold up the next gather)
         if (c == 0 && k > 0 && t < B) p.tokens[(size_t)t * gamma + k - 1] = DSW_TOKEN(t);
@@ -1431,6 +1460,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         DSW_TRACE(k, kTrSelected);
         DSW_TRACE_REAL(k);
     }
+    if (PF > 0) wait_vmcnt(0);  // no LDS load may land after the workgroup ends
     if (c == 0 && t < B && !s_abort && gamma > 0) p.tokens[(size_t)t * gamma + gamma - 1] = DSW_TOKEN(t);
 #undef DSW_TOKEN
 #undef DSW_ONE_ROW_OK

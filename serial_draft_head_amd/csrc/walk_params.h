@@ -122,6 +122,8 @@ struct WalkParams {
     int lds_rows;            // rows per workgroup resident in LDS (after the register slots)
     int tiles_per_wave;      // MFMA engine: 16-row tiles per wave (contiguous rows)
     int lds_tiles;           // MFMA engine: tiles per wave held in LDS after the VGPR tiles
+    int pf_tiles;            // MFMA engine, one bf16 request: streamed tiles per wave loaded
+                             // into LDS one step ahead (after the LDS tiles' slots)
     int rows_pad;            // batched kernel: shard rows rounded up to a multiple of 128
     int ring;                // batched kernel: LDS slots for u rows and base logits of groups
     int aligned;             // batched kernel: V % 8 == 0 (16-byte aligned base rows)

@@ -127,6 +127,32 @@ def shards_cover(V, grid, R):
     return covered == V
 
 
+def test_planner_follows_a_reduced_grid(dsw):
+    """dsw_set_grid hands the planner a device with fewer CUs: shards grow to
+    ceil(V / grid) rows, up to what one workgroup holds."""
+    for G in (8, 37, 255):
+        for B, flags, gamma in ((1, 0, 16), (1, 4, 7), (3, 0, 7), (20, 0, 16)):
+            p = dsw.plan(fake_device(dsw, cus=G), 6_007, gamma, B, flags=flags).as_dict()
+            assert p["grid"] == G and p["rows_per_wg"] >= -(-6_007 // G)
+    with pytest.raises(dsw.DswError):   # 1,025 rows: more than a workgroup takes
+        dsw.plan(fake_device(dsw, cus=8), 8_193, 7, 1)
+
+
+def test_planner_prefetches_streamed_tiles_only_where_lds_is_left(dsw):
+    """The cross-step prefetch of streamed tiles: one bf16 request with
+    nothing resident gets LDS slots for the first streamed tiles of each
+    wave; resident shards, several requests and int8 rows get none."""
+    dev = fake_device(dsw)
+    for V in (60_000, 151_936, 248_320):
+        p = dsw.plan(dev, V, 7, 1, flags=1).as_dict()  # DSW_FLAG_FORCE_STREAM
+        assert p["reg_tiles"] == 0 and p["lds_tiles"] == 0 and p["stream_rows"] == p["rows_per_wg"]
+        assert 0 < p["prefetch_tiles"] <= p["tiles_per_wave"]
+        assert 4 * p["prefetch_tiles"] * 8192 <= p["lds_bytes"] <= dev.max_lds_per_block - p["static_lds_bytes"]
+        assert dsw.plan(dev, V, 7, 1).as_dict()["prefetch_tiles"] == 0            # resident
+        assert dsw.plan(dev, V, 7, 4, flags=1).as_dict()["prefetch_tiles"] == 0   # four requests
+        assert dsw.plan(dev, V, 7, 1, w2_dtype=1, flags=1).as_dict()["prefetch_tiles"] == 0  # int8
+
+
 ENGINES = {"mfma": 8, "valu": 4, "batched": 16}   # flags forcing each kernel / engine
 
 

@@ -7,7 +7,8 @@
   the error is latched leaves its outputs untouched, and after dsw_status the
   next walk is correct again;
 * scrambled arrival order: every workgroup sleeps a pseudo-random time
-  before each post, and the walk must give the same bits as without;
+  before it posts, and the walk must give the same bits as without;
+* fewer workgroups than CUs (larger shards, fewer in each rendezvous);
 * the Gumbel-max variate the kernels compute, against binary64 for every
   uniform their noise can take (the basis of the Gumbel-max tolerance).
 
@@ -153,6 +154,28 @@ def test_scrambled_arrival_order_gives_the_same_bits(dsw, name, B, flags, gamma_
         walker.set_debug(skew=1)
         t1, l1 = _walk_and_check(dsw, name, walker, w, W1, W1d, W2d, inp)
         assert np.array_equal(t0, t1) and np.array_equal(l0, l1)
+    walker.close()
+
+
+@pytest.mark.parametrize("name,B,flags,gamma_max", FAMILIES[:4])
+@pytest.mark.parametrize("grid", [8, 37, 255])
+def test_fewer_workgroups(dsw, name, B, flags, gamma_max, grid):
+    """dsw_set_grid: the walk over fewer workgroups than CUs, so that each
+    owns a larger shard (V = 6,007: 751 rows each over 8) and fewer take
+    part in every rendezvous, against the oracle."""
+    Vg = 6_007
+    gh.say(f"{name} B={B}: grid {grid}")
+    W1, W2 = workloads.weights(2, V=Vg)
+    w = parity.Weights(W1, W2)
+    W1d, W2d = gh.bf16_dev(torch, W1), gh.bf16_dev(torch, W2)
+    walker = dsw.Walker(Vg, gamma_max=gamma_max, B_max=B, flags=flags)
+    walker.set_grid(grid)
+    plan = walker.query_plan(B).as_dict()
+    gh.say("plan", plan)
+    assert plan["grid"] == grid
+    for r in range(2):
+        inp = workloads.round_inputs(2, 5300 + r, B=B, gamma=min(gamma_max, 7), V=Vg, temps="mixed")
+        _walk_and_check(dsw, name, walker, w, W1, W1d, W2d, inp)
     walker.close()
 
 

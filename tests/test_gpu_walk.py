@@ -149,6 +149,32 @@ def test_force_stream_is_bit_identical_to_resident(dsw, engine):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("V", [60_000, 151_936, 248_320])
+def test_streamed_prefetch_one_request(dsw, V):
+    """One request with nothing on chip: the first streamed tiles of every
+    wave are loaded into LDS one step ahead, the rest streamed in the step.
+    Tokens and logits are the resident walk's, bit for bit, greedy and
+    sampled, and the oracle's."""
+    say(f"one request, W2 streamed with the cross-step prefetch, V={V}")
+    W1, W2 = workloads.weights(1, V=V)
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    res = dsw.Walker(V, gamma_max=7, B_max=1)
+    st = dsw.Walker(V, gamma_max=7, B_max=1, flags=dsw.FLAG_FORCE_STREAM)
+    plan = st.query_plan(1)
+    say("plan", plan.as_dict())
+    assert plan.stream_rows == plan.rows_per_wg and 0 < plan.prefetch_tiles <= plan.tiles_per_wave
+    w = parity.Weights(W1, W2)
+    for r, temps in enumerate(("greedy", "cycle", "cycle")):
+        inp = workloads.round_inputs(1, 60 + r, B=1, gamma=7, V=V, temps=temps)
+        a = run(res, W1d, W2d, inp, want_logits=True)
+        b = run(st, W1d, W2d, inp, want_logits=True)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], b[0], b[1])
+        say(rep)
+    res.close()
+    st.close()
+
+
 def test_outputs_outside_the_request_untouched(dsw):
     V, B, gamma = 9_999, 3, 5
     say("sentinels around tokens and logits")
