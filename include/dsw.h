@@ -222,9 +222,10 @@ int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int
  * and zeroes the device workspace (per-workgroup mailboxes for both step
  * parities, per-kernel-family launch counters that select the step epochs, a
  * round counter and a status word), and, when the handle can run the batched
- * kernel (B_max >= 4 or DSW_FLAG_BATCHED), B_max * V * 2 bytes where that
- * kernel keeps the current step's logits of its sampled requests for the shard
- * that draws their token; the handle owns both.  It also checks, with the
+ * kernel (B_max >= 4 or DSW_FLAG_BATCHED), about B_max * (V + 16384) * 2
+ * bytes (B_max rounded up to 16) where that kernel keeps the current step's
+ * logits of its sampled requests for the shard that draws their token; the
+ * handle owns both.  It also checks, with the
  * occupancy API, that every kernel the handle can run fits one workgroup per
  * CU (DSW_ERR_LAUNCH otherwise).  The calling thread's current device is left
  * unchanged. */
@@ -446,8 +447,9 @@ int dsw_destroy(dsw_handle_t h);
  *             sampled requests need `uniforms`)
  *   the tensors, B (0 .. 256), gamma (0 .. 256) and stream   as dsw_walk
  * Errors as dsw_walk, and DSW_ERR_SCRATCH when the planner picks the batched
- * kernel (4 or more requests by default), logits is NULL and B * V * 2
- * exceeds 32 MiB (pass logits, or split the batch).  Every call on a GPU
+ * kernel (4 or more requests by default), logits is NULL and
+ * ceil(B / 16) * 16 * (V + 16384) * 2 bytes exceed 32 MiB (pass logits, or
+ * split the batch).  Every call on a GPU
  * shares that GPU's array and leaves its contents for the next (no clearing
  * is needed between calls): calls that overlap on one GPU race, so issue
  * them one at a time per GPU.  The first call on a device (or

@@ -196,10 +196,10 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
     h->ws.bext = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bext);
     // the batched kernel keeps the current step's logits of its sampled
-    // requests here for the token shards (B_max * V * 2 bytes)
+    // requests here for the token shards
     h->blog_mem = nullptr;
     if (B_max >= dsw::kBatchedFrom || (flags & DSW_FLAG_BATCHED)) {
-        if (hipMalloc(&h->blog_mem, (size_t)B_max * (size_t)V * 2) != hipSuccess) {
+        if (hipMalloc(&h->blog_mem, dsw::batched_logits_bytes(V, B_max)) != hipSuccess) {
             (void)hipFree(h->ws_mem);
             delete h;
             return DSW_ERR_HIP;

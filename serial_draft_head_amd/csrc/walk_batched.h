@@ -351,9 +351,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 // Branch-free, so that the matrix cores' work and this VALU work can be
 // interleaved; a tile beyond this wave's rows has -inf base logits and its
 // logits lose every max.  bw: the tile's four base logits.  STORE (a
-// constant): the logits go back into the slot over the base logits (the
-// sampled requests' exp-sum pass reads them there) and out to `lout`, with one
-// 8-byte store per lane where the vocabulary allows.
+// constant): the logits go out -- to the caller's `lout` (one 8-byte store
+// per lane where the vocabulary allows), else to this group's private block
+// `lpriv` (the wave's 64 lanes write 512 contiguous bytes) -- and the lane's
+// running exp-sum of them, relative to its running maximum, is updated
+// (sampled lanes: sc > 0; it is rescaled when the maximum grows).
 #define DSW_EPI(dv, j, bw, STORE)                                                                \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
@@ -376,20 +378,31 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }                                                                                        \
         const uint32_t q01_ = pack_bf16_rne(bf16_lo(bw_.x) + x0_, bf16_hi(bw_.x) + x1_);         \
         const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
+        const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
         if (STORE) {                                                                             \
-            *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                           \
-            const int lim_ = live_ ? nrows - rb_ : 0;                                            \
-            if (lout != nullptr && lim_ > 0) {                                                   \
-                if (al4 && lim_ >= 4) {                                                          \
-                    *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);              \
-                } else {                                                                         \
-                    const uint32_t l4_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16}; \
-                    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                              \
-                        if (i_ < lim_) lout[rb_ + i_] = (uint16_t)l4_[i_];                        \
+            if (lpriv != nullptr) {                                                              \
+                if (live_) lpriv[(j) * 64] = make_uint2(q01_, q23_);                             \
+            } else {                                                                             \
+                const int lim_ = live_ ? nrows - rb_ : 0;                                        \
+                if (lout != nullptr && lim_ > 0) {                                               \
+                    if (al4 && lim_ >= 4) {                                                      \
+                        *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);          \
+                    } else {                                                                     \
+                        const uint32_t l4_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16}; \
+                        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                          \
+                            if (i_ < lim_) lout[rb_ + i_] = (uint16_t)l4_[i_];                    \
+                    }                                                                            \
                 }                                                                                \
             }                                                                                    \
+            const float mn_ = fmaxf(mrun, tm_);                                                  \
+            const float rf_ = mn_ == -__builtin_inff() ? 0.0f : mn_;                             \
+            srun = srun * __builtin_amdgcn_exp2f((mrun - rf_) * sc) +                            \
+                   ((__builtin_amdgcn_exp2f((bf16_lo(q01_) - rf_) * sc) +                         \
+                     __builtin_amdgcn_exp2f((bf16_hi(q01_) - rf_) * sc)) +                        \
+                    (__builtin_amdgcn_exp2f((bf16_lo(q23_) - rf_) * sc) +                         \
+                     __builtin_amdgcn_exp2f((bf16_hi(q23_) - rf_) * sc)));                        \
+            mrun = mn_;                                                                          \
         }                                                                                        \
-        const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
         const bool gt_ = tm_ > bestv;                                                            \
         bestv = gt_ ? tm_ : bestv;                                                               \
         bestj = gt_ ? (j) : bestj;                                                               \
@@ -399,14 +412,21 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #define DSW_EPI_G(dv, j, bw) DSW_EPI(dv, j, bw, 0)
 #define DSW_EPI_GS(dv, j, bw) DSW_EPI(dv, j, bw, 1)
             // Logits go out straight from the epilogue: to `logits` when asked
-            // for, and for sampled requests in any case (to the workspace
-            // otherwise), where the token shard reads them back.  A group with
-            // nothing to store runs the epilogue without the stores (their
-            // branches cost a greedy batch ~12% even when no lane stores).
+            // for, and for sampled requests in any case (to the workspace's
+            // private blocks otherwise), where the token shard reads them back.
+            // A group with nothing to store runs the epilogue without the
+            // stores and without exp-sums (their branches cost a greedy batch
+            // ~12% even when no lane stores).
+            const bool samp = bval && s_T[b] > 0.0f;
+            const float sc = samp ? kLog2e / s_T[b] : 0.0f;
             uint16_t* lout = nullptr;
-            if (bval && (p.logits != nullptr || s_T[b] > 0.0f))
-                lout = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V : p.ws.blog + (size_t)b * V) + v0;
-            if (__builtin_amdgcn_ballot_w64(lout != nullptr) != 0ull) {
+            if (bval && p.logits != nullptr) lout = p.logits + ((size_t)b * gamma + k) * V + v0;
+            uint2* lpriv = nullptr;
+            if (p.logits == nullptr)
+                lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
+            float mrun = -__builtin_inff(), srun = 0.0f;  // the lane's running maximum and exp-sum
+            const bool stored = __builtin_amdgcn_ballot_w64(lout != nullptr || samp) != 0ull;
+            if (stored) {
                 DSW_TILES(DSW_EPI_GS);
             } else {
                 DSW_TILES(DSW_EPI_G);
@@ -425,29 +445,12 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             if (g == 0 && bval) s_rkey[wave][b] = best;
             const float Tb = bval ? s_T[b] : 0.0f;
             const bool on = Tb > 0.0f && best != 0u;
-            if (any_samp && __builtin_amdgcn_ballot_w64(on) != 0ull) {
+            if (stored && __builtin_amdgcn_ballot_w64(on) != 0ull) {
                 // exp-sum of this wave's logits of request n relative to its
-                // maximum: every live tile's four logits are read first (all
-                // reads in flight), then the exps; rows past the vocabulary hold
-                // -inf (exp 0); lanes of greedy or empty columns drop theirs
+                // maximum: the four lanes' running sums, rescaled to it (a lane
+                // whose rows all lie past the vocabulary holds 0 at -inf)
                 const float mw = local_key_logit(best);
-                const float sc = on ? kLog2e / Tb : 0.0f;
-                float sw4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four independent sums
-                uint2 lw[M];
-#pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    const int rb = min(wrow0 + j * kTileRows + 4 * g, Rpad - 4);
-                    lw[j] = *reinterpret_cast<const uint2*>(sb + (n * CPR + ((rb >> 3) ^ n)) * 8 + (rb & 7));
-                }
-#pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    if (j < nt_w) {  // wave-uniform
-                        const float lv[4] = {bf16_lo(lw[j].x), bf16_hi(lw[j].x), bf16_lo(lw[j].y), bf16_hi(lw[j].y)};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sw4[i] += __builtin_amdgcn_exp2f((lv[i] - mw) * sc);
-                    }
-                }
-                float sw = on ? (sw4[0] + sw4[1]) + (sw4[2] + sw4[3]) : 0.0f;
+                float sw = on ? srun * __builtin_amdgcn_exp2f((mrun - mw) * sc) : 0.0f;
                 sw += __shfl_xor(sw, 16);
                 sw += __shfl_xor(sw, 32);
                 if (g == 0 && bval) {
@@ -619,13 +622,30 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const float sc2 = kLog2e / s_T[b];
                 // this shard's logits of request b, requested before the owner's
                 // words are polled (both round trips overlap)
-                const uint16_t* lrow = (p.logits != nullptr ? p.logits + ((size_t)b * gamma + k) * V
-                                                            : p.ws.blog + (size_t)b * V) + v0;
                 uint32_t lb[RLMAX];
+                if (p.logits != nullptr) {
+                    const uint16_t* lrow = p.logits + ((size_t)b * gamma + k) * V + v0;
 #pragma unroll
-                for (int rr = 0; rr < RLMAX; ++rr) {
-                    const int r = lane * RL + rr;
-                    lb[rr] = (rr < RL && r < nrows) ? (uint32_t)lrow[r] : 0u;
+                    for (int rr = 0; rr < RLMAX; ++rr) {
+                        const int r = lane * RL + rr;
+                        lb[rr] = (rr < RL && r < nrows) ? (uint32_t)lrow[r] : 0u;
+                    }
+                } else {
+                    // row r of the shard: wave r / (16 TW), tile j, lane 16 g + n
+                    // of that block, logit (r % 4) of the lane's four
+                    const uint2* lpb = reinterpret_cast<const uint2*>(p.ws.blog) +
+                                       ((size_t)c * NG + (b >> 4)) * 4 * TW * 64 + (b & 15);
+#pragma unroll
+                    for (int rr = 0; rr < RLMAX; ++rr) {
+                        const int r = lane * RL + rr;
+                        lb[rr] = 0u;
+                        if (rr < RL && r < nrows) {
+                            const int w = r / (TW * kTileRows), rem = r - w * TW * kTileRows;
+                            const uint2 v = lpb[(w * TW + (rem >> 4)) * 64 + ((rem >> 2) & 3) * 16];
+                            const uint32_t h = (rem & 2) ? v.y : v.x;
+                            lb[rr] = (rem & 1) ? (h >> 16) : (h & 0xFFFFu);
+                        }
+                    }
                 }
                 // the owner's prefix before this shard (lane 0) and u*Z (lane 1)
                 float ev = 0.0f;

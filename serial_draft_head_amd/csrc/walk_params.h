@@ -71,10 +71,14 @@ struct Workspace {
                                    // in the row of the shard that found it
     unsigned long long* bext;      // [2][kMaxBatch][2]  owner's prefix before the token
                                    // shard and u*Z, fp32 bits << 32 | epoch
-    uint16_t* blog;                // [B_max][V] batched kernel: this step's logits of the
-                                   // sampled requests (when the caller wants none written),
-                                   // read back by the token shards; NULL if the handle
-                                   // never runs the batched kernel
+    uint16_t* blog;                // batched kernel: this step's logits of the sampled
+                                   // requests (when the caller wants none written), read
+                                   // back by the token shards, batched_logits_bytes() long;
+                                   // NULL if the handle never runs the batched kernel.
+                                   // Per workgroup c, 16-request group, wave and tile j:
+                                   // 64 lanes x 4 bf16 (rows 4g .. 4g+3 of request n),
+                                   // [c][group][wave][j][lane], so that each store of the
+                                   // epilogue is one contiguous 512-byte block
 };
 
 // Status bits latched by the device (translated to DSW_ERR_DEV_* on the host).
@@ -100,6 +104,13 @@ inline WorkspaceLayout workspace_layout() {
     L.bext = o;      o = up(o + 2 * (size_t)kMaxBatch * 2 * 8);
     L.total = o;
     return L;
+}
+
+// Bytes of Workspace::blog for up to B_max requests over any grid: per
+// workgroup its 16-request groups x ceil(V / grid) rows rounded up to 64
+// (four waves of whole 16-row tiles) x 2 bytes.
+constexpr size_t batched_logits_bytes(int V, int B_max) {
+    return (size_t)((B_max + 15) / 16 * 16) * ((size_t)V + 64u * (size_t)kMaxGrid) * 2u;
 }
 
 struct WalkParams {

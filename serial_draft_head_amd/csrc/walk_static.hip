@@ -18,7 +18,7 @@
 namespace {
 
 constexpr size_t kWsBytes = 4u << 20;      // the workspace part (its layout needs about 3.2 MiB)
-constexpr size_t kBlogBytes = 32u << 20;   // the batched kernel's sampled logits: B * V * 2 bytes at most
+constexpr size_t kBlogBytes = 32u << 20;   // the batched kernel's sampled logits (batched_logits_bytes)
 constexpr size_t kScratchBytes = kWsBytes + kBlogBytes;
 constexpr int kMaxDevices = 64;
 constexpr int kStaticGammaMax = 256;       // the step count every call's epochs are spaced by
@@ -134,7 +134,7 @@ extern "C" int dsw_walk_static(int device, int V, int w2_dtype, unsigned flags, 
     if (rc) return rc;
     // the batched kernel keeps the sampled requests' logits of the current
     // step in the caller's logits, or else in the scratch array
-    if (plan.batch_tile == dsw::kMaxBatch && logits == nullptr && (size_t)B * (size_t)V * 2 > kBlogBytes)
+    if (plan.batch_tile == dsw::kMaxBatch && logits == nullptr && dsw::batched_logits_bytes(V, B) > kBlogBytes)
         return DSW_ERR_SCRATCH;
     dsw::LaunchCtx x;
     x.device = device;
