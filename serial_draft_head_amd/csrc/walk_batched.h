@@ -351,11 +351,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 // Branch-free, so that the matrix cores' work and this VALU work can be
 // interleaved; a tile beyond this wave's rows has -inf base logits and its
 // logits lose every max.  bw: the tile's four base logits.  STORE (a
-// constant): the logits go out -- to the caller's `lout` (one 8-byte store
-// per lane where the vocabulary allows), else to this group's private block
-// `lpriv` (the wave's 64 lanes write 512 contiguous bytes) -- and the lane's
-// running exp-sum of them, relative to its running maximum, is updated
-// (sampled lanes: sc > 0; it is rescaled when the maximum grows).
+// constant): the logits go out -- to this group's private block `lpriv` (the
+// wave's 64 lanes write 512 contiguous bytes), or, when the caller wants
+// them, back into the slot over the base logits (a tile beyond the wave's
+// rows rewrites s_junk's -inf), copied out row-contiguously after the tiles
+// -- and the lane's running exp-sum of them, relative to its running
+// maximum, is updated (sampled lanes: sc > 0; it is rescaled when the
+// maximum grows).
 #define DSW_EPI(dv, j, bw, STORE)                                                                \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
@@ -380,19 +382,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
         const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
         if (STORE) {                                                                             \
-            if (lpriv != nullptr) {                                                              \
+            /* wave-uniform branches only: no exec masks in the tiles */                        \
+            if (priv) {                                                                          \
                 if (live_) lpriv[(j) * 64] = make_uint2(q01_, q23_);                             \
             } else {                                                                             \
-                const int lim_ = live_ ? nrows - rb_ : 0;                                        \
-                if (lout != nullptr && lim_ > 0) {                                               \
-                    if (al4 && lim_ >= 4) {                                                      \
-                        *reinterpret_cast<uint2*>(lout + rb_) = make_uint2(q01_, q23_);          \
-                    } else {                                                                     \
-                        const uint32_t l4_[4] = {q01_ & 0xFFFFu, q01_ >> 16, q23_ & 0xFFFFu, q23_ >> 16}; \
-                        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                          \
-                            if (i_ < lim_) lout[rb_ + i_] = (uint16_t)l4_[i_];                    \
-                    }                                                                            \
-                }                                                                                \
+                *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);  /* staged for the caller's copy */   \
             }                                                                                    \
             const float mn_ = fmaxf(mrun, tm_);                                                  \
             const float rf_ = mn_ == -__builtin_inff() ? 0.0f : mn_;                             \
@@ -419,13 +413,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             // ~12% even when no lane stores).
             const bool samp = bval && s_T[b] > 0.0f;
             const float sc = samp ? kLog2e / s_T[b] : 0.0f;
-            uint16_t* lout = nullptr;
-            if (bval && p.logits != nullptr) lout = p.logits + ((size_t)b * gamma + k) * V + v0;
-            uint2* lpriv = nullptr;
-            if (p.logits == nullptr)
-                lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
+            const bool priv = p.logits == nullptr;  // the private blocks (wave-uniform)
+            uint2* lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
             float mrun = -__builtin_inff(), srun = 0.0f;  // the lane's running maximum and exp-sum
-            const bool stored = __builtin_amdgcn_ballot_w64(lout != nullptr || samp) != 0ull;
+            const bool stored = !priv || __builtin_amdgcn_ballot_w64(samp) != 0ull;
             if (stored) {
                 DSW_TILES(DSW_EPI_GS);
             } else {
@@ -443,6 +434,26 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             best = max(best, (uint32_t)__shfl_xor((int)best, 16));
             best = max(best, (uint32_t)__shfl_xor((int)best, 32));
             if (g == 0 && bval) s_rkey[wave][b] = best;
+            if (!priv) {
+                // the caller's logits of the group's requests over this wave's
+                // rows, from the slot: four consecutive rows per lane, so that
+                // the wave's stores to one request's row are contiguous
+                const int rend = min(wrow0 + nt_w * kTileRows, nrows);
+                for (int nn = 0; nn < kGroup && grp * kGroup + nn < B; ++nn) {
+                    uint16_t* dst = p.logits + ((size_t)(grp * kGroup + nn) * gamma + k) * V + v0;
+                    for (int r0 = wrow0 + 4 * lane; r0 < rend; r0 += 256) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(sb + (nn * CPR + ((r0 >> 3) ^ nn)) * 8 + (r0 & 7));
+                        if (al4 && r0 + 4 <= rend) {
+                            *reinterpret_cast<uint2*>(dst + r0) = v;
+                        } else {
+                            const uint32_t l4[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (r0 + i < rend) dst[r0 + i] = (uint16_t)l4[i];
+                        }
+                    }
+                }
+            }
             const float Tb = bval ? s_T[b] : 0.0f;
             const bool on = Tb > 0.0f && best != 0u;
             if (stored && __builtin_amdgcn_ballot_w64(on) != 0ull) {

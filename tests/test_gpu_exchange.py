@@ -39,10 +39,11 @@ def dsw():
 
 
 # (name, requests, flags, gamma_max): one-request MFMA, VALU, the all-to-all
-# MFMA kernel with a 4-request tile, the batched kernel, and the GRU head
-# (whose state gather is one more exchange per step)
+# MFMA kernel with a 4-request tile, the batched kernel with more requests
+# than one MFMA column block and with fewer, and the GRU head (whose state
+# gather is one more exchange per step)
 FAMILIES = [("mfma_b1", 1, 0, 16), ("valu_b1", 1, 4, 7), ("mfma_b4", 3, 0, 7), ("batched", 20, 0, 16),
-            ("gru", 1, 128, 5)]
+            ("batched_small", 12, 16, 16), ("gru", 1, 128, 5)]
 
 
 def _setup(dsw, B, flags, gamma_max):
@@ -157,7 +158,7 @@ def test_scrambled_arrival_order_gives_the_same_bits(dsw, name, B, flags, gamma_
     walker.close()
 
 
-@pytest.mark.parametrize("name,B,flags,gamma_max", FAMILIES[:4])
+@pytest.mark.parametrize("name,B,flags,gamma_max", [f for f in FAMILIES if f[0] != "gru"])
 @pytest.mark.parametrize("grid", [8, 37, 255])
 def test_fewer_workgroups(dsw, name, B, flags, gamma_max, grid):
     """dsw_set_grid: the walk over fewer workgroups than CUs, so that each
