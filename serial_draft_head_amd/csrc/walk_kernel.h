@@ -275,6 +275,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
         a_in = p.anchor[t];
         t_in = p.T[t];
     }
+    // one bf16 request (the Markov head, up to 10 register tiles per wave:
+    // wider shapes have no registers to spare): thread t < 32 fetches chunk t
+    // of the anchor's W1 row for the first step, and the first step's base
+    // logits, right after the shard's loads are issued, so that these round
+    // trips overlap the shard load instead of following it
+    constexpr bool kEarly = kMfma && kOne && !kI8 && !kCell && A <= 10;
+    int a_pre = 0;
+    if (kEarly && B > 0 && t < kRowChunks) a_pre = p.anchor[0];
+    uint4 u_pre = make_uint4(0u, 0u, 0u, 0u);
     // every word this workgroup posts in this launch, both parities, starts
     // at 0 (the barriers before the first post order these stores first)
     if (t < 2 * kMailWords)
@@ -457,6 +466,14 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[DSW_KC(kb, g)];
         }
+        if constexpr (kEarly) {
+            // an anchor out of range walks from row 0 (and is flagged below)
+            const int a0 = (a_pre >= 0 && a_pre < V) ? a_pre : 0;
+            if (B > 0 && t < kRowChunks) u_pre = W1[(size_t)a0 * kRowChunks + t];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                bq[q] = (B > 0 && DSW_ONE_ROW_OK(q)) ? (uint32_t)base[v0 + wrow0 + 64 * q + lane] : 0u;
+        }
         // pinned only once every tile's loads are in flight: a pin waits for
         // its registers, so pinning tile by tile would turn the shard load
         // into one memory round trip per tile
@@ -469,7 +486,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             }
     }
     if constexpr (kMfma) {
-        if constexpr (kOne) {
+        if constexpr (kOne && !kEarly) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
                 bq[q] = (B > 0 && DSW_ONE_ROW_OK(q)) ? (uint32_t)base[v0 + wrow0 + 64 * q + lane] : 0u;
@@ -772,10 +789,14 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
             }
         }
         // gather u = W1[prev] for every request
-        for (int j = t; j < B * kRowChunks; j += kBlock) {
-            const int b = j >> 5, ch = j & 31;
-            const int prev = (k == 0) ? s_anchor[b] : DSW_TOKEN(b);
-            s_u[b * US + ch] = W1[(size_t)prev * kRowChunks + ch];
+        if (kEarly && k == 0) {
+            if (t < B * kRowChunks) s_u[t] = u_pre;  // fetched at entry
+        } else {
+            for (int j = t; j < B * kRowChunks; j += kBlock) {
+                const int b = j >> 5, ch = j & 31;
+                const int prev = (k == 0) ? s_anchor[b] : DSW_TOKEN(b);
+                s_u[b * US + ch] = W1[(size_t)prev * kRowChunks + ch];
+            }
         }
         if (PF > 0) wait_vmcnt(0);  // the prefetched tiles are in LDS (issued a step ago)
         __syncthreads();
