@@ -85,26 +85,30 @@ def test_parity_small_and_ragged(dsw, V, B, gamma, temps, engine):
 
 
 def test_toy_workload_many_rounds(dsw):
-    """Back-to-back rounds on one handle: the parity state alternates, no memset."""
+    """1,000 rounds back to back on one handle (V = 32,000, gamma = 7, T cycling
+    0, 0.6, 1): the parity state alternates with no memset; each chunk of 100
+    rounds is launched without a host synchronisation, then every round is
+    checked against the oracle."""
     wl = workloads.WORKLOADS[0]
-    say("toy workload, 40 rounds back to back")
+    say("toy workload, 1,000 rounds back to back")
     W1, W2 = workloads.weights(0)
     w = parity.Weights(W1, W2)
     walker = dsw.Walker(wl.V, gamma_max=wl.gamma, B_max=1)
     W1d, W2d = bf16_dev(W1), bf16_dev(W2)
-    rounds = [workloads.round_inputs(0, r, B=1) for r in range(40)]
-    outs = []
-    for inp in rounds:
-        base, anchor, T, uni = round_dev(inp)
-        outs.append(walker.walk(W1d, W2d, base, anchor, T, uni, want_logits=True))
-    torch.cuda.synchronize()
-    assert walker.status() == 0
-    for r, (inp, (t, l)) in enumerate(zip(rounds, outs)):
-        lg = l.view(torch.int16).cpu().numpy().view(np.uint16)
-        rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"],
-                                 t.cpu().numpy(), lg)
-        if r % 10 == 0:
-            say("round", r, rep)
+    for chunk in range(10):
+        rounds = [workloads.round_inputs(0, 100 * chunk + r, B=1, temps="cycle") for r in range(100)]
+        outs = []
+        for inp in rounds:
+            base, anchor, T, uni = round_dev(inp)
+            outs.append(walker.walk(W1d, W2d, base, anchor, T, uni, want_logits=True))
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        for r, (inp, (t, l)) in enumerate(zip(rounds, outs)):
+            lg = l.view(torch.int16).cpu().numpy().view(np.uint16)
+            rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"],
+                                     t.cpu().numpy(), lg)
+        say("rounds", 100 * chunk, "..", 100 * chunk + 99, rep)
+    walker.close()
 
 
 def test_no_state_pollution_between_greedy_and_sampled(dsw):
@@ -434,8 +438,8 @@ def test_gumbel_max_needs_a_seed_and_a_small_batch(dsw):
 # device round counter) and device-drawn noise is keyed by that counter, so
 # each replay must be a correct walk with fresh noise.  Eager copies and
 # synchronisations run between the replays.
-@pytest.mark.parametrize("B,flags,temps", [(1, 0, "cycle"), (3, 64, "mixed"), (20, 0, "mixed")])
-def test_graph_replays_are_fresh_walks(dsw, B, flags, temps):
+@pytest.mark.parametrize("B,flags,temps,replays", [(1, 0, "cycle", 100), (3, 64, "mixed", 8), (20, 0, "mixed", 8)])
+def test_graph_replays_are_fresh_walks(dsw, B, flags, temps, replays):
     import oracle
     say(f"graph replays B={B} flags={flags} {temps}")
     V, gamma = 32_000, 4
@@ -457,7 +461,7 @@ def test_graph_replays_are_fresh_walks(dsw, B, flags, temps):
         walker.walk(W1d, W2d, base, anchor, T, None, tokens=tokens, logits=logits)
     torch.cuda.synchronize()
     seen = []
-    for r in range(4):
+    for r in range(replays):
         inp = workloads.round_inputs(2, 301 + r, B=B, gamma=gamma, V=V, temps=temps)
         nb, na, nt, _ = round_dev(inp)
         base.copy_(nb)
@@ -476,10 +480,11 @@ def test_graph_replays_are_fresh_walks(dsw, B, flags, temps):
         else:
             uni = oracle.device_uniforms(seed, ctr, B, gamma)
             rep = parity.check_round(w, inp["base"], inp["anchor"], inp["T"], uni, toks, lg)
-        say(r, "round counter", ctr, rep)
+        if r % 10 == 0:
+            say(r, "round counter", ctr, rep)
         assert walker.round_counter() == ctr + 1
         seen.append(ctr)
-    assert len(set(seen)) == 4
+    assert len(set(seen)) == replays
     del g
     walker.close()
 
