@@ -194,7 +194,6 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.bsum = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bsum);
     h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
     h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
-    h->ws.bext = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bext);
     // the batched kernel keeps the current step's logits of its sampled
     // requests here for the token shards
     h->blog_mem = nullptr;

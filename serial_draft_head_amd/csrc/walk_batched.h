@@ -89,6 +89,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const int wrow0 = wave * TW * kTileRows;
     const int nt_w = max(0, min(TW, (nrows - wrow0 + kTileRows - 1) / kTileRows));
     const int NG = (B + kGroup - 1) / kGroup;
+    // Owner words: request b's decision, prefix and u*Z words at 3 (b / G)
+    // in owner b % G's region of OS words.  Large batches: regions of whole
+    // lines, one writer each (253 requests: 335 -> 329 us, 64: 136 -> 131 us
+    // against one line shared by 16 owners).  Up to 16 requests, one per
+    // owner: regions of 3 words, so that a reader's B decision words sit in
+    // a few lines (16 requests: 255 -> 253 us against whole lines).
+    const int OS = (B <= kGroup && B <= G) ? 3 : owner_stride(G);
     const int D = p.ring;
     const bool aligned = p.aligned != 0;
     const bool al4 = (V & 3) == 0;  // 8-byte stores of 4 logits (rows 4g .. 4g+3)
@@ -127,12 +134,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         st_agent64(p.ws.bsum + o, 0ull);
         st_agent64(p.ws.btok + o, 0ull);
     }
-    for (int b = c + (t >> 1) * G; b < p.B_max; b += (kBlock >> 1) * G) {
-        const int par = t & 1;
-        st_agent64(p.ws.bdec + (size_t)par * kMaxBatch + b, 0ull);
-        st_agent64(p.ws.bext + ((size_t)par * kMaxBatch + b) * 2, 0ull);
-        st_agent64(p.ws.bext + ((size_t)par * kMaxBatch + b) * 2 + 1, 0ull);
-    }
+    for (int i = t; i < 2 * OS; i += kBlock)
+        st_agent64(p.ws.bdec + (size_t)(i / OS) * kOwnWords + (size_t)c * OS + i % OS, 0ull);
     __syncthreads();  // s_any_samp and s_junk set (LDS only: no wait for the loads above)
     DSW_TRACE(gamma, 0);
 
@@ -270,7 +273,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const int q = (int)(seq & 1u);
         unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch;
         unsigned long long* bsum = p.ws.bsum + (size_t)q * kMaxGrid * kMaxBatch;
-        unsigned long long* bdec = p.ws.bdec + (size_t)q * kMaxBatch;
+        // request b's decision word; its prefix and u*Z follow it
+        unsigned long long* bown = p.ws.bdec + (size_t)q * kOwnWords;
+#define DSW_OWN(b_) (bown + (size_t)((b_) % G) * OS + 3 * ((b_) / G))
         unsigned long long* btok = p.ws.btok + (size_t)q * kMaxGrid * kMaxBatch;  // [shard][request]
 
         // group gq's u rows and base logits into ring slot gq % D.  Each lane
@@ -577,18 +582,18 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 if (t == 0) {
                     const int tok = checked_token(key_index(win), V, status);
                     walk_skew(p, c, k, 1);
-                    st_agent64(&bdec[b], ((unsigned long long)(unsigned)tok << 28) | epoch);
+                    st_agent64(DSW_OWN(b), ((unsigned long long)(unsigned)tok << 28) | epoch);
                 }
             } else {
                 DSW_OWNER_SHARD(b, kw, sw, key_logit(win));
                 if (t == 0) {
                     walk_skew(p, c, k, 1);
-                    unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2;
+                    unsigned long long* ext = DSW_OWN(b) + 1;
                     st_agent64(&ext[0], ((unsigned long long)__float_as_uint(s_pex) << 32) | epoch);
                     st_agent64(&ext[1], ((unsigned long long)__float_as_uint(s_tgt) << 32) | epoch);
                     const unsigned d = kDecPending | ((unsigned)max(s_own, 0) << 21) |
                                        (uint32_t)((win >> kIdxBits) & 0xFFFFu);
-                    st_agent64(&bdec[b], ((unsigned long long)d << 28) | epoch);
+                    st_agent64(DSW_OWN(b), ((unsigned long long)d << 28) | epoch);
                 }
             }
             __syncthreads();
@@ -602,7 +607,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             unsigned it = 0;
             unsigned long long w = 0ull;
             bool ok = true;
-            while (((w = ld_agent64(&bdec[t])) & kEpochMod) != epoch) {
+            while (((w = ld_agent64(DSW_OWN(t))) & kEpochMod) != epoch) {
                 if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
                 if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
                 __builtin_amdgcn_s_sleep(1);
@@ -662,7 +667,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 float ev = 0.0f;
                 bool ok = true;
                 if (lane < 2) {
-                    const unsigned long long* ext = p.ws.bext + ((size_t)q * kMaxBatch + b) * 2 + lane;
+                    const unsigned long long* ext = DSW_OWN(b) + 1 + lane;
                     unsigned it = 0;
                     unsigned long long w = 0ull;
                     while (((w = ld_agent64(ext)) & kEpochMod) != epoch) {
@@ -737,6 +742,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         DSW_TRACE(k, kTrSelected);
         DSW_TRACE_REAL(k);
     }
+#undef DSW_OWN
 #undef DSW_ISSUE_GROUP
 #undef DSW_READ_COLUMN
 #undef DSW_OWNER_SHARD

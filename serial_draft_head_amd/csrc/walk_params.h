@@ -42,6 +42,17 @@ constexpr int kCellMaxPerWg = 4;   // recurrent heads: state elements per workgr
 constexpr int kDominoMaxGamma = 16;  // Domino's head: steps per round (its drafters' blocks)
 constexpr int kDominoMaxD = 4096;    // Domino's head: the drafter's hidden width, bound
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
+// Batched kernel: words of one owner workgroup's region (three per request it
+// owns, rounded up to whole 128-byte lines), and a bound on G * owner_stride(G)
+// over every grid of up to kMaxGrid workgroups.
+constexpr int owner_stride(int G) { return (3 * ((kMaxBatch + G - 1) / G) + 15) / 16 * 16; }
+constexpr int kOwnWords = 4096;
+constexpr int max_owner_words() {
+    int m = 0;
+    for (int G = 1; G <= kMaxGrid; ++G) m = G * owner_stride(G) > m ? G * owner_stride(G) : m;
+    return m;
+}
+static_assert(max_owner_words() <= kOwnWords, "owner regions of every grid fit kOwnWords");
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
 constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests
 constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // the 28-bit epoch field of a mailbox word
@@ -66,11 +77,14 @@ struct Workspace {
     // reads column b and publishes a decision; a token shard publishes tokens
     unsigned long long* bkey;      // [2][kMaxGrid][kMaxBatch]  key << 28 | epoch
     unsigned long long* bsum;      // [2][kMaxGrid][kMaxBatch]  exp-sum bits << 32 | epoch
-    unsigned long long* bdec;      // [2][kMaxBatch]  decision << 28 | epoch
+    unsigned long long* bdec;      // [2][kOwnWords]  per owner workgroup c, a region of
+                                   // owner_stride(G) words (whole 128-byte lines, one
+                                   // writer each; 3 words for up to 16 requests); request
+                                   // b = c + i G takes words 3i .. 3i + 2: decision << 28 |
+                                   // epoch, then the prefix before the token shard and u*Z,
+                                   // fp32 bits << 32 | epoch
     unsigned long long* btok;      // [2][kMaxGrid][kMaxBatch]  sampled token << 28 | epoch,
                                    // in the row of the shard that found it
-    unsigned long long* bext;      // [2][kMaxBatch][2]  owner's prefix before the token
-                                   // shard and u*Z, fp32 bits << 32 | epoch
     uint16_t* blog;                // batched kernel: this step's logits of the sampled
                                    // requests (when the caller wants none written), read
                                    // back by the token shards, batched_logits_bytes() long;
@@ -88,7 +102,7 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, tokw, ctl, bkey, bsum, bdec, btok, bext, total;
+    size_t mail, tokw, ctl, bkey, bsum, bdec, btok, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -99,9 +113,8 @@ inline WorkspaceLayout workspace_layout() {
     L.ctl = o;       o = up(o + 16);
     L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.bsum = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
-    L.bdec = o;      o = up(o + 2 * (size_t)kMaxBatch * 8);
+    L.bdec = o;      o = up(o + 2 * (size_t)kOwnWords * 8);
     L.btok = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
-    L.bext = o;      o = up(o + 2 * (size_t)kMaxBatch * 2 * 8);
     L.total = o;
     return L;
 }
@@ -112,6 +125,7 @@ inline WorkspaceLayout workspace_layout() {
 constexpr size_t batched_logits_bytes(int V, int B_max) {
     return (size_t)((B_max + 15) / 16 * 16) * ((size_t)V + 64u * (size_t)kMaxGrid) * 2u;
 }
+
 
 struct WalkParams {
     const uint16_t* W1;

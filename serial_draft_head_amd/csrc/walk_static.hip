@@ -102,7 +102,6 @@ dsw::Workspace workspace_at(unsigned char* base) {
     ws.bsum = reinterpret_cast<unsigned long long*>(base + L.bsum);
     ws.bdec = reinterpret_cast<unsigned long long*>(base + L.bdec);
     ws.btok = reinterpret_cast<unsigned long long*>(base + L.btok);
-    ws.bext = reinterpret_cast<unsigned long long*>(base + L.bext);
     ws.blog = reinterpret_cast<uint16_t*>(base + kWsBytes);
     return ws;
 }
