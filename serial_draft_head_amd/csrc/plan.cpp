@@ -75,7 +75,7 @@ static int cell_lds(unsigned flags) {
 }
 static int mfma_static_lds(int nb, int max_tiles, bool i8, bool gum, unsigned flags) {
     const int rpad = max_tiles * 4 * kTileRows;
-    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + (i8 ? 4 * rpad : 0) +
+    return nb * ((kRowChunks + 1) * 16 + 4 * rpad + 2 * 4 * kBlock + 144) + 1048 + 96 + 128 + (i8 ? 4 * rpad : 0) +
            kTraceLds + gumbel_noise_lds(nb, rpad, gum) + cell_lds(flags);
 }
 

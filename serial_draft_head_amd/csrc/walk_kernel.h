@@ -221,6 +221,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     __shared__ unsigned s_fam;
     __shared__ int s_abort;
     DSW_TRACE_DECL;
+    // one request, up to 10 register tiles: the branch-free epilogue's logits
+    // of lanes past the shard
+    __shared__ uint16_t s_lj[kMfma && kOne && A <= 10 ? 64 : 1];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -890,48 +893,98 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) a[kb] = (n < B) ? s_u[n * US + DSW_KC(kb, g)] : make_uint4(0u, 0u, 0u, 0u);
           if constexpr (kOne) {
-            // Groups of four tiles: four independent MFMA chains, gathered into
-            // one register, then one 64-lane epilogue.  Register tiles are
-            // multiplied even beyond nt_w (they hold valid rows; results are
-            // masked), LDS and streamed tiles only where they exist.
+            if constexpr (A <= 10) {
+                // Groups of four tiles: four independent MFMA chains, gathered into
+                // one register, then one 64-lane epilogue.  Register tiles are
+                // multiplied even beyond nt_w (they hold valid rows; results are
+                // masked), LDS and streamed tiles only where they exist.  Up to 10
+                // register tiles per wave, groups that start with a register tile
+                // run without a branch, and every epilogue is branch-free, so that
+                // the scheduler can overlap one group's epilogue with the next
+                // group's MFMAs (the wider shapes have no registers for it).
 #pragma unroll
-            for (int gq = 0; gq < NQ; ++gq) {
-                if (4 * gq < nt_w) {
-                    f32x4_t d[4];
+                for (int gq = 0; gq < NQ; ++gq) {
+                    if (4 * gq < A || 4 * gq < nt_w) {
+                        f32x4_t d[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int j = 4 * gq + jj;
-                        d[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                        if (j < A) {
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int j = 4 * gq + jj;
+                            d[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                            if (j < A) {
 #pragma unroll
-                            for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], wr[j < A ? j : 0][kb], d[jj]);
-                        } else if (j < M && j < nt_w) {
-                            if (j - A < LT) {
-                                const int sb = (wave * LT + (j - A)) * 512 + lane;
+                                for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], wr[j < A ? j : 0][kb], d[jj]);
+                            } else if (j < M && j < nt_w) {
+                                if (j - A < LT) {
+                                    const int sb = (wave * LT + (j - A)) * 512 + lane;
 #pragma unroll
-                                for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
-                            } else if (j - A - LT < PF) {
-                                const int sb = (4 * LT + wave * PF + (j - A - LT)) * 512 + lane;
+                                    for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
+                                } else if (j - A - LT < PF) {
+                                    const int sb = (4 * LT + wave * PF + (j - A - LT)) * 512 + lane;
 #pragma unroll
-                                for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
-                            } else {
-                                const int r = wrow0 + j * kTileRows + n;
-                                const bool ok = r < nrows;
-                                const MT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
+                                    for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
+                                } else {
+                                    const int r = wrow0 + j * kTileRows + n;
+                                    const bool ok = r < nrows;
+                                    const MT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
 #pragma unroll
-                                for (int kb = 0; kb < 8; ++kb)
-                                    d[jj] = mfma_tile(a[kb], ok ? as_bf16x8(src[DSW_KC(kb, g)]) : make_uint4(0u, 0u, 0u, 0u),
-                                                      d[jj]);
+                                    for (int kb = 0; kb < 8; ++kb)
+                                        d[jj] = mfma_tile(a[kb], ok ? as_bf16x8(src[DSW_KC(kb, g)]) : make_uint4(0u, 0u, 0u, 0u),
+                                                          d[jj]);
+                                }
                             }
                         }
-                    }
-                    const float acc1 = combine4(d[0][0], d[1][0], d[2][0], d[3][0]);
-                    if (DSW_ONE_ROW_OK(gq)) {
+                        const float acc1 = combine4(d[0][0], d[1][0], d[2][0], d[3][0]);
+                        const bool ok = DSW_ONE_ROW_OK(gq);
                         const int r = wrow0 + 64 * gq + lane;
-                        const float bias = bias_round(kI8 ? s_scale[r] * acc1 : acc1, dbl_round);
+                        const float bias = bias_round(kI8 ? s_scale[ok ? r : 0] * acc1 : acc1, dbl_round);
                         const uint32_t lbits = f32_to_bf16(bf16_to_f32(bq[gq]) + bias);
-                        best[0] = max(best[0], local_key(lbits, r));
-                        s_logit[r] = (uint16_t)lbits;
+                        const uint32_t key = local_key(lbits, r);
+                        best[0] = ok ? max(best[0], key) : best[0];
+                        *(ok ? &s_logit[r] : &s_lj[lane]) = (uint16_t)lbits;  // lanes past the shard: junk
+                    }
+                }
+            } else {
+                // the same with a branch per group and per epilogue (12 register
+                // tiles per wave leave no registers for the straight-line form)
+#pragma unroll
+                for (int gq = 0; gq < NQ; ++gq) {
+                    if (4 * gq < nt_w) {
+                        f32x4_t d[4];
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int j = 4 * gq + jj;
+                            d[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                            if (j < A) {
+#pragma unroll
+                                for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], wr[j < A ? j : 0][kb], d[jj]);
+                            } else if (j < M && j < nt_w) {
+                                if (j - A < LT) {
+                                    const int sb = (wave * LT + (j - A)) * 512 + lane;
+#pragma unroll
+                                    for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
+                                } else if (j - A - LT < PF) {
+                                    const int sb = (4 * LT + wave * PF + (j - A - LT)) * 512 + lane;
+#pragma unroll
+                                    for (int kb = 0; kb < 8; ++kb) d[jj] = mfma_tile(a[kb], s_w[sb + kb * 64], d[jj]);
+                                } else {
+                                    const int r = wrow0 + j * kTileRows + n;
+                                    const bool ok = r < nrows;
+                                    const MT* src = W2 + (size_t)(v0 + (ok ? r : 0)) * kRowChunks;
+#pragma unroll
+                                    for (int kb = 0; kb < 8; ++kb)
+                                        d[jj] = mfma_tile(a[kb], ok ? as_bf16x8(src[DSW_KC(kb, g)]) : make_uint4(0u, 0u, 0u, 0u),
+                                                          d[jj]);
+                                }
+                            }
+                        }
+                        const float acc1 = combine4(d[0][0], d[1][0], d[2][0], d[3][0]);
+                        if (DSW_ONE_ROW_OK(gq)) {
+                            const int r = wrow0 + 64 * gq + lane;
+                            const float bias = bias_round(kI8 ? s_scale[r] * acc1 : acc1, dbl_round);
+                            const uint32_t lbits = f32_to_bf16(bf16_to_f32(bq[gq]) + bias);
+                            best[0] = max(best[0], local_key(lbits, r));
+                            s_logit[r] = (uint16_t)lbits;
+                        }
                     }
                 }
             }
