@@ -436,8 +436,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const int bestr = bestj >= 0 ? wrow0 + bestj * kTileRows + 4 * g + bi : -1;
             uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
             // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
-            best = max(best, (uint32_t)__shfl_xor((int)best, 16));
-            best = max(best, (uint32_t)__shfl_xor((int)best, 32));
+            best = column4_max_u32(best);
             if (g == 0 && bval) s_rkey[wave][b] = best;
             if (!priv) {
                 // the caller's logits of the group's requests over this wave's
@@ -467,8 +466,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 // whose rows all lie past the vocabulary holds 0 at -inf)
                 const float mw = local_key_logit(best);
                 float sw = on ? srun * __builtin_amdgcn_exp2f((mrun - mw) * sc) : 0.0f;
-                sw += __shfl_xor(sw, 16);
-                sw += __shfl_xor(sw, 32);
+                sw = column4_sum_f32(sw);
                 if (g == 0 && bval) {
                     s_rm[wave][b] = mw;
                     s_rs[wave][b] = sw;

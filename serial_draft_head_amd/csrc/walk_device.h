@@ -136,6 +136,23 @@ __device__ __forceinline__ int key_index(unsigned long long key) {
 }
 
 // ------------------------------------------------------- wave reductions
+// Over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one 16-lane column in each
+// row of 16): v_permlane16_swap of a value with itself leaves rows {0, 0, 2,
+// 2} in one result and {1, 1, 3, 3} in the other, v_permlane32_swap halves
+// {lo, lo} and {hi, hi}; combining the two results after each swap gives
+// every lane the column's maximum (or sum) with VALU work only.
+__device__ __forceinline__ uint32_t column4_max_u32(uint32_t x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)a[0], (uint32_t)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+__device__ __forceinline__ float column4_sum_f32(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
