@@ -15,7 +15,8 @@ extern "C" const void* dsw_internal_mfma_kernel_b1(int reg_tiles, int max_tiles)
 extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
-extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round);
+extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round,
+                                                   int keep);
 // the same all-to-all kernels with Gumbel-max sampling
 extern "C" const void* dsw_internal_walk_kernel_gumbel(int reg_slots, int batch_tile, int w2_dtype);
 extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max_tiles);
@@ -45,7 +46,7 @@ int cell_of(unsigned flags) {
 
 // cell: as cell_of; single: DSW_FLAG_SINGLE_ROUND (the batched kernel is
 // compiled for each rounding)
-const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell, bool single) {
+const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell, bool single, int B) {
     if (cell) {  // the planner gives the recurrent heads only the one-request MFMA engine
         if (pl.engine != DSW_ENGINE_MFMA || pl.batch_tile != 1 || pl.w2_dtype != DSW_BF16) return nullptr;
         const void* (*const lookup[])(int, int) = {dsw_internal_mfma_kernel_b1_gru, dsw_internal_mfma_kernel_b1_rnn,
@@ -54,7 +55,9 @@ const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell, bool sing
         return cell <= 4 ? lookup[cell - 1](pl.reg_tiles, pl.max_tiles) : nullptr;
     }
     if (pl.batch_tile == dsw::kMaxBatch)
-        return gumbel ? nullptr : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single);
+        return gumbel ? nullptr
+                      : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single,
+                                                    (B + dsw::kGroup - 1) / dsw::kGroup <= pl.ring_slots - 1);
     if (pl.engine == DSW_ENGINE_VALU)
         return gumbel ? dsw_internal_walk_kernel_gumbel(pl.reg_slots, pl.batch_tile, pl.w2_dtype)
                       : dsw_internal_walk_kernel(pl.reg_slots, pl.batch_tile, pl.w2_dtype);
@@ -221,7 +224,7 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
         dsw_plan_info pl;
         int prc = dsw_plan_compute(&dev, V, r, gm, B, w2_dtype, flags, &pl);
         const void* fn = prc == DSW_OK ? kernel_for(pl, (flags & DSW_FLAG_GUMBEL) != 0, cell_of(flags),
-                                                    (flags & DSW_FLAG_SINGLE_ROUND) != 0)
+                                                    (flags & DSW_FLAG_SINGLE_ROUND) != 0, B)
                                         : nullptr;
         hipFuncAttributes attr;
         int per_cu = 0;
@@ -325,7 +328,7 @@ int launch_walk(const LaunchCtx& x, const void* W1, const void* W2, const float*
     if (rc) return rc;
     if (plan_out) *plan_out = plan;
     const void* fn = kernel_for(plan, (x.flags & DSW_FLAG_GUMBEL) != 0, gru != nullptr ? cell_of(x.flags) : 0,
-                                (x.flags & DSW_FLAG_SINGLE_ROUND) != 0);
+                                (x.flags & DSW_FLAG_SINGLE_ROUND) != 0, B);
     if (!fn) return DSW_ERR_PLAN;
     if (plan.batch_tile == kMaxBatch && x.ws.blog == nullptr) return DSW_ERR_PLAN;
 

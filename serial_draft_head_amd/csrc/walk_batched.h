@@ -36,7 +36,9 @@ constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8
 constexpr unsigned kDecPending = 1u << 20;
 
 // SR = 1: single rounding (logit = bf16(base + fp32 dot)), DSW_FLAG_SINGLE_ROUND.
-template <int A, int M, int DT, int SR>
+// LK = 1 (bf16, small batches): the step's logits stay in the LDS ring slots
+// for the token shards when every group has a slot of its own.
+template <int A, int M, int DT, int SR, int LK = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
@@ -97,6 +99,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     // a few lines (16 requests: 255 -> 253 us against whole lines).
     const int OS = (B <= kGroup && B <= G) ? 3 : owner_stride(G);
     const int D = p.ring;
+    // every group of the step has a ring slot of its own (no DMA reuses one
+    // before the next step): the step's logits stay in the slots, where the
+    // token shards read them, instead of going out to memory and back
+    const bool lds_keep = LK != 0 && (B + kGroup - 1) / kGroup <= D - 1;
     const bool aligned = p.aligned != 0;
     const bool al4 = (V & 3) == 0;  // 8-byte stores of 4 logits (rows 4g .. 4g+3)
     const int P = 2 + (aligned ? CPR / 16 : 0);  // DMA instructions per wave and group
@@ -388,10 +394,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
         if (STORE) {                                                                             \
             /* wave-uniform branches only: no exec masks in the tiles */                        \
-            if (priv) {                                                                          \
+            if (priv && !lds_keep) {                                                             \
                 if (live_) lpriv[(j) * 64] = make_uint2(q01_, q23_);                             \
-            } else {                                                                             \
-                *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);  /* staged for the caller's copy */   \
+            } else {  /* in the slot: for the caller's copy, or read there by the token shard */ \
+                *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                       \
             }                                                                                    \
             const float mn_ = fmaxf(mrun, tm_);                                                  \
             const float rf_ = mn_ == -__builtin_inff() ? 0.0f : mn_;                             \
@@ -637,7 +643,16 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 // this shard's logits of request b, requested before the owner's
                 // words are polled (both round trips overlap)
                 uint32_t lb[RLMAX];
-                if (p.logits != nullptr) {
+                if (lds_keep) {
+                    // the group's slot holds the logits over the base logits
+                    const uint16_t* sl = reinterpret_cast<const uint16_t*>(ring + ((b >> 4) % D) * slot_bytes + kSlotUBytes);
+                    const int nn = b & 15;
+#pragma unroll
+                    for (int rr = 0; rr < RLMAX; ++rr) {
+                        const int r = lane * RL + rr;
+                        lb[rr] = (rr < RL && r < nrows) ? (uint32_t)sl[(nn * CPR + ((r >> 3) ^ nn)) * 8 + (r & 7)] : 0u;
+                    }
+                } else if (p.logits != nullptr) {
                     const uint16_t* lrow = p.logits + ((size_t)b * gamma + k) * V + v0;
 #pragma unroll
                     for (int rr = 0; rr < RLMAX; ++rr) {

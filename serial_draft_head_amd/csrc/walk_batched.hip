@@ -3,13 +3,16 @@
 #include "walk_batched.h"
 
 // Host-side lookup used by the launcher: the batched kernel for (W2 dtype,
-// register tiles, tiles per wave, single rounding), or nullptr when that shape
-// is not compiled.
-extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round) {
+// register tiles, tiles per wave, single rounding, logits kept in LDS), or
+// nullptr when that shape is not compiled.  Keeping the logits in LDS is
+// compiled for bf16 with double rounding (the small batches' default).
+extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round,
+                                                   int keep) {
 #define DSW_PICK(R, M)                                                   \
     if (w2_dtype == 0 && reg_tiles == (R) && max_tiles == (M))           \
         return single_round ? (const void*)dsw::walk_batched<(R), (M), 0, 1> \
-                            : (const void*)dsw::walk_batched<(R), (M), 0, 0>;
+                            : (keep ? (const void*)dsw::walk_batched<(R), (M), 0, 0, 1> \
+                                    : (const void*)dsw::walk_batched<(R), (M), 0, 0>);
 #define DSW_PICK_I8(R, M)                                                \
     if (w2_dtype == 1 && reg_tiles == (R) && max_tiles == (M))           \
         return single_round ? (const void*)dsw::walk_batched<(R), (M), 1, 1> \
