@@ -497,6 +497,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             }
         }
         DSW_TRACE(k, kTrPosted);
+        // ~0.2 us before the first poll of the columns: no other workgroup's
+        // words can be there yet, and early polls only load the fabric
+        // (measured: V = 129,280, gamma 5, B = 16: 231.5 -> 229.7 us)
+        __builtin_amdgcn_s_sleep(8);
 
         // read column b of every workgroup's row: kw, sw of shard t (t < G)
 #define DSW_READ_COLUMN(b_, kw_, sw_)                                                            \
