@@ -20,20 +20,28 @@
 // * Exchange: an all-to-all of B keys per workgroup would read B * 2 KiB per
 //   workgroup and step.  Here request b is owned by workgroup b % G: every
 //   workgroup stores its B key words (and exp-sum words) in one row, the owner
-//   reads column b, and publishes the token (greedy) or the shard whose mass
-//   holds u*Z (sampled).  That shard scans its logits of request b (written
-//   out during the step: to `logits` if the caller wants them, else to the
-//   workspace), finds the token, and publishes it.  Greedy steps take two
-//   exchanges, sampled steps three.
+//   reads column b, and publishes in one word the token (greedy), or the
+//   shard whose mass holds u*Z together with the mass that shard has to
+//   accumulate, in its own scale, before the token (sampled).  That shard
+//   scans its logits of request b (kept in LDS, or written out during the
+//   step: to `logits` if the caller wants them, else to the workspace), finds
+//   the token, and publishes it.  Greedy steps take two exchanges, sampled
+//   steps three.
 #pragma once
 #include "walk_kernel.h"
 
 namespace dsw {
 
 constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8 KiB
-// Decision payload: a token id (< 2^20), or kDecPending | shard << 21 |
-// ord16(max logit) for a sampled request whose token shard still has to find it.
-constexpr unsigned kDecPending = 1u << 20;
+// Decision words carry a 24-bit epoch, (seq mod 2^23) + 1: never 0, and two
+// steps share it only 2^23 steps apart (the words a reader can meet are fewer
+// than 2 gamma_max <= 8192 steps apart).  Above it: a greedy request's token
+// (bits 24..43); a sampled request's token shard (bits 24..31) and, as fp32
+// bits 32..63, the mass q that shard accumulates over its rows, relative to
+// its own maximum, before the token: (u*Z - mass of the shards before it) /
+// exp((its max - M) / T).
+constexpr unsigned long long kDecEpochMask = 0xFFFFFFull;
+__device__ __forceinline__ unsigned long long dec_epoch(unsigned seq) { return (seq & 0x7FFFFFu) + 1u; }
 
 // SR = 1: single rounding (logit = bf16(base + fp32 dot)), DSW_FLAG_SINGLE_ROUND.
 // LK = 1 (bf16, small batches): the step's logits stay in the LDS ring slots
@@ -52,15 +60,16 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ int s_prev[kMaxBatch];
     __shared__ int s_next[kMaxBatch];
     __shared__ float s_T[kMaxBatch];
-    __shared__ unsigned s_dec[kMaxBatch];
+    __shared__ unsigned s_dec[kMaxBatch];      // sampled requests: the token shard
+    __shared__ float s_q[kMaxBatch];           // sampled requests: the token shard's mass before the token
     __shared__ float s_S[kMaxGrid];
+    __shared__ float s_E[kMaxGrid];
     __shared__ float s_scale[kI8 ? RPAD : 1];
     __shared__ int s_tasks[kMaxBatch];
     __shared__ uint2 s_junk[4][64];            // base logits (-inf) of tiles beyond a wave's rows
     __shared__ unsigned long long s_red64[4];
     __shared__ int s_own;
-    __shared__ float s_pex;
-    __shared__ float s_tgt;
+    __shared__ float s_qown;
     __shared__ int s_ntask;
     __shared__ unsigned s_round;
     __shared__ unsigned s_fam;
@@ -91,13 +100,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const int wrow0 = wave * TW * kTileRows;
     const int nt_w = max(0, min(TW, (nrows - wrow0 + kTileRows - 1) / kTileRows));
     const int NG = (B + kGroup - 1) / kGroup;
-    // Owner words: request b's decision, prefix and u*Z words at 3 (b / G)
-    // in owner b % G's region of OS words.  Large batches: regions of whole
-    // lines, one writer each (253 requests: 335 -> 329 us, 64: 136 -> 131 us
-    // against one line shared by 16 owners).  Up to 16 requests, one per
-    // owner: regions of 3 words, so that a reader's B decision words sit in
-    // a few lines (16 requests: 255 -> 253 us against whole lines).
-    const int OS = (B <= kGroup && B <= G) ? 3 : owner_stride(G);
+    // Owner words: request b's decision word at b / G in owner b % G's region
+    // of OS words, whole lines with one writer each (253 requests: 335 -> 329
+    // us, 64: 136 -> 131 us against one line shared by 16 owners; 16 requests:
+    // 224 -> 216 us against their 16 words in one line).
+    const int OS = owner_stride(G);
     const int D = p.ring;
     // every group of the step has a ring slot of its own (no DMA reuses one
     // before the next step): the step's logits stay in the slots, where the
@@ -279,9 +286,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const int q = (int)(seq & 1u);
         unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch;
         unsigned long long* bsum = p.ws.bsum + (size_t)q * kMaxGrid * kMaxBatch;
-        // request b's decision word; its prefix and u*Z follow it
         unsigned long long* bown = p.ws.bdec + (size_t)q * kOwnWords;
-#define DSW_OWN(b_) (bown + (size_t)((b_) % G) * OS + 3 * ((b_) / G))
+#define DSW_OWN(b_) (bown + (size_t)((b_) % G) * OS + (b_) / G)
         unsigned long long* btok = p.ws.btok + (size_t)q * kMaxGrid * kMaxBatch;  // [shard][request]
 
         // group gq's u rows and base logits into ring slot gq % D.  Each lane
@@ -399,13 +405,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             } else {  /* in the slot: for the caller's copy, or read there by the token shard */ \
                 *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                       \
             }                                                                                    \
+            /* finite, since mrun starts at -FLT_MAX: no -inf - -inf */                         \
             const float mn_ = fmaxf(mrun, tm_);                                                  \
-            const float rf_ = mn_ == -__builtin_inff() ? 0.0f : mn_;                             \
-            srun = srun * __builtin_amdgcn_exp2f((mrun - rf_) * sc) +                            \
-                   ((__builtin_amdgcn_exp2f((bf16_lo(q01_) - rf_) * sc) +                         \
-                     __builtin_amdgcn_exp2f((bf16_hi(q01_) - rf_) * sc)) +                        \
-                    (__builtin_amdgcn_exp2f((bf16_lo(q23_) - rf_) * sc) +                         \
-                     __builtin_amdgcn_exp2f((bf16_hi(q23_) - rf_) * sc)));                        \
+            srun = srun * __builtin_amdgcn_exp2f((mrun - mn_) * sc) +                            \
+                   ((__builtin_amdgcn_exp2f((bf16_lo(q01_) - mn_) * sc) +                         \
+                     __builtin_amdgcn_exp2f((bf16_hi(q01_) - mn_) * sc)) +                        \
+                    (__builtin_amdgcn_exp2f((bf16_lo(q23_) - mn_) * sc) +                         \
+                     __builtin_amdgcn_exp2f((bf16_hi(q23_) - mn_) * sc)));                        \
             mrun = mn_;                                                                          \
         }                                                                                        \
         const bool gt_ = tm_ > bestv;                                                            \
@@ -426,7 +432,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const float sc = samp ? kLog2e / s_T[b] : 0.0f;
             const bool priv = p.logits == nullptr;  // the private blocks (wave-uniform)
             uint2* lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
-            float mrun = -__builtin_inff(), srun = 0.0f;  // the lane's running maximum and exp-sum
+            float mrun = -__FLT_MAX__, srun = 0.0f;  // the lane's running maximum and exp-sum
             const bool stored = !priv || __builtin_amdgcn_ballot_w64(samp) != 0ull;
             if (stored) {
                 DSW_TILES(DSW_EPI_GS);
@@ -469,7 +475,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             if (stored && __builtin_amdgcn_ballot_w64(on) != 0ull) {
                 // exp-sum of this wave's logits of request n relative to its
                 // maximum: the four lanes' running sums, rescaled to it (a lane
-                // whose rows all lie past the vocabulary holds 0 at -inf)
+                // whose rows all lie past the vocabulary holds 0 at -FLT_MAX)
                 const float mw = local_key_logit(best);
                 float sw = on ? srun * __builtin_amdgcn_exp2f((mrun - mw) * sc) : 0.0f;
                 sw = column4_sum_f32(sw);
@@ -530,15 +536,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }                                                                                        \
     } while (0)
 
-        // shard masses S_t of sampled request b_ into s_S, then wave 0 finds
-        // the first shard with positive mass whose prefix exceeds u*Z (else the
-        // last with positive mass): s_own, s_pex (mass before it), s_tgt = u*Z.
-        // Every caller runs this same code on the same words: same results.
+        // shard masses S_t of sampled request b_ into s_S (and their scales
+        // exp((m_t - M) / T) into s_E), then wave 0 finds the first shard with
+        // positive mass whose prefix exceeds u*Z (else the last with positive
+        // mass): s_own, and s_qown = (u*Z - mass before it) / its scale.
 #define DSW_OWNER_SHARD(b_, kw_, sw_, M_)                                                        \
     do {                                                                                         \
-        s_S[t] = (t < G && kw_ != 0ull)                                                          \
-                     ? sw_ * __builtin_amdgcn_exp2f((key_logit(kw_) - (M_)) * (kLog2e / s_T[b_])) \
-                     : 0.0f;                                                                     \
+        const float e_ = (t < G && kw_ != 0ull)                                                  \
+                             ? __builtin_amdgcn_exp2f((key_logit(kw_) - (M_)) * (kLog2e / s_T[b_])) \
+                             : 0.0f;                                                             \
+        s_S[t] = (t < G && kw_ != 0ull) ? sw_ * e_ : 0.0f;                                       \
+        s_E[t] = e_;                                                                             \
         __syncthreads();                                                                         \
         if (wave == 0) {                                                                         \
             const float4 m4_ = reinterpret_cast<const float4*>(s_S)[lane];                       \
@@ -562,8 +570,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const float pex_ = __shfl(cj_, pj_ >> 2);                                            \
             if (lane == 0) {                                                                     \
                 s_own = own_;                                                                    \
-                s_pex = own_ > 0 ? pex_ : 0.0f;                                                  \
-                s_tgt = tgt_;                                                                    \
+                /* own_ >= 0: the winner's shard has mass >= 1 */                               \
+                s_qown = (tgt_ - (own_ > 0 ? pex_ : 0.0f)) * __builtin_amdgcn_rcpf(s_E[max(own_, 0)]); \
             }                                                                                    \
         }                                                                                        \
         __syncthreads();                                                                         \
@@ -579,6 +587,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     } while (0)
 
         // ---- owners: the winner of every request this workgroup owns -------
+        // (the decision words' epoch, formed here: a scalar pair less held
+        // through the group loop)
+        const unsigned long long dep = dec_epoch(fam * (unsigned)p.gamma_max + (unsigned)k);
         for (int b = c; b < B; b += G) {
             unsigned long long kw;
             float sw;
@@ -590,18 +601,14 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 if (t == 0) {
                     const int tok = checked_token(key_index(win), V, status);
                     walk_skew(p, c, k, 1);
-                    st_agent64(DSW_OWN(b), ((unsigned long long)(unsigned)tok << 28) | epoch);
+                    st_agent64(DSW_OWN(b), ((unsigned long long)(unsigned)tok << 24) | dep);
                 }
             } else {
                 DSW_OWNER_SHARD(b, kw, sw, key_logit(win));
                 if (t == 0) {
                     walk_skew(p, c, k, 1);
-                    unsigned long long* ext = DSW_OWN(b) + 1;
-                    st_agent64(&ext[0], ((unsigned long long)__float_as_uint(s_pex) << 32) | epoch);
-                    st_agent64(&ext[1], ((unsigned long long)__float_as_uint(s_tgt) << 32) | epoch);
-                    const unsigned d = kDecPending | ((unsigned)max(s_own, 0) << 21) |
-                                       (uint32_t)((win >> kIdxBits) & 0xFFFFu);
-                    st_agent64(DSW_OWN(b), ((unsigned long long)d << 28) | epoch);
+                    st_agent64(DSW_OWN(b), ((unsigned long long)__float_as_uint(s_qown) << 32) |
+                                               ((unsigned long long)(unsigned)max(s_own, 0) << 24) | dep);
                 }
             }
             __syncthreads();
@@ -615,27 +622,32 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             unsigned it = 0;
             unsigned long long w = 0ull;
             bool ok = true;
-            while (((w = ld_agent64(DSW_OWN(t))) & kEpochMod) != epoch) {
+            while (((w = ld_agent64(DSW_OWN(t))) & kDecEpochMask) != dep) {
                 if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
                 if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
                 __builtin_amdgcn_s_sleep(1);
             }
             if (!ok) s_abort = 1;
-            const unsigned d = ok ? (unsigned)(w >> 28) : 0u;
-            s_dec[t] = d;
-            if (!(d & kDecPending)) s_next[t] = checked_token((int)(d & 0xFFFFFu), V, status);
+            if (!ok) w = 0ull;
+            if (s_T[t] > 0.0f) {
+                s_dec[t] = (unsigned)(w >> 24) & 0xFFu;
+                s_q[t] = __uint_as_float((uint32_t)(w >> 32));
+            } else {
+                s_next[t] = checked_token((int)((w >> 24) & 0xFFFFFu), V, status);
+            }
         }
         __syncthreads();
         if (s_abort) break;
         DSW_TRACE(k, kTrArrived);
 
         // ---- sampled requests whose token lies in this shard --------------
-        // Their logits of this shard were written out in the group loop; each
-        // wave takes every fourth task and scans the shard's rows in vocabulary
-        // order (RL consecutive rows per lane) for the first cumulative mass
-        // above u*Z, from the owner's prefix before this shard.
+        // Their logits of this shard are in LDS or were written out in the
+        // group loop; each wave takes every fourth task and scans the shard's
+        // rows in vocabulary order (RL consecutive rows per lane) for the
+        // first cumulative mass, relative to the shard's maximum, above the
+        // owner's q.
         if (any_samp) {
-            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] >> 21) == c)
+            if (t < B && s_T[t] > 0.0f && (int)s_dec[t] == c)
                 s_tasks[atomicAdd(&s_ntask, 1)] = t;
             __syncthreads();
             const int ntask = s_ntask;
@@ -644,8 +656,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             for (int i = wave; i < ntask; i += 4) {
                 const int b = s_tasks[i];
                 const float sc2 = kLog2e / s_T[b];
-                // this shard's logits of request b, requested before the owner's
-                // words are polled (both round trips overlap)
+                // this shard's logits of request b
                 uint32_t lb[RLMAX];
                 if (lds_keep) {
                     // the group's slot holds the logits over the base logits
@@ -680,26 +691,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                         }
                     }
                 }
-                // the owner's prefix before this shard (lane 0) and u*Z (lane 1)
-                float ev = 0.0f;
-                bool ok = true;
-                if (lane < 2) {
-                    const unsigned long long* ext = DSW_OWN(b) + 1 + lane;
-                    unsigned it = 0;
-                    unsigned long long w = 0ull;
-                    while (((w = ld_agent64(ext)) & kEpochMod) != epoch) {
-                        if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
-                        if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                    ev = __uint_as_float((uint32_t)(w >> 32));
-                }
-                if (!ok) s_abort = 1;
-                const float pexcl = __shfl(ev, 0), target = __shfl(ev, 1);
-                const float Mg = bf16_to_f32(unord16(s_dec[b] & 0xFFFFu));
+                const float qb = s_q[b];
                 const uint32_t lk = max(max(s_rkey[0][b], s_rkey[1][b]), max(s_rkey[2][b], s_rkey[3][b]));
                 const float ml = local_key_logit(lk);
-                const float scale = __builtin_amdgcn_exp2f((ml - Mg) * sc2);
                 float wv[RLMAX];
                 float part = 0.0f;
 #pragma unroll
@@ -716,7 +710,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                     const int r = lane * RL + rr;
                     if (rr < RL && r < nrows) {
                         run += wv[rr];
-                        if (first == 0u && pexcl + scale * run > target) first = (uint32_t)r + 1u;
+                        if (first == 0u && run > qb) first = (uint32_t)r + 1u;
                         if (wv[rr] > 0.0f) lastw = (uint32_t)r + 1u;
                     }
                 }
@@ -734,11 +728,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             __syncthreads();
             if (s_abort) break;
             // tokens found by other shards
-            if (t < B && (s_dec[t] & kDecPending) && (int)(s_dec[t] >> 21) != c) {
+            if (t < B && s_T[t] > 0.0f && (int)s_dec[t] != c) {
                 unsigned it = 0;
                 unsigned long long w = 0ull;
                 bool ok = true;
-                const unsigned long long* tw = &btok[(size_t)(s_dec[t] >> 21) * kMaxBatch + t];
+                const unsigned long long* tw = &btok[(size_t)s_dec[t] * kMaxBatch + t];
                 while (((w = ld_agent64(tw)) & kEpochMod) != epoch) {
                     if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
                     if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }

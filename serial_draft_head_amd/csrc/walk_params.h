@@ -42,10 +42,10 @@ constexpr int kCellMaxPerWg = 4;   // recurrent heads: state elements per workgr
 constexpr int kDominoMaxGamma = 16;  // Domino's head: steps per round (its drafters' blocks)
 constexpr int kDominoMaxD = 4096;    // Domino's head: the drafter's hidden width, bound
 constexpr int kMaxBatch = 256;           // requests per launch of the batched kernel
-// Batched kernel: words of one owner workgroup's region (three per request it
+// Batched kernel: words of one owner workgroup's region (one per request it
 // owns, rounded up to whole 128-byte lines), and a bound on G * owner_stride(G)
 // over every grid of up to kMaxGrid workgroups.
-constexpr int owner_stride(int G) { return (3 * ((kMaxBatch + G - 1) / G) + 15) / 16 * 16; }
+constexpr int owner_stride(int G) { return (((kMaxBatch + G - 1) / G) + 15) / 16 * 16; }
 constexpr int kOwnWords = 4096;
 constexpr int max_owner_words() {
     int m = 0;
@@ -79,10 +79,10 @@ struct Workspace {
     unsigned long long* bsum;      // [2][kMaxGrid][kMaxBatch]  exp-sum bits << 32 | epoch
     unsigned long long* bdec;      // [2][kOwnWords]  per owner workgroup c, a region of
                                    // owner_stride(G) words (whole 128-byte lines, one
-                                   // writer each; 3 words for up to 16 requests); request
-                                   // b = c + i G takes words 3i .. 3i + 2: decision << 28 |
-                                   // epoch, then the prefix before the token shard and u*Z,
-                                   // fp32 bits << 32 | epoch
+                                   // writer each; 1 word for up to 16 requests); request
+                                   // b = c + i G takes word i: its decision, payload << 24 |
+                                   // a 24-bit epoch (the token, or the token shard and the
+                                   // mass that shard accumulates before the token)
     unsigned long long* btok;      // [2][kMaxGrid][kMaxBatch]  sampled token << 28 | epoch,
                                    // in the row of the shard that found it
     uint16_t* blog;                // batched kernel: this step's logits of the sampled
