@@ -43,11 +43,43 @@ constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8
 constexpr unsigned long long kDecEpochMask = 0xFFFFFFull;
 __device__ __forceinline__ unsigned long long dec_epoch(unsigned seq) { return (seq & 0x7FFFFFu) + 1u; }
 
+// Four 16x16 results whose columns 0..3 alone are needed: lane column 4q + b
+// of each 16-lane row takes column b of t_q (DPP row shifts by 4q, written
+// into bank q only).
+__device__ __forceinline__ f32x4_t fold4(const f32x4_t& t0, const f32x4_t& t1, const f32x4_t& t2,
+                                         const f32x4_t& t3) {
+    f32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int v = __float_as_int(t0[i]);
+        v = __builtin_amdgcn_update_dpp(v, __float_as_int(t1[i]), 0x114, 0xF, 0x2, false);  // row_shr:4
+        v = __builtin_amdgcn_update_dpp(v, __float_as_int(t2[i]), 0x118, 0xF, 0x4, false);  // row_shr:8
+        v = __builtin_amdgcn_update_dpp(v, __float_as_int(t3[i]), 0x11C, 0xF, 0x8, false);  // row_shr:12
+        r[i] = __int_as_float(v);
+    }
+    return r;
+}
+// The maximum and the sum over lane columns n, n + 4, n + 8, n + 12 of each
+// 16-lane row (DPP row rotations by 4 and 8).
+__device__ __forceinline__ uint32_t fold4_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false));  // row_ror:4
+    return max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));  // row_ror:8
+}
+__device__ __forceinline__ float fold4_sum_f32(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
 // SR = 1: single rounding (logit = bf16(base + fp32 dot)), DSW_FLAG_SINGLE_ROUND.
 // LK = 1 (bf16, small batches): the step's logits stay in the LDS ring slots
 // for the token shards when every group has a slot of its own.
-template <int A, int M, int DT, int SR, int LK = 0>
+// FD = 4 (with LK = 1, up to 4 requests): only columns 0..3 of a tile's result
+// hold requests, so four tiles share one epilogue: tile j0 + q's column b
+// moves to lane column 4q + b (DPP row shifts), and each lane works on its
+// own tile and request.
+template <int A, int M, int DT, int SR, int LK = 0, int FD = 1>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
+    static_assert(FD == 1 || (FD == 4 && LK == 1 && DT == 0 && A % 4 == 0), "fold: bf16, LDS-kept logits");
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
     static_assert(A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles && (A % 2) == 0, "shape");
@@ -81,7 +113,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // provably wave-uniform
     const int g = lane >> 4;  // rows 4g .. 4g+3 of a tile
-    const int n = lane & 15;  // request column within a group
+    const int n = lane & 15;  // request column within a group (MFMA B operand)
+    // the lane's request within its group and its tile offset in the epilogue
+    const int nreq = FD == 4 ? (n & 3) : n;
+    const int qf = FD == 4 ? (n >> 2) : 0;
     const int c = blockIdx.x;
     const int G = gridDim.x;
     const int V = p.V;
@@ -278,6 +313,47 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }                                                                                        \
     } while (0)
 
+    // FD = 4: four tiles per epilogue (the lane's tile is j0 + qf); the MFMAs
+    // of four register tiles are issued before the epilogue of the previous four
+#define DSW_TILES_F4(EPI)                                                                        \
+    do {                                                                                         \
+        f32x4_t e_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                            \
+        uint2 eb_ = make_uint2(0u, 0u);                                                          \
+        _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 4) {                                    \
+            const uint2 nb_ = *DSW_BASE_PTR(j0 + qf);                                            \
+            f32x4_t c_[4];                                                                       \
+            _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                                   \
+                c_[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                        \
+                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
+                    c_[jj] = mfma_tile(as_bf16x8(wr[j0 + jj][kb]), ub[kb], c_[jj]);              \
+            }                                                                                    \
+            if (j0 > 0) EPI(e_, j0 - 4 + qf, eb_);                                               \
+            e_ = fold4(c_[0], c_[1], c_[2], c_[3]);                                              \
+            eb_ = nb_;                                                                           \
+        }                                                                                        \
+        if (A > 0) EPI(e_, A - 4 + qf, eb_);                                                     \
+        _Pragma("unroll 1") for (int j0 = A; j0 < nt_w; j0 += 4) {                               \
+            f32x4_t c_[4];                                                                       \
+            _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                                   \
+                const int j = j0 + jj;                                                           \
+                c_[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                        \
+                if (j < nt_w) {                                                                  \
+                    if (j - A < LT) {                                                            \
+                        const int sb_ = (wave * LT + (j - A)) * 512 + lane;                      \
+                        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                         \
+                            c_[jj] = mfma_tile(as_bf16x8(s_wt[sb_ + kb * 64]), ub[kb], c_[jj]);  \
+                    } else {                                                                     \
+                        const int row_ = min(v0 + wrow0 + j * kTileRows + n, last_row);          \
+                        const WT* src_ = W2 + (size_t)row_ * kRowChunks + g;                     \
+                        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                         \
+                            c_[jj] = mfma_tile(as_bf16x8(src_[kb * 4]), ub[kb], c_[jj]);         \
+                    }                                                                            \
+                }                                                                                \
+            }                                                                                    \
+            EPI(fold4(c_[0], c_[1], c_[2], c_[3]), j0 + qf, *DSW_BASE_PTR(j0 + qf));             \
+        }                                                                                        \
+    } while (0)
+
     // ---- the walk --------------------------------------------------------
     for (int k = 0; k < gamma; ++k) {
         DSW_TRACE(k, kTrStepStart);
@@ -336,7 +412,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const char* slot = ring + (grp % D) * slot_bytes;
             const uint4* su = reinterpret_cast<const uint4*>(slot);
             uint16_t* sb = reinterpret_cast<uint16_t*>(const_cast<char*>(slot) + kSlotUBytes);
-            const int b = grp * kGroup + n;
+            const int b = grp * kGroup + nreq;
             const bool bval = b < B;
             uint4 ub[8];
 #pragma unroll
@@ -359,10 +435,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             float bestv = -__builtin_inff();
             int bestj = -1;
             uint32_t bq01 = 0u, bq23 = 0u;
-// Base logits of tile j for this lane: the slot, or s_junk (-inf) for a
-// register tile beyond this wave's rows.
+// Base logits of tile j for this lane's request: the slot, or s_junk (-inf)
+// for a tile beyond this wave's rows.
 #define DSW_BASE_PTR(j)                                                                          \
-    (((j) < nt_w) ? reinterpret_cast<uint2*>(sb + (n * CPR + (((wrow0 + (j) * kTileRows + 4 * g) >> 3) ^ n)) * 8 + \
+    (((j) < nt_w) ? reinterpret_cast<uint2*>(sb + (nreq * CPR + (((wrow0 + (j) * kTileRows + 4 * g) >> 3) ^ nreq)) * 8 + \
                                              ((wrow0 + (j) * kTileRows + 4 * g) & 7))            \
                   : &s_junk[wave][lane])
 // Branch-free, so that the matrix cores' work and this VALU work can be
@@ -400,7 +476,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
         if (STORE) {                                                                             \
             /* wave-uniform branches only: no exec masks in the tiles */                        \
-            if (priv && !lds_keep) {                                                             \
+            if (FD == 1 && priv && !lds_keep) {                                                  \
                 if (live_) lpriv[(j) * 64] = make_uint2(q01_, q23_);                             \
             } else {  /* in the slot: for the caller's copy, or read there by the token shard */ \
                 *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                       \
@@ -434,10 +510,18 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             uint2* lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
             float mrun = -__FLT_MAX__, srun = 0.0f;  // the lane's running maximum and exp-sum
             const bool stored = !priv || __builtin_amdgcn_ballot_w64(samp) != 0ull;
-            if (stored) {
-                DSW_TILES(DSW_EPI_GS);
+            if constexpr (FD == 4) {
+                if (stored) {
+                    DSW_TILES_F4(DSW_EPI_GS);
+                } else {
+                    DSW_TILES_F4(DSW_EPI_G);
+                }
             } else {
-                DSW_TILES(DSW_EPI_G);
+                if (stored) {
+                    DSW_TILES(DSW_EPI_GS);
+                } else {
+                    DSW_TILES(DSW_EPI_G);
+                }
             }
 #undef DSW_EPI_G
 #undef DSW_EPI_GS
@@ -448,8 +532,10 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             const int bestr = bestj >= 0 ? wrow0 + bestj * kTileRows + 4 * g + bi : -1;
             uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
             // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
+            // (and, folded, the four tiles of each epilogue)
             best = column4_max_u32(best);
-            if (g == 0 && bval) s_rkey[wave][b] = best;
+            if constexpr (FD == 4) best = fold4_max_u32(best);
+            if (g == 0 && qf == 0 && bval) s_rkey[wave][b] = best;
             if (!priv) {
                 // the caller's logits of the group's requests over this wave's
                 // rows, from the slot: four consecutive rows per lane, so that
@@ -479,7 +565,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const float mw = local_key_logit(best);
                 float sw = on ? srun * __builtin_amdgcn_exp2f((mrun - mw) * sc) : 0.0f;
                 sw = column4_sum_f32(sw);
-                if (g == 0 && bval) {
+                if constexpr (FD == 4) sw = fold4_sum_f32(sw);
+                if (g == 0 && qf == 0 && bval) {
                     s_rm[wave][b] = mw;
                     s_rs[wave][b] = sw;
                 }
@@ -759,6 +846,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #undef DSW_OWNER_SHARD
 #undef DSW_BLOCK_MAX64
 #undef DSW_TILES
+#undef DSW_TILES_F4
 
     DSW_TRACE_FLUSH();
     if (c == 0 && t == 0 && !s_abort) {

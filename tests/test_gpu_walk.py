@@ -1101,6 +1101,32 @@ def test_batched_kernel_at_small_batches(dsw, B):
     walker.close()
 
 
+# Up to 4 requests on the batched kernel: four tiles share one epilogue.
+# Vocabularies with dead register tiles (V = 4,099: shards of 17 rows; V =
+# 100,003: 7 tiles per wave on the 8-tile shape), LDS tiles (V = 151,936)
+# and streamed tiles (FORCE_STREAM), an unaligned vocabulary, logits out or
+# kept in LDS only.
+@pytest.mark.parametrize("B", [1, 2, 4])
+@pytest.mark.parametrize("V,stream", [(4_099, False), (100_003, False), (151_936, False), (60_000, True)])
+def test_batched_four_tile_epilogue(dsw, V, stream, B):
+    say(f"batched four-tile epilogue V={V} B={B} stream={stream}")
+    W1, W2 = workloads.weights(2, V=V)
+    w = parity.Weights(W1, W2)
+    flags = dsw.FLAG_BATCHED | (dsw.FLAG_FORCE_STREAM if stream else 0)
+    walker = dsw.Walker(V, gamma_max=5, B_max=B, flags=flags)
+    pl = walker.query_plan(B)
+    say("plan", pl.as_dict())
+    assert pl.batch_tile == 256
+    W1d, W2d = bf16_dev(W1), bf16_dev(W2)
+    for rnd in range(2):
+        inp = workloads.round_inputs(2, 80 + rnd, B=B, gamma=5, V=V, temps="mixed")
+        toks, lg = run(walker, W1d, W2d, inp)
+        say(parity.check_round(w, inp["base"], inp["anchor"], inp["T"], inp["uniforms"], toks, lg))
+        toks2, _ = run(walker, W1d, W2d, inp, want_logits=False)
+        assert np.array_equal(toks, toks2)
+    walker.close()
+
+
 def test_batched_stream_logits_and_state(dsw):
     V, B = 40_000, 37
     say(f"batched streamed vs resident, logits optional, V={V} B={B}")
