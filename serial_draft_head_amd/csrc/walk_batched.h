@@ -90,6 +90,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ float s_rm[4][kMaxBatch];       // per wave: max logit (sampled requests)
     __shared__ float s_rs[4][kMaxBatch];       // per wave: exp-sum relative to s_rm
     __shared__ int s_prev[kMaxBatch];
+    __shared__ unsigned long long s_rowb[kMaxBatch];  // request b's base logits of step 0 at this shard, in 16 B
     __shared__ int s_next[kMaxBatch];
     __shared__ float s_T[kMaxBatch];
     __shared__ unsigned s_dec[kMaxBatch];      // sampled requests: the token shard
@@ -244,6 +245,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         s_prev[t] = a;
         s_T[t] = temp;
         if (temp > 0.0f) s_any_samp = 1;
+        s_rowb[t] = (unsigned long long)t * (unsigned)gamma * (unsigned)(V >> 3) + (unsigned)(v0 >> 3);
     }
     __syncthreads();
     if (s_abort) return;  // uniform: read after the barrier
@@ -381,15 +383,17 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                   __builtin_amdgcn_readfirstlane(lds_addr(slot_ + inst_ * 1024)));               \
         }                                                                                        \
         if (aligned) {                                                                           \
+            /* 16-byte chunk (pc ^ nn) of request nn's row past the shard start, */             \
+            /* clamped to the row's last chunk; 24-bit products (pos < 16 CPR)   */             \
             const int per_ = CPR / 16;                                                           \
             for (int ii = 0; ii < per_; ++ii) {                                                  \
                 const int inst_ = wave * per_ + ii;                                              \
                 const int pos_ = inst_ * 64 + lane;                                              \
-                const int nn_ = (int)(((unsigned)pos_ * cpr_mul) >> 20), pc_ = pos_ - nn_ * CPR; \
+                const int nn_ = (int)((unsigned)__umul24((unsigned)pos_, cpr_mul) >> 20);        \
+                const int pc_ = pos_ - __umul24((unsigned)nn_, (unsigned)CPR);                   \
                 const int b_ = min(gq_ * kGroup + nn_, B - 1);                                   \
-                const int cr_ = min((v0 >> 3) + (pc_ ^ nn_), (V >> 3) - 1);                      \
-                const uint4* src_ = reinterpret_cast<const uint4*>(base) +                       \
-                                    ((size_t)b_ * gamma + k) * (size_t)(V >> 3) + cr_;           \
+                const int x_ = min(pc_ ^ nn_, lastc);                                            \
+                const uint4* src_ = reinterpret_cast<const uint4*>(base) + (s_rowb[b_] + koff) + x_; \
                 dma16(src_, __builtin_amdgcn_readfirstlane(lds_addr(slot_ + kSlotUBytes + inst_ * 1024))); \
             }                                                                                    \
         } else {                                                                                 \
@@ -403,6 +407,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }                                                                                        \
     } while (0)
 
+        const unsigned long long koff = (unsigned long long)k * (unsigned)(V >> 3);  // step k's rows, in 16 B
+        const int lastc = (V >> 3) - 1 - (v0 >> 3);  // the row's last chunk past the shard start (< 0: empty shard)
         for (int gq = 0; gq < min(D - 1, NG); ++gq) DSW_ISSUE_GROUP(gq);
 
         for (int grp = 0; grp < NG; ++grp) {
