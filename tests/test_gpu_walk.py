@@ -438,7 +438,8 @@ def test_gumbel_max_needs_a_seed_and_a_small_batch(dsw):
 # device round counter) and device-drawn noise is keyed by that counter, so
 # each replay must be a correct walk with fresh noise.  Eager copies and
 # synchronisations run between the replays.
-@pytest.mark.parametrize("B,flags,temps,replays", [(1, 0, "cycle", 100), (3, 64, "mixed", 8), (20, 0, "mixed", 8)])
+@pytest.mark.parametrize("B,flags,temps,replays", [(1, 0, "cycle", 100), (3, 64, "mixed", 8), (4, 0, "mixed", 8),
+                                                   (20, 0, "mixed", 8)])
 def test_graph_replays_are_fresh_walks(dsw, B, flags, temps, replays):
     import oracle
     say(f"graph replays B={B} flags={flags} {temps}")
