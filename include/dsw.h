@@ -121,10 +121,15 @@ extern "C" {
                                     word v mod 4, as (2 (w >> 9) + 1) 2^-24.
                                     The uniforms argument is not used.  Needs a
                                     seed: dsw_walk returns DSW_ERR_ARG until
-                                    dsw_set_seed(h, seed, 1).  Served by the
-                                    all-to-all kernel only: with
-                                    DSW_FLAG_BATCHED or B_max > 16, dsw_create
-                                    returns DSW_ERR_ARG.                       */
+                                    dsw_set_seed(h, seed, 1).  bf16 rows with
+                                    double rounding: the kernels the inverse
+                                    CDF would use (the batched one from 4
+                                    requests, with one exchange less per
+                                    sampled step).  int8 rows or
+                                    DSW_FLAG_SINGLE_ROUND: the all-to-all
+                                    kernels only, so with DSW_FLAG_BATCHED or
+                                    B_max > 16 dsw_create returns
+                                    DSW_ERR_ARG.                               */
 #define DSW_FLAG_GRU 128u        /* the GRU serial head ("Keeping the Draft Walk on
                                     Chip", section "Beyond DSpark: other serial
                                     heads"): walks go through dsw_walk_gru.

@@ -16,7 +16,7 @@ extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles)
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round,
-                                                   int keep, int fold);
+                                                   int keep, int fold, int gumbel);
 // the same all-to-all kernels with Gumbel-max sampling
 extern "C" const void* dsw_internal_walk_kernel_gumbel(int reg_slots, int batch_tile, int w2_dtype);
 extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max_tiles);
@@ -56,11 +56,11 @@ const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell, bool sing
     }
     if (pl.batch_tile == dsw::kMaxBatch) {
         // the step's logits stay in LDS when every group has a ring slot of its
-        // own; then up to 4 requests share one epilogue per four tiles
-        const bool keep = (B + dsw::kGroup - 1) / dsw::kGroup <= pl.ring_slots - 1;
-        return gumbel ? nullptr
-                      : dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single, keep,
-                                                    keep && B <= 4);
+        // own; then up to 4 requests share one epilogue per four tiles.
+        // Gumbel-max needs no logits kept (no token shard scans them).
+        const bool keep = !gumbel && (B + dsw::kGroup - 1) / dsw::kGroup <= pl.ring_slots - 1;
+        return dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single, keep,
+                                           (keep || gumbel) && B <= 4, gumbel);
     }
     if (pl.engine == DSW_ENGINE_VALU)
         return gumbel ? dsw_internal_walk_kernel_gumbel(pl.reg_slots, pl.batch_tile, pl.w2_dtype)

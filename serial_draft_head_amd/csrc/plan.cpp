@@ -352,9 +352,12 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;
-    // Gumbel-max is the small-batch sampler: the all-to-all kernel, up to 16 requests
+    // Gumbel-max: the batched kernel has it for bf16 rows with double rounding
+    // (from kBatchedFrom requests, as the inverse CDF); otherwise the
+    // all-to-all kernels, up to 16 requests
     const bool gumbel = (flags & DSW_FLAG_GUMBEL) != 0;
-    if (batched && gumbel) return DSW_ERR_ARG;
+    const bool gumbel_batched = gumbel && !i8 && !(flags & DSW_FLAG_SINGLE_ROUND);
+    if (batched && gumbel && !gumbel_batched) return DSW_ERR_ARG;
     // the recurrent heads: one bf16 request on the one-request MFMA engine, and
     // (GRU, RNN) a grid of at least r / kCellMaxPerWg workgroups to hold the
     // state; the gated head keeps the whole state in every workgroup
@@ -377,7 +380,7 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     int rc;
     if (batched) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);
-    } else if (!forced && !gumbel && B >= kBatchedFrom) {
+    } else if (!forced && (!gumbel || gumbel_batched) && B >= kBatchedFrom) {
         rc = plan_batched(dev, V, B, flags, grid, i8, out);
         if (rc != DSW_OK) {
             memset(out, 0, sizeof(*out));

@@ -59,11 +59,36 @@ __device__ __forceinline__ f32x4_t fold4(const f32x4_t& t0, const f32x4_t& t1, c
     }
     return r;
 }
+// column4_max_u32 for 64-bit keys (both halves through the same swaps)
+__device__ __forceinline__ unsigned long long column4_max_u64(unsigned long long x) {
+    const auto ah = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    const auto al = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    const unsigned long long a0 = ((unsigned long long)(uint32_t)ah[0] << 32) | (uint32_t)al[0];
+    const unsigned long long a1 = ((unsigned long long)(uint32_t)ah[1] << 32) | (uint32_t)al[1];
+    x = a0 > a1 ? a0 : a1;
+    const auto bh = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    const auto bl = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    const unsigned long long b0 = ((unsigned long long)(uint32_t)bh[0] << 32) | (uint32_t)bl[0];
+    const unsigned long long b1 = ((unsigned long long)(uint32_t)bh[1] << 32) | (uint32_t)bl[1];
+    return b0 > b1 ? b0 : b1;
+}
 // The maximum and the sum over lane columns n, n + 4, n + 8, n + 12 of each
 // 16-lane row (DPP row rotations by 4 and 8).
 __device__ __forceinline__ uint32_t fold4_max_u32(uint32_t x) {
     x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false));  // row_ror:4
     return max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));  // row_ror:8
+}
+template <int CTL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+    const uint32_t h = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTL, 0xF, 0xF, false);
+    const uint32_t l = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTL, 0xF, 0xF, false);
+    return ((unsigned long long)h << 32) | l;
+}
+__device__ __forceinline__ unsigned long long fold4_max_u64(unsigned long long x) {
+    unsigned long long y = dpp_u64<0x124>(x);  // row_ror:4
+    x = x > y ? x : y;
+    y = dpp_u64<0x128>(x);                     // row_ror:8
+    return x > y ? x : y;
 }
 __device__ __forceinline__ float fold4_sum_f32(float x) {
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));
@@ -73,13 +98,19 @@ __device__ __forceinline__ float fold4_sum_f32(float x) {
 // SR = 1: single rounding (logit = bf16(base + fp32 dot)), DSW_FLAG_SINGLE_ROUND.
 // LK = 1 (bf16, small batches): the step's logits stay in the LDS ring slots
 // for the token shards when every group has a slot of its own.
-// FD = 4 (with LK = 1, up to 4 requests): only columns 0..3 of a tile's result
-// hold requests, so four tiles share one epilogue: tile j0 + q's column b
-// moves to lane column 4q + b (DPP row shifts), and each lane works on its
-// own tile and request.
-template <int A, int M, int DT, int SR, int LK = 0, int FD = 1>
+// FD = 4 (up to 4 requests, with LK = 1 or GU = 1): only columns 0..3 of a
+// tile's result hold requests, so four tiles share one epilogue: tile j0 + q's
+// column b moves to lane column 4q + b (DPP row shifts), and each lane works
+// on its own tile and request.
+// GU = 1: sampled requests draw by Gumbel-max (DSW_FLAG_GUMBEL): the epilogue
+// adds each row's noise to l / T and keeps the best score, the owner of a
+// request reduces the shards' {score, ~id} and publishes the token itself, so
+// every step takes two exchanges and no token shard scans its rows.
+template <int A, int M, int DT, int SR, int LK = 0, int FD = 1, int GU = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
-    static_assert(FD == 1 || (FD == 4 && LK == 1 && DT == 0 && A % 4 == 0), "fold: bf16, LDS-kept logits");
+    static_assert(FD == 1 || (FD == 4 && (LK == 1 || GU == 1) && DT == 0 && A % 4 == 0),
+                  "fold: bf16, logits kept in LDS or Gumbel-max");
+    static_assert(GU == 0 || (DT == 0 && SR == 0 && LK == 0), "Gumbel-max: bf16, double rounding");
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
     static_assert(A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles && (A % 2) == 0, "shape");
@@ -87,8 +118,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     extern __shared__ uint4 s_dyn[];  // [LDS weight tiles][ring slots]
 
     __shared__ uint32_t s_rkey[4][kMaxBatch];  // per wave and request: local key
-    __shared__ float s_rm[4][kMaxBatch];       // per wave: max logit (sampled requests)
-    __shared__ float s_rs[4][kMaxBatch];       // per wave: exp-sum relative to s_rm
+    // per wave and request: max logit and exp-sum relative to it (sampled
+    // requests, inverse CDF), or (Gumbel-max) the best {ord32(score), ~id}
+    __shared__ float s_rm[GU ? 1 : 4][GU ? 1 : kMaxBatch];
+    __shared__ float s_rs[GU ? 1 : 4][GU ? 1 : kMaxBatch];
+    __shared__ unsigned long long s_gk[GU ? 4 : 1][GU ? kMaxBatch : 1];
     __shared__ int s_prev[kMaxBatch];
     __shared__ unsigned long long s_rowb[kMaxBatch];  // request b's base logits of step 0 at this shard, in 16 B
     __shared__ int s_next[kMaxBatch];
@@ -441,6 +475,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             float bestv = -__builtin_inff();
             int bestj = -1;
             uint32_t bq01 = 0u, bq23 = 0u;
+            // Gumbel-max: the lane's best score and its row (-1: none finite)
+            float bestS = -__builtin_inff();
+            int bestR = -1;
 // Base logits of tile j for this lane's request: the slot, or s_junk (-inf)
 // for a tile beyond this wave's rows.
 #define DSW_BASE_PTR(j)                                                                          \
@@ -457,7 +494,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 // -- and the lane's running exp-sum of them, relative to its running
 // maximum, is updated (sampled lanes: sc > 0; it is rescaled when the
 // maximum grows).
-#define DSW_EPI(dv, j, bw, STORE)                                                                \
+#define DSW_EPI(dv, j, bw, STORE, NOISE)                                                         \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
         const bool live_ = (j) < nt_w;                                                           \
@@ -487,6 +524,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             } else {  /* in the slot: for the caller's copy, or read there by the token shard */ \
                 *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                       \
             }                                                                                    \
+            if constexpr (!GU) {                                                                 \
             /* finite, since mrun starts at -FLT_MAX: no -inf - -inf */                         \
             const float mn_ = fmaxf(mrun, tm_);                                                  \
             srun = srun * __builtin_amdgcn_exp2f((mrun - mn_) * sc) +                            \
@@ -496,27 +534,66 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                      __builtin_amdgcn_exp2f((bf16_hi(q23_) - mn_) * sc)));                        \
             mrun = mn_;                                                                          \
         }                                                                                        \
-        const bool gt_ = tm_ > bestv;                                                            \
-        bestv = gt_ ? tm_ : bestv;                                                               \
-        bestj = gt_ ? (j) : bestj;                                                               \
-        bq01 = gt_ ? q01_ : bq01;                                                                \
-        bq23 = gt_ ? q23_ : bq23;                                                                \
+        }                                                                                        \
+        if constexpr (GU) {                                                                      \
+            /* score l / T + G of the tile's four rows (sampled lanes; l itself */             \
+            /* otherwise), the first best kept; NOISE: some lane samples      */                 \
+            float s_[4] = {bf16_lo(q01_), bf16_hi(q01_), bf16_lo(q23_), bf16_hi(q23_)};          \
+            if (NOISE) {                                                                         \
+                uint32_t w_[4] = {(uint32_t)(v0 + rb_) >> 2, gc1, round, 0x47554D42u};          \
+                philox4(w_, (uint32_t)p.seed, (uint32_t)(p.seed >> 32));                         \
+                _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_)                                 \
+                    s_[e_] = samp ? s_[e_] * invT + gumbel_of_word(w_[e_]) : s_[e_];             \
+            }                                                                                    \
+            _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) {                                   \
+                const bool gt_ = s_[e_] > bestS;                                                 \
+                bestS = gt_ ? s_[e_] : bestS;                                                    \
+                bestR = gt_ ? rb_ + e_ : bestR;                                                  \
+            }                                                                                    \
+        } else {                                                                                 \
+            const bool gt_ = tm_ > bestv;                                                        \
+            bestv = gt_ ? tm_ : bestv;                                                           \
+            bestj = gt_ ? (j) : bestj;                                                           \
+            bq01 = gt_ ? q01_ : bq01;                                                            \
+            bq23 = gt_ ? q23_ : bq23;                                                            \
+        }                                                                                        \
     } while (0)
-#define DSW_EPI_G(dv, j, bw) DSW_EPI(dv, j, bw, 0)
-#define DSW_EPI_GS(dv, j, bw) DSW_EPI(dv, j, bw, 1)
+#define DSW_EPI_G(dv, j, bw) DSW_EPI(dv, j, bw, 0, 0)
+#define DSW_EPI_GS(dv, j, bw) DSW_EPI(dv, j, bw, 1, 0)
+#define DSW_EPI_N(dv, j, bw) DSW_EPI(dv, j, bw, 0, 1)
+#define DSW_EPI_NS(dv, j, bw) DSW_EPI(dv, j, bw, 1, 1)
             // Logits go out straight from the epilogue: to `logits` when asked
             // for, and for sampled requests in any case (to the workspace's
             // private blocks otherwise), where the token shard reads them back.
             // A group with nothing to store runs the epilogue without the
             // stores and without exp-sums (their branches cost a greedy batch
             // ~12% even when no lane stores).
+            // Gumbel-max: the logits go out only when the caller wants them, and
+            // the noise is drawn only in groups with a sampled request.
             const bool samp = bval && s_T[b] > 0.0f;
             const float sc = samp ? kLog2e / s_T[b] : 0.0f;
+            const float invT = samp ? 1.0f / s_T[b] : 1.0f;          // Gumbel-max: l / T
+            const uint32_t gc1 = ((uint32_t)k << 8) | (uint32_t)b;    // Gumbel-max: the noise counter
             const bool priv = p.logits == nullptr;  // the private blocks (wave-uniform)
             uint2* lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
             float mrun = -__FLT_MAX__, srun = 0.0f;  // the lane's running maximum and exp-sum
-            const bool stored = !priv || __builtin_amdgcn_ballot_w64(samp) != 0ull;
-            if constexpr (FD == 4) {
+            const bool anys = __builtin_amdgcn_ballot_w64(samp) != 0ull;
+            const bool stored = !priv || (!GU && anys);
+            if constexpr (GU) {
+                if (FD == 4) {
+                    if (stored) {
+                        if (anys) DSW_TILES_F4(DSW_EPI_NS); else DSW_TILES_F4(DSW_EPI_GS);
+                    } else {
+                        if (anys) DSW_TILES_F4(DSW_EPI_N); else DSW_TILES_F4(DSW_EPI_G);
+                    }
+                } else {
+                    if (stored) {
+                        if (anys) DSW_TILES(DSW_EPI_NS); else DSW_TILES(DSW_EPI_GS);
+                    } else {
+                        if (anys) DSW_TILES(DSW_EPI_N); else DSW_TILES(DSW_EPI_G);
+                    }
+                }
+            } else if constexpr (FD == 4) {
                 if (stored) {
                     DSW_TILES_F4(DSW_EPI_GS);
                 } else {
@@ -531,17 +608,32 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             }
 #undef DSW_EPI_G
 #undef DSW_EPI_GS
+#undef DSW_EPI_N
+#undef DSW_EPI_NS
 #undef DSW_EPI
 #undef DSW_BASE_PTR
+            if constexpr (GU) {
+                // {ord32(score), ~id} of the lane's best row, reduced over the
+                // request's lanes
+                unsigned long long gk = bestR >= 0 ? (((unsigned long long)ord32(bestS) << kIdxBits) |
+                                                      (unsigned long long)(kIdxMask - (uint32_t)(v0 + bestR)))
+                                                   : 0ull;
+                gk = column4_max_u64(gk);
+                if constexpr (FD == 4) gk = fold4_max_u64(gk);
+                if (g == 0 && qf == 0 && bval) s_gk[wave][b] = gk;
+            }
             // the first of the best tile's four rows with the best value
-            const int bi = bf16_lo(bq01) == bestv ? 0 : (bf16_hi(bq01) == bestv ? 1 : (bf16_lo(bq23) == bestv ? 2 : 3));
-            const int bestr = bestj >= 0 ? wrow0 + bestj * kTileRows + 4 * g + bi : -1;
-            uint32_t best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
-            // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
-            // (and, folded, the four tiles of each epilogue)
-            best = column4_max_u32(best);
-            if constexpr (FD == 4) best = fold4_max_u32(best);
-            if (g == 0 && qf == 0 && bval) s_rkey[wave][b] = best;
+            uint32_t best = 0u;
+            if constexpr (!GU) {
+                const int bi = bf16_lo(bq01) == bestv ? 0 : (bf16_hi(bq01) == bestv ? 1 : (bf16_lo(bq23) == bestv ? 2 : 3));
+                const int bestr = bestj >= 0 ? wrow0 + bestj * kTileRows + 4 * g + bi : -1;
+                best = bestr >= 0 ? local_key(__float_as_uint(bestv) >> 16, bestr) : 0u;
+                // the four lanes of request column n: rows 4g .. 4g+3 for g = 0..3
+                // (and, folded, the four tiles of each epilogue)
+                best = column4_max_u32(best);
+                if constexpr (FD == 4) best = fold4_max_u32(best);
+                if (g == 0 && qf == 0 && bval) s_rkey[wave][b] = best;
+            }
             if (!priv) {
                 // the caller's logits of the group's requests over this wave's
                 // rows, from the slot: four consecutive rows per lane, so that
@@ -563,8 +655,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 }
             }
             const float Tb = bval ? s_T[b] : 0.0f;
-            const bool on = Tb > 0.0f && best != 0u;
-            if (stored && __builtin_amdgcn_ballot_w64(on) != 0ull) {
+            const bool on = !GU && Tb > 0.0f && best != 0u;
+            if (!GU && stored && __builtin_amdgcn_ballot_w64(on) != 0ull) {
                 // exp-sum of this wave's logits of request n relative to its
                 // maximum: the four lanes' running sums, rescaled to it (a lane
                 // whose rows all lie past the vocabulary holds 0 at -FLT_MAX)
@@ -572,9 +664,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 float sw = on ? srun * __builtin_amdgcn_exp2f((mrun - mw) * sc) : 0.0f;
                 sw = column4_sum_f32(sw);
                 if constexpr (FD == 4) sw = fold4_sum_f32(sw);
-                if (g == 0 && qf == 0 && bval) {
-                    s_rm[wave][b] = mw;
-                    s_rs[wave][b] = sw;
+                if constexpr (!GU) {
+                    if (g == 0 && qf == 0 && bval) {
+                        s_rm[wave][b] = mw;
+                        s_rs[wave][b] = sw;
+                    }
                 }
             }
         }
@@ -584,15 +678,23 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         // ---- post: one key word (and exp-sum word) per request -----------
         walk_skew(p, c, k, 0);
         if (t < B) {
-            const uint32_t lk = max(max(s_rkey[0][t], s_rkey[1][t]), max(s_rkey[2][t], s_rkey[3][t]));
-            st_agent64(&bkey[(size_t)c * kMaxBatch + t], (global_key(lk, v0) << 28) | epoch);
-            if (s_T[t] > 0.0f) {
-                const float mc = local_key_logit(lk);
-                float sc = 0.0f;
-                const float scl = kLog2e / s_T[t];
-                for (int w = 0; w < 4; ++w)
-                    if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __builtin_amdgcn_exp2f((s_rm[w][t] - mc) * scl);
-                st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
+            if constexpr (GU) {
+                // Gumbel-max, every request: ord32(best score) in the key word,
+                // ~id in the second
+                const unsigned long long gk = max(max(s_gk[0][t], s_gk[1][t]), max(s_gk[2][t], s_gk[3][t]));
+                st_agent64(&bkey[(size_t)c * kMaxBatch + t], ((gk >> kIdxBits) << 28) | epoch);
+                st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((gk & kIdxMask) << 32) | epoch);
+            } else {
+                const uint32_t lk = max(max(s_rkey[0][t], s_rkey[1][t]), max(s_rkey[2][t], s_rkey[3][t]));
+                st_agent64(&bkey[(size_t)c * kMaxBatch + t], (global_key(lk, v0) << 28) | epoch);
+                if (s_T[t] > 0.0f) {
+                    const float mc = local_key_logit(lk);
+                    float sc = 0.0f;
+                    const float scl = kLog2e / s_T[t];
+                    for (int w = 0; w < 4; ++w)
+                        if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __builtin_amdgcn_exp2f((s_rm[w][t] - mc) * scl);
+                    st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
+                }
             }
         }
         DSW_TRACE(k, kTrPosted);
@@ -607,7 +709,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         kw_ = 0ull;                                                                              \
         sw_ = 0.0f;                                                                              \
         if (t < G) {                                                                             \
-            const bool samp_ = s_T[b_] > 0.0f;                                                   \
+            const bool samp_ = GU || s_T[b_] > 0.0f;  /* Gumbel-max: both words, always */       \
             const unsigned long long* pk_ = &bkey[(size_t)t * kMaxBatch + (b_)];                 \
             const unsigned long long* ps_ = &bsum[(size_t)t * kMaxBatch + (b_)];                 \
             unsigned it_ = 0;                                                                    \
@@ -687,10 +789,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             unsigned long long kw;
             float sw;
             DSW_READ_COLUMN(b, kw, sw);
+            if constexpr (GU) {  // the shard's {ord32(score), ~id}
+                kw = t < G ? ((kw << kIdxBits) | (unsigned long long)(__float_as_uint(sw) & kIdxMask)) : 0ull;
+            }
             unsigned long long win;
             DSW_BLOCK_MAX64(kw, win);
             if (s_abort) break;
-            if (!(s_T[b] > 0.0f)) {
+            if (GU || !(s_T[b] > 0.0f)) {
                 if (t == 0) {
                     const int tok = checked_token(key_index(win), V, status);
                     walk_skew(p, c, k, 1);
@@ -722,7 +827,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             }
             if (!ok) s_abort = 1;
             if (!ok) w = 0ull;
-            if (s_T[t] > 0.0f) {
+            if (!GU && s_T[t] > 0.0f) {
                 s_dec[t] = (unsigned)(w >> 24) & 0xFFu;
                 s_q[t] = __uint_as_float((uint32_t)(w >> 32));
             } else {
@@ -739,7 +844,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         // rows in vocabulary order (RL consecutive rows per lane) for the
         // first cumulative mass, relative to the shard's maximum, above the
         // owner's q.
-        if (any_samp) {
+        if (!GU && any_samp) {
             if (t < B && s_T[t] > 0.0f && (int)s_dec[t] == c)
                 s_tasks[atomicAdd(&s_ntask, 1)] = t;
             __syncthreads();

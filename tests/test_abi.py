@@ -258,25 +258,34 @@ def test_planner_batched_kernel(dsw):
     assert e.value.code == -11
 
 
-def test_planner_gumbel_max_stays_on_the_all_to_all_kernel(dsw):
+def test_planner_gumbel_max_kernels(dsw):
     d = fake_device(dsw)
     G = dsw.FLAG_GUMBEL
-    # Gumbel-max is the small-batch sampler: 4..16 requests keep the all-to-all kernel
-    for B, tile in ((1, 1), (3, 4), (4, 4), (8, 16), (16, 16)):
+    # bf16 rows, double rounding: the same kernels as the inverse CDF (the
+    # batched kernel from 4 requests); the shard layout is the same plan as
+    # without the flag, and up to 4 requests on the all-to-all kernels keep one
+    # step's noise per row in LDS
+    for B, tile in ((1, 1), (3, 4), (4, 256), (8, 256), (16, 256), (17, 256), (253, 256)):
         assert dsw.plan(d, 129_280, 5, B, flags=G).batch_tile == tile
-    assert dsw.plan(d, 129_280, 5, 8).batch_tile == 256  # without the flag: batched
-    # the shard layout is the same plan as without the flag; up to 4 requests
-    # keep one step's noise per row in LDS
+    for B in (4, 16, 253):
+        a, b = dsw.plan(d, 129_280, 5, B, flags=G), dsw.plan(d, 129_280, 5, B)
+        assert a.as_dict() == b.as_dict()
+    assert dsw.plan(d, 129_280, 5, 4, flags=G | dsw.FLAG_BATCHED).batch_tile == 256
     a, b = dsw.plan(d, 151_936, 7, 1, flags=G), dsw.plan(d, 151_936, 7, 1)
     keys = ("engine", "rows_per_wg", "tiles_per_wave", "reg_tiles", "lds_tiles", "stream_rows", "batch_tile")
     assert [a.as_dict()[k] for k in keys] == [b.as_dict()[k] for k in keys]
     assert a.static_lds_bytes == b.static_lds_bytes + 4 * 640
-    a16, b16 = dsw.plan(d, 151_936, 7, 16, flags=G), dsw.plan(d, 151_936, 7, 16, flags=dsw.FLAG_MFMA_GEMV)
+    a16, b16 = dsw.plan(d, 151_936, 7, 16, flags=G | dsw.FLAG_MFMA_GEMV), dsw.plan(d, 151_936, 7, 16,
+                                                                                   flags=dsw.FLAG_MFMA_GEMV)
     assert a16.static_lds_bytes == b16.static_lds_bytes
+    # int8 rows or single rounding: the all-to-all kernels, up to 16 requests
     assert dsw.plan(d, 248_320, 16, 2, w2_dtype=dsw.INT8, flags=G).batch_tile == 4
-    for B, flags in ((17, G), (253, G), (4, G | dsw.FLAG_BATCHED)):
+    assert dsw.plan(d, 129_280, 5, 8, w2_dtype=dsw.INT8, flags=G).batch_tile == 16
+    assert dsw.plan(d, 129_280, 5, 8, flags=G | dsw.FLAG_SINGLE_ROUND).batch_tile == 16
+    for B, flags, dt in ((17, G, dsw.INT8), (253, G | dsw.FLAG_SINGLE_ROUND, dsw.BF16),
+                         (4, G | dsw.FLAG_BATCHED, dsw.INT8)):
         with pytest.raises(dsw.DswError) as e:
-            dsw.plan(d, 129_280, 5, B, flags=flags)
+            dsw.plan(d, 129_280, 5, B, w2_dtype=dt, flags=flags)
         assert e.value.code == -11
 
 

@@ -364,18 +364,26 @@ def test_device_uniforms(dsw, V, B, gamma, flags):
     walker.close()
 
 
-# Gumbel-max sampling (DSW_FLAG_GUMBEL): every all-to-all kernel family, ragged
-# and full sizes; the oracle draws the same Philox noise from (seed, round counter)
+# Gumbel-max sampling (DSW_FLAG_GUMBEL): every kernel family, ragged and full
+# sizes; the oracle draws the same Philox noise from (seed, round counter)
 GUMBEL_CASES = [  # (V, B, gamma, flags, w2 dtype)
     (32_000, 1, 6, 0, "bf16"),        # one-request MFMA engine
     (60_001, 1, 3, 0, "bf16"),        # short walk: VALU engine, ragged vocabulary
     (4_097, 3, 5, 0, "bf16"),         # MFMA, batch tile 4, ragged
     (151_936, 1, 7, 0, "bf16"),       # the headline shape
     (248_320, 1, 4, 0, "bf16"),       # 12 register + 4 LDS tiles per wave
-    (151_936, 16, 3, 0, "bf16"),      # MFMA, batch tile 16 (no batched kernel with the flag)
+    (151_936, 16, 3, 8, "bf16"),      # MFMA, batch tile 16
     (60_000, 4, 4, 4, "bf16"),        # VALU, batch tile 4
     (129_280, 1, 4, 0, "int8"),       # int8 rows, VALU
     (60_000, 4, 3, 0, "int8"),        # int8 rows, MFMA
+    # the batched kernel: four tiles per epilogue up to 4 requests, ragged
+    # and empty shards, LDS and streamed tiles, full groups and many groups
+    (4_097, 4, 5, 0, "bf16"),
+    (151_936, 2, 3, 16, "bf16"),
+    (151_936, 16, 3, 0, "bf16"),
+    (60_000, 20, 4, 1, "bf16"),
+    (129_280, 64, 3, 0, "bf16"),
+    (32_000, 253, 2, 0, "bf16"),
 ]
 
 
@@ -415,6 +423,12 @@ def test_gumbel_max(dsw, V, B, gamma, flags, dt):
         say(rnd, "round counter", ctr, rep)
         checked += rep["sampled_exact_checked"]
         assert walker.round_counter() == ctr + 1
+        # the same round without logits out draws the same noise: same tokens
+        walker.set_round_counter(ctr)
+        tokens2, _ = walker.walk(W1d, W2d, base, anchor, T, None, w2_scale=sd)
+        torch.cuda.synchronize()
+        assert walker.status() == 0
+        assert np.array_equal(tokens2.cpu().numpy(), toks)
     assert checked > 0
     walker.close()
 
@@ -429,9 +443,15 @@ def test_gumbel_max_needs_a_seed_and_a_small_batch(dsw):
         walker.walk(bf16_dev(W1), bf16_dev(W2), base, anchor, T, None)
     assert e.value.code == -11
     walker.close()
-    with pytest.raises(dsw.DswError) as e:   # beyond 16 requests the batched kernel has no Gumbel-max
-        dsw.Walker(V, gamma_max=3, B_max=17, flags=dsw.FLAG_GUMBEL)
+    # beyond 16 requests only the batched kernel serves, and it has Gumbel-max
+    # for bf16 rows with double rounding only
+    with pytest.raises(dsw.DswError) as e:
+        dsw.Walker(V, gamma_max=3, B_max=17, flags=dsw.FLAG_GUMBEL, w2_dtype=dsw.INT8)
     assert e.value.code == -11
+    with pytest.raises(dsw.DswError) as e:
+        dsw.Walker(V, gamma_max=3, B_max=17, flags=dsw.FLAG_GUMBEL | dsw.FLAG_SINGLE_ROUND)
+    assert e.value.code == -11
+    dsw.Walker(V, gamma_max=3, B_max=17, flags=dsw.FLAG_GUMBEL).close()
 
 
 # HIP graph replays: nothing is cleared between replays (epochs come from the
