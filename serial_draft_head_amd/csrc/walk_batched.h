@@ -26,7 +26,8 @@
 //   scans its logits of request b (kept in LDS, or written out during the
 //   step: to `logits` if the caller wants them, else to the workspace), finds
 //   the token, and publishes it.  Greedy steps take two exchanges, sampled
-//   steps three.
+//   steps three (two with Gumbel-max, whose owner reduces {score, ~id} words
+//   and publishes the token itself).
 #pragma once
 #include "walk_kernel.h"
 
