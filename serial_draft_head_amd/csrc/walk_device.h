@@ -223,6 +223,18 @@ __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
 __device__ __forceinline__ unsigned long long ld_agent64(const unsigned long long* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two adjacent mailbox words (16-byte aligned) with one agent-scope load: each
+// word carries its own epoch, so a read that sees one half updated and not
+// the other is simply not ready yet.  The asm waits for its own load, so its
+// outputs are complete when it returns (and the wait also covers this wave's
+// earlier memory operations).
+__device__ __forceinline__ void ld_agent64_pair(const unsigned long long* p, unsigned long long& lo,
+                                                unsigned long long& hi) {
+    uint4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p));
+    lo = ((unsigned long long)v.y << 32) | v.x;
+    hi = ((unsigned long long)v.w << 32) | v.z;
+}
 __device__ __forceinline__ void st_agent64(unsigned long long* p, unsigned long long v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
