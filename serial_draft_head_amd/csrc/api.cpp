@@ -198,7 +198,6 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.fam_ctr = reinterpret_cast<unsigned*>(h->ws_mem + L.ctl) + dsw::kCtlFam;
     h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.ctl) + dsw::kCtlStatus;
     h->ws.bkey = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bkey);
-    h->ws.bsum = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bsum);
     h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
     h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
     // the batched kernel keeps the current step's logits of its sampled

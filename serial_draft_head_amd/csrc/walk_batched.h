@@ -214,8 +214,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     // of keys, exp-sums and tokens, and the decision words of the requests it owns
     for (int i = t; i < 2 * p.B_max; i += kBlock) {
         const size_t o = ((size_t)(i / p.B_max) * kMaxGrid + c) * kMaxBatch + i % p.B_max;
-        st_agent64(p.ws.bkey + o, 0ull);
-        st_agent64(p.ws.bsum + o, 0ull);
+        st_agent64(p.ws.bkey + 2 * o, 0ull);
+        st_agent64(p.ws.bkey + 2 * o + 1, 0ull);
         st_agent64(p.ws.btok + o, 0ull);
     }
     for (int i = t; i < 2 * OS; i += kBlock)
@@ -397,8 +397,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const unsigned seq = fam * (unsigned)p.gamma_max + (unsigned)k;
         const unsigned long long epoch = epoch_of(seq);
         const int q = (int)(seq & 1u);
-        unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch;
-        unsigned long long* bsum = p.ws.bsum + (size_t)q * kMaxGrid * kMaxBatch;
+        // workgroup c's words for request b: bkey[2 (c kMaxBatch + b)] (key), + 1 (exp-sum or ~id)
+        unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch * 2;
         unsigned long long* bown = p.ws.bdec + (size_t)q * kOwnWords;
 #define DSW_OWN(b_) (bown + (size_t)((b_) % G) * OS + (b_) / G)
         unsigned long long* btok = p.ws.btok + (size_t)q * kMaxGrid * kMaxBatch;  // [shard][request]
@@ -683,18 +683,19 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 // Gumbel-max, every request: ord32(best score) in the key word,
                 // ~id in the second
                 const unsigned long long gk = max(max(s_gk[0][t], s_gk[1][t]), max(s_gk[2][t], s_gk[3][t]));
-                st_agent64(&bkey[(size_t)c * kMaxBatch + t], ((gk >> kIdxBits) << 28) | epoch);
-                st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((gk & kIdxMask) << 32) | epoch);
+                st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t)], ((gk >> kIdxBits) << 28) | epoch);
+                st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t) + 1], ((gk & kIdxMask) << 32) | epoch);
             } else {
                 const uint32_t lk = max(max(s_rkey[0][t], s_rkey[1][t]), max(s_rkey[2][t], s_rkey[3][t]));
-                st_agent64(&bkey[(size_t)c * kMaxBatch + t], (global_key(lk, v0) << 28) | epoch);
+                st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t)], (global_key(lk, v0) << 28) | epoch);
                 if (s_T[t] > 0.0f) {
                     const float mc = local_key_logit(lk);
                     float sc = 0.0f;
                     const float scl = kLog2e / s_T[t];
                     for (int w = 0; w < 4; ++w)
                         if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __builtin_amdgcn_exp2f((s_rm[w][t] - mc) * scl);
-                    st_agent64(&bsum[(size_t)c * kMaxBatch + t], ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
+                    st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t) + 1],
+                               ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
                 }
             }
         }
@@ -704,30 +705,40 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         // (measured: V = 129,280, gamma 5, B = 16: 231.5 -> 229.7 us)
         __builtin_amdgcn_s_sleep(8);
 
-        // read column b of every workgroup's row: kw, sw of shard t (t < G)
+        // read column b of every workgroup's row: kw, sw of shard t (t < G); a
+        // request with a second word takes both with one 16-byte load per poll
 #define DSW_READ_COLUMN(b_, kw_, sw_)                                                            \
     do {                                                                                         \
         kw_ = 0ull;                                                                              \
         sw_ = 0.0f;                                                                              \
         if (t < G) {                                                                             \
             const bool samp_ = GU || s_T[b_] > 0.0f;  /* Gumbel-max: both words, always */       \
-            const unsigned long long* pk_ = &bkey[(size_t)t * kMaxBatch + (b_)];                 \
-            const unsigned long long* ps_ = &bsum[(size_t)t * kMaxBatch + (b_)];                 \
+            const unsigned long long* pk_ = &bkey[2 * ((size_t)t * kMaxBatch + (b_))];           \
             unsigned it_ = 0;                                                                    \
-            bool gotk_ = false, gots_ = !samp_;                                                  \
-            for (;;) {                                                                           \
-                if (!gotk_) {                                                                    \
+            if (samp_) {                                                                         \
+                for (;;) {                                                                       \
+                    unsigned long long k_, s_;                                                   \
+                    ld_agent64_pair(pk_, k_, s_);                                                \
+                    if ((k_ & kEpochMod) == epoch && (s_ & kEpochMod) == epoch) {                \
+                        kw_ = k_ >> 28;                                                          \
+                        sw_ = __uint_as_float((uint32_t)(s_ >> 32));                             \
+                        break;                                                                   \
+                    }                                                                            \
+                    if (++it_ >= p.spin_limit) { latch(status, kStatusTimeout); s_abort = 1; break; } \
+                    if ((it_ & 255u) == 0u && ld_agent(status) != 0u) { s_abort = 1; break; }    \
+                    __builtin_amdgcn_s_sleep(1);                                                 \
+                }                                                                                \
+            } else {                                                                             \
+                for (;;) {                                                                       \
                     const unsigned long long w_ = ld_agent64(pk_);                               \
-                    if ((w_ & kEpochMod) == epoch) { kw_ = w_ >> 28; gotk_ = true; }             \
+                    if ((w_ & kEpochMod) == epoch) {                                             \
+                        kw_ = w_ >> 28;                                                          \
+                        break;                                                                   \
+                    }                                                                            \
+                    if (++it_ >= p.spin_limit) { latch(status, kStatusTimeout); s_abort = 1; break; } \
+                    if ((it_ & 255u) == 0u && ld_agent(status) != 0u) { s_abort = 1; break; }    \
+                    __builtin_amdgcn_s_sleep(1);                                                 \
                 }                                                                                \
-                if (!gots_) {                                                                    \
-                    const unsigned long long w_ = ld_agent64(ps_);                               \
-                    if ((w_ & kEpochMod) == epoch) { sw_ = __uint_as_float((uint32_t)(w_ >> 32)); gots_ = true; } \
-                }                                                                                \
-                if (gotk_ && gots_) break;                                                       \
-                if (++it_ >= p.spin_limit) { latch(status, kStatusTimeout); s_abort = 1; break; } \
-                if ((it_ & 255u) == 0u && ld_agent(status) != 0u) { s_abort = 1; break; }        \
-                __builtin_amdgcn_s_sleep(1);                                                     \
             }                                                                                    \
         }                                                                                        \
     } while (0)

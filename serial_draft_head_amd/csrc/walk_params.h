@@ -73,10 +73,12 @@ struct Workspace {
     unsigned* fam_ctr;             // ctl[1..2]  completed launches per kernel family (the epochs)
     unsigned* status;              // ctl[3]  latched kStatus* bits
     // batched kernel (requests owned by workgroups): every workgroup posts one
-    // key word (and one exp-sum word) per request; the owner of request b
-    // reads column b and publishes a decision; a token shard publishes tokens
-    unsigned long long* bkey;      // [2][kMaxGrid][kMaxBatch]  key << 28 | epoch
-    unsigned long long* bsum;      // [2][kMaxGrid][kMaxBatch]  exp-sum bits << 32 | epoch
+    // key word and next to it one exp-sum word per request (a reader takes both
+    // with one 16-byte load); the owner of request b reads column b and
+    // publishes a decision; a token shard publishes tokens
+    unsigned long long* bkey;      // [2][kMaxGrid][kMaxBatch][2]  key << 28 | epoch, then exp-sum
+                                   // bits << 32 | epoch (Gumbel-max: ord32(score) << 28 | epoch,
+                                   // then ~id << 32 | epoch)
     unsigned long long* bdec;      // [2][kOwnWords]  per owner workgroup c, a region of
                                    // owner_stride(G) words (whole 128-byte lines, one
                                    // writer each; 1 word for up to 16 requests); request
@@ -102,7 +104,7 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, tokw, ctl, bkey, bsum, bdec, btok, total;
+    size_t mail, tokw, ctl, bkey, bdec, btok, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -111,8 +113,7 @@ inline WorkspaceLayout workspace_layout() {
     L.mail = o;      o = up(o + 2 * (size_t)kMaxGrid * kMailWords * 8);
     L.tokw = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatchPersistent * 8);
     L.ctl = o;       o = up(o + 16);
-    L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
-    L.bsum = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
+    L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 16);
     L.bdec = o;      o = up(o + 2 * (size_t)kOwnWords * 8);
     L.btok = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.total = o;

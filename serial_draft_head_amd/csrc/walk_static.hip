@@ -99,7 +99,6 @@ dsw::Workspace workspace_at(unsigned char* base) {
     ws.fam_ctr = reinterpret_cast<unsigned*>(base + L.ctl) + dsw::kCtlFam;
     ws.status = reinterpret_cast<unsigned*>(base + L.ctl) + dsw::kCtlStatus;
     ws.bkey = reinterpret_cast<unsigned long long*>(base + L.bkey);
-    ws.bsum = reinterpret_cast<unsigned long long*>(base + L.bsum);
     ws.bdec = reinterpret_cast<unsigned long long*>(base + L.bdec);
     ws.btok = reinterpret_cast<unsigned long long*>(base + L.btok);
     ws.blog = reinterpret_cast<uint16_t*>(base + kWsBytes);
