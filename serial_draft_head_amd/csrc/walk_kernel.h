@@ -158,11 +158,13 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
     constexpr bool kGru = CELL == 1 || kDomino;
     constexpr bool kGated = CELL == 3;                          // the whole state in every workgroup
     constexpr bool kShard = kCell && !kGated;                   // the state spread over the workgroups
-    // One request (not a recurrent head, whose state words follow the key):
+    // One request (not the gated head, which polls before forming its gates):
     // the second word sits next to the key, and a reader fetches both with one
     // 16-byte load -- half the polls through the fabric (V = 151,936, gamma
-    // 16, mixed T: 106.2 -> 99.9 us; Gumbel-max: 83.0 -> 76.9 us).
-    constexpr bool kPair = NB == 1 && !kCell;
+    // 16, mixed T: 106.2 -> 99.9 us; Gumbel-max: 83.0 -> 76.9 us).  The
+    // recurrent heads' state words follow at 2 .. 5.
+    constexpr bool kPair = NB == 1 && !kGated;
+    constexpr int kStateWord = 2;
     constexpr int kSumWord = kPair ? 1 : kMailSums;
     constexpr int kGates = kGru ? 3 : 1;                         // cell rows per input, per element
     static_assert(CELL >= 0 && CELL <= 4, "cell");
@@ -855,7 +857,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                     hn = tanhf((acc[0] + cb[0]) + gh[0]);
                 }
                 if (lane == 0) {
-                    st_agent64(&box[1 + wave], ((unsigned long long)__float_as_uint(hn) << 32) | epoch);
+                    st_agent64(&box[kStateWord + wave], ((unsigned long long)__float_as_uint(hn) << 32) | epoch);
                     if (p.states != nullptr) p.states[(size_t)k * kRank + j] = hn;
                 }
             }
@@ -865,7 +867,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_kernel(WalkParams p) {
                 // as before the key polls: nothing can have arrived this early
                 // (measured: GRU head, V = 151,936, gamma 7: 58.8 -> 58.1 us)
                 __builtin_amdgcn_s_sleep(8);
-                const unsigned long long* sbox = mail_q + (size_t)(t % G) * kMailWords + 1 + t / G;
+                const unsigned long long* sbox = mail_q + (size_t)(t % G) * kMailWords + kStateWord + t / G;
                 unsigned it = 0;
                 unsigned long long v = 0ull;
                 bool ok = true;
