@@ -16,7 +16,7 @@ extern "C" const void* dsw_internal_mfma_kernel_b4(int reg_tiles, int max_tiles)
 extern "C" const void* dsw_internal_mfma_kernel_b16(int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_mfma_i8_kernel(int batch_tile, int reg_tiles, int max_tiles);
 extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round,
-                                                   int keep, int fold, int gumbel);
+                                                   int fold, int gumbel);
 // the same all-to-all kernels with Gumbel-max sampling
 extern "C" const void* dsw_internal_walk_kernel_gumbel(int reg_slots, int batch_tile, int w2_dtype);
 extern "C" const void* dsw_internal_mfma_kernel_b1_gumbel(int reg_tiles, int max_tiles);
@@ -55,12 +55,9 @@ const void* kernel_for(const dsw_plan_info& pl, bool gumbel, int cell, bool sing
         return cell <= 4 ? lookup[cell - 1](pl.reg_tiles, pl.max_tiles) : nullptr;
     }
     if (pl.batch_tile == dsw::kMaxBatch) {
-        // the step's logits stay in LDS when every group has a ring slot of its
-        // own; then up to 4 requests share one epilogue per four tiles.
-        // Gumbel-max needs no logits kept (no token shard scans them).
-        const bool keep = !gumbel && (B + dsw::kGroup - 1) / dsw::kGroup <= pl.ring_slots - 1;
-        return dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single, keep,
-                                           (keep || gumbel) && B <= 4, gumbel);
+        // up to 4 requests share one epilogue per four tiles (bf16, double
+        // rounding)
+        return dsw_internal_batched_kernel(pl.w2_dtype, pl.reg_tiles, pl.max_tiles, single, B <= 4, gumbel);
     }
     if (pl.engine == DSW_ENGINE_VALU)
         return gumbel ? dsw_internal_walk_kernel_gumbel(pl.reg_slots, pl.batch_tile, pl.w2_dtype)
@@ -199,9 +196,8 @@ extern "C" int dsw_create(dsw_handle_t* out, int device, int V, int r, int gamma
     h->ws.status = reinterpret_cast<unsigned*>(h->ws_mem + L.ctl) + dsw::kCtlStatus;
     h->ws.bkey = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bkey);
     h->ws.bdec = reinterpret_cast<unsigned long long*>(h->ws_mem + L.bdec);
-    h->ws.btok = reinterpret_cast<unsigned long long*>(h->ws_mem + L.btok);
-    // the batched kernel keeps the current step's logits of its sampled
-    // requests here for the token shards
+    // the batched kernel writes the current step's logits of its sampled
+    // requests here for their owners
     h->blog_mem = nullptr;
     if (B_max >= dsw::kBatchedFrom || (flags & DSW_FLAG_BATCHED)) {
         if (hipMalloc(&h->blog_mem, dsw::batched_logits_bytes(V, B_max)) != hipSuccess) {

@@ -199,11 +199,11 @@ static const int kBShapesI8[][2] = {{8, 8}, {8, 12}};
 static const int kBStreamShape[2] = {0, 12};
 static int batched_static_lds(int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
-    // per-request keys, maxima and exp-sums per wave; tokens, temperatures,
-    // token shards and their masses q; base-row offsets (8 bytes); tasks; the
-    // shard masses and scales; int8 row scales; the -inf base rows of dead
-    // tiles (4 waves x 64 lanes x 8 bytes) and a few scalars; the trace
-    return 4 * kMaxBatch * 4 * 3 + 5 * kMaxBatch * 4 + kMaxBatch * 8 + 2 * kMaxGrid * 4 + kMaxBatch * 4 +
+    // per-request keys, maxima and exp-sums per wave; tokens (two) and
+    // temperatures; base-row offsets (8 bytes); the shard masses, scales and
+    // maxima; int8 row scales; the -inf base rows of dead tiles (4 waves x 64
+    // lanes x 8 bytes) and a few scalars; the trace
+    return 4 * kMaxBatch * 4 * 3 + 3 * kMaxBatch * 4 + kMaxBatch * 8 + 3 * kMaxGrid * 4 +
            (i8 ? 4 * rpad : 0) + 4 * 64 * 8 + 1024 + kTraceLds;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }

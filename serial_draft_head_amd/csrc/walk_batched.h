@@ -20,14 +20,13 @@
 // * Exchange: an all-to-all of B keys per workgroup would read B * 2 KiB per
 //   workgroup and step.  Here request b is owned by workgroup b % G: every
 //   workgroup stores its B key words (and exp-sum words) in one row, the owner
-//   reads column b, and publishes in one word the token (greedy), or the
-//   shard whose mass holds u*Z together with the mass that shard has to
-//   accumulate, in its own scale, before the token (sampled).  That shard
-//   scans its logits of request b (kept in LDS, or written out during the
-//   step: to `logits` if the caller wants them, else to the workspace), finds
-//   the token, and publishes it.  Greedy steps take two exchanges, sampled
-//   steps three (two with Gumbel-max, whose owner reduces {score, ~id} words
-//   and publishes the token itself).
+//   reads column b and publishes the token in one word.  Greedy: the best key.
+//   Sampled: the owner finds the shard whose mass holds u*Z and the mass that
+//   shard accumulates, in its own scale, before the token, reads that shard's
+//   logits of request b (every shard writes the logits of its groups with a
+//   sampled request to the workspace with agent-scope stores before its key
+//   words) and scans them for the token.  Gumbel-max: the owner reduces
+//   {score, ~id} words.  Every step takes two exchanges.
 #pragma once
 #include "walk_kernel.h"
 
@@ -36,11 +35,8 @@ namespace dsw {
 constexpr int kSlotUBytes = kGroup * kRowChunks * 16;  // u rows of one group: 8 KiB
 // Decision words carry a 24-bit epoch, (seq mod 2^23) + 1: never 0, and two
 // steps share it only 2^23 steps apart (the words a reader can meet are fewer
-// than 2 gamma_max <= 8192 steps apart).  Above it: a greedy request's token
-// (bits 24..43); a sampled request's token shard (bits 24..31) and, as fp32
-// bits 32..63, the mass q that shard accumulates over its rows, relative to
-// its own maximum, before the token: (u*Z - mass of the shards before it) /
-// exp((its max - M) / T).
+// than 2 gamma_max <= 8192 steps apart).  Above it: the request's token
+// (bits 24..43).
 constexpr unsigned long long kDecEpochMask = 0xFFFFFFull;
 __device__ __forceinline__ unsigned long long dec_epoch(unsigned seq) { return (seq & 0x7FFFFFu) + 1u; }
 
@@ -97,21 +93,18 @@ __device__ __forceinline__ float fold4_sum_f32(float x) {
 }
 
 // SR = 1: single rounding (logit = bf16(base + fp32 dot)), DSW_FLAG_SINGLE_ROUND.
-// LK = 1 (bf16, small batches): the step's logits stay in the LDS ring slots
-// for the token shards when every group has a slot of its own.
-// FD = 4 (up to 4 requests, with LK = 1 or GU = 1): only columns 0..3 of a
-// tile's result hold requests, so four tiles share one epilogue: tile j0 + q's
-// column b moves to lane column 4q + b (DPP row shifts), and each lane works
-// on its own tile and request.
+// FD = 4 (bf16, up to 4 requests): only columns 0..3 of a tile's result hold
+// requests, so four tiles share one epilogue: tile j0 + q's column b moves to
+// lane column 4q + b (DPP row shifts), and each lane works on its own tile and
+// request.
 // GU = 1: sampled requests draw by Gumbel-max (DSW_FLAG_GUMBEL): the epilogue
 // adds each row's noise to l / T and keeps the best score, the owner of a
 // request reduces the shards' {score, ~id} and publishes the token itself, so
 // every step takes two exchanges and no token shard scans its rows.
-template <int A, int M, int DT, int SR, int LK = 0, int FD = 1, int GU = 0>
+template <int A, int M, int DT, int SR, int FD = 1, int GU = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
-    static_assert(FD == 1 || (FD == 4 && (LK == 1 || GU == 1) && DT == 0 && A % 4 == 0),
-                  "fold: bf16, logits kept in LDS or Gumbel-max");
-    static_assert(GU == 0 || (DT == 0 && SR == 0 && LK == 0), "Gumbel-max: bf16, double rounding");
+    static_assert(FD == 1 || (FD == 4 && DT == 0 && A % 4 == 0), "fold: bf16");
+    static_assert(GU == 0 || (DT == 0 && SR == 0), "Gumbel-max: bf16, double rounding");
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
     static_assert(A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles && (A % 2) == 0, "shape");
@@ -128,17 +121,16 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ unsigned long long s_rowb[kMaxBatch];  // request b's base logits of step 0 at this shard, in 16 B
     __shared__ int s_next[kMaxBatch];
     __shared__ float s_T[kMaxBatch];
-    __shared__ unsigned s_dec[kMaxBatch];      // sampled requests: the token shard
-    __shared__ float s_q[kMaxBatch];           // sampled requests: the token shard's mass before the token
     __shared__ float s_S[kMaxGrid];
     __shared__ float s_E[kMaxGrid];
+    __shared__ float s_M[kMaxGrid];            // owner: the shards' max logits of the request
+    __shared__ float s_wsum[4];                // owner: per-wave mass totals of the token search
+    __shared__ uint32_t s_wfirst[4], s_wlast[4];
     __shared__ float s_scale[kI8 ? RPAD : 1];
-    __shared__ int s_tasks[kMaxBatch];
     __shared__ uint2 s_junk[4][64];            // base logits (-inf) of tiles beyond a wave's rows
     __shared__ unsigned long long s_red64[4];
     __shared__ int s_own;
     __shared__ float s_qown;
-    __shared__ int s_ntask;
     __shared__ unsigned s_round;
     __shared__ unsigned s_fam;
     __shared__ int s_abort;
@@ -177,10 +169,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     // 224 -> 216 us against their 16 words in one line).
     const int OS = owner_stride(G);
     const int D = p.ring;
-    // every group of the step has a ring slot of its own (no DMA reuses one
-    // before the next step): the step's logits stay in the slots, where the
-    // token shards read them, instead of going out to memory and back
-    const bool lds_keep = LK != 0 && (B + kGroup - 1) / kGroup <= D - 1;
     const bool aligned = p.aligned != 0;
     const bool al4 = (V & 3) == 0;  // 8-byte stores of 4 logits (rows 4g .. 4g+3)
     const int P = 2 + (aligned ? CPR / 16 : 0);  // DMA instructions per wave and group
@@ -211,12 +199,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     s_junk[t >> 6][t & 63] = make_uint2(0xFF80FF80u, 0xFF80FF80u);  // -inf base logits
     // every word this workgroup posts in this launch, both parities, starts at
     // 0 (the barriers before the first post order these stores first): its row
-    // of keys, exp-sums and tokens, and the decision words of the requests it owns
+    // of keys and exp-sums, and the decision words of the requests it owns
     for (int i = t; i < 2 * p.B_max; i += kBlock) {
         const size_t o = ((size_t)(i / p.B_max) * kMaxGrid + c) * kMaxBatch + i % p.B_max;
         st_agent64(p.ws.bkey + 2 * o, 0ull);
         st_agent64(p.ws.bkey + 2 * o + 1, 0ull);
-        st_agent64(p.ws.btok + o, 0ull);
     }
     for (int i = t; i < 2 * OS; i += kBlock)
         st_agent64(p.ws.bdec + (size_t)(i / OS) * kOwnWords + (size_t)c * OS + i % OS, 0ull);
@@ -401,7 +388,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         unsigned long long* bkey = p.ws.bkey + (size_t)q * kMaxGrid * kMaxBatch * 2;
         unsigned long long* bown = p.ws.bdec + (size_t)q * kOwnWords;
 #define DSW_OWN(b_) (bown + (size_t)((b_) % G) * OS + (b_) / G)
-        unsigned long long* btok = p.ws.btok + (size_t)q * kMaxGrid * kMaxBatch;  // [shard][request]
 
         // group gq's u rows and base logits into ring slot gq % D.  Each lane
         // names its own source; the wave's 64 chunks land contiguously.
@@ -488,13 +474,14 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 // Branch-free, so that the matrix cores' work and this VALU work can be
 // interleaved; a tile beyond this wave's rows has -inf base logits and its
 // logits lose every max.  bw: the tile's four base logits.  STORE (a
-// constant): the logits go out -- to this group's private block `lpriv` (the
-// wave's 64 lanes write 512 contiguous bytes), or, when the caller wants
-// them, back into the slot over the base logits (a tile beyond the wave's
-// rows rewrites s_junk's -inf), copied out row-contiguously after the tiles
-// -- and the lane's running exp-sum of them, relative to its running
-// maximum, is updated (sampled lanes: sc > 0; it is rescaled when the
-// maximum grows).
+// constant): the logits go out -- when the caller wants them, back into the
+// slot over the base logits (a tile beyond the wave's rows rewrites s_junk's
+// -inf), copied out row-contiguously after the tiles; otherwise, in a group
+// with a sampled request, to the group's private block `lblog` with
+// agent-scope stores (the wave's 64 lanes write 512 contiguous bytes); the
+// owners of sampled requests read them from either -- and the lane's running
+// exp-sum of them, relative to its running maximum, is updated (sampled
+// lanes: sc > 0; it is rescaled when the maximum grows).
 #define DSW_EPI(dv, j, bw, STORE, NOISE)                                                         \
     do {                                                                                         \
         const int rb_ = wrow0 + (j) * kTileRows + 4 * g;                                         \
@@ -519,11 +506,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         const uint32_t q23_ = pack_bf16_rne(bf16_lo(bw_.y) + x2_, bf16_hi(bw_.y) + x3_);         \
         const float tm_ = fmaxf(fmaxf(bf16_lo(q01_), bf16_hi(q01_)), fmaxf(bf16_lo(q23_), bf16_hi(q23_))); \
         if (STORE) {                                                                             \
-            /* wave-uniform branches only: no exec masks in the tiles */                        \
-            if (FD == 1 && priv && !lds_keep) {                                                  \
-                if (live_) lpriv[(j) * 64] = make_uint2(q01_, q23_);                             \
-            } else {  /* in the slot: for the caller's copy, or read there by the token shard */ \
-                *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);                                       \
+            if (priv) {  /* wave-uniform */                                                      \
+                if (tolog && live_)  /* for the owners' token search */                         \
+                    st_agent64(&lblog[(j) * 64], ((unsigned long long)q23_ << 32) | q01_);       \
+            } else {                                                                             \
+                *DSW_BASE_PTR(j) = make_uint2(q01_, q23_);  /* for the caller's copy */          \
             }                                                                                    \
             if constexpr (!GU) {                                                                 \
             /* finite, since mrun starts at -FLT_MAX: no -inf - -inf */                         \
@@ -564,22 +551,26 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #define DSW_EPI_N(dv, j, bw) DSW_EPI(dv, j, bw, 0, 1)
 #define DSW_EPI_NS(dv, j, bw) DSW_EPI(dv, j, bw, 1, 1)
             // Logits go out straight from the epilogue: to `logits` when asked
-            // for, and for sampled requests in any case (to the workspace's
-            // private blocks otherwise), where the token shard reads them back.
-            // A group with nothing to store runs the epilogue without the
-            // stores and without exp-sums (their branches cost a greedy batch
-            // ~12% even when no lane stores).
+            // for (with agent-scope stores in a group with a sampled request),
+            // else for such groups to the workspace's private blocks, where the
+            // owners read them back.  A group with
+            // nothing to store runs the epilogue without the stores and
+            // without exp-sums (their branches cost a greedy batch ~12% even
+            // when no lane stores).
             // Gumbel-max: the logits go out only when the caller wants them, and
             // the noise is drawn only in groups with a sampled request.
             const bool samp = bval && s_T[b] > 0.0f;
             const float sc = samp ? kLog2e / s_T[b] : 0.0f;
             const float invT = samp ? 1.0f / s_T[b] : 1.0f;          // Gumbel-max: l / T
             const uint32_t gc1 = ((uint32_t)k << 8) | (uint32_t)b;    // Gumbel-max: the noise counter
-            const bool priv = p.logits == nullptr;  // the private blocks (wave-uniform)
-            uint2* lpriv = reinterpret_cast<uint2*>(p.ws.blog) + (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + lane;
+            const bool priv = p.logits == nullptr;  // no caller logits (wave-uniform)
+            // this lane's column of the group's private block: tile j at 64 j
+            unsigned long long* lblog = reinterpret_cast<unsigned long long*>(p.ws.blog) +
+                                        (((size_t)c * NG + grp) * 4 + wave) * TW * 64 + g * 16 + nreq;
             float mrun = -__FLT_MAX__, srun = 0.0f;  // the lane's running maximum and exp-sum
             const bool anys = __builtin_amdgcn_ballot_w64(samp) != 0ull;
-            const bool stored = !priv || (!GU && anys);
+            const bool tolog = !GU && anys;  // owners read these logits (wave-uniform)
+            const bool stored = !priv || tolog;
             if constexpr (GU) {
                 if (FD == 4) {
                     if (stored) {
@@ -638,19 +629,30 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             if (!priv) {
                 // the caller's logits of the group's requests over this wave's
                 // rows, from the slot: four consecutive rows per lane, so that
-                // the wave's stores to one request's row are contiguous
+                // the wave's stores to one request's row are contiguous; with
+                // agent-scope stores when an owner reads them
                 const int rend = min(wrow0 + nt_w * kTileRows, nrows);
                 for (int nn = 0; nn < kGroup && grp * kGroup + nn < B; ++nn) {
                     uint16_t* dst = p.logits + ((size_t)(grp * kGroup + nn) * gamma + k) * V + v0;
                     for (int r0 = wrow0 + 4 * lane; r0 < rend; r0 += 256) {
                         const uint2 v = *reinterpret_cast<const uint2*>(sb + (nn * CPR + ((r0 >> 3) ^ nn)) * 8 + (r0 & 7));
                         if (al4 && r0 + 4 <= rend) {
-                            *reinterpret_cast<uint2*>(dst + r0) = v;
+                            if (tolog)
+                                st_agent64(reinterpret_cast<unsigned long long*>(dst + r0),
+                                           ((unsigned long long)v.y << 32) | v.x);
+                            else
+                                *reinterpret_cast<uint2*>(dst + r0) = v;
                         } else {
                             const uint32_t l4[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (r0 + i < rend) dst[r0 + i] = (uint16_t)l4[i];
+                            for (int i = 0; i < 4; ++i) {
+                                if (r0 + i < rend) {
+                                    if (tolog)
+                                        st_agent16(dst + r0 + i, (uint16_t)l4[i]);
+                                    else
+                                        dst[r0 + i] = (uint16_t)l4[i];
+                                }
+                            }
                         }
                     }
                 }
@@ -673,6 +675,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 }
             }
         }
+        // the logits' agent-scope stores (private blocks or the caller's
+        // logits) complete before any key word of this step is posted
+        if (!GU && any_samp) wait_vmcnt(0);
         __syncthreads();
         DSW_TRACE(k, kTrGemvDone);
 
@@ -743,8 +748,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         }                                                                                        \
     } while (0)
 
-        // shard masses S_t of sampled request b_ into s_S (and their scales
-        // exp((m_t - M) / T) into s_E), then wave 0 finds the first shard with
+        // shard masses S_t of sampled request b_ into s_S (their scales
+        // exp((m_t - M) / T) into s_E, their maxima m_t into s_M), then wave 0
+        // finds the first shard with
         // positive mass whose prefix exceeds u*Z (else the last with positive
         // mass): s_own, and s_qown = (u*Z - mass before it) / its scale.
 #define DSW_OWNER_SHARD(b_, kw_, sw_, M_)                                                        \
@@ -754,6 +760,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                              : 0.0f;                                                             \
         s_S[t] = (t < G && kw_ != 0ull) ? sw_ * e_ : 0.0f;                                       \
         s_E[t] = e_;                                                                             \
+        s_M[t] = (t < G && kw_ != 0ull) ? key_logit(kw_) : 0.0f;                                 \
         __syncthreads();                                                                         \
         if (wave == 0) {                                                                         \
             const float4 m4_ = reinterpret_cast<const float4*>(s_S)[lane];                       \
@@ -815,10 +822,76 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 }
             } else {
                 DSW_OWNER_SHARD(b, kw, sw, key_logit(win));
+                // The token: shard s_own's logits of request b, read back from
+                // the caller's logits or its private block (written before its
+                // key word), scanned in
+                // vocabulary order for the first cumulative mass, relative to
+                // the shard's maximum, above s_qown -- rows 4t .. 4t+3 per
+                // thread; no crossing row (rounding): the last row with mass.
+                const int own = s_own;
+                const int ov0 = max(own, 0) * R;
+                const int onr = own < 0 ? 0 : max(0, min(V, ov0 + R) - ov0);
+                const float sc2 = kLog2e / s_T[b];
+                const float mo = s_M[max(own, 0)];
+                const float qo = s_qown;
+                const int r0 = 4 * t;
+                float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (r0 < onr) {
+                    unsigned long long v;
+                    if (p.logits != nullptr) {
+                        // row ov0 + r0 of request b's step-k logits (8-byte
+                        // aligned when 4 | V: ov0 and r0 are multiples of 4)
+                        const uint16_t* src = p.logits + ((size_t)b * gamma + k) * V + ov0 + r0;
+                        if (al4) {
+                            v = ld_agent64(reinterpret_cast<const unsigned long long*>(src));
+                        } else {
+                            v = 0ull;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (r0 + i < onr) v |= (unsigned long long)ld_agent16(src + i) << (16 * i);
+                        }
+                    } else {
+                        // row r0 of the shard: wave r0 / (16 TW), tile rem / 16,
+                        // lane 16 ((rem / 4) % 4) + b % 16 of that block, its
+                        // four logits
+                        const int wv = r0 / (TW * kTileRows), rem = r0 - wv * TW * kTileRows;
+                        v = ld_agent64(reinterpret_cast<const unsigned long long*>(p.ws.blog) +
+                                       ((((size_t)own * NG + (b >> 4)) * 4 + wv) * TW + (rem >> 4)) * 64 +
+                                       ((rem >> 2) & 3) * 16 + (b & 15));
+                    }
+                    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+                    const float l4[4] = {bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        w4[i] = r0 + i < onr ? __builtin_amdgcn_exp2f((l4[i] - mo) * sc2) : 0.0f;
+                }
+                const float part = ((w4[0] + w4[1]) + w4[2]) + w4[3];
+                const float incl = wave_incl_scan_dpp(part);
+                if (lane == 63) s_wsum[wave] = incl;
+                __syncthreads();
+                float run = incl - part;
+                for (int w = 0; w < wave; ++w) run += s_wsum[w];
+                uint32_t first = 0u, lastw = 0u;  // row + 1, 0 = none
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    run += w4[i];
+                    if (first == 0u && w4[i] > 0.0f && run > qo) first = (uint32_t)(r0 + i) + 1u;
+                    if (w4[i] > 0.0f) lastw = (uint32_t)(r0 + i) + 1u;
+                }
+                const uint32_t fmin = wave_max_u32(first ? 0xFFFFFFFFu - first : 0u);
+                const uint32_t lmax = wave_max_u32(lastw);
+                if (lane == 0) {
+                    s_wfirst[wave] = fmin;
+                    s_wlast[wave] = lmax;
+                }
+                __syncthreads();
                 if (t == 0) {
+                    const uint32_t f = max(max(s_wfirst[0], s_wfirst[1]), max(s_wfirst[2], s_wfirst[3]));
+                    const uint32_t l = max(max(s_wlast[0], s_wlast[1]), max(s_wlast[2], s_wlast[3]));
+                    const int row = f ? (int)(0xFFFFFFFFu - f) - 1 : (l ? (int)l - 1 : -1);
+                    const int tok = checked_token(row < 0 ? -1 : ov0 + row, V, status);
                     walk_skew(p, c, k, 1);
-                    st_agent64(DSW_OWN(b), ((unsigned long long)__float_as_uint(s_qown) << 32) |
-                                               ((unsigned long long)(unsigned)max(s_own, 0) << 24) | dep);
+                    st_agent64(DSW_OWN(b), ((unsigned long long)(unsigned)tok << 24) | dep);
                 }
             }
             __syncthreads();
@@ -826,8 +899,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         __syncthreads();
         if (s_abort) break;
 
-        // ---- decisions of every request ----------------------------------
-        if (t == 0) s_ntask = 0;
+        // ---- decisions of every request: its token ---------------------------
         if (t < B) {
             unsigned it = 0;
             unsigned long long w = 0ull;
@@ -838,122 +910,11 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 __builtin_amdgcn_s_sleep(1);
             }
             if (!ok) s_abort = 1;
-            if (!ok) w = 0ull;
-            if (!GU && s_T[t] > 0.0f) {
-                s_dec[t] = (unsigned)(w >> 24) & 0xFFu;
-                s_q[t] = __uint_as_float((uint32_t)(w >> 32));
-            } else {
-                s_next[t] = checked_token((int)((w >> 24) & 0xFFFFFu), V, status);
-            }
+            s_next[t] = ok ? checked_token((int)((w >> 24) & 0xFFFFFu), V, status) : 0;
         }
         __syncthreads();
         if (s_abort) break;
         DSW_TRACE(k, kTrArrived);
-
-        // ---- sampled requests whose token lies in this shard --------------
-        // Their logits of this shard are in LDS or were written out in the
-        // group loop; each wave takes every fourth task and scans the shard's
-        // rows in vocabulary order (RL consecutive rows per lane) for the
-        // first cumulative mass, relative to the shard's maximum, above the
-        // owner's q.
-        if (!GU && any_samp) {
-            if (t < B && s_T[t] > 0.0f && (int)s_dec[t] == c)
-                s_tasks[atomicAdd(&s_ntask, 1)] = t;
-            __syncthreads();
-            const int ntask = s_ntask;
-            constexpr int RLMAX = (RPAD + 63) / 64;  // rows per lane, bound
-            const int RL = (nrows + 63) / 64;
-            for (int i = wave; i < ntask; i += 4) {
-                const int b = s_tasks[i];
-                const float sc2 = kLog2e / s_T[b];
-                // this shard's logits of request b
-                uint32_t lb[RLMAX];
-                if (lds_keep) {
-                    // the group's slot holds the logits over the base logits
-                    const uint16_t* sl = reinterpret_cast<const uint16_t*>(ring + ((b >> 4) % D) * slot_bytes + kSlotUBytes);
-                    const int nn = b & 15;
-#pragma unroll
-                    for (int rr = 0; rr < RLMAX; ++rr) {
-                        const int r = lane * RL + rr;
-                        lb[rr] = (rr < RL && r < nrows) ? (uint32_t)sl[(nn * CPR + ((r >> 3) ^ nn)) * 8 + (r & 7)] : 0u;
-                    }
-                } else if (p.logits != nullptr) {
-                    const uint16_t* lrow = p.logits + ((size_t)b * gamma + k) * V + v0;
-#pragma unroll
-                    for (int rr = 0; rr < RLMAX; ++rr) {
-                        const int r = lane * RL + rr;
-                        lb[rr] = (rr < RL && r < nrows) ? (uint32_t)lrow[r] : 0u;
-                    }
-                } else {
-                    // row r of the shard: wave r / (16 TW), tile j, lane 16 g + n
-                    // of that block, logit (r % 4) of the lane's four
-                    const uint2* lpb = reinterpret_cast<const uint2*>(p.ws.blog) +
-                                       ((size_t)c * NG + (b >> 4)) * 4 * TW * 64 + (b & 15);
-#pragma unroll
-                    for (int rr = 0; rr < RLMAX; ++rr) {
-                        const int r = lane * RL + rr;
-                        lb[rr] = 0u;
-                        if (rr < RL && r < nrows) {
-                            const int w = r / (TW * kTileRows), rem = r - w * TW * kTileRows;
-                            const uint2 v = lpb[(w * TW + (rem >> 4)) * 64 + ((rem >> 2) & 3) * 16];
-                            const uint32_t h = (rem & 2) ? v.y : v.x;
-                            lb[rr] = (rem & 1) ? (h >> 16) : (h & 0xFFFFu);
-                        }
-                    }
-                }
-                const float qb = s_q[b];
-                const uint32_t lk = max(max(s_rkey[0][b], s_rkey[1][b]), max(s_rkey[2][b], s_rkey[3][b]));
-                const float ml = local_key_logit(lk);
-                float wv[RLMAX];
-                float part = 0.0f;
-#pragma unroll
-                for (int rr = 0; rr < RLMAX; ++rr) {
-                    const int r = lane * RL + rr;
-                    wv[rr] = (rr < RL && r < nrows) ? __builtin_amdgcn_exp2f((bf16_to_f32(lb[rr]) - ml) * sc2) : 0.0f;
-                    part += wv[rr];
-                }
-                const float incl = wave_incl_scan_dpp(part);
-                float run = incl - part;
-                uint32_t first = 0u, lastw = 0u;  // row + 1, 0 = none
-#pragma unroll
-                for (int rr = 0; rr < RLMAX; ++rr) {
-                    const int r = lane * RL + rr;
-                    if (rr < RL && r < nrows) {
-                        run += wv[rr];
-                        if (first == 0u && run > qb) first = (uint32_t)r + 1u;
-                        if (wv[rr] > 0.0f) lastw = (uint32_t)r + 1u;
-                    }
-                }
-                const uint32_t fmin = wave_max_u32(first ? 0xFFFFFFFFu - first : 0u);
-                const uint32_t lmax = wave_max_u32(lastw);
-                // no crossing row (rounding): the last row with positive mass
-                const int row = fmin ? (int)(0xFFFFFFFFu - fmin) - 1 : (lmax ? (int)lmax - 1 : -1);
-                if (lane == 0) {
-                    const int tok = checked_token(row < 0 ? -1 : v0 + row, V, status);
-                    s_next[b] = tok;
-                    walk_skew(p, c, k, 2);
-                    st_agent64(&btok[(size_t)c * kMaxBatch + b], ((unsigned long long)(unsigned)tok << 28) | epoch);
-                }
-            }
-            __syncthreads();
-            if (s_abort) break;
-            // tokens found by other shards
-            if (t < B && s_T[t] > 0.0f && (int)s_dec[t] != c) {
-                unsigned it = 0;
-                unsigned long long w = 0ull;
-                bool ok = true;
-                const unsigned long long* tw = &btok[(size_t)s_dec[t] * kMaxBatch + t];
-                while (((w = ld_agent64(tw)) & kEpochMod) != epoch) {
-                    if (++it >= p.spin_limit) { latch(status, kStatusTimeout); ok = false; break; }
-                    if ((it & 255u) == 0u && ld_agent(status) != 0u) { ok = false; break; }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                if (!ok) s_abort = 1;
-                s_next[t] = ok ? checked_token((int)(w >> 28), V, status) : 0;
-            }
-            __syncthreads();
-            if (s_abort) break;
-        }
 
         if (t < B) {
             if (c == 0) p.tokens[(size_t)t * gamma + k] = s_next[t];

@@ -3,23 +3,20 @@
 #include "walk_batched.h"
 
 // Host-side lookup used by the launcher: the batched kernel for (W2 dtype,
-// register tiles, tiles per wave, single rounding, logits kept in LDS, four
-// tiles per epilogue, Gumbel-max), or nullptr when that shape is not compiled.
-// Keeping the logits in LDS is compiled for bf16 with double rounding (the
-// small batches' default), and with it the four-tile epilogue for up to 4
-// requests; Gumbel-max for bf16 with double rounding, with or without it.
+// register tiles, tiles per wave, single rounding, four tiles per epilogue,
+// Gumbel-max), or nullptr when that shape is not compiled.  The four-tile
+// epilogue (up to 4 requests) and Gumbel-max are compiled for bf16 with double
+// rounding.
 extern "C" const void* dsw_internal_batched_kernel(int w2_dtype, int reg_tiles, int max_tiles, int single_round,
-                                                   int keep, int fold, int gumbel) {
+                                                   int fold, int gumbel) {
 #define DSW_PICK(R, M)                                                                       \
     if (w2_dtype == 0 && reg_tiles == (R) && max_tiles == (M)) {                             \
+        if (single_round) return gumbel ? nullptr : (const void*)dsw::walk_batched<(R), (M), 0, 1>; \
         if (gumbel)                                                                          \
-            return single_round ? nullptr                                                    \
-                                : (fold ? (const void*)dsw::walk_batched<(R), (M), 0, 0, 0, 4, 1> \
-                                        : (const void*)dsw::walk_batched<(R), (M), 0, 0, 0, 1, 1>); \
-        return single_round ? (const void*)dsw::walk_batched<(R), (M), 0, 1>                 \
-                            : (keep ? (fold ? (const void*)dsw::walk_batched<(R), (M), 0, 0, 1, 4> \
-                                            : (const void*)dsw::walk_batched<(R), (M), 0, 0, 1>) \
-                                    : (const void*)dsw::walk_batched<(R), (M), 0, 0>);       \
+            return fold ? (const void*)dsw::walk_batched<(R), (M), 0, 0, 4, 1>                \
+                        : (const void*)dsw::walk_batched<(R), (M), 0, 0, 1, 1>;               \
+        return fold ? (const void*)dsw::walk_batched<(R), (M), 0, 0, 4>                      \
+                    : (const void*)dsw::walk_batched<(R), (M), 0, 0>;                        \
     }
 #define DSW_PICK_I8(R, M)                                                \
     if (w2_dtype == 1 && reg_tiles == (R) && max_tiles == (M))           \

@@ -74,22 +74,21 @@ struct Workspace {
     unsigned* status;              // ctl[3]  latched kStatus* bits
     // batched kernel (requests owned by workgroups): every workgroup posts one
     // key word and next to it one exp-sum word per request (a reader takes both
-    // with one 16-byte load); the owner of request b reads column b and
-    // publishes a decision; a token shard publishes tokens
+    // with one 16-byte load); the owner of request b reads column b, and for a
+    // sampled request the token shard's logits from blog, and publishes the
+    // token
     unsigned long long* bkey;      // [2][kMaxGrid][kMaxBatch][2]  key << 28 | epoch, then exp-sum
                                    // bits << 32 | epoch (Gumbel-max: ord32(score) << 28 | epoch,
                                    // then ~id << 32 | epoch)
     unsigned long long* bdec;      // [2][kOwnWords]  per owner workgroup c, a region of
                                    // owner_stride(G) words (whole 128-byte lines, one
                                    // writer each; 1 word for up to 16 requests); request
-                                   // b = c + i G takes word i: its decision, payload << 24 |
-                                   // a 24-bit epoch (the token, or the token shard and the
-                                   // mass that shard accumulates before the token)
-    unsigned long long* btok;      // [2][kMaxGrid][kMaxBatch]  sampled token << 28 | epoch,
-                                   // in the row of the shard that found it
-    uint16_t* blog;                // batched kernel: this step's logits of the sampled
-                                   // requests (when the caller wants none written), read
-                                   // back by the token shards, batched_logits_bytes() long;
+                                   // b = c + i G takes word i: its decision, token << 24 |
+                                   // a 24-bit epoch
+    uint16_t* blog;                // batched kernel: this step's logits of the 16-request
+                                   // groups with a sampled request (agent-scope stores,
+                                   // complete before the key words), read back by the
+                                   // requests' owners, batched_logits_bytes() long;
                                    // NULL if the handle never runs the batched kernel.
                                    // Per workgroup c, 16-request group, wave and tile j:
                                    // 64 lanes x 4 bf16 (rows 4g .. 4g+3 of request n),
@@ -104,7 +103,7 @@ constexpr unsigned kStatusUniforms = 4u;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
-    size_t mail, tokw, ctl, bkey, bdec, btok, total;
+    size_t mail, tokw, ctl, bkey, bdec, total;
 };
 inline WorkspaceLayout workspace_layout() {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -115,7 +114,6 @@ inline WorkspaceLayout workspace_layout() {
     L.ctl = o;       o = up(o + 16);
     L.bkey = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 16);
     L.bdec = o;      o = up(o + 2 * (size_t)kOwnWords * 8);
-    L.btok = o;      o = up(o + 2 * (size_t)kMaxGrid * kMaxBatch * 8);
     L.total = o;
     return L;
 }

@@ -100,7 +100,6 @@ dsw::Workspace workspace_at(unsigned char* base) {
     ws.status = reinterpret_cast<unsigned*>(base + L.ctl) + dsw::kCtlStatus;
     ws.bkey = reinterpret_cast<unsigned long long*>(base + L.bkey);
     ws.bdec = reinterpret_cast<unsigned long long*>(base + L.bdec);
-    ws.btok = reinterpret_cast<unsigned long long*>(base + L.btok);
     ws.blog = reinterpret_cast<uint16_t*>(base + kWsBytes);
     return ws;
 }
