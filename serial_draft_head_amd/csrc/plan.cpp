@@ -199,11 +199,11 @@ static const int kBShapesI8[][2] = {{8, 8}, {8, 12}};
 static const int kBStreamShape[2] = {0, 12};
 static int batched_static_lds(int max_tiles, bool i8) {
     const int rpad = max_tiles * 4 * kTileRows;
-    // per-request keys, maxima and exp-sums per wave; tokens (two) and
-    // temperatures; base-row offsets (8 bytes); the shard masses, scales and
-    // maxima; int8 row scales; the -inf base rows of dead tiles (4 waves x 64
-    // lanes x 8 bytes) and a few scalars; the trace
-    return 4 * kMaxBatch * 4 * 3 + 3 * kMaxBatch * 4 + kMaxBatch * 8 + 3 * kMaxGrid * 4 +
+    // per-request keys, maxima and exp-sums per wave; tokens (two),
+    // temperatures and their two scales; base-row offsets (8 bytes); the shard
+    // masses, scales and maxima; int8 row scales; the -inf base rows of dead
+    // tiles (4 waves x 64 lanes x 8 bytes) and a few scalars; the trace
+    return 4 * kMaxBatch * 4 * 3 + 5 * kMaxBatch * 4 + kMaxBatch * 8 + 3 * kMaxGrid * 4 +
            (i8 ? 4 * rpad : 0) + 4 * 64 * 8 + 1024 + kTraceLds;
 }
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -234,6 +234,10 @@ static int plan_batched(const dsw_devinfo* dev, int V, int B, unsigned flags, in
                 max_t = sh[1];
                 break;
             }
+        // 10 to 12 tiles per wave: two more register tiles (in VGPRs), so that
+        // a shard of 10 tiles needs no LDS tiles -- except for Gumbel-max beyond
+        // 4 requests, whose one-tile epilogue leaves no registers for them
+        if (reg_t == 8 && max_t == 12 && TW >= 10 && !((flags & DSW_FLAG_GUMBEL) && B > 4)) reg_t = 10;
     }
     if (max_t < TW) return DSW_ERR_VOCAB;
     const int lds_static = batched_static_lds(max_t, i8);

@@ -103,11 +103,13 @@ __device__ __forceinline__ float fold4_sum_f32(float x) {
 // every step takes two exchanges and no token shard scans its rows.
 template <int A, int M, int DT, int SR, int FD = 1, int GU = 0>
 __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
-    static_assert(FD == 1 || (FD == 4 && DT == 0 && A % 4 == 0), "fold: bf16");
+    static_assert(FD == 1 || (FD == 4 && DT == 0), "fold: bf16");
     static_assert(GU == 0 || (DT == 0 && SR == 0), "Gumbel-max: bf16, double rounding");
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
-    static_assert(A <= M && A <= (kI8 ? 2 : 1) * kMaxRegTiles && (A % 2) == 0, "shape");
+    // bf16: up to kMaxRegTiles tiles in AGPRs and two more in VGPRs
+    static_assert(A <= M && A <= (kI8 ? 2 * kMaxRegTiles : kMaxRegTiles + 2) && (A % 2) == 0, "shape");
+    constexpr int kA4 = (A + 3) / 4 * 4;  // FD = 4: the first tile after the register groups
     constexpr int RPAD = M * 4 * kTileRows;  // shard rows, bound
     extern __shared__ uint4 s_dyn[];  // [LDS weight tiles][ring slots]
 
@@ -121,6 +123,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     __shared__ unsigned long long s_rowb[kMaxBatch];  // request b's base logits of step 0 at this shard, in 16 B
     __shared__ int s_next[kMaxBatch];
     __shared__ float s_T[kMaxBatch];
+    __shared__ float s_scl[kMaxBatch];             // log2(e) / T of sampled requests, else 0
+    __shared__ float s_invT[GU ? kMaxBatch : 1];   // Gumbel-max: 1 / T of sampled requests
     __shared__ float s_S[kMaxGrid];
     __shared__ float s_E[kMaxGrid];
     __shared__ float s_M[kMaxGrid];            // owner: the shards' max logits of the request
@@ -223,7 +227,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #pragma unroll
     for (int j = 0; j < A; ++j)
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) pin_agpr(wr[j][kb]);
+        for (int kb = 0; kb < 8; ++kb)
+            if (kI8 || j < kMaxRegTiles) pin_agpr(wr[j][kb]);
     for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
         WT v[8];
 #pragma unroll
@@ -266,6 +271,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         if (!(temp > 0.0f)) temp = 0.0f;
         s_prev[t] = a;
         s_T[t] = temp;
+        s_scl[t] = temp > 0.0f ? kLog2e / temp : 0.0f;
+        if constexpr (GU) s_invT[t] = temp > 0.0f ? 1.0f / temp : 1.0f;
         if (temp > 0.0f) s_any_samp = 1;
         s_rowb[t] = (unsigned long long)t * (unsigned)gamma * (unsigned)(V >> 3) + (unsigned)(v0 >> 3);
     }
@@ -274,6 +281,21 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     const unsigned round = s_round;
     const unsigned fam = s_fam;
     const bool any_samp = s_any_samp != 0;
+
+    // acc_ += tile j >= A (in LDS, else streamed from W2) times ub
+#define DSW_TILE_OFFCHIP(j_, acc_)                                                               \
+    do {                                                                                         \
+        if ((j_) - A < LT) {                                                                     \
+            const int sb_ = (wave * LT + ((j_) - A)) * 512 + lane;                               \
+            _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                     \
+                acc_ = mfma_tile(as_bf16x8(s_wt[sb_ + kb * 64]), ub[kb], acc_);                  \
+        } else {                                                                                 \
+            const int row_ = min(v0 + wrow0 + (j_) * kTileRows + n, last_row);                   \
+            const WT* src_ = W2 + (size_t)row_ * kRowChunks + g;                                 \
+            _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                     \
+                acc_ = mfma_tile(as_bf16x8(src_[kb * 4]), ub[kb], acc_);                         \
+        }                                                                                        \
+    } while (0)
 
     // MFMA over every tile of this wave with B operand ub[8]; EPI(d, j) gets
     // the four results (rows 4g .. 4g+3 of tile j, request column n)
@@ -338,7 +360,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     } while (0)
 
     // FD = 4: four tiles per epilogue (the lane's tile is j0 + qf); the MFMAs
-    // of four register tiles are issued before the epilogue of the previous four
+    // of four register tiles are issued before the epilogue of the previous
+    // four.  A last group of four that holds fewer than four register tiles
+    // (A % 4 == 2) takes its other tiles from LDS or W2.
 #define DSW_TILES_F4(EPI)                                                                        \
     do {                                                                                         \
         f32x4_t e_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                            \
@@ -348,31 +372,24 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             f32x4_t c_[4];                                                                       \
             _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                                   \
                 c_[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                        \
-                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                                 \
-                    c_[jj] = mfma_tile(as_bf16x8(wr[j0 + jj][kb]), ub[kb], c_[jj]);              \
+                if (j0 + jj < A) {                                                               \
+                    _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                             \
+                        c_[jj] = mfma_tile(as_bf16x8(wr[min(j0 + jj, A - 1)][kb]), ub[kb], c_[jj]); \
+                } else if (j0 + jj < nt_w) {                                                     \
+                    DSW_TILE_OFFCHIP(j0 + jj, c_[jj]);                                           \
+                }                                                                                \
             }                                                                                    \
             if (j0 > 0) EPI(e_, j0 - 4 + qf, eb_);                                               \
             e_ = fold4(c_[0], c_[1], c_[2], c_[3]);                                              \
             eb_ = nb_;                                                                           \
         }                                                                                        \
-        if (A > 0) EPI(e_, A - 4 + qf, eb_);                                                     \
-        _Pragma("unroll 1") for (int j0 = A; j0 < nt_w; j0 += 4) {                               \
+        if (A > 0) EPI(e_, kA4 - 4 + qf, eb_);                                                   \
+        _Pragma("unroll 1") for (int j0 = kA4; j0 < nt_w; j0 += 4) {                             \
             f32x4_t c_[4];                                                                       \
             _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                                   \
                 const int j = j0 + jj;                                                           \
                 c_[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                        \
-                if (j < nt_w) {                                                                  \
-                    if (j - A < LT) {                                                            \
-                        const int sb_ = (wave * LT + (j - A)) * 512 + lane;                      \
-                        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                         \
-                            c_[jj] = mfma_tile(as_bf16x8(s_wt[sb_ + kb * 64]), ub[kb], c_[jj]);  \
-                    } else {                                                                     \
-                        const int row_ = min(v0 + wrow0 + j * kTileRows + n, last_row);          \
-                        const WT* src_ = W2 + (size_t)row_ * kRowChunks + g;                     \
-                        _Pragma("unroll") for (int kb = 0; kb < 8; ++kb)                         \
-                            c_[jj] = mfma_tile(as_bf16x8(src_[kb * 4]), ub[kb], c_[jj]);         \
-                    }                                                                            \
-                }                                                                                \
+                if (j < nt_w) DSW_TILE_OFFCHIP(j, c_[jj]);                                       \
             }                                                                                    \
             EPI(fold4(c_[0], c_[1], c_[2], c_[3]), j0 + qf, *DSW_BASE_PTR(j0 + qf));             \
         }                                                                                        \
@@ -389,13 +406,15 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
         unsigned long long* bown = p.ws.bdec + (size_t)q * kOwnWords;
 #define DSW_OWN(b_) (bown + (size_t)((b_) % G) * OS + (b_) / G)
 
-        // group gq's u rows and base logits into ring slot gq % D.  Each lane
-        // names its own source; the wave's 64 chunks land contiguously.
-#define DSW_ISSUE_GROUP(grp_)                                                                    \
+        // group gq's u rows (U_) and base logits (BASE_, of the step whose rows
+        // start koff_ 16-byte chunks into a request's base) into ring slot
+        // gq % D.  Each lane names its own source; the wave's 64 chunks land
+        // contiguously.
+#define DSW_ISSUE_GROUP(grp_, U_, BASE_, koff_)                                                  \
     do {                                                                                         \
         const int gq_ = (grp_);                                                                  \
         char* slot_ = ring + (gq_ % D) * slot_bytes;                                             \
-        _Pragma("unroll") for (int ii = 0; ii < 2; ++ii) {                                       \
+        if (U_) _Pragma("unroll") for (int ii = 0; ii < 2; ++ii) {                               \
             const int inst_ = wave * 2 + ii;                                                     \
             const int pos_ = inst_ * 64 + lane;                                                  \
             const int nn_ = pos_ >> 5, pc_ = pos_ & 31;                                          \
@@ -403,7 +422,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             dma16(W1 + (size_t)s_prev[b_] * kRowChunks + (pc_ ^ nn_),                            \
                   __builtin_amdgcn_readfirstlane(lds_addr(slot_ + inst_ * 1024)));               \
         }                                                                                        \
-        if (aligned) {                                                                           \
+        if (!(BASE_)) {                                                                          \
+        } else if (aligned) {                                                                    \
             /* 16-byte chunk (pc ^ nn) of request nn's row past the shard start, */             \
             /* clamped to the row's last chunk; 24-bit products (pos < 16 CPR)   */             \
             const int per_ = CPR / 16;                                                           \
@@ -414,7 +434,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const int pc_ = pos_ - __umul24((unsigned)nn_, (unsigned)CPR);                   \
                 const int b_ = min(gq_ * kGroup + nn_, B - 1);                                   \
                 const int x_ = min(pc_ ^ nn_, lastc);                                            \
-                const uint4* src_ = reinterpret_cast<const uint4*>(base) + (s_rowb[b_] + koff) + x_; \
+                const uint4* src_ = reinterpret_cast<const uint4*>(base) + (s_rowb[b_] + (koff_)) + x_; \
                 dma16(src_, __builtin_amdgcn_readfirstlane(lds_addr(slot_ + kSlotUBytes + inst_ * 1024))); \
             }                                                                                    \
         } else {                                                                                 \
@@ -430,12 +450,16 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 
         const unsigned long long koff = (unsigned long long)k * (unsigned)(V >> 3);  // step k's rows, in 16 B
         const int lastc = (V >> 3) - 1 - (v0 >> 3);  // the row's last chunk past the shard start (< 0: empty shard)
-        for (int gq = 0; gq < min(D - 1, NG); ++gq) DSW_ISSUE_GROUP(gq);
+        // one group (up to 16 requests, DMA-able base rows): its base logits of
+        // steps after the first were fetched during the previous step's
+        // exchange (below)
+        const bool pref = NG == 1 && aligned;
+        for (int gq = 0; gq < min(D - 1, NG); ++gq) DSW_ISSUE_GROUP(gq, true, !(pref && k > 0), koff);
 
         for (int grp = 0; grp < NG; ++grp) {
             wait_vmcnt(P * min(D - 2, NG - 1 - grp));
             barrier_keep_vm();
-            if (grp + D - 1 < NG) DSW_ISSUE_GROUP(grp + D - 1);
+            if (grp + D - 1 < NG) DSW_ISSUE_GROUP(grp + D - 1, true, true, koff);
             const char* slot = ring + (grp % D) * slot_bytes;
             const uint4* su = reinterpret_cast<const uint4*>(slot);
             uint16_t* sb = reinterpret_cast<uint16_t*>(const_cast<char*>(slot) + kSlotUBytes);
@@ -560,8 +584,8 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
             // Gumbel-max: the logits go out only when the caller wants them, and
             // the noise is drawn only in groups with a sampled request.
             const bool samp = bval && s_T[b] > 0.0f;
-            const float sc = samp ? kLog2e / s_T[b] : 0.0f;
-            const float invT = samp ? 1.0f / s_T[b] : 1.0f;          // Gumbel-max: l / T
+            const float sc = bval ? s_scl[b] : 0.0f;
+            const float invT = GU && bval ? s_invT[GU ? b : 0] : 1.0f;  // Gumbel-max: l / T
             const uint32_t gc1 = ((uint32_t)k << 8) | (uint32_t)b;    // Gumbel-max: the noise counter
             const bool priv = p.logits == nullptr;  // no caller logits (wave-uniform)
             // this lane's column of the group's private block: tile j at 64 j
@@ -691,20 +715,37 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t)], ((gk >> kIdxBits) << 28) | epoch);
                 st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t) + 1], ((gk & kIdxMask) << 32) | epoch);
             } else {
-                const uint32_t lk = max(max(s_rkey[0][t], s_rkey[1][t]), max(s_rkey[2][t], s_rkey[3][t]));
+                // every LDS read issued at once, the sum branch-free (a wave
+                // without rows adds nothing)
+                uint32_t kk[4];
+                float rm[4], rs[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    kk[w] = s_rkey[w][t];
+                    rm[w] = s_rm[w][t];
+                    rs[w] = s_rs[w][t];
+                }
+                const float scl = s_scl[t];
+                const bool smp = s_T[t] > 0.0f;
+                const uint32_t lk = max(max(kk[0], kk[1]), max(kk[2], kk[3]));
                 st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t)], (global_key(lk, v0) << 28) | epoch);
-                if (s_T[t] > 0.0f) {
+                if (smp) {
                     const float mc = local_key_logit(lk);
                     float sc = 0.0f;
-                    const float scl = kLog2e / s_T[t];
+#pragma unroll
                     for (int w = 0; w < 4; ++w)
-                        if (s_rkey[w][t] != 0u) sc += s_rs[w][t] * __builtin_amdgcn_exp2f((s_rm[w][t] - mc) * scl);
+                        sc += kk[w] != 0u ? rs[w] * __builtin_amdgcn_exp2f((rm[w] - mc) * scl) : 0.0f;
                     st_agent64(&bkey[2 * ((size_t)c * kMaxBatch + t) + 1],
                                ((unsigned long long)__float_as_uint(sc) << 32) | epoch);
                 }
             }
         }
         DSW_TRACE(k, kTrPosted);
+        // One group: the next step's base logits go into its slot now (every
+        // wave is done with the slot), so that the next step waits only for
+        // its u rows.  The polls below wait for these loads too (vmcnt counts
+        // in order), but the exchange takes longer than they do.
+        if (pref && k + 1 < gamma) DSW_ISSUE_GROUP(0, false, true, koff + (unsigned long long)(unsigned)(V >> 3));
         // ~0.2 us before the first poll of the columns: no other workgroup's
         // words can be there yet, and early polls only load the fabric
         // (measured: V = 129,280, gamma 5, B = 16: 231.5 -> 229.7 us)
@@ -756,7 +797,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #define DSW_OWNER_SHARD(b_, kw_, sw_, M_)                                                        \
     do {                                                                                         \
         const float e_ = (t < G && kw_ != 0ull)                                                  \
-                             ? __builtin_amdgcn_exp2f((key_logit(kw_) - (M_)) * (kLog2e / s_T[b_])) \
+                             ? __builtin_amdgcn_exp2f((key_logit(kw_) - (M_)) * s_scl[b_])          \
                              : 0.0f;                                                             \
         s_S[t] = (t < G && kw_ != 0ull) ? sw_ * e_ : 0.0f;                                       \
         s_E[t] = e_;                                                                             \
@@ -831,7 +872,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 const int own = s_own;
                 const int ov0 = max(own, 0) * R;
                 const int onr = own < 0 ? 0 : max(0, min(V, ov0 + R) - ov0);
-                const float sc2 = kLog2e / s_T[b];
+                const float sc2 = s_scl[b];
                 const float mo = s_M[max(own, 0)];
                 const float qo = s_qown;
                 const int r0 = 4 * t;
@@ -931,7 +972,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 #undef DSW_BLOCK_MAX64
 #undef DSW_TILES
 #undef DSW_TILES_F4
+#undef DSW_TILE_OFFCHIP
 
+    wait_vmcnt(0);  // a walk that gave up may still have a prefetch in flight
     DSW_TRACE_FLUSH();
     if (c == 0 && t == 0 && !s_abort) {
         __hip_atomic_fetch_add(p.ws.round_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -940,7 +983,7 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
 }
 
 // (register tiles, tiles per wave) shapes of the batched kernel
-#define DSW_BATCHED_SHAPES(X) X(4, 4) X(8, 8) X(8, 12) X(0, 12)
+#define DSW_BATCHED_SHAPES(X) X(4, 4) X(8, 8) X(8, 12) X(10, 12) X(0, 12)
 #define DSW_BATCHED_I8_SHAPES(X) X(8, 8) X(8, 12) X(0, 12)
 
 }  // namespace dsw

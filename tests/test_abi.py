@@ -190,8 +190,9 @@ def test_planner_partitions_rows_and_respects_capacity(dsw, engine, cus, V, B):
         assert p.lds_bytes >= 4 * p.lds_tiles * 8192 + p.ring_slots * (8192 + 32 * p.rows_pad)
     if engine != "valu":
         assert p.tiles_per_wave * 4 * 16 >= rows
-        # one request keeps up to 4 more tiles per wave in VGPRs
-        assert p.reg_tiles <= (12 if p.batch_tile == 1 else 8) and p.tiles_per_wave <= p.max_tiles
+        # one request keeps up to 4 more tiles per wave in VGPRs, the batched
+        # kernel (bf16) 2 more
+        assert p.reg_tiles <= {1: 12, 256: 10}.get(p.batch_tile, 8) and p.tiles_per_wave <= p.max_tiles
         assert p.reg_tiles + p.lds_tiles <= max(p.tiles_per_wave, p.reg_tiles)
         assert p.lds_bytes >= p.lds_rows * 512
     else:
@@ -247,10 +248,17 @@ def test_planner_batched_kernel(dsw):
     assert dsw.plan(d, 129_280, 5, 3, flags=dsw.FLAG_BATCHED).batch_tile == 256
     # int8 rows beyond the batched shapes fall back to the all-to-all kernel
     assert dsw.plan(d, 248_320, 16, 8, w2_dtype=dsw.INT8).batch_tile == 16
-    # V = 151,936 with 64 requests: two LDS tiles per wave beside the ring
+    # V = 151,936 with 64 requests: ten register tiles per wave (two in VGPRs)
     c2 = dsw.plan(d, 151_936, 16, 64)
-    assert (c2.rows_per_wg, c2.tiles_per_wave, c2.reg_tiles, c2.lds_tiles, c2.stream_rows) == (608, 10, 8, 2, 0)
+    assert (c2.rows_per_wg, c2.tiles_per_wave, c2.reg_tiles, c2.lds_tiles, c2.stream_rows) == (608, 10, 10, 0, 0)
     assert c2.ring_slots >= 2
+    # Gumbel-max beyond 4 requests keeps 8 register tiles and two LDS tiles
+    g2 = dsw.plan(d, 151_936, 16, 64, flags=dsw.FLAG_GUMBEL)
+    assert (g2.reg_tiles, g2.lds_tiles) == (8, 2)
+    assert dsw.plan(d, 151_936, 16, 4, flags=dsw.FLAG_GUMBEL | dsw.FLAG_BATCHED).reg_tiles == 10
+    # 9 tiles per wave: 8 register tiles and one LDS tile
+    c9 = dsw.plan(d, 140_000, 16, 64)
+    assert (c9.tiles_per_wave, c9.reg_tiles, c9.lds_tiles) == (9, 8, 1)
     i8 = dsw.plan(d, 129_280, 5, 64, w2_dtype=dsw.INT8)
     assert (i8.reg_tiles, i8.max_tiles, i8.w2_dtype, i8.onchip_bytes) == (8, 8, dsw.INT8, 129_280 * 256)
     with pytest.raises(dsw.DswError) as e:   # no VALU engine for the batched kernel

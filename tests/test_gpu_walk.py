@@ -1083,7 +1083,12 @@ def check_subset(w, inp, toks, lg, idx, steps=None):
 
 # aligned (V % 8 == 0: base rows stream straight into LDS) and unaligned vocabularies
 # V = 151,936 keeps two tiles per wave in LDS beside the ring
-BATCHED_CASES = [(257, 17), (4_096, 40), (32_000, 64), (65_537, 33), (129_280, 24), (151_936, 20)]
+BATCHED_CASES = [(257, 17), (4_096, 40), (32_000, 64), (65_537, 33), (129_280, 24), (140_000, 19),
+                 (151_936, 20), (190_000, 18)]
+# plans with LDS tiles (9 tiles per wave: 8 register tiles and one in LDS; 12:
+# 10 register tiles and two in LDS) and with ten register tiles
+LDS_TILE_VOCABS = (140_000, 190_000)
+TEN_TILE_VOCABS = (151_936, 190_000)
 
 
 @pytest.mark.parametrize("temps", ["greedy", "mixed"])
@@ -1096,7 +1101,8 @@ def test_batched_parity(dsw, V, B, temps):
     pl = walker.query_plan(B)
     say("plan", pl.as_dict())
     assert pl.batch_tile == 256
-    assert (pl.lds_tiles > 0) == (V == 151_936)
+    assert (pl.lds_tiles > 0) == (V in LDS_TILE_VOCABS)
+    assert (pl.reg_tiles == 10) == (V in TEN_TILE_VOCABS)
     W1d, W2d = bf16_dev(W1), bf16_dev(W2)
     inp = workloads.round_inputs(4, 3, B=B, gamma=3, V=V, temps=temps)
     toks, lg = run(walker, W1d, W2d, inp)
@@ -1124,11 +1130,13 @@ def test_batched_kernel_at_small_batches(dsw, B):
 
 # Up to 4 requests on the batched kernel: four tiles share one epilogue.
 # Vocabularies with dead register tiles (V = 4,099: shards of 17 rows; V =
-# 100,003: 7 tiles per wave on the 8-tile shape), LDS tiles (V = 151,936)
-# and streamed tiles (FORCE_STREAM), an unaligned vocabulary, logits out or
-# kept in LDS only.
+# 100,003: 7 tiles per wave on the 8-tile shape), ten register tiles (V =
+# 151,936: the last group of four holds two), ten register tiles and two LDS
+# tiles in that group (V = 190,000), streamed tiles (FORCE_STREAM), an
+# unaligned vocabulary, logits out or not.
 @pytest.mark.parametrize("B", [1, 2, 4])
-@pytest.mark.parametrize("V,stream", [(4_099, False), (100_003, False), (151_936, False), (60_000, True)])
+@pytest.mark.parametrize("V,stream", [(4_099, False), (100_003, False), (151_936, False), (190_000, False),
+                                      (60_000, True)])
 def test_batched_four_tile_epilogue(dsw, V, stream, B):
     say(f"batched four-tile epilogue V={V} B={B} stream={stream}")
     W1, W2 = workloads.weights(2, V=V)
