@@ -389,7 +389,7 @@ def grid_sweep(torch, dsw, grids=(8, 16, 32, 64, 128, 256), rounds=20, K=200):
 # Every configuration the walk is checked on, timed briefly after the headline
 # line's own measurements: (workload, requests, gamma, W2 storage).
 SWEEP = [(0, 1, 7, "bf16"), (2, 1, 16, "bf16"), (2, 4, 16, "bf16"), (2, 16, 16, "bf16"),
-         (3, 1, 16, "bf16"), (3, 1, 16, "int8"), (4, 64, 5, "bf16"), (4, 128, 5, "bf16"),
+         (3, 1, 16, "bf16"), (3, 1, 16, "int8"), (4, 64, 5, "bf16"), (4, 64, 5, "int8"), (4, 128, 5, "bf16"),
          (4, 253, 5, "bf16"),
          # the mixed-temperature walks again, sampled by Gumbel-max (DSW_FLAG_GUMBEL)
          (2, 1, 16, "bf16", "gumbel"), (2, 4, 16, "bf16", "gumbel"), (2, 16, 16, "bf16", "gumbel"),

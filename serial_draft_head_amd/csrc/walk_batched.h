@@ -107,8 +107,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     static_assert(GU == 0 || (DT == 0 && SR == 0), "Gumbel-max: bf16, double rounding");
     constexpr bool kI8 = DT == 1;
     using WT = typename std::conditional<kI8, uint2, uint4>::type;
-    // bf16: up to kMaxRegTiles tiles in AGPRs and two more in VGPRs
-    static_assert(A <= M && A <= (kI8 ? 2 * kMaxRegTiles : kMaxRegTiles + 2) && (A % 2) == 0, "shape");
+    // register tiles in bf16 (int8 rows widened once at entry): up to
+    // kMaxRegTiles in AGPRs and two more in VGPRs
+    static_assert(A <= M && A <= kMaxRegTiles + 2 && (A % 2) == 0, "shape");
     constexpr int kA4 = (A + 3) / 4 * 4;  // FD = 4: the first tile after the register groups
     constexpr int RPAD = M * 4 * kTileRows;  // shard rows, bound
     extern __shared__ uint4 s_dyn[];  // [LDS weight tiles][ring slots]
@@ -215,20 +216,29 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     DSW_TRACE(gamma, 0);
 
     // ---- entry: this workgroup's shard on chip (as walk_kernel.h) --------
-    WT wr[A > 0 ? A : 1][8];
+    // Register tiles hold bf16 operands: int8 rows are widened once here
+    // (exactly: every int8 value is a bf16 value), not before every MFMA.
+    uint4 wr[A > 0 ? A : 1][8];
+    {
+        WT raw[A > 0 ? A : 1][8];
 #pragma unroll
-    for (int j = 0; j < A; ++j) {
-        const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
-        const WT* src = W2 + (size_t)row * kRowChunks + g;
+        for (int j = 0; j < A; ++j) {
+            const int row = min(v0 + wrow0 + j * kTileRows + n, last_row);
+            const WT* src = W2 + (size_t)row * kRowChunks + g;
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) wr[j][kb] = src[kb * 4];
+            for (int kb = 0; kb < 8; ++kb) raw[j][kb] = src[kb * 4];
+        }
+#pragma unroll
+        for (int j = 0; j < A; ++j)
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) wr[j][kb] = as_bf16x8(raw[j][kb]);
     }
     // pinned once every tile's loads are in flight (a pin waits for its registers)
 #pragma unroll
     for (int j = 0; j < A; ++j)
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
-            if (kI8 || j < kMaxRegTiles) pin_agpr(wr[j][kb]);
+            if (j < kMaxRegTiles) pin_agpr(wr[j][kb]);
     for (int i0 = 0; i0 < 4 * LT * 512; i0 += 8 * kBlock) {
         WT v[8];
 #pragma unroll
@@ -301,9 +311,9 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
     // the four results (rows 4g .. 4g+3 of tile j, request column n)
 #define DSW_TILES(EPI)                                                                           \
     do {                                                                                         \
-        if constexpr (!kI8) {                                                                    \
-            /* bf16: the MFMAs of a pair of tiles are issued before the epilogue of  */          \
-            /* the previous pair, whose VALU work then overlaps them                 */          \
+        {                                                                                        \
+            /* the MFMAs of a pair of tiles are issued before the epilogue of the    */          \
+            /* previous pair, whose VALU work then overlaps them;                    */          \
             /* their base logits are read from LDS with the MFMAs, a pair ahead     */          \
             f32x4_t p0_ = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, p1_ = p0_;                            \
             uint2 pb0_ = make_uint2(0u, 0u), pb1_ = pb0_;                                        \
@@ -327,21 +337,6 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 EPI(p0_, A - 2, pb0_);                                                           \
                 EPI(p1_, A - 1, pb1_);                                                           \
             }                                                                                    \
-        } else _Pragma("unroll") for (int j0 = 0; j0 < A; j0 += 2) {                             \
-            f32x4_t d0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;                               \
-            if constexpr (kI8) {                                                                 \
-                _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                               \
-                    pin_agpr(wr[j0][kb]);                                                        \
-                    pin_agpr(wr[j0 + 1][kb]);                                                    \
-                }                                                                                \
-            }                                                                                    \
-            _Pragma("unroll") for (int kb = 0; kb < 8; ++kb) {                                   \
-                d0 = mfma_tile(as_bf16x8(wr[j0][kb]), ub[kb], d0);                               \
-                d1 = mfma_tile(as_bf16x8(wr[j0 + 1][kb]), ub[kb], d1);                           \
-            }                                                                                    \
-            if (j0 < nt_w) EPI(d0, j0, *DSW_BASE_PTR(j0));                                       \
-            if (j0 + 1 < nt_w) EPI(d1, j0 + 1, *DSW_BASE_PTR(j0 + 1));                           \
-            __builtin_amdgcn_sched_barrier(0);                                                   \
         }                                                                                        \
         _Pragma("unroll 1") for (int j = A; j < nt_w; ++j) {                                     \
             f32x4_t dd = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};                                        \

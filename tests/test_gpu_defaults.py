@@ -77,7 +77,7 @@ def test_headline_100_rounds(dsw):
 
 # (workload, requests, rounds, W2 storage)
 DEFAULT_CASES = [(2, 1, 3, "bf16"), (2, 4, 2, "bf16"), (2, 16, 2, "bf16"), (3, 1, 2, "bf16"), (3, 1, 2, "int8"),
-                 (4, 64, 1, "bf16"), (4, 128, 1, "bf16"), (4, 253, 1, "bf16")]
+                 (4, 64, 1, "bf16"), (4, 64, 1, "int8"), (4, 128, 1, "bf16"), (4, 253, 1, "bf16")]
 
 
 @pytest.mark.parametrize("index,B,n_rounds,dt", DEFAULT_CASES)
