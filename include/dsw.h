@@ -123,9 +123,8 @@ extern "C" {
                                     seed: dsw_walk returns DSW_ERR_ARG until
                                     dsw_set_seed(h, seed, 1).  bf16 rows with
                                     double rounding: the kernels the inverse
-                                    CDF would use (the batched one from 4
-                                    requests, with one exchange less per
-                                    sampled step).  int8 rows or
+                                    CDF would use (the batched one from 2
+                                    requests).  int8 rows or
                                     DSW_FLAG_SINGLE_ROUND: the all-to-all
                                     kernels only, so with DSW_FLAG_BATCHED or
                                     B_max > 16 dsw_create returns
@@ -227,9 +226,9 @@ int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma, int B, int
  * and zeroes the device workspace (per-workgroup mailboxes for both step
  * parities, per-kernel-family launch counters that select the step epochs, a
  * round counter and a status word), and, when the handle can run the batched
- * kernel (B_max >= 4 or DSW_FLAG_BATCHED), about B_max * (V + 16384) * 2
+ * kernel (B_max >= 2 or DSW_FLAG_BATCHED), about B_max * (V + 16384) * 2
  * bytes (B_max rounded up to 16) where that kernel keeps the current step's
- * logits of its sampled requests for the shard that draws their token; the
+ * logits of its sampled requests for the workgroups that draw their tokens; the
  * handle owns both.  It also checks, with the
  * occupancy API, that every kernel the handle can run fits one workgroup per
  * CU (DSW_ERR_LAUNCH otherwise).  The calling thread's current device is left
@@ -452,7 +451,7 @@ int dsw_destroy(dsw_handle_t h);
  *             sampled requests need `uniforms`)
  *   the tensors, B (0 .. 256), gamma (0 .. 256) and stream   as dsw_walk
  * Errors as dsw_walk, and DSW_ERR_SCRATCH when the planner picks the batched
- * kernel (4 or more requests by default), logits is NULL and
+ * kernel (2 or more requests by default), logits is NULL and
  * ceil(B / 16) * 16 * (V + 16384) * 2 bytes exceed 32 MiB (pass logits, or
  * split the batch).  Every call on a GPU
  * shares that GPU's array and leaves its contents for the next (no clearing

@@ -350,9 +350,11 @@ extern "C" int dsw_plan_compute(const dsw_devinfo* dev, int V, int r, int gamma,
     // flag forces the all-to-all kernel (up to 16 requests).  Otherwise, as
     // measured on MI355X: one request on the MFMA engine (V = 151,936,
     // gamma = 7: 39.7 against 42.5 us per round on VALU; int8 rows widened to
-    // bf16 on chip when the shard is loaded), the MFMA all-to-all kernel for 2-3,
-    // the batched kernel from 4 requests (falling back to the all-to-all kernel
-    // where it has no shape, e.g. int8 rows beyond 12 tiles per wave).
+    // bf16 on chip when the shard is loaded), the batched kernel from 2
+    // requests (V = 151,936, gamma = 16, mixed T: 2 requests 107.2 against
+    // 175.1 us on the all-to-all kernel, 3: 130.6 against 254.5; greedy and at
+    // V = 32,000 as well), falling back to the all-to-all kernel where it has
+    // no shape (e.g. int8 rows beyond 12 tiles per wave).
     const bool forced = (flags & (DSW_FLAG_VALU_GEMV | DSW_FLAG_MFMA_GEMV)) != 0;
     const bool batched = B > kMaxBatchPersistent || (flags & DSW_FLAG_BATCHED);
     if (batched && (flags & DSW_FLAG_VALU_GEMV)) return DSW_ERR_ARG;

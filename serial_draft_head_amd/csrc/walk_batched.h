@@ -946,17 +946,28 @@ __global__ void __launch_bounds__(kBlock, 1) walk_batched(WalkParams p) {
                 __builtin_amdgcn_s_sleep(1);
             }
             if (!ok) s_abort = 1;
-            s_next[t] = ok ? checked_token((int)((w >> 24) & 0xFFFFFu), V, status) : 0;
+            const int tok = ok ? checked_token((int)((w >> 24) & 0xFFFFFu), V, status) : 0;
+            if constexpr (FD == 4) {
+                // up to 4 requests: straight into the next step's previous
+                // token (nothing reads s_prev between this step's DMA issue and
+                // the barrier below), one barrier per step fewer
+                s_prev[t] = tok;
+                if (c == 0 && ok) p.tokens[(size_t)t * gamma + k] = tok;
+            } else {
+                s_next[t] = tok;
+            }
         }
         __syncthreads();
         if (s_abort) break;
         DSW_TRACE(k, kTrArrived);
 
-        if (t < B) {
-            if (c == 0) p.tokens[(size_t)t * gamma + k] = s_next[t];
-            s_prev[t] = s_next[t];
+        if constexpr (FD != 4) {
+            if (t < B) {
+                if (c == 0) p.tokens[(size_t)t * gamma + k] = s_next[t];
+                s_prev[t] = s_next[t];
+            }
+            __syncthreads();
         }
-        __syncthreads();
         DSW_TRACE(k, kTrSelected);
         DSW_TRACE_REAL(k);
     }

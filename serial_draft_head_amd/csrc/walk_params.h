@@ -54,7 +54,7 @@ constexpr int max_owner_words() {
 }
 static_assert(max_owner_words() <= kOwnWords, "owner regions of every grid fit kOwnWords");
 constexpr int kGroup = 16;               // batched kernel: requests per MFMA column block
-constexpr int kBatchedFrom = 4;          // the planner's default: the batched kernel from this many requests
+constexpr int kBatchedFrom = 2;          // the planner's default: the batched kernel from this many requests
 constexpr unsigned kEpochMod = 0x0FFFFFFFu;   // the 28-bit epoch field of a mailbox word
 constexpr unsigned kEpochPeriod = 1u << 27;   // epochs repeat after this many steps
 constexpr int kMaxGammaMax = 4096;            // gamma_max bound: 2 gamma_max stays far below the period

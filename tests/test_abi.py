@@ -223,8 +223,10 @@ def test_planner_choices_on_mi355x_shapes(dsw):
     assert pick(dsw.plan(d, 151_936, 7, 2, flags=8)) == (594, 10, 8, 2, 0)
     c2 = dsw.plan(d, 151_936, 16, 16, flags=8)
     assert pick(c2) == (594, 10, 8, 2, 0) and c2.batch_tile == 16
-    # by default 2-3 requests take the all-to-all MFMA kernel, 4 and more the batched one
-    assert [dsw.plan(d, 151_936, 16, b).batch_tile for b in (2, 3, 4, 16)] == [4, 4, 256, 256]
+    # by default 2 and more requests take the batched kernel; where it has no
+    # shape (beyond 12 tiles per wave) the all-to-all MFMA kernel
+    assert [dsw.plan(d, 151_936, 16, b).batch_tile for b in (1, 2, 3, 4, 16)] == [1, 256, 256, 256, 256]
+    assert [dsw.plan(d, 248_320, 16, b).batch_tile for b in (2, 3, 4, 16)] == [4, 4, 4, 16]
     # 4 requests at V = 248,320: 8 AGPR tiles per wave, LDS for some, the rest streamed
     c3 = dsw.plan(d, 248_320, 16, 4, flags=8)
     assert c3.rows_per_wg == 970 and c3.tiles_per_wave == 16 and c3.path == 1 and c3.stream_rows > 0
@@ -270,10 +272,10 @@ def test_planner_gumbel_max_kernels(dsw):
     d = fake_device(dsw)
     G = dsw.FLAG_GUMBEL
     # bf16 rows, double rounding: the same kernels as the inverse CDF (the
-    # batched kernel from 4 requests); the shard layout is the same plan as
+    # batched kernel from 2 requests); the shard layout is the same plan as
     # without the flag, and up to 4 requests on the all-to-all kernels keep one
     # step's noise per row in LDS
-    for B, tile in ((1, 1), (3, 4), (4, 256), (8, 256), (16, 256), (17, 256), (253, 256)):
+    for B, tile in ((1, 1), (2, 256), (3, 256), (4, 256), (8, 256), (16, 256), (17, 256), (253, 256)):
         assert dsw.plan(d, 129_280, 5, B, flags=G).batch_tile == tile
     for B in (4, 16, 253):
         a, b = dsw.plan(d, 129_280, 5, B, flags=G), dsw.plan(d, 129_280, 5, B)
@@ -397,9 +399,12 @@ def test_planner_int8_rows(dsw):
     assert dsw.plan(d, 100_000, 7, 1, w2_dtype=dsw.INT8, flags=dsw.FLAG_VALU_GEMV).path == 0
     # short walks of one int8 request take the VALU engine, like bf16
     assert dsw.plan(d, 100_000, 3, 1, w2_dtype=dsw.INT8).engine == 0
-    # smaller vocabularies take the smaller compiled shapes
-    assert dsw.plan(d, 60_000, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 4
-    assert dsw.plan(d, 129_280, 7, 3, w2_dtype=dsw.INT8).reg_tiles == 8
+    # smaller vocabularies take the smaller compiled shapes of the all-to-all
+    # kernel; by default 3 requests take the batched one
+    M = dsw.FLAG_MFMA_GEMV
+    assert dsw.plan(d, 60_000, 7, 3, w2_dtype=dsw.INT8, flags=M).reg_tiles == 4
+    assert dsw.plan(d, 129_280, 7, 3, w2_dtype=dsw.INT8, flags=M).reg_tiles == 8
+    assert dsw.plan(d, 129_280, 7, 3, w2_dtype=dsw.INT8).batch_tile == 256
     # streaming everything works for int8 too
     s = dsw.plan(d, 248_320, 16, 1, w2_dtype=dsw.INT8, flags=1)
     assert (s.reg_rows, s.lds_rows, s.stream_rows, s.stream_bytes) == (0, 0, 970, 248_320 * 256)

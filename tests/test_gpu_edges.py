@@ -38,8 +38,9 @@ def dsw():
 
 
 # (name, requests, flags): the one-request MFMA and VALU engines, the MFMA
-# all-to-all kernel with 4- and 16-request tiles, and the batched kernel
-FAMILIES = [("mfma_b1", 1, 0), ("valu_b1", 1, 4), ("mfma_b4", 3, 0), ("mfma_b16", 8, 8), ("batched_b4", 4, 0),
+# all-to-all kernel with 4- and 16-request tiles (forced: by default 2 and
+# more requests take the batched kernel), and the batched kernel
+FAMILIES = [("mfma_b1", 1, 0), ("valu_b1", 1, 4), ("mfma_b4", 3, 8), ("mfma_b16", 8, 8), ("batched_b3", 3, 0),
             ("batched_b20", 20, 0)]
 
 

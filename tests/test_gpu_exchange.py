@@ -42,7 +42,7 @@ def dsw():
 # MFMA kernel with a 4-request tile, the batched kernel with more requests
 # than one MFMA column block and with fewer, and the GRU head (whose state
 # gather is one more exchange per step)
-FAMILIES = [("mfma_b1", 1, 0, 16), ("valu_b1", 1, 4, 7), ("mfma_b4", 3, 0, 7), ("batched", 20, 0, 16),
+FAMILIES = [("mfma_b1", 1, 0, 16), ("valu_b1", 1, 4, 7), ("mfma_b4", 3, 8, 7), ("batched", 20, 0, 16),
             ("batched_small", 12, 16, 16), ("gru", 1, 128, 5)]
 
 

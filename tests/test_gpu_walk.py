@@ -369,7 +369,7 @@ def test_device_uniforms(dsw, V, B, gamma, flags):
 GUMBEL_CASES = [  # (V, B, gamma, flags, w2 dtype)
     (32_000, 1, 6, 0, "bf16"),        # one-request MFMA engine
     (60_001, 1, 3, 0, "bf16"),        # short walk: VALU engine, ragged vocabulary
-    (4_097, 3, 5, 0, "bf16"),         # MFMA, batch tile 4, ragged
+    (4_097, 3, 5, 8, "bf16"),         # MFMA, batch tile 4, ragged
     (151_936, 1, 7, 0, "bf16"),       # the headline shape
     (248_320, 1, 4, 0, "bf16"),       # 12 register + 4 LDS tiles per wave
     (151_936, 16, 3, 8, "bf16"),      # MFMA, batch tile 16

@@ -23,14 +23,16 @@ def dsw():
     return m
 
 
-# (V, B, gamma, temps) of the first and the second (smaller) call: the
-# one-request MFMA kernel, the all-to-all kernel with a 4-request tile and the
-# batched kernel (whose sampled logits go to the static array when no logits
-# are asked for)
+# (V, B, gamma, temps) of the first and the second (smaller) call, and the
+# flags: the one-request MFMA kernel, the all-to-all kernel with a 4-request
+# tile (forced), and the batched kernel (whose sampled logits go to the static
+# array when no logits are asked for) with four tiles per epilogue and with
+# more requests
 PAIRS = [
-    ((151_936, 1, 7, "greedy"), (32_000, 1, 5, "cycle")),
-    ((100_003, 3, 7, "mixed"), (4_097, 2, 4, "mixed")),
-    ((129_280, 40, 5, "mixed"), (60_000, 6, 3, "mixed")),
+    ((151_936, 1, 7, "greedy"), (32_000, 1, 5, "cycle"), 0),
+    ((100_003, 3, 7, "mixed"), (4_097, 2, 4, "mixed"), 8),
+    ((100_003, 3, 7, "mixed"), (4_097, 2, 4, "mixed"), 0),
+    ((129_280, 40, 5, "mixed"), (60_000, 6, 3, "mixed"), 0),
 ]
 
 
@@ -40,20 +42,20 @@ def _inputs(V, B, gamma, temps, rnd):
     return W1, W2, inp
 
 
-@pytest.mark.parametrize("first,second", PAIRS)
-def test_static_entry_matches_dsw_walk(dsw, first, second):
+@pytest.mark.parametrize("first,second,flags", PAIRS)
+def test_static_entry_matches_dsw_walk(dsw, first, second, flags):
     for i, (V, B, gamma, temps) in enumerate((first, second)):
-        gh.say(f"static entry, call {i + 1}: V={V} B={B} gamma={gamma} {temps}")
+        gh.say(f"static entry, call {i + 1}: V={V} B={B} gamma={gamma} {temps} flags={flags}")
         W1, W2, inp = _inputs(V, B, gamma, temps, i)
         W1d, W2d = gh.bf16_dev(torch, W1), gh.bf16_dev(torch, W2)
         base, anchor, T, uni = gh.round_dev(torch, inp)
         # with and without the logits output (the batched kernel then keeps the
         # sampled logits in the static array)
-        ts, ls = dsw.walk_static(W1d, W2d, base, anchor, T, uni, want_logits=True)
-        ts2, _ = dsw.walk_static(W1d, W2d, base, anchor, T, uni)
+        ts, ls = dsw.walk_static(W1d, W2d, base, anchor, T, uni, want_logits=True, flags=flags)
+        ts2, _ = dsw.walk_static(W1d, W2d, base, anchor, T, uni, flags=flags)
         torch.cuda.synchronize()
         assert dsw.static_status(0) == 0
-        walker = dsw.Walker(V, gamma_max=gamma, B_max=B)
+        walker = dsw.Walker(V, gamma_max=gamma, B_max=B, flags=flags)
         th, lh = walker.walk(W1d, W2d, base, anchor, T, uni, want_logits=True)
         torch.cuda.synchronize()
         assert walker.status() == 0
